@@ -1,0 +1,231 @@
+"""Benchmark: one step = the whole hot path on one batch of synthetic input.
+
+Step = compress (probe scores, propagation, DP slots, prototype trees,
+floor + auction, pack) + T_dec decode steps over the full cache and over the
+compressed cache + per-step KL through the vocab projection. Inputs are
+generated on the GPU and resident in HBM before timing starts.
+
+Prints ONE JSON line. `value` is whole-step throughput: cached tokens
+compressed (and decoded over) per second, T / step time. Phase times come from
+HIP events on the stream the library runs on; the decode figure is algorithmic
+bytes (every packed K/V byte, ln mu, appended tokens) per decode call divided by
+the call's event time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="fulldepth")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
+    return ap.parse_args()
+
+
+def describe(cfg):
+    lens = cfg.lens if len(cfg.lens) <= 4 else f"{len(cfg.lens)} ragged, sum {sum(cfg.lens)}"
+    slots = "token-level top-B" if cfg.token_mode else (
+        f"DP slots {cfg.slot_min}-{cfg.slot_max}" if cfg.slot_len == 0 else f"fixed {cfg.slot_len}-token slots")
+    return (f"{cfg.name}: S={cfg.S} L={lens} Ly={cfg.Ly} H={cfg.H} G={cfg.G} d={cfg.d} {cfg.dtype}, "
+            f"{slots}, budget {cfg.budget_ratio:g}, {cfg.T_dec} decode steps, vocab {cfg.vocab}")
+
+
+def cpu_baseline(cfg):
+    """The oracle as it stands, on a bounded sample of the same workload: the
+    first 2048 tokens of one sequence, one layer, two KV heads, two decode
+    steps. Reported as tokens/s of the full job if its cost scaled with
+    (tokens x layers x KV heads)."""
+    import numpy as np
+    import torch
+    import oracle
+    from workload import make_inputs
+    # the oracle's DP evaluates every (end, length) cost in numpy: keep its
+    # sample short when the workload cuts slots by DP
+    n_tok = 384 if cfg.slot_len == 0 and not cfg.token_mode else 2048
+    sample = cfg.replace(S=1, Ly=1, H=2, lens=[min(n_tok, cfg.lens[0])], T_dec=2,
+                         n_plant=max(1, cfg.n_plant // 8))
+    inp = make_inputs(sample, device="cpu")
+    t0 = time.perf_counter()
+    oracle.run_pipeline(inp, sample)
+    dt = time.perf_counter() - t0
+    token_units = sample.lens[0] * sample.Ly * sample.H
+    per_token_unit = dt / token_units
+    full_units = cfg.Ly * cfg.H
+    value = 1.0 / (per_token_unit * full_units)
+    cores = torch.get_num_threads()
+    try:
+        import numpy.__config__  # noqa: F401
+    except Exception:
+        pass
+    return {"value": round(value, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"oracle pipeline (compress + 2 decode steps x 2 caches + KL) on {sample.lens[0]} tokens x "
+                       f"1 layer x 2 KV heads of the {cfg.name} workload in {dt:.1f} s; scaled by "
+                       f"token-units to {cfg.Ly} layers x {cfg.H} KV heads")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from workload import get_config, make_inputs
+    from eviction_probe_softmax_amd import kvc
+    from eviction_probe_softmax_amd.pipeline import Compressor, _row_view
+
+    cfg = get_config(args.config)
+    dev = "cuda"
+    t_gen = time.perf_counter()
+    inp = make_inputs(cfg, device=dev, seed=args.seed)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs for {cfg.name} ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    comp = Compressor(cfg, inp["cu_seqlens"], inp["K"].dtype, device=dev)
+    full = kvc.full_view(comp.pb, inp["K"], inp["V"])
+    S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
+    x_full = torch.empty((S, Td, Dm), dtype=torch.float32, device=dev)
+    x_comp = torch.empty((S, Td, Dm), dtype=torch.float32, device=dev)
+    kl_op = kvc.KL(S * Td, Dm, cfg.vocab, inp["W"].dtype, device=dev)
+    elt = inp["K"].element_size()
+    d = cfg.d
+    stream = torch.cuda.current_stream()
+
+    def step(record=None):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record is not None else None
+        if ev:
+            ev[0].record(stream)
+        out = comp.compress(inp)
+        if ev:
+            ev[1].record(stream)
+        cache = out["cache"]
+        dfull = kvc.Decoder(full, cfg.G, Td)
+        dcomp = kvc.Decoder(cache, cfg.G, Td)
+        dec_ev = []
+        for t in range(Td):
+            q = inp["Qd"][t]
+            if record is not None:
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(stream)
+            # outputs land directly in x[s, t] (row stride T_dec * d_model)
+            dfull.step(inp["Kd"], inp["Vd"], t + 1, q, _row_view(x_full, t), Td * Dm)
+            if record is not None:
+                e1.record(stream)
+            dcomp.step(inp["Kd"], inp["Vd"], t + 1, q, _row_view(x_comp, t), Td * Dm)
+            if record is not None:
+                e2.record(stream)
+                dec_ev.append((e0, e1, e2))
+        if ev:
+            ev[2].record(stream)
+        klv = kl_op(x_full.reshape(S * Td, Dm), x_comp.reshape(S * Td, Dm), inp["W"])
+        if ev:
+            ev[3].record(stream)
+        if record is not None:
+            record.append((ev, dec_ev, out, klv))
+        return out, klv
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    comp_ms, dec_ms, kl_ms, dfull_ms, dcomp_ms = [], [], [], [], []
+    for ev, dec_ev, out, klv in recs:
+        comp_ms.append(ev[0].elapsed_time(ev[1]))
+        dec_ms.append(ev[1].elapsed_time(ev[2]))
+        kl_ms.append(ev[2].elapsed_time(ev[3]))
+        for e0, e1, e2 in dec_ev:
+            dfull_ms.append(e0.elapsed_time(e1))
+            dcomp_ms.append(e1.elapsed_time(e2))
+    out, klv = recs[-1][2], recs[-1][3]
+    seg_len = out["cache"]["seg_len"].to(torch.int64)
+    n_comp = int(seg_len.sum())
+    n_full = cfg.T * cfg.Ly * cfg.H
+    units = cfg.S * cfg.Ly * cfg.H
+    # algorithmic bytes of one decode call: packed K+V (+ ln mu) once, the
+    # appended tail (mean over steps) once, the queries once
+    tail_mean = (Td + 1) / 2.0
+    q_bytes = units * cfg.G * d * elt
+    bytes_comp = n_comp * (2 * d * elt + 4) + units * tail_mean * 2 * d * elt + q_bytes
+    bytes_full = n_full * 2 * d * elt + units * tail_mean * 2 * d * elt + q_bytes
+    mean_comp_ms = float(np.mean(dcomp_ms))
+    mean_full_ms = float(np.mean(dfull_ms))
+    gbs_comp = bytes_comp / (mean_comp_ms * 1e-3) / 1e9
+    gbs_full = bytes_full / (mean_full_ms * 1e-3) / 1e9
+    # dominant kernel: decode over both caches (average bytes / average call)
+    ach = (bytes_comp + bytes_full) / ((mean_comp_ms + mean_full_ms) * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("config") == cfg.name:
+                traffic = tj.get("traffic_bytes_per_call")
+        except Exception:
+            traffic = None
+    klh = klv.detach().float().cpu().numpy()
+    B, A, F = comp.pb.budgets()
+    res = {
+        "metric": "KV tokens compressed/sec + decode-attn HBM GB/s at 25% budget; mean KL",
+        "value": round(cfg.T / (ms_per_step / 1e3), 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "seq_lens": cfg.lens if len(cfg.lens) <= 4 else None,
+                   "budget_ratio": cfg.budget_ratio, "entries_budget": B, "decode_steps": Td,
+                   "vocab": cfg.vocab},
+        "compress_ms": round(float(np.mean(comp_ms)), 3),
+        "compress_tokens_per_s": round(cfg.T / (float(np.mean(comp_ms)) / 1e3), 1),
+        "compress_entries_per_s": round(n_full / (float(np.mean(comp_ms)) / 1e3), 1),
+        "decode_ms_total": round(float(np.mean(dec_ms)), 3),
+        "decode_comp_ms_per_call": round(mean_comp_ms, 4),
+        "decode_full_ms_per_call": round(mean_full_ms, 4),
+        "decode_hbm_gbps_25pct": round(gbs_comp, 1),
+        "decode_hbm_gbps_full": round(gbs_full, 1),
+        "packed_entries": n_comp,
+        "full_entries": n_full,
+        "kl_ms": round(float(np.mean(kl_ms)), 3),
+        "mean_kl": round(float(klh.mean()), 5),
+        "max_kl": round(float(klh.max()), 5),
+        "roofline": {"bound": "hbm", "kernel": "decode (decode_partial + decode_combine per call)",
+                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_call_comp": int(bytes_comp), "bytes_per_call_full": int(bytes_full)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(cfg)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+// Internal helpers shared by the libkvc sources (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string>
+#include <vector>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+// ------------------------------------------------------------------ errors
+int set_error(int status, const std::string& msg);
+#define KVC_REQUIRE(cond, status, msg)                         \
+  do {                                                         \
+    if (!(cond)) return ::kvc::set_error((status), (msg));     \
+  } while (0)
+#define KVC_LAUNCH_CHECK(what)                                                        \
+  do {                                                                                \
+    hipError_t e_ = hipGetLastError();                                                \
+    if (e_ != hipSuccess)                                                             \
+      return ::kvc::set_error(KVC_E_HIP, std::string(what) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// ------------------------------------------------------------------ host shape helpers
+struct Regions {
+  int64_t pe, c0, c1, ss;  // prompt end, compressible [c0,c1), suffix start
+};
+inline Regions regions_of(int64_t L, const kvc_params& p) {
+  Regions r;
+  r.pe = L < p.prompt_exact ? L : p.prompt_exact;
+  int64_t ss = L - p.suffix_exact;
+  r.ss = ss > r.pe ? ss : r.pe;
+  int64_t rs = r.ss - p.recent_exact;
+  r.c1 = rs > r.pe ? rs : r.pe;
+  r.c0 = r.pe;
+  return r;
+}
+int validate_shape(const kvc_shape* s);
+int validate_params(const kvc_shape* s, const kvc_params* p);
+int64_t max_len(const kvc_shape* s);
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carver {
+  char* base;
+  size_t size, off = 0;
+  Carver(void* b, size_t n) : base((char*)b), size(n) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = (T*)(base ? base + off : nullptr);
+    off += count * sizeof(T);
+    return p;
+  }
+  bool ok() const { return off <= size; }
+};
+
+// Per-stage workspace sizes (each stage file defines its own).
+size_t ws_score(const kvc_shape* s, const kvc_params* p);
+size_t ws_propagate(const kvc_shape* s, const kvc_params* p);
+size_t ws_partition(const kvc_shape* s, const kvc_params* p);
+size_t ws_trees(const kvc_shape* s, const kvc_params* p);
+size_t ws_auction(const kvc_shape* s, const kvc_params* p);
+size_t ws_pack(const kvc_shape* s, const kvc_params* p);
+
+// Segmented selection (select.hip): among elements of each segment, find the
+// largest set by 64-bit key (descending) whose summed weight stays <= budget.
+struct SelectPlan;
+
+}  // namespace kvc
+
+// ------------------------------------------------------------------ device helpers
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 kvc_bf16x8;
+typedef float kvc_f32x16 __attribute__((ext_vector_type(16)));
+typedef float kvc_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// round-to-nearest-even fp32 -> bf16 bits (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <class T> struct ElemIO;
+template <> struct ElemIO<float> {
+  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct ElemIO<uint16_t> {
+  static __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+  static __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Order-preserving map of an fp32 score to uint32 (NaN -> 0, i.e. lowest).
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  if (f != f) return 0u;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// 64-bit selection key: larger = earlier; ties on the score go to the lower id.
+__device__ __forceinline__ uint64_t make_key(float score, uint32_t id) {
+  return ((uint64_t)f32_order_key(score) << 32) | (uint64_t)(0xffffffffu - id);
+}
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xffffffffu - (uint32_t)k; }
+
+// Sequence of a global token index (S is small; linear scan).
+__device__ __forceinline__ int seq_of(const int64_t* cu, int S, int64_t t) {
+  int s = 0;
+  while (s + 1 < S && cu[s + 1] <= t) ++s;
+  return s;
+}
+
+inline unsigned kvc_blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }

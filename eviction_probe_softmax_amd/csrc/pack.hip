@@ -1,0 +1,371 @@
+// Physical ragged cache packing.
+//
+// GraceKV page, '05 Physical cache packing': every (layer, KV head) gets an
+// independently sized segment; an unselected root writes nothing, an internal
+// frontier node writes its prototype, a singleton writes the original K/V;
+// 'Inside one cache entry': the prototype key is the mean of the
+// inverse-rotated keys re-rotated at a representative position, the value is
+// relevance weighted with a uniform base.
+//
+// Every taken op adds exactly one stored entry (Add creates the root, a
+// binary Split replaces one node by two), so the entries of a slot are the
+// taken ops of its 2n op range. Per token t the count c[t] is: 1 for exact
+// tokens, taken[t] in token mode, taken[2t] + taken[2t+1] inside slots (the
+// slot starting at t0 owns ops [2 t0, 2 t0 + 2n)). One exclusive scan over the
+// whole [Ly][H][T] count array - whose order is exactly the (l, h, s, t) order
+// of the segments - gives every token's (and every slot's first) output
+// offset. Writers: exact/kept tokens copy their bits; one wave per slot walks
+// the frontier in pre-order (= position order) and writes leaves and
+// prototypes.
+#include <cmath>
+
+#include "kvc_internal.h"
+
+namespace {
+
+constexpr int SCAN_BLOCK = 4096;  // elements per scan block (256 threads x 16)
+
+struct PackArgs {
+  const void* K;
+  const void* V;
+  const float* rel;
+  const float* node_rel;
+  const float* node_mu;
+  const uint8_t* taken;
+  const int32_t* slot_start;
+  const int32_t* n_slots;
+  const float* rc;  // rope cos [pos][d/2]
+  const float* rs;
+  const int64_t* cu;
+  int S, Ly, H, stride, token_mode;
+  int64_t T;
+  int64_t pe[64], c1[64];   // per sequence: prompt end (= compressible start), compressible end
+  float beta;               // uniform share of prototype values
+  void* oK;
+  void* oV;
+  float* olnmu;
+  int32_t* opos;
+  int64_t capacity;
+};
+
+__device__ __forceinline__ int seq_of_tok(const PackArgs& a, int64_t t) { return seq_of(a.cu, a.S, t); }
+
+__global__ void count_kernel(PackArgs a, int32_t* cnt) {
+  int64_t E = (int64_t)a.Ly * a.H * a.T;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= E) return;
+  int64_t lh = i / a.T, t = i % a.T;
+  int s = seq_of_tok(a, t);
+  int64_t p = t - a.cu[s];
+  int c;
+  if (p < a.pe[s] || p >= a.c1[s]) c = 1;
+  else if (a.token_mode) c = a.taken[i];
+  else {
+    int64_t o = lh * 2 * a.T + 2 * t;
+    c = a.taken[o] + a.taken[o + 1];
+  }
+  cnt[i] = c;
+}
+
+// block-local exclusive scan; block totals to bsum
+__global__ __launch_bounds__(256) void scan_local_kernel(const int32_t* cnt, int64_t n, int64_t* out, int64_t* bsum) {
+  __shared__ int64_t part[256];
+  int64_t b0 = (int64_t)blockIdx.x * SCAN_BLOCK;
+  int64_t v[16];
+  int64_t run = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int64_t i = b0 + threadIdx.x * 16 + j;
+    v[j] = i < n ? cnt[i] : 0;
+    run += v[j];
+  }
+  part[threadIdx.x] = run;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int64_t x = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += x;
+    __syncthreads();
+  }
+  int64_t ex = part[threadIdx.x] - run;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int64_t i = b0 + threadIdx.x * 16 + j;
+    if (i < n) out[i] = ex;
+    ex += v[j];
+  }
+  if (threadIdx.x == 255) bsum[blockIdx.x] = part[255];
+}
+
+// exclusive scan of the block totals in one block (sequential over chunks)
+__global__ __launch_bounds__(256) void scan_blocks_kernel(int64_t* bsum, int64_t nb, int64_t* total) {
+  __shared__ int64_t part[256];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int64_t c0 = 0; c0 < nb; c0 += 256) {
+    int64_t i = c0 + threadIdx.x;
+    int64_t v = i < nb ? bsum[i] : 0;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+      int64_t x = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+      __syncthreads();
+      part[threadIdx.x] += x;
+      __syncthreads();
+    }
+    if (i < nb) bsum[i] = carry + part[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == 255) carry += part[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *total = carry;
+}
+
+__global__ void scan_add_kernel(int64_t* out, int64_t n, const int64_t* bsum) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] += bsum[i / SCAN_BLOCK];
+}
+
+__global__ void seg_kernel(PackArgs a, const int64_t* off, const int64_t* total, int64_t* seg_off,
+                           int32_t* seg_len) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.S * a.Ly * a.H) return;
+  int s = i / (a.Ly * a.H), lh = i % (a.Ly * a.H);
+  int64_t b = (int64_t)lh * a.T + a.cu[s];
+  int64_t e = (int64_t)lh * a.T + a.cu[s + 1];
+  int64_t E = (int64_t)a.Ly * a.H * a.T;
+  int64_t ob = b < E ? off[b] : *total;
+  int64_t oe = e < E ? off[e] : *total;
+  seg_off[i] = ob;
+  seg_len[i] = (int32_t)(oe - ob);
+}
+
+template <class T, int D>
+__device__ __forceinline__ void copy_row(const PackArgs& a, int64_t src_row, int64_t dst, int32_t pos, int lane,
+                                         int nlanes) {
+  const T* K = (const T*)a.K + src_row * D;
+  const T* V = (const T*)a.V + src_row * D;
+  T* oK = (T*)a.oK + dst * D;
+  T* oV = (T*)a.oV + dst * D;
+  for (int j = lane; j < D; j += nlanes) {
+    oK[j] = K[j];
+    oV[j] = V[j];
+  }
+  if (lane == 0) {
+    a.olnmu[dst] = 0.f;
+    a.opos[dst] = pos;
+  }
+}
+
+// exact tokens and (token mode) kept tokens: one thread group of 16 per token
+template <class T, int D>
+__global__ void write_tokens_kernel(PackArgs a, const int64_t* off) {
+  int64_t E = (int64_t)a.Ly * a.H * a.T;
+  int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
+  int lane = threadIdx.x % 16;
+  if (i >= E) return;
+  int64_t t = i % a.T;
+  int s = seq_of_tok(a, t);
+  int64_t p = t - a.cu[s];
+  bool exact = p < a.pe[s] || p >= a.c1[s];
+  bool kept = exact || (a.token_mode && a.taken[i]);
+  if (!kept) return;
+  int64_t dst = off[i];
+  if (dst >= a.capacity) return;
+  copy_row<T, D>(a, i, dst, (int32_t)p, lane, 16);
+}
+
+// one wave per slot: frontier in pre-order, leaves copied, prototypes built
+template <class T, int D>
+__global__ __launch_bounds__(64) void write_slots_kernel(PackArgs a, const int64_t* off) {
+  constexpr int HD = D / 2;
+  __shared__ int fr_node[256], fr_st[256], fr_sz[256];
+  __shared__ int nfr;
+  const int lane = threadIdx.x;
+  // block -> (unit lh, sequence s, slot k): grid is (Ly*H*S*stride)
+  int64_t b = blockIdx.x;
+  int k = (int)(b % a.stride);
+  int64_t rest = b / a.stride;
+  int s = (int)(rest % a.S);
+  int64_t lh = rest / a.S;
+  if (k >= a.n_slots[s]) return;
+  const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
+  const int t0 = ss[k], n = ss[k + 1] - ss[k];
+  const int64_t tok0 = a.cu[s] + t0;                 // global token of the slot start
+  const int64_t obase = lh * 2 * a.T + 2 * tok0;      // op / node base
+  const uint8_t* tk = a.taken + obase;
+  if (!tk[0]) return;                                 // Add not taken: no entry
+  if (lane == 0) {
+    // pre-order walk of the frontier
+    int sj[20], sst[20], ssz[20], top = 0, m = 0;
+    sj[top] = 0; sst[top] = t0; ssz[top] = n; ++top;
+    while (top > 0) {
+      --top;
+      int j = sj[top], st = sst[top], sz = ssz[top];
+      if (sz > 1 && tk[1 + j]) {
+        int nl = (sz + 1) >> 1;
+        sj[top] = j + 2 * nl; sst[top] = st + nl; ssz[top] = sz - nl; ++top;   // right
+        sj[top] = j + 1; sst[top] = st; ssz[top] = nl; ++top;                 // left first
+      } else {
+        fr_node[m] = j;
+        fr_st[m] = st;
+        fr_sz[m] = sz;
+        ++m;
+      }
+    }
+    nfr = m;
+  }
+  __syncthreads();
+  const int64_t dst0 = off[lh * a.T + tok0];
+  const T* Ku = (const T*)a.K + (lh * a.T + a.cu[s]) * D;
+  const T* Vu = (const T*)a.V + (lh * a.T + a.cu[s]) * D;
+  const float* ru = a.rel + lh * a.T + a.cu[s];
+  for (int q = 0; q < nfr; ++q) {
+    int64_t dst = dst0 + q;
+    if (dst >= a.capacity) break;
+    int j = fr_node[q], st = fr_st[q], sz = fr_sz[q];
+    if (sz == 1) {
+      copy_row<T, D>(a, lh * a.T + a.cu[s] + st, dst, st, lane, 64);
+      continue;
+    }
+    // prototype key: lane owns rotate-half pair (p, p + D/2)
+    const float rel_n = a.node_rel[obase + j];
+    const float mu = a.node_mu[obase + j];
+    T* oK = (T*)a.oK + dst * D;
+    T* oV = (T*)a.oV + dst * D;
+    for (int p = lane; p < HD; p += 64) {
+      float s0 = 0.f, s1 = 0.f;
+      for (int i = st; i < st + sz; ++i) {
+        float x0 = ElemIO<T>::ld(Ku, (int64_t)i * D + p), x1 = ElemIO<T>::ld(Ku, (int64_t)i * D + p + HD);
+        float c = a.rc[(int64_t)i * HD + p], sn = a.rs[(int64_t)i * HD + p];
+        s0 += x0 * c + x1 * sn;       // rotation by -theta
+        s1 += x1 * c - x0 * sn;
+      }
+      float m0 = s0 / (float)sz, m1 = s1 / (float)sz;
+      int prep = st + (sz - 1) / 2;
+      float c = a.rc[(int64_t)prep * HD + p], sn = a.rs[(int64_t)prep * HD + p];
+      ElemIO<T>::st(oK, p, m0 * c - m1 * sn);
+      ElemIO<T>::st(oK, p + HD, m1 * c + m0 * sn);
+    }
+    // prototype value: (1-beta) r_i/rel + beta/n weights (uniform if rel = 0)
+    for (int dd = lane; dd < D; dd += 64) {
+      float acc = 0.f;
+      for (int i = st; i < st + sz; ++i) {
+        float w = rel_n > 0.f ? (1.f - a.beta) * ru[i] / rel_n + a.beta / (float)sz : 1.f / (float)sz;
+        acc += w * ElemIO<T>::ld(Vu, (int64_t)i * D + dd);
+      }
+      ElemIO<T>::st(oV, dd, acc);
+    }
+    if (lane == 0) {
+      a.olnmu[dst] = logf(mu);
+      a.opos[dst] = st + (sz - 1) / 2;
+    }
+  }
+}
+
+}  // namespace
+
+namespace kvc {
+size_t ws_pack(const kvc_shape* s, const kvc_params* p) {
+  int64_t E = (int64_t)s->n_layers * s->n_kv_heads * s->total_tokens;
+  int64_t nb = (E + SCAN_BLOCK - 1) / SCAN_BLOCK;
+  Carver c(nullptr, 0);
+  c.take<int32_t>((size_t)E);
+  c.take<int64_t>((size_t)E);
+  c.take<int64_t>((size_t)nb + 1);
+  c.take<int64_t>(1);
+  return c.off + 256;
+}
+}  // namespace kvc
+
+extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V, const float* rel,
+                        const kvc_trees* trees, const uint8_t* op_taken, const int32_t* slot_start,
+                        const int32_t* n_slots, const float* rope_cos, const float* rope_sin, kvc_ragged* out,
+                        void* ws, size_t ws_bytes, hipStream_t st) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  if ((r = kvc::validate_params(sh, p))) return r;
+  KVC_REQUIRE(sh->n_seq <= 64, KVC_E_SHAPE, "kvc_pack: at most 64 sequences per call");
+  KVC_REQUIRE(K && V && op_taken && out, KVC_E_INVAL, "kvc_pack: NULL input");
+  KVC_REQUIRE(out->K && out->V && out->lnmu && out->pos && out->seg_off && out->seg_len, KVC_E_INVAL,
+              "kvc_pack: NULL output buffer");
+  KVC_REQUIRE(out->capacity >= kvc_pack_capacity(sh, p), KVC_E_INVAL, "kvc_pack: capacity below kvc_pack_capacity()");
+  KVC_REQUIRE(out->dtype == sh->dtype && out->head_dim == sh->head_dim, KVC_E_DTYPE,
+              "kvc_pack: output dtype/head_dim differ from the input");
+  if (!p->token_mode)
+    KVC_REQUIRE(trees && trees->node_rel && trees->node_mu && rel && slot_start && n_slots && rope_cos && rope_sin,
+                KVC_E_INVAL, "kvc_pack: tree mode needs trees, rel, slots and RoPE tables");
+  KVC_REQUIRE(ws && ws_bytes >= kvc::ws_pack(sh, p), KVC_E_WORKSPACE, "kvc_pack: workspace too small");
+  int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
+  int64_t nb = (E + SCAN_BLOCK - 1) / SCAN_BLOCK;
+  kvc::Carver c(ws, ws_bytes);
+  int32_t* cnt = c.take<int32_t>((size_t)E);
+  int64_t* off = c.take<int64_t>((size_t)E);
+  int64_t* bsum = c.take<int64_t>((size_t)nb + 1);
+  int64_t* total = c.take<int64_t>(1);
+  PackArgs a{};
+  a.K = K;
+  a.V = V;
+  a.rel = rel;
+  a.node_rel = trees ? trees->node_rel : nullptr;
+  a.node_mu = trees ? trees->node_mu : nullptr;
+  a.taken = op_taken;
+  a.slot_start = slot_start;
+  a.n_slots = n_slots;
+  a.rc = rope_cos;
+  a.rs = rope_sin;
+  a.cu = sh->cu_seqlens_d;
+  a.S = sh->n_seq;
+  a.Ly = sh->n_layers;
+  a.H = sh->n_kv_heads;
+  a.stride = p->token_mode ? 1 : kvc_slot_stride(sh, p);
+  a.token_mode = p->token_mode;
+  a.T = sh->total_tokens;
+  for (int s = 0; s < sh->n_seq; ++s) {
+    kvc::Regions g = kvc::regions_of(sh->cu_seqlens[s + 1] - sh->cu_seqlens[s], *p);
+    a.pe[s] = g.pe;
+    a.c1[s] = g.c1;
+  }
+  a.beta = p->value_base;
+  a.oK = out->K;
+  a.oV = out->V;
+  a.olnmu = out->lnmu;
+  a.opos = out->pos;
+  a.capacity = out->capacity;
+  if (E == 0) return KVC_OK;
+  hipLaunchKernelGGL(count_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, st, a, cnt);
+  KVC_LAUNCH_CHECK("pack_count");
+  hipLaunchKernelGGL(scan_local_kernel, dim3((unsigned)nb), dim3(256), 0, st, cnt, E, off, bsum);
+  KVC_LAUNCH_CHECK("pack_scan_local");
+  hipLaunchKernelGGL(scan_blocks_kernel, dim3(1), dim3(256), 0, st, bsum, nb, total);
+  KVC_LAUNCH_CHECK("pack_scan_blocks");
+  hipLaunchKernelGGL(scan_add_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, st, off, E, bsum);
+  KVC_LAUNCH_CHECK("pack_scan_add");
+  int nseg = sh->n_seq * sh->n_layers * sh->n_kv_heads;
+  hipLaunchKernelGGL(seg_kernel, dim3(kvc_blocks(nseg, 256)), dim3(256), 0, st, a, off, total, out->seg_off,
+                     out->seg_len);
+  KVC_LAUNCH_CHECK("pack_seg");
+  int d = sh->head_dim;
+  dim3 tg(kvc_blocks(E * 16, 256));
+  if (sh->dtype == KVC_BF16) {
+    if (d == 128) hipLaunchKernelGGL((write_tokens_kernel<uint16_t, 128>), tg, dim3(256), 0, st, a, off);
+    else hipLaunchKernelGGL((write_tokens_kernel<uint16_t, 64>), tg, dim3(256), 0, st, a, off);
+  } else {
+    if (d == 128) hipLaunchKernelGGL((write_tokens_kernel<float, 128>), tg, dim3(256), 0, st, a, off);
+    else hipLaunchKernelGGL((write_tokens_kernel<float, 64>), tg, dim3(256), 0, st, a, off);
+  }
+  KVC_LAUNCH_CHECK("pack_tokens");
+  if (!p->token_mode) {
+    dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride));
+    if (sh->dtype == KVC_BF16) {
+      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(64), 0, st, a, off);
+      else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(64), 0, st, a, off);
+    } else {
+      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<float, 128>), sg, dim3(64), 0, st, a, off);
+      else hipLaunchKernelGGL((write_slots_kernel<float, 64>), sg, dim3(64), 0, st, a, off);
+    }
+    KVC_LAUNCH_CHECK("pack_slots");
+  }
+  return KVC_OK;
+}

@@ -1,0 +1,338 @@
+// Slot partition of each sequence's compressible region.
+//
+// GraceKV page, '01 Curvature-guided partition' and technical details: the
+// normalized hidden states form a trajectory; cut where it turns; a dynamic
+// program also weighs within-slot dispersion and reasonable slot lengths
+// (16-128 tokens, target 64).
+//
+// Costs are quantized to integers (round(x * 2^20)) so the DP itself is exact
+// integer arithmetic: given the same quantized costs it reproduces the same
+// cuts on any machine.
+//   turning: one workgroup per token, three dot products per window.
+//   costs:   one wave per slot END token; the wave walks back over at most
+//            slot_max tokens keeping the window sum in registers (lane = 64
+//            hidden dims), so every (end, length) dispersion is
+//            sum ||h^||^2 - ||sum h^||^2 / n without a prefix-sum cancellation.
+//   dp:      one 1024-thread workgroup per sequence. A slot is at least
+//            slot_min tokens long, so the values of slot_min consecutive ends
+//            depend only on earlier ends: wave w evaluates end e0 + w, all
+//            candidates of a lane pair packed into one int64 key
+//            (value * 256 + (255 - (n - slot_min))) whose minimum breaks ties
+//            toward the longer last slot (the earlier cut).
+#include <cmath>
+
+#include "kvc_internal.h"
+
+namespace {
+
+constexpr double QSCALE = 1048576.0;  // 2^20
+constexpr int64_t INF_Q = (int64_t)1 << 52;
+
+struct PartArgs {
+  const void* hidden;
+  int Dh;
+  const int64_t* cu;
+  int S;
+  int64_t T;
+  int nmin, nmax, target, stride;
+  float lam_len, lam_curv;
+  int64_t c0[64], c1[64];   // compressible region per sequence (sequence positions)
+  int64_t* cost_q;          // [T][nmax - nmin + 1]
+  int64_t* cut_q;           // [T]
+  float* inv;               // [T] 1/||h_t||
+  float* nrm2;              // [T] ||h^_t||^2
+  int32_t* slot_start;      // [S][stride + 1]
+  int32_t* n_slots;         // [S]
+};
+
+template <class T>
+__global__ __launch_bounds__(256) void norm_kernel(PartArgs a) {
+  int64_t t = blockIdx.x;
+  const T* h = (const T*)a.hidden + t * a.Dh;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < a.Dh; i += 256) {
+    float x = ElemIO<T>::ld(h, i);
+    ss += x * x;
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float tot = red[0] + red[1] + red[2] + red[3];
+    float iv = tot > 0.f ? 1.f / sqrtf(tot) : 0.f;
+    a.inv[t] = iv;
+    a.nrm2[t] = tot * iv * iv;
+  }
+}
+
+__device__ __forceinline__ int64_t qround(double x) { return (int64_t)floor(x * QSCALE + 0.5); }
+
+// kappa_b = mean over valid windows of (1 - cos(h^_b - h^_{b-w}, h^_{b+w} - h^_b)) / 2
+template <class T>
+__global__ __launch_bounds__(256) void turning_kernel(PartArgs a) {
+  int64_t t = blockIdx.x;
+  int s = seq_of(a.cu, a.S, t);
+  int64_t L = a.cu[s + 1] - a.cu[s];
+  int64_t b = t - a.cu[s];
+  __shared__ float red[4][3];
+  const int ws[2] = {2, 8};
+  float acc = 0.f;
+  int nval = 0;
+  const T* H = (const T*)a.hidden;
+  for (int wi = 0; wi < 2; ++wi) {
+    int w = ws[wi];
+    if (b - w < 0 || b + w > L - 1) continue;
+    float ib = a.inv[t], ip = a.inv[t - w], iq = a.inv[t + w];
+    float uv = 0.f, uu = 0.f, vv = 0.f;
+    for (int i = threadIdx.x; i < a.Dh; i += 256) {
+      float xb = ElemIO<T>::ld(H, t * a.Dh + i) * ib;
+      float u = xb - ElemIO<T>::ld(H, (t - w) * a.Dh + i) * ip;
+      float v = ElemIO<T>::ld(H, (t + w) * a.Dh + i) * iq - xb;
+      uv += u * v;
+      uu += u * u;
+      vv += v * v;
+    }
+    uv = wave_sum(uv);
+    uu = wave_sum(uu);
+    vv = wave_sum(vv);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) {
+      red[threadIdx.x >> 6][0] = uv;
+      red[threadIdx.x >> 6][1] = uu;
+      red[threadIdx.x >> 6][2] = vv;
+    }
+    __syncthreads();
+    float UV = red[0][0] + red[1][0] + red[2][0] + red[3][0];
+    float UU = red[0][1] + red[1][1] + red[2][1] + red[3][1];
+    float VV = red[0][2] + red[1][2] + red[2][2] + red[3][2];
+    if (UU > 0.f && VV > 0.f) {
+      acc += (1.f - UV / (sqrtf(UU) * sqrtf(VV))) * 0.5f;
+      ++nval;
+    }
+  }
+  if (threadIdx.x == 0) {
+    float kap = nval ? acc / (float)nval : 0.f;
+    a.cut_q[t] = qround((double)a.lam_curv * (double)kap);
+  }
+}
+
+// one wave per slot end token (the slot's last token)
+template <class T>
+__global__ __launch_bounds__(256) void cost_kernel(PartArgs a) {
+  constexpr int MAXDPL = 64;  // hidden dims per lane (Dh <= 4096)
+  int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (t >= a.T) return;
+  int s = seq_of(a.cu, a.S, t);
+  int64_t p = t - a.cu[s];             // the slot [p - n + 1, p] ends here
+  if (p < a.c0[s] || p >= a.c1[s]) return;
+  const int ncol = a.nmax - a.nmin + 1;
+  int64_t* row = a.cost_q + t * ncol;
+  const int dpl = (a.Dh + 63) / 64;
+  float S[MAXDPL];
+#pragma unroll
+  for (int j = 0; j < MAXDPL; ++j) S[j] = 0.f;
+  float sq = 0.f;
+  const T* H = (const T*)a.hidden;
+  for (int n = 1; n <= a.nmax; ++n) {
+    int64_t i = p - n + 1;             // token added to the window
+    if (i < a.c0[s]) break;
+    int64_t g = a.cu[s] + i;
+    float iv = a.inv[g];
+    sq += a.nrm2[g];
+#pragma unroll
+    for (int j = 0; j < MAXDPL; ++j) {
+      if (j >= dpl) break;
+      int dd = j * 64 + lane;
+      if (dd < a.Dh) S[j] += ElemIO<T>::ld(H, g * a.Dh + dd) * iv;
+    }
+    if (n >= a.nmin) {
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < MAXDPL; ++j)
+        if (j < dpl) part += S[j] * S[j];
+      float ss = wave_sum(part);
+      if (lane == 0) {
+        double disp = (double)sq - (double)ss / (double)n;
+        double x = ((double)n - a.target) / (double)a.target;
+        row[n - a.nmin] = qround(disp + (double)a.lam_len * x * x);
+      }
+    }
+  }
+}
+
+// exact integer DP; one 1024-thread block per sequence
+__global__ __launch_bounds__(1024) void dp_kernel(PartArgs a) {
+  constexpr int RING = 512;
+  __shared__ int64_t fr[RING];
+  __shared__ uint8_t arg[32768 + 8];
+  const int s = blockIdx.x;
+  const int64_t c0 = a.c0[s], c1 = a.c1[s];
+  const int64_t Lc = c1 - c0;
+  int32_t* out = a.slot_start + (int64_t)s * (a.stride + 1);
+  if (Lc <= 0) {
+    if (threadIdx.x == 0) {
+      a.n_slots[s] = 0;
+      out[0] = (int32_t)c0;
+    }
+    return;
+  }
+  if (Lc < a.nmin) {
+    if (threadIdx.x == 0) {
+      a.n_slots[s] = 1;
+      out[0] = (int32_t)c0;
+      out[1] = (int32_t)c1;
+    }
+    return;
+  }
+  const int ncol = a.nmax - a.nmin + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t gbase = a.cu[s] + c0;    // global token of region position 0
+  if (threadIdx.x == 0) fr[0] = 0;
+  __syncthreads();
+  const int step = a.nmin < 16 ? a.nmin : 16;  // ends that depend only on earlier ends
+  for (int64_t e0 = 1; e0 <= Lc; e0 += step) {
+    int64_t e = e0 + wave;               // region-relative end (exclusive)
+    int64_t best = INT64_MAX;
+    const bool mine = wave < step && e <= Lc;
+    if (mine) {
+      for (int c = lane; c < ncol; c += 64) {
+        int n = a.nmin + c;
+        int64_t pv = e - n;
+        if (pv < 0) continue;
+        int64_t f = fr[pv % RING];
+        if (f >= INF_Q) continue;
+        int64_t v = f + a.cost_q[(gbase + e - 1) * ncol + c];
+        if (pv > 0) v -= a.cut_q[gbase + pv];
+        int64_t key = v * 256 + (255 - c);
+        best = key < best ? key : best;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        int64_t other = __shfl_xor(best, o, 64);
+        best = other < best ? other : best;
+      }
+    }
+    __syncthreads();                    // every read of fr for this block is done
+    if (mine && lane == 0) {
+      if (best == INT64_MAX) {
+        fr[e % RING] = INF_Q;
+        arg[e] = 255;
+      } else {
+        int64_t v = best >= 0 ? best / 256 : -((-best + 255) / 256);
+        int c = 255 - (int)(best - v * 256);
+        fr[e % RING] = v;
+        arg[e] = (uint8_t)c;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    // backtrack twice: count, then write the starts in position order
+    int m = 0;
+    for (int64_t e = Lc; e > 0; e -= a.nmin + arg[e]) ++m;
+    a.n_slots[s] = m;
+    out[m] = (int32_t)c1;
+    int k = m;
+    for (int64_t e = Lc; e > 0;) {
+      e -= a.nmin + arg[e];
+      out[--k] = (int32_t)(c0 + e);
+    }
+  }
+}
+
+__global__ void fixed_slots_kernel(PartArgs a, int slot_len) {
+  int s = blockIdx.x;
+  int64_t c0 = a.c0[s], c1 = a.c1[s];
+  int64_t n = c1 > c0 ? (c1 - c0 + slot_len - 1) / slot_len : 0;
+  int32_t* out = a.slot_start + (int64_t)s * (a.stride + 1);
+  for (int64_t k = threadIdx.x; k <= n; k += blockDim.x) {
+    int64_t v = c0 + k * slot_len;
+    out[k] = (int32_t)(v < c1 ? v : c1);
+  }
+  if (threadIdx.x == 0) a.n_slots[s] = (int32_t)n;
+}
+
+}  // namespace
+
+namespace kvc {
+size_t ws_partition(const kvc_shape* s, const kvc_params* p) {
+  int ncol = p->slot_max - p->slot_min + 1;
+  Carver c(nullptr, 0);
+  c.take<float>((size_t)s->total_tokens * 2);
+  c.take<int64_t>((size_t)s->total_tokens * (ncol > 0 ? ncol : 1));
+  c.take<int64_t>((size_t)s->total_tokens);
+  return c.off + 256;
+}
+}  // namespace kvc
+
+extern "C" int kvc_partition(const kvc_shape* sh, const kvc_params* p, const void* hidden, int32_t hidden_dim,
+                             int32_t mode, int64_t* dp_cost_q, int64_t* dp_cut_q, int32_t* slot_start,
+                             int32_t* n_slots, void* ws, size_t ws_bytes, hipStream_t st) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  if ((r = kvc::validate_params(sh, p))) return r;
+  KVC_REQUIRE(!p->token_mode, KVC_E_INVAL, "kvc_partition: token mode has no slots");
+  KVC_REQUIRE(sh->n_seq <= 64, KVC_E_SHAPE, "kvc_partition: at most 64 sequences per call");
+  KVC_REQUIRE(slot_start && n_slots, KVC_E_INVAL, "kvc_partition: NULL output");
+  KVC_REQUIRE(mode == 0 || mode == 1, KVC_E_INVAL, "kvc_partition: mode must be 0 or 1");
+  PartArgs a{};
+  a.cu = sh->cu_seqlens_d;
+  a.S = sh->n_seq;
+  a.T = sh->total_tokens;
+  a.nmin = p->slot_min;
+  a.nmax = p->slot_max;
+  a.target = p->slot_target;
+  a.stride = kvc_slot_stride(sh, p);
+  a.lam_len = p->lambda_len;
+  a.lam_curv = p->lambda_curv;
+  a.slot_start = slot_start;
+  a.n_slots = n_slots;
+  for (int s = 0; s < sh->n_seq; ++s) {
+    kvc::Regions g = kvc::regions_of(sh->cu_seqlens[s + 1] - sh->cu_seqlens[s], *p);
+    a.c0[s] = g.c0;
+    a.c1[s] = g.c1;
+  }
+  if (p->slot_len > 0) {
+    hipLaunchKernelGGL(fixed_slots_kernel, dim3(sh->n_seq), dim3(256), 0, st, a, p->slot_len);
+    KVC_LAUNCH_CHECK("fixed_slots");
+    return KVC_OK;
+  }
+  KVC_REQUIRE(kvc::max_len(sh) <= 32768, KVC_E_SHAPE, "kvc_partition: DP slots need sequences <= 32768 tokens");
+  KVC_REQUIRE(ws && ws_bytes >= kvc::ws_partition(sh, p), KVC_E_WORKSPACE, "kvc_partition: workspace too small");
+  int ncol = p->slot_max - p->slot_min + 1;
+  kvc::Carver c(ws, ws_bytes);
+  a.inv = c.take<float>((size_t)sh->total_tokens);
+  a.nrm2 = c.take<float>((size_t)sh->total_tokens);
+  int64_t* cq = c.take<int64_t>((size_t)sh->total_tokens * ncol);
+  int64_t* kq = c.take<int64_t>((size_t)sh->total_tokens);
+  if (mode == 1) {
+    KVC_REQUIRE(dp_cost_q && dp_cut_q, KVC_E_INVAL, "kvc_partition: mode 1 needs dp_cost_q and dp_cut_q");
+    a.cost_q = dp_cost_q;
+    a.cut_q = dp_cut_q;
+  } else {
+    KVC_REQUIRE(hidden && hidden_dim >= 1 && hidden_dim <= 4096, KVC_E_INVAL,
+                "kvc_partition: hidden states with 1 <= hidden_dim <= 4096 are required");
+    a.hidden = hidden;
+    a.Dh = hidden_dim;
+    a.cost_q = dp_cost_q ? dp_cost_q : cq;
+    a.cut_q = dp_cut_q ? dp_cut_q : kq;
+    dim3 gt((unsigned)sh->total_tokens), gc(kvc_blocks(sh->total_tokens, 4));
+    if (sh->total_tokens > 0) {
+      if (sh->dtype == KVC_BF16) {
+        hipLaunchKernelGGL(norm_kernel<uint16_t>, gt, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(turning_kernel<uint16_t>, gt, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(cost_kernel<uint16_t>, gc, dim3(256), 0, st, a);
+      } else {
+        hipLaunchKernelGGL(norm_kernel<float>, gt, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(turning_kernel<float>, gt, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(cost_kernel<float>, gc, dim3(256), 0, st, a);
+      }
+      KVC_LAUNCH_CHECK("partition_costs");
+    }
+  }
+  hipLaunchKernelGGL(dp_kernel, dim3(sh->n_seq), dim3(1024), 0, st, a);
+  KVC_LAUNCH_CHECK("partition_dp");
+  return KVC_OK;
+}

@@ -1,0 +1,783 @@
+// Budget spending: token-level top-B, singleton floor, Add/Split auction.
+//
+// DistillCache paper, Algorithm 1 (keep the top-B tokens by score);
+// GraceKV page, 'Exact-information safeguard' (singleton floor: high-value
+// leaves first, each paying its untaken tree path, under a hard cap) and
+// '04 Top-down budget flow' (one global queue of exposed Add/Split ops; the
+// highest affordable utility wins next).
+//
+// Everything is integer selection on 64-bit keys (score bits above, inverted
+// id below, so larger = earlier and ties go to the lower id):
+//
+// * select(): per sequence, the largest key T whose cumulative weight from the
+//   top first exceeds the budget; keys above T are the answer. MSB-first radix
+//   over 8 digits; each digit is a grid-wide histogram (integer atomics, so
+//   the result is exact and repeatable) plus a one-block choose step.
+// * Auction: the best-first greedy pops ops in non-increasing order of
+//   beta(op) = min over the op's untaken root path of (u, -id); ties in beta
+//   are exactly the ops that share the op b* achieving that minimum, and they
+//   are popped together in best-first order below b*. So the taken set is
+//   {beta > T} plus the first k best-first pops of the tied group, which one
+//   block per sequence finishes inside b*'s slot.
+// * Floor: top-F leaves by fp32(s * r); every candidate's marginal path cost
+//   assuming all earlier candidates were accepted (first coverer of each op by
+//   atomicMax of keys); a weighted select finds the first candidate that does
+//   not fit; the few candidates after it are resolved by at most
+//   (remaining budget) rounds of "earliest candidate whose current path cost
+//   fits".
+#include <cmath>
+
+#include "kvc_internal.h"
+
+namespace {
+
+constexpr int MAXS = 64;
+constexpr int CH = 2048;  // elements per workgroup in the histogram pass
+
+struct Ranges {
+  int S, U;                 // segments (sequences) and units per segment
+  int64_t unit_stride;      // element index stride between units
+  int64_t start[MAXS];      // first element of segment s within a unit
+  int64_t len[MAXS];        // elements of segment s per unit
+  int64_t nchunk[MAXS];     // ceil(len / CH)
+};
+
+__device__ __forceinline__ bool range_work(const Ranges& r, int64_t b, int& s, int64_t& base, int64_t& n) {
+  int64_t acc = 0;
+  for (int q = 0; q < r.S; ++q) {
+    int64_t nb = r.nchunk[q] * r.U;
+    if (b < acc + nb) {
+      int64_t x = b - acc;
+      int64_t u = x / r.nchunk[q], c = x % r.nchunk[q];
+      s = q;
+      int64_t off = c * CH;
+      base = u * r.unit_stride + r.start[q] + off;
+      n = r.len[q] - off < CH ? r.len[q] - off : CH;
+      return true;
+    }
+    acc += nb;
+  }
+  return false;
+}
+
+struct SelState {
+  uint64_t prefix;
+  int64_t above;    // weight of keys strictly above the prefix range
+  int64_t budget;
+  int all;          // total weight <= budget: everything is selected
+  int pad;
+};
+
+// ------------------------------------------------------------------ sources
+struct TokSrc {       // token mode: rel of every compressible token
+  const float* rel;
+  __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
+    k = make_key(rel[i], (uint32_t)i);
+    w = 1;
+    return true;
+  }
+};
+struct LeafSrc {      // floor candidates: fp32(s_lh * r_i)
+  const float* rel;
+  const float* sens;  // [S][Ly][H]
+  int64_t T;
+  int LH;
+  __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
+    int lh = (int)(i / T);
+    float v = __fmul_rn(sens[(int64_t)s * LH + lh], rel[i]);
+    k = make_key(v, (uint32_t)i);
+    w = 1;
+    return true;
+  }
+};
+struct CandSrc {      // floor candidates with their marginal path costs
+  const uint64_t* key;
+  const int32_t* cost;
+  __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
+    k = key[i];
+    w = cost[i];
+    return true;
+  }
+};
+struct OpSrc {        // auction: untaken real ops keyed by beta
+  const uint64_t* beta;
+  const uint8_t* cost;
+  const uint8_t* taken;
+  __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
+    if (cost[i] == 0 || taken[i]) return false;
+    k = beta[i];
+    w = 1;
+    return true;
+  }
+};
+
+template <class Src>
+__global__ __launch_bounds__(256) void hist_kernel(Ranges r, Src src, const SelState* st, int pass,
+                                                   unsigned long long* hist) {
+  __shared__ unsigned long long h[256];
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  SelState S_ = st[s];
+  if (S_.all) return;
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  int shift = 56 - 8 * pass;
+  uint64_t hmask = pass == 0 ? 0ull : (~0ull << (64 - 8 * pass));
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    uint64_t k;
+    int64_t w;
+    if (!src.get(base + i, s, k, w)) continue;
+    if ((k & hmask) == S_.prefix && w) atomicAdd(&h[(k >> shift) & 255], (unsigned long long)w);
+  }
+  __syncthreads();
+  if (h[threadIdx.x]) atomicAdd(&hist[s * 256 + threadIdx.x], h[threadIdx.x]);
+}
+
+// one block per segment: pick the digit where the cumulative weight first
+// exceeds the budget, then clear the histogram for the next pass
+__global__ __launch_bounds__(256) void choose_kernel(SelState* st, int pass, unsigned long long* hist) {
+  __shared__ unsigned long long h[256];
+  int s = blockIdx.x;
+  h[threadIdx.x] = hist[s * 256 + threadIdx.x];
+  hist[s * 256 + threadIdx.x] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0 && !st[s].all) {
+    SelState S_ = st[s];
+    int64_t acc = S_.above;
+    int shift = 56 - 8 * pass;
+    int dsel = -1;
+    for (int d = 255; d >= 0; --d) {
+      if (acc + (int64_t)h[d] > S_.budget) {
+        dsel = d;
+        break;
+      }
+      acc += (int64_t)h[d];
+    }
+    if (dsel < 0) {
+      // only possible on the first pass: the whole segment fits
+      st[s].all = 1;
+      st[s].above = acc;
+    } else {
+      st[s].above = acc;
+      st[s].prefix = S_.prefix | ((uint64_t)dsel << shift);
+    }
+  }
+}
+
+__global__ void init_state_kernel(SelState* st, int S, const int64_t* budget_dev, Ranges r_host_budget,
+                                  int use_dev, const int64_t* subtract) {
+  int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= S) return;
+  SelState x;
+  x.prefix = 0;
+  x.above = 0;
+  int64_t b = use_dev ? budget_dev[s] : r_host_budget.len[s];
+  if (subtract) b -= subtract[s];
+  x.budget = b < 0 ? 0 : b;
+  x.all = 0;
+  x.pad = 0;
+  st[s] = x;
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+__global__ void zero_u8_kernel(uint8_t* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+int64_t ranges_blocks(const Ranges& r) {
+  int64_t n = 0;
+  for (int s = 0; s < r.S; ++s) n += r.nchunk[s] * r.U;
+  return n;
+}
+
+template <class Src>
+int run_select(const Ranges& r, const Src& src, SelState* st, unsigned long long* hist, hipStream_t stream) {
+  int64_t nb = ranges_blocks(r);
+  for (int pass = 0; pass < 8; ++pass) {
+    if (nb > 0) {
+      hipLaunchKernelGGL(hist_kernel<Src>, dim3((unsigned)nb), dim3(256), 0, stream, r, src, st, pass, hist);
+      KVC_LAUNCH_CHECK("select_hist");
+    }
+    hipLaunchKernelGGL(choose_kernel, dim3(r.S), dim3(256), 0, stream, st, pass, hist);
+    KVC_LAUNCH_CHECK("select_choose");
+  }
+  return KVC_OK;
+}
+
+// ------------------------------------------------------------------ token mode
+__global__ __launch_bounds__(256) void mark_tokens_kernel(Ranges r, TokSrc src, const SelState* st, uint8_t* taken,
+                                                          int64_t* spent) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  SelState S_ = st[s];
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    uint64_t k;
+    int64_t w;
+    src.get(base + i, s, k, w);
+    if (S_.all || k > S_.prefix) taken[base + i] = 1;
+  }
+}
+__global__ void token_spent_kernel(const SelState* st, const Ranges r, int64_t* spent, int64_t* spent_floor) {
+  int s = threadIdx.x;
+  if (s >= r.S) return;
+  spent[s] = st[s].above;
+  if (spent_floor) spent_floor[s] = 0;
+}
+
+// ------------------------------------------------------------------ slot / tree helpers
+struct TreeArgs {
+  const int64_t* cu;
+  const int32_t* slot_start;  // [S][stride+1]
+  const int32_t* n_slots;
+  int stride;
+  int S, Ly, H;
+  int64_t T;
+};
+
+// slot of sequence position t (binary search over the slot starts)
+__device__ __forceinline__ int slot_of(const TreeArgs& a, int s, int t, int& t0, int& n) {
+  const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
+  int lo = 0, hi = a.n_slots[s] - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (ss[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  t0 = ss[lo];
+  n = ss[lo + 1] - ss[lo];
+  return lo;
+}
+
+// Root-to-leaf path of token t in a slot [t0, t0+n): writes internal node
+// pre-order indices, returns their count.
+__device__ __forceinline__ int leaf_path(int t0, int n, int t, int* nodes) {
+  int j = 0, st = t0, sz = n, c = 0;
+  while (sz > 1) {
+    nodes[c++] = j;
+    int nl = (sz + 1) >> 1;
+    if (t < st + nl) {
+      j += 1;
+      sz = nl;
+    } else {
+      j += 2 * nl;
+      st += nl;
+      sz -= nl;
+    }
+  }
+  return c;
+}
+
+// ------------------------------------------------------------------ floor
+struct FloorArgs {
+  TreeArgs ta;
+  const float* rel;
+  const float* sens;
+  const uint8_t* op_cost;
+  uint8_t* taken;
+  uint64_t* cover;     // [Ly][H][2T] first coverer key per op
+  uint64_t* ckey;      // [S][Fmax]
+  int32_t* cid;        // [S][Fmax] leaf flat index
+  int32_t* ccost;      // [S][Fmax]
+  int32_t* ccount;     // [S]
+  int64_t Fmax;
+};
+
+__global__ __launch_bounds__(256) void floor_collect_kernel(Ranges r, LeafSrc src, const SelState* st, FloorArgs f) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  SelState S_ = st[s];
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    uint64_t k;
+    int64_t w;
+    src.get(base + i, s, k, w);
+    if (S_.all || k > S_.prefix) {
+      int slot = atomicAdd(&f.ccount[s], 1);
+      if (slot < f.Fmax) {
+        f.ckey[(int64_t)s * f.Fmax + slot] = k;
+        f.cid[(int64_t)s * f.Fmax + slot] = (int32_t)(base + i);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void cand_path(const FloorArgs& f, int s, int64_t leaf, int64_t* ops, int& nops) {
+  const TreeArgs& a = f.ta;
+  int64_t lh = leaf / a.T;
+  int t = (int)(leaf % a.T - a.cu[s]);
+  int t0, n;
+  slot_of(a, s, t, t0, n);
+  int nodes[8];
+  int c = leaf_path(t0, n, t, nodes);
+  int64_t base = lh * 2 * a.T + 2 * (a.cu[s] + t0);
+  ops[0] = base;
+  for (int q = 0; q < c; ++q) ops[1 + q] = base + 1 + nodes[q];
+  nops = 1 + c;
+}
+
+// one thread per candidate slot of every sequence
+__global__ void floor_cover_kernel(FloorArgs f, int S) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int s = (int)(i / f.Fmax);
+  int64_t k = i % f.Fmax;
+  if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
+  int64_t ops[9];
+  int nops;
+  cand_path(f, s, f.cid[i], ops, nops);
+  uint64_t key = f.ckey[i];
+  for (int q = 0; q < nops; ++q) atomicMax((unsigned long long*)&f.cover[ops[q]], (unsigned long long)key);
+}
+__global__ void floor_cost_kernel(FloorArgs f, int S) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int s = (int)(i / f.Fmax);
+  int64_t k = i % f.Fmax;
+  if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
+  int64_t ops[9];
+  int nops;
+  cand_path(f, s, f.cid[i], ops, nops);
+  uint64_t key = f.ckey[i];
+  int c = 0;
+  for (int q = 0; q < nops; ++q)
+    if (f.cover[ops[q]] == key) c += f.op_cost[ops[q]];
+  f.ccost[i] = c;
+}
+// accept the prefix (keys above the first candidate that does not fit)
+__global__ void floor_accept_kernel(FloorArgs f, int S, const SelState* st) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int s = (int)(i / f.Fmax);
+  int64_t k = i % f.Fmax;
+  if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
+  SelState S_ = st[s];
+  if (!(S_.all || f.ckey[i] > S_.prefix)) return;
+  int64_t ops[9];
+  int nops;
+  cand_path(f, s, f.cid[i], ops, nops);
+  for (int q = 0; q < nops; ++q) f.taken[ops[q]] = 1;
+}
+// Candidates after the first one that did not fit, in order; one block per
+// sequence. Each round accepts the earliest remaining candidate whose current
+// path cost is between 1 and the remaining floor budget (candidates before it
+// cost more than what is left, or nothing); at most `remaining` rounds.
+__global__ __launch_bounds__(256) void floor_tail_kernel(FloorArgs f, const SelState* st, Ranges fb,
+                                                         int64_t* spent_floor) {
+  __shared__ unsigned long long best;
+  __shared__ unsigned long long pre;
+  __shared__ int64_t rem_s;
+  int s = blockIdx.x;
+  SelState S_ = st[s];
+  int64_t F = fb.len[s];
+  int64_t cnt = min((int64_t)f.ccount[s], f.Fmax);
+  if (threadIdx.x == 0) pre = 0;
+  __syncthreads();
+  unsigned long long loc = 0;
+  for (int64_t k = threadIdx.x; k < cnt; k += 256) {
+    int64_t i = (int64_t)s * f.Fmax + k;
+    if (S_.all || f.ckey[i] > S_.prefix) loc += (unsigned long long)f.ccost[i];
+  }
+  if (loc) atomicAdd(&pre, loc);
+  __syncthreads();
+  if (threadIdx.x == 0) rem_s = F - (int64_t)pre;
+  __syncthreads();
+  uint64_t pos = S_.prefix;  // the first candidate that did not fit; only later ones remain
+  for (int round = 0; round < 64 && !S_.all; ++round) {
+    int64_t rem = rem_s;
+    if (rem <= 0) break;
+    if (threadIdx.x == 0) best = 0;
+    __syncthreads();
+    for (int64_t k = threadIdx.x; k < cnt; k += 256) {
+      int64_t i = (int64_t)s * f.Fmax + k;
+      uint64_t key = f.ckey[i];
+      if (key >= pos) continue;
+      int64_t ops[9];
+      int nops;
+      cand_path(f, s, f.cid[i], ops, nops);
+      int c = 0;
+      for (int q = 0; q < nops; ++q)
+        if (!f.taken[ops[q]]) c += f.op_cost[ops[q]];
+      if (c >= 1 && c <= rem) atomicMax(&best, (unsigned long long)key);
+    }
+    __syncthreads();
+    uint64_t win = best;
+    __syncthreads();
+    if (win == 0) break;
+    for (int64_t k = threadIdx.x; k < cnt; k += 256) {
+      int64_t i = (int64_t)s * f.Fmax + k;
+      if (f.ckey[i] != win) continue;
+      int64_t ops[9];
+      int nops;
+      cand_path(f, s, f.cid[i], ops, nops);
+      int c = 0;
+      for (int q = 0; q < nops; ++q)
+        if (!f.taken[ops[q]]) c += f.op_cost[ops[q]];
+      for (int q = 0; q < nops; ++q) f.taken[ops[q]] = 1;
+      rem_s = rem - c;
+    }
+    pos = win;
+    __syncthreads();
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) spent_floor[s] = F - rem_s;
+}
+
+// ------------------------------------------------------------------ auction
+struct AucArgs {
+  TreeArgs ta;
+  const float* util;
+  const uint8_t* cost;
+  uint8_t* taken;
+  uint64_t* beta;
+  int64_t c0[MAXS], c1[MAXS];  // compressible region per sequence
+};
+
+__device__ __forceinline__ uint64_t op_key(const AucArgs& a, int64_t op) {
+  float u = a.util[op];
+  return make_key(u, (uint32_t)op);
+}
+
+// beta of every op = min key over the untaken part of its root path
+__global__ void beta_kernel(AucArgs a, Ranges r) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  const TreeArgs& ta = a.ta;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    int64_t op = base + i;
+    uint64_t b = 0;
+    if (a.cost[op] != 0 && !a.taken[op]) {
+      int64_t lh = op / (2 * ta.T);
+      int64_t x = op % (2 * ta.T);
+      int t = (int)(x / 2 - ta.cu[s]);
+      int t0, nn;
+      slot_of(ta, s, t, t0, nn);
+      int64_t sbase = lh * 2 * ta.T + 2 * (ta.cu[s] + t0);
+      int jop = (int)(op - sbase);  // 0 = Add, 1+j = Split(node j)
+      b = ~0ull;
+      // Add
+      if (!a.taken[sbase]) b = op_key(a, sbase);
+      if (jop > 0) {
+        int target = jop - 1;
+        int j = 0, sz = nn;
+        while (true) {
+          int64_t o = sbase + 1 + j;
+          if (!a.taken[o]) {
+            uint64_t k = op_key(a, o);
+            if (k < b) b = k;
+          }
+          if (j == target) break;
+          int nl = (sz + 1) >> 1;
+          if (target < j + 2 * nl) {
+            j += 1;
+            sz = nl;
+          } else {
+            j += 2 * nl;
+            sz -= nl;
+          }
+        }
+      }
+    }
+    a.beta[op] = b;
+  }
+}
+
+__global__ void auction_mark_kernel(AucArgs a, Ranges r, const SelState* st) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  SelState S_ = st[s];
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    int64_t op = base + i;
+    if (a.cost[op] == 0 || a.taken[op]) continue;
+    if (S_.all || a.beta[op] > S_.prefix) a.taken[op] = 2;  // 2 = taken by the auction in this call
+  }
+}
+
+// Finish the tied group below b* with a best-first walk; one block per
+// sequence (thread 0 works: the slot holds at most 2*128 ops).
+__global__ __launch_bounds__(64) void auction_fixup_kernel(AucArgs a, const SelState* st, const int64_t* spent_floor,
+                                                           int64_t* spent) {
+  __shared__ int sz_[256], lc_[256], rc_[256];
+  __shared__ uint8_t exposed[257];
+  int s = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  SelState S_ = st[s];
+  if (S_.all) {
+    spent[s] = spent_floor[s] + S_.above;
+    return;
+  }
+  int64_t k = S_.budget - S_.above;
+  spent[s] = spent_floor[s] + S_.budget;
+  if (k <= 0) return;
+  const uint64_t T = S_.prefix;
+  const int64_t bop = (int64_t)key_id(T);
+  const TreeArgs& ta = a.ta;
+  int64_t lh = bop / (2 * ta.T);
+  int64_t x = bop % (2 * ta.T);
+  int t = (int)(x / 2 - ta.cu[s]);
+  int t0, nn;
+  slot_of(ta, s, t, t0, nn);
+  const int64_t sbase = lh * 2 * ta.T + 2 * (ta.cu[s] + t0);
+  // pre-order node table of the slot: pop a frame, number it, push right then left
+  struct Fr { int sz, parent, side; };
+  Fr fr[20];
+  int ftop = 0, m = 0;
+  fr[ftop++] = {nn, -1, 0};
+  while (ftop > 0) {
+    Fr q = fr[--ftop];
+    int j = m++;
+    sz_[j] = q.sz;
+    lc_[j] = -1;
+    rc_[j] = -1;
+    if (q.parent >= 0) {
+      if (q.side == 0) lc_[q.parent] = j;
+      else rc_[q.parent] = j;
+    }
+    if (q.sz > 1) {
+      int nl = (q.sz + 1) >> 1;
+      fr[ftop++] = {q.sz - nl, j, 1};
+      fr[ftop++] = {nl, j, 0};
+    }
+  }
+  // exposed[0] = Add, exposed[1+j] = Split(node j)
+  for (int q = 0; q <= m; ++q) exposed[q] = 0;
+  exposed[bop - sbase] = 1;
+  while (k > 0) {
+    int best = -1;
+    uint64_t bk = 0;
+    for (int q = 0; q <= m; ++q) {
+      if (!exposed[q]) continue;
+      uint64_t kk = op_key(a, sbase + q);
+      if (best < 0 || kk > bk) {
+        best = q;
+        bk = kk;
+      }
+    }
+    if (best < 0) break;
+    exposed[best] = 0;
+    a.taken[sbase + best] = 2;
+    --k;
+    int kids[2], nk = 0;
+    if (best == 0) {
+      if (sz_[0] > 1) kids[nk++] = 1;
+    } else {
+      int j = best - 1;
+      if (lc_[j] >= 0 && sz_[lc_[j]] > 1) kids[nk++] = 1 + lc_[j];
+      if (rc_[j] >= 0 && sz_[rc_[j]] > 1) kids[nk++] = 1 + rc_[j];
+    }
+    for (int q = 0; q < nk; ++q) {
+      int64_t o = sbase + kids[q];
+      if (a.cost[o] != 0 && a.taken[o] == 0 && a.beta[o] == T) exposed[kids[q]] = 1;
+    }
+  }
+}
+
+__global__ void taken_normalize_kernel(uint8_t* taken, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n && taken[i]) taken[i] = 1;
+}
+
+// ------------------------------------------------------------------ host helpers
+void fill_ranges(Ranges& r, const kvc_shape* sh, const kvc_params* p, int per_token, bool ops) {
+  r.S = sh->n_seq;
+  r.U = sh->n_layers * sh->n_kv_heads;
+  int mul = ops ? 2 : 1;
+  r.unit_stride = mul * sh->total_tokens;
+  for (int s = 0; s < sh->n_seq; ++s) {
+    int64_t L = sh->cu_seqlens[s + 1] - sh->cu_seqlens[s];
+    kvc::Regions g = kvc::regions_of(L, *p);
+    r.start[s] = mul * (sh->cu_seqlens[s] + g.c0);
+    r.len[s] = mul * (g.c1 - g.c0);
+    r.nchunk[s] = (r.len[s] + CH - 1) / CH;
+  }
+  (void)per_token;
+}
+
+}  // namespace
+
+namespace kvc {
+size_t ws_auction(const kvc_shape* s, const kvc_params* p) {
+  int64_t E = (int64_t)s->n_layers * s->n_kv_heads * s->total_tokens;
+  std::vector<int64_t> B(s->n_seq), A(s->n_seq), F(s->n_seq);
+  kvc_budgets(s, p, B.data(), A.data(), F.data());
+  int64_t Fmax = 1;
+  for (int i = 0; i < s->n_seq; ++i) Fmax = F[i] > Fmax ? F[i] : Fmax;
+  Carver c(nullptr, 0);
+  c.take<SelState>(MAXS);
+  c.take<unsigned long long>((size_t)MAXS * 256);
+  c.take<int64_t>(MAXS * 2);
+  if (!p->token_mode) {
+    c.take<uint64_t>((size_t)E * 2);       // cover / beta
+    c.take<uint64_t>((size_t)s->n_seq * Fmax);
+    c.take<int32_t>((size_t)s->n_seq * Fmax);
+    c.take<int32_t>((size_t)s->n_seq * Fmax);
+    c.take<int32_t>(MAXS);
+  }
+  return c.off + 256;
+}
+}  // namespace kvc
+
+extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_trees* trees, const float* rel,
+                           const float* head_sens, const int32_t* slot_start, const int32_t* n_slots,
+                           uint8_t* op_taken, int64_t* spent, int64_t* spent_floor, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  if ((r = kvc::validate_params(sh, p))) return r;
+  KVC_REQUIRE(sh->n_seq <= MAXS, KVC_E_SHAPE, "kvc_auction: at most 64 sequences per call");
+  KVC_REQUIRE(op_taken && spent, KVC_E_INVAL, "kvc_auction: NULL output");
+  KVC_REQUIRE(ws && ws_bytes >= kvc::ws_auction(sh, p), KVC_E_WORKSPACE, "kvc_auction: workspace too small");
+  std::vector<int64_t> B(sh->n_seq), A(sh->n_seq), F(sh->n_seq);
+  if ((r = kvc_budgets(sh, p, B.data(), A.data(), F.data()))) return r;
+  int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
+  kvc::Carver c(ws, ws_bytes);
+  SelState* st = c.take<SelState>(MAXS);
+  unsigned long long* hist = c.take<unsigned long long>((size_t)MAXS * 256);
+  int64_t* dev_i64 = c.take<int64_t>(MAXS * 2);
+  int64_t* sfloor = spent_floor ? spent_floor : dev_i64;
+  Ranges budget_r{};  // carries host budgets through kernel arguments
+  budget_r.S = sh->n_seq;
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(kvc_blocks(MAXS * 256, 256)), dim3(256), 0, stream, hist,
+                     (int64_t)MAXS * 256);
+  KVC_LAUNCH_CHECK("zero_hist");
+
+  if (p->token_mode) {
+    KVC_REQUIRE(rel, KVC_E_INVAL, "kvc_auction: token mode needs rel");
+    hipLaunchKernelGGL(zero_u8_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, stream, op_taken, E);
+    KVC_LAUNCH_CHECK("zero_taken");
+    Ranges rg{};
+    fill_ranges(rg, sh, p, 1, false);
+    for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = A[s];
+    hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
+                       budget_r, 0, (const int64_t*)nullptr);
+    KVC_LAUNCH_CHECK("init_state");
+    TokSrc src{rel};
+    if ((r = run_select(rg, src, st, hist, stream))) return r;
+    int64_t nb = ranges_blocks(rg);
+    if (nb > 0) {
+      hipLaunchKernelGGL(mark_tokens_kernel, dim3((unsigned)nb), dim3(256), 0, stream, rg, src, st, op_taken, spent);
+      KVC_LAUNCH_CHECK("mark_tokens");
+    }
+    hipLaunchKernelGGL(token_spent_kernel, dim3(1), dim3(MAXS), 0, stream, st, rg, spent, spent_floor);
+    KVC_LAUNCH_CHECK("token_spent");
+    return KVC_OK;
+  }
+
+  KVC_REQUIRE(trees && trees->op_util && trees->op_cost && rel && head_sens && slot_start && n_slots, KVC_E_INVAL,
+              "kvc_auction: tree mode needs trees, rel, head_sens and slots");
+  int64_t Fmax = 1;
+  for (int s = 0; s < sh->n_seq; ++s) Fmax = F[s] > Fmax ? F[s] : Fmax;
+  uint64_t* cover = c.take<uint64_t>((size_t)E * 2);  // reused as beta by the auction
+  uint64_t* ckey = c.take<uint64_t>((size_t)sh->n_seq * Fmax);
+  int32_t* cid = c.take<int32_t>((size_t)sh->n_seq * Fmax);
+  int32_t* ccost = c.take<int32_t>((size_t)sh->n_seq * Fmax);
+  int32_t* ccount = c.take<int32_t>(MAXS);
+  int64_t E2 = 2 * E;
+  hipLaunchKernelGGL(zero_u8_kernel, dim3(kvc_blocks(E2, 256)), dim3(256), 0, stream, op_taken, E2);
+  KVC_LAUNCH_CHECK("zero_taken");
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(kvc_blocks(E2, 256)), dim3(256), 0, stream, (unsigned long long*)cover, E2);
+  KVC_LAUNCH_CHECK("zero_cover");
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(MAXS), 0, stream, (unsigned long long*)ccount, (int64_t)MAXS / 2);
+  KVC_LAUNCH_CHECK("zero_count");
+
+  TreeArgs ta{};
+  ta.cu = sh->cu_seqlens_d;
+  ta.slot_start = slot_start;
+  ta.n_slots = n_slots;
+  ta.stride = kvc_slot_stride(sh, p);
+  ta.S = sh->n_seq;
+  ta.Ly = sh->n_layers;
+  ta.H = sh->n_kv_heads;
+  ta.T = sh->total_tokens;
+
+  // ---- floor: top-F leaves
+  Ranges leaves{};
+  fill_ranges(leaves, sh, p, 1, false);
+  for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = F[s];
+  hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
+                     budget_r, 0, (const int64_t*)nullptr);
+  KVC_LAUNCH_CHECK("init_state");
+  LeafSrc lsrc{rel, head_sens, sh->total_tokens, sh->n_layers * sh->n_kv_heads};
+  if ((r = run_select(leaves, lsrc, st, hist, stream))) return r;
+  FloorArgs fa{};
+  fa.ta = ta;
+  fa.rel = rel;
+  fa.sens = head_sens;
+  fa.op_cost = trees->op_cost;
+  fa.taken = op_taken;
+  fa.cover = cover;
+  fa.ckey = ckey;
+  fa.cid = cid;
+  fa.ccost = ccost;
+  fa.ccount = ccount;
+  fa.Fmax = Fmax;
+  int64_t nb = ranges_blocks(leaves);
+  bool any_floor = false;
+  for (int s = 0; s < sh->n_seq; ++s) any_floor |= F[s] > 0;
+  if (nb > 0 && any_floor) {
+    // a sequence with F = 0 selects nothing: its budget is 0, so no key fits
+    hipLaunchKernelGGL(floor_collect_kernel, dim3((unsigned)nb), dim3(256), 0, stream, leaves, lsrc, st, fa);
+    KVC_LAUNCH_CHECK("floor_collect");
+  }
+  int64_t ncand = (int64_t)sh->n_seq * Fmax;
+  hipLaunchKernelGGL(floor_cover_kernel, dim3(kvc_blocks(ncand, 256)), dim3(256), 0, stream, fa, sh->n_seq);
+  KVC_LAUNCH_CHECK("floor_cover");
+  hipLaunchKernelGGL(floor_cost_kernel, dim3(kvc_blocks(ncand, 256)), dim3(256), 0, stream, fa, sh->n_seq);
+  KVC_LAUNCH_CHECK("floor_cost");
+  // weighted select over the candidates: first candidate that does not fit
+  Ranges cr{};
+  cr.S = sh->n_seq;
+  cr.U = 1;
+  cr.unit_stride = 0;
+  int64_t nleaf_unit = 0;
+  for (int s = 0; s < sh->n_seq; ++s) {
+    nleaf_unit = leaves.len[s] * leaves.U;
+    cr.start[s] = (int64_t)s * Fmax;
+    cr.len[s] = F[s] < nleaf_unit ? F[s] : nleaf_unit;
+    cr.nchunk[s] = (cr.len[s] + CH - 1) / CH;
+  }
+  hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
+                     budget_r, 0, (const int64_t*)nullptr);
+  KVC_LAUNCH_CHECK("init_state");
+  CandSrc csrc{ckey, ccost};
+  if ((r = run_select(cr, csrc, st, hist, stream))) return r;
+  hipLaunchKernelGGL(floor_accept_kernel, dim3(kvc_blocks(ncand, 256)), dim3(256), 0, stream, fa, sh->n_seq, st);
+  KVC_LAUNCH_CHECK("floor_accept");
+  hipLaunchKernelGGL(floor_tail_kernel, dim3(sh->n_seq), dim3(256), 0, stream, fa, st, budget_r, sfloor);
+  KVC_LAUNCH_CHECK("floor_tail");
+
+  // ---- auction over every untaken op
+  AucArgs aa{};
+  aa.ta = ta;
+  aa.util = trees->op_util;
+  aa.cost = trees->op_cost;
+  aa.taken = op_taken;
+  aa.beta = cover;
+  Ranges ops{};
+  fill_ranges(ops, sh, p, 0, true);
+  int64_t nbo = ranges_blocks(ops);
+  if (nbo > 0) {
+    hipLaunchKernelGGL(beta_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops);
+    KVC_LAUNCH_CHECK("beta");
+  }
+  for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = A[s];
+  hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
+                     budget_r, 0, (const int64_t*)sfloor);
+  KVC_LAUNCH_CHECK("init_state");
+  OpSrc osrc{cover, trees->op_cost, op_taken};
+  if ((r = run_select(ops, osrc, st, hist, stream))) return r;
+  if (nbo > 0) {
+    hipLaunchKernelGGL(auction_mark_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops, st);
+    KVC_LAUNCH_CHECK("auction_mark");
+  }
+  hipLaunchKernelGGL(auction_fixup_kernel, dim3(sh->n_seq), dim3(64), 0, stream, aa, st, (const int64_t*)sfloor,
+                     spent);
+  KVC_LAUNCH_CHECK("auction_fixup");
+  hipLaunchKernelGGL(taken_normalize_kernel, dim3(kvc_blocks(E2, 256)), dim3(256), 0, stream, op_taken, E2);
+  KVC_LAUNCH_CHECK("taken_normalize");
+  return KVC_OK;
+}

@@ -1,0 +1,380 @@
+"""Python binding of libkvc (ctypes).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels. PyTorch provides device memory and the current HIP stream. Importing
+this module loads libkvc.so from the package directory and raises if it is
+missing; there is no fallback implementation.
+
+Function names follow the C ABI (include/kvc.h): score, propagate, partition,
+build_trees, auction, pack, full_view, decode_attn, kl, rope_table.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libkvc.so not found at {LIB_PATH}: run eviction_probe_softmax_amd.build_lib "
+                      "(or __graft_entry__.build()) first")
+_lib = C.CDLL(LIB_PATH)
+
+KVC_F32, KVC_BF16 = 0, 1
+STAGE_SCORE, STAGE_PROPAGATE, STAGE_PARTITION, STAGE_TREES, STAGE_AUCTION, STAGE_PACK = range(6)
+
+EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets", "kvc_pack_capacity",
+           "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
+           "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_pack", "kvc_full_view",
+           "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl"]
+
+
+class Shape(C.Structure):
+    _fields_ = [("n_seq", C.c_int32), ("n_layers", C.c_int32), ("n_kv_heads", C.c_int32),
+                ("group", C.c_int32), ("head_dim", C.c_int32), ("dtype", C.c_int32),
+                ("total_tokens", C.c_int64), ("cu_seqlens", C.POINTER(C.c_int64)),
+                ("cu_seqlens_d", C.c_void_p)]
+
+
+class Params(C.Structure):
+    _fields_ = [("budget_ratio", C.c_float), ("budget_min", C.c_int32), ("prompt_exact", C.c_int32),
+                ("recent_exact", C.c_int32), ("suffix_exact", C.c_int32), ("n_probe", C.c_int32),
+                ("n_hops", C.c_int32), ("n_seeds", C.c_int32), ("hop_weight", C.c_float),
+                ("n_dprobe", C.c_int32), ("w_attn", C.c_float), ("w_value", C.c_float),
+                ("value_base", C.c_float), ("floor_frac", C.c_float), ("token_mode", C.c_int32),
+                ("slot_len", C.c_int32), ("slot_min", C.c_int32), ("slot_max", C.c_int32),
+                ("slot_target", C.c_int32), ("lambda_len", C.c_float), ("lambda_curv", C.c_float),
+                ("rope_base", C.c_float)]
+
+
+class Trees(C.Structure):
+    _fields_ = [("node_rel", C.c_void_p), ("node_D", C.c_void_p), ("node_mu", C.c_void_p),
+                ("op_util", C.c_void_p), ("op_cost", C.c_void_p)]
+
+
+class Ragged(C.Structure):
+    _fields_ = [("K", C.c_void_p), ("V", C.c_void_p), ("lnmu", C.c_void_p), ("pos", C.c_void_p),
+                ("seg_off", C.c_void_p), ("seg_len", C.c_void_p), ("n_seq", C.c_int32),
+                ("n_layers", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("dtype", C.c_int32), ("max_seg", C.c_int32), ("capacity", C.c_int64)]
+
+
+_P = C.c_void_p
+_sig = {
+    "kvc_strerror": (C.c_char_p, [C.c_int]),
+    "kvc_last_error": (C.c_char_p, []),
+    "kvc_params_default": (None, [C.POINTER(Params)]),
+    "kvc_budgets": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P]),
+    "kvc_pack_capacity": (C.c_int64, [C.POINTER(Shape), C.POINTER(Params)]),
+    "kvc_slot_stride": (C.c_int32, [C.POINTER(Shape), C.POINTER(Params)]),
+    "kvc_workspace_size": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params), C.c_int32]),
+    "kvc_rope_table": (C.c_int, [C.c_float, C.c_int32, C.c_int32, _P, _P, _P]),
+    "kvc_score": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                            C.c_size_t, _P]),
+    "kvc_propagate": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "kvc_partition": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, C.c_int32, C.c_int32, _P, _P, _P,
+                                _P, _P, C.c_size_t, _P]),
+    "kvc_build_trees": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P, C.POINTER(Trees), _P, C.c_size_t, _P]),
+    "kvc_auction": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.POINTER(Trees), _P, _P, _P, _P, _P,
+                              _P, _P, _P, C.c_size_t, _P]),
+    "kvc_pack": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Trees), _P, _P, _P,
+                           _P, _P, C.POINTER(Ragged), _P, C.c_size_t, _P]),
+    "kvc_full_view": (C.c_int, [C.POINTER(Shape), _P, _P, _P]),
+    "kvc_decode_workspace": (C.c_size_t, [C.POINTER(Ragged), C.c_int32, C.c_int32]),
+    "kvc_decode_attn": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
+                                  C.c_int64, _P, _P, C.c_size_t, _P]),
+    "kvc_kl_workspace": (C.c_size_t, [C.c_int64, C.c_int32, C.c_int32, C.c_int32]),
+    "kvc_kl": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib.kvc_last_error().decode()
+        super().__init__(f"{fn} failed: {_lib.kvc_strerror(status).decode()} ({status}): {msg}")
+        self.status = status
+
+
+def _check(fn, st):
+    if st != 0:
+        raise KvcError(fn, st)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors passed to libkvc must be contiguous"
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+_DT = {torch.bfloat16: KVC_BF16, torch.float32: KVC_F32}
+
+
+@dataclass
+class Problem:
+    """Shape + parameters of one compression call, with device offsets."""
+    shape: Shape
+    params: Params
+    cu_host: object
+    cu_dev: torch.Tensor
+    device: torch.device
+
+    @property
+    def S(self):
+        return self.shape.n_seq
+
+    @property
+    def Ly(self):
+        return self.shape.n_layers
+
+    @property
+    def H(self):
+        return self.shape.n_kv_heads
+
+    @property
+    def T(self):
+        return self.shape.total_tokens
+
+    def budgets(self):
+        S = self.S
+        B = (C.c_int64 * S)()
+        A = (C.c_int64 * S)()
+        F = (C.c_int64 * S)()
+        st = _lib.kvc_budgets(C.byref(self.shape), C.byref(self.params), B, A, F)
+        _check("kvc_budgets", st)
+        return list(B), list(A), list(F)
+
+    def pack_capacity(self):
+        return int(_lib.kvc_pack_capacity(C.byref(self.shape), C.byref(self.params)))
+
+    def slot_stride(self):
+        return int(_lib.kvc_slot_stride(C.byref(self.shape), C.byref(self.params)))
+
+    def ws(self, stage):
+        n = int(_lib.kvc_workspace_size(C.byref(self.shape), C.byref(self.params), stage))
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+
+
+def make_problem(cfg, cu_seqlens: torch.Tensor, dtype: torch.dtype, device="cuda") -> Problem:
+    """cfg: any object with the workload fields (workload.Config works)."""
+    dev = torch.device(device)
+    cu = cu_seqlens.to(torch.int64).cpu().contiguous()
+    cu_host = (C.c_int64 * len(cu))(*cu.tolist())
+    cu_dev = cu.to(dev)
+    sh = Shape(n_seq=len(cu) - 1, n_layers=cfg.Ly, n_kv_heads=cfg.H, group=cfg.G, head_dim=cfg.d,
+               dtype=_DT[dtype], total_tokens=int(cu[-1]), cu_seqlens=C.cast(cu_host, C.POINTER(C.c_int64)),
+               cu_seqlens_d=C.c_void_p(cu_dev.data_ptr()))
+    p = Params()
+    _lib.kvc_params_default(C.byref(p))
+    p.budget_ratio = cfg.budget_ratio
+    p.budget_min = cfg.budget_min
+    p.prompt_exact, p.recent_exact, p.suffix_exact = cfg.prompt_exact, cfg.recent_exact, cfg.suffix_exact
+    p.n_probe = cfg.P
+    p.n_hops, p.n_seeds, p.hop_weight = cfg.n_hops, cfg.n_seeds, cfg.hop_weight
+    p.n_dprobe, p.w_attn, p.w_value, p.value_base = cfg.n_dprobe, cfg.w_attn, cfg.w_value, cfg.value_base
+    p.floor_frac = cfg.floor_frac
+    p.token_mode = 1 if cfg.token_mode else 0
+    p.slot_len, p.slot_min, p.slot_max, p.slot_target = cfg.slot_len, cfg.slot_min, cfg.slot_max, cfg.slot_target
+    p.lambda_len, p.lambda_curv = cfg.lambda_len, cfg.lambda_curv
+    p.rope_base = cfg.rope_base
+    return Problem(sh, p, cu_host, cu_dev, dev)
+
+
+# ------------------------------------------------------------------ entry points
+def rope_table(base: float, head_dim: int, n_pos: int, device="cuda"):
+    cs = torch.empty((n_pos, head_dim // 2), dtype=torch.float32, device=device)
+    sn = torch.empty_like(cs)
+    _check("kvc_rope_table", _lib.kvc_rope_table(base, head_dim, n_pos, _ptr(cs), _ptr(sn), _stream()))
+    return cs, sn
+
+
+def score(pb: Problem, K, V, Qp, feats=True):
+    dev = pb.device
+    E = pb.Ly * pb.H * pb.T
+    R = pb.shape.group * pb.params.n_probe
+    rel0 = torch.empty((pb.Ly, pb.H, pb.T), dtype=torch.float32, device=dev)
+    ft = torch.empty((5, pb.Ly, pb.H, pb.T), dtype=torch.float32, device=dev) if feats else None
+    lse = torch.empty((pb.S, pb.Ly, pb.H * pb.shape.group, pb.params.n_probe), dtype=torch.float32, device=dev)
+    ent = torch.empty_like(lse)
+    sens = torch.empty((pb.S, pb.Ly, pb.H), dtype=torch.float32, device=dev)
+    ws = pb.ws(STAGE_SCORE)
+    st = _lib.kvc_score(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(V), _ptr(Qp), _ptr(rel0), _ptr(ft),
+                        _ptr(lse), _ptr(ent), _ptr(sens), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_score", st)
+    del E, R
+    return {"r0": rel0, "feats": ft, "lse": lse, "ent": ent, "head_sens": sens}
+
+
+def propagate(pb: Problem, K, Qctx, rel0, want_seeds=True):
+    dev = pb.device
+    rel = torch.empty_like(rel0)
+    seeds = None
+    if want_seeds and pb.params.n_hops > 0:
+        seeds = torch.empty((pb.params.n_hops, pb.S, pb.Ly, pb.H, pb.params.n_seeds), dtype=torch.int32,
+                            device=dev)
+    ws = pb.ws(STAGE_PROPAGATE)
+    st = _lib.kvc_propagate(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(Qctx), _ptr(rel0), _ptr(rel),
+                            _ptr(seeds), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_propagate", st)
+    return {"rel": rel, "seeds": seeds}
+
+
+def partition(pb: Problem, hidden=None, hidden_dim=0, cost_q=None, cut_q=None, inject=False, export=False):
+    dev = pb.device
+    stride = pb.slot_stride()
+    slot_start = torch.empty((pb.S, stride + 1), dtype=torch.int32, device=dev)
+    n_slots = torch.empty((pb.S,), dtype=torch.int32, device=dev)
+    nmin, nmax = pb.params.slot_min, pb.params.slot_max
+    if export and cost_q is None:
+        cost_q = torch.zeros((pb.T, nmax - nmin + 1), dtype=torch.int64, device=dev)
+        cut_q = torch.zeros((pb.T,), dtype=torch.int64, device=dev)
+    ws = pb.ws(STAGE_PARTITION)
+    st = _lib.kvc_partition(C.byref(pb.shape), C.byref(pb.params), _ptr(hidden), hidden_dim, 1 if inject else 0,
+                            _ptr(cost_q), _ptr(cut_q), _ptr(slot_start), _ptr(n_slots), _ptr(ws), ws.numel(),
+                            _stream())
+    _check("kvc_partition", st)
+    return {"slot_start": slot_start, "n_slots": n_slots, "dp_cost_q": cost_q, "dp_cut_q": cut_q}
+
+
+def empty_trees(pb: Problem):
+    dev = pb.device
+    n = (pb.Ly, pb.H, 2 * pb.T)
+    return {"node_rel": torch.zeros(n, dtype=torch.float32, device=dev),
+            "node_D": torch.zeros(n, dtype=torch.float32, device=dev),
+            "node_mu": torch.zeros(n, dtype=torch.float32, device=dev),
+            "op_util": torch.zeros(n, dtype=torch.float32, device=dev),
+            "op_cost": torch.zeros(n, dtype=torch.uint8, device=dev)}
+
+
+def _trees_struct(tr):
+    if tr is None:
+        return None
+    return Trees(node_rel=_ptr(tr["node_rel"]), node_D=_ptr(tr["node_D"]), node_mu=_ptr(tr["node_mu"]),
+                 op_util=_ptr(tr["op_util"]), op_cost=_ptr(tr["op_cost"]))
+
+
+def build_trees(pb: Problem, K, V, Qp, lse, rel, head_sens, rope_cos, rope_sin, slot_start, n_slots, out=None):
+    tr = out if out is not None else empty_trees(pb)
+    ts = _trees_struct(tr)
+    ws = pb.ws(STAGE_TREES)
+    st = _lib.kvc_build_trees(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(V), _ptr(Qp), _ptr(lse),
+                              _ptr(rel), _ptr(head_sens), _ptr(rope_cos), _ptr(rope_sin), _ptr(slot_start),
+                              _ptr(n_slots), C.byref(ts), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_build_trees", st)
+    return tr
+
+
+def auction(pb: Problem, trees=None, rel=None, head_sens=None, slot_start=None, n_slots=None):
+    dev = pb.device
+    if pb.params.token_mode:
+        taken = torch.empty((pb.Ly, pb.H, pb.T), dtype=torch.uint8, device=dev)
+    else:
+        taken = torch.empty((pb.Ly, pb.H, 2 * pb.T), dtype=torch.uint8, device=dev)
+    spent = torch.empty((pb.S,), dtype=torch.int64, device=dev)
+    spent_floor = torch.empty((pb.S,), dtype=torch.int64, device=dev)
+    ts = _trees_struct(trees)
+    ws = pb.ws(STAGE_AUCTION)
+    st = _lib.kvc_auction(C.byref(pb.shape), C.byref(pb.params), C.byref(ts) if ts is not None else None,
+                          _ptr(rel), _ptr(head_sens), _ptr(slot_start), _ptr(n_slots), _ptr(taken), _ptr(spent),
+                          _ptr(spent_floor), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_auction", st)
+    return {"taken": taken, "spent": spent, "spent_floor": spent_floor}
+
+
+def _ragged_struct(c):
+    return Ragged(K=_ptr(c["K"]), V=_ptr(c["V"]), lnmu=_ptr(c.get("lnmu")), pos=_ptr(c.get("pos")),
+                  seg_off=_ptr(c["seg_off"]), seg_len=_ptr(c["seg_len"]), n_seq=c["n_seq"],
+                  n_layers=c["n_layers"], n_kv_heads=c["n_kv_heads"], head_dim=c["head_dim"],
+                  dtype=_DT[c["K"].dtype], max_seg=c["max_seg"], capacity=c["K"].shape[0])
+
+
+def pack(pb: Problem, K, V, rel, trees, taken, slot_start, n_slots, rope_cos, rope_sin, capacity=None):
+    dev = pb.device
+    cap = pb.pack_capacity() if capacity is None else capacity
+    d = pb.shape.head_dim
+    L = [pb.cu_host[i + 1] - pb.cu_host[i] for i in range(pb.S)]
+    c = {"K": torch.empty((max(cap, 1), d), dtype=K.dtype, device=dev),
+         "V": torch.empty((max(cap, 1), d), dtype=K.dtype, device=dev),
+         "lnmu": torch.empty((max(cap, 1),), dtype=torch.float32, device=dev),
+         "pos": torch.empty((max(cap, 1),), dtype=torch.int32, device=dev),
+         "seg_off": torch.empty((pb.S, pb.Ly, pb.H), dtype=torch.int64, device=dev),
+         "seg_len": torch.empty((pb.S, pb.Ly, pb.H), dtype=torch.int32, device=dev),
+         "n_seq": pb.S, "n_layers": pb.Ly, "n_kv_heads": pb.H, "head_dim": d, "max_seg": int(max(L))}
+    rs = _ragged_struct(c)
+    rs.capacity = cap
+    ts = _trees_struct(trees)
+    ws = pb.ws(STAGE_PACK)
+    st = _lib.kvc_pack(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(V), _ptr(rel),
+                       C.byref(ts) if ts is not None else None, _ptr(taken), _ptr(slot_start), _ptr(n_slots),
+                       _ptr(rope_cos), _ptr(rope_sin), C.byref(rs), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_pack", st)
+    return c
+
+
+def full_view(pb: Problem, K, V):
+    dev = pb.device
+    seg_off = torch.empty((pb.S, pb.Ly, pb.H), dtype=torch.int64, device=dev)
+    seg_len = torch.empty((pb.S, pb.Ly, pb.H), dtype=torch.int32, device=dev)
+    _check("kvc_full_view", _lib.kvc_full_view(C.byref(pb.shape), _ptr(seg_off), _ptr(seg_len), _stream()))
+    L = [pb.cu_host[i + 1] - pb.cu_host[i] for i in range(pb.S)]
+    d = pb.shape.head_dim
+    return {"K": K.reshape(-1, d), "V": V.reshape(-1, d), "lnmu": None, "pos": None, "seg_off": seg_off,
+            "seg_len": seg_len, "n_seq": pb.S, "n_layers": pb.Ly, "n_kv_heads": pb.H, "head_dim": d,
+            "max_seg": int(max(L))}
+
+
+class Decoder:
+    """Holds the marshalled cache description and a reusable workspace for
+    repeated decode steps over one cache."""
+
+    def __init__(self, cache, group: int, t_cap: int):
+        self.cache = cache
+        self.rs = _ragged_struct(cache)
+        self.group = group
+        self.t_cap = t_cap
+        n = int(_lib.kvc_decode_workspace(C.byref(self.rs), group, t_cap))
+        self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=cache["K"].device)
+
+    def step(self, K_tail, V_tail, t_valid, Q, x_out, x_stride, o_out=None):
+        st = _lib.kvc_decode_attn(C.byref(self.rs), _ptr(K_tail), _ptr(V_tail), t_valid, self.t_cap, _ptr(Q),
+                                  self.group, _ptr(x_out), x_stride, _ptr(o_out), _ptr(self.ws), self.ws.numel(),
+                                  _stream())
+        _check("kvc_decode_attn", st)
+
+
+def decode_attn(cache, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, o_out=None):
+    Decoder(cache, group, t_cap).step(K_tail, V_tail, t_valid, Q, x_out, x_stride, o_out)
+
+
+class KL:
+    def __init__(self, n_pairs, d_model, vocab, w_dtype, device="cuda"):
+        self.n_pairs, self.d_model, self.vocab, self.w_dtype = n_pairs, d_model, vocab, _DT[w_dtype]
+        n = int(_lib.kvc_kl_workspace(n_pairs, d_model, vocab, self.w_dtype))
+        self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+    def __call__(self, x_full, x_comp, W, out=None):
+        out = torch.empty((self.n_pairs,), dtype=torch.float32, device=x_full.device) if out is None else out
+        st = _lib.kvc_kl(self.n_pairs, self.d_model, self.vocab, _ptr(x_full), _ptr(x_comp), _ptr(W), self.w_dtype,
+                         _ptr(out), _ptr(self.ws), self.ws.numel(), _stream())
+        _check("kvc_kl", st)
+        return out
+
+
+def kl(x_full, x_comp, W):
+    n, dm = x_full.shape
+    return KL(n, dm, W.shape[0], W.dtype, device=x_full.device)(x_full, x_comp, W)

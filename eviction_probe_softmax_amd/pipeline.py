@@ -1,0 +1,93 @@
+"""The whole path as a sequence of libkvc calls on one stream.
+
+Orchestration only: every step below is a C-ABI call into the HIP library;
+this module allocates outputs (via the binding) and passes tensors along.
+Order follows the GraceKV page ('Method': partition -> represent -> value ->
+allocate -> pack) and the DistillCache paper (decode over the pruned cache,
+per-step KL against the full cache).
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import kvc
+
+
+class Compressor:
+    """Holds the problem description, RoPE tables and reusable buffers for
+    repeated compression of inputs with one shape."""
+
+    def __init__(self, cfg, cu_seqlens: torch.Tensor, dtype: torch.dtype, device="cuda"):
+        self.cfg = cfg
+        self.pb = kvc.make_problem(cfg, cu_seqlens, dtype, device)
+        self.device = torch.device(device)
+        lens = [int(cu_seqlens[i + 1] - cu_seqlens[i]) for i in range(len(cu_seqlens) - 1)]
+        self.max_len = max(lens)
+        self.rope_cos = self.rope_sin = None
+        if not cfg.token_mode:
+            self.rope_cos, self.rope_sin = kvc.rope_table(cfg.rope_base, cfg.d, self.max_len, device=device)
+
+    def compress(self, inp: Dict[str, torch.Tensor], stop_after: Optional[str] = None) -> Dict[str, object]:
+        pb, cfg = self.pb, self.cfg
+        out: Dict[str, object] = {}
+        sc = kvc.score(pb, inp["K"], inp["V"], inp["Qp"])
+        out.update(sc)
+        pr = kvc.propagate(pb, inp["K"], inp["Qctx"], sc["r0"])
+        out.update(pr)
+        rel = pr["rel"]
+        if stop_after == "propagate":
+            return out
+        if cfg.token_mode:
+            au = kvc.auction(pb, rel=rel)
+            out.update(au)
+            out["cache"] = kvc.pack(pb, inp["K"], inp["V"], rel, None, au["taken"], None, None, None, None)
+            return out
+        if cfg.slot_len > 0:
+            part = kvc.partition(pb)
+        else:
+            part = kvc.partition(pb, inp["hidden"], cfg.hidden_dim)
+        out.update(part)
+        tr = kvc.build_trees(pb, inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"], self.rope_cos,
+                             self.rope_sin, part["slot_start"], part["n_slots"])
+        out["trees"] = tr
+        au = kvc.auction(pb, tr, rel, sc["head_sens"], part["slot_start"], part["n_slots"])
+        out.update(au)
+        out["cache"] = kvc.pack(pb, inp["K"], inp["V"], rel, tr, au["taken"], part["slot_start"],
+                                part["n_slots"], self.rope_cos, self.rope_sin)
+        return out
+
+
+def decode_both(comp_cache, full_cache, inp, cfg, x_full=None, x_comp=None):
+    """All decode steps over both caches. Returns x_full, x_comp
+    [S][T_dec][d_model] fp32."""
+    S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
+    dev = inp["K"].device
+    x_full = torch.empty((S, Td, Dm), dtype=torch.float32, device=dev) if x_full is None else x_full
+    x_comp = torch.empty((S, Td, Dm), dtype=torch.float32, device=dev) if x_comp is None else x_comp
+    df = kvc.Decoder(full_cache, cfg.G, Td)
+    dc = kvc.Decoder(comp_cache, cfg.G, Td)
+    for t in range(Td):
+        q = inp["Qd"][t]
+        # row (s, t) lives at x[s, t]: base pointer of x[0, t], stride T_dec * d_model
+        df.step(inp["Kd"], inp["Vd"], t + 1, q, _row_view(x_full, t), Td * Dm)
+        dc.step(inp["Kd"], inp["Vd"], t + 1, q, _row_view(x_comp, t), Td * Dm)
+    return x_full, x_comp
+
+
+class _RowView:
+    """A strided output target: data_ptr of x[0, t] with the caller's stride."""
+
+    def __init__(self, x, t):
+        self._ptr = x[0, t].data_ptr()
+
+    def is_contiguous(self):
+        return True
+
+    def data_ptr(self):
+        return self._ptr
+
+
+def _row_view(x, t):
+    return _RowView(x, t)

@@ -63,7 +63,7 @@ def budgets(lens: List[int], cfg) -> List[dict]:
     """
     out = []
     for L in lens:
-        B = max(int(math.floor(float(np.float32(cfg.budget_ratio)) * L * cfg.Ly * cfg.H)),
+        B = max(int(math.floor(float(np.float32(cfg.budget_ratio)) * (L * cfg.Ly * cfg.H))),
                 cfg.budget_min)
         pe, cs, ce, ss = regions(L, cfg)
         recent = (ss - ce) * cfg.Ly * cfg.H

@@ -1,0 +1,112 @@
+"""GPU parity: decode attention over ragged caches (kvc_decode_attn) and the
+vocab KL (kvc_kl) against the CPU oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workload import small_config, make_inputs
+from parity import close, as_np, to_dev, inputs_to
+
+pytestmark = pytest.mark.gpu
+
+# decode outputs are sums of attention outputs that can sit near zero; the
+# relative bar applies above 1e-3 of the tensor's largest magnitude
+DEC_RTOL, DEC_FLOOR = 2e-2, 1e-3
+
+
+def _kvc():
+    from eviction_probe_softmax_amd import kvc
+    return kvc
+
+
+def _run_decode(kvc, cache_dev, inp_dev, cfg, S):
+    Td = cfg.T_dec
+    d_model = cfg.d_model
+    x = torch.zeros((S, Td, d_model), dtype=torch.float32, device="cuda")
+    dec = kvc.Decoder(cache_dev, cfg.G, Td)
+    row = torch.zeros((S, d_model), dtype=torch.float32, device="cuda")
+    for t in range(Td):
+        dec.step(inp_dev["Kd"], inp_dev["Vd"], t + 1, inp_dev["Qd"][t].contiguous(), row, d_model)
+        x[:, t] = row
+    torch.cuda.synchronize()
+    return x
+
+
+@pytest.mark.parametrize("name", ["tiny", "mistral1", "ragged", "stress"])
+def test_decode_full_cache(name):
+    kvc = _kvc()
+    cfg = small_config(name)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    print(f"[decode-full] {name} lens={cfg.lens} T_dec={cfg.T_dec}", flush=True)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    cache = kvc.full_view(pb, dinp["K"], dinp["V"])
+    x = _run_decode(kvc, cache, dinp, cfg, cfg.S)
+    cu = inp["cu_seqlens"].numpy()
+    want = oracle.decode_all(oracle.full_view(inp["K"], inp["V"], cu), inp["Kd"], inp["Vd"], inp["Qd"], cfg.G)
+    close(x, want, DEC_RTOL, "x_full", floor=DEC_FLOOR)
+    # the fp32 path is far tighter than the bar: keep an eye on it
+    err = np.abs(as_np(x) - want).max() / np.abs(want).max()
+    assert err < 1e-4, err
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged"])
+def test_decode_ragged_cache_with_multiplicity(name):
+    kvc = _kvc()
+    cfg = small_config(name)
+    inp = make_inputs(cfg)
+    rng = np.random.default_rng(5)
+    S, Ly, H, d = cfg.S, cfg.Ly, cfg.H, cfg.d
+    # a ragged cache of random entries (lengths 0..700, crossing split chunks)
+    lens = rng.integers(0, 700, (S, Ly, H))
+    lens[0, 0, 0] = 0
+    N = int(lens.sum())
+    dt = inp["K"].dtype
+    Kc = torch.randn((N, d)).to(dt)
+    Vc = torch.randn((N, d)).to(dt)
+    lnmu = torch.tensor(np.log(rng.uniform(1, 4, N)), dtype=torch.float32)
+    seg_off = np.zeros((S, Ly, H), np.int64)
+    off = 0
+    for l in range(Ly):
+        for h in range(H):
+            for s in range(S):
+                seg_off[s, l, h] = off
+                off += lens[s, l, h]
+    ocache = {"K": oracle.to64(Kc), "V": oracle.to64(Vc), "lnmu": lnmu.numpy(), "seg_off": seg_off,
+              "seg_len": lens.astype(np.int32)}
+    gcache = {"K": Kc.cuda(), "V": Vc.cuda(), "lnmu": lnmu.cuda(), "pos": None,
+              "seg_off": torch.from_numpy(seg_off).cuda(), "seg_len": torch.from_numpy(lens.astype(np.int32)).cuda(),
+              "n_seq": S, "n_layers": Ly, "n_kv_heads": H, "head_dim": d, "max_seg": int(lens.max())}
+    dinp = inputs_to(inp)
+    x = _run_decode(kvc, gcache, dinp, cfg, S)
+    want = oracle.decode_all(ocache, inp["Kd"], inp["Vd"], inp["Qd"], cfg.G)
+    close(x, want, DEC_RTOL, "x_ragged", floor=DEC_FLOOR)
+    # per-layer outputs through o_out
+    o = torch.zeros((S, Ly, H * cfg.G, d), dtype=torch.float32, device="cuda")
+    xx = torch.zeros((S, cfg.d_model), dtype=torch.float32, device="cuda")
+    kvc.decode_attn(gcache, dinp["Kd"], dinp["Vd"], 1, cfg.T_dec, dinp["Qd"][0].contiguous(), cfg.G, xx,
+                    cfg.d_model, o)
+    _, oo = oracle.decode_step(ocache, inp["Kd"], inp["Vd"], inp["Qd"][0], 0, cfg.G)
+    close(o, oo, DEC_RTOL, "o_layers", floor=DEC_FLOOR)
+
+
+@pytest.mark.parametrize("w_dtype,dm,vocab", [("f32", 256, 2048), ("bf16", 1024, 1000), ("bf16", 4096, 32768)])
+def test_kl_matches_oracle(w_dtype, dm, vocab):
+    kvc = _kvc()
+    g = torch.Generator().manual_seed(3)
+    n = 37
+    xf = torch.randn((n, dm), generator=g)
+    xc = xf + 0.5 * torch.randn((n, dm), generator=g)
+    W = (torch.randn((vocab, dm), generator=g) * (4.0 / math.sqrt(dm))).to(
+        torch.bfloat16 if w_dtype == "bf16" else torch.float32)
+    print(f"[kl] {w_dtype} dm={dm} vocab={vocab}", flush=True)
+    got = kvc.kl(xf.cuda(), xc.cuda(), W.cuda())
+    torch.cuda.synchronize()
+    want = oracle.kl_rows(xf.numpy(), xc.numpy(), W, w_dtype)
+    err = np.abs(as_np(got) - want)
+    assert err.max() <= 1e-3, (err.max(), want[:4], as_np(got)[:4])
+    same = kvc.kl(xf.cuda(), xf.cuda(), W.cuda())
+    assert torch.all(same == 0), same

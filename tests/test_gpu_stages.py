@@ -1,0 +1,181 @@
+"""GPU stage parity: every integer stage is bit-exact when fed the oracle's
+inputs to that stage (top-B, floor + auction, DP cuts, pack indices, order and
+leaf copies); float stages (trees, prototypes, DP costs) within tolerance.
+All calls go through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import partition as opart
+from workload import small_config, make_inputs
+from parity import (close, as_np, to_dev, inputs_to, slots_to_dev, slots_from_dev, trees_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _kvc():
+    from eviction_probe_softmax_amd import kvc
+    return kvc
+
+
+def _oracle_front(cfg, inp):
+    cu = inp["cu_seqlens"].numpy()
+    sc = oracle.probe_scores(inp["K"], inp["V"], inp["Qp"], cu, cfg)
+    pr = oracle.propagate(inp["K"], inp["Qctx"], sc["r0"], cu, cfg)
+    return cu, sc, pr
+
+
+@pytest.mark.parametrize("name,kw", [("mistral1", {}), ("ragged", {"token_mode": True, "slot_len": 0}),
+                                     ("mistral1", {"budget_ratio": 0.9})])
+def test_token_topk_and_pack_bit_exact(name, kw):
+    kvc = _kvc()
+    cfg = small_config(name, **kw)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    print(f"[token] {name} {kw}", flush=True)
+    cu, sc, pr = _oracle_front(cfg, inp)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    rel = to_dev(pr["rel"])
+    g = kvc.auction(pb, rel=rel)
+    otaken, ospent = oracle.token_topk(pr["rel"], cu, cfg)
+    assert np.array_equal(as_np(g["taken"]), otaken)
+    assert np.array_equal(as_np(g["spent"]), ospent)
+    c = kvc.pack(pb, dinp["K"], dinp["V"], rel, None, g["taken"], None, None, None, None)
+    oc = oracle.pack(inp["K"], inp["V"], pr["rel"], None, otaken, cu, [[]] * cfg.S, cfg)
+    _compare_cache(c, oc, exact=True)
+
+
+def _compare_cache(c, oc, exact):
+    assert np.array_equal(as_np(c["seg_off"]), oc["seg_off"])
+    assert np.array_equal(as_np(c["seg_len"]), oc["seg_len"])
+    N = oc["K"].shape[0]
+    assert np.array_equal(as_np(c["pos"])[:N], oc["pos"])
+    gk, gv = as_np(c["K"])[:N].astype(np.float64), as_np(c["V"])[:N].astype(np.float64)
+    lm = as_np(c["lnmu"])[:N]
+    if exact:
+        assert np.array_equal(gk, oc["K"]) and np.array_equal(gv, oc["V"])
+        assert np.all(lm == 0)
+        return
+    leaf = oc["lnmu"] == 0
+    # token leaves are bit copies of the cache
+    assert np.array_equal(gk[leaf], oc["K"][leaf]) and np.array_equal(gv[leaf], oc["V"][leaf])
+    close(gk, oc["K"], 2e-2, "packed K", floor=1e-2)
+    close(gv, oc["V"], 2e-2, "packed V", floor=1e-2)
+    close(lm, oc["lnmu"], 1e-3, "ln mu", floor=1e-3)
+
+
+@pytest.mark.parametrize("name", ["tiny", "stress", "ragged", "fulldepth"])
+def test_trees_match_oracle(name):
+    kvc = _kvc()
+    cfg = small_config(name)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    print(f"[trees] {name}", flush=True)
+    cu, sc, pr = _oracle_front(cfg, inp)
+    cq = kq = None
+    if cfg.slot_len == 0:
+        cq, kq = opart.slot_costs(inp["hidden"], cu, cfg)
+    slots = oracle.slots_for(cu, cfg, cq, kq)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    ss, ns = slots_to_dev(slots, pb.slot_stride())
+    rc, rs = kvc.rope_table(cfg.rope_base, cfg.d, max(cfg.lens))
+    g = kvc.build_trees(pb, dinp["K"], dinp["V"], dinp["Qp"], to_dev(sc["lse"]), to_dev(pr["rel"]),
+                        to_dev(sc["head_sens"]), rc, rs, ss, ns)
+    torch.cuda.synchronize()
+    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
+    assert np.array_equal(as_np(g["op_cost"]), o["op_cost"])
+    close(g["node_rel"], o["node_rel"], 1e-5, "node_rel")
+    close(g["node_mu"], o["node_mu"], 1e-4, "node_mu")
+    close(g["node_D"], o["node_D"], 1e-3, "node_D", floor=1e-3)
+    close(g["op_util"], o["op_util"], 1e-3, "op_util", floor=1e-3)
+    # P4 on the GPU output: parents are the exact fp32 sums of their children
+    nr = as_np(g["node_rel"])
+    for s, lst in enumerate(slots):
+        for (a, n) in lst[:3]:
+            nodes = oracle.tree_nodes(0, n)
+            base = 2 * (int(cu[s]) + a)
+            for j, (_, _, lc, rc_) in enumerate(nodes):
+                if lc >= 0:
+                    assert nr[0, 0, base + j] == np.float32(nr[0, 0, base + lc] + nr[0, 0, base + rc_])
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("fulldepth", {}),
+                                     ("stress", {"budget_ratio": 1.0 / 128, "floor_frac": 0.3}),
+                                     ("ragged", {"floor_frac": 0.5})])
+def test_floor_and_auction_bit_exact(name, kw):
+    kvc = _kvc()
+    cfg = small_config(name, **kw)
+    inp = make_inputs(cfg)
+    print(f"[auction] {name} {kw}", flush=True)
+    cu, sc, pr = _oracle_front(cfg, inp)
+    cq = kq = None
+    if cfg.slot_len == 0:
+        cq, kq = opart.slot_costs(inp["hidden"], cu, cfg)
+    slots = oracle.slots_for(cu, cfg, cq, kq)
+    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
+    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg)
+    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    ss, ns = slots_to_dev(slots, pb.slot_stride())
+    g = kvc.auction(pb, trees_to_dev(o), to_dev(pr["rel"]), to_dev(sc["head_sens"]), ss, ns)
+    torch.cuda.synchronize()
+    assert np.array_equal(as_np(g["spent_floor"]), fs), (as_np(g["spent_floor"]), fs)
+    assert np.array_equal(as_np(g["spent"]), spent), (as_np(g["spent"]), spent)
+    gt = as_np(g["taken"])
+    assert np.array_equal(gt, taken), f"{int((gt != taken).sum())} ops differ"
+
+
+@pytest.mark.parametrize("name", ["tiny", "stress", "ragged"])
+def test_pack_tree_mode(name):
+    kvc = _kvc()
+    cfg = small_config(name)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    print(f"[pack] {name}", flush=True)
+    cu, sc, pr = _oracle_front(cfg, inp)
+    slots = oracle.slots_for(cu, cfg)
+    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
+    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg)
+    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    ss, ns = slots_to_dev(slots, pb.slot_stride())
+    rc, rs = kvc.rope_table(cfg.rope_base, cfg.d, max(cfg.lens))
+    c = kvc.pack(pb, dinp["K"], dinp["V"], to_dev(pr["rel"]), trees_to_dev(o), to_dev(taken), ss, ns, rc, rs)
+    torch.cuda.synchronize()
+    oc = oracle.pack(inp["K"], inp["V"], pr["rel"], o, taken, cu, slots, cfg)
+    _compare_cache(c, oc, exact=False)
+
+
+@pytest.mark.parametrize("name,kw", [("fulldepth", {}), ("fulldepth", {"lens": [300, 21, 517], "S": 3}),
+                                     ("fulldepth", {"slot_min": 4, "slot_max": 12, "slot_target": 8})])
+def test_partition_dp(name, kw):
+    kvc = _kvc()
+    cfg = small_config(name, **kw)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    print(f"[partition] {name} {kw}", flush=True)
+    cu = inp["cu_seqlens"].numpy()
+    cq, kq = opart.slot_costs(inp["hidden"], cu, cfg)
+    slots = oracle.slots_for(cu, cfg, cq, kq)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    # DP fed the oracle's quantized costs: identical cuts
+    g = kvc.partition(pb, cost_q=to_dev(cq), cut_q=to_dev(kq), inject=True)
+    assert slots_from_dev(g["slot_start"], g["n_slots"]) == slots
+    # the GPU's own costs
+    g2 = kvc.partition(pb, dinp["hidden"], cfg.hidden_dim, export=True)
+    torch.cuda.synchronize()
+    gq = as_np(g2["dp_cost_q"]).astype(np.float64)
+    valid = cq != 0
+    err = np.abs(gq - cq)[valid]
+    assert err.max() <= 1e-4 * np.abs(cq[valid]).max() + 64, err.max()
+    gk = as_np(g2["dp_cut_q"]).astype(np.float64)
+    assert np.abs(gk - kq).max() <= 1e-4 * (1 << 22) + 64
+    # every region is covered by valid slots
+    for s, lst in enumerate(slots_from_dev(g2["slot_start"], g2["n_slots"])):
+        L = cfg.lens[s]
+        pe, c0, c1, _ = oracle.regions(L, cfg)
+        if c1 > c0:
+            assert lst[0][0] == c0 and lst[-1][0] + lst[-1][1] == c1
+            if c1 - c0 >= cfg.slot_min:
+                assert all(cfg.slot_min <= n <= cfg.slot_max for _, n in lst)
