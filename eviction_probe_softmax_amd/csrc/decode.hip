@@ -38,8 +38,9 @@ struct DecArgs {
 
 template <class T> struct Vec8;
 template <> struct Vec8<uint16_t> {
-  static __device__ __forceinline__ void load(const uint16_t* p, float* f) {
-    uint4 u = *(const uint4*)p;
+  typedef uint4 Raw;   // 8 bf16 in 4 registers
+  static __device__ __forceinline__ Raw raw(const uint16_t* p) { return *(const uint4*)p; }
+  static __device__ __forceinline__ void cvt(const Raw& u, float* f) {
     uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -47,24 +48,28 @@ template <> struct Vec8<uint16_t> {
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  static __device__ __forceinline__ void load(const uint16_t* p, float* f) { cvt(raw(p), f); }
 };
 template <> struct Vec8<float> {
-  static __device__ __forceinline__ void load(const float* p, float* f) {
-    float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  struct Raw { float4 a, b; };
+  static __device__ __forceinline__ Raw raw(const float* p) { return Raw{*(const float4*)p, *(const float4*)(p + 4)}; }
+  static __device__ __forceinline__ void cvt(const Raw& r, float* f) {
+    f[0] = r.a.x; f[1] = r.a.y; f[2] = r.a.z; f[3] = r.a.w;
+    f[4] = r.b.x; f[5] = r.b.y; f[6] = r.b.z; f[7] = r.b.w;
   }
+  static __device__ __forceinline__ void load(const float* p, float* f) { cvt(raw(p), f); }
 };
 
 // partial layout: [unit][chunk][G][D + 2] = o[D], max2, sum
-template <class T, int D>
+template <class T, int D, int G>
 __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, float* part) {
   constexpr int LPE = D / 8;       // lanes per entry
   constexpr int EPI = 64 / LPE;    // entries per wave iteration
-  constexpr int GMAX = 8;
-  __shared__ float z_s[GMAX][CHUNK];
-  __shared__ float m_s[GMAX], l_s[GMAX];
-  __shared__ float o_s[4][GMAX][D];
+  constexpr int STEP = 4 * EPI;    // entries per workgroup iteration
+  constexpr int ITER = CHUNK / STEP;
+  __shared__ float z_s[G][CHUNK];
+  __shared__ float m_s[G], l_s[G];
+  __shared__ float o_s[4][G][D];
   const int unit = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
   const int s = unit / (a.Ly * a.H), lh = unit % (a.Ly * a.H);
   const int l = lh / a.H, h = lh % a.H;
@@ -94,33 +99,41 @@ __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, floa
   }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPE, slot = lane / LPE;
-  const int G = a.G;
   // query slice of every head of the group for this lane's 8 dims
-  float q[GMAX][8];
+  float q[G][8];
   const T* Qb = (const T*)a.Q + (((int64_t)s * a.Ly + l) * a.H * G + (int64_t)h * G) * D + sub * 8;
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g)
-    if (g < G) Vec8<T>::load(Qb + (int64_t)g * D, q[g]);
-  // phase 1: logits
-  for (int e = wave * EPI + slot; e < CHUNK; e += 4 * EPI) {
-    float k[8];
+  for (int g = 0; g < G; ++g) Vec8<T>::load(Qb + (int64_t)g * D, q[g]);
+  // phase 1: logits; every lane issues all of its K loads before using them
+  typename Vec8<T>::Raw kraw[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    int e = it * STEP + wave * EPI + slot;
+    if (e < n) kraw[it] = Vec8<T>::raw(Kb + (int64_t)e * D + sub * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    int e = it * STEP + wave * EPI + slot;
     bool ok = e < n;
-    if (ok) Vec8<T>::load(Kb + (int64_t)e * D + sub * 8, k);
-    else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) k[j] = 0.f;
-    }
     float bias = (ok && lm) ? lm[e] * LOG2E : 0.f;
+    float kf[8];
+    Vec8<T>::cvt(kraw[it], kf);
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g >= G) break;
+    for (int g = 0; g < G; ++g) {
       float dsum = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dsum += q[g][j] * k[j];
+      for (int j = 0; j < 8; ++j) dsum += q[g][j] * (ok ? kf[j] : 0.f);
 #pragma unroll
       for (int o = LPE / 2; o > 0; o >>= 1) dsum += __shfl_xor(dsum, o, 64);
-      if (sub == 0 && e < CHUNK) z_s[g][e] = ok ? dsum * a.scale2 + bias : -INFINITY;
+      if (sub == 0) z_s[g][e] = ok ? dsum * a.scale2 + bias : -INFINITY;
     }
+  }
+  // V loads go out before the softmax barrier
+  typename Vec8<T>::Raw vraw[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    int e = it * STEP + wave * EPI + slot;
+    if (e < n) vraw[it] = Vec8<T>::raw(Vb + (int64_t)e * D + sub * 8);
   }
   __syncthreads();
   // phase 2: per-head max and exponentials (one wave per head, strided)
@@ -142,26 +155,28 @@ __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, floa
   }
   __syncthreads();
   // phase 3: o_g = sum_e p_g(e) v_e over this lane's 8 dims
-  float acc[GMAX][8];
+  float acc[G][8];
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g)
+  for (int g = 0; g < G; ++g)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
-  for (int e = wave * EPI + slot; e < n; e += 4 * EPI) {
-    float v[8];
-    Vec8<T>::load(Vb + (int64_t)e * D + sub * 8, v);
 #pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-      if (g >= G) break;
-      float p = z_s[g][e];
+  for (int it = 0; it < ITER; ++it) {
+    int e = it * STEP + wave * EPI + slot;
+    if (e < n) {
+      float vf[8];
+      Vec8<T>::cvt(vraw[it], vf);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[g][j] += p * v[j];
+      for (int g = 0; g < G; ++g) {
+        float p = z_s[g][e];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[g][j] += p * vf[j];
+      }
     }
   }
   // reduce over the wave's entry slots (lanes sharing `sub`)
 #pragma unroll
-  for (int g = 0; g < GMAX; ++g) {
-    if (g >= G) break;
+  for (int g = 0; g < G; ++g) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float x = acc[g][j];
@@ -182,38 +197,56 @@ __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, floa
   }
 }
 
-// one workgroup per (s, h, g); D threads; layers summed in order
+// Merge the chunks of every (s, l, h): one workgroup of G*D threads per unit;
+// o[s][l][h*G+g][d] normalized.
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a, const float* part, float* x_out,
-                                                           int64_t x_stride, float* o_out) {
+__global__ __launch_bounds__(1024) void decode_merge_kernel(DecArgs a, const float* part, float* o) {
   const int G = a.G;
-  const int s = blockIdx.x / (a.H * G);
-  const int hg = blockIdx.x % (a.H * G);
-  const int h = hg / G, g = hg % G;
-  const int dd = threadIdx.x;
-  float x = 0.f;
-  for (int l = 0; l < a.Ly; ++l) {
-    const int seg_idx = (s * a.Ly + l) * a.H + h;
-    const int unit = (s * a.Ly + l) * a.H + h;  // same numbering as the partial kernel
-    const int64_t slen = a.seg_len[seg_idx];
-    const int nseg = min((int)((slen + CHUNK - 1) / CHUNK), a.nchunk - (a.t_cap + CHUNK - 1) / CHUNK);
-    const int ntail = (a.t_valid + CHUNK - 1) / CHUNK;
-    float m = -INFINITY, sum = 0.f, o = 0.f;
-    for (int c = 0; c < nseg + ntail; ++c) {
-      const float* pb = part + (((int64_t)unit * a.nchunk + c) * G + g) * (D + 2);
-      float mc = pb[D], lc = pb[D + 1];
-      if (mc == -INFINITY) continue;
-      float mn = fmaxf(m, mc);
-      float f1 = exp2f(m - mn), f2 = exp2f(mc - mn);
-      sum = sum * f1 + lc * f2;
-      o = o * f1 + pb[dd] * f2;
+  const int unit = blockIdx.x;                         // (s*Ly + l)*H + h
+  const int g = threadIdx.x / D, dd = threadIdx.x % D;
+  if (g >= G) return;
+  const int64_t slen = a.seg_len[unit];
+  const int nseg = min((int)((slen + CHUNK - 1) / CHUNK), a.nchunk - (a.t_cap + CHUNK - 1) / CHUNK);
+  const int ntail = (a.t_valid + CHUNK - 1) / CHUNK;
+  float m = -INFINITY, sum = 0.f, acc = 0.f;
+  const int nc = nseg + ntail;
+  constexpr int BATCH = 8;
+  for (int c0 = 0; c0 < nc; c0 += BATCH) {
+    float mc[BATCH], lc[BATCH], oc[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      mc[q] = -INFINITY;
+      lc[q] = oc[q] = 0.f;
+      if (c0 + q < nc) {
+        const float* pb = part + (((int64_t)unit * a.nchunk + c0 + q) * G + g) * (D + 2);
+        mc[q] = pb[D];
+        lc[q] = pb[D + 1];
+        oc[q] = pb[dd];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      if (mc[q] == -INFINITY) continue;
+      float mn = fmaxf(m, mc[q]);
+      float f1 = exp2f(m - mn), f2 = exp2f(mc[q] - mn);
+      sum = sum * f1 + lc[q] * f2;
+      acc = acc * f1 + oc[q] * f2;
       m = mn;
     }
-    float ov = sum > 0.f ? o / sum : 0.f;
-    if (o_out) o_out[(((int64_t)s * a.Ly + l) * a.H * G + hg) * D + dd] = ov;
-    x += ov;
   }
-  x_out[(int64_t)s * x_stride + (int64_t)hg * D + dd] = x;
+  o[((int64_t)unit * G + g) * D + dd] = sum > 0.f ? acc / sum : 0.f;
+}
+
+// x[s][j] = sum over layers (in order) of o[s][l][j], j < H*G*D
+__global__ void decode_layersum_kernel(DecArgs a, int D, const float* o, float* x_out, int64_t x_stride) {
+  const int64_t HGD = (int64_t)a.H * a.G * D;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)a.S * HGD) return;
+  int s = (int)(i / HGD);
+  int64_t j = i % HGD;
+  float x = 0.f;
+  for (int l = 0; l < a.Ly; ++l) x += o[((int64_t)s * a.Ly + l) * HGD + j];
+  x_out[(int64_t)s * x_stride + j] = x;
 }
 
 int nchunk_of(const kvc_ragged* c, int t_cap) {
@@ -225,7 +258,10 @@ int nchunk_of(const kvc_ragged* c, int t_cap) {
 extern "C" size_t kvc_decode_workspace(const kvc_ragged* c, int32_t group, int32_t t_cap) {
   if (!c || group < 1 || t_cap < 0 || c->max_seg < 0) return 0;
   int64_t units = (int64_t)c->n_seq * c->n_layers * c->n_kv_heads;
-  return (size_t)units * nchunk_of(c, t_cap) * group * (c->head_dim + 2) * sizeof(float) + 256;
+  kvc::Carver cv(nullptr, 0);
+  cv.take<float>((size_t)units * nchunk_of(c, t_cap) * group * (c->head_dim + 2));
+  cv.take<float>((size_t)units * group * c->head_dim);
+  return cv.off + 256;
 }
 
 extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const void* V_tail, int32_t t_valid,
@@ -263,20 +299,36 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
   a.nchunk = nchunk_of(c, t_cap);
   a.scale2 = 1.4426950408889634f / sqrtf((float)c->head_dim);
   int64_t units = (int64_t)a.S * a.Ly * a.H;
-  float* part = (float*)ws;
+  kvc::Carver cv(ws, ws_bytes);
+  float* part = cv.take<float>((size_t)units * a.nchunk * group * (c->head_dim + 2));
+  float* obuf = o_out ? o_out : cv.take<float>((size_t)units * group * c->head_dim);
   dim3 grid((unsigned)(units * a.nchunk));
   int d = c->head_dim;
-  if (c->dtype == KVC_BF16) {
-    if (d == 128) hipLaunchKernelGGL((decode_partial_kernel<uint16_t, 128>), grid, dim3(THREADS), 0, st, a, part);
-    else hipLaunchKernelGGL((decode_partial_kernel<uint16_t, 64>), grid, dim3(THREADS), 0, st, a, part);
-  } else {
-    if (d == 128) hipLaunchKernelGGL((decode_partial_kernel<float, 128>), grid, dim3(THREADS), 0, st, a, part);
-    else hipLaunchKernelGGL((decode_partial_kernel<float, 64>), grid, dim3(THREADS), 0, st, a, part);
+#define KVC_DEC(TT, DD, GG) hipLaunchKernelGGL((decode_partial_kernel<TT, DD, GG>), grid, dim3(THREADS), 0, st, a, part)
+#define KVC_DEC_G(TT, DD)                      \
+  switch (group) {                             \
+    case 1: KVC_DEC(TT, DD, 1); break;         \
+    case 2: KVC_DEC(TT, DD, 2); break;         \
+    case 4: KVC_DEC(TT, DD, 4); break;         \
+    default: KVC_DEC(TT, DD, 8); break;        \
   }
+  KVC_REQUIRE(group == 1 || group == 2 || group == 4 || group == 8, KVC_E_UNSUPPORTED,
+              "kvc_decode_attn: group must be 1, 2, 4 or 8");
+  if (c->dtype == KVC_BF16) {
+    if (d == 128) { KVC_DEC_G(uint16_t, 128); } else { KVC_DEC_G(uint16_t, 64); }
+  } else {
+    if (d == 128) { KVC_DEC_G(float, 128); } else { KVC_DEC_G(float, 64); }
+  }
+#undef KVC_DEC_G
+#undef KVC_DEC
   KVC_LAUNCH_CHECK("decode_partial");
-  dim3 cg((unsigned)(a.S * a.H * group));
-  if (d == 128) hipLaunchKernelGGL((decode_combine_kernel<128>), cg, dim3(128), 0, st, a, part, x_out, x_stride, o_out);
-  else hipLaunchKernelGGL((decode_combine_kernel<64>), cg, dim3(64), 0, st, a, part, x_out, x_stride, o_out);
-  KVC_LAUNCH_CHECK("decode_combine");
+  if (d == 128)
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((unsigned)units), dim3(group * 128), 0, st, a, part, obuf);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3((unsigned)units), dim3(group * 64), 0, st, a, part, obuf);
+  KVC_LAUNCH_CHECK("decode_merge");
+  int64_t nx = (int64_t)a.S * a.H * group * d;
+  hipLaunchKernelGGL(decode_layersum_kernel, dim3(kvc_blocks(nx, 256)), dim3(256), 0, st, a, d, obuf, x_out, x_stride);
+  KVC_LAUNCH_CHECK("decode_layersum");
   return KVC_OK;
 }

@@ -129,10 +129,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kl_kernel(const T* xh, const T* 
     for (int v = 0; v < 16; v += 2) {
       int row = rb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
       int64_t pair = (r0 + row) >> 1;
-      float y = acc[rb][v] * LOG2E, yh = acc[rb][v + 1] * LOG2E;   // base-2 logits
+      // base-2 logits for the partition sums; the logit difference is taken
+      // from the accumulators themselves so identical rows give exactly 0
+      float y = acc[rb][v] * LOG2E, yh = acc[rb][v + 1] * LOG2E;
+      float dy = acc[rb][v] - acc[rb][v + 1];
       Stat5 st;
       if (cvalid) {
-        st.mf = y; st.sf = 1.f; st.mc = yh; st.sc = 1.f; st.t = (y - yh) * LN2;
+        st.mf = y; st.sf = 1.f; st.mc = yh; st.sc = 1.f; st.t = dy;
       } else {
         st.mf = -INFINITY; st.sf = 0.f; st.mc = -INFINITY; st.sc = 0.f; st.t = 0.f;
       }

@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/kvc.h"
+#include "kvc.h"
 
 namespace kvc {
 

@@ -22,6 +22,7 @@
 #include <cmath>
 
 #include "kvc_internal.h"
+#include "mfma_frag.h"
 
 namespace {
 
@@ -117,47 +118,78 @@ __global__ __launch_bounds__(256) void turning_kernel(PartArgs a) {
   }
 }
 
-// one wave per slot end token (the slot's last token)
+// Banded Gram matrix of the normalized trajectory on MFMA:
+// G[i][k] = <h^_i, h^_{i+k}> for 0 <= k < BW, tokens of one sequence only.
+// Tiles of 32 x 32 token pairs; the bf16 hidden states enter the MFMA as they
+// are (products exact, fp32 sums) and the two inverse norms scale the result.
+constexpr int BW = 128;   // band width = longest slot
 template <class T>
-__global__ __launch_bounds__(256) void cost_kernel(PartArgs a) {
-  constexpr int MAXDPL = 64;  // hidden dims per lane (Dh <= 4096)
-  int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256) void gram_kernel(PartArgs a, float* G) {
+  using namespace kvcmf;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // block = 32-row i-block; its 4 waves take j-blocks ib + wave .. (5 tiles cover the band)
+  const int64_t ib = blockIdx.x;
+  const int64_t i0 = ib * 32;
+  if (i0 >= a.T) return;
+  const T* H = (const T*)a.hidden;
+  for (int jt = wave; jt < 5; jt += 4) {
+    const int64_t j0 = i0 + (int64_t)jt * 32;
+    if (j0 >= a.T) break;
+    kvc_f32x16 acc = {};
+    const int64_t ri = i0 + (lane & 31), rj = j0 + (lane & 31);
+    const bool vi = ri < a.T, vj = rj < a.T;
+    for (int c = 0; c < a.Dh; c += 16) {
+      int cc = c + 8 * (lane >> 5);
+      Frag<T> fa = vi ? load_frag<T>(H + ri * a.Dh + cc) : zero_frag<T>();
+      Frag<T> fb = vj ? load_frag<T>(H + rj * a.Dh + cc) : zero_frag<T>();
+      mma(acc, fa, fb);
+    }
+    // register v: row i = i0 + acc_row(v), column j = j0 + lane % 32
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      int64_t i = i0 + acc_row(v, lane), j = rj;
+      int64_t kk = j - i;
+      if (i < a.T && j < a.T && kk >= 0 && kk < BW) G[i * BW + kk] = acc[v] * a.inv[i] * a.inv[j];
+    }
+  }
+}
+
+// Inclusive prefix sums along every band row, in place.
+__global__ void band_prefix_kernel(PartArgs a, float* G) {
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= a.T) return;
+  float* r = G + g * BW;
+  float run = 0.f;
+  for (int k = 0; k < BW; ++k) {
+    run += r[k];
+    r[k] = run;
+  }
+}
+
+// One thread per slot END token e (inclusive last token): growing the window
+// [a, e] one token to the left adds 2 sum_{j=a+1..e} G[a][j-a] + G[a][0],
+// read from the band-row prefix sums.
+__global__ __launch_bounds__(256) void window_cost_kernel(PartArgs a, const float* G) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= a.T) return;
   int s = seq_of(a.cu, a.S, t);
-  int64_t p = t - a.cu[s];             // the slot [p - n + 1, p] ends here
+  int64_t p = t - a.cu[s];
   if (p < a.c0[s] || p >= a.c1[s]) return;
   const int ncol = a.nmax - a.nmin + 1;
   int64_t* row = a.cost_q + t * ncol;
-  const int dpl = (a.Dh + 63) / 64;
-  float S[MAXDPL];
-#pragma unroll
-  for (int j = 0; j < MAXDPL; ++j) S[j] = 0.f;
-  float sq = 0.f;
-  const T* H = (const T*)a.hidden;
+  float W = 0.f, sq = 0.f;
   for (int n = 1; n <= a.nmax; ++n) {
-    int64_t i = p - n + 1;             // token added to the window
+    int64_t i = p - n + 1;                    // token joining the window
     if (i < a.c0[s]) break;
     int64_t g = a.cu[s] + i;
-    float iv = a.inv[g];
+    const float* gr = G + g * BW;
+    float g0 = gr[0];
+    W += 2.f * (gr[n - 1] - g0) + g0;
     sq += a.nrm2[g];
-#pragma unroll
-    for (int j = 0; j < MAXDPL; ++j) {
-      if (j >= dpl) break;
-      int dd = j * 64 + lane;
-      if (dd < a.Dh) S[j] += ElemIO<T>::ld(H, g * a.Dh + dd) * iv;
-    }
     if (n >= a.nmin) {
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < MAXDPL; ++j)
-        if (j < dpl) part += S[j] * S[j];
-      float ss = wave_sum(part);
-      if (lane == 0) {
-        double disp = (double)sq - (double)ss / (double)n;
-        double x = ((double)n - a.target) / (double)a.target;
-        row[n - a.nmin] = qround(disp + (double)a.lam_len * x * x);
-      }
+      double disp = (double)sq - (double)W / (double)n;
+      double x = ((double)n - a.target) / (double)a.target;
+      row[n - a.nmin] = qround(disp + (double)a.lam_len * x * x);
     }
   }
 }
@@ -197,14 +229,27 @@ __global__ __launch_bounds__(1024) void dp_kernel(PartArgs a) {
     int64_t best = INT64_MAX;
     const bool mine = wave < step && e <= Lc;
     if (mine) {
-      for (int c = lane; c < ncol; c += 64) {
-        int n = a.nmin + c;
-        int64_t pv = e - n;
-        if (pv < 0) continue;
-        int64_t f = fr[pv % RING];
-        if (f >= INF_Q) continue;
-        int64_t v = f + a.cost_q[(gbase + e - 1) * ncol + c];
-        if (pv > 0) v -= a.cut_q[gbase + pv];
+      // two candidates per lane (slot_max - slot_min < 128); the global loads
+      // go out before the LDS reads of earlier ends
+      int64_t cq[2], kq[2], fv[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int c = lane + 64 * q;
+        int64_t pv = e - (a.nmin + c);
+        cq[q] = (c < ncol && pv >= 0) ? a.cost_q[(gbase + e - 1) * ncol + c] : 0;
+        kq[q] = (c < ncol && pv > 0) ? a.cut_q[gbase + pv] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int c = lane + 64 * q;
+        int64_t pv = e - (a.nmin + c);
+        fv[q] = (c < ncol && pv >= 0) ? fr[pv % RING] : INF_Q;
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        int c = lane + 64 * q;
+        if (fv[q] >= INF_Q) continue;
+        int64_t v = fv[q] + cq[q] - kq[q];
         int64_t key = v * 256 + (255 - c);
         best = key < best ? key : best;
       }
@@ -263,6 +308,7 @@ size_t ws_partition(const kvc_shape* s, const kvc_params* p) {
   c.take<float>((size_t)s->total_tokens * 2);
   c.take<int64_t>((size_t)s->total_tokens * (ncol > 0 ? ncol : 1));
   c.take<int64_t>((size_t)s->total_tokens);
+  c.take<float>((size_t)s->total_tokens * BW);
   return c.off + 256;
 }
 }  // namespace kvc
@@ -307,6 +353,7 @@ extern "C" int kvc_partition(const kvc_shape* sh, const kvc_params* p, const voi
   a.nrm2 = c.take<float>((size_t)sh->total_tokens);
   int64_t* cq = c.take<int64_t>((size_t)sh->total_tokens * ncol);
   int64_t* kq = c.take<int64_t>((size_t)sh->total_tokens);
+  float* gband = c.take<float>((size_t)sh->total_tokens * BW);
   if (mode == 1) {
     KVC_REQUIRE(dp_cost_q && dp_cut_q, KVC_E_INVAL, "kvc_partition: mode 1 needs dp_cost_q and dp_cut_q");
     a.cost_q = dp_cost_q;
@@ -318,17 +365,21 @@ extern "C" int kvc_partition(const kvc_shape* sh, const kvc_params* p, const voi
     a.Dh = hidden_dim;
     a.cost_q = dp_cost_q ? dp_cost_q : cq;
     a.cut_q = dp_cut_q ? dp_cut_q : kq;
-    dim3 gt((unsigned)sh->total_tokens), gc(kvc_blocks(sh->total_tokens, 4));
+    KVC_REQUIRE(p->slot_max <= BW, KVC_E_UNSUPPORTED, "kvc_partition: slot_max above 128");
+    KVC_REQUIRE(hidden_dim % 16 == 0, KVC_E_SHAPE, "kvc_partition: hidden_dim must be a multiple of 16");
+    dim3 gt((unsigned)sh->total_tokens), gg(kvc_blocks(sh->total_tokens, 32)), gw(kvc_blocks(sh->total_tokens, 256));
     if (sh->total_tokens > 0) {
       if (sh->dtype == KVC_BF16) {
         hipLaunchKernelGGL(norm_kernel<uint16_t>, gt, dim3(256), 0, st, a);
         hipLaunchKernelGGL(turning_kernel<uint16_t>, gt, dim3(256), 0, st, a);
-        hipLaunchKernelGGL(cost_kernel<uint16_t>, gc, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(gram_kernel<uint16_t>, gg, dim3(256), 0, st, a, gband);
       } else {
         hipLaunchKernelGGL(norm_kernel<float>, gt, dim3(256), 0, st, a);
         hipLaunchKernelGGL(turning_kernel<float>, gt, dim3(256), 0, st, a);
-        hipLaunchKernelGGL(cost_kernel<float>, gc, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(gram_kernel<float>, gg, dim3(256), 0, st, a, gband);
       }
+      hipLaunchKernelGGL(band_prefix_kernel, gw, dim3(256), 0, st, a, gband);
+      hipLaunchKernelGGL(window_cost_kernel, gw, dim3(256), 0, st, a, (const float*)gband);
       KVC_LAUNCH_CHECK("partition_costs");
     }
   }

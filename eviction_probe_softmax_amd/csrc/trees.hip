@@ -21,6 +21,7 @@
 #include <cmath>
 
 #include "kvc_internal.h"
+#include "mfma_frag.h"
 
 namespace {
 
@@ -51,27 +52,38 @@ struct TreeKArgs {
   uint8_t* op_cost;
 };
 
+// hi/lo bf16 split of 8 fp32 softmax weights (for the fp32-accurate MFMA)
+__device__ __forceinline__ void split8(const float* x, kvc_bf16x8& hi, kvc_bf16x8& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t u = __float_as_uint(x[j]) & 0xffff0000u;
+    float r = x[j] - __uint_as_float(u);
+    hi[j] = __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
+    lo[j] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(r));
+  }
+}
+
 template <class T, int D>
 __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
+  using namespace kvcmf;
   constexpr int HD = D / 2;
+  constexpr int KS = D / 16;
+  constexpr int NPV = 136;   // token stride of the transposed values (68 dwords: b128 reads conflict-free)
+  constexpr int NPA = 132;   // token stride of the transposed softmax weights
   extern __shared__ __align__(16) char smem[];
   const int nmax = a.nmax;
-  T* Kl = (T*)smem;                                   // [nmax][D]
-  T* Vl = Kl + (size_t)nmax * D;                      // [nmax][D]
-  float* A = (float*)(Vl + (size_t)nmax * D);         // [nmax][PDMAX]
-  T* Ql = (T*)(A + (size_t)nmax * PDMAX);             // [D][PDMAX]
-  float* lse_s = (float*)(Ql + (size_t)D * PDMAX);    // [PDMAX]
-  float* knorm = lse_s + PDMAX;                       // [nmax]
-  float* rtok = knorm + nmax;                         // [nmax]
-  float* nrel = rtok + nmax;                          // [2 nmax]
-  float* nD = nrel + 2 * nmax;                        // [2 nmax]
-  float* nmu = nD + 2 * nmax;                         // [2 nmax]
-  int* nst = (int*)(nmu + 2 * nmax);                  // [2 nmax]
-  int* nsz = nst + 2 * nmax;
-  int* nlc = nsz + 2 * nmax;
-  int* nrc = nlc + 2 * nmax;
-  float* scratch = (float*)(nrc + 2 * nmax);          // [WAVES][2][D]
-  __shared__ int n_nodes;
+  float* Kt = (float*)smem;                                        // [nmax][D] unrotated keys (fp32)
+  T* Vt = (T*)(Kt + (size_t)nmax * D);                             // [D][NPV] values, transposed
+  float* At = (float*)(Vt + (size_t)D * NPV);                      // [PDMAX][NPA] softmax weights
+  float* lse_s = At + (size_t)PDMAX * NPA;                         // [PDMAX]
+  float* knorm = lse_s + PDMAX;                                    // [nmax]
+  float* rtok = knorm + nmax;                                      // [nmax]
+  float* nrel = rtok + nmax;                                       // [2 nmax]
+  float* nD = nrel + 2 * nmax;                                     // [2 nmax]
+  float* nmu = nD + 2 * nmax;                                      // [2 nmax]
+  int16_t* nst = (int16_t*)(nmu + 2 * nmax);                       // [2 nmax]
+  int16_t* nsz = nst + 2 * nmax;                                   // [2 nmax]
+  float* scratch = (float*)(nsz + 2 * nmax);                       // [WAVES][2][D]
 
   int64_t b = blockIdx.x;
   const int k = (int)(b % a.stride);
@@ -82,6 +94,8 @@ __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
   const int l = (int)(lh / a.H), h = (int)(lh % a.H);
   const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
   const int t0 = ss[k], n = ss[k + 1] - ss[k];
+  const int n16 = (n + 15) & ~15;
+  const int m = 2 * n - 1;
   const int64_t tok0 = a.cu[s] + t0;
   const int64_t obase = lh * 2 * a.T + 2 * tok0;
   const T* Kg = (const T*)a.K + (lh * a.T + tok0) * D;
@@ -89,69 +103,94 @@ __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int unit = (s * a.Ly + l) * a.H + h;
   const float sens = a.sens[unit];
-
-  // ---- stage K, V, distortion probe rows (transposed), lse, relevance
-  for (int i = tid; i < n * D; i += THREADS) {
-    Kl[i] = Kg[i];
-    Vl[i] = Vg[i];
-  }
   const T* Qu = (const T*)a.Qp + ((((int64_t)s * a.Ly + l) * a.H * a.G + (int64_t)h * a.G) * a.P) * D;
-  for (int i = tid; i < a.pd * D; i += THREADS) {
-    int rho = i / D, dd = i % D;
-    Ql[dd * PDMAX + rho] = Qu[(int64_t)rho * a.pstride * D + dd];
+
+  // ---- stage transposed values (bf16; zero past the slot up to a 16 multiple),
+  // lse, r, node table; unrotated keys and key norms straight from HBM
+  for (int i = tid; i < n16 * (D / 8); i += THREADS) {
+    int r = i / (D / 8), c = (i % (D / 8)) * 8;
+    float x[8];
+    if (r < n) Load8<T>::f(Vg + (int64_t)r * D + c, x);
+    else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ElemIO<T>::st(Vt, (int64_t)(c + j) * NPV + r, x[j]);
   }
   for (int rho = tid; rho < a.pd; rho += THREADS) lse_s[rho] = a.lse[(int64_t)unit * a.G * a.P + (int64_t)rho * a.pstride];
   for (int i = tid; i < n; i += THREADS) rtok[i] = a.rel[lh * a.T + tok0 + i];
-  if (tid == 0) {
-    // pre-order node table: pop, number, push right then left
-    int fs[24], fz[24], fp[24], fd[24], top = 0, m = 0;
-    fs[top] = 0; fz[top] = n; fp[top] = -1; fd[top] = 0; ++top;
-    while (top > 0) {
-      --top;
-      int st = fs[top], sz = fz[top], par = fp[top], side = fd[top];
-      int j = m++;
-      nst[j] = st;
-      nsz[j] = sz;
-      nlc[j] = -1;
-      nrc[j] = -1;
-      if (par >= 0) {
-        if (side == 0) nlc[par] = j;
-        else nrc[par] = j;
-      }
-      if (sz > 1) {
-        int nl = (sz + 1) >> 1;
-        fs[top] = st + nl; fz[top] = sz - nl; fp[top] = j; fd[top] = 1; ++top;
-        fs[top] = st; fz[top] = nl; fp[top] = j; fd[top] = 0; ++top;
+  for (int j = tid; j < m; j += THREADS) {
+    int cur = 0, st = 0, sz = n;
+    while (cur != j) {
+      int nl = (sz + 1) >> 1;
+      if (j < cur + 2 * nl) {
+        cur += 1;
+        sz = nl;
+      } else {
+        cur += 2 * nl;
+        st += nl;
+        sz -= nl;
       }
     }
-    n_nodes = m;
+    nst[j] = (int16_t)st;
+    nsz[j] = (int16_t)sz;
   }
-  __syncthreads();
-  // key norms (rotation keeps the norm) and softmax weights of the probe rows
+  for (int it = tid; it < n * HD; it += THREADS) {
+    int i = it / HD, p = it % HD;
+    float x0 = ElemIO<T>::ld(Kg, (int64_t)i * D + p), x1 = ElemIO<T>::ld(Kg, (int64_t)i * D + p + HD);
+    int64_t pos = t0 + i;
+    float c = a.rc[pos * HD + p], sn = a.rs[pos * HD + p];
+    Kt[(size_t)i * D + p] = x0 * c + x1 * sn;       // rotation by -theta
+    Kt[(size_t)i * D + p + HD] = x1 * c - x0 * sn;
+  }
   for (int i = tid; i < n; i += THREADS) {
     float q = 0.f;
-    for (int dd = 0; dd < D; ++dd) {
-      float x = ElemIO<T>::ld(Kl, (int64_t)i * D + dd);
-      q += x * x;
+    for (int c = 0; c < D; c += 8) {
+      float x[8];
+      Load8<T>::f(Kg + (int64_t)i * D + c, x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q += x[j] * x[j];
     }
     knorm[i] = sqrtf(q);
   }
-  for (int i = tid; i < n * PDMAX; i += THREADS) {
-    int t = i / PDMAX, rho = i % PDMAX;
-    float v = 0.f;
-    if (rho < a.pd) {
-      float dot = 0.f;
-      for (int dd = 0; dd < D; ++dd) dot += ElemIO<T>::ld(Ql, dd * PDMAX + rho) * ElemIO<T>::ld(Kl, (int64_t)t * D + dd);
-      v = expf(dot * a.c - lse_s[rho]);
+  // softmax weights of the distortion rows on MFMA (K Q^T), stored transposed;
+  // zero for tokens past the slot up to the 16 multiple
+  {
+    const int ntb = (n16 + 31) / 32, nrb = (a.pd + 31) / 32;
+    for (int tile = wave; tile < ntb * nrb; tile += WAVES) {
+      int tb = tile / nrb, rb = tile % nrb;
+      int tok = tb * 32 + (lane & 31), rho = rb * 32 + (lane & 31);
+      kvc_f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        int c = ks * 16 + 8 * (lane >> 5);
+        Frag<T> ka = tok < n ? load_frag<T>(Kg + (int64_t)tok * D + c) : zero_frag<T>();
+        Frag<T> qb = rho < a.pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
+        mma(acc, ka, qb);
+      }
+      float ls = rho < a.pd ? a.lse[(int64_t)unit * a.G * a.P + (int64_t)rho * a.pstride] : 0.f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        int ti = tb * 32 + acc_row(v, lane);
+        if (ti < n16 && rho < PDMAX)
+          At[rho * NPA + ti] = (ti < n && rho < a.pd) ? expf(acc[v] * a.c - ls) : 0.f;
+      }
     }
-    A[i] = v;
-  }
-  if (tid == 0) {
-    // bottom-up value flow: reverse pre-order visits children before parents
-    for (int j = n_nodes - 1; j >= 0; --j) nrel[j] = nlc[j] < 0 ? rtok[nst[j]] : nrel[nlc[j]] + nrel[nrc[j]];
   }
   __syncthreads();
-  const int m = n_nodes;
+  // ---- bottom-up value flow by height (a parent is the exact fp32 sum of its
+  // children; children of pre-order node j are j+1 and j + 2 ceil(sz/2))
+  for (int j = tid; j < m; j += THREADS)
+    if (nsz[j] == 1) nrel[j] = rtok[nst[j]];
+  __syncthreads();
+  for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
+    for (int j = tid; j < m; j += THREADS) {
+      int sz = nsz[j];
+      if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
+    }
+    __syncthreads();
+  }
   float* kh = scratch + (size_t)wave * 2 * D;
   float* vh = kh + D;
   for (int j = wave; j < m; j += WAVES) {
@@ -166,17 +205,16 @@ __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
     const float reln = nrel[j];
     // prototype key and coherence: lane = rotate-half pair
     float s0 = 0.f, s1 = 0.f, kn = 0.f;
-    for (int i = st; i < st + sz; ++i) kn += knorm[i];
     if (lane < HD) {
+#pragma unroll 8
       for (int i = st; i < st + sz; ++i) {
-        float x0 = ElemIO<T>::ld(Kl, (int64_t)i * D + lane), x1 = ElemIO<T>::ld(Kl, (int64_t)i * D + lane + HD);
-        int64_t pos = t0 + i;
-        float c = a.rc[pos * HD + lane], sn = a.rs[pos * HD + lane];
-        s0 += x0 * c + x1 * sn;
-        s1 += x1 * c - x0 * sn;
+        s0 += Kt[(size_t)i * D + lane];
+        s1 += Kt[(size_t)i * D + lane + HD];
+        kn += knorm[i];
       }
     }
     float nrm2 = wave_sum(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
+    kn = __shfl(kn, 0, 64);
     float coh = kn > 0.f ? sqrtf(nrm2) / kn : 1.f;
     float mu = fmaxf(1.f, (float)sz * coh);
     if (lane < HD) {
@@ -186,44 +224,83 @@ __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
       kh[lane] = m0 * c - m1 * sn;
       kh[lane + HD] = m1 * c + m0 * sn;
     }
+    // prototype value: (1 - beta) r_i / rel + beta / n, lane = dimension
     for (int dd = lane; dd < D; dd += 64) {
       float acc = 0.f;
+#pragma unroll 8
       for (int i = st; i < st + sz; ++i) {
         float w = reln > 0.f ? (1.f - a.beta) * rtok[i] / reln + a.beta / (float)sz : 1.f / (float)sz;
-        acc += w * ElemIO<T>::ld(Vl, (int64_t)i * D + dd);
+        acc += w * ElemIO<T>::ld(Vt, (int64_t)dd * NPV + i);
       }
       vh[dd] = acc;
     }
     __builtin_amdgcn_wave_barrier();  // kh/vh written by this wave's lanes, read below
-    // lane rho: Z, Z_hat and the value aggregate u_rho
-    float eAn = 0.f, eAd = 0.f, eVn = 0.f, eVd = 0.f;
+    // lane rho: Z and Z_hat
+    float z = 0.f, zh = 0.f;
     if (lane < a.pd) {
-      const int rho = lane;
+      for (int i = st; i < st + sz; ++i) z += At[lane * NPA + i];
+      const T* qr = Qu + (int64_t)lane * a.pstride * D;
       float dot = 0.f;
-      for (int dd = 0; dd < D; ++dd) dot += ElemIO<T>::ld(Ql, dd * PDMAX + rho) * kh[dd];
-      float zh = mu * expf(dot * a.c - lse_s[rho]);
-      float z = 0.f;
-      for (int i = st; i < st + sz; ++i) z += A[i * PDMAX + rho];
-      float u[D];
-#pragma unroll
-      for (int dd = 0; dd < D; ++dd) u[dd] = 0.f;
-      for (int i = st; i < st + sz; ++i) {
-        float ai = A[i * PDMAX + rho];
-#pragma unroll
-        for (int dd = 0; dd < D; ++dd) u[dd] += ai * ElemIO<T>::ld(Vl, (int64_t)i * D + dd);
+#pragma unroll 4
+      for (int c = 0; c < D; c += 8) {
+        float x[8];
+        Load8<T>::f(qr + c, x);
+        float4 k0 = *(const float4*)(kh + c), k1 = *(const float4*)(kh + c + 4);
+        dot += x[0] * k0.x + x[1] * k0.y + x[2] * k0.z + x[3] * k0.w + x[4] * k1.x + x[5] * k1.y +
+               x[6] * k1.z + x[7] * k1.w;
       }
-      float n1 = 0.f, n2 = 0.f;
-#pragma unroll
-      for (int dd = 0; dd < D; ++dd) {
-        float df = u[dd] - z * vh[dd];
-        n1 += df * df;
-        n2 += u[dd] * u[dd];
-      }
-      eAn = fabsf(zh - z);
-      eAd = z;
-      eVn = sqrtf(n1);
-      eVd = sqrtf(n2);
+      zh = mu * expf(dot * a.c - lse_s[lane]);
     }
+    // u^T = V_node^T A_node^T on MFMA: rows = value dims, columns = probe rows;
+    // lane keeps column rho = pb*32 + lane%32 and 16 of the 32 rows of a tile
+    float eVn = 0.f, eVd = 0.f;
+    const int kb0 = st >> 4, kb1 = (st + sz + 15) >> 4;
+#pragma unroll 1
+    for (int pb = 0; pb < (a.pd + 31) / 32; ++pb) {
+      const int rho = pb * 32 + (lane & 31);
+      const float zr = __shfl(z, rho, 64);
+      float n1 = 0.f, n2 = 0.f;
+#pragma unroll 1
+      for (int db = 0; db < D / 32; ++db) {
+        kvc_f32x16 acc = {};
+        for (int kb = kb0; kb < kb1; ++kb) {
+          const int t8 = kb * 16 + 8 * (lane >> 5);
+          Frag<T> va = load_frag<T>(Vt + (size_t)(db * 32 + (lane & 31)) * NPV + t8);
+          float w8[8];
+          float4 w0 = *(const float4*)(At + rho * NPA + t8), w1 = *(const float4*)(At + rho * NPA + t8 + 4);
+          w8[0] = w0.x; w8[1] = w0.y; w8[2] = w0.z; w8[3] = w0.w;
+          w8[4] = w1.x; w8[5] = w1.y; w8[6] = w1.z; w8[7] = w1.w;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (t8 + q < st || t8 + q >= st + sz) w8[q] = 0.f;   // tokens outside the node
+          if constexpr (sizeof(T) == 2) {
+            Frag<uint16_t> hi, lo;
+            split8(w8, hi.v, lo.v);
+            mma(acc, va, hi);
+            mma(acc, va, lo);
+          } else {
+            Frag<float> wf;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) wf.v[q] = w8[q];
+            mma(acc, va, wf);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float u = acc[v];
+          float df = u - zr * vh[db * 32 + acc_row(v, lane)];
+          n1 += df * df;
+          n2 += u * u;
+        }
+      }
+      n1 += __shfl_xor(n1, 32, 64);
+      n2 += __shfl_xor(n2, 32, 64);
+      if (lane < 32 && rho < a.pd) {
+        eVn += sqrtf(n1);
+        eVd += sqrtf(n2);
+      }
+    }
+    float eAn = lane < a.pd ? fabsf(zh - z) : 0.f, eAd = lane < a.pd ? z : 0.f;
     eAn = wave_sum(eAn);
     eAd = wave_sum(eAd);
     eVn = wave_sum(eVn);
@@ -249,8 +326,8 @@ __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
     if (q == 0) {
       u = sens * (nrel[0] * (1.f - nD[0]));
       cst = 1;
-    } else if (q - 1 < m && nlc[q - 1] >= 0) {
-      int j = q - 1, lc = nlc[j], rc = nrc[j];
+    } else if (q - 1 < m && nsz[q - 1] > 1) {
+      int j = q - 1, lc = j + 1, rc = j + 2 * ((nsz[j] + 1) >> 1);
       float gain = nrel[j] * nD[j] - (nrel[lc] * nD[lc] + nrel[rc] * nD[rc]);
       u = sens * gain;
       cst = 1;
@@ -261,13 +338,13 @@ __global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
 }
 
 size_t tree_smem(int nmax, int d, int elt) {
-  size_t b = (size_t)nmax * d * elt * 2;
-  b += (size_t)nmax * PDMAX * 4;
-  b += (size_t)d * PDMAX * elt;
-  b += PDMAX * 4 + (size_t)nmax * 4 * 2;
-  b += (size_t)2 * nmax * 4 * 3 + (size_t)2 * nmax * 4 * 4;
-  b += (size_t)WAVES * 2 * d * 4;
-  return b + 64;
+  size_t b = (size_t)nmax * d * 4;                  // unrotated keys
+  b += (size_t)d * 136 * elt;                       // transposed values
+  b += (size_t)PDMAX * 132 * 4;                     // transposed softmax weights
+  b += PDMAX * 4 + (size_t)nmax * 4 * 2;            // lse, norms, r
+  b += (size_t)2 * nmax * 4 * 3 + (size_t)2 * nmax * 2 * 2;  // node values, starts, sizes
+  b += (size_t)WAVES * 2 * d * 4;                   // per-wave prototype scratch
+  return b;
 }
 
 int slot_nmax(const kvc_params* p) { return p->slot_len > 0 ? p->slot_len : p->slot_max; }
@@ -308,7 +385,7 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   a.G = sh->group;
   a.P = p->n_probe;
   a.stride = kvc_slot_stride(sh, p);
-  a.nmax = slot_nmax(p);
+  a.nmax = (slot_nmax(p) + 7) & ~7;  // LDS layout keeps every array 16-byte aligned
   int R = sh->group * p->n_probe;
   a.pd = p->n_dprobe < R ? p->n_dprobe : R;
   a.pstride = R / a.pd;

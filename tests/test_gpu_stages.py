@@ -65,13 +65,16 @@ def _compare_cache(c, oc, exact):
     close(lm, oc["lnmu"], 1e-3, "ln mu", floor=1e-3)
 
 
-@pytest.mark.parametrize("name", ["tiny", "stress", "ragged", "fulldepth"])
-def test_trees_match_oracle(name):
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("fulldepth", {}),
+                                     ("stress", {"slot_len": 128}),
+                                     ("fulldepth", {"slot_min": 64, "slot_max": 128, "slot_target": 120}),
+                                     ("tiny", {"slot_len": 128})])
+def test_trees_match_oracle(name, kw):
     kvc = _kvc()
-    cfg = small_config(name)
+    cfg = small_config(name, **kw)
     inp = make_inputs(cfg)
     dinp = inputs_to(inp)
-    print(f"[trees] {name}", flush=True)
+    print(f"[trees] {name} {kw}", flush=True)
     cu, sc, pr = _oracle_front(cfg, inp)
     cq = kq = None
     if cfg.slot_len == 0:
@@ -126,13 +129,13 @@ def test_floor_and_auction_bit_exact(name, kw):
     assert np.array_equal(gt, taken), f"{int((gt != taken).sum())} ops differ"
 
 
-@pytest.mark.parametrize("name", ["tiny", "stress", "ragged"])
-def test_pack_tree_mode(name):
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("stress", {"slot_len": 128})])
+def test_pack_tree_mode(name, kw):
     kvc = _kvc()
-    cfg = small_config(name)
+    cfg = small_config(name, **kw)
     inp = make_inputs(cfg)
     dinp = inputs_to(inp)
-    print(f"[pack] {name}", flush=True)
+    print(f"[pack] {name} {kw}", flush=True)
     cu, sc, pr = _oracle_front(cfg, inp)
     slots = oracle.slots_for(cu, cfg)
     o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
