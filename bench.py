@@ -33,8 +33,38 @@ def parse():
     ap.add_argument("--config", default="fulldepth")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_fulldepth_traffic.json"))
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run five plain device-to-device copies of MIB MiB (to scale HBM byte "
+                         "counters against a kernel of known traffic), then exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """Five torch copies of `mib` MiB: each reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 5}), flush=True)
+
+
+def measured_traffic(path, name):
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it covers another workload or the decode source changed since."""
+    import hashlib
+    try:
+        tj = json.load(open(path))
+        src = os.path.join(ROOT, "eviction_probe_softmax_amd", "csrc", "decode.hip")
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except (OSError, ValueError):
+        return None
+    if tj.get("config") != name or tj.get("decode_source_sha256_16") != sha:
+        return None
+    return tj.get("traffic_bytes_per_call")
 
 
 def describe(cfg):
@@ -84,6 +114,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import numpy as np
     import torch
     from workload import get_config, make_inputs
@@ -175,14 +208,7 @@ def main():
     gbs_full = bytes_full / (mean_full_ms * 1e-3) / 1e9
     # dominant kernel: decode over both caches (average bytes / average call)
     ach = (bytes_comp + bytes_full) / ((mean_comp_ms + mean_full_ms) * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            tj = json.load(open(args.traffic_json))
-            if tj.get("config") == cfg.name:
-                traffic = tj.get("traffic_bytes_per_call")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(args.traffic_json, cfg.name)
     klh = klv.detach().float().cpu().numpy()
     B, A, F = comp.pb.budgets()
     res = {
@@ -214,7 +240,7 @@ def main():
         "kl_ms": round(float(np.mean(kl_ms)), 3),
         "mean_kl": round(float(klh.mean()), 5),
         "max_kl": round(float(klh.max()), 5),
-        "roofline": {"bound": "hbm", "kernel": "decode (decode_partial + decode_combine per call)",
+        "roofline": {"bound": "hbm", "kernel": "decode call (decode_partial + decode_merge + decode_layersum)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_call_comp": int(bytes_comp), "bytes_per_call_full": int(bytes_full)},
