@@ -10,14 +10,23 @@
 // budget flow' (utility per entry = relevance x fidelity gain x head
 // sensitivity / new entries).
 //
-// One workgroup per slot. The slot's keys, values, the distortion probe rows
-// and their softmax weights a[i][rho] = exp(<q_rho,k_i>/sqrt d - lse_rho) sit
-// in LDS; node relevance is summed bottom-up by one thread (so a parent is
-// exactly the fp32 sum of its children); the internal nodes are independent
-// and spread over the waves. Per node a wave forms the prototype key (lane =
-// rotate-half pair) and value, then lane rho accumulates
-// u_rho = sum_node a[i][rho] v_i in registers so that ||u_rho - Z_rho v^|| and
-// ||u_rho|| never leave the lane.
+// A persistent grid walks the slots of every (layer, KV head) unit; one
+// workgroup builds one tree at a time, entirely in LDS:
+//  A. node table (pre-order), relevance summed bottom-up by height (a parent
+//     is exactly the fp32 sum of its children), inverse-rotated keys, and the
+//     distortion rows' softmax weights a[i][rho] = exp(<q_rho,k_i>/sqrt d -
+//     lse_rho) from K Q^T on MFMA;
+//  B. per internal node (one wave each, lane = rotate-half pair) the summed
+//     key, coherence and multiplicity and the re-rotated prototype key; the
+//     prototype logits <q_rho, k^> of 32 nodes at a time on MFMA (hi/lo bf16
+//     split of the fp32 keys); the attention-partition error from them;
+//  C. the value-aggregate error. With c_i = a_i - Z w_i (w = the prototype's
+//     value weights, sum c = 0), u - Z v^ = sum_i c_i v_i, so
+//     ||u - Z v^||^2 = c^T G c and ||u||^2 = a^T G a + 2 Z a.s + Z^2 |m|^2 with
+//     G the Gram matrix of the slot's values centred on their mean m (on MFMA,
+//     hi/lo split) and s_i = <v_i - m, m>. Lane rho evaluates its two forms
+//     over the node's block of G; the root and its children are spread over
+//     every wave by 8-row blocks, deeper nodes take one wave each.
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -25,9 +34,11 @@
 
 namespace {
 
-constexpr int WAVES = 8;
-constexpr int THREADS = WAVES * 64;
-constexpr int PDMAX = 64;
+constexpr int PDMAX = 64;   // distortion rows (one per lane)
+constexpr int PA = 64;      // token stride of the softmax weights a[i][rho]
+constexpr int NB = 32;      // internal nodes per prototype-logit batch
+constexpr int LGS = PDMAX + 4;
+constexpr int SMALL = 64;   // slots up to this length use the small-slot variant
 
 struct TreeKArgs {
   const void* K;
@@ -39,9 +50,10 @@ struct TreeKArgs {
   const float* rc;
   const float* rs;
   const int32_t* slot_start;
-  const int32_t* n_slots;
+  const int2* list;        // [S][stride] (start, length) of the slots of this size class
+  const int32_t* count;    // [S] their number
   const int64_t* cu;
-  int S, Ly, H, G, P, stride, nmax, pd, pstride;
+  int S, Ly, H, G, P, stride, pd, pstride;
   int64_t T;
   float c;                 // 1/sqrt(d)
   float beta, wA, wV;
@@ -52,307 +64,724 @@ struct TreeKArgs {
   uint8_t* op_cost;
 };
 
-// hi/lo bf16 split of 8 fp32 softmax weights (for the fp32-accurate MFMA)
-__device__ __forceinline__ void split8(const float* x, kvc_bf16x8& hi, kvc_bf16x8& lo) {
+// LDS layout (byte offsets, 16-byte aligned) for slots of at most NMAX tokens.
+template <int NMAX, int D, int WAVES>
+struct TreeLayout {
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr int N32 = (NMAX + 31) & ~31;
+  static constexpr int NG = N32 + 4;  // row stride of the Gram matrix
+  static constexpr size_t KT = (size_t)NMAX * D * 4, GM = (size_t)N32 * NG * 4;
+  static constexpr size_t KHB = (size_t)NB * (D + 4) * 4, PARTB = (size_t)WAVES * 3 * 2 * PDMAX * 4;
+  static constexpr size_t r1 = 0;
+  static constexpr size_t at = al(r1 + (KT > GM ? KT : GM));
+  static constexpr size_t kh = al(at + (size_t)NMAX * PA * 4);
+  // the logits of a batch overwrite its prototype keys once the MFMA has read them
+  static constexpr size_t lg = kh;
+  static_assert((size_t)NB * LGS * 4 <= KHB, "logits fit over the prototype keys");
+  static constexpr size_t vm = al(kh + (KHB > PARTB ? KHB : PARTB));
+  static constexpr size_t sdot = al(vm + (size_t)D * 4);
+  static constexpr size_t knorm = al(sdot + (size_t)NMAX * 4);
+  static constexpr size_t rtok = al(knorm + (size_t)NMAX * 4);
+  static constexpr size_t lse = al(rtok + (size_t)NMAX * 4);
+  static constexpr size_t zc = al(lse + PDMAX * 4);
+  static constexpr size_t nrel = al(zc + 3 * 2 * PDMAX * 4);
+  static constexpr size_t nmu = al(nrel + (size_t)2 * NMAX * 4);
+  static constexpr size_t nD = al(nmu + (size_t)2 * NMAX * 4);
+  static constexpr size_t nst = al(nD + (size_t)2 * NMAX * 4);
+  static constexpr size_t nsz = al(nst + (size_t)2 * NMAX * 2);
+  static constexpr size_t ndep = al(nsz + (size_t)2 * NMAX * 2);
+  static constexpr size_t ilist = al(ndep + (size_t)2 * NMAX * 2);
+  static constexpr size_t misc = al(ilist + (size_t)NMAX * 2);
+  static constexpr size_t total = al(misc + 16);
+  // phase-A scratch for the per-group value column sums lives in the weight array
+  static_assert((size_t)(WAVES * 64 / (D / 8)) * D * 4 <= (size_t)NMAX * PA * 4, "value-sum scratch");
+};
+
+// x = hi + lo (+ lo2) in bf16 pieces, each the round-to-nearest-even of the
+// remainder so far: |x - hi - lo| <= 2^-18 |x|, |x - hi - lo - lo2| <= 2^-27 |x|
+__device__ __forceinline__ void split8(float* x, kvc_bf16x8& hi, kvc_bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint32_t u = __float_as_uint(x[j]) & 0xffff0000u;
-    float r = x[j] - __uint_as_float(u);
-    hi[j] = __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
-    lo[j] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(r));
+    uint16_t b = f32_to_bf16_bits(x[j]);
+    x[j] -= bf16_bits_to_f32(b);
+    hi[j] = __builtin_bit_cast(__bf16, b);
+    uint16_t c = f32_to_bf16_bits(x[j]);
+    x[j] -= bf16_bits_to_f32(c);
+    lo[j] = __builtin_bit_cast(__bf16, c);
   }
 }
 
-template <class T, int D>
-__global__ __launch_bounds__(THREADS) void tree_kernel(TreeKArgs a) {
+// acc += x (8 fp32 of A, consumed) times b: three-piece split for bf16
+// operands (b exact in bf16), plain fp32 otherwise
+template <class T>
+__device__ __forceinline__ void mma_f32a(kvc_f32x16& acc, float* x, const kvcmf::Frag<T>& b) {
   using namespace kvcmf;
+  if constexpr (sizeof(T) == 2) {
+    Frag<uint16_t> hi, lo, lo2;
+    split8(x, hi.v, lo.v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lo2.v[j] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(x[j]));
+    mma(acc, hi, b);
+    mma(acc, lo, b);
+    mma(acc, lo2, b);
+  } else {
+    Frag<float> f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) f.v[q] = x[q];
+    mma(acc, f, b);
+  }
+}
+
+// 8 raw elements (loaded now, converted later, so that many loads are in flight)
+template <class T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *(const uint4*)p; }
+  __device__ __forceinline__ void zero() { u = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void get(float* o) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) { a = *(const float4*)p; b = *(const float4*)(p + 4); }
+  __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  __device__ __forceinline__ void get(float* o) const {
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+};
+
+// One 8-row block [i0, i0+8) of a node's two quadratic forms for lane rho:
+// num += c^T G c restricted to the block's rows, den += a^T G a likewise.
+__device__ __forceinline__ void qform_block(const float* Gm, int NG, const float* At, const float* rtok, int lane,
+                                            int i0, int st, int sz, float Z, float al, float ga, float& num,
+                                            float& den) {
+  float ci[8], ai[8], tc[8], ta[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int i = i0 + k;
+    float av = 0.f, cv = 0.f;
+    if (i >= st && i < st + sz) {
+      av = At[i * PA + lane];
+      cv = av - Z * fmaf(al, rtok[i], ga);
+    }
+    ai[k] = av;
+    ci[k] = cv;
+    tc[k] = 0.f;
+    ta[k] = 0.f;
+  }
+#pragma unroll 2
+  for (int j = st; j < st + sz; ++j) {
+    const float4 g0 = *(const float4*)(Gm + j * NG + i0), g1 = *(const float4*)(Gm + j * NG + i0 + 4);
+    const float aj = At[j * PA + lane];
+    const float cj = aj - Z * fmaf(al, rtok[j], ga);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      tc[k] = fmaf(g[k], cj, tc[k]);
+      ta[k] = fmaf(g[k], aj, ta[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    num = fmaf(ci[k], tc[k], num);
+    den = fmaf(ai[k], ta[k], den);
+  }
+}
+
+struct ItemDesc {
+  int64_t lh;
+  int s, t0, n;
+};
+
+// Work item w (unit-major over this size class) -> unit, sequence, slot.
+// pre[s] = number of this class's slots in sequences before s (pre[S] = total).
+__device__ __forceinline__ ItemDesc item_desc(const TreeKArgs& a, const int* pre, int64_t nsl, int64_t w) {
+  ItemDesc d;
+  d.lh = w / nsl;
+  const int rr = (int)(w - d.lh * nsl);
+  int s = 0;
+  while (rr >= pre[s + 1]) ++s;
+  d.s = s;
+  const int2 e = a.list[(int64_t)s * a.stride + (rr - pre[s])];
+  d.t0 = e.x;
+  d.n = e.y;
+  return d;
+}
+
+constexpr int MAX_SEQ = 256;  // sequences per call (prefix of the class counts lives in LDS)
+
+template <class T, int D, int NMAX, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void tree_kernel(TreeKArgs a) {
+  using namespace kvcmf;
+  using Lo = TreeLayout<NMAX, D, WAVES>;
+  constexpr int THREADS = WAVES * 64;
   constexpr int HD = D / 2;
   constexpr int KS = D / 16;
-  constexpr int NPV = 136;   // token stride of the transposed values (68 dwords: b128 reads conflict-free)
-  constexpr int NPA = 132;   // token stride of the transposed softmax weights
+  constexpr int KHS = D + 4;
+  constexpr int NG = Lo::NG;
+  constexpr int CH = HD / 8;              // 8-wide chunks per key half
+  constexpr int VC = D / 8;               // 8-wide chunks per value row
+  constexpr int VG = THREADS / VC;        // token groups for the value statistics
+  constexpr int VR = (NMAX + VG - 1) / VG;
+  constexpr int NPW = NB / WAVES;         // nodes per wave in a logit batch
   extern __shared__ __align__(16) char smem[];
-  const int nmax = a.nmax;
-  float* Kt = (float*)smem;                                        // [nmax][D] unrotated keys (fp32)
-  T* Vt = (T*)(Kt + (size_t)nmax * D);                             // [D][NPV] values, transposed
-  float* At = (float*)(Vt + (size_t)D * NPV);                      // [PDMAX][NPA] softmax weights
-  float* lse_s = At + (size_t)PDMAX * NPA;                         // [PDMAX]
-  float* knorm = lse_s + PDMAX;                                    // [nmax]
-  float* rtok = knorm + nmax;                                      // [nmax]
-  float* nrel = rtok + nmax;                                       // [2 nmax]
-  float* nD = nrel + 2 * nmax;                                     // [2 nmax]
-  float* nmu = nD + 2 * nmax;                                      // [2 nmax]
-  int16_t* nst = (int16_t*)(nmu + 2 * nmax);                       // [2 nmax]
-  int16_t* nsz = nst + 2 * nmax;                                   // [2 nmax]
-  float* scratch = (float*)(nsz + 2 * nmax);                       // [WAVES][2][D]
+  float* Kt = (float*)(smem + Lo::r1);     // [NMAX][D] inverse-rotated keys (phases A, B)
+  float* Gm = (float*)(smem + Lo::r1);     // [N32][NG] centred value Gram (phase C)
+  float* At = (float*)(smem + Lo::at);     // [NMAX][PA] softmax weights of the distortion rows
+  float* vsum = (float*)(smem + Lo::at);   // [VG][D] value column sums (phase A, before At)
+  float* KH = (float*)(smem + Lo::kh);     // [NB][KHS] prototype keys of one batch (phase B)
+                                           // then [NB][LGS] their logits
+  float* part = (float*)(smem + Lo::kh);   // [WAVES][3][2][PDMAX] quadratic-form partials (phase C)
+  float* LG = (float*)(smem + Lo::lg);     // [NB][LGS] prototype logits of one batch (over KH)
+  float* vm = (float*)(smem + Lo::vm);     // [D] value mean of the slot
+  float* sdot = (float*)(smem + Lo::sdot); // [NMAX] <v_i - m, m>
+  float* knorm = (float*)(smem + Lo::knorm);
+  float* rtok = (float*)(smem + Lo::rtok);
+  float* lse_s = (float*)(smem + Lo::lse);
+  float* zc = (float*)(smem + Lo::zc);     // [3][2][PDMAX] Z and a.s of the root and its children
+  float* nrel = (float*)(smem + Lo::nrel);
+  float* nmu = (float*)(smem + Lo::nmu);
+  float* nD = (float*)(smem + Lo::nD);
+  int16_t* nst = (int16_t*)(smem + Lo::nst);
+  int16_t* nsz = (int16_t*)(smem + Lo::nsz);
+  int16_t* ndep = (int16_t*)(smem + Lo::ndep);
+  int16_t* ilist = (int16_t*)(smem + Lo::ilist);
+  float* misc = (float*)(smem + Lo::misc);
 
-  int64_t b = blockIdx.x;
-  const int k = (int)(b % a.stride);
-  int64_t rest = b / a.stride;
-  const int s = (int)(rest % a.S);
-  const int64_t lh = rest / a.S;
-  if (k >= a.n_slots[s]) return;
-  const int l = (int)(lh / a.H), h = (int)(lh % a.H);
-  const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
-  const int t0 = ss[k], n = ss[k + 1] - ss[k];
-  const int n16 = (n + 15) & ~15;
-  const int m = 2 * n - 1;
-  const int64_t tok0 = a.cu[s] + t0;
-  const int64_t obase = lh * 2 * a.T + 2 * tok0;
-  const T* Kg = (const T*)a.K + (lh * a.T + tok0) * D;
-  const T* Vg = (const T*)a.V + (lh * a.T + tok0) * D;
+  __shared__ int pre[MAX_SEQ + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int unit = (s * a.Ly + l) * a.H + h;
-  const float sens = a.sens[unit];
-  const T* Qu = (const T*)a.Qp + ((((int64_t)s * a.Ly + l) * a.H * a.G + (int64_t)h * a.G) * a.P) * D;
+  const int pd = a.pd;
+  if (tid == 0) {
+    int acc = 0;
+    pre[0] = 0;
+    for (int s = 0; s < a.S; ++s) pre[s + 1] = (acc += a.count[s]);
+  }
+  __syncthreads();
+  const int64_t nsl = pre[a.S];
+  const int64_t nitems = (int64_t)a.Ly * a.H * nsl;
+  ItemDesc nxt{};
+  if ((int64_t)blockIdx.x < nitems) nxt = item_desc(a, pre, nsl, blockIdx.x);
 
-  // ---- stage transposed values (bf16; zero past the slot up to a 16 multiple),
-  // lse, r, node table; unrotated keys and key norms straight from HBM
-  for (int i = tid; i < n16 * (D / 8); i += THREADS) {
-    int r = i / (D / 8), c = (i % (D / 8)) * 8;
-    float x[8];
-    if (r < n) Load8<T>::f(Vg + (int64_t)r * D + c, x);
-    else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ElemIO<T>::st(Vt, (int64_t)(c + j) * NPV + r, x[j]);
-  }
-  for (int rho = tid; rho < a.pd; rho += THREADS) lse_s[rho] = a.lse[(int64_t)unit * a.G * a.P + (int64_t)rho * a.pstride];
-  for (int i = tid; i < n; i += THREADS) rtok[i] = a.rel[lh * a.T + tok0 + i];
-  for (int j = tid; j < m; j += THREADS) {
-    int cur = 0, st = 0, sz = n;
-    while (cur != j) {
-      int nl = (sz + 1) >> 1;
-      if (j < cur + 2 * nl) {
-        cur += 1;
-        sz = nl;
-      } else {
-        cur += 2 * nl;
-        st += nl;
-        sz -= nl;
-      }
-    }
-    nst[j] = (int16_t)st;
-    nsz[j] = (int16_t)sz;
-  }
-  for (int it = tid; it < n * HD; it += THREADS) {
-    int i = it / HD, p = it % HD;
-    float x0 = ElemIO<T>::ld(Kg, (int64_t)i * D + p), x1 = ElemIO<T>::ld(Kg, (int64_t)i * D + p + HD);
-    int64_t pos = t0 + i;
-    float c = a.rc[pos * HD + p], sn = a.rs[pos * HD + p];
-    Kt[(size_t)i * D + p] = x0 * c + x1 * sn;       // rotation by -theta
-    Kt[(size_t)i * D + p + HD] = x1 * c - x0 * sn;
-  }
-  for (int i = tid; i < n; i += THREADS) {
-    float q = 0.f;
-    for (int c = 0; c < D; c += 8) {
-      float x[8];
-      Load8<T>::f(Kg + (int64_t)i * D + c, x);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) q += x[j] * x[j];
-    }
-    knorm[i] = sqrtf(q);
-  }
-  // softmax weights of the distortion rows on MFMA (K Q^T), stored transposed;
-  // zero for tokens past the slot up to the 16 multiple
-  {
-    const int ntb = (n16 + 31) / 32, nrb = (a.pd + 31) / 32;
-    for (int tile = wave; tile < ntb * nrb; tile += WAVES) {
-      int tb = tile / nrb, rb = tile % nrb;
-      int tok = tb * 32 + (lane & 31), rho = rb * 32 + (lane & 31);
-      kvc_f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        int c = ks * 16 + 8 * (lane >> 5);
-        Frag<T> ka = tok < n ? load_frag<T>(Kg + (int64_t)tok * D + c) : zero_frag<T>();
-        Frag<T> qb = rho < a.pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
-        mma(acc, ka, qb);
-      }
-      float ls = rho < a.pd ? a.lse[(int64_t)unit * a.G * a.P + (int64_t)rho * a.pstride] : 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int ti = tb * 32 + acc_row(v, lane);
-        if (ti < n16 && rho < PDMAX)
-          At[rho * NPA + ti] = (ti < n && rho < a.pd) ? expf(acc[v] * a.c - ls) : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-  // ---- bottom-up value flow by height (a parent is the exact fp32 sum of its
-  // children; children of pre-order node j are j+1 and j + 2 ceil(sz/2))
-  for (int j = tid; j < m; j += THREADS)
-    if (nsz[j] == 1) nrel[j] = rtok[nst[j]];
-  __syncthreads();
-  for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
+  for (int64_t w = blockIdx.x; w < nitems; w += gridDim.x) {
+    const ItemDesc cur = nxt;
+    if (w + gridDim.x < nitems) nxt = item_desc(a, pre, nsl, w + gridDim.x);  // in flight during this slot
+    const int64_t lh = cur.lh;
+    const int s = cur.s, t0 = cur.t0, n = cur.n;
+    const int l = (int)(lh / a.H), h = (int)(lh % a.H);
+    const int m = 2 * n - 1, nint = n - 1;
+    const int n32 = (n + 31) & ~31;
+    const int64_t tok0 = a.cu[s] + t0;
+    const int64_t obase = lh * 2 * a.T + 2 * tok0;
+    const T* Kg = (const T*)a.K + (lh * a.T + tok0) * D;
+    const T* Vg = (const T*)a.V + (lh * a.T + tok0) * D;
+    const int unit = (s * a.Ly + l) * a.H + h;
+    const T* Qu = (const T*)a.Qp + ((((int64_t)s * a.Ly + l) * a.H * a.G + (int64_t)h * a.G) * a.P) * D;
+    const float* lse_g = a.lse + (int64_t)unit * a.G * a.P;
+
+    // ---- A: node table, token data, value statistics, softmax weights
     for (int j = tid; j < m; j += THREADS) {
-      int sz = nsz[j];
-      if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
-    }
-    __syncthreads();
-  }
-  float* kh = scratch + (size_t)wave * 2 * D;
-  float* vh = kh + D;
-  for (int j = wave; j < m; j += WAVES) {
-    const int st = nst[j], sz = nsz[j];
-    if (sz == 1) {
-      if (lane == 0) {
+      int cu = 0, st = 0, sz = n, dep = 0;
+      while (cu != j) {
+        int nl = (sz + 1) >> 1;
+        if (j < cu + 2 * nl) {
+          cu += 1;
+          sz = nl;
+        } else {
+          cu += 2 * nl;
+          st += nl;
+          sz -= nl;
+        }
+        ++dep;
+      }
+      nst[j] = (int16_t)st;
+      nsz[j] = (int16_t)sz;
+      ndep[j] = (int16_t)dep;
+      if (sz > 1) ilist[j - st] = (int16_t)j;  // internal nodes before j = j - (leaves left of st)
+      else {
         nD[j] = 0.f;
         nmu[j] = 1.f;
       }
-      continue;
     }
-    const float reln = nrel[j];
-    // prototype key and coherence: lane = rotate-half pair
-    float s0 = 0.f, s1 = 0.f, kn = 0.f;
-    if (lane < HD) {
-#pragma unroll 8
-      for (int i = st; i < st + sz; ++i) {
-        s0 += Kt[(size_t)i * D + lane];
-        s1 += Kt[(size_t)i * D + lane + HD];
-        kn += knorm[i];
+    for (int rho = tid; rho < PDMAX; rho += THREADS) lse_s[rho] = rho < pd ? lse_g[(int64_t)rho * a.pstride] : 0.f;
+    for (int i = tid; i < n; i += THREADS) rtok[i] = a.rel[lh * a.T + tok0 + i];
+    // inverse-rotated keys and key norms: one 8-pair chunk per item, all loads issued together
+#pragma unroll
+    for (int r = 0; r < (NMAX * CH + THREADS - 1) / THREADS; ++r) {
+      const int it = tid + r * THREADS;
+      const int i = it / CH, c = (it % CH) * 8;
+      const bool ok = i < n;
+      Raw8<T> k0, k1;
+      float4 c0, c1, s0, s1;
+      if (ok) {
+        k0.load(Kg + (int64_t)i * D + c);
+        k1.load(Kg + (int64_t)i * D + c + HD);
+        const int64_t pr = (int64_t)(t0 + i) * HD + c;
+        c0 = *(const float4*)(a.rc + pr);
+        c1 = *(const float4*)(a.rc + pr + 4);
+        s0 = *(const float4*)(a.rs + pr);
+        s1 = *(const float4*)(a.rs + pr + 4);
+      } else {
+        k0.zero();
+        k1.zero();
+        c0 = c1 = s0 = s1 = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      float x0[8], x1[8];
+      k0.get(x0);
+      k1.get(x1);
+      const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      float q = 0.f, y0[8], y1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        q += x0[e] * x0[e] + x1[e] * x1[e];
+        y0[e] = x0[e] * cs[e] + x1[e] * sn[e];   // rotation by -theta
+        y1[e] = x1[e] * cs[e] - x0[e] * sn[e];
+      }
+#pragma unroll
+      for (int o = 1; o < CH; o <<= 1) q += __shfl_xor(q, o, 64);
+      if (ok) {
+        float* d0 = Kt + (size_t)i * D + c;
+        *(float4*)d0 = make_float4(y0[0], y0[1], y0[2], y0[3]);
+        *(float4*)(d0 + 4) = make_float4(y0[4], y0[5], y0[6], y0[7]);
+        *(float4*)(d0 + HD) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+        *(float4*)(d0 + HD + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
+        if (c == 0) knorm[i] = sqrtf(q);
       }
     }
-    float nrm2 = wave_sum(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
-    kn = __shfl(kn, 0, 64);
-    float coh = kn > 0.f ? sqrtf(nrm2) / kn : 1.f;
-    float mu = fmaxf(1.f, (float)sz * coh);
-    if (lane < HD) {
-      float m0 = s0 / (float)sz, m1 = s1 / (float)sz;
-      int64_t prep = t0 + st + (sz - 1) / 2;
-      float c = a.rc[prep * HD + lane], sn = a.rs[prep * HD + lane];
-      kh[lane] = m0 * c - m1 * sn;
-      kh[lane + HD] = m1 * c + m0 * sn;
+    // value statistics: thread (group g, chunk vc) keeps tokens g, g+VG, ... in registers
+    const int vc = (tid % VC) * 8, vg = tid / VC;
+    Raw8<T> vr[VR];
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int i = vg + r * VG;
+      if (i < n) vr[r].load(Vg + (int64_t)i * D + vc);
+      else vr[r].zero();
     }
-    // prototype value: (1 - beta) r_i / rel + beta / n, lane = dimension
-    for (int dd = lane; dd < D; dd += 64) {
-      float acc = 0.f;
-#pragma unroll 8
-      for (int i = st; i < st + sz; ++i) {
-        float w = reln > 0.f ? (1.f - a.beta) * rtok[i] / reln + a.beta / (float)sz : 1.f / (float)sz;
-        acc += w * ElemIO<T>::ld(Vt, (int64_t)dd * NPV + i);
-      }
-      vh[dd] = acc;
-    }
-    __builtin_amdgcn_wave_barrier();  // kh/vh written by this wave's lanes, read below
-    // lane rho: Z and Z_hat
-    float z = 0.f, zh = 0.f;
-    if (lane < a.pd) {
-      for (int i = st; i < st + sz; ++i) z += At[lane * NPA + i];
-      const T* qr = Qu + (int64_t)lane * a.pstride * D;
-      float dot = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < D; c += 8) {
+    {
+      float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < VR; ++r) {
         float x[8];
-        Load8<T>::f(qr + c, x);
-        float4 k0 = *(const float4*)(kh + c), k1 = *(const float4*)(kh + c + 4);
-        dot += x[0] * k0.x + x[1] * k0.y + x[2] * k0.z + x[3] * k0.w + x[4] * k1.x + x[5] * k1.y +
-               x[6] * k1.z + x[7] * k1.w;
+        vr[r].get(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] += x[e];
       }
-      zh = mu * expf(dot * a.c - lse_s[lane]);
+      float* dst = vsum + (size_t)vg * D + vc;
+      *(float4*)dst = make_float4(cs[0], cs[1], cs[2], cs[3]);
+      *(float4*)(dst + 4) = make_float4(cs[4], cs[5], cs[6], cs[7]);
     }
-    // u^T = V_node^T A_node^T on MFMA: rows = value dims, columns = probe rows;
-    // lane keeps column rho = pb*32 + lane%32 and 16 of the 32 rows of a tile
-    float eVn = 0.f, eVd = 0.f;
-    const int kb0 = st >> 4, kb1 = (st + sz + 15) >> 4;
-#pragma unroll 1
-    for (int pb = 0; pb < (a.pd + 31) / 32; ++pb) {
-      const int rho = pb * 32 + (lane & 31);
-      const float zr = __shfl(z, rho, 64);
-      float n1 = 0.f, n2 = 0.f;
-#pragma unroll 1
-      for (int db = 0; db < D / 32; ++db) {
+    __syncthreads();
+    for (int dd = tid; dd < D; dd += THREADS) {
+      float acc = 0.f;
+#pragma unroll
+      for (int g = 0; g < VG; ++g) acc += vsum[g * D + dd];
+      vm[dd] = acc / (float)n;
+    }
+    __syncthreads();
+    {
+      float vmc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vmc[e] = vm[vc + e];
+#pragma unroll
+      for (int r = 0; r < VR; ++r) {
+        const int i = vg + r * VG;
+        float x[8], q = 0.f;
+        vr[r].get(x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q = fmaf(x[e] - vmc[e], vmc[e], q);
+#pragma unroll
+        for (int o = 1; o < VC; o <<= 1) q += __shfl_xor(q, o, 64);
+        if (i < n && (tid % VC) == 0) sdot[i] = q;
+      }
+      if (wave == 0) {
+        float q = 0.f;
+        for (int dd = lane; dd < D; dd += 64) q += vm[dd] * vm[dd];
+        q = wave_sum(q);
+        if (lane == 0) misc[0] = q;
+      }
+    }
+    // softmax weights of the distortion rows on MFMA (K Q^T); the value-sum
+    // scratch in the same array was consumed before the barrier above
+    {
+      const int ntb = n32 / 32, nrb = (pd + 31) / 32;
+      for (int tile = wave; tile < ntb * nrb; tile += WAVES) {
+        int tb = tile / nrb, rb = tile % nrb;
+        int tok = tb * 32 + (lane & 31), rho = rb * 32 + (lane & 31);
+        Frag<T> ka[KS], qb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          int c = ks * 16 + 8 * (lane >> 5);
+          ka[ks] = tok < n ? load_frag<T>(Kg + (int64_t)tok * D + c) : zero_frag<T>();
+          qb[ks] = rho < pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
+        }
         kvc_f32x16 acc = {};
-        for (int kb = kb0; kb < kb1; ++kb) {
-          const int t8 = kb * 16 + 8 * (lane >> 5);
-          Frag<T> va = load_frag<T>(Vt + (size_t)(db * 32 + (lane & 31)) * NPV + t8);
-          float w8[8];
-          float4 w0 = *(const float4*)(At + rho * NPA + t8), w1 = *(const float4*)(At + rho * NPA + t8 + 4);
-          w8[0] = w0.x; w8[1] = w0.y; w8[2] = w0.z; w8[3] = w0.w;
-          w8[4] = w1.x; w8[5] = w1.y; w8[6] = w1.z; w8[7] = w1.w;
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (t8 + q < st || t8 + q >= st + sz) w8[q] = 0.f;   // tokens outside the node
+        for (int ks = 0; ks < KS; ++ks) mma(acc, ka[ks], qb[ks]);
+        float ls = lse_s[rho];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          int ti = tb * 32 + acc_row(v, lane);
+          if (ti < n && rho < pd) At[ti * PA + rho] = expf(acc[v] * a.c - ls);
+        }
+      }
+      if (pd < PDMAX)
+        for (int it = tid; it < n * (PDMAX - pd); it += THREADS) At[(it / (PDMAX - pd)) * PA + pd + it % (PDMAX - pd)] = 0.f;
+    }
+    // bottom-up value flow by height (children of pre-order node j: j+1 and j + 2 ceil(sz/2))
+    for (int j = tid; j < m; j += THREADS)
+      if (nsz[j] == 1) nrel[j] = rtok[nst[j]];
+    __syncthreads();
+    for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
+      for (int j = tid; j < m; j += THREADS) {
+        int sz = nsz[j];
+        if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
+      }
+      __syncthreads();
+    }
+
+    // ---- B: prototype keys, multiplicity, attention-partition error
+    const int nrb = (pd + 31) / 32;
+    Frag<T> qf[KS];
+    if (wave < nrb) {
+      const int rho = wave * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        int c = ks * 16 + 8 * (lane >> 5);
+        qf[ks] = rho < pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
+      }
+    }
+    for (int q0 = 0; q0 < nint; q0 += NB) {
+      const int nb = min(NB, nint - q0);
+      float pc[NPW], ps[NPW];
+#pragma unroll
+      for (int u = 0; u < NPW; ++u) {  // rotation of every node this wave will form, loaded up front
+        const int qq = wave + u * WAVES;
+        pc[u] = ps[u] = 0.f;
+        if (qq < nb && lane < HD) {
+          const int j = ilist[q0 + qq];
+          const int64_t prep = t0 + nst[j] + (nsz[j] - 1) / 2;
+          pc[u] = a.rc[prep * HD + lane];
+          ps[u] = a.rs[prep * HD + lane];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NPW; ++u) {
+        const int qq = wave + u * WAVES;
+        float* kh = KH + qq * KHS;
+        if (qq >= nb) {
+          for (int c = lane; c < D; c += 64) kh[c] = 0.f;
+          continue;
+        }
+        const int j = ilist[q0 + qq];
+        const int st = nst[j], sz = nsz[j];
+        float s0 = 0.f, s1 = 0.f, kn = 0.f;
+        if (lane < HD) {
+#pragma unroll 4
+          for (int i = st; i < st + sz; ++i) {
+            s0 += Kt[(size_t)i * D + lane];
+            s1 += Kt[(size_t)i * D + lane + HD];
+            kn += knorm[i];
+          }
+        }
+        float nrm2 = wave_sum(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
+        kn = __shfl(kn, 0, 64);
+        float coh = kn > 0.f ? sqrtf(nrm2) / kn : 1.f;
+        float mu = fmaxf(1.f, (float)sz * coh);
+        if (lane == 0) nmu[j] = mu;
+        if (lane < HD) {
+          float m0 = s0 / (float)sz, m1 = s1 / (float)sz;
+          kh[lane] = m0 * pc[u] - m1 * ps[u];
+          kh[lane + HD] = m1 * pc[u] + m0 * ps[u];
+        }
+      }
+      __syncthreads();
+      kvc_f32x16 acc = {};
+      if (wave < nrb) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          int c = ks * 16 + 8 * (lane >> 5);
+          float x[8];
+          const float* kr = KH + (lane & 31) * KHS + c;
+          float4 x0 = *(const float4*)kr, x1 = *(const float4*)(kr + 4);
+          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+          x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+          mma_f32a<T>(acc, x, qf[ks]);
+        }
+      }
+      __syncthreads();  // every read of the prototype keys is done before the logits overwrite them
+      if (wave < nrb) {
+        const int rho = wave * 32 + (lane & 31);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) LG[acc_row(v, lane) * LGS + rho] = acc[v];
+      }
+      __syncthreads();
+      for (int qq = wave; qq < nb; qq += WAVES) {
+        const int j = ilist[q0 + qq];
+        const int st = nst[j], sz = nsz[j];
+        float z = 0.f, zh = 0.f;
+        if (lane < pd) {
+          for (int i = st; i < st + sz; ++i) z += At[i * PA + lane];
+          zh = nmu[j] * expf(LG[qq * LGS + lane] * a.c - lse_s[lane]);
+        }
+        float eAn = wave_sum(fabsf(zh - z)), eAd = wave_sum(z);
+        if (lane == 0) nD[j] = eAd > 0.f ? eAn / eAd : 0.f;
+      }
+      __syncthreads();  // the next batch's keys overwrite these logits
+    }
+
+    // ---- C: value-aggregate error
+    if (nint > 0) {
+      const int nt = n32 / 32;
+      for (int tile = wave; tile < nt * (nt + 1) / 2; tile += WAVES) {
+        int ti = 0, rem = tile;
+        while (rem >= nt - ti) {
+          rem -= nt - ti;
+          ++ti;
+        }
+        const int tj = ti + rem;
+        const int ra = ti * 32 + (lane & 31), rb = tj * 32 + (lane & 31);
+        Raw8<T> xa[KS], xb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = ks * 16 + 8 * (lane >> 5);
+          if (ra < n) xa[ks].load(Vg + (int64_t)ra * D + c);
+          else xa[ks].zero();
+          if (rb < n) xb[ks].load(Vg + (int64_t)rb * D + c);
+          else xb[ks].zero();
+        }
+        kvc_f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = ks * 16 + 8 * (lane >> 5);
+          float ya[8], yb[8];
+          xa[ks].get(ya);
+          xb[ks].get(yb);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            ya[q] = ra < n ? ya[q] - vm[c + q] : 0.f;
+            yb[q] = rb < n ? yb[q] - vm[c + q] : 0.f;
+          }
           if constexpr (sizeof(T) == 2) {
-            Frag<uint16_t> hi, lo;
-            split8(w8, hi.v, lo.v);
-            mma(acc, va, hi);
-            mma(acc, va, lo);
+            Frag<uint16_t> ha, la, hb, lb;
+            split8(ya, ha.v, la.v);
+            split8(yb, hb.v, lb.v);
+            mma(acc, ha, hb);
+            mma(acc, ha, lb);
+            mma(acc, la, hb);
+            mma(acc, la, lb);
           } else {
-            Frag<float> wf;
+            Frag<float> fa, fb;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) wf.v[q] = w8[q];
-            mma(acc, va, wf);
+            for (int q = 0; q < 8; ++q) {
+              fa.v[q] = ya[q];
+              fb.v[q] = yb[q];
+            }
+            mma(acc, fa, fb);
           }
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float u = acc[v];
-          float df = u - zr * vh[db * 32 + acc_row(v, lane)];
-          n1 += df * df;
-          n2 += u * u;
+          const int r = ti * 32 + acc_row(v, lane), cc = tj * 32 + (lane & 31);
+          Gm[r * NG + cc] = acc[v];
+          if (ti != tj) Gm[cc * NG + r] = acc[v];
         }
       }
-      n1 += __shfl_xor(n1, 32, 64);
-      n2 += __shfl_xor(n2, 32, 64);
-      if (lane < 32 && rho < a.pd) {
-        eVn += sqrtf(n1);
-        eVd += sqrtf(n2);
+      // the root (c = 0) and its children (c = 1, 2) are shared by every wave
+      const int nl0 = (n + 1) >> 1;
+      auto coop_j = [&](int c) { return c == 0 ? 0 : (c == 1 ? 1 : 2 * nl0); };
+      auto coop_ok = [&](int c) { return c == 0 ? n >= 2 : (c == 1 ? nl0 >= 2 : n - nl0 >= 2); };
+      if (wave < 3 && coop_ok(wave)) {
+        const int j = coop_j(wave);
+        const int st = nst[j], sz = nsz[j];
+        float z = 0.f, as = 0.f;
+        for (int i = st; i < st + sz; ++i) {
+          float av = At[i * PA + lane];
+          z += av;
+          as = fmaf(av, sdot[i], as);
+        }
+        zc[(wave * 2) * PDMAX + lane] = z;
+        zc[(wave * 2 + 1) * PDMAX + lane] = as;
       }
+      __syncthreads();
+      {
+        float pn[3] = {0.f, 0.f, 0.f}, pq[3] = {0.f, 0.f, 0.f};
+        int item = 0;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          if (!coop_ok(c)) continue;
+          const int j = coop_j(c);
+          const int st = nst[j], sz = nsz[j];
+          const float Z = zc[(c * 2) * PDMAX + lane];
+          const float rl = nrel[j];
+          const float al = rl > 0.f ? (1.f - a.beta) / rl : 0.f;
+          const float ga = rl > 0.f ? a.beta / (float)sz : 1.f / (float)sz;
+          const int b0 = st >> 3, b1 = (st + sz + 7) >> 3;
+          for (int b = b0; b < b1; ++b, ++item)
+            if (item % WAVES == wave) qform_block(Gm, NG, At, rtok, lane, b * 8, st, sz, Z, al, ga, pn[c], pq[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          part[((wave * 3 + c) * 2) * PDMAX + lane] = pn[c];
+          part[((wave * 3 + c) * 2 + 1) * PDMAX + lane] = pq[c];
+        }
+      }
+      __syncthreads();
+      const float mm = misc[0];
+      for (int q = wave; q < nint; q += WAVES) {
+        const int j = ilist[q];
+        const int st = nst[j], sz = nsz[j];
+        float num = 0.f, den = 0.f, Z, as;
+        if (ndep[j] <= 1) {
+          const int c = j == 0 ? 0 : (j == 1 ? 1 : 2);
+#pragma unroll
+          for (int w2 = 0; w2 < WAVES; ++w2) {
+            num += part[((w2 * 3 + c) * 2) * PDMAX + lane];
+            den += part[((w2 * 3 + c) * 2 + 1) * PDMAX + lane];
+          }
+          Z = zc[(c * 2) * PDMAX + lane];
+          as = zc[(c * 2 + 1) * PDMAX + lane];
+        } else {
+          Z = 0.f;
+          as = 0.f;
+          for (int i = st; i < st + sz; ++i) {
+            float av = At[i * PA + lane];
+            Z += av;
+            as = fmaf(av, sdot[i], as);
+          }
+          const float rl = nrel[j];
+          const float al = rl > 0.f ? (1.f - a.beta) / rl : 0.f;
+          const float ga = rl > 0.f ? a.beta / (float)sz : 1.f / (float)sz;
+          for (int b = st >> 3; b < (st + sz + 7) >> 3; ++b)
+            qform_block(Gm, NG, At, rtok, lane, b * 8, st, sz, Z, al, ga, num, den);
+        }
+        den = den + 2.f * Z * as + Z * Z * mm;
+        float eVn = wave_sum(lane < pd ? sqrtf(fmaxf(num, 0.f)) : 0.f);
+        float eVd = wave_sum(lane < pd ? sqrtf(fmaxf(den, 0.f)) : 0.f);
+        if (lane == 0) {
+          float eA = nD[j];
+          float eV = eVd > 0.f ? eVn / eVd : 0.f;
+          nD[j] = fminf(1.f, a.wA * eA + a.wV * eV);
+        }
+      }
+      __syncthreads();
     }
-    float eAn = lane < a.pd ? fabsf(zh - z) : 0.f, eAd = lane < a.pd ? z : 0.f;
-    eAn = wave_sum(eAn);
-    eAd = wave_sum(eAd);
-    eVn = wave_sum(eVn);
-    eVd = wave_sum(eVd);
-    if (lane == 0) {
-      float eA = eAd > 0.f ? eAn / eAd : 0.f;
-      float eV = eVd > 0.f ? eVn / eVd : 0.f;
-      nD[j] = fminf(1.f, a.wA * eA + a.wV * eV);
-      nmu[j] = mu;
+    // ---- outputs: node arrays and op utilities
+    const float sens = a.sens[unit];
+    for (int j = tid; j < m; j += THREADS) {
+      a.node_rel[obase + j] = nrel[j];
+      a.node_D[obase + j] = nD[j];
+      a.node_mu[obase + j] = nmu[j];
     }
-    __builtin_amdgcn_wave_barrier();
-  }
-  __syncthreads();
-  // ---- outputs: node arrays and op utilities
-  for (int j = tid; j < m; j += THREADS) {
-    a.node_rel[obase + j] = nrel[j];
-    a.node_D[obase + j] = nD[j];
-    a.node_mu[obase + j] = nmu[j];
-  }
-  for (int q = tid; q < 2 * n; q += THREADS) {
-    float u = 0.f;
-    uint8_t cst = 0;
-    if (q == 0) {
-      u = sens * (nrel[0] * (1.f - nD[0]));
-      cst = 1;
-    } else if (q - 1 < m && nsz[q - 1] > 1) {
-      int j = q - 1, lc = j + 1, rc = j + 2 * ((nsz[j] + 1) >> 1);
-      float gain = nrel[j] * nD[j] - (nrel[lc] * nD[lc] + nrel[rc] * nD[rc]);
-      u = sens * gain;
-      cst = 1;
+    for (int q = tid; q < 2 * n; q += THREADS) {
+      float u = 0.f;
+      uint8_t cst = 0;
+      if (q == 0) {
+        u = sens * (nrel[0] * (1.f - nD[0]));
+        cst = 1;
+      } else if (q - 1 < m && nsz[q - 1] > 1) {
+        int j = q - 1, lc = j + 1, rc = j + 2 * ((nsz[j] + 1) >> 1);
+        float gain = nrel[j] * nD[j] - (nrel[lc] * nD[lc] + nrel[rc] * nD[rc]);
+        u = sens * gain;
+        cst = 1;
+      }
+      a.op_util[obase + q] = u;
+      a.op_cost[obase + q] = cst;
     }
-    a.op_util[obase + q] = u;
-    a.op_cost[obase + q] = cst;
+    __syncthreads();
   }
 }
 
-size_t tree_smem(int nmax, int d, int elt) {
-  size_t b = (size_t)nmax * d * 4;                  // unrotated keys
-  b += (size_t)d * 136 * elt;                       // transposed values
-  b += (size_t)PDMAX * 132 * 4;                     // transposed softmax weights
-  b += PDMAX * 4 + (size_t)nmax * 4 * 2;            // lse, norms, r
-  b += (size_t)2 * nmax * 4 * 3 + (size_t)2 * nmax * 2 * 2;  // node values, starts, sizes
-  b += (size_t)WAVES * 2 * d * 4;                   // per-wave prototype scratch
-  return b;
+// Split each sequence's slots into two size classes (ids in slot order).
+__global__ __launch_bounds__(1024) void tree_bucket_kernel(const int32_t* slot_start, const int32_t* n_slots,
+                                                           int stride, int split, int2* lists,
+                                                           int32_t* counts, int S) {
+  __shared__ int wtot[2][16];
+  __shared__ int base[2];
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ns = n_slots[s];
+  const int32_t* ss = slot_start + (int64_t)s * (stride + 1);
+  if (tid < 2) base[tid] = 0;
+  __syncthreads();
+  for (int k0 = 0; k0 < ns; k0 += 1024) {
+    const int k = k0 + tid;
+    const bool valid = k < ns;
+    const int len = valid ? ss[k + 1] - ss[k] : 0;
+    const bool big = len > split;
+    uint64_t m[2] = {__ballot(valid && !big), __ballot(valid && big)};
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (lane == 0) {
+      wtot[0][wave] = __popcll(m[0]);
+      wtot[1][wave] = __popcll(m[1]);
+    }
+    __syncthreads();
+    if (valid) {
+      const int b = big ? 1 : 0;
+      int off = base[b];
+      for (int w2 = 0; w2 < wave; ++w2) off += wtot[b][w2];
+      off += __popcll(m[b] & below);
+      lists[((int64_t)b * S + s) * stride + off] = make_int2(ss[k], len);
+    }
+    __syncthreads();
+    if (tid < 2) {
+      int t = 0;
+      for (int w2 = 0; w2 < 16; ++w2) t += wtot[tid][w2];
+      base[tid] += t;
+    }
+    if (tid < 32) wtot[tid >> 4][tid & 15] = 0;
+    __syncthreads();
+  }
+  if (tid < 2) counts[tid * S + s] = base[tid];
 }
 
 int slot_nmax(const kvc_params* p) { return p->slot_len > 0 ? p->slot_len : p->slot_max; }
 
+template <class T, int D, int NMAX, int WAVES>
+int launch_trees(const TreeKArgs& a, int64_t bound, int ncu, hipStream_t st) {
+  using Lo = TreeLayout<NMAX, D, WAVES>;
+  static_assert(Lo::total <= 160 * 1024, "tree LDS");
+  auto kfn = tree_kernel<T, D, NMAX, WAVES>;
+  (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lo::total);
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kfn, WAVES * 64, Lo::total) != hipSuccess || per < 1) per = 1;
+  int64_t grid = (int64_t)ncu * per;
+  if (grid > bound) grid = bound;
+  if (grid < 1) return KVC_OK;
+  hipLaunchKernelGGL(kfn, dim3((unsigned)grid), dim3(WAVES * 64), Lo::total, st, a);
+  KVC_LAUNCH_CHECK("tree_build");
+  return KVC_OK;
+}
+
+template <class T, int D>
+int launch_both(TreeKArgs a, int2* lists, int32_t* counts, int64_t bound, int nmax, int ncu, hipStream_t st) {
+  a.list = lists;
+  a.count = counts;
+  int r = launch_trees<T, D, SMALL, 4>(a, bound, ncu, st);
+  if (r || nmax <= SMALL) return r;
+  a.list = lists + (int64_t)a.S * a.stride;
+  a.count = counts + a.S;
+  return launch_trees<T, D, 128, 8>(a, bound, ncu, st);
+}
+
 }  // namespace
 
 namespace kvc {
-size_t ws_trees(const kvc_shape*, const kvc_params*) { return 0; }
+// size-class lists [2][S][stride] of (start, length) and their counts [2][S] int32
+size_t ws_trees(const kvc_shape* sh, const kvc_params* p) {
+  if (p->token_mode) return 0;
+  int64_t stride = kvc_slot_stride(sh, p);
+  if (stride < 0) return 0;
+  Carver c(nullptr, 0);
+  c.take<int2>((size_t)2 * sh->n_seq * stride);
+  c.take<int32_t>((size_t)2 * sh->n_seq);
+  return c.off;
+}
 }  // namespace kvc
 
 extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V,
@@ -367,6 +796,11 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   KVC_REQUIRE(K && V && Qprobe && probe_lse && rel && head_sens && rope_cos && rope_sin && slot_start && n_slots &&
                   out && out->node_rel && out->node_D && out->node_mu && out->op_util && out->op_cost,
               KVC_E_INVAL, "kvc_build_trees: NULL pointer");
+  const int d = sh->head_dim;
+  KVC_REQUIRE(d == 64 || d == 128, KVC_E_UNSUPPORTED, "kvc_build_trees: head_dim must be 64 or 128");
+  const size_t need = kvc::ws_trees(sh, p);
+  KVC_REQUIRE(ws && ws_bytes >= need, KVC_E_WORKSPACE, "kvc_build_trees: workspace too small");
+  KVC_REQUIRE(sh->n_seq <= MAX_SEQ, KVC_E_UNSUPPORTED, "kvc_build_trees: at most 256 sequences per call");
   TreeKArgs a{};
   a.K = K;
   a.V = V;
@@ -377,7 +811,6 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   a.rc = rope_cos;
   a.rs = rope_sin;
   a.slot_start = slot_start;
-  a.n_slots = n_slots;
   a.cu = sh->cu_seqlens_d;
   a.S = sh->n_seq;
   a.Ly = sh->n_layers;
@@ -385,12 +818,11 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   a.G = sh->group;
   a.P = p->n_probe;
   a.stride = kvc_slot_stride(sh, p);
-  a.nmax = (slot_nmax(p) + 7) & ~7;  // LDS layout keeps every array 16-byte aligned
   int R = sh->group * p->n_probe;
   a.pd = p->n_dprobe < R ? p->n_dprobe : R;
   a.pstride = R / a.pd;
   a.T = sh->total_tokens;
-  a.c = 1.0f / sqrtf((float)sh->head_dim);
+  a.c = 1.0f / sqrtf((float)d);
   a.beta = p->value_base;
   a.wA = p->w_attn;
   a.wV = p->w_value;
@@ -399,28 +831,21 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   a.node_mu = out->node_mu;
   a.op_util = out->op_util;
   a.op_cost = out->op_cost;
-  int d = sh->head_dim;
-  int elt = sh->dtype == KVC_BF16 ? 2 : 4;
-  size_t sm = tree_smem(a.nmax, d, elt);
-  KVC_REQUIRE(sm <= 160 * 1024, KVC_E_UNSUPPORTED, "kvc_build_trees: slot too large for LDS at this dtype/head_dim");
-  int64_t nb = (int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride;
-  if (nb == 0) return KVC_OK;
-#define KVC_TREE_LAUNCH(TT, DD)                                                                             \
-  do {                                                                                                      \
-    (void)hipFuncSetAttribute((const void*)tree_kernel<TT, DD>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                              (int)sm);                                                                     \
-    hipLaunchKernelGGL((tree_kernel<TT, DD>), dim3((unsigned)nb), dim3(THREADS), sm, st, a);                 \
-  } while (0)
-  if (sh->dtype == KVC_BF16) {
-    if (d == 128) KVC_TREE_LAUNCH(uint16_t, 128);
-    else KVC_TREE_LAUNCH(uint16_t, 64);
-  } else {
-    if (d == 128) KVC_TREE_LAUNCH(float, 128);
-    else KVC_TREE_LAUNCH(float, 64);
-  }
-#undef KVC_TREE_LAUNCH
-  KVC_LAUNCH_CHECK("tree_build");
-  (void)ws;
-  (void)ws_bytes;
-  return KVC_OK;
+  const int64_t bound = (int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride;  // slot count bound
+  if (bound == 0) return KVC_OK;
+  kvc::Carver cv(ws, ws_bytes);
+  int2* lists = cv.take<int2>((size_t)2 * a.S * a.stride);
+  int32_t* counts = cv.take<int32_t>((size_t)2 * a.S);
+  hipLaunchKernelGGL(tree_bucket_kernel, dim3((unsigned)a.S), dim3(1024), 0, st, slot_start, n_slots, a.stride,
+                     SMALL, lists, counts, a.S);
+  KVC_LAUNCH_CHECK("tree_bucket");
+  int dev = 0, ncu = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+  const int nmax = slot_nmax(p);
+  if (sh->dtype == KVC_BF16)
+    return d == 128 ? launch_both<uint16_t, 128>(a, lists, counts, bound, nmax, ncu, st)
+                    : launch_both<uint16_t, 64>(a, lists, counts, bound, nmax, ncu, st);
+  return d == 128 ? launch_both<float, 128>(a, lists, counts, bound, nmax, ncu, st)
+                  : launch_both<float, 64>(a, lists, counts, bound, nmax, ncu, st);
 }
