@@ -16,10 +16,12 @@
 #include <cmath>
 
 #include "kvc_internal.h"
+#include "mfma_frag.h"
 
 namespace {
 
-constexpr int CHUNK = 256;
+constexpr int CHUNK = 256;   // entries per workgroup, fp32 caches (VALU kernel)
+constexpr int MCHUNK = 512;  // entries per workgroup, bf16 caches (MFMA kernel)
 constexpr int THREADS = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -33,6 +35,7 @@ struct DecArgs {
   const void* Vt;
   const void* Q;
   int S, Ly, H, G, t_valid, t_cap, nchunk;
+  int chunk;     // entries per partial (CHUNK or MCHUNK)
   float scale2;  // log2(e)/sqrt(d)
 };
 
@@ -197,6 +200,205 @@ __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, floa
   }
 }
 
+// bf16 caches: the logits of a 32-entry group come from one MFMA chain
+// (A = the G query heads padded to 32 rows, B = the entries' keys), each wave
+// runs an online softmax over rounds of 64 entries, and the values are
+// accumulated on the VALU with the probabilities broadcast through LDS.
+// Partial layout as the VALU kernel: [unit][chunk][G][D + 2].
+template <int D, int G>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 ? 2 : 3))) void decode_mfma_kernel(DecArgs a, float* part) {
+  using namespace kvcmf;
+  constexpr int KS = D / 16;          // MFMA steps per group (16 dims each)
+  constexpr int LPE = D / 8;          // lanes per entry in the value pass
+  constexpr int EPI = 64 / LPE;       // entries per value iteration
+  constexpr int VIT = 32 / EPI;       // value iterations per 32-entry round
+  constexpr int WE = MCHUNK / 4;      // entries per wave
+  constexpr int GP = G < 4 ? G : 4;   // heads held per logit lane
+  constexpr int PS = G <= 4 ? 4 : 8;  // row stride of the probability table
+  __shared__ __align__(16) uint16_t qs[G][D];
+  __shared__ __align__(16) float pw[4][32][PS];
+  __shared__ float mw[4][G], lw[4][G];
+  __shared__ __align__(16) float ow[4][G][D];
+  const int unit = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
+  const int s = unit / (a.Ly * a.H), lh = unit % (a.Ly * a.H);
+  const int l = lh / a.H, h = lh % a.H;
+  const int seg_idx = (s * a.Ly + l) * a.H + h;
+  const int64_t slen = a.seg_len[seg_idx];
+  const int nseg = min((int)((slen + MCHUNK - 1) / MCHUNK), a.nchunk - (a.t_cap + MCHUNK - 1) / MCHUNK);
+  const uint16_t* Kb;
+  const uint16_t* Vb;
+  const float* lm = nullptr;
+  int64_t n;
+  if (chunk < nseg) {
+    const int64_t off = a.seg_off[seg_idx], e0 = (int64_t)chunk * MCHUNK;
+    n = slen - e0 < MCHUNK ? slen - e0 : MCHUNK;
+    Kb = (const uint16_t*)a.K + (off + e0) * D;
+    Vb = (const uint16_t*)a.V + (off + e0) * D;
+    if (a.lnmu) lm = a.lnmu + off + e0;
+  } else {
+    const int64_t e0 = (int64_t)(chunk - nseg) * MCHUNK;
+    if (e0 >= a.t_valid) return;
+    n = a.t_valid - e0 < MCHUNK ? a.t_valid - e0 : MCHUNK;
+    const int64_t tb = (((int64_t)l * a.H + h) * a.S + s) * a.t_cap + e0;
+    Kb = (const uint16_t*)a.Kt + tb * D;
+    Vb = (const uint16_t*)a.Vt + tb * D;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int es = lane / LPE, sub = lane % LPE;
+  {
+    const uint16_t* Qb = (const uint16_t*)a.Q + (((int64_t)s * a.Ly + l) * a.H * G + (int64_t)h * G) * D;
+    for (int i = threadIdx.x; i < G * D / 8; i += THREADS) *(uint4*)&qs[0][i * 8] = *(const uint4*)(Qb + i * 8);
+  }
+  float m[GP], lsum[GP], acc[G][8];
+#pragma unroll
+  for (int j = 0; j < GP; ++j) {
+    m[j] = -INFINITY;
+    lsum[j] = 0.f;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
+  __syncthreads();
+  const int wbase = wave * WE;
+  // Rounds of 32 entries; many waves per SIMD hide the load latency. Loads
+  // past the chunk read its last entry (always valid) and are masked
+  // afterwards, so no load sits behind a branch.
+  const float* lmp = lm ? lm : (const float*)Kb;
+#pragma unroll 1
+  for (int rb = wbase; rb < wbase + WE; rb += 32) {
+    const int ek = rb + col, ekc = min(ek, (int)n - 1);
+    const float bv = lmp[ekc];  // unconditional, selected away without ln mu
+    uint4 kr[KS], vr[VIT];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kr[ks] = *(const uint4*)(Kb + (int64_t)ekc * D + half * (D / 2) + ks * 8);
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int e = min(rb + it * EPI + es, (int)n - 1);
+      vr[it] = *(const uint4*)(Vb + (int64_t)e * D + sub * 8);
+    }
+    const float bias = lm ? bv * LOG2E : 0.f;
+    // logits on MFMA: A = query heads (rows, zero past G), B = keys (columns);
+    // lane (half, col) receives heads 4*half + j of entry col; lane half
+    // `half` holds the dims [half*D/2, half*D/2 + D/2) in 8-wide steps
+    kvc_f32x16 sacc = {};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      Frag<uint16_t> qf, kf;
+      qf = col < G ? load_frag<uint16_t>(&qs[col < G ? col : 0][half * (D / 2) + ks * 8]) : zero_frag<uint16_t>();
+      kf.v = __builtin_bit_cast(kvc_bf16x8, kr[ks]);
+      mma(sacc, qf, kf);
+    }
+    // online softmax: new running max per head over the 32 lanes of a half
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      const bool ok = ek < n && 4 * half + j < G;
+      const float z = ok ? sacc[j] * a.scale2 + bias : -INFINITY;
+      float mx = z;
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mn = fmaxf(m[j], mx);
+      const float alpha = mn == -INFINITY ? 1.f : exp2f(m[j] - mn);
+      m[j] = mn;
+      const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+      lsum[j] = lsum[j] * alpha + p;
+      if (4 * half + j < G) pw[wave][col][4 * half + j] = p;
+      // every lane rescales its value sums of the heads this (half, j) holds
+#pragma unroll
+      for (int hh = 0; hh < (G + 3) / 4; ++hh) {
+        if (4 * hh + j >= G) continue;
+        const float f = __shfl(alpha, hh * 32, 64);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[4 * hh + j][q] *= f;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int el = it * EPI + es;
+      float vf[8];
+      const uint32_t w4[4] = {vr[it].x, vr[it].y, vr[it].z, vr[it].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        vf[2 * q] = __uint_as_float(w4[q] << 16);
+        vf[2 * q + 1] = __uint_as_float(w4[q] & 0xffff0000u);
+      }
+      float pg[G];
+      if constexpr (G >= 4) {
+#pragma unroll
+        for (int g4 = 0; g4 < G; g4 += 4) {
+          const float4 t = *(const float4*)&pw[wave][el][g4];
+          pg[g4] = t.x; pg[g4 + 1] = t.y; pg[g4 + 2] = t.z; pg[g4 + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) pg[g] = pw[wave][el][g];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[g][q] = fmaf(pg[g], vf[q], acc[g][q]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // the next round rewrites pw
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  // wave totals: probability sums over the 32 lanes of a half, value sums over
+  // the lanes that share `sub`
+#pragma unroll
+  for (int j = 0; j < GP; ++j) {
+    float t = lsum[j];
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) t += __shfl_xor(t, o, 64);
+    lsum[j] = t;
+  }
+  if (col == 0) {
+#pragma unroll
+    for (int j = 0; j < GP; ++j)
+      if (4 * half + j < G) {
+        mw[wave][4 * half + j] = m[j];
+        lw[wave][4 * half + j] = lsum[j];
+      }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x = acc[g][j];
+#pragma unroll
+      for (int o = LPE; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+      if (es == 0) ow[wave][g][sub * 8 + j] = x;
+    }
+  __syncthreads();
+  float* pb = part + ((int64_t)unit * a.nchunk + chunk) * G * (D + 2);
+  for (int i = threadIdx.x; i < G * D; i += THREADS) {
+    const int g = i / D, dd = i % D;
+    float mx = mw[0][g];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, mw[w][g]);
+    float o = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (mw[w][g] != -INFINITY) o += ow[w][g][dd] * exp2f(mw[w][g] - mx);
+    pb[g * (D + 2) + dd] = o;
+  }
+  if (threadIdx.x < G) {
+    const int g = threadIdx.x;
+    float mx = mw[0][g];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) mx = fmaxf(mx, mw[w][g]);
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (mw[w][g] != -INFINITY) t += lw[w][g] * exp2f(mw[w][g] - mx);
+    pb[g * (D + 2) + D] = mx;
+    pb[g * (D + 2) + D + 1] = t;
+  }
+}
+
 // Merge the chunks of every (s, l, h): one workgroup of G*D threads per unit;
 // o[s][l][h*G+g][d] normalized.
 template <int D>
@@ -206,11 +408,12 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(DecArgs a, const flo
   const int g = threadIdx.x / D, dd = threadIdx.x % D;
   if (g >= G) return;
   const int64_t slen = a.seg_len[unit];
-  const int nseg = min((int)((slen + CHUNK - 1) / CHUNK), a.nchunk - (a.t_cap + CHUNK - 1) / CHUNK);
-  const int ntail = (a.t_valid + CHUNK - 1) / CHUNK;
+  const int ck = a.chunk;
+  const int nseg = min((int)((slen + ck - 1) / ck), a.nchunk - (a.t_cap + ck - 1) / ck);
+  const int ntail = (a.t_valid + ck - 1) / ck;
   float m = -INFINITY, sum = 0.f, acc = 0.f;
   const int nc = nseg + ntail;
-  constexpr int BATCH = 8;
+  constexpr int BATCH = 16;
   for (int c0 = 0; c0 < nc; c0 += BATCH) {
     float mc[BATCH], lc[BATCH], oc[BATCH];
 #pragma unroll
@@ -249,8 +452,8 @@ __global__ void decode_layersum_kernel(DecArgs a, int D, const float* o, float* 
   x_out[(int64_t)s * x_stride + j] = x;
 }
 
-int nchunk_of(const kvc_ragged* c, int t_cap) {
-  return (c->max_seg + CHUNK - 1) / CHUNK + (t_cap + CHUNK - 1) / CHUNK;
+int nchunk_of(const kvc_ragged* c, int t_cap, int chunk) {
+  return (c->max_seg + chunk - 1) / chunk + (t_cap + chunk - 1) / chunk;
 }
 
 }  // namespace
@@ -259,7 +462,7 @@ extern "C" size_t kvc_decode_workspace(const kvc_ragged* c, int32_t group, int32
   if (!c || group < 1 || t_cap < 0 || c->max_seg < 0) return 0;
   int64_t units = (int64_t)c->n_seq * c->n_layers * c->n_kv_heads;
   kvc::Carver cv(nullptr, 0);
-  cv.take<float>((size_t)units * nchunk_of(c, t_cap) * group * (c->head_dim + 2));
+  cv.take<float>((size_t)units * nchunk_of(c, t_cap, CHUNK) * group * (c->head_dim + 2));  // bound for both kernels
   cv.take<float>((size_t)units * group * c->head_dim);
   return cv.off + 256;
 }
@@ -296,7 +499,8 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
   a.G = group;
   a.t_valid = t_valid;
   a.t_cap = t_cap;
-  a.nchunk = nchunk_of(c, t_cap);
+  a.chunk = c->dtype == KVC_BF16 ? MCHUNK : CHUNK;
+  a.nchunk = nchunk_of(c, t_cap, a.chunk);
   a.scale2 = 1.4426950408889634f / sqrtf((float)c->head_dim);
   int64_t units = (int64_t)a.S * a.Ly * a.H;
   kvc::Carver cv(ws, ws_bytes);
@@ -305,21 +509,23 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
   dim3 grid((unsigned)(units * a.nchunk));
   int d = c->head_dim;
 #define KVC_DEC(TT, DD, GG) hipLaunchKernelGGL((decode_partial_kernel<TT, DD, GG>), grid, dim3(THREADS), 0, st, a, part)
-#define KVC_DEC_G(TT, DD)                      \
+#define KVC_DECM(DD, GG) hipLaunchKernelGGL((decode_mfma_kernel<DD, GG>), grid, dim3(THREADS), 0, st, a, part)
+#define KVC_DEC_G(MAC, ...)                    \
   switch (group) {                             \
-    case 1: KVC_DEC(TT, DD, 1); break;         \
-    case 2: KVC_DEC(TT, DD, 2); break;         \
-    case 4: KVC_DEC(TT, DD, 4); break;         \
-    default: KVC_DEC(TT, DD, 8); break;        \
+    case 1: MAC(__VA_ARGS__, 1); break;        \
+    case 2: MAC(__VA_ARGS__, 2); break;        \
+    case 4: MAC(__VA_ARGS__, 4); break;        \
+    default: MAC(__VA_ARGS__, 8); break;       \
   }
   KVC_REQUIRE(group == 1 || group == 2 || group == 4 || group == 8, KVC_E_UNSUPPORTED,
               "kvc_decode_attn: group must be 1, 2, 4 or 8");
   if (c->dtype == KVC_BF16) {
-    if (d == 128) { KVC_DEC_G(uint16_t, 128); } else { KVC_DEC_G(uint16_t, 64); }
+    if (d == 128) { KVC_DEC_G(KVC_DECM, 128); } else { KVC_DEC_G(KVC_DECM, 64); }
   } else {
-    if (d == 128) { KVC_DEC_G(float, 128); } else { KVC_DEC_G(float, 64); }
+    if (d == 128) { KVC_DEC_G(KVC_DEC, float, 128); } else { KVC_DEC_G(KVC_DEC, float, 64); }
   }
 #undef KVC_DEC_G
+#undef KVC_DECM
 #undef KVC_DEC
   KVC_LAUNCH_CHECK("decode_partial");
   if (d == 128)

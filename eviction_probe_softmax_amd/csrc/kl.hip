@@ -4,8 +4,8 @@
 // D_KL(P_t || P^_t) between the next-token distributions of the full-cache
 // and the pruned-cache model, from logits with numerical stabilization.
 //
-// 1. rmsnorm_cast: x^ = x / sqrt(mean x^2 + 1e-6), cast to W's dtype; the
-//    full and compressed rows of pair p become rows 2p and 2p+1.
+// 1. rmsnorm_cast: x^ = x / sqrt(mean x^2 + 1e-6) in fp64, cast to W's
+//    dtype; the full and compressed rows of pair p become rows 2p and 2p+1.
 // 2. gemm_kl: y = x^ W^T on MFMA (W is [vocab][d_model], so both operands
 //    are contiguous along d_model). A workgroup owns 128 vocab columns and
 //    up to 128 rows; its epilogue reduces each pair over its columns to
@@ -25,6 +25,9 @@ constexpr int KC = 128;    // d_model chunk staged in LDS
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// The normalisation runs in fp64 and is rounded fp64 -> fp32 -> W's dtype:
+// the cast is a rounding decision, and taking it from a correctly rounded
+// fp64 value keeps it independent of the summation order.
 template <class T>
 __global__ __launch_bounds__(256) void rmsnorm_cast_kernel(const float* xf, const float* xc, int64_t n_pairs,
                                                            int dm, int64_t m_pad, T* out) {
@@ -35,16 +38,16 @@ __global__ __launch_bounds__(256) void rmsnorm_cast_kernel(const float* xf, cons
     return;
   }
   const float* x = ((row & 1) ? xc : xf) + (row >> 1) * dm;
-  __shared__ float red[8];
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < dm; i += blockDim.x) ss += x[i] * x[i];
-  ss = wave_sum(ss);
+  __shared__ double red[8];
+  double ss = 0.0;
+  for (int i = threadIdx.x; i < dm; i += blockDim.x) ss += (double)x[i] * (double)x[i];
+  ss = wave_sum_d(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  float tot = 0.f;
+  double tot = 0.0;
   for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
-  float r = 1.0f / sqrtf(tot / (float)dm + 1e-6f);
-  for (int i = threadIdx.x; i < dm; i += blockDim.x) ElemIO<T>::st(o, i, x[i] * r);
+  const double r = 1.0 / sqrt(tot / (double)dm + 1e-6);
+  for (int i = threadIdx.x; i < dm; i += blockDim.x) ElemIO<T>::st(o, i, (float)((double)x[i] * r));
 }
 
 template <class T> struct Frag;
