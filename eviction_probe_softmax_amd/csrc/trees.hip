@@ -71,14 +71,24 @@ struct TreeLayout {
   static constexpr int N32 = (NMAX + 31) & ~31;
   static constexpr int NG = N32 + 4;  // row stride of the Gram matrix
   static constexpr size_t KT = (size_t)NMAX * D * 4, GM = (size_t)N32 * NG * 4;
-  static constexpr size_t KHB = (size_t)NB * (D + 4) * 4, PARTB = (size_t)WAVES * 3 * 2 * PDMAX * 4;
+  // prototype keys of a batch: [NB][D + 8] as two bf16 pieces (hi, lo) for bf16 inputs, one fp32 row otherwise
+  static constexpr size_t KHB = (size_t)NB * (D + 8) * 4, PARTB = (size_t)WAVES * 3 * 2 * PDMAX * 4;
+  // Small slots stage the centred values in fp32 ([N32][D + 4]) over the keys
+  // and put the Gram matrix over the prototype keys; large slots keep the Gram
+  // matrix over the keys and centre on the fly.
+  static constexpr bool STAGED = NMAX <= SMALL;
+  static constexpr int VS = D + 4;    // row stride of the staged centred values
+  static constexpr size_t VSB = STAGED ? (size_t)N32 * VS * 4 : 0;
+  static constexpr size_t R1B = STAGED ? (KT > VSB ? KT : VSB) : (KT > GM ? KT : GM);
+  static constexpr size_t KHR = STAGED ? (KHB > GM ? KHB : GM) : (KHB > PARTB ? KHB : PARTB);
+  static_assert(!STAGED || PARTB <= R1B, "partials fit over the staged values");
   static constexpr size_t r1 = 0;
-  static constexpr size_t at = al(r1 + (KT > GM ? KT : GM));
+  static constexpr size_t at = al(r1 + R1B);
   static constexpr size_t kh = al(at + (size_t)NMAX * PA * 4);
   // the logits of a batch overwrite its prototype keys once the MFMA has read them
   static constexpr size_t lg = kh;
   static_assert((size_t)NB * LGS * 4 <= KHB, "logits fit over the prototype keys");
-  static constexpr size_t vm = al(kh + (KHB > PARTB ? KHB : PARTB));
+  static constexpr size_t vm = al(kh + KHR);
   static constexpr size_t sdot = al(vm + (size_t)D * 4);
   static constexpr size_t knorm = al(sdot + (size_t)NMAX * 4);
   static constexpr size_t rtok = al(knorm + (size_t)NMAX * 4);
@@ -97,8 +107,8 @@ struct TreeLayout {
   static_assert((size_t)(WAVES * 64 / (D / 8)) * D * 4 <= (size_t)NMAX * PA * 4, "value-sum scratch");
 };
 
-// x = hi + lo (+ lo2) in bf16 pieces, each the round-to-nearest-even of the
-// remainder so far: |x - hi - lo| <= 2^-18 |x|, |x - hi - lo - lo2| <= 2^-27 |x|
+// x = hi + lo in bf16 pieces, each the round-to-nearest-even of the
+// remainder so far: |x - hi - lo| <= 2^-18 |x|
 __device__ __forceinline__ void split8(float* x, kvc_bf16x8& hi, kvc_bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -108,27 +118,6 @@ __device__ __forceinline__ void split8(float* x, kvc_bf16x8& hi, kvc_bf16x8& lo)
     uint16_t c = f32_to_bf16_bits(x[j]);
     x[j] -= bf16_bits_to_f32(c);
     lo[j] = __builtin_bit_cast(__bf16, c);
-  }
-}
-
-// acc += x (8 fp32 of A, consumed) times b: three-piece split for bf16
-// operands (b exact in bf16), plain fp32 otherwise
-template <class T>
-__device__ __forceinline__ void mma_f32a(kvc_f32x16& acc, float* x, const kvcmf::Frag<T>& b) {
-  using namespace kvcmf;
-  if constexpr (sizeof(T) == 2) {
-    Frag<uint16_t> hi, lo, lo2;
-    split8(x, hi.v, lo.v);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lo2.v[j] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(x[j]));
-    mma(acc, hi, b);
-    mma(acc, lo, b);
-    mma(acc, lo2, b);
-  } else {
-    Frag<float> f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) f.v[q] = x[q];
-    mma(acc, f, b);
   }
 }
 
@@ -157,17 +146,20 @@ template <> struct Raw8<float> {
   }
 };
 
-// One 8-row block [i0, i0+8) of a node's two quadratic forms for lane rho:
-// num += c^T G c restricted to the block's rows, den += a^T G a likewise.
+// One 8-row block [i0, i0+8) of a node's two quadratic forms for lane rho,
+// using the symmetry of G: for every row i of the block, the columns j < i of
+// the node count twice and j = i once, so that summing over all blocks gives
+// num += c^T G c and den += a^T G a.
 __device__ __forceinline__ void qform_block(const float* Gm, int NG, const float* At, const float* rtok, int lane,
                                             int i0, int st, int sz, float Z, float al, float ga, float& num,
                                             float& den) {
   float ci[8], ai[8], tc[8], ta[8];
+  const int e = st + sz;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int i = i0 + k;
     float av = 0.f, cv = 0.f;
-    if (i >= st && i < st + sz) {
+    if (i >= st && i < e) {
       av = At[i * PA + lane];
       cv = av - Z * fmaf(al, rtok[i], ga);
     }
@@ -176,8 +168,10 @@ __device__ __forceinline__ void qform_block(const float* Gm, int NG, const float
     tc[k] = 0.f;
     ta[k] = 0.f;
   }
+  // columns before the block: every row of the block lies below them
+  const int jm = min(i0, e);
 #pragma unroll 2
-  for (int j = st; j < st + sz; ++j) {
+  for (int j = st; j < jm; ++j) {
     const float4 g0 = *(const float4*)(Gm + j * NG + i0), g1 = *(const float4*)(Gm + j * NG + i0 + 4);
     const float aj = At[j * PA + lane];
     const float cj = aj - Z * fmaf(al, rtok[j], ga);
@@ -188,11 +182,28 @@ __device__ __forceinline__ void qform_block(const float* Gm, int NG, const float
       ta[k] = fmaf(g[k], aj, ta[k]);
     }
   }
+  // the block's own columns: weight 1 below the diagonal, 1/2 on it
+  for (int j = max(i0, st); j < min(i0 + 8, e); ++j) {
+    const float4 g0 = *(const float4*)(Gm + j * NG + i0), g1 = *(const float4*)(Gm + j * NG + i0 + 4);
+    const float aj = At[j * PA + lane];
+    const float cj = aj - Z * fmaf(al, rtok[j], ga);
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const int jj = j - i0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = k > jj ? g[k] : (k == jj ? 0.5f * g[k] : 0.f);
+      tc[k] = fmaf(w, cj, tc[k]);
+      ta[k] = fmaf(w, aj, ta[k]);
+    }
+  }
+  float sn = 0.f, sd = 0.f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    num = fmaf(ci[k], tc[k], num);
-    den = fmaf(ai[k], ta[k], den);
+    sn = fmaf(ci[k], tc[k], sn);
+    sd = fmaf(ai[k], ta[k], sd);
   }
+  num = fmaf(2.f, sn, num);
+  den = fmaf(2.f, sd, den);
 }
 
 struct ItemDesc {
@@ -217,14 +228,14 @@ __device__ __forceinline__ ItemDesc item_desc(const TreeKArgs& a, const int* pre
 
 constexpr int MAX_SEQ = 256;  // sequences per call (prefix of the class counts lives in LDS)
 
-template <class T, int D, int NMAX, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2))) void tree_kernel(TreeKArgs a) {
+template <class T, int D, int NMAX, int WAVES, int OCC>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void tree_kernel(TreeKArgs a) {
   using namespace kvcmf;
   using Lo = TreeLayout<NMAX, D, WAVES>;
   constexpr int THREADS = WAVES * 64;
   constexpr int HD = D / 2;
   constexpr int KS = D / 16;
-  constexpr int KHS = D + 4;
+  constexpr int KHS = D + 8;                // row stride of the prototype-key pieces (elements)
   constexpr int NG = Lo::NG;
   constexpr int CH = HD / 8;              // 8-wide chunks per key half
   constexpr int VC = D / 8;               // 8-wide chunks per value row
@@ -232,13 +243,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   constexpr int VR = (NMAX + VG - 1) / VG;
   constexpr int NPW = NB / WAVES;         // nodes per wave in a logit batch
   extern __shared__ __align__(16) char smem[];
+  constexpr bool STAGED = Lo::STAGED;
   float* Kt = (float*)(smem + Lo::r1);     // [NMAX][D] inverse-rotated keys (phases A, B)
-  float* Gm = (float*)(smem + Lo::r1);     // [N32][NG] centred value Gram (phase C)
+  float* Vc = (float*)(smem + Lo::r1);     // [N32][VS] centred values (phase C, small slots)
+  float* Gm = (float*)(smem + (STAGED ? Lo::kh : Lo::r1));  // [N32][NG] centred value Gram (phase C)
   float* At = (float*)(smem + Lo::at);     // [NMAX][PA] softmax weights of the distortion rows
   float* vsum = (float*)(smem + Lo::at);   // [VG][D] value column sums (phase A, before At)
-  float* KH = (float*)(smem + Lo::kh);     // [NB][KHS] prototype keys of one batch (phase B)
+  float* KH = (float*)(smem + Lo::kh);     // [NB][KHS] fp32 prototype keys of one batch (fp32 inputs)
+  uint16_t* KHh = (uint16_t*)(smem + Lo::kh);          // [NB][KHS] hi bf16 pieces (bf16 inputs)
+  uint16_t* KHl = KHh + (size_t)NB * KHS;               // [NB][KHS] lo bf16 pieces
                                            // then [NB][LGS] their logits
-  float* part = (float*)(smem + Lo::kh);   // [WAVES][3][2][PDMAX] quadratic-form partials (phase C)
+  float* part = (float*)(smem + (STAGED ? Lo::r1 : Lo::kh));  // [WAVES][3][2][PDMAX] quadratic-form partials (C)
   float* LG = (float*)(smem + Lo::lg);     // [NB][LGS] prototype logits of one batch (over KH)
   float* vm = (float*)(smem + Lo::vm);     // [D] value mean of the slot
   float* sdot = (float*)(smem + Lo::sdot); // [NMAX] <v_i - m, m>
@@ -266,12 +281,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
   __syncthreads();
   const int64_t nsl = pre[a.S];
   const int64_t nitems = (int64_t)a.Ly * a.H * nsl;
+  // a contiguous range of items per workgroup: neighbouring slots of one unit
+  // share their probe rows and sit next to each other in HBM
+  const int64_t wb = (int64_t)blockIdx.x * nitems / gridDim.x, we = (int64_t)(blockIdx.x + 1) * nitems / gridDim.x;
   ItemDesc nxt{};
-  if ((int64_t)blockIdx.x < nitems) nxt = item_desc(a, pre, nsl, blockIdx.x);
+  if (wb < we) nxt = item_desc(a, pre, nsl, wb);
 
-  for (int64_t w = blockIdx.x; w < nitems; w += gridDim.x) {
+  for (int64_t w = wb; w < we; ++w) {
     const ItemDesc cur = nxt;
-    if (w + gridDim.x < nitems) nxt = item_desc(a, pre, nsl, w + gridDim.x);  // in flight during this slot
+    if (w + 1 < we) nxt = item_desc(a, pre, nsl, w + 1);  // in flight during this slot
     const int64_t lh = cur.lh;
     const int s = cur.s, t0 = cur.t0, n = cur.n;
     const int l = (int)(lh / a.H), h = (int)(lh % a.H);
@@ -414,16 +432,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
       for (int tile = wave; tile < ntb * nrb; tile += WAVES) {
         int tb = tile / nrb, rb = tile % nrb;
         int tok = tb * 32 + (lane & 31), rho = rb * 32 + (lane & 31);
-        Frag<T> ka[KS], qb[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          int c = ks * 16 + 8 * (lane >> 5);
-          ka[ks] = tok < n ? load_frag<T>(Kg + (int64_t)tok * D + c) : zero_frag<T>();
-          qb[ks] = rho < pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
-        }
         kvc_f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma(acc, ka[ks], qb[ks]);
+        for (int k0 = 0; k0 < KS; k0 += KS / 2) {  // half the steps' loads in flight at a time
+          Frag<T> ka[KS / 2], qb[KS / 2];
+#pragma unroll
+          for (int u = 0; u < KS / 2; ++u) {
+            int c = (k0 + u) * 16 + 8 * (lane >> 5);
+            ka[u] = tok < n ? load_frag<T>(Kg + (int64_t)tok * D + c) : zero_frag<T>();
+            qb[u] = rho < pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
+          }
+#pragma unroll
+          for (int u = 0; u < KS / 2; ++u) mma(acc, ka[u], qb[u]);
+        }
         float ls = lse_s[rho];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -448,15 +469,6 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 
     // ---- B: prototype keys, multiplicity, attention-partition error
     const int nrb = (pd + 31) / 32;
-    Frag<T> qf[KS];
-    if (wave < nrb) {
-      const int rho = wave * 32 + (lane & 31);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        int c = ks * 16 + 8 * (lane >> 5);
-        qf[ks] = rho < pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
-      }
-    }
     for (int q0 = 0; q0 < nint; q0 += NB) {
       const int nb = min(NB, nint - q0);
       float pc[NPW], ps[NPW];
@@ -474,9 +486,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int u = 0; u < NPW; ++u) {
         const int qq = wave + u * WAVES;
-        float* kh = KH + qq * KHS;
         if (qq >= nb) {
-          for (int c = lane; c < D; c += 64) kh[c] = 0.f;
+          for (int c = lane; c < D; c += 64) {
+            if constexpr (sizeof(T) == 2) KHh[qq * KHS + c] = KHl[qq * KHS + c] = 0;
+            else KH[qq * KHS + c] = 0.f;
+          }
           continue;
         }
         const int j = ilist[q0 + qq];
@@ -497,22 +511,45 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
         if (lane == 0) nmu[j] = mu;
         if (lane < HD) {
           float m0 = s0 / (float)sz, m1 = s1 / (float)sz;
-          kh[lane] = m0 * pc[u] - m1 * ps[u];
-          kh[lane + HD] = m1 * pc[u] + m0 * ps[u];
+          const float k0 = m0 * pc[u] - m1 * ps[u], k1 = m1 * pc[u] + m0 * ps[u];
+          if constexpr (sizeof(T) == 2) {
+            // k^ = hi + lo with |k^ - hi - lo| <= 2^-18 |k^|; the queries are exact in bf16
+            const uint16_t h0 = f32_to_bf16_bits(k0), h1 = f32_to_bf16_bits(k1);
+            KHh[qq * KHS + lane] = h0;
+            KHh[qq * KHS + lane + HD] = h1;
+            KHl[qq * KHS + lane] = f32_to_bf16_bits(k0 - bf16_bits_to_f32(h0));
+            KHl[qq * KHS + lane + HD] = f32_to_bf16_bits(k1 - bf16_bits_to_f32(h1));
+          } else {
+            KH[qq * KHS + lane] = k0;
+            KH[qq * KHS + lane + HD] = k1;
+          }
         }
       }
       __syncthreads();
       kvc_f32x16 acc = {};
       if (wave < nrb) {
+        const int rho = wave * 32 + (lane & 31);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          int c = ks * 16 + 8 * (lane >> 5);
-          float x[8];
-          const float* kr = KH + (lane & 31) * KHS + c;
-          float4 x0 = *(const float4*)kr, x1 = *(const float4*)(kr + 4);
-          x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-          x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-          mma_f32a<T>(acc, x, qf[ks]);
+        for (int k0 = 0; k0 < KS; k0 += KS / 2) {
+          Frag<T> qf[KS / 2];
+#pragma unroll
+          for (int u = 0; u < KS / 2; ++u) {
+            int c = (k0 + u) * 16 + 8 * (lane >> 5);
+            qf[u] = rho < pd ? load_frag<T>(Qu + (int64_t)rho * a.pstride * D + c) : zero_frag<T>();
+          }
+#pragma unroll
+          for (int u = 0; u < KS / 2; ++u) {
+            int c = (k0 + u) * 16 + 8 * (lane >> 5);
+            if constexpr (sizeof(T) == 2) {
+              Frag<uint16_t> hi = load_frag<uint16_t>(KHh + (lane & 31) * KHS + c);
+              Frag<uint16_t> lo = load_frag<uint16_t>(KHl + (lane & 31) * KHS + c);
+              mma(acc, hi, qf[u]);
+              mma(acc, lo, qf[u]);
+            } else {
+              Frag<T> x = load_frag<T>(KH + (lane & 31) * KHS + c);
+              mma(acc, x, qf[u]);
+            }
+          }
         }
       }
       __syncthreads();  // every read of the prototype keys is done before the logits overwrite them
@@ -539,6 +576,52 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
     // ---- C: value-aggregate error
     if (nint > 0) {
       const int nt = n32 / 32;
+      if constexpr (STAGED) {
+        // centred values in fp32 (zero rows past the slot), then the Gram
+        // tiles on the fp32 MFMA straight from LDS
+        constexpr int VC8 = D / 8;
+#pragma unroll
+        for (int r = 0; r < (Lo::N32 * VC8 + THREADS - 1) / THREADS; ++r) {
+          const int it = tid + r * THREADS;
+          const int i = it / VC8, c = (it % VC8) * 8;
+          if (i < n32) {
+            float x[8];
+            if (i < n) {
+              Raw8<T> v;
+              v.load(Vg + (int64_t)i * D + c);
+              v.get(x);
+#pragma unroll
+              for (int q = 0; q < 8; ++q) x[q] -= vm[c + q];
+            } else {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) x[q] = 0.f;
+            }
+            float* d0 = Vc + i * Lo::VS + c;
+            *(float4*)d0 = make_float4(x[0], x[1], x[2], x[3]);
+            *(float4*)(d0 + 4) = make_float4(x[4], x[5], x[6], x[7]);
+          }
+        }
+        __syncthreads();
+        for (int tile = wave; tile < nt * (nt + 1) / 2; tile += WAVES) {
+          int ti = 0, rem = tile;
+          while (rem >= nt - ti) {
+            rem -= nt - ti;
+            ++ti;
+          }
+          const int tj = ti + rem;
+          const float* pa = Vc + (ti * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
+          const float* pb = Vc + (tj * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
+          kvc_f32x16 acc = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma(acc, load_frag<float>(pa + ks * 16), load_frag<float>(pb + ks * 16));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = ti * 32 + acc_row(v, lane), cc = tj * 32 + (lane & 31);
+            Gm[r * NG + cc] = acc[v];
+            if (ti != tj) Gm[cc * NG + r] = acc[v];
+          }
+        }
+      } else
       for (int tile = wave; tile < nt * (nt + 1) / 2; tile += WAVES) {
         int ti = 0, rem = tile;
         while (rem >= nt - ti) {
@@ -547,22 +630,24 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
         }
         const int tj = ti + rem;
         const int ra = ti * 32 + (lane & 31), rb = tj * 32 + (lane & 31);
-        Raw8<T> xa[KS], xb[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = ks * 16 + 8 * (lane >> 5);
-          if (ra < n) xa[ks].load(Vg + (int64_t)ra * D + c);
-          else xa[ks].zero();
-          if (rb < n) xb[ks].load(Vg + (int64_t)rb * D + c);
-          else xb[ks].zero();
-        }
         kvc_f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int c = ks * 16 + 8 * (lane >> 5);
+        for (int k0 = 0; k0 < KS; k0 += KS / 2) {  // half the steps' loads in flight at a time
+        Raw8<T> xa[KS / 2], xb[KS / 2];
+#pragma unroll
+        for (int u = 0; u < KS / 2; ++u) {
+          const int c = (k0 + u) * 16 + 8 * (lane >> 5);
+          if (ra < n) xa[u].load(Vg + (int64_t)ra * D + c);
+          else xa[u].zero();
+          if (rb < n) xb[u].load(Vg + (int64_t)rb * D + c);
+          else xb[u].zero();
+        }
+#pragma unroll
+        for (int u = 0; u < KS / 2; ++u) {
+          const int c = (k0 + u) * 16 + 8 * (lane >> 5);
           float ya[8], yb[8];
-          xa[ks].get(ya);
-          xb[ks].get(yb);
+          xa[u].get(ya);
+          xb[u].get(yb);
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             ya[q] = ra < n ? ya[q] - vm[c + q] : 0.f;
@@ -585,6 +670,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
             }
             mma(acc, fa, fb);
           }
+        }
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -742,11 +828,11 @@ __global__ __launch_bounds__(1024) void tree_bucket_kernel(const int32_t* slot_s
 
 int slot_nmax(const kvc_params* p) { return p->slot_len > 0 ? p->slot_len : p->slot_max; }
 
-template <class T, int D, int NMAX, int WAVES>
+template <class T, int D, int NMAX, int WAVES, int OCC>
 int launch_trees(const TreeKArgs& a, int64_t bound, int ncu, hipStream_t st) {
   using Lo = TreeLayout<NMAX, D, WAVES>;
   static_assert(Lo::total <= 160 * 1024, "tree LDS");
-  auto kfn = tree_kernel<T, D, NMAX, WAVES>;
+  auto kfn = tree_kernel<T, D, NMAX, WAVES, OCC>;
   (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Lo::total);
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kfn, WAVES * 64, Lo::total) != hipSuccess || per < 1) per = 1;
@@ -762,11 +848,12 @@ template <class T, int D>
 int launch_both(TreeKArgs a, int2* lists, int32_t* counts, int64_t bound, int nmax, int ncu, hipStream_t st) {
   a.list = lists;
   a.count = counts;
-  int r = launch_trees<T, D, SMALL, 4>(a, bound, ncu, st);
+  // small slots: two 8-wave workgroups per CU (4 waves per SIMD); large: one
+  int r = launch_trees<T, D, SMALL, 8, 4>(a, bound, ncu, st);
   if (r || nmax <= SMALL) return r;
   a.list = lists + (int64_t)a.S * a.stride;
   a.count = counts + a.S;
-  return launch_trees<T, D, 128, 8>(a, bound, ncu, st);
+  return launch_trees<T, D, 128, 8, 2>(a, bound, ncu, st);
 }
 
 }  // namespace
