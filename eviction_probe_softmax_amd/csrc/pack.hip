@@ -20,6 +20,7 @@
 #include <cmath>
 
 #include "kvc_internal.h"
+#include "mfma_frag.h"
 
 namespace {
 
@@ -176,13 +177,23 @@ __global__ void write_tokens_kernel(PackArgs a, const int64_t* off) {
   copy_row<T, D>(a, i, dst, (int32_t)p, lane, 16);
 }
 
-// one wave per slot: frontier in pre-order, leaves copied, prototypes built
+// One workgroup per (unit, slot). Every node decides in parallel whether it
+// is on the frontier (its creator op taken, its own Split not taken; the
+// root's creator is the Add); a block scan gives the frontier in pre-order,
+// which is position order. Then 16-byte pieces of the output rows are spread
+// over the threads: leaves are copied, prototype keys (8 rotate-half pairs a
+// piece) and values (8 dims a piece) are averaged over the node's tokens.
+constexpr int WS_THREADS = 256;  // >= 2 * 128 - 1 nodes of the largest slot
+
 template <class T, int D>
-__global__ __launch_bounds__(64) void write_slots_kernel(PackArgs a, const int64_t* off) {
+__global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, const int64_t* off) {
   constexpr int HD = D / 2;
-  __shared__ int fr_node[256], fr_st[256], fr_sz[256];
-  __shared__ int nfr;
-  const int lane = threadIdx.x;
+  constexpr int KP = HD / 8;       // key pieces (8 rotate-half pairs each)
+  constexpr int VP = D / 8;        // value pieces (8 dims each)
+  constexpr int CPN = KP + VP;
+  __shared__ int16_t fnode[WS_THREADS], fst[WS_THREADS], fsz[WS_THREADS];
+  __shared__ int wcnt[WS_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // block -> (unit lh, sequence s, slot k): grid is (Ly*H*S*stride)
   int64_t b = blockIdx.x;
   int k = (int)(b % a.stride);
@@ -196,71 +207,124 @@ __global__ __launch_bounds__(64) void write_slots_kernel(PackArgs a, const int64
   const int64_t obase = lh * 2 * a.T + 2 * tok0;      // op / node base
   const uint8_t* tk = a.taken + obase;
   if (!tk[0]) return;                                 // Add not taken: no entry
-  if (lane == 0) {
-    // pre-order walk of the frontier
-    int sj[20], sst[20], ssz[20], top = 0, m = 0;
-    sj[top] = 0; sst[top] = t0; ssz[top] = n; ++top;
-    while (top > 0) {
-      --top;
-      int j = sj[top], st = sst[top], sz = ssz[top];
-      if (sz > 1 && tk[1 + j]) {
-        int nl = (sz + 1) >> 1;
-        sj[top] = j + 2 * nl; sst[top] = st + nl; ssz[top] = sz - nl; ++top;   // right
-        sj[top] = j + 1; sst[top] = st; ssz[top] = nl; ++top;                 // left first
+  const int64_t dst0 = off[lh * a.T + tok0];
+  // frontier flags: one node per thread (pre-order walk from the root)
+  const int m = 2 * n - 1;
+  bool fl = false;
+  int st = 0, sz = n;
+  if (tid < m) {
+    int cur = 0, par = -1;
+    while (cur != tid) {
+      const int nl = (sz + 1) >> 1;
+      par = cur;
+      if (tid < cur + 2 * nl) {
+        cur += 1;
+        sz = nl;
       } else {
-        fr_node[m] = j;
-        fr_st[m] = st;
-        fr_sz[m] = sz;
-        ++m;
+        cur += 2 * nl;
+        st += nl;
+        sz -= nl;
       }
     }
-    nfr = m;
+    const int creator = par < 0 ? 0 : 1 + par;
+    fl = tk[creator] && !(sz > 1 && tk[1 + tid]);
+  }
+  const uint64_t bm = __ballot(fl);
+  if (lane == 0) wcnt[wave] = __popcll(bm);
+  __syncthreads();
+  int q = 0, nfr = 0;
+#pragma unroll
+  for (int w = 0; w < WS_THREADS / 64; ++w) {
+    q += w < wave ? wcnt[w] : 0;
+    nfr += wcnt[w];
+  }
+  if (fl) {
+    q += __popcll(bm & (lane == 0 ? 0ull : (~0ull >> (64 - lane))));
+    fnode[q] = (int16_t)tid;
+    fst[q] = (int16_t)st;
+    fsz[q] = (int16_t)sz;
   }
   __syncthreads();
-  const int64_t dst0 = off[lh * a.T + tok0];
   const T* Ku = (const T*)a.K + (lh * a.T + a.cu[s]) * D;
   const T* Vu = (const T*)a.V + (lh * a.T + a.cu[s]) * D;
   const float* ru = a.rel + lh * a.T + a.cu[s];
-  for (int q = 0; q < nfr; ++q) {
-    int64_t dst = dst0 + q;
-    if (dst >= a.capacity) break;
-    int j = fr_node[q], st = fr_st[q], sz = fr_sz[q];
-    if (sz == 1) {
-      copy_row<T, D>(a, lh * a.T + a.cu[s] + st, dst, st, lane, 64);
-      continue;
-    }
-    // prototype key: lane owns rotate-half pair (p, p + D/2)
-    const float rel_n = a.node_rel[obase + j];
-    const float mu = a.node_mu[obase + j];
+  for (int it = tid; it < nfr * CPN; it += WS_THREADS) {
+    const int f = it / CPN, c = it % CPN;
+    const int64_t dst = dst0 + f;
+    if (dst >= a.capacity) continue;
+    const int j = fnode[f], a0 = t0 + fst[f], nz = fsz[f];   // sequence positions [a0, a0 + nz)
     T* oK = (T*)a.oK + dst * D;
     T* oV = (T*)a.oV + dst * D;
-    for (int p = lane; p < HD; p += 64) {
-      float s0 = 0.f, s1 = 0.f;
-      for (int i = st; i < st + sz; ++i) {
-        float x0 = ElemIO<T>::ld(Ku, (int64_t)i * D + p), x1 = ElemIO<T>::ld(Ku, (int64_t)i * D + p + HD);
-        float c = a.rc[(int64_t)i * HD + p], sn = a.rs[(int64_t)i * HD + p];
-        s0 += x0 * c + x1 * sn;       // rotation by -theta
-        s1 += x1 * c - x0 * sn;
+    if (nz == 1) {  // leaf: bit copy of the token's 16-byte pieces
+      if (c < KP) {
+        *(uint4*)(oK + c * 8) = *(const uint4*)(Ku + (int64_t)a0 * D + c * 8);
+        *(uint4*)(oK + HD + c * 8) = *(const uint4*)(Ku + (int64_t)a0 * D + HD + c * 8);
+        if constexpr (sizeof(T) == 4) {
+          *(uint4*)(oK + c * 8 + 4) = *(const uint4*)(Ku + (int64_t)a0 * D + c * 8 + 4);
+          *(uint4*)(oK + HD + c * 8 + 4) = *(const uint4*)(Ku + (int64_t)a0 * D + HD + c * 8 + 4);
+        }
+      } else {
+        const int d0 = (c - KP) * 8;
+        *(uint4*)(oV + d0) = *(const uint4*)(Vu + (int64_t)a0 * D + d0);
+        if constexpr (sizeof(T) == 4) *(uint4*)(oV + d0 + 4) = *(const uint4*)(Vu + (int64_t)a0 * D + d0 + 4);
       }
-      float m0 = s0 / (float)sz, m1 = s1 / (float)sz;
-      int prep = st + (sz - 1) / 2;
-      float c = a.rc[(int64_t)prep * HD + p], sn = a.rs[(int64_t)prep * HD + p];
-      ElemIO<T>::st(oK, p, m0 * c - m1 * sn);
-      ElemIO<T>::st(oK, p + HD, m1 * c + m0 * sn);
+      continue;
     }
-    // prototype value: (1-beta) r_i/rel + beta/n weights (uniform if rel = 0)
-    for (int dd = lane; dd < D; dd += 64) {
-      float acc = 0.f;
-      for (int i = st; i < st + sz; ++i) {
-        float w = rel_n > 0.f ? (1.f - a.beta) * ru[i] / rel_n + a.beta / (float)sz : 1.f / (float)sz;
-        acc += w * ElemIO<T>::ld(Vu, (int64_t)i * D + dd);
+    if (c < KP) {
+      // prototype key: mean of the inverse-rotated keys, re-rotated at the representative position
+      const int p0 = c * 8;
+      float s0[8], s1[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s0[e] = s1[e] = 0.f;
+      for (int i = a0; i < a0 + nz; ++i) {
+        float x0[8], x1[8];
+        kvcmf::Load8<T>::f(Ku + (int64_t)i * D + p0, x0);
+        kvcmf::Load8<T>::f(Ku + (int64_t)i * D + HD + p0, x1);
+        const float4 ca = *(const float4*)(a.rc + (int64_t)i * HD + p0), cb = *(const float4*)(a.rc + (int64_t)i * HD + p0 + 4);
+        const float4 sa = *(const float4*)(a.rs + (int64_t)i * HD + p0), sb = *(const float4*)(a.rs + (int64_t)i * HD + p0 + 4);
+        const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+        const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          s0[e] += x0[e] * cs[e] + x1[e] * sn[e];   // rotation by -theta
+          s1[e] += x1[e] * cs[e] - x0[e] * sn[e];
+        }
       }
-      ElemIO<T>::st(oV, dd, acc);
+      const int64_t prep = a0 + (nz - 1) / 2;
+      const float4 ca = *(const float4*)(a.rc + prep * HD + p0), cb = *(const float4*)(a.rc + prep * HD + p0 + 4);
+      const float4 sa = *(const float4*)(a.rs + prep * HD + p0), sb = *(const float4*)(a.rs + prep * HD + p0 + 4);
+      const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
+      const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float m0 = s0[e] / (float)nz, m1 = s1[e] / (float)nz;
+        ElemIO<T>::st(oK, p0 + e, m0 * cs[e] - m1 * sn[e]);
+        ElemIO<T>::st(oK, p0 + HD + e, m1 * cs[e] + m0 * sn[e]);
+      }
+    } else {
+      // prototype value: (1 - beta) r_i / rel + beta / n weights (uniform if rel = 0)
+      const int d0 = (c - KP) * 8;
+      const float rel_n = a.node_rel[obase + j];
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int i = a0; i < a0 + nz; ++i) {
+        const float w = rel_n > 0.f ? (1.f - a.beta) * ru[i] / rel_n + a.beta / (float)nz : 1.f / (float)nz;
+        float x[8];
+        kvcmf::Load8<T>::f(Vu + (int64_t)i * D + d0, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ElemIO<T>::st(oV, d0 + e, acc[e]);
     }
-    if (lane == 0) {
-      a.olnmu[dst] = logf(mu);
-      a.opos[dst] = st + (sz - 1) / 2;
-    }
+  }
+  for (int f = tid; f < nfr; f += WS_THREADS) {
+    const int64_t dst = dst0 + f;
+    if (dst >= a.capacity) continue;
+    const int nz = fsz[f];
+    a.olnmu[dst] = nz == 1 ? 0.f : logf(a.node_mu[obase + fnode[f]]);
+    a.opos[dst] = t0 + fst[f] + (nz - 1) / 2;
   }
 }
 
@@ -359,11 +423,11 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
   if (!p->token_mode) {
     dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride));
     if (sh->dtype == KVC_BF16) {
-      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(64), 0, st, a, off);
-      else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(64), 0, st, a, off);
+      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(WS_THREADS), 0, st, a, off);
+      else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(WS_THREADS), 0, st, a, off);
     } else {
-      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<float, 128>), sg, dim3(64), 0, st, a, off);
-      else hipLaunchKernelGGL((write_slots_kernel<float, 64>), sg, dim3(64), 0, st, a, off);
+      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<float, 128>), sg, dim3(WS_THREADS), 0, st, a, off);
+      else hipLaunchKernelGGL((write_slots_kernel<float, 64>), sg, dim3(WS_THREADS), 0, st, a, off);
     }
     KVC_LAUNCH_CHECK("pack_slots");
   }
