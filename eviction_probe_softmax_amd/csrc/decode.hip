@@ -399,45 +399,55 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
   }
 }
 
-// Merge the chunks of every (s, l, h): one workgroup of G*D threads per unit;
-// o[s][l][h*G+g][d] normalized.
+// Merge the chunks of every (s, l, h, g): one workgroup of D threads per
+// (unit, head). The chunk statistics go to LDS first, the chunk weights
+// exp2(m_c - max) and 1 / sum follow from two block reductions, then every
+// thread sums its dimension over the chunks with all loads independent.
 template <int D>
-__global__ __launch_bounds__(1024) void decode_merge_kernel(DecArgs a, const float* part, float* o) {
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecArgs a, const float* part, float* o) {
+  extern __shared__ float ms[];            // [2][nchunk]: chunk max, then weight; chunk sum
+  __shared__ float red[D / 64];
   const int G = a.G;
-  const int unit = blockIdx.x;                         // (s*Ly + l)*H + h
-  const int g = threadIdx.x / D, dd = threadIdx.x % D;
-  if (g >= G) return;
+  const int unit = blockIdx.x / G, g = blockIdx.x % G;  // unit = (s*Ly + l)*H + h
+  const int tid = threadIdx.x;
+  float* mc = ms;
+  float* lc = ms + a.nchunk;
   const int64_t slen = a.seg_len[unit];
   const int ck = a.chunk;
   const int nseg = min((int)((slen + ck - 1) / ck), a.nchunk - (a.t_cap + ck - 1) / ck);
-  const int ntail = (a.t_valid + ck - 1) / ck;
-  float m = -INFINITY, sum = 0.f, acc = 0.f;
-  const int nc = nseg + ntail;
-  constexpr int BATCH = 16;
-  for (int c0 = 0; c0 < nc; c0 += BATCH) {
-    float mc[BATCH], lc[BATCH], oc[BATCH];
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      mc[q] = -INFINITY;
-      lc[q] = oc[q] = 0.f;
-      if (c0 + q < nc) {
-        const float* pb = part + (((int64_t)unit * a.nchunk + c0 + q) * G + g) * (D + 2);
-        mc[q] = pb[D];
-        lc[q] = pb[D + 1];
-        oc[q] = pb[dd];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      if (mc[q] == -INFINITY) continue;
-      float mn = fmaxf(m, mc[q]);
-      float f1 = exp2f(m - mn), f2 = exp2f(mc[q] - mn);
-      sum = sum * f1 + lc[q] * f2;
-      acc = acc * f1 + oc[q] * f2;
-      m = mn;
-    }
+  const int nc = nseg + (a.t_valid + ck - 1) / ck;
+  const int64_t cs = (int64_t)G * (D + 2);  // chunk stride
+  const float* pb = part + ((int64_t)unit * a.nchunk * G + g) * (D + 2);
+  float mx = -INFINITY;
+  for (int c = tid; c < nc; c += D) {
+    const float m = pb[c * cs + D];
+    mc[c] = m;
+    lc[c] = pb[c * cs + D + 1];
+    mx = fmaxf(mx, m);
   }
-  o[((int64_t)unit * G + g) * D + dd] = sum > 0.f ? acc / sum : 0.f;
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+  float sm = 0.f;
+  for (int c = tid; c < nc; c += D) {
+    const float w = mc[c] == -INFINITY ? 0.f : exp2f(mc[c] - mx);
+    mc[c] = w;
+    sm += lc[c] * w;
+  }
+  sm = wave_sum(sm);
+  if ((tid & 63) == 0) red[tid >> 6] = sm;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / 64; ++w) tot += red[w];
+  float acc = 0.f;
+#pragma unroll 8
+  for (int c = 0; c < nc; ++c) acc += pb[c * cs + tid] * mc[c];
+  o[((int64_t)unit * G + g) * D + tid] = tot > 0.f ? acc / tot : 0.f;
 }
 
 // x[s][j] = sum over layers (in order) of o[s][l][j], j < H*G*D
@@ -447,8 +457,10 @@ __global__ void decode_layersum_kernel(DecArgs a, int D, const float* o, float* 
   if (i >= (int64_t)a.S * HGD) return;
   int s = (int)(i / HGD);
   int64_t j = i % HGD;
+  const float* os = o + (int64_t)s * a.Ly * HGD + j;
   float x = 0.f;
-  for (int l = 0; l < a.Ly; ++l) x += o[((int64_t)s * a.Ly + l) * HGD + j];
+#pragma unroll 8
+  for (int l = 0; l < a.Ly; ++l) x += os[(int64_t)l * HGD];
   x_out[(int64_t)s * x_stride + j] = x;
 }
 
@@ -528,10 +540,11 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
 #undef KVC_DECM
 #undef KVC_DEC
   KVC_LAUNCH_CHECK("decode_partial");
+  const size_t msm = (size_t)2 * a.nchunk * sizeof(float);
   if (d == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((unsigned)units), dim3(group * 128), 0, st, a, part, obuf);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((unsigned)(units * group)), dim3(128), msm, st, a, part, obuf);
   else
-    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3((unsigned)units), dim3(group * 64), 0, st, a, part, obuf);
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3((unsigned)(units * group)), dim3(64), msm, st, a, part, obuf);
   KVC_LAUNCH_CHECK("decode_merge");
   int64_t nx = (int64_t)a.S * a.H * group * d;
   hipLaunchKernelGGL(decode_layersum_kernel, dim3(kvc_blocks(nx, 256)), dim3(256), 0, st, a, d, obuf, x_out, x_stride);
