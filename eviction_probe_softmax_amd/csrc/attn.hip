@@ -211,11 +211,11 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
       }
       if (mx == -INFINITY) continue;
       float mn = fmaxf(m[rb], mx);
-      float f = exp2f(m[rb] - mn);
+      float f = fast_exp2(m[rb] - mn);
       float s2 = 0.f, t2 = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float e = exp2f(x[v] - mn);
+        float e = fast_exp2(x[v] - mn);
         s2 += e;
         t2 += x[v] == -INFINITY ? 0.f : e * x[v];
       }
@@ -301,10 +301,11 @@ __global__ void rowcombine_kernel(AttnArgs a, const float* part, float2* rowstat
 }
 
 // ------------------------------------------------------------------ pass 2
-template <class T, int D>
-__global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, int mode, const float2* rowstat,
+template <class T, int D, int MODE>
+__global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float2* rowstat,
                                                           float* out0, float* feats, float* head_part,
                                                           const float* rel_in, float* rel_out) {
+  constexpr int mode = MODE;
   constexpr int KS = D / 16;
   extern __shared__ __align__(16) char smem[];
   Frag<T>* qf = (Frag<T>*)smem;
@@ -338,43 +339,94 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, int mode, c
   const int64_t ubase = ((int64_t)w.l * a.H + w.h) * a.T + w.tok0;
   const T* K = (const T*)a.K + ubase * D;
   float hs_num = 0.f, hs_den = 0.f;
+  // key blocks are double-buffered: the next block's keys (and, for the
+  // features, this block's values) load while this block is computed; past
+  // the end a lane reads the last key (masked by kvalid)
+  Frag<T> kf[KS];
+  {
+    const int64_t key = min(w.k0 + wave * 32 + (lane & 31), w.k1 - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(K + key * D + ks * 16 + 8 * (lane >> 5));
+  }
   for (int64_t kb = w.k0 + wave * 32; kb < w.k1; kb += WAVES * 32) {
     int64_t key = kb + (lane & 31);
     bool kvalid = key < w.k1;
+    const int64_t keyc = kvalid ? key : w.k1 - 1;
+    Frag<T> kn[KS];
+    {
+      const int64_t kk = min(kb + WAVES * 32 + (lane & 31), w.k1 - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kn[ks] = load_frag<T>(K + kk * D + ks * 16 + 8 * (lane >> 5));
+    }
+    Frag<T> vrow[MODE == 0 ? D / 16 : 1];
+    if constexpr (MODE == 0) {
+      const T* Vr = (const T*)a.V + (ubase + keyc) * D + (lane >> 5) * (D / 2);
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) vrow[j] = load_frag<T>(Vr + j * 8);
+    }
     float colsum = 0.f, hsum = 0.f;
     float mg[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) mg[g] = 0.f;
     if (kb <= maxlim) {
-      Frag<T> kf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = kvalid ? load_frag<T>(K + key * D + ks * 16 + 8 * (lane >> 5)) : zero_frag<T>();
-      for (int rb = 0; rb < nrb; ++rb) {
+      for (int rb = 0; rb < 8; ++rb) {
+        if (rb >= nrb) break;
         kvc_f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mma(acc, qf[(rb * KS + ks) * 64 + lane], kf[ks]);
-        // lane owns key `key`; register v holds query row rb*32 + acc_row(v)
+        // lane owns key `key`; register v holds query row rb*32 + acc_row(v),
+        // and registers 4q..4q+3 hold four consecutive rows
+        float rbs = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float part_g = 0.f;
+          const int row0 = rb * 32 + acc_row(q * 4, lane);
+          const float4 ls4 = *(const float4*)(lse_s + row0);
+          const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w};
+          float env[4] = {0.f, 0.f, 0.f, 0.f}, wv[4] = {1.f, 1.f, 1.f, 1.f};
+          int lmv[4] = {0x7fffffff, 0x7fffffff, 0x7fffffff, 0x7fffffff};
+          if constexpr (MODE == 0) {
+            const float4 e4 = *(const float4*)(ent_s + row0);
+            env[0] = e4.x; env[1] = e4.y; env[2] = e4.z; env[3] = e4.w;
+          } else {
+            const float4 w4 = *(const float4*)(w_s + row0);
+            wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+            const int4 l4 = *(const int4*)(lim_s + row0);
+            lmv[0] = l4.x; lmv[1] = l4.y; lmv[2] = l4.z; lmv[3] = l4.w;
+          }
 #pragma unroll
           for (int vv = 0; vv < 4; ++vv) {
             int v = q * 4 + vv;
-            int row = rb * 32 + acc_row(v, lane);
-            bool ok = kvalid && key <= lim_s[row];
-            float p = ok ? exp2f(acc[v] * a.scale2 - lse_s[row]) : 0.f;
-            colsum += w_s[row] * p;
-            hsum += p * ent_s[row];
+            bool ok = kvalid && (MODE == 0 || key <= lmv[vv]);
+            const float e = fast_exp2(acc[v] * a.scale2 - lsv[vv]);
+            float p = ok ? e : 0.f;
+            if constexpr (MODE == 0) {
+              colsum += p;
+              hsum += p * env[vv];
+            } else {
+              colsum += wv[vv] * p;
+            }
             part_g += p;
           }
           if (mode == 0) {
-            // an 8-row group lies inside one query head (P is a multiple of 8)
-            int g = (rb * 32 + q * 8) / a.P;
+            // an 8-row group lies inside one query head (P is a multiple of 8);
+            // with P >= 32 the whole 32-row block does
+            if (a.P >= 32) {
+              rbs += part_g;
+            } else {
+              int g = (rb * 32 + q * 8) / a.P;
 #pragma unroll
-            for (int gg = 0; gg < 8; ++gg)
-              if (gg == g) mg[gg] += part_g;
+              for (int gg = 0; gg < 8; ++gg)
+                if (gg == g) mg[gg] += part_g;
+            }
           }
+        }
+        if (mode == 0 && a.P >= 32) {
+          const int g = rb * 32 / a.P;
+#pragma unroll
+          for (int gg = 0; gg < 8; ++gg)
+            if (gg == g) mg[gg] += rbs;
         }
       }
     }
@@ -384,15 +436,23 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, int mode, c
 #pragma unroll
       for (int g = 0; g < 8; ++g) mg[g] += __shfl_xor(mg[g], 32, 64);
       // value norm: lanes l and l+32 each sum half of the row
-      const T* Vr = (const T*)a.V + (ubase + key) * D + (lane >> 5) * (D / 2);
       float vs = 0.f;
-      if (kvalid) {
 #pragma unroll
-        for (int j = 0; j < D / 2; ++j) {
-          float x = ElemIO<T>::ld(Vr, j);
-          vs += x * x;
+      for (int j = 0; j < D / 16; ++j) {
+        if constexpr (sizeof(T) == 2) {
+          const uint4 u = __builtin_bit_cast(uint4, vrow[j].v);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x0 = __uint_as_float(w4[e] << 16), x1 = __uint_as_float(w4[e] & 0xffff0000u);
+            vs += x0 * x0 + x1 * x1;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vs += vrow[j].v[e] * vrow[j].v[e];
         }
       }
+      if (!kvalid) vs = 0.f;
       vs += __shfl_xor(vs, 32, 64);
       float vn = sqrtf(vs);
       if (lane < 32 && kvalid) {
@@ -420,6 +480,8 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, int mode, c
       out0[tix] = colsum;                           // delta_t
       rel_out[tix] = rel_in[tix] + colsum;          // running relevance
     }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
   }
   if (mode == 0) {
     hs_num = wave_sum(hs_num);
@@ -589,9 +651,15 @@ int launch_pass2(const AttnArgs& a, int mode, int64_t nsplit, const float2* rows
                  float* feats, float* head_part, const float* rel_in, float* rel_out, hipStream_t st) {
   size_t sm = smem_rows(a, D, sizeof(T)) + a.Rpad * sizeof(int) + 3 * a.Rpad * sizeof(float) +
               WAVES * 2 * sizeof(float);
-  (void)hipFuncSetAttribute((const void*)colsum_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
-  hipLaunchKernelGGL((colsum_kernel<T, D>), dim3((unsigned)nsplit), dim3(THREADS), sm, st, a, mode, rowstat,
-                     out0, feats, head_part, rel_in, rel_out);
+  if (mode == 0) {
+    (void)hipFuncSetAttribute((const void*)colsum_kernel<T, D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    hipLaunchKernelGGL((colsum_kernel<T, D, 0>), dim3((unsigned)nsplit), dim3(THREADS), sm, st, a, rowstat, out0,
+                       feats, head_part, rel_in, rel_out);
+  } else {
+    (void)hipFuncSetAttribute((const void*)colsum_kernel<T, D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    hipLaunchKernelGGL((colsum_kernel<T, D, 1>), dim3((unsigned)nsplit), dim3(THREADS), sm, st, a, rowstat, out0,
+                       feats, head_part, rel_in, rel_out);
+  }
   KVC_LAUNCH_CHECK("colsum");
   return KVC_OK;
 }

@@ -299,9 +299,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
       const float mn = fmaxf(m[j], mx);
-      const float alpha = mn == -INFINITY ? 1.f : exp2f(m[j] - mn);
+      const float ea = fast_exp2(m[j] - mn), ep = fast_exp2(z - mn);
+      const float alpha = mn == -INFINITY ? 1.f : ea;
       m[j] = mn;
-      const float p = mn == -INFINITY ? 0.f : exp2f(z - mn);
+      const float p = mn == -INFINITY ? 0.f : ep;
       lsum[j] = lsum[j] * alpha + p;
       if (4 * half + j < G) pw[wave][col][4 * half + j] = p;
       // every lane rescales its value sums of the heads this (half, j) holds

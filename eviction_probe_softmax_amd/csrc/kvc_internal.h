@@ -113,6 +113,10 @@ __device__ __forceinline__ double wave_sum_d(double v) {
   return v;
 }
 
+// 2^x on the hardware exponential (results below 2^-126 flush to zero; the
+// library's denormal-safe exp2f adds a range check and a rescale per call).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Order-preserving map of an fp32 score to uint32 (NaN -> 0, i.e. lowest).
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   if (f != f) return 0u;

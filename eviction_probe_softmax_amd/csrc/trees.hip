@@ -449,7 +449,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           int ti = tb * 32 + acc_row(v, lane);
-          if (ti < n && rho < pd) At[ti * PA + rho] = expf(acc[v] * a.c - ls);
+          if (ti < n && rho < pd) At[ti * PA + rho] = fast_exp2((acc[v] * a.c - ls) * 1.4426950408889634f);
         }
       }
       if (pd < PDMAX)
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         float z = 0.f, zh = 0.f;
         if (lane < pd) {
           for (int i = st; i < st + sz; ++i) z += At[i * PA + lane];
-          zh = nmu[j] * expf(LG[qq * LGS + lane] * a.c - lse_s[lane]);
+          zh = nmu[j] * fast_exp2((LG[qq * LGS + lane] * a.c - lse_s[lane]) * 1.4426950408889634f);
         }
         float eAn = wave_sum(fabsf(zh - z)), eAd = wave_sum(z);
         if (lane == 0) nD[j] = eAd > 0.f ? eAn / eAd : 0.f;
