@@ -77,7 +77,7 @@ struct TreeLayout {
   // and put the Gram matrix over the prototype keys; large slots keep the Gram
   // matrix over the keys and centre on the fly.
   static constexpr bool STAGED = NMAX <= SMALL;
-  static constexpr int VS = D + 4;    // row stride of the staged centred values
+  static constexpr int VS = D + 8;    // row stride of the staged centred values (elements)
   static constexpr size_t VSB = STAGED ? (size_t)N32 * VS * 4 : 0;
   static constexpr size_t R1B = STAGED ? (KT > VSB ? KT : VSB) : (KT > GM ? KT : GM);
   static constexpr size_t KHR = STAGED ? (KHB > GM ? KHB : GM) : (KHB > PARTB ? KHB : PARTB);
@@ -577,26 +577,32 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     if (nint > 0) {
       const int nt = n32 / 32;
       if constexpr (STAGED) {
-        // centred values in fp32 (zero rows past the slot), then the Gram
-        // tiles on the fp32 MFMA straight from LDS
-        constexpr int VC8 = D / 8;
+        // centred values (zero rows past the slot) from the value chunks this
+        // thread has held since the value statistics: as two bf16 pieces for
+        // bf16 inputs (|v' - hi - lo| <= 2^-18 |v'|), in fp32 otherwise
+        static_assert(Lo::N32 == VR * VG, "staging reuses the value-statistics chunks");
+        uint16_t* Vh = (uint16_t*)Vc;
+        uint16_t* Vl = Vh + (size_t)Lo::N32 * Lo::VS;
 #pragma unroll
-        for (int r = 0; r < (Lo::N32 * VC8 + THREADS - 1) / THREADS; ++r) {
-          const int it = tid + r * THREADS;
-          const int i = it / VC8, c = (it % VC8) * 8;
-          if (i < n32) {
-            float x[8];
-            if (i < n) {
-              Raw8<T> v;
-              v.load(Vg + (int64_t)i * D + c);
-              v.get(x);
+        for (int r = 0; r < VR; ++r) {
+          const int i = vg + r * VG;
+          float x[8];
+          vr[r].get(x);
 #pragma unroll
-              for (int q = 0; q < 8; ++q) x[q] -= vm[c + q];
-            } else {
+          for (int q = 0; q < 8; ++q) x[q] = i < n ? x[q] - vm[vc + q] : 0.f;
+          if constexpr (sizeof(T) == 2) {
+            uint16_t hb[8], lb[8];
 #pragma unroll
-              for (int q = 0; q < 8; ++q) x[q] = 0.f;
+            for (int q = 0; q < 8; ++q) {
+              hb[q] = f32_to_bf16_bits(x[q]);
+              lb[q] = f32_to_bf16_bits(x[q] - bf16_bits_to_f32(hb[q]));
             }
-            float* d0 = Vc + i * Lo::VS + c;
+            *(uint4*)(Vh + i * Lo::VS + vc) = make_uint4(hb[0] | (uint32_t)hb[1] << 16, hb[2] | (uint32_t)hb[3] << 16,
+                                                          hb[4] | (uint32_t)hb[5] << 16, hb[6] | (uint32_t)hb[7] << 16);
+            *(uint4*)(Vl + i * Lo::VS + vc) = make_uint4(lb[0] | (uint32_t)lb[1] << 16, lb[2] | (uint32_t)lb[3] << 16,
+                                                          lb[4] | (uint32_t)lb[5] << 16, lb[6] | (uint32_t)lb[7] << 16);
+          } else {
+            float* d0 = Vc + i * Lo::VS + vc;
             *(float4*)d0 = make_float4(x[0], x[1], x[2], x[3]);
             *(float4*)(d0 + 4) = make_float4(x[4], x[5], x[6], x[7]);
           }
@@ -609,11 +615,23 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
             ++ti;
           }
           const int tj = ti + rem;
-          const float* pa = Vc + (ti * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
-          const float* pb = Vc + (tj * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
+          const int oa = (ti * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
+          const int ob = (tj * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
           kvc_f32x16 acc = {};
+          if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) mma(acc, load_frag<float>(pa + ks * 16), load_frag<float>(pb + ks * 16));
+            for (int ks = 0; ks < KS; ++ks) {
+              const Frag<uint16_t> ha = load_frag<uint16_t>(Vh + oa + ks * 16), la = load_frag<uint16_t>(Vl + oa + ks * 16);
+              const Frag<uint16_t> hb = load_frag<uint16_t>(Vh + ob + ks * 16), lb = load_frag<uint16_t>(Vl + ob + ks * 16);
+              mma(acc, ha, hb);
+              mma(acc, ha, lb);
+              mma(acc, la, hb);
+              mma(acc, la, lb);
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma(acc, load_frag<float>(Vc + oa + ks * 16), load_frag<float>(Vc + ob + ks * 16));
+          }
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int r = ti * 32 + acc_row(v, lane), cc = tj * 32 + (lane & 31);
