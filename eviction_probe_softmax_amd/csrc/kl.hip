@@ -7,11 +7,12 @@
 // 1. rmsnorm_cast: x^ = x / sqrt(mean x^2 + 1e-6) in fp64, cast to W's
 //    dtype; the full and compressed rows of pair p become rows 2p and 2p+1.
 // 2. gemm_kl: y = x^ W^T on MFMA (W is [vocab][d_model], so both operands
-//    are contiguous along d_model). A workgroup owns 128 vocab columns and
+//    are contiguous along d_model). A workgroup owns 64 vocab columns and
 //    up to 128 rows; its epilogue reduces each pair over its columns to
 //    (max_f, sum_f, max_c, sum_c, sum e^(y-max_f) (y - y^)) - the logits
 //    never reach memory.
-// 3. kl_combine: merge the column-tile partials of every pair.
+// 3. kl_combine: merge the column-tile partials of every pair (one
+//    workgroup per pair).
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -19,9 +20,10 @@
 namespace {
 
 constexpr int THREADS = 256;
-constexpr int NT = 128;    // vocab columns per workgroup (4 waves x 32)
-constexpr int MT = 128;    // rows per workgroup (4 row blocks of 32)
-constexpr int KC = 128;    // d_model chunk staged in LDS
+constexpr int NT = 128;    // vocab columns per workgroup (4 column waves x 32)
+constexpr int MT = 128;    // rows per workgroup (4 blocks of 32 per wave)
+constexpr int NCW = NT / 32;           // column waves
+constexpr int RBW = MT / 32 / (4 / NCW);  // 32-row blocks per wave
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -65,6 +67,15 @@ __device__ __forceinline__ Frag<float> ldfrag(const float* p) {
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
   return f;
 }
+__device__ __forceinline__ Frag<uint16_t> keep(Frag<uint16_t> f, bool k) {
+  f.v = k ? f.v : kvc_bf16x8{};
+  return f;
+}
+__device__ __forceinline__ Frag<float> keep(Frag<float> f, bool k) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = k ? f.v[j] : 0.f;
+  return f;
+}
 __device__ __forceinline__ void mma(kvc_f32x16& acc, const Frag<uint16_t>& a, const Frag<uint16_t>& b) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, acc, 0, 0, 0);
 }
@@ -91,91 +102,207 @@ __device__ __forceinline__ Stat5 merge5(Stat5 a, Stat5 b) {
   return r;
 }
 
-// grid: (vocab / NT, m_pad / MT). part: [n_pairs][n_col_tiles][5]
+// Both operands go through LDS in fragment order, two stages deep: while the
+// waves run the MFMAs of one k chunk, every thread already has the loads of
+// the next two chunks' 16-byte pieces in flight (row-contiguous, fully
+// coalesced loads of W and x^). One barrier per chunk suffices with two
+// stages. Each workgroup starts at a different k chunk so that the W rows
+// the grid reads at one moment do not all share an address phase. With few
+// rows the kernel streams W once and is bound by HBM.
+typedef unsigned int kl_u32x4 __attribute__((ext_vector_type(4)));
+
+template <class T> struct KlTile {
+  static constexpr int KC = sizeof(T) == 2 ? 128 : 64;  // k per chunk: 256 bytes of a row
+  static constexpr int NKS = KC / 16;                   // 16-k MFMA steps per chunk
+  static constexpr int NPC = sizeof(T) * 8 / 16;        // 16-byte pieces per fragment
+  static constexpr int ELP = 16 / sizeof(T);            // elements per piece
+  static constexpr int PPR = KC / ELP;                  // pieces per tile row (16)
+  static constexpr int RPP = THREADS / PPR;             // tile rows per pass of the workgroup (16)
+  static constexpr int XP = MT / RPP;                   // passes over the x^ tile
+  static constexpr int WP = NT / RPP;                   // passes over the W tile
+  static constexpr int RG = 16 / PPR;                   // rows per group of 16 storing threads
+  static constexpr int SWZ = 16 / NPC - 1;              // fragment-lane swizzle mask
+  static constexpr int XS = (MT / 32) * NKS * 64 * NPC; // pieces of the x^ tile
+  static constexpr int WS = (NT / 32) * NKS * 64 * NPC; // pieces of the W tile
+};
+
+// LDS slot (in 16-byte pieces) of piece p of tile row `row`. Fragments are
+// stored lane-contiguous; the lane index is XOR-swizzled by the fragment's
+// k position so that each group of 16 storing threads (RG rows x PPR
+// pieces) hits 16 different bank groups, while a wave reading one fragment
+// still touches each bank group once.
+template <class T>
+__device__ __forceinline__ int frag_slot(int row, int p) {
+  using L = KlTile<T>;
+  const int k = p * L::ELP, ks = k >> 4, half = (k >> 3) & 1, sub = (k & 7) / L::ELP;
+  const int ln = ((row & 31) + 32 * half) ^ (((2 * ks + half) * L::RG) & L::SWZ);
+  return (((row >> 5) * L::NKS + ks) * 64 + ln) * L::NPC + sub;
+}
+template <class T>
+__device__ __forceinline__ int frag_read(int blk, int ks, int lane) {
+  using L = KlTile<T>;
+  return (blk * L::NKS + ks) * 64 + (lane ^ (((2 * ks + (lane >> 5)) * L::RG) & L::SWZ));
+}
+
+// grid: (vocab / NT, m_pad / MT). part: [n_pairs][vocab / 32 column tiles][5]
 template <class T>
 __global__ __launch_bounds__(THREADS) void gemm_kl_kernel(const T* xh, const T* W, int64_t n_pairs, int dm,
                                                           int vocab, int64_t m_pad, float* part) {
-  __shared__ __align__(16) Frag<T> af[MT / 32][KC / 16][64];
+  using L = KlTile<T>;
+  extern __shared__ __align__(16) kl_u32x4 kl_lds[];  // [2][XS + WS]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cw = wave % NCW, rw = wave / NCW;
   const int64_t r0 = (int64_t)blockIdx.y * MT;
   const int nrb = (int)((m_pad - r0) < MT ? (m_pad - r0) / 32 : MT / 32);
-  const int col = blockIdx.x * NT + wave * 32 + (lane & 31);
+  const int col = blockIdx.x * NT + cw * 32 + (lane & 31);
   const bool cvalid = col < vocab;
-  const T* wrow = W + (int64_t)(cvalid ? col : 0) * dm;
-  kvc_f32x16 acc[MT / 32];
+  const int nch = dm / L::KC;
+  const int c0 = (int)(blockIdx.x % (unsigned)nch);
+  // pieces of this thread: rows trow + RPP*i of both tiles, piece index tp
+  const int trow = threadIdx.x / L::PPR, tp = threadIdx.x % L::PPR;
+  const T* xb = xh + tp * L::ELP;
+  const int64_t wc0 = (int64_t)blockIdx.x * NT + trow;
+  const T* wb = W + tp * L::ELP;
+  kl_u32x4 xr[2][L::XP], wr[2][L::WP];
+  kvc_f32x16 acc[RBW];
 #pragma unroll
-  for (int rb = 0; rb < MT / 32; ++rb) acc[rb] = kvc_f32x16{};
-  for (int k0 = 0; k0 < dm; k0 += KC) {
-    __syncthreads();
-    // stage x^ rows [r0, r0 + 32 nrb) x [k0, k0 + KC) in fragment order
-    for (int c = threadIdx.x; c < nrb * 32 * (KC / 8); c += THREADS) {
-      int row = c / (KC / 8), c8 = c % (KC / 8);
-      int rb = row >> 5, ks = c8 >> 1, ln = (row & 31) + 32 * (c8 & 1);
-      af[rb][ks][ln] = ldfrag(xh + (r0 + row) * dm + k0 + c8 * 8);
+  for (int j = 0; j < RBW; ++j) acc[j] = kvc_f32x16{};
+  // Two register sets hold the next two chunks, so two chunks' loads are in
+  // flight while a third is multiplied out of LDS.
+  // Every fetch is issued, also past the last chunk (then it re-reads the
+  // chunk of two steps before, which is still in L2): a branch around the
+  // loads would make the wait before each LDS store count conservatively
+  // and drain both register sets.
+  auto fetch = [&](int r, int it) {
+    int ch = c0 + (it < nch ? it : it - 2);
+    ch = ch >= nch ? ch - nch : ch;
+    ch = ch < 0 ? 0 : ch;
+    const int k0 = ch * L::KC;
+    // rows past the last valid one re-read row m_pad - 1: every load is
+    // unconditional and in bounds, and those rows' products are never used
+#pragma unroll
+    for (int i = 0; i < L::XP; ++i) {
+      const int64_t xrow = min(r0 + trow + L::RPP * i, m_pad - 1);
+      xr[r][i] = *(const kl_u32x4*)(xb + xrow * dm + k0);
     }
-    __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < KC / 16; ++ks) {
-      Frag<T> b = ldfrag(wrow + k0 + ks * 16 + 8 * (lane >> 5));
-#pragma unroll
-      for (int rb = 0; rb < MT / 32; ++rb)
-        if (rb < nrb) mma(acc[rb], af[rb][ks][lane], b);
+    for (int i = 0; i < L::WP; ++i) {
+      const int64_t wc = min(wc0 + L::RPP * i, (int64_t)vocab - 1);
+      wr[r][i] = *(const kl_u32x4*)(wb + wc * dm + k0);
     }
+  };
+  auto step = [&](int r, int it) {
+    const bool live = it < nch;  // false only for the padding step of an odd chunk count
+    kl_u32x4* stg = kl_lds + r * (L::XS + L::WS);
+#pragma unroll
+    for (int i = 0; i < L::XP; ++i) stg[frag_slot<T>(trow + L::RPP * i, tp)] = xr[r][i];
+#pragma unroll
+    for (int i = 0; i < L::WP; ++i) stg[L::XS + frag_slot<T>(trow + L::RPP * i, tp)] = wr[r][i];
+    __syncthreads();
+    fetch(r, it + 2);
+    const Frag<T>* xf = (const Frag<T>*)stg;
+    const Frag<T>* wf = (const Frag<T>*)(stg + L::XS);
+    // the fragments of step ks + 1 are read from LDS before the products of
+    // step ks are issued (no branches around the MFMAs)
+    Frag<T> b[2], a[2][RBW];
+    b[0] = wf[frag_read<T>(cw, 0, lane)];
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) a[0][j] = xf[frag_read<T>(rw * RBW + j, 0, lane)];
+#pragma unroll
+    for (int ks = 0; ks < L::NKS; ++ks) {
+      const int c = ks & 1, n = c ^ 1;
+      if (ks + 1 < L::NKS) {
+        b[n] = wf[frag_read<T>(cw, ks + 1, lane)];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) a[n][j] = xf[frag_read<T>(rw * RBW + j, ks + 1, lane)];
+      }
+      const Frag<T> bk = keep(b[c], live);
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) mma(acc[j], a[c][j], bk);
+    }
+  };
+  fetch(0, 0);
+  fetch(1, nch > 1 ? 1 : 0);
+  // an odd chunk count gets one padding step whose W fragments are zero, so
+  // the loop body has no branch
+  for (int it = 0; it < nch; it += 2) {
+    step(0, it);
+    step(1, it + 1);
   }
   // epilogue: lane owns column `col`; registers v, v+1 (v%4 in {0,2}) hold
-  // rows 2p and 2p+1 of one pair
+  // rows 2p and 2p+1 of one pair. Each pair's statistics over the wave's 32
+  // columns: the maxima first, then one exponential per lane and sums.
+  // Contraction stays off so that identical rows give identical statistics.
   const int ntile = (vocab + NT - 1) / NT;
 #pragma unroll
-  for (int rb = 0; rb < MT / 32; ++rb) {
+  for (int j = 0; j < RBW; ++j) {
+    const int rb = rw * RBW + j;
     if (rb >= nrb) break;
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
-      int row = rb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-      int64_t pair = (r0 + row) >> 1;
+#pragma clang fp contract(off)
+      const int row = rb * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      const int64_t pair = (r0 + row) >> 1;
       // base-2 logits for the partition sums; the logit difference is taken
       // from the accumulators themselves so identical rows give exactly 0
-      float y = acc[rb][v] * LOG2E, yh = acc[rb][v + 1] * LOG2E;
-      float dy = acc[rb][v] - acc[rb][v + 1];
-      Stat5 st;
-      if (cvalid) {
-        st.mf = y; st.sf = 1.f; st.mc = yh; st.sc = 1.f; st.t = dy;
-      } else {
-        st.mf = -INFINITY; st.sf = 0.f; st.mc = -INFINITY; st.sc = 0.f; st.t = 0.f;
-      }
-      // reduce over the 32 lanes (columns) that share this row pair
+      const float y = cvalid ? acc[j][v] * LOG2E : -INFINITY;
+      const float yh = cvalid ? acc[j][v + 1] * LOG2E : -INFINITY;
+      const float dy = cvalid ? acc[j][v] - acc[j][v + 1] : 0.f;
+      float mf = y, mc = yh;
 #pragma unroll
       for (int o = 1; o < 32; o <<= 1) {
-        Stat5 other;
-        other.mf = __shfl_xor(st.mf, o, 64);
-        other.sf = __shfl_xor(st.sf, o, 64);
-        other.mc = __shfl_xor(st.mc, o, 64);
-        other.sc = __shfl_xor(st.sc, o, 64);
-        other.t = __shfl_xor(st.t, o, 64);
-        st = merge5(st, other);
+        mf = fmaxf(mf, __shfl_xor(mf, o, 64));
+        mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+      }
+      // all 32 columns past the vocab: an empty statistic
+      const float ef = mf == -INFINITY ? 0.f : fast_exp2(y - mf);
+      const float ec = mc == -INFINITY ? 0.f : fast_exp2(yh - mc);
+      float sf = ef, sc = ec, t = ef * dy;
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        sf += __shfl_xor(sf, o, 64);
+        sc += __shfl_xor(sc, o, 64);
+        t += __shfl_xor(t, o, 64);
       }
       if ((lane & 31) == 0 && pair < n_pairs) {
         // column sub-tile of this wave: tiles of 32 columns
-        float* p = part + ((pair * ntile + blockIdx.x) * 4 + wave) * 5;
-        p[0] = st.mf; p[1] = st.sf; p[2] = st.mc; p[3] = st.sc; p[4] = st.t;
+        float* p = part + ((pair * ntile + blockIdx.x) * NCW + cw) * 5;
+        p[0] = mf; p[1] = sf; p[2] = mc; p[3] = sc; p[4] = t;
       }
     }
   }
 }
 
-__global__ void kl_combine_kernel(const float* part, int64_t n_pairs, int nsub, float* kl) {
+// One workgroup per pair: threads merge strided subsets of the column-tile
+// partials, then the wave and the workgroup merge theirs.
+__global__ __launch_bounds__(256) void kl_combine_kernel(const float* part, int64_t n_pairs, int nsub, float* kl) {
 #pragma clang fp contract(off)
-  int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (p >= n_pairs) return;
-  Stat5 st{-INFINITY, 0.f, -INFINITY, 0.f, 0.f};
+  __shared__ Stat5 red[4];
+  const int64_t p = blockIdx.x;
   const float* q = part + p * nsub * 5;
-  for (int i = 0; i < nsub; ++i) {
+  Stat5 st{-INFINITY, 0.f, -INFINITY, 0.f, 0.f};
+  for (int i = threadIdx.x; i < nsub; i += blockDim.x) {
     Stat5 o{q[i * 5], q[i * 5 + 1], q[i * 5 + 2], q[i * 5 + 3], q[i * 5 + 4]};
     st = merge5(st, o);
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    Stat5 other;
+    other.mf = __shfl_xor(st.mf, o, 64);
+    other.sf = __shfl_xor(st.sf, o, 64);
+    other.mc = __shfl_xor(st.mc, o, 64);
+    other.sc = __shfl_xor(st.sc, o, 64);
+    other.t = __shfl_xor(st.t, o, 64);
+    st = merge5(st, other);
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = st;
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  st = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) st = merge5(st, red[w]);
   // natural-log partition functions from base-2 maxima
   float lse_f = (st.mf + log2f(st.sf)) * LN2, lse_c = (st.mc + log2f(st.sc)) * LN2;
-  float v = st.t / st.sf - lse_f + lse_c;
-  kl[p] = v;
+  kl[p] = st.t / st.sf - lse_f + lse_c;
 }
 
 }  // namespace
@@ -187,14 +314,14 @@ extern "C" size_t kvc_kl_workspace(int64_t n_pairs, int32_t d_model, int32_t voc
   int64_t ntile = (vocab + NT - 1) / NT;
   kvc::Carver c(nullptr, 0);
   c.take<char>((size_t)m_pad * d_model * elt);
-  c.take<float>((size_t)n_pairs * ntile * 4 * 5);
+  c.take<float>((size_t)n_pairs * ntile * NCW * 5);
   return c.off + 256;
 }
 
 extern "C" int kvc_kl(int64_t n_pairs, int32_t d_model, int32_t vocab, const float* x_full, const float* x_comp,
                       const void* W, int32_t w_dtype, float* kl_out, void* ws, size_t ws_bytes, hipStream_t st) {
   KVC_REQUIRE(n_pairs >= 0 && vocab >= 1, KVC_E_INVAL, "kvc_kl: bad sizes");
-  KVC_REQUIRE(d_model >= KC && d_model % KC == 0, KVC_E_SHAPE, "kvc_kl: d_model must be a multiple of 128");
+  KVC_REQUIRE(d_model >= 128 && d_model % 128 == 0, KVC_E_SHAPE, "kvc_kl: d_model must be a multiple of 128");
   KVC_REQUIRE(w_dtype == KVC_BF16 || w_dtype == KVC_F32, KVC_E_DTYPE, "kvc_kl: W must be bf16 or f32");
   if (n_pairs == 0) return KVC_OK;
   KVC_REQUIRE(x_full && x_comp && W && kl_out, KVC_E_INVAL, "kvc_kl: NULL pointer");
@@ -205,24 +332,28 @@ extern "C" int kvc_kl(int64_t n_pairs, int32_t d_model, int32_t vocab, const flo
   kvc::Carver c(ws, ws_bytes);
   size_t elt = w_dtype == KVC_BF16 ? 2 : 4;
   char* xh = c.take<char>((size_t)m_pad * d_model * elt);
-  float* part = c.take<float>((size_t)n_pairs * ntile * 4 * 5);
+  float* part = c.take<float>((size_t)n_pairs * ntile * NCW * 5);
   dim3 g2((unsigned)ntile, (unsigned)((m_pad + MT - 1) / MT));
   if (w_dtype == KVC_BF16) {
     hipLaunchKernelGGL(rmsnorm_cast_kernel<uint16_t>, dim3((unsigned)m_pad), dim3(256), 0, st, x_full, x_comp,
                        n_pairs, d_model, m_pad, (uint16_t*)xh);
     KVC_LAUNCH_CHECK("rmsnorm_cast");
-    hipLaunchKernelGGL(gemm_kl_kernel<uint16_t>, g2, dim3(THREADS), 0, st, (const uint16_t*)xh, (const uint16_t*)W,
-                       n_pairs, d_model, vocab, m_pad, part);
+    const int sm = 2 * (KlTile<uint16_t>::XS + KlTile<uint16_t>::WS) * 16;
+    (void)hipFuncSetAttribute((const void*)gemm_kl_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
+    hipLaunchKernelGGL(gemm_kl_kernel<uint16_t>, g2, dim3(THREADS), sm, st, (const uint16_t*)xh,
+                       (const uint16_t*)W, n_pairs, d_model, vocab, m_pad, part);
   } else {
     hipLaunchKernelGGL(rmsnorm_cast_kernel<float>, dim3((unsigned)m_pad), dim3(256), 0, st, x_full, x_comp, n_pairs,
                        d_model, m_pad, (float*)xh);
     KVC_LAUNCH_CHECK("rmsnorm_cast");
-    hipLaunchKernelGGL(gemm_kl_kernel<float>, g2, dim3(THREADS), 0, st, (const float*)xh, (const float*)W, n_pairs,
+    const int sm = 2 * (KlTile<float>::XS + KlTile<float>::WS) * 16;
+    (void)hipFuncSetAttribute((const void*)gemm_kl_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
+    hipLaunchKernelGGL(gemm_kl_kernel<float>, g2, dim3(THREADS), sm, st, (const float*)xh, (const float*)W, n_pairs,
                        d_model, vocab, m_pad, part);
   }
   KVC_LAUNCH_CHECK("gemm_kl");
-  hipLaunchKernelGGL(kl_combine_kernel, dim3(kvc_blocks(n_pairs, 256)), dim3(256), 0, st, part, n_pairs,
-                     (int)(ntile * 4), kl_out);
+  hipLaunchKernelGGL(kl_combine_kernel, dim3((unsigned)n_pairs), dim3(256), 0, st, part, n_pairs,
+                     (int)(ntile * NCW), kl_out);
   KVC_LAUNCH_CHECK("kl_combine");
   return KVC_OK;
 }

@@ -93,16 +93,19 @@ def test_decode_ragged_cache_with_multiplicity(name):
     close(o, oo, DEC_RTOL, "o_layers", floor=DEC_FLOOR)
 
 
-@pytest.mark.parametrize("w_dtype,dm,vocab", [("f32", 256, 2048), ("bf16", 1024, 1000), ("bf16", 4096, 32768)])
-def test_kl_matches_oracle(w_dtype, dm, vocab):
+@pytest.mark.parametrize("w_dtype,dm,vocab,n", [("f32", 256, 2048, 37), ("bf16", 1024, 1000, 37),
+                                                 ("bf16", 4096, 32768, 37), ("bf16", 512, 1000, 100),
+                                                 ("f32", 384, 300, 70), ("bf16", 128, 64, 1)])
+def test_kl_matches_oracle(w_dtype, dm, vocab, n):
+    """n pairs give 2n rows: 37 leaves a partial last row block, 100 and 70
+    span two 128-row tiles, vocab 1000 / 300 / 64 leave partial column tiles."""
     kvc = _kvc()
     g = torch.Generator().manual_seed(3)
-    n = 37
     xf = torch.randn((n, dm), generator=g)
     xc = xf + 0.5 * torch.randn((n, dm), generator=g)
     W = (torch.randn((vocab, dm), generator=g) * (4.0 / math.sqrt(dm))).to(
         torch.bfloat16 if w_dtype == "bf16" else torch.float32)
-    print(f"[kl] {w_dtype} dm={dm} vocab={vocab}", flush=True)
+    print(f"[kl] {w_dtype} dm={dm} vocab={vocab} n={n}", flush=True)
     got = kvc.kl(xf.cuda(), xc.cuda(), W.cuda())
     torch.cuda.synchronize()
     want = oracle.kl_rows(xf.numpy(), xc.numpy(), W, w_dtype)
