@@ -60,17 +60,28 @@ def budgets(lens: List[int], cfg) -> List[dict]:
     L * Ly * H. The recent window is charged first; the rest is allocatable.
     The singleton floor may spend at most floor(phi * allocatable) entries
     (GraceKV page, 'Technical details and default settings', singleton floor).
+    Head-level hybrid (DistillCache paper, Appendix E.3: the most important
+    heads get their full cache, token selection runs in the others, under
+    the same overall budget): K = min(floor(f * Ly*H), floor(alloc / C))
+    units keep all C compressible tokens and are paid first; the selection
+    and the floor share the rest, alloc - K*C. With f = 0, K = 0.
     """
     out = []
+    U = cfg.Ly * cfg.H
+    f = float(np.float32(getattr(cfg, "hybrid_frac", 0.0)))
     for L in lens:
-        B = max(int(math.floor(float(np.float32(cfg.budget_ratio)) * (L * cfg.Ly * cfg.H))),
-                cfg.budget_min)
+        B = max(int(math.floor(float(np.float32(cfg.budget_ratio)) * (L * U))), cfg.budget_min)
         pe, cs, ce, ss = regions(L, cfg)
-        recent = (ss - ce) * cfg.Ly * cfg.H
+        recent = (ss - ce) * U
         alloc = B - recent
-        F = int(math.floor(float(np.float32(cfg.floor_frac)) * alloc)) if alloc > 0 else 0
+        C = ce - cs
+        K = 0
+        if f > 0 and C > 0 and alloc > 0:
+            K = min(int(math.floor(f * U)), alloc // C, U)
+        rest = alloc - K * C
+        F = int(math.floor(float(np.float32(cfg.floor_frac)) * rest)) if rest > 0 else 0
         out.append({"B": B, "alloc": alloc, "floor": F, "recent": recent,
-                    "free": (pe + (L - ss)) * cfg.Ly * cfg.H})
+                    "free": (pe + (L - ss)) * U, "full_units": K, "comp_len": C, "rest": rest})
     return out
 
 

@@ -14,7 +14,7 @@ from .score import probe_scores
 from .propagate import propagate
 from .partition import slot_costs, slots_for
 from .trees import build_trees
-from .select import floor_select, auction, token_topk
+from .select import floor_select, auction, token_topk, hybrid_units
 from .pack import pack
 from .decode import decode_all, full_view
 from .kl import kl_rows
@@ -28,9 +28,11 @@ def run_pipeline(inp, cfg, stages=("compress", "decode", "kl")):
     pr = propagate(inp["K"], inp["Qctx"], sc["r0"], cu, cfg)
     out.update(pr)
     rel = pr["rel"]
+    full = hybrid_units(sc["head_sens"], cu, cfg) if getattr(cfg, "hybrid_frac", 0.0) > 0 else None
+    out["full_units"] = full
     if cfg.token_mode:
         slots = [[] for _ in range(len(cu) - 1)]
-        taken, spent = token_topk(rel, cu, cfg)
+        taken, spent = token_topk(rel, cu, cfg, full)
         trees = None
     else:
         cost_q = cut_q = None
@@ -41,9 +43,9 @@ def run_pipeline(inp, cfg, stages=("compress", "decode", "kl")):
         trees = build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"],
                             cu, slots, cfg)
         out["trees"] = trees
-        ftaken, fspent = floor_select(rel, sc["head_sens"], trees["op_cost"], cu, slots, cfg)
+        ftaken, fspent = floor_select(rel, sc["head_sens"], trees["op_cost"], cu, slots, cfg, full=full)
         out["floor_taken"], out["floor_spent"] = ftaken, fspent
-        taken, spent = auction(trees["op_util"], trees["op_cost"], ftaken, fspent, cu, slots, cfg)
+        taken, spent = auction(trees["op_util"], trees["op_cost"], ftaken, fspent, cu, slots, cfg, full=full)
     out["slots"] = slots
     out["taken"], out["spent"] = taken, spent
     cache = pack(inp["K"], inp["V"], rel, trees, taken, cu, slots, cfg)

@@ -27,6 +27,13 @@ Readings:
   even with non-positive utilities. A NaN utility counts as -infinity.
 * Token mode: the first B_alloc compressible tokens of the sequence by
   (r descending, flat id ascending).
+* Head-level hybrid (DistillCache paper, Appendix E.3): per sequence the K
+  units (l, h) with the largest head sensitivity s_lh (the probe pass's
+  attention statistic; ties to the lower unit index l*H + h) keep every
+  compressible token: in tree mode all their Add and Split operations are
+  taken, in token mode all their tokens. K and the remaining budget come
+  from common.budgets; the floor, the auction and the token top-B then run
+  over the other units only.
 """
 from __future__ import annotations
 
@@ -57,10 +64,25 @@ def _leaf_path(nodes, i):
     return path
 
 
-def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None):
+def hybrid_units(head_sens, cu, cfg):
+    """Units kept whole: bool [S][Ly][H] (all False when hybrid_frac = 0)."""
+    S = len(cu) - 1
+    Ly, H = cfg.Ly, cfg.H
+    full = np.zeros((S, Ly, H), dtype=bool)
+    bud = budgets([int(cu[s + 1] - cu[s]) for s in range(S)], cfg)
+    for s in range(S):
+        K = bud[s]["full_units"]
+        order = sorted(range(Ly * H), key=lambda u: (-_f32key(head_sens[s].reshape(-1)[u]), u))
+        for u in order[:K]:
+            full[s, u // H, u % H] = True
+    return full
+
+
+def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None, full=None):
     """Returns op_taken uint8 [Ly][H][2T] (floor ops only) and spent [S].
     If ``trace`` is a list, accepted candidates are appended as
-    (leaf flat id, path cost paid)."""
+    (leaf flat id, path cost paid). ``full`` [S][Ly][H] excludes the units
+    kept whole by the head-level hybrid."""
     Ly, H, T2 = op_cost.shape
     T = T2 // 2
     taken = np.zeros((Ly, H, 2 * T), dtype=np.uint8)
@@ -76,6 +98,8 @@ def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None):
         cands = []
         for l in range(Ly):
             for h in range(H):
+                if full is not None and full[s, l, h]:
+                    continue
                 sens = np.float64(head_sens[s, l, h])
                 for (st, n) in slots[s]:
                     nodes = tree_nodes(st, n)
@@ -97,12 +121,13 @@ def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None):
     return taken, spent
 
 
-def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=None):
+def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=None, full=None):
     """Best-first greedy over every exposed op of each sequence.
 
     Returns op_taken uint8 [Ly][H][2T] (floor ops included) and spent [S]
-    (floor + auction entries). If ``trace`` is a list, the taken ops are
-    appended to it in the order the queue pops them."""
+    (floor + auction entries, and the units kept whole). If ``trace`` is a
+    list, the taken ops are appended to it in the order the queue pops them.
+    ``full`` [S][Ly][H]: units kept whole (every real op taken up front)."""
     Ly, H, T2 = op_util.shape
     T = T2 // 2
     taken = floor_taken.copy().reshape(-1)
@@ -114,6 +139,17 @@ def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=No
         if not slots[s]:
             continue
         a0 = int(cu[s])
+        if full is not None:
+            for l in range(Ly):
+                for h in range(H):
+                    if not full[s, l, h]:
+                        continue
+                    for (st, n) in slots[s]:
+                        base = _slot_ops(T, H, l, h, a0 + st)
+                        for o in range(base, base + 2 * n):
+                            if cost[o] > 0 and not taken[o]:
+                                taken[o] = 1
+                                spent[s] += int(cost[o])
         rem = bud[s]["alloc"] - int(spent[s])
         heap = []
         children = {}   # op id -> list of op ids it exposes
@@ -154,8 +190,9 @@ def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=No
     return taken.reshape(Ly, H, 2 * T), spent
 
 
-def token_topk(rel_tok, cu, cfg):
-    """Token-level mode: returns taken uint8 [Ly][H][T] and spent [S]."""
+def token_topk(rel_tok, cu, cfg, full=None):
+    """Token-level mode: returns taken uint8 [Ly][H][T] and spent [S].
+    ``full`` [S][Ly][H]: units kept whole by the head-level hybrid."""
     Ly, H, T = rel_tok.shape
     taken = np.zeros((Ly, H, T), dtype=np.uint8)
     bud = budgets([int(cu[s + 1] - cu[s]) for s in range(len(cu) - 1)], cfg)
@@ -164,13 +201,18 @@ def token_topk(rel_tok, cu, cfg):
         a0, b0 = int(cu[s]), int(cu[s + 1])
         pe, c0, c1, ss = regions(b0 - a0, cfg)
         keys = []
+        whole = 0
         for l in range(Ly):
             for h in range(H):
+                if full is not None and full[s, l, h]:
+                    taken[l, h, a0 + c0:a0 + c1] = 1
+                    whole += c1 - c0
+                    continue
                 for i in range(c0, c1):
                     keys.append((-_f32key(rel_tok[l, h, a0 + i]), (l * H + h) * T + a0 + i, l, h, i))
         keys.sort(key=lambda k: (k[0], k[1]))
-        k = max(0, min(bud[s]["alloc"], len(keys)))
+        k = max(0, min(bud[s]["alloc"] - whole, len(keys)))
         for _, _, l, h, i in keys[:k]:
             taken[l, h, a0 + i] = 1
-        spent[s] = k
+        spent[s] = k + whole
     return taken, spent

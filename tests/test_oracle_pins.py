@@ -680,3 +680,135 @@ def test_full_budget_recovers_the_cache_and_kl_is_zero(name):
     assert np.all(c["lnmu"] == 0)
     assert np.array_equal(out["x_comp"], out["x_full"])
     assert np.all(out["kl"] == 0.0)
+
+
+# ---------------------------------------------------------------- head-level hybrid (NEXT 4)
+def _hybrid_cfg(**kw):
+    return _cfg(**kw).replace(hybrid_frac=kw.get("hybrid_frac", 0.34))
+
+
+def test_hybrid_units_are_the_top_heads_under_the_budget_cap():
+    # DistillCache Appendix E.3: the most important heads keep the full cache;
+    # K = min(floor(f*U), floor(alloc / C)); ranking by s_lh desc, unit asc
+    rng = np.random.default_rng(21)
+    for trial in range(30):
+        Ly, H, L = 2, 3, int(rng.integers(4, 30))
+        sens = rng.integers(0, 3, (2, Ly, H)).astype(np.float32)   # ties
+        r = float(rng.choice([0.05, 0.2, 0.5, 1.0]))
+        cfg = _hybrid_cfg(Ly=Ly, H=H, lens=[L, L], budget_ratio=r, budget_min=1, hybrid_frac=0.34)
+        cu = np.array([0, L, 2 * L])
+        full = osel.hybrid_units(sens, cu, cfg)
+        for s in range(2):
+            b = common.budgets([L], cfg)[0]
+            K = min(math.floor(np.float32(0.34) * Ly * H), b["alloc"] // L)
+            assert b["full_units"] == K and b["rest"] == b["alloc"] - K * L
+            order = np.lexsort((np.arange(Ly * H), -sens[s].reshape(-1)))
+            want = np.zeros(Ly * H, dtype=bool)
+            want[order[:K]] = True
+            assert np.array_equal(full[s].reshape(-1), want), (trial, s)
+    # f = 0 keeps nothing whole
+    cfg0 = _cfg(Ly=2, H=3, lens=[8])
+    assert not osel.hybrid_units(np.ones((1, 2, 3), np.float32), np.array([0, 8]), cfg0).any()
+
+
+def test_hybrid_token_mode_keeps_whole_heads_and_tops_the_rest():
+    rng = np.random.default_rng(22)
+    for trial in range(20):
+        Ly, H, L = 2, 3, int(rng.integers(5, 30))
+        rel = rng.integers(0, 5, (Ly, H, L)).astype(np.float32)
+        sens = rng.random((1, Ly, H)).astype(np.float32)
+        cfg = _hybrid_cfg(Ly=Ly, H=H, lens=[L], token_mode=True, budget_min=1,
+                          budget_ratio=float(rng.uniform(0.2, 0.9)), hybrid_frac=0.34)
+        cu = np.array([0, L])
+        full = osel.hybrid_units(sens, cu, cfg)
+        taken, spent = osel.token_topk(rel, cu, cfg, full)
+        b = common.budgets([L], cfg)[0]
+        K = int(full.sum())
+        assert K == b["full_units"]
+        assert np.all(taken[full[0]] == 1)
+        # the rest: a top set of (rel desc, flat id asc) over the other units
+        ids = [(l * H + h) * L + i for l in range(Ly) for h in range(H) if not full[0, l, h] for i in range(L)]
+        vals = np.array([rel.reshape(-1)[f] for f in ids])
+        order = np.lexsort((np.array(ids), -vals))
+        k = min(b["rest"], len(ids))
+        want = np.zeros(Ly * H * L, dtype=np.uint8)
+        want[np.array(ids)[order[:k]]] = 1
+        want.reshape(Ly, H, L)[full[0]] = 1
+        assert np.array_equal(taken.reshape(-1), want), trial
+        assert spent[0] == K * L + k
+
+
+def test_hybrid_auction_equals_the_greedy_over_the_other_heads():
+    rng = np.random.default_rng(23)
+    for trial in range(25):
+        lens, starts, T, _, _, _ = _random_forest(rng, int(rng.integers(1, 4)), False)
+        H = 3
+        util = np.zeros((1, H, 2 * T), dtype=np.float32)
+        cost = np.zeros((1, H, 2 * T), dtype=np.uint8)
+        slots_ops_all = []
+        for h in range(H):
+            for st, n in zip(starts, lens):
+                nodes = otrees.tree_nodes(st, n)
+                base = h * 2 * T + 2 * st
+                slots_ops_all.append((h, base, nodes))
+                cost[0, h, 2 * st] = 1
+                util[0, h, 2 * st] = rng.standard_normal()
+                for j, nd in enumerate(nodes):
+                    if nd[2] >= 0:
+                        cost[0, h, 2 * st + 1 + j] = 1
+                        util[0, h, 2 * st + 1 + j] = rng.standard_normal()
+        sens = rng.random((1, 1, H)).astype(np.float32)
+        for B in (T, T + 1, T + 4, 2 * T, 3 * T):
+            cfg = _hybrid_cfg(H=H, lens=[T], slot_len=0, budget_ratio=0.0, budget_min=B,
+                              floor_frac=0.0, hybrid_frac=0.34)
+            slots = [[(st, n) for st, n in zip(starts, lens)]]
+            cu = np.array([0, T])
+            full = osel.hybrid_units(sens, cu, cfg)
+            fh = int(np.argmax(full[0, 0]))
+            assert full.sum() == 1 and full[0, 0, fh] == (sens[0, 0, fh] == sens[0, 0].max())
+            ftaken, fspent = osel.floor_select(util * 0 + 1, sens, cost, cu, slots, cfg, full=full)
+            assert fspent[0] == 0
+            got, spent = osel.auction(util, cost, ftaken, fspent, cu, slots, cfg, full=full)
+            # brute force: the whole head's real ops up front, then the literal
+            # greedy over the other heads with what is left
+            taken0 = np.zeros(H * 2 * T, dtype=np.uint8)
+            taken0[fh * 2 * T:(fh + 1) * 2 * T] = cost[0, fh] > 0
+            others = [(base, nodes) for h, base, nodes in slots_ops_all if h != fh]
+            want, _ = _greedy_by_enumeration(util.reshape(-1), cost.reshape(-1), taken0, others, B - T)
+            assert np.array_equal(got.reshape(-1), want), (trial, B)
+            other_ops = int(cost.sum()) - T
+            assert spent[0] == T + min(B - T, other_ops)
+
+
+def test_hybrid_floor_skips_whole_heads_and_caps_on_the_rest():
+    L = 32
+    H = 3
+    slots = [[(0, 16), (16, 16)]]
+    cost = np.zeros((1, H, 2 * L), dtype=np.uint8)
+    for h in range(H):
+        for st in (0, 16):
+            nodes = otrees.tree_nodes(st, 16)
+            cost[0, h, 2 * st] = 1
+            for j, nd in enumerate(nodes):
+                if nd[2] >= 0:
+                    cost[0, h, 2 * st + 1 + j] = 1
+    rel = np.zeros((1, H, L), dtype=np.float32)
+    rel[0, 0, 5] = 9.0          # the best leaf sits in the head kept whole
+    rel[0, 1, 7] = 2.0
+    rel[0, 2, 20] = 1.0
+    sens = np.array([[[3.0, 1.0, 1.0]]], dtype=np.float32)
+    cfg = _hybrid_cfg(H=H, lens=[L], slot_len=16, budget_ratio=0.0, budget_min=L + 20,
+                      floor_frac=0.5, hybrid_frac=0.34)
+    cu = np.array([0, L])
+    full = osel.hybrid_units(sens, cu, cfg)
+    assert full[0, 0, 0] and full.sum() == 1
+    b = common.budgets([L], cfg)[0]
+    assert b["rest"] == 20 and b["floor"] == 10
+    tr = []
+    ftaken, fspent = osel.floor_select(rel, sens, cost, cu, slots, cfg, trace=tr, full=full)
+    assert not ftaken[0, 0].any()
+    # head 1 token 7: Add + 4 splits = 5; head 2 token 20: 5 more -> 10 = F;
+    # later candidates are only those whose path is already paid (token 6
+    # shares token 7's last split)
+    assert [t[0] for t in tr[:2]] == [1 * L + 7, 2 * L + 20] and fspent[0] == 10
+    assert all(c == 0 for _, c in tr[2:]) and (1 * L + 6, 0) in tr[2:]
