@@ -47,6 +47,9 @@ int validate_params(const kvc_shape* s, const kvc_params* p) {
               "n_seeds must be in [1, 64] with n_seeds * group <= 256");
   KVC_REQUIRE(p->n_dprobe >= 1 && p->n_dprobe <= 64, KVC_E_INVAL, "n_dprobe must be in [1, 64]");
   KVC_REQUIRE(p->floor_frac >= 0.f && p->floor_frac <= 1.f, KVC_E_INVAL, "floor_frac must be in [0, 1]");
+  KVC_REQUIRE(p->hybrid_frac >= 0.f && p->hybrid_frac <= 1.f, KVC_E_INVAL, "hybrid_frac must be in [0, 1]");
+  KVC_REQUIRE(p->hybrid_frac == 0.f || (int64_t)s->n_layers * s->n_kv_heads <= 4096, KVC_E_SHAPE,
+              "the head-level hybrid needs n_layers * n_kv_heads <= 4096");
   if (!p->token_mode) {
     KVC_REQUIRE(p->slot_len >= 0 && p->slot_len <= 128, KVC_E_INVAL, "slot_len must be in [0, 128]");
     KVC_REQUIRE(p->slot_min >= 1 && p->slot_min <= p->slot_max && p->slot_max <= 128, KVC_E_INVAL,
@@ -124,7 +127,9 @@ extern "C" int kvc_budgets(const kvc_shape* shape, const kvc_params* prm, int64_
     if (b < prm->budget_min) b = prm->budget_min;
     Regions r = regions_of(L, *prm);
     int64_t a = b - (r.ss - r.c1) * units;
-    int64_t f = a > 0 ? (int64_t)std::floor((double)prm->floor_frac * (double)a) : 0;
+    // the floor shares what the units kept whole leave
+    int64_t rest = a - hybrid_units_of(a, r.c1 - r.c0, units, *prm) * (r.c1 - r.c0);
+    int64_t f = rest > 0 ? (int64_t)std::floor((double)prm->floor_frac * (double)rest) : 0;
     if (B) B[s] = b;
     if (alloc) alloc[s] = a;
     if (floor_cap) floor_cap[s] = f;

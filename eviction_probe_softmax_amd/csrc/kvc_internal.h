@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <cmath>
 #include <stddef.h>
 #include <string>
 #include <vector>
@@ -37,6 +38,15 @@ inline Regions regions_of(int64_t L, const kvc_params& p) {
   r.c1 = rs > r.pe ? rs : r.pe;
   r.c0 = r.pe;
   return r;
+}
+// Head-level hybrid: units of a sequence kept whole, given its allocatable
+// budget and its compressible tokens per unit C.
+inline int64_t hybrid_units_of(int64_t alloc, int64_t C, int64_t units, const kvc_params& p) {
+  if (!(p.hybrid_frac > 0.f) || C <= 0 || alloc <= 0) return 0;
+  int64_t k = (int64_t)std::floor((double)p.hybrid_frac * (double)units);
+  int64_t byb = alloc / C;
+  k = k < byb ? k : byb;
+  return k < units ? k : units;
 }
 int validate_shape(const kvc_shape* s);
 int validate_params(const kvc_shape* s, const kvc_params* p);

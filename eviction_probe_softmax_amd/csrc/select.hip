@@ -69,9 +69,18 @@ struct SelState {
 };
 
 // ------------------------------------------------------------------ sources
+// Per-sequence host values carried through kernel arguments.
+struct PerSeq {
+  int64_t v[MAXS];
+};
+
 struct TokSrc {       // token mode: rel of every compressible token
   const float* rel;
+  const uint8_t* full;  // [S][Ly][H] units kept whole (head-level hybrid), or NULL
+  int64_t T;
+  int LH;
   __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
+    if (full && full[(int64_t)s * LH + i / T]) return false;
     k = make_key(rel[i], (uint32_t)i);
     w = 1;
     return true;
@@ -80,10 +89,12 @@ struct TokSrc {       // token mode: rel of every compressible token
 struct LeafSrc {      // floor candidates: fp32(s_lh * r_i)
   const float* rel;
   const float* sens;  // [S][Ly][H]
+  const uint8_t* full;  // units kept whole: not candidates
   int64_t T;
   int LH;
   __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
     int lh = (int)(i / T);
+    if (full && full[(int64_t)s * LH + lh]) return false;
     float v = __fmul_rn(sens[(int64_t)s * LH + lh], rel[i]);
     k = make_key(v, (uint32_t)i);
     w = 1;
@@ -219,15 +230,55 @@ __global__ __launch_bounds__(256) void mark_tokens_kernel(Ranges r, TokSrc src, 
   for (int64_t i = threadIdx.x; i < n; i += 256) {
     uint64_t k;
     int64_t w;
-    src.get(base + i, s, k, w);
+    if (!src.get(base + i, s, k, w)) {  // a unit kept whole
+      taken[base + i] = 1;
+      continue;
+    }
     if (S_.all || k > S_.prefix) taken[base + i] = 1;
   }
 }
-__global__ void token_spent_kernel(const SelState* st, const Ranges r, int64_t* spent, int64_t* spent_floor) {
+__global__ void token_spent_kernel(const SelState* st, const Ranges r, PerSeq whole, int64_t* spent,
+                                   int64_t* spent_floor) {
   int s = threadIdx.x;
   if (s >= r.S) return;
-  spent[s] = st[s].above;
+  spent[s] = st[s].above + whole.v[s];
   if (spent_floor) spent_floor[s] = 0;
+}
+
+// ------------------------------------------------------------------ head-level hybrid
+// One block per sequence: a unit is kept whole when fewer than K units rank
+// above it by (head sensitivity desc, unit index asc); NaN ranks last.
+__global__ __launch_bounds__(256) void hybrid_units_kernel(const float* sens, int LH, PerSeq K, uint8_t* full) {
+  __shared__ float sv[4096];
+  const int s = blockIdx.x;
+  for (int u = threadIdx.x; u < LH; u += 256) {
+    float v = sens[(int64_t)s * LH + u];
+    sv[u] = v != v ? -INFINITY : v;
+  }
+  __syncthreads();
+  for (int u = threadIdx.x; u < LH; u += 256) {
+    const float x = sv[u];
+    int64_t rank = 0;
+    for (int v = 0; v < LH; ++v) {
+      const float y = sv[v];
+      rank += (y > x) || (y == x && v < u);
+    }
+    full[(int64_t)s * LH + u] = rank < K.v[s] ? 1 : 0;
+  }
+}
+// every real op of a unit kept whole is taken before the floor and the auction
+__global__ __launch_bounds__(256) void hybrid_take_kernel(Ranges r, const uint8_t* cost, const uint8_t* full, int LH,
+                                                          uint8_t* taken) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  if (!full[(int64_t)s * LH + base / r.unit_stride]) return;
+  for (int64_t i = threadIdx.x; i < n; i += 256)
+    if (cost[base + i]) taken[base + i] = 1;
+}
+__global__ void add_whole_kernel(int S, PerSeq whole, int64_t* spent) {
+  int s = threadIdx.x;
+  if (s < S) spent[s] += whole.v[s];
 }
 
 // ------------------------------------------------------------------ slot / tree helpers
@@ -296,7 +347,7 @@ __global__ __launch_bounds__(256) void floor_collect_kernel(Ranges r, LeafSrc sr
   for (int64_t i = threadIdx.x; i < n; i += 256) {
     uint64_t k;
     int64_t w;
-    src.get(base + i, s, k, w);
+    if (!src.get(base + i, s, k, w)) continue;
     if (S_.all || k > S_.prefix) {
       int slot = atomicAdd(&f.ccount[s], 1);
       if (slot < f.Fmax) {
@@ -610,6 +661,7 @@ size_t ws_auction(const kvc_shape* s, const kvc_params* p) {
   c.take<SelState>(MAXS);
   c.take<unsigned long long>((size_t)MAXS * 256);
   c.take<int64_t>(MAXS * 2);
+  c.take<uint8_t>((size_t)s->n_seq * s->n_layers * s->n_kv_heads);  // units kept whole
   if (!p->token_mode) {
     c.take<uint64_t>((size_t)E * 2);       // cover / beta
     c.take<uint64_t>((size_t)s->n_seq * Fmax);
@@ -634,16 +686,34 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   std::vector<int64_t> B(sh->n_seq), A(sh->n_seq), F(sh->n_seq);
   if ((r = kvc_budgets(sh, p, B.data(), A.data(), F.data()))) return r;
   int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
+  const int LH = sh->n_layers * sh->n_kv_heads;
   kvc::Carver c(ws, ws_bytes);
   SelState* st = c.take<SelState>(MAXS);
   unsigned long long* hist = c.take<unsigned long long>((size_t)MAXS * 256);
   int64_t* dev_i64 = c.take<int64_t>(MAXS * 2);
+  uint8_t* full_mask = c.take<uint8_t>((size_t)sh->n_seq * LH);
   int64_t* sfloor = spent_floor ? spent_floor : dev_i64;
   Ranges budget_r{};  // carries host budgets through kernel arguments
   budget_r.S = sh->n_seq;
   hipLaunchKernelGGL(zero_u64_kernel, dim3(kvc_blocks(MAXS * 256, 256)), dim3(256), 0, stream, hist,
                      (int64_t)MAXS * 256);
   KVC_LAUNCH_CHECK("zero_hist");
+  // head-level hybrid: units kept whole and the entries they take
+  PerSeq whole{}, nfull{};
+  bool hybrid = false;
+  for (int s = 0; s < sh->n_seq; ++s) {
+    kvc::Regions g = kvc::regions_of(sh->cu_seqlens[s + 1] - sh->cu_seqlens[s], *p);
+    nfull.v[s] = kvc::hybrid_units_of(A[s], g.c1 - g.c0, LH, *p);
+    whole.v[s] = nfull.v[s] * (g.c1 - g.c0);
+    hybrid |= nfull.v[s] > 0;
+  }
+  const uint8_t* full = nullptr;
+  if (hybrid) {
+    KVC_REQUIRE(head_sens, KVC_E_INVAL, "kvc_auction: the head-level hybrid needs head_sens");
+    hipLaunchKernelGGL(hybrid_units_kernel, dim3(sh->n_seq), dim3(256), 0, stream, head_sens, LH, nfull, full_mask);
+    KVC_LAUNCH_CHECK("hybrid_units");
+    full = full_mask;
+  }
 
   if (p->token_mode) {
     KVC_REQUIRE(rel, KVC_E_INVAL, "kvc_auction: token mode needs rel");
@@ -651,18 +721,18 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
     KVC_LAUNCH_CHECK("zero_taken");
     Ranges rg{};
     fill_ranges(rg, sh, p, 1, false);
-    for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = A[s];
+    for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = A[s] - whole.v[s];
     hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
                        budget_r, 0, (const int64_t*)nullptr);
     KVC_LAUNCH_CHECK("init_state");
-    TokSrc src{rel};
+    TokSrc src{rel, full, sh->total_tokens, LH};
     if ((r = run_select(rg, src, st, hist, stream))) return r;
     int64_t nb = ranges_blocks(rg);
     if (nb > 0) {
       hipLaunchKernelGGL(mark_tokens_kernel, dim3((unsigned)nb), dim3(256), 0, stream, rg, src, st, op_taken, spent);
       KVC_LAUNCH_CHECK("mark_tokens");
     }
-    hipLaunchKernelGGL(token_spent_kernel, dim3(1), dim3(MAXS), 0, stream, st, rg, spent, spent_floor);
+    hipLaunchKernelGGL(token_spent_kernel, dim3(1), dim3(MAXS), 0, stream, st, rg, whole, spent, spent_floor);
     KVC_LAUNCH_CHECK("token_spent");
     return KVC_OK;
   }
@@ -693,6 +763,14 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   ta.Ly = sh->n_layers;
   ta.H = sh->n_kv_heads;
   ta.T = sh->total_tokens;
+  Ranges ops{};
+  fill_ranges(ops, sh, p, 0, true);
+  int64_t nbo = ranges_blocks(ops);
+  if (full && nbo > 0) {
+    hipLaunchKernelGGL(hybrid_take_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, ops, trees->op_cost, full, LH,
+                       op_taken);
+    KVC_LAUNCH_CHECK("hybrid_take");
+  }
 
   // ---- floor: top-F leaves
   Ranges leaves{};
@@ -701,7 +779,7 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
                      budget_r, 0, (const int64_t*)nullptr);
   KVC_LAUNCH_CHECK("init_state");
-  LeafSrc lsrc{rel, head_sens, sh->total_tokens, sh->n_layers * sh->n_kv_heads};
+  LeafSrc lsrc{rel, head_sens, full, sh->total_tokens, LH};
   if ((r = run_select(leaves, lsrc, st, hist, stream))) return r;
   FloorArgs fa{};
   fa.ta = ta;
@@ -757,14 +835,11 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   aa.cost = trees->op_cost;
   aa.taken = op_taken;
   aa.beta = cover;
-  Ranges ops{};
-  fill_ranges(ops, sh, p, 0, true);
-  int64_t nbo = ranges_blocks(ops);
   if (nbo > 0) {
     hipLaunchKernelGGL(beta_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops);
     KVC_LAUNCH_CHECK("beta");
   }
-  for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = A[s];
+  for (int s = 0; s < sh->n_seq; ++s) budget_r.len[s] = A[s] - whole.v[s];
   hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, sh->n_seq, (const int64_t*)nullptr,
                      budget_r, 0, (const int64_t*)sfloor);
   KVC_LAUNCH_CHECK("init_state");
@@ -777,7 +852,32 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   hipLaunchKernelGGL(auction_fixup_kernel, dim3(sh->n_seq), dim3(64), 0, stream, aa, st, (const int64_t*)sfloor,
                      spent);
   KVC_LAUNCH_CHECK("auction_fixup");
+  if (hybrid) {
+    hipLaunchKernelGGL(add_whole_kernel, dim3(1), dim3(MAXS), 0, stream, sh->n_seq, whole, spent);
+    KVC_LAUNCH_CHECK("add_whole");
+  }
   hipLaunchKernelGGL(taken_normalize_kernel, dim3(kvc_blocks(E2, 256)), dim3(256), 0, stream, op_taken, E2);
   KVC_LAUNCH_CHECK("taken_normalize");
+  return KVC_OK;
+}
+
+extern "C" int kvc_hybrid_units(const kvc_shape* sh, const kvc_params* p, const float* head_sens,
+                                uint8_t* unit_full, hipStream_t stream) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  if ((r = kvc::validate_params(sh, p))) return r;
+  KVC_REQUIRE(sh->n_seq <= MAXS, KVC_E_SHAPE, "kvc_hybrid_units: at most 64 sequences per call");
+  const int LH = sh->n_layers * sh->n_kv_heads;
+  KVC_REQUIRE(LH <= 4096, KVC_E_SHAPE, "kvc_hybrid_units: n_layers * n_kv_heads must be <= 4096");
+  KVC_REQUIRE(head_sens && unit_full, KVC_E_INVAL, "kvc_hybrid_units: NULL pointer");
+  std::vector<int64_t> B(sh->n_seq), A(sh->n_seq);
+  if ((r = kvc_budgets(sh, p, B.data(), A.data(), nullptr))) return r;
+  PerSeq nfull{};
+  for (int s = 0; s < sh->n_seq; ++s) {
+    kvc::Regions g = kvc::regions_of(sh->cu_seqlens[s + 1] - sh->cu_seqlens[s], *p);
+    nfull.v[s] = kvc::hybrid_units_of(A[s], g.c1 - g.c0, LH, *p);
+  }
+  hipLaunchKernelGGL(hybrid_units_kernel, dim3(sh->n_seq), dim3(256), 0, stream, head_sens, LH, nfull, unit_full);
+  KVC_LAUNCH_CHECK("hybrid_units");
   return KVC_OK;
 }

@@ -31,7 +31,7 @@ STAGE_SCORE, STAGE_PROPAGATE, STAGE_PARTITION, STAGE_TREES, STAGE_AUCTION, STAGE
 
 EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets", "kvc_pack_capacity",
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
-           "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_pack", "kvc_full_view",
+           "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
            "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl"]
 
 
@@ -50,7 +50,7 @@ class Params(C.Structure):
                 ("value_base", C.c_float), ("floor_frac", C.c_float), ("token_mode", C.c_int32),
                 ("slot_len", C.c_int32), ("slot_min", C.c_int32), ("slot_max", C.c_int32),
                 ("slot_target", C.c_int32), ("lambda_len", C.c_float), ("lambda_curv", C.c_float),
-                ("rope_base", C.c_float)]
+                ("rope_base", C.c_float), ("hybrid_frac", C.c_float)]
 
 
 class Trees(C.Structure):
@@ -86,6 +86,7 @@ _sig = {
                               _P, _P, _P, C.c_size_t, _P]),
     "kvc_pack": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Trees), _P, _P, _P,
                            _P, _P, C.POINTER(Ragged), _P, C.c_size_t, _P]),
+    "kvc_hybrid_units": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P]),
     "kvc_full_view": (C.c_int, [C.POINTER(Shape), _P, _P, _P]),
     "kvc_decode_workspace": (C.c_size_t, [C.POINTER(Ragged), C.c_int32, C.c_int32]),
     "kvc_decode_attn": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
@@ -192,6 +193,7 @@ def make_problem(cfg, cu_seqlens: torch.Tensor, dtype: torch.dtype, device="cuda
     p.slot_len, p.slot_min, p.slot_max, p.slot_target = cfg.slot_len, cfg.slot_min, cfg.slot_max, cfg.slot_target
     p.lambda_len, p.lambda_curv = cfg.lambda_len, cfg.lambda_curv
     p.rope_base = cfg.rope_base
+    p.hybrid_frac = getattr(cfg, "hybrid_frac", 0.0)
     return Problem(sh, p, cu_host, cu_dev, dev)
 
 
@@ -294,6 +296,14 @@ def auction(pb: Problem, trees=None, rel=None, head_sens=None, slot_start=None, 
                           _ptr(spent_floor), _ptr(ws), ws.numel(), _stream())
     _check("kvc_auction", st)
     return {"taken": taken, "spent": spent, "spent_floor": spent_floor}
+
+
+def hybrid_units(pb: Problem, head_sens):
+    """Units kept whole by the head-level hybrid: uint8 [S][Ly][H]."""
+    full = torch.empty((pb.S, pb.Ly, pb.H), dtype=torch.uint8, device=pb.device)
+    st = _lib.kvc_hybrid_units(C.byref(pb.shape), C.byref(pb.params), _ptr(head_sens), _ptr(full), _stream())
+    _check("kvc_hybrid_units", st)
+    return full
 
 
 def _ragged_struct(c):

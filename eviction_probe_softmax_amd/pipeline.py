@@ -40,7 +40,7 @@ class Compressor:
         if stop_after == "propagate":
             return out
         if cfg.token_mode:
-            au = kvc.auction(pb, rel=rel)
+            au = kvc.auction(pb, rel=rel, head_sens=sc["head_sens"])
             out.update(au)
             out["cache"] = kvc.pack(pb, inp["K"], inp["V"], rel, None, au["taken"], None, None, None, None)
             return out

@@ -87,6 +87,7 @@ typedef struct kvc_params {
   float lambda_len;        /* DP slot-length penalty weight */
   float lambda_curv;       /* DP turning-score reward weight */
   float rope_base;         /* RoPE theta base */
+  float hybrid_frac;       /* head-level hybrid: share of (l, h) units kept whole (0 = off) */
 } kvc_params;
 
 typedef struct kvc_trees {
@@ -115,7 +116,9 @@ const char* kvc_last_error(void);
 /* Defaults of every parameter (values the pages state where they state one). */
 void kvc_params_default(kvc_params* p);
 /* Per-sequence budget (host arithmetic): B_s, the allocatable part (B_s minus
- * the recent window's Ly*H*n entries) and the floor cap floor(frac*alloc).
+ * the recent window's Ly*H*n entries) and the floor cap floor(frac*rest),
+ * rest = alloc minus the entries of the units the head-level hybrid keeps
+ * whole (rest = alloc when hybrid_frac = 0).
  * Returns KVC_E_BUDGET if any allocatable budget is negative. Any output
  * pointer may be NULL. */
 int kvc_budgets(const kvc_shape* shape, const kvc_params* prm, int64_t* B, int64_t* alloc,
@@ -222,11 +225,29 @@ int kvc_build_trees(const kvc_shape* shape, const kvc_params* prm, const void* K
  * Token mode (prm->token_mode): DistillCache Algorithm 1 (deterministic top-B
  * by score); trees, head_sens, slot arrays may be NULL; op_taken is then
  * [Ly][H][T]: the allocatable budget's top tokens by (rel desc, flat index
- * (l*H+h)*T + t asc). NaN utilities or scores rank below everything. */
+ * (l*H+h)*T + t asc). NaN utilities or scores rank below everything.
+ * Head-level hybrid (prm->hybrid_frac > 0; DistillCache paper, Appendix E.3:
+ * the most important heads keep their full cache, token selection runs in
+ * the others, at the same overall budget): per sequence the K units of
+ * kvc_hybrid_units keep every compressible token (tree mode: all their real
+ * ops taken; token mode: all their tokens) and are paid first; the floor,
+ * the auction and the token top-B run over the other units with the
+ * allocatable budget minus K*C (C = compressible tokens per unit). spent
+ * includes the K*C entries; spent_floor does not. head_sens is then needed
+ * in token mode too. */
 int kvc_auction(const kvc_shape* shape, const kvc_params* prm, const kvc_trees* trees,
                 const float* rel, const float* head_sens, const int32_t* slot_start,
                 const int32_t* n_slots, uint8_t* op_taken, int64_t* spent,
                 int64_t* spent_floor, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Head-level hybrid units (DistillCache paper, Appendix E.3): writes
+ * unit_full [S][Ly][H] uint8 (device), 1 for the K units of sequence s with
+ * the largest head_sens[s][l][h] (ties to the lower l*H + h; NaN ranks
+ * last), K = min(floor(hybrid_frac * Ly*H), floor(alloc / C)) with alloc the
+ * allocatable budget of kvc_budgets and C the compressible tokens per unit
+ * (K = 0 when hybrid_frac = 0 or C = 0). Requires Ly*H <= 4096. */
+int kvc_hybrid_units(const kvc_shape* shape, const kvc_params* prm, const float* head_sens,
+                     uint8_t* unit_full, hipStream_t stream);
 
 /* ------------------------------------------------------------------ A7
  * kvc_pack: write the physical ragged cache.

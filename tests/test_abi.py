@@ -44,7 +44,9 @@ def _problem(kvc, lens, **kw):
 
 def test_budgets_match_the_oracle(kvc):
     import oracle
-    for kw in ({}, {"prompt_exact": 64, "recent_exact": 32, "suffix_exact": 48}, {"budget_ratio": 1 / 128}):
+    for kw in ({}, {"prompt_exact": 64, "recent_exact": 32, "suffix_exact": 48}, {"budget_ratio": 1 / 128},
+               {"hybrid_frac": 0.2}, {"hybrid_frac": 0.75, "budget_ratio": 0.5, "floor_frac": 0.3},
+               {"hybrid_frac": 1.0, "recent_exact": 32, "budget_ratio": 0.6}):
         pb, cfg = _problem(kvc, [1100, 777, 90], **kw)
         B, A, F = pb.budgets()
         ob = oracle.budgets(cfg.lens, cfg)

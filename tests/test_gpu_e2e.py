@@ -26,11 +26,14 @@ def _run_gpu(cfg, inp):
     return out, xf, xc, klv
 
 
-@pytest.mark.parametrize("name", ["tiny", "mistral1", "stress", "ragged", "fulldepth"])
-def test_end_to_end_matches_oracle(name):
-    cfg = small_config(name)
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("mistral1", {}), ("stress", {}), ("ragged", {}),
+                                     ("fulldepth", {}), ("ragged", {"hybrid_frac": 0.5}),
+                                     ("fulldepth", {"hybrid_frac": 0.25, "budget_ratio": 0.4}),
+                                     ("mistral1", {"hybrid_frac": 0.5, "budget_ratio": 0.6})])
+def test_end_to_end_matches_oracle(name, kw):
+    cfg = small_config(name, **kw)
     inp = make_inputs(cfg)
-    print(f"[e2e] {name} lens={cfg.lens}", flush=True)
+    print(f"[e2e] {name} {kw} lens={cfg.lens}", flush=True)
     out, xf, xc, klv = _run_gpu(cfg, inp)
     o = oracle.run_pipeline(inp, cfg)
     j = jaccard(as_np(out["taken"]), o["taken"])
@@ -61,6 +64,16 @@ def test_full_budget_is_the_identity_on_gpu(name):
                 assert torch.equal(c["K"][a:a + n].cpu(), K[l, h, cu[s]:cu[s + 1]])
                 assert torch.equal(c["V"][a:a + n].cpu(), inp["V"][l, h, cu[s]:cu[s + 1]])
     assert torch.all(c["lnmu"][: int(c["seg_len"].sum())] == 0)
+    assert torch.equal(xf, xc)
+    assert torch.all(klv == 0)
+
+
+def test_whole_heads_at_full_budget_are_the_identity():
+    # the head-level hybrid keeping every unit whole is the full cache again
+    cfg = small_config("stress").replace(budget_ratio=1.0, hybrid_frac=1.0)
+    inp = make_inputs(cfg)
+    out, xf, xc, klv = _run_gpu(cfg, inp)
+    assert int(as_np(out["spent"]).sum()) == sum(cfg.lens) * cfg.Ly * cfg.H
     assert torch.equal(xf, xc)
     assert torch.all(klv == 0)
 

@@ -26,8 +26,14 @@ def _oracle_front(cfg, inp):
     return cu, sc, pr
 
 
+def _full(cfg, cu, sc):
+    return oracle.select.hybrid_units(sc["head_sens"], cu, cfg) if cfg.hybrid_frac > 0 else None
+
+
 @pytest.mark.parametrize("name,kw", [("mistral1", {}), ("ragged", {"token_mode": True, "slot_len": 0}),
-                                     ("mistral1", {"budget_ratio": 0.9})])
+                                     ("mistral1", {"budget_ratio": 0.9}),
+                                     ("mistral1", {"hybrid_frac": 0.5, "budget_ratio": 0.6}),
+                                     ("ragged", {"token_mode": True, "slot_len": 0, "hybrid_frac": 0.5})])
 def test_token_topk_and_pack_bit_exact(name, kw):
     kvc = _kvc()
     cfg = small_config(name, **kw)
@@ -37,8 +43,11 @@ def test_token_topk_and_pack_bit_exact(name, kw):
     cu, sc, pr = _oracle_front(cfg, inp)
     pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
     rel = to_dev(pr["rel"])
-    g = kvc.auction(pb, rel=rel)
-    otaken, ospent = oracle.token_topk(pr["rel"], cu, cfg)
+    g = kvc.auction(pb, rel=rel, head_sens=to_dev(sc["head_sens"]))
+    full = _full(cfg, cu, sc)
+    if cfg.hybrid_frac > 0:
+        assert np.array_equal(as_np(kvc.hybrid_units(pb, to_dev(sc["head_sens"]))).astype(bool), full)
+    otaken, ospent = oracle.token_topk(pr["rel"], cu, cfg, full)
     assert np.array_equal(as_np(g["taken"]), otaken)
     assert np.array_equal(as_np(g["spent"]), ospent)
     c = kvc.pack(pb, dinp["K"], dinp["V"], rel, None, g["taken"], None, None, None, None)
@@ -105,7 +114,11 @@ def test_trees_match_oracle(name, kw):
 
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("fulldepth", {}),
                                      ("stress", {"budget_ratio": 1.0 / 128, "floor_frac": 0.3}),
-                                     ("ragged", {"floor_frac": 0.5})])
+                                     ("ragged", {"floor_frac": 0.5}),
+                                     ("fulldepth", {"hybrid_frac": 0.25, "budget_ratio": 0.4}),
+                                     ("ragged", {"hybrid_frac": 0.5, "floor_frac": 0.3}),
+                                     ("stress", {"hybrid_frac": 0.5}),
+                                     ("tiny", {"hybrid_frac": 1.0, "budget_ratio": 1.0})])
 def test_floor_and_auction_bit_exact(name, kw):
     kvc = _kvc()
     cfg = small_config(name, **kw)
@@ -117,11 +130,14 @@ def test_floor_and_auction_bit_exact(name, kw):
         cq, kq = opart.slot_costs(inp["hidden"], cu, cfg)
     slots = oracle.slots_for(cu, cfg, cq, kq)
     o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
-    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg)
-    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg)
+    full = _full(cfg, cu, sc)
+    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg, full=full)
+    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg, full=full)
     pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
     ss, ns = slots_to_dev(slots, pb.slot_stride())
     g = kvc.auction(pb, trees_to_dev(o), to_dev(pr["rel"]), to_dev(sc["head_sens"]), ss, ns)
+    if full is not None:
+        print(f"  units kept whole: {int(full.sum())}", flush=True)
     torch.cuda.synchronize()
     assert np.array_equal(as_np(g["spent_floor"]), fs), (as_np(g["spent_floor"]), fs)
     assert np.array_equal(as_np(g["spent"]), spent), (as_np(g["spent"]), spent)
