@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--config", default="fulldepth")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the untimed-line variant measurements (head-level hybrid)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_fulldepth_traffic.json"))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run five plain device-to-device copies of MIB MiB (to scale HBM byte "
@@ -106,6 +108,46 @@ def cpu_baseline(cfg):
             "sample": (f"oracle pipeline (compress + 2 decode steps x 2 caches + KL) on {sample.lens[0]} tokens x "
                        f"1 layer x 2 KV heads of the {cfg.name} workload in {dt:.1f} s; scaled by "
                        f"token-units to {cfg.Ly} layers x {cfg.H} KV heads")}
+
+
+def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
+    """Selection variants on the same inputs, outside the headline value:
+    compression time, packed entries, decode time per call over the packed
+    cache and the per-step KL against the full cache (x_full of the timed
+    steps). Head-level hybrid: 20% of the (layer, KV head) units kept whole
+    (DistillCache paper, Appendix E.3)."""
+    import numpy as np
+    import torch
+    from eviction_probe_softmax_amd import kvc
+    from eviction_probe_softmax_amd.pipeline import Compressor, _row_view
+    out = {}
+    S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
+    for name, kw in (("head_hybrid_0.2", {"hybrid_frac": 0.2}),):
+        vcfg = cfg.replace(**kw)
+        comp = Compressor(vcfg, inp["cu_seqlens"], inp["K"].dtype)
+        x_comp = torch.empty((S, Td, Dm), dtype=torch.float32, device="cuda")
+        comp.compress(inp)  # warm-up
+        cms, dms = [], []
+        for _ in range(steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            res = comp.compress(inp)
+            e[1].record(stream)
+            dec = kvc.Decoder(res["cache"], vcfg.G, Td)
+            for t in range(Td):
+                dec.step(inp["Kd"], inp["Vd"], t + 1, inp["Qd"][t], _row_view(x_comp, t), Td * Dm)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            cms.append(e[0].elapsed_time(e[1]))
+            dms.append(e[1].elapsed_time(e[2]) / Td)
+        klv = kl_op(x_full.reshape(S * Td, Dm), x_comp.reshape(S * Td, Dm), inp["W"]).float().cpu().numpy()
+        full_units = kvc.hybrid_units(comp.pb, res["head_sens"])
+        out[name] = {"compress_ms": round(float(np.mean(cms)), 3),
+                     "decode_ms_per_call": round(float(np.mean(dms)), 4),
+                     "packed_entries": int(res["cache"]["seg_len"].to(torch.int64).sum()),
+                     "units_kept_whole": int(full_units.sum()),
+                     "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
+    return out
 
 
 def main():
@@ -245,6 +287,8 @@ def main():
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_call_comp": int(bytes_comp), "bytes_per_call_full": int(bytes_full)},
     }
+    if not args.no_variants:
+        res["variants"] = measure_variants(cfg, inp, full, x_full, kl_op, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg)
