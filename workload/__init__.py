@@ -6,4 +6,4 @@ describe. It holds none of the compression method's arithmetic, so both the
 CPU oracle and the GPU library can consume its tensors without sharing code.
 """
 from .configs import Config, CONFIGS, get_config, small_config  # noqa: F401
-from .gen import make_inputs  # noqa: F401
+from .gen import make_inputs, make_policy  # noqa: F401

@@ -43,6 +43,7 @@ class Config:
     suffix_exact: int = 0
     floor_frac: float = 0.02
     hybrid_frac: float = 0.0     # head-level hybrid: share of (layer, KV head) units kept whole
+    window: int = 64             # step-wise eviction: recent queries behind the features
     n_hops: int = 2
     n_seeds: int = 32
     hop_weight: float = 0.3

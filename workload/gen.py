@@ -217,3 +217,23 @@ def make_inputs(cfg: Config, device: str = "cpu", seed: int | None = None,
         "planted": planted,
     }
     return out
+
+
+def make_policy(seed: int = 7, hidden: int = 128, device: str = "cpu") -> Dict[str, torch.Tensor]:
+    """Seeded weights of the scoring MLP of step-wise eviction (5 features ->
+    hidden -> hidden -> 1, a LayerNorm scale and shift after each hidden
+    layer). No trained policy exists here: the weights are random draws with
+    fan-in scaling, fp32."""
+    g = torch.Generator().manual_seed(seed)
+
+    def rnd(*shape, scale=1.0):
+        return (torch.randn(shape, generator=g, dtype=torch.float64) * scale).float()
+
+    p = {
+        "w1": rnd(hidden, 5, scale=1.0 / math.sqrt(5)), "b1": rnd(hidden, scale=0.1),
+        "g1": 1.0 + rnd(hidden, scale=0.1), "be1": rnd(hidden, scale=0.1),
+        "w2": rnd(hidden, hidden, scale=1.0 / math.sqrt(hidden)), "b2": rnd(hidden, scale=0.1),
+        "g2": 1.0 + rnd(hidden, scale=0.1), "be2": rnd(hidden, scale=0.1),
+        "w3": rnd(hidden, scale=1.0 / math.sqrt(hidden)), "b3": rnd(1, scale=0.1),
+    }
+    return {k: v.contiguous().to(device) for k, v in p.items()}
