@@ -719,14 +719,14 @@ size_t ws_propagate(const kvc_shape* s, const kvc_params* p) {
 
 }  // namespace kvc
 
-extern "C" int kvc_score(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V,
-                         const void* Qprobe, float* rel0, float* feats, float* probe_lse, float* probe_ent,
-                         float* head_sens, void* ws, size_t ws_bytes, hipStream_t st) {
-  int r = kvc::validate_shape(sh);
-  if (r) return r;
-  if ((r = kvc::validate_params(sh, p))) return r;
-  KVC_REQUIRE(K && V && Qprobe && rel0 && probe_lse && probe_ent && head_sens, KVC_E_INVAL,
-              "kvc_score: NULL input or output");
+namespace kvc {
+// The probe pass with sh->total_tokens as the row stride of K, V and the
+// per-token outputs, which may exceed cu_seqlens[S] (the step-wise student
+// keeps spare slots past each sequence's tokens).
+int score_strided(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V, const void* Qprobe,
+                  float* rel0, float* feats, float* probe_lse, float* probe_ent, float* head_sens, void* ws,
+                  size_t ws_bytes, hipStream_t st) {
+  int r;
   KVC_REQUIRE(ws_bytes >= kvc::ws_score(sh, p) && ws, KVC_E_WORKSPACE, "kvc_score: workspace too small");
   int kw = pick_kw(sh);
   int64_t ns = n_splits(sh, kw);
@@ -748,6 +748,18 @@ extern "C" int kvc_score(const kvc_shape* sh, const kvc_params* p, const void* K
   hipLaunchKernelGGL(headsens_kernel, dim3(kvc_blocks(units, 256)), dim3(256), 0, st, a, head_part, head_sens);
   KVC_LAUNCH_CHECK("headsens");
   return KVC_OK;
+}
+}  // namespace kvc
+
+extern "C" int kvc_score(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V,
+                         const void* Qprobe, float* rel0, float* feats, float* probe_lse, float* probe_ent,
+                         float* head_sens, void* ws, size_t ws_bytes, hipStream_t st) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  if ((r = kvc::validate_params(sh, p))) return r;
+  KVC_REQUIRE(K && V && Qprobe && rel0 && probe_lse && probe_ent && head_sens, KVC_E_INVAL,
+              "kvc_score: NULL input or output");
+  return kvc::score_strided(sh, p, K, V, Qprobe, rel0, feats, probe_lse, probe_ent, head_sens, ws, ws_bytes, st);
 }
 
 extern "C" int kvc_propagate(const kvc_shape* sh, const kvc_params* p, const void* K, const void* Qctx,

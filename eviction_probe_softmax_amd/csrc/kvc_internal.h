@@ -48,6 +48,15 @@ inline int64_t hybrid_units_of(int64_t alloc, int64_t C, int64_t units, const kv
   k = k < byb ? k : byb;
   return k < units ? k : units;
 }
+// keep[i] = 1 for the top-budget[s] elements of each segment
+// [start[s], start[s] + len[s]) of score by (score desc, pos asc) (the element
+// index when pos is NULL); other elements of the segments get 0. Host arrays.
+size_t ws_topk_segments();
+int topk_segments(int S, const int64_t* start, const int64_t* len, const int64_t* budget, const float* score,
+                  const int32_t* pos, uint8_t* keep, void* ws, size_t ws_bytes, hipStream_t stream);
+int score_strided(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V, const void* Qprobe,
+                  float* rel0, float* feats, float* probe_lse, float* probe_ent, float* head_sens, void* ws,
+                  size_t ws_bytes, hipStream_t st);
 int validate_shape(const kvc_shape* s);
 int validate_params(const kvc_shape* s, const kvc_params* p);
 int64_t max_len(const kvc_shape* s);

@@ -627,6 +627,29 @@ __global__ __launch_bounds__(64) void auction_fixup_kernel(AucArgs a, const SelS
   }
 }
 
+// ------------------------------------------------------------------ per-segment top-B
+struct SegSrc {       // step-wise eviction: policy score per cached token, ties to the earlier position
+  const float* score;
+  const int32_t* pos;  // or NULL: the element index orders ties
+  __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
+    k = make_key(score[i], pos ? (uint32_t)pos[i] : (uint32_t)i);
+    w = 1;
+    return true;
+  }
+};
+__global__ __launch_bounds__(256) void mark_keep_kernel(Ranges r, SegSrc src, const SelState* st, uint8_t* keep) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  SelState S_ = st[s];
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    uint64_t k;
+    int64_t w;
+    src.get(base + i, s, k, w);
+    keep[base + i] = (S_.all || k > S_.prefix) ? 1 : 0;
+  }
+}
+
 __global__ void taken_normalize_kernel(uint8_t* taken, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n && taken[i]) taken[i] = 1;
@@ -881,3 +904,48 @@ extern "C" int kvc_hybrid_units(const kvc_shape* sh, const kvc_params* p, const 
   KVC_LAUNCH_CHECK("hybrid_units");
   return KVC_OK;
 }
+
+namespace kvc {
+size_t ws_topk_segments() {
+  Carver c(nullptr, 0);
+  c.take<SelState>(MAXS);
+  c.take<unsigned long long>((size_t)MAXS * 256);
+  return c.off + 256;
+}
+
+int topk_segments(int S, const int64_t* start, const int64_t* len, const int64_t* budget, const float* score,
+                  const int32_t* pos, uint8_t* keep, void* ws, size_t ws_bytes, hipStream_t stream) {
+  KVC_REQUIRE(S >= 1 && S <= MAXS, KVC_E_SHAPE, "top-B: 1 to 64 segments");
+  KVC_REQUIRE(ws && ws_bytes >= ws_topk_segments(), KVC_E_WORKSPACE, "top-B: workspace too small");
+  Carver c(ws, ws_bytes);
+  SelState* st = c.take<SelState>(MAXS);
+  unsigned long long* hist = c.take<unsigned long long>((size_t)MAXS * 256);
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(kvc_blocks(MAXS * 256, 256)), dim3(256), 0, stream, hist,
+                     (int64_t)MAXS * 256);
+  KVC_LAUNCH_CHECK("zero_hist");
+  Ranges r{};
+  r.S = S;
+  r.U = 1;
+  r.unit_stride = 0;
+  Ranges budget_r{};
+  budget_r.S = S;
+  for (int s = 0; s < S; ++s) {
+    r.start[s] = start[s];
+    r.len[s] = len[s];
+    r.nchunk[s] = (len[s] + CH - 1) / CH;
+    budget_r.len[s] = budget[s];
+  }
+  hipLaunchKernelGGL(init_state_kernel, dim3(1), dim3(MAXS), 0, stream, st, S, (const int64_t*)nullptr, budget_r, 0,
+                     (const int64_t*)nullptr);
+  KVC_LAUNCH_CHECK("init_state");
+  SegSrc src{score, pos};
+  int rc = run_select(r, src, st, hist, stream);
+  if (rc) return rc;
+  int64_t nb = ranges_blocks(r);
+  if (nb > 0) {
+    hipLaunchKernelGGL(mark_keep_kernel, dim3((unsigned)nb), dim3(256), 0, stream, r, src, st, keep);
+    KVC_LAUNCH_CHECK("mark_keep");
+  }
+  return KVC_OK;
+}
+}  // namespace kvc

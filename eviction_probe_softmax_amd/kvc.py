@@ -32,7 +32,8 @@ STAGE_SCORE, STAGE_PROPAGATE, STAGE_PARTITION, STAGE_TREES, STAGE_AUCTION, STAGE
 EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets", "kvc_pack_capacity",
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
            "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
-           "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl"]
+           "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
+           "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune"]
 
 
 class Shape(C.Structure):
@@ -50,12 +51,22 @@ class Params(C.Structure):
                 ("value_base", C.c_float), ("floor_frac", C.c_float), ("token_mode", C.c_int32),
                 ("slot_len", C.c_int32), ("slot_min", C.c_int32), ("slot_max", C.c_int32),
                 ("slot_target", C.c_int32), ("lambda_len", C.c_float), ("lambda_curv", C.c_float),
-                ("rope_base", C.c_float), ("hybrid_frac", C.c_float)]
+                ("rope_base", C.c_float), ("hybrid_frac", C.c_float), ("window", C.c_int32)]
 
 
 class Trees(C.Structure):
     _fields_ = [("node_rel", C.c_void_p), ("node_D", C.c_void_p), ("node_mu", C.c_void_p),
                 ("op_util", C.c_void_p), ("op_cost", C.c_void_p)]
+
+
+class Policy(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("w1", "b1", "g1", "be1", "w2", "b2", "g2", "be2", "w3", "b3")]
+
+
+class Student(C.Structure):
+    _fields_ = [("K", C.c_void_p), ("V", C.c_void_p), ("pos", C.c_void_p), ("Qwin", C.c_void_p),
+                ("seg_off", C.c_void_p), ("seg_len", C.c_void_p), ("seq_off", C.POINTER(C.c_int64)),
+                ("seq_cap", C.POINTER(C.c_int32)), ("seq_len", C.POINTER(C.c_int32)), ("cap_total", C.c_int64)]
 
 
 class Ragged(C.Structure):
@@ -91,6 +102,14 @@ _sig = {
     "kvc_decode_workspace": (C.c_size_t, [C.POINTER(Ragged), C.c_int32, C.c_int32]),
     "kvc_decode_attn": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
                                   C.c_int64, _P, _P, C.c_size_t, _P]),
+    "kvc_step_capacity": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.c_int32, _P]),
+    "kvc_step_workspace": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params), C.c_int64]),
+    "kvc_step_init": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Policy),
+                                C.POINTER(Student), _P, _P, _P, C.c_size_t, _P]),
+    "kvc_step_append": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.POINTER(Student), _P, _P, _P, C.c_int32,
+                                  C.c_int32, _P]),
+    "kvc_step_prune": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.POINTER(Student), C.c_int32,
+                                 C.POINTER(Policy), _P, _P, _P, C.c_size_t, _P]),
     "kvc_kl_workspace": (C.c_size_t, [C.c_int64, C.c_int32, C.c_int32, C.c_int32]),
     "kvc_kl": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]),
 }
@@ -194,6 +213,7 @@ def make_problem(cfg, cu_seqlens: torch.Tensor, dtype: torch.dtype, device="cuda
     p.lambda_len, p.lambda_curv = cfg.lambda_len, cfg.lambda_curv
     p.rope_base = cfg.rope_base
     p.hybrid_frac = getattr(cfg, "hybrid_frac", 0.0)
+    p.window = getattr(cfg, "window", 64)
     return Problem(sh, p, cu_host, cu_dev, dev)
 
 
@@ -388,3 +408,75 @@ class KL:
 def kl(x_full, x_comp, W):
     n, dm = x_full.shape
     return KL(n, dm, W.shape[0], W.dtype, device=x_full.device)(x_full, x_comp, W)
+
+
+class Stepwise:
+    """Step-wise eviction (kvc_step_*): a student cache with one slot region
+    per sequence, sized for t_steps decode steps, and its window of recent
+    queries. ``policy`` holds the scoring MLP's fp32 tensors on the device."""
+
+    def __init__(self, pb: Problem, policy, t_steps: int, dtype, group: int):
+        S, Ly, H, d = pb.S, pb.Ly, pb.H, pb.shape.head_dim
+        dev = pb.device
+        self.pb, self.t_steps, self.group = pb, t_steps, group
+        caps = (C.c_int32 * S)()
+        _check("kvc_step_capacity", _lib.kvc_step_capacity(C.byref(pb.shape), C.byref(pb.params), t_steps, caps))
+        self.caps = [int(c) for c in caps]
+        offs = [0]
+        for c in self.caps[:-1]:
+            offs.append(offs[-1] + c)
+        self.cap_total = sum(self.caps)
+        self._off = (C.c_int64 * S)(*offs)
+        self._cap = (C.c_int32 * S)(*self.caps)
+        self._len = (C.c_int32 * S)()
+        self.K = torch.empty((Ly, H, self.cap_total, d), dtype=dtype, device=dev)
+        self.V = torch.empty_like(self.K)
+        self.pos = torch.zeros((self.cap_total,), dtype=torch.int32, device=dev)
+        self.Qwin = torch.empty((S, Ly, H * group, pb.params.window, d), dtype=dtype, device=dev)
+        self.seg_off = torch.empty((S, Ly, H), dtype=torch.int64, device=dev)
+        self.seg_len = torch.empty((S, Ly, H), dtype=torch.int32, device=dev)
+        self.st = Student(K=_ptr(self.K), V=_ptr(self.V), pos=_ptr(self.pos), Qwin=_ptr(self.Qwin),
+                          seg_off=_ptr(self.seg_off), seg_len=_ptr(self.seg_len), seq_off=self._off,
+                          seq_cap=self._cap, seq_len=self._len, cap_total=self.cap_total)
+        self._pol_t = policy
+        self.pol = Policy(**{k: _ptr(policy[k]) for k in ("w1", "b1", "g1", "be1", "w2", "b2", "g2", "be2",
+                                                         "w3", "b3")})
+        n = int(_lib.kvc_step_workspace(C.byref(pb.shape), C.byref(pb.params), self.cap_total))
+        if n == 0:
+            raise KvcError("kvc_step_workspace", -1)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.decoder = None
+
+    @property
+    def lengths(self):
+        return [int(x) for x in self._len]
+
+    def init(self, K, V, Qctx, feats=None, scores=None):
+        st = _lib.kvc_step_init(C.byref(self.pb.shape), C.byref(self.pb.params), _ptr(K), _ptr(V), _ptr(Qctx),
+                                C.byref(self.pol), C.byref(self.st), _ptr(feats), _ptr(scores), _ptr(self.ws),
+                                self.ws.numel(), _stream())
+        _check("kvc_step_init", st)
+
+    def append(self, K_tail, V_tail, Q_t, t):
+        st = _lib.kvc_step_append(C.byref(self.pb.shape), C.byref(self.pb.params), C.byref(self.st), _ptr(K_tail),
+                                  _ptr(V_tail), _ptr(Q_t), t, self.t_steps, _stream())
+        _check("kvc_step_append", st)
+
+    def prune(self, t, feats=None, scores=None):
+        st = _lib.kvc_step_prune(C.byref(self.pb.shape), C.byref(self.pb.params), C.byref(self.st), t,
+                                 C.byref(self.pol), _ptr(feats), _ptr(scores), _ptr(self.ws), self.ws.numel(),
+                                 _stream())
+        _check("kvc_step_prune", st)
+
+    def view(self):
+        """The occupied slots as a ragged cache for kvc_decode_attn (no tail)."""
+        d = self.pb.shape.head_dim
+        return {"K": self.K.reshape(-1, d), "V": self.V.reshape(-1, d), "lnmu": None, "pos": self.pos,
+                "seg_off": self.seg_off, "seg_len": self.seg_len, "n_seq": self.pb.S, "n_layers": self.pb.Ly,
+                "n_kv_heads": self.pb.H, "head_dim": d, "max_seg": int(max(self.caps))}
+
+    def decode(self, K_tail, V_tail, Q_t, x_out, x_stride):
+        """Attention of Q_t over the occupied slots (the appended token included)."""
+        if self.decoder is None:
+            self.decoder = Decoder(self.view(), self.group, self.t_steps)
+        self.decoder.step(K_tail, V_tail, 0, Q_t, x_out, x_stride)

@@ -91,3 +91,46 @@ class _RowView:
 
 def _row_view(x, t):
     return _RowView(x, t)
+
+
+def run_stepwise(cfg, inp, policy, record=None):
+    """Step-wise eviction over the decode steps (DistillCache paper,
+    Algorithm 1): prune the prefill cache once, then per step append the new
+    pair, decode over the student, prune; the full cache is decoded beside it
+    and the per-step KL compares the two. ``record`` (a list) receives HIP
+    event pairs (init, per-step prune) on the library's stream."""
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    sw = kvc.Stepwise(pb, policy, cfg.T_dec, inp["K"].dtype, cfg.G)
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    e0 = ev() if record is not None else None
+    sw.init(inp["K"], inp["V"], inp["Qctx"])
+    if record is not None:
+        record.append(("init", e0, ev()))
+    full = kvc.full_view(pb, inp["K"], inp["V"])
+    dfull = kvc.Decoder(full, cfg.G, cfg.T_dec)
+    S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
+    x_full = torch.empty((S, Td, Dm), dtype=torch.float32, device=inp["K"].device)
+    x_comp = torch.empty_like(x_full)
+    for t in range(Td):
+        q = inp["Qd"][t]
+        dfull.step(inp["Kd"], inp["Vd"], t + 1, q, _row_view(x_full, t), Td * Dm)
+        e0 = ev() if record is not None else None
+        sw.append(inp["Kd"], inp["Vd"], q, t)
+        sw.decode(inp["Kd"], inp["Vd"], q, _row_view(x_comp, t), Td * Dm)
+        e1 = ev() if record is not None else None
+        sw.prune(t)
+        if record is not None:
+            record.append(("step", e0, e1, ev()))
+    klv = kvc.kl(x_full.reshape(S * Td, Dm), x_comp.reshape(S * Td, Dm), inp["W"]).reshape(S, Td)
+    pos = sw.pos.cpu()
+    kept, off = [], 0
+    for s in range(S):
+        kept.append(pos[off:off + sw.lengths[s]].numpy().copy())
+        off += sw.caps[s]
+    return {"x_full": x_full, "x_comp": x_comp, "kl": klv, "kept": kept, "stepwise": sw}

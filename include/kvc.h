@@ -88,6 +88,7 @@ typedef struct kvc_params {
   float lambda_curv;       /* DP turning-score reward weight */
   float rope_base;         /* RoPE theta base */
   float hybrid_frac;       /* head-level hybrid: share of (l, h) units kept whole (0 = off) */
+  int32_t window;          /* step-wise eviction: recent queries behind the features (w = 64) */
 } kvc_params;
 
 typedef struct kvc_trees {
@@ -297,6 +298,73 @@ size_t kvc_kl_workspace(int64_t n_pairs, int32_t d_model, int32_t vocab, int32_t
 int kvc_kl(int64_t n_pairs, int32_t d_model, int32_t vocab, const float* x_full,
            const float* x_comp, const void* W, int32_t w_dtype, float* kl_out, void* ws,
            size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ step-wise eviction
+ * DistillCache paper, Sec. 3.1.1 (per-token state: attention mass, value
+ * norm, variance across heads, attention-weighted entropy of the recent
+ * queries, position), Sec. 3.1.2 (deterministic top-B by the policy score)
+ * and Algorithm 1 (after every decode step the new pair is appended, the
+ * cache is scored and pruned to B = max(floor(r * n_seen), B_min), n_seen
+ * the tokens seen so far: L before the first step, L + t + 1 after step t).
+ * Features of a cached token, over all layers, query heads and the w window
+ * queries (each attends the whole current cache): mean attention mass,
+ * mean value norm over (l, h), population variance over the Ly*H*G query
+ * heads of the window-mean mass, sum a*H(a) / sum a, position /
+ * max(n_seen - 1, 1). Score: Linear(5,128) -> LayerNorm -> ReLU ->
+ * Linear(128,128) -> LayerNorm -> ReLU -> Linear(128,1), LayerNorm eps 1e-5.
+ * Kept: the top-B by (fp32 score desc, position asc); the same tokens leave
+ * every (l, h). No region is protected. Window size prm->window (multiple of
+ * 8, group * window <= 256, every sequence at least window tokens long). */
+typedef struct kvc_policy {
+  const float* w1;         /* [128][5] */
+  const float* b1;         /* [128] */
+  const float* g1;         /* [128] LayerNorm scale */
+  const float* be1;        /* [128] LayerNorm shift */
+  const float* w2;         /* [128][128] */
+  const float* b2, *g2, *be2;  /* [128] each */
+  const float* w3;         /* [128] */
+  const float* b3;         /* [1] */
+} kvc_policy;
+
+typedef struct kvc_student {
+  void* K;                 /* [Ly][H][cap_total][d] kept keys (cache dtype), slot order */
+  void* V;                 /* [Ly][H][cap_total][d] */
+  int32_t* pos;            /* [cap_total] sequence position of each slot's token */
+  void* Qwin;              /* [S][Ly][H*G][window][d] window queries (ring, queries dtype) */
+  int64_t* seg_off;        /* DEVICE [S][Ly][H] ragged view of the occupied slots (for kvc_decode_attn) */
+  int32_t* seg_len;        /* DEVICE [S][Ly][H] */
+  const int64_t* seq_off;  /* HOST [S] first slot of sequence s (regions must not overlap) */
+  const int32_t* seq_cap;  /* HOST [S] slots of sequence s (kvc_step_capacity) */
+  int32_t* seq_len;        /* HOST [S] occupied slots; the calls below update it */
+  int64_t cap_total;       /* slots per (l, h) */
+} kvc_student;
+
+/* Slots each sequence needs for t_steps decode steps: the largest cache
+ * before a prune, min(L + t_steps, max(floor(r (L + t_steps)), B_min) + 1). */
+int kvc_step_capacity(const kvc_shape* shape, const kvc_params* prm, int32_t t_steps, int32_t* seq_cap);
+size_t kvc_step_workspace(const kvc_shape* shape, const kvc_params* prm, int64_t cap_total);
+/* Fill the window with the last `window` prefill queries of every sequence
+ * (Qctx [Ly][H*G][T][d]), score the prefill cache (K, V [Ly][H][T][d]), keep
+ * the top-B of each sequence and write them to the student in position
+ * order; sets seq_len and the ragged view. feats_out [5][T] and scores_out
+ * [T] (fp32, nullable) receive the features and scores. */
+int kvc_step_init(const kvc_shape* shape, const kvc_params* prm, const void* K, const void* V,
+                  const void* Qctx, const kvc_policy* policy, kvc_student* st, float* feats_out,
+                  float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Step t: append decode token t of every sequence (K_tail/V_tail
+ * [Ly][H][S][t_cap][d], position L_s + t) to the student, replace the
+ * oldest window query with Q_t ([S][Ly][H*G][d]) and refresh the ragged
+ * view; decoding q_t then reads the student through kvc_decode_attn with
+ * t_valid = 0. KVC_E_SHAPE if a sequence has no free slot. */
+int kvc_step_append(const kvc_shape* shape, const kvc_params* prm, kvc_student* st, const void* K_tail,
+                    const void* V_tail, const void* Q_t, int32_t t, int32_t t_cap, hipStream_t stream);
+/* Step t: score the student's tokens with the window (n_seen = L + t + 1),
+ * keep the top-B of each sequence; an evicted slot below the new length is
+ * refilled by a kept token from the slots past it. feats_out [5][cap_total]
+ * and scores_out [cap_total] (slot order, nullable). */
+int kvc_step_prune(const kvc_shape* shape, const kvc_params* prm, kvc_student* st, int32_t t,
+                   const kvc_policy* policy, float* feats_out, float* scores_out, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

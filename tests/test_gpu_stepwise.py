@@ -1,0 +1,148 @@
+"""GPU parity of step-wise eviction (kvc_step_*) against the oracle
+(DistillCache paper, Sec. 3.1.1 features, Sec. 3.1.2 top-B, Algorithm 1):
+features and scores of every cached token within tolerance, the kept set
+bit-exact given the scores, the student's rows bit copies of the kept
+tokens, decode over the student, and the whole loop end to end."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import stepwise as osw, common
+from workload import small_config, make_inputs, make_policy
+from parity import close, as_np, inputs_to, jaccard
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(name="stress", **kw):
+    from eviction_probe_softmax_amd import kvc
+    cfg = small_config(name).replace(window=kw.pop("window", 64), **kw)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    pol_h = make_policy(seed=11)
+    pol = {k: v.cuda() for k, v in pol_h.items()}
+    sw = kvc.Stepwise(pb, pol, cfg.T_dec, inp["K"].dtype, cfg.G)
+    return kvc, cfg, inp, dinp, pb, pol_h, sw
+
+
+def _student_rows(sw, s):
+    off = int(sum(sw.caps[:s]))
+    n = sw.lengths[s]
+    K = common.to64(sw.K[:, :, off:off + n].cpu())
+    V = common.to64(sw.V[:, :, off:off + n].cpu())
+    pos = as_np(sw.pos[off:off + n]).astype(np.int64)
+    return off, n, K, V, pos
+
+
+def _check_scores_and_keep(feats_g, scores_g, Kc, Vc, pos, Qwin, n_seen, pol_h, B, kept_pos):
+    want_f = osw.window_features(Kc, Vc, pos, Qwin, n_seen)
+    for c, nm in enumerate(["alpha", "vnorm", "sigma", "H", "pos"]):
+        close(feats_g[c], want_f[:, c], 1e-3, f"feature {nm}", floor=1e-3 * float(np.abs(want_f[:, c]).max()))
+    # the MLP alone: the oracle's policy on the GPU's features
+    close(scores_g, osw.policy_scores(feats_g.T.astype(np.float64), pol_h), 1e-4, "policy scores", floor=1e-4)
+    # end to end scores
+    close(scores_g, osw.policy_scores(want_f, pol_h), 1e-3, "scores", floor=1e-3)
+    # selection given the GPU's scores: bit-exact
+    keep = osw.keep_top(scores_g.astype(np.float32), pos, B)
+    assert np.array_equal(np.sort(pos[keep]), np.sort(kept_pos))
+
+
+def test_init_scores_select_and_gather():
+    kvc, cfg, inp, dinp, pb, pol_h, sw = _setup()
+    T = cfg.T
+    feats = torch.zeros((5, T), dtype=torch.float32, device="cuda")
+    scores = torch.zeros((T,), dtype=torch.float32, device="cuda")
+    sw.init(dinp["K"], dinp["V"], dinp["Qctx"], feats, scores)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].numpy()
+    K, V, Qctx = common.to64(inp["K"]), common.to64(inp["V"]), common.to64(inp["Qctx"])
+    for s in range(cfg.S):
+        a0, L = int(cu[s]), int(cu[s + 1] - cu[s])
+        print(f"[step init] seq {s} L={L}", flush=True)
+        B = osw.step_budget(L, cfg)
+        off, n, Ks, Vs, pos = _student_rows(sw, s)
+        assert n == min(B, L)
+        assert np.all(np.diff(pos) > 0)          # position order after the first prune
+        Qwin = Qctx[:, :, a0 + L - cfg.window:a0 + L]
+        _check_scores_and_keep(as_np(feats[:, a0:a0 + L]), as_np(scores[a0:a0 + L]), K[:, :, a0:a0 + L],
+                               V[:, :, a0:a0 + L], np.arange(L), Qwin, L, pol_h, B, pos)
+        # rows are bit copies of the kept tokens
+        assert np.array_equal(Ks, K[:, :, a0 + pos]) and np.array_equal(Vs, V[:, :, a0 + pos])
+
+
+@pytest.mark.parametrize("r", [0.25, 0.05])
+def test_steps_append_decode_prune(r):
+    kvc, cfg, inp, dinp, pb, pol_h, sw = _setup(budget_ratio=r, T_dec=6)
+    sw.init(dinp["K"], dinp["V"], dinp["Qctx"])
+    cu = inp["cu_seqlens"].numpy()
+    K, V, Qctx = common.to64(inp["K"]), common.to64(inp["V"]), common.to64(inp["Qctx"])
+    Kd, Vd, Qd = common.to64(inp["Kd"]), common.to64(inp["Vd"]), common.to64(inp["Qd"])
+    cap = sw.cap_total
+    feats = torch.zeros((5, cap), dtype=torch.float32, device="cuda")
+    scores = torch.zeros((cap,), dtype=torch.float32, device="cuda")
+    Dm = cfg.d_model
+    x = torch.zeros((cfg.S, Dm), dtype=torch.float32, device="cuda")
+    G, d = cfg.G, cfg.d
+    for t in range(cfg.T_dec):
+        print(f"[step] r={r} t={t} lengths={sw.lengths}", flush=True)
+        sw.append(dinp["Kd"], dinp["Vd"], dinp["Qd"][t].contiguous(), t)
+        sw.decode(dinp["Kd"], dinp["Vd"], dinp["Qd"][t].contiguous(), x, Dm)
+        torch.cuda.synchronize()
+        before = [_student_rows(sw, s) for s in range(cfg.S)]
+        for s in range(cfg.S):
+            off, n, Ks, Vs, pos = before[s]
+            L = int(cu[s + 1] - cu[s])
+            assert pos[-1] == L + t and len(set(pos.tolist())) == n
+            # decode over exactly the student's tokens
+            want = np.zeros(Dm)
+            for l in range(cfg.Ly):
+                for qh in range(cfg.H * G):
+                    z = Ks[l, qh // G] @ Qd[t, s, l, qh] / math.sqrt(d)
+                    p = np.exp(z - z.max())
+                    want[qh * d:(qh + 1) * d] += (p / p.sum()) @ Vs[l, qh // G]
+            close(x[s], want, 2e-2, "student decode", floor=1e-3)
+        sw.prune(t, feats, scores)
+        torch.cuda.synchronize()
+        for s in range(cfg.S):
+            off, n, Ks, Vs, pos = before[s]
+            L, a0 = int(cu[s + 1] - cu[s]), int(cu[s])
+            B = osw.step_budget(L + t + 1, cfg)
+            off2, n2, Ks2, Vs2, pos2 = _student_rows(sw, s)
+            assert n2 == min(B, n)
+            hist = [Qctx[:, :, a0 + i] for i in range(L)] + [Qd[u, s] for u in range(t + 1)]
+            Qwin = np.stack(hist[-cfg.window:], axis=2)
+            _check_scores_and_keep(as_np(feats[:, off:off + n]), as_np(scores[off:off + n]), Ks, Vs, pos, Qwin,
+                                   L + t + 1, pol_h, B, pos2)
+            # every kept row still holds its token's bits
+            src = {int(p): i for i, p in enumerate(pos)}
+            idx = [src[int(p)] for p in pos2]
+            assert np.array_equal(Ks2, Ks[:, :, idx]) and np.array_equal(Vs2, Vs[:, :, idx])
+
+
+@pytest.mark.parametrize("name,kw", [("stress", {}), ("ragged", {"prompt_exact": 0, "recent_exact": 0,
+                                                                 "suffix_exact": 0}),
+                                     ("stress", {"budget_ratio": 1.0})])
+def test_stepwise_end_to_end(name, kw):
+    from eviction_probe_softmax_amd.pipeline import run_stepwise
+    kvc, cfg, inp, dinp, pb, pol_h, sw = _setup(name, **kw)
+    print(f"[stepwise e2e] {name} {kw}", flush=True)
+    pol = {k: v.cuda() for k, v in pol_h.items()}
+    out = run_stepwise(cfg, dinp, pol)
+    o = osw.run_stepwise(inp, cfg, pol_h)
+    js = []
+    for s in range(cfg.S):
+        js.append(jaccard(np.isin(np.arange(cfg.lens[s] + cfg.T_dec), out["kept"][s]),
+                          np.isin(np.arange(cfg.lens[s] + cfg.T_dec), o["kept"][s])))
+    j = min(js)
+    close(out["x_full"], o["x_full"], 2e-2, "x_full", floor=1e-3)
+    err = np.abs(as_np(out["kl"]) - o["kl"])
+    print(f"  jaccard={j:.4f} kl_oracle_mean={o['kl'].mean():.4f} max|dKL|={err.max():.2e}", flush=True)
+    assert j >= 0.99, j
+    if j == 1.0:
+        close(out["x_comp"], o["x_comp"], 2e-2, "x_comp", floor=1e-3)
+        assert err.max() <= 1e-3
+    if kw.get("budget_ratio") == 1.0:
+        assert np.abs(as_np(out["kl"])).max() <= 1e-5
