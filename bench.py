@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the untimed-line variant measurements (head-level hybrid)")
+                    help="skip the variant measurements beside the headline line (head-level hybrid, "
+                         "step-wise eviction)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_fulldepth_traffic.json"))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run five plain device-to-device copies of MIB MiB (to scale HBM byte "
@@ -115,7 +116,8 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     compression time, packed entries, decode time per call over the packed
     cache and the per-step KL against the full cache (x_full of the timed
     steps). Head-level hybrid: 20% of the (layer, KV head) units kept whole
-    (DistillCache paper, Appendix E.3)."""
+    (DistillCache paper, Appendix E.3). Step-wise eviction: the scoring-MLP
+    loop of DistillCache's Algorithm 1 at the same budget ratio."""
     import numpy as np
     import torch
     from eviction_probe_softmax_amd import kvc
@@ -147,6 +149,26 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
                      "packed_entries": int(res["cache"]["seg_len"].to(torch.int64).sum()),
                      "units_kept_whole": int(full_units.sum()),
                      "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
+    # Step-wise eviction (DistillCache Algorithm 1) with a seeded scoring MLP:
+    # one prefill prune, then per decode step append + decode + score + prune
+    from workload import make_policy
+    from eviction_probe_softmax_amd.pipeline import run_stepwise
+    pol = make_policy(device="cuda")
+    run_stepwise(cfg, inp, pol)  # warm-up
+    rec = []
+    torch.cuda.synchronize()
+    res = run_stepwise(cfg, inp, pol, record=rec)
+    torch.cuda.synchronize()
+    init_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "init"]
+    dec_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "step"]
+    prune_ms = [r[2].elapsed_time(r[3]) for r in rec if r[0] == "step"]
+    klv = res["kl"].float().cpu().numpy()
+    out["stepwise_r%g" % cfg.budget_ratio] = {
+        "init_prune_ms": round(float(np.mean(init_ms)), 3),
+        "append_decode_ms_per_step": round(float(np.mean(dec_ms)), 4),
+        "score_prune_ms_per_step": round(float(np.mean(prune_ms)), 4),
+        "cached_entries_last_step": int(sum(res["stepwise"].lengths)) * cfg.Ly * cfg.H,
+        "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
     return out
 
 

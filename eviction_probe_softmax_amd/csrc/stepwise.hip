@@ -18,7 +18,7 @@
 // 1. the probe pass (rowstats / colsum of the scoring path) with the w
 //    window queries as probes writes per-(l, h) features of every slot;
 // 2. policy_kernel folds them over all (l, h) into the five features and
-//    runs the MLP, one thread per token, weights in LDS;
+//    runs the MLP, 16 tokens per workgroup, weights in LDS;
 // 3. the segmented radix select keeps the top-B by (score, position);
 // 4. evict_pairs_kernel pairs holes below the new length with kept slots
 //    past it; move_rows_kernel copies those rows (K, V, position).
@@ -51,8 +51,27 @@ struct PolArgs {
   float* score;         // [n]
 };
 
+// A workgroup scores TOK tokens; its NSL slices of TOK threads split the
+// fold over units and the hidden units of both layers (JS each), meeting in
+// LDS for the LayerNorm statistics and the output sum.
 constexpr int PT = 256;
+constexpr int TOK = 16;
+constexpr int NSL = PT / TOK;    // 16 slices
+constexpr int JS = HID / NSL;    // 8 hidden units per slice
 constexpr int W1N = HID * 5, W2N = HID * HID;
+constexpr int HPAD = HID + 1;    // h1 and w2 rows padded against bank conflicts
+constexpr int W2S = HPAD * HID;
+
+__device__ __forceinline__ float slice_sum(float* red, int q, int tok, float v) {
+  // sum of v over the NSL slices of one token (all threads return it)
+  red[q * TOK + tok] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int k = 0; k < NSL; ++k) t += red[k * TOK + tok];
+  __syncthreads();
+  return t;
+}
 
 __global__ __launch_bounds__(PT) void policy_kernel(PolArgs a) {
   extern __shared__ float pl[];
@@ -60,13 +79,15 @@ __global__ __launch_bounds__(PT) void policy_kernel(PolArgs a) {
   float* b1 = w1 + W1N;
   float* g1 = b1 + HID;
   float* be1 = g1 + HID;
-  float* w2 = be1 + HID;          // [128][128]
-  float* b2 = w2 + W2N;
+  float* w2 = be1 + HID;          // [128][HPAD]
+  float* b2 = w2 + W2S;
   float* g2 = b2 + HID;
   float* be2 = g2 + HID;
   float* w3 = be2 + HID;
+  float* h1 = w3 + HID;           // [TOK][HPAD]
+  float* red = h1 + TOK * HPAD;   // [NSL][TOK]
   for (int i = threadIdx.x; i < W1N; i += PT) w1[i] = a.pol.w1[i];
-  for (int i = threadIdx.x; i < W2N; i += PT) w2[i] = a.pol.w2[i];
+  for (int i = threadIdx.x; i < W2N; i += PT) w2[(i / HID) * HPAD + i % HID] = a.pol.w2[i];
   for (int i = threadIdx.x; i < HID; i += PT) {
     b1[i] = a.pol.b1[i];
     g1[i] = a.pol.g1[i];
@@ -77,87 +98,99 @@ __global__ __launch_bounds__(PT) void policy_kernel(PolArgs a) {
     w3[i] = a.pol.w3[i];
   }
   __syncthreads();
-  const int i = blockIdx.x * PT + threadIdx.x;
-  if (i >= a.n) return;
-  // fold the per-(l, h) features over every unit (consecutive threads read
-  // consecutive tokens of one unit)
+  const int tok = threadIdx.x % TOK, q = threadIdx.x / TOK;
+  const int i = blockIdx.x * TOK + tok;
+  const bool live = i < a.n;
+  const int ic = live ? i : a.n - 1;
+  // fold the per-(l, h) features over every unit: slice q takes units q, q+NSL, ...
   const int64_t plane = (int64_t)a.U * a.stride;
-  const float* f0 = a.feats + i;
-  float s0 = 0.f, s1 = 0.f, s3 = 0.f;
-  for (int u = 0; u < a.U; ++u) {
+  const float* f0 = a.feats + ic;
+  float p0 = 0.f, p1 = 0.f, p3 = 0.f;
+  for (int u = q; u < a.U; u += NSL) {
     const int64_t o = (int64_t)u * a.stride;
     const float m = f0[o];
-    s0 += m;
-    s1 += f0[plane + o];
-    s3 += f0[3 * plane + o] * m;
+    p0 += m;
+    p1 += f0[plane + o];
+    p3 += f0[3 * plane + o] * m;
   }
+  const float s0 = slice_sum(red, q, tok, p0);
+  const float s1 = slice_sum(red, q, tok, p1);
+  const float s3 = slice_sum(red, q, tok, p3);
   // variance over all U*G query heads of the per-head mass: the mean of the
   // per-unit variances plus the variance of the per-unit means
   const float M = s0 / (float)(a.U * a.G);
-  float sv = 0.f;
-  for (int u = 0; u < a.U; ++u) {
+  float pv = 0.f;
+  for (int u = q; u < a.U; u += NSL) {
     const int64_t o = (int64_t)u * a.stride;
     const float dm = f0[o] / (float)a.G - M;
-    sv += f0[2 * plane + o] + dm * dm;
+    pv += f0[2 * plane + o] + dm * dm;
   }
+  const float sv = slice_sum(red, q, tok, pv);
   float x[5];
   x[0] = s0 / (float)(a.U * a.G * a.P);
   x[1] = s1 / (float)a.U;
   x[2] = sv / (float)a.U / ((float)a.P * (float)a.P);
   x[3] = s0 > 0.f ? s3 / s0 : 0.f;
-  x[4] = (float)(a.pos ? a.pos[i] : i) * a.inv_seen;
-  if (a.x_out) {
+  x[4] = (float)(a.pos ? a.pos[ic] : ic) * a.inv_seen;
+  if (a.x_out && live && q < 5) a.x_out[q * a.x_stride + i] = x[q];
+  // layer 1 (slice q: hidden units q*JS ..), LayerNorm over all 128, ReLU
+  float z[JS];
+  float pm = 0.f;
 #pragma unroll
-    for (int c = 0; c < 5; ++c) a.x_out[c * a.x_stride + i] = x[c];
+  for (int jj = 0; jj < JS; ++jj) {
+    const int k = q * JS + jj;
+    float v = b1[k];
+#pragma unroll
+    for (int c = 0; c < 5; ++c) v += w1[k * 5 + c] * x[c];
+    z[jj] = v;
+    pm += v;
   }
-  // layer 1 + LayerNorm + ReLU, kept in registers
-  float h[HID];
-  float mu = 0.f;
+  float mu = slice_sum(red, q, tok, pm) * (1.f / HID);
+  float pq = 0.f;
 #pragma unroll
-  for (int k = 0; k < HID; ++k) {
-    float z = b1[k];
+  for (int jj = 0; jj < JS; ++jj) pq += (z[jj] - mu) * (z[jj] - mu);
+  float rs = 1.f / sqrtf(slice_sum(red, q, tok, pq) * (1.f / HID) + LN_EPS);
 #pragma unroll
-    for (int c = 0; c < 5; ++c) z += w1[k * 5 + c] * x[c];
-    h[k] = z;
-    mu += z;
+  for (int jj = 0; jj < JS; ++jj) {
+    const int k = q * JS + jj;
+    h1[tok * HPAD + k] = fmaxf((z[jj] - mu) * rs * g1[k] + be1[k], 0.f);
   }
-  mu *= 1.f / HID;
-  float var = 0.f;
+  __syncthreads();
+  // layer 2 (slice q: outputs q*JS ..), LayerNorm, ReLU, output layer
+  pm = 0.f;
 #pragma unroll
-  for (int k = 0; k < HID; ++k) var += (h[k] - mu) * (h[k] - mu);
-  float rs = 1.f / sqrtf(var * (1.f / HID) + LN_EPS);
-#pragma unroll
-  for (int k = 0; k < HID; ++k) h[k] = fmaxf((h[k] - mu) * rs * g1[k] + be1[k], 0.f);
-  // layer 2: its pre-activations are recomputed for the mean, the variance
-  // and the output rather than stored
-  auto pre2 = [&](int j) {
-    float z = b2[j];
-    const float* wr = w2 + j * HID;
-#pragma unroll
-    for (int k = 0; k < HID; ++k) z += wr[k] * h[k];
-    return z;
-  };
-  float m2 = 0.f;
-  for (int j = 0; j < HID; ++j) m2 += pre2(j);
-  m2 *= 1.f / HID;
-  float v2 = 0.f;
-  for (int j = 0; j < HID; ++j) {
-    const float dz = pre2(j) - m2;
-    v2 += dz * dz;
+  for (int jj = 0; jj < JS; ++jj) {
+    const int j = q * JS + jj;
+    const float* wr = w2 + j * HPAD;
+    const float* hr = h1 + tok * HPAD;
+    float v = b2[j];
+#pragma unroll 16
+    for (int k = 0; k < HID; ++k) v += wr[k] * hr[k];
+    z[jj] = v;
+    pm += v;
   }
-  const float rs2 = 1.f / sqrtf(v2 * (1.f / HID) + LN_EPS);
-  float out = a.pol.b3[0];
-  for (int j = 0; j < HID; ++j) out += w3[j] * fmaxf((pre2(j) - m2) * rs2 * g2[j] + be2[j], 0.f);
-  a.score[i] = out;
+  mu = slice_sum(red, q, tok, pm) * (1.f / HID);
+  pq = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < JS; ++jj) pq += (z[jj] - mu) * (z[jj] - mu);
+  rs = 1.f / sqrtf(slice_sum(red, q, tok, pq) * (1.f / HID) + LN_EPS);
+  float po = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < JS; ++jj) {
+    const int j = q * JS + jj;
+    po += w3[j] * fmaxf((z[jj] - mu) * rs * g2[j] + be2[j], 0.f);
+  }
+  const float out = slice_sum(red, q, tok, po) + a.pol.b3[0];
+  if (live && q == 0) a.score[i] = out;
 }
 
-size_t policy_smem() { return (size_t)(W1N + W2N + 7 * HID) * sizeof(float); }
+size_t policy_smem() { return (size_t)(W1N + W2S + 7 * HID + TOK * HPAD + NSL * TOK) * sizeof(float); }
 
 int run_policy(PolArgs a, hipStream_t st) {
   if (a.n <= 0) return KVC_OK;
   const int sm = (int)policy_smem();
   (void)hipFuncSetAttribute((const void*)policy_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
-  hipLaunchKernelGGL(policy_kernel, dim3((unsigned)((a.n + PT - 1) / PT)), dim3(PT), sm, st, a);
+  hipLaunchKernelGGL(policy_kernel, dim3((unsigned)((a.n + TOK - 1) / TOK)), dim3(PT), sm, st, a);
   KVC_LAUNCH_CHECK("policy");
   return KVC_OK;
 }
