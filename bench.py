@@ -33,6 +33,8 @@ def parse():
     ap.add_argument("--config", default="fulldepth")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-variants", action="store_true",
+                    help="measure only the variants (one JSON object with a 'variants' key); for profiling")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the variant measurements beside the headline line (head-level hybrid, "
                          "step-wise eviction)")
@@ -199,6 +201,13 @@ def main():
     x_full = torch.empty((S, Td, Dm), dtype=torch.float32, device=dev)
     x_comp = torch.empty((S, Td, Dm), dtype=torch.float32, device=dev)
     kl_op = kvc.KL(S * Td, Dm, cfg.vocab, inp["W"].dtype, device=dev)
+    if args.only_variants:
+        dfull = kvc.Decoder(full, cfg.G, Td)
+        for t in range(Td):
+            dfull.step(inp["Kd"], inp["Vd"], t + 1, inp["Qd"][t], _row_view(x_full, t), Td * Dm)
+        v = measure_variants(cfg, inp, full, x_full, kl_op, torch.cuda.current_stream())
+        print(json.dumps({"config": {"workload": describe(cfg)}, "variants": v}), flush=True)
+        return
     elt = inp["K"].element_size()
     d = cfg.d
     stream = torch.cuda.current_stream()
