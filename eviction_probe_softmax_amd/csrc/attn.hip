@@ -85,7 +85,15 @@ struct AttnArgs {
   int KW;                 // keys per workgroup (multiple of 32*WAVES)
   float scale2;           // log2(e) / sqrt(d)
   float hop_w;            // prop: w / G
+  int accumulate;         // prop: add this call's increments to delta (row blocks of the dense rollout)
 };
+
+// Largest seed position of a unit (-1 if none): keys past it see no row.
+__device__ __forceinline__ int max_seed(const AttnArgs& a, int unit) {
+  int m = -1;
+  for (int k = 0; k < a.M; ++k) m = max(m, a.seeds[(int64_t)unit * a.M + k]);
+  return m;
+}
 
 struct Work {
   int s, l, h, split, ns;
@@ -170,6 +178,16 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
   float* red = (float*)(lim_s + a.Rpad);  // [WAVES][Rpad][3]
   Work w = decode_work(a, blockIdx.x);
   if (w.s < 0) return;
+  if (mode == 1 && w.k0 > max_seed(a, w.unit)) {
+    // no row reaches this split's keys: an empty partial
+    for (int r = threadIdx.x; r < a.Rpad; r += THREADS) {
+      float* o = part + ((size_t)blockIdx.x * a.Rpad + r) * 3;
+      o[0] = -INFINITY;
+      o[1] = 0.f;
+      o[2] = 0.f;
+    }
+    return;
+  }
   stage_rows<T, D>(a, w, mode, qf, lim_s);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -316,6 +334,8 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
   float* hred = w_s + a.Rpad;  // [WAVES][2]
   Work w = decode_work(a, blockIdx.x);
   if (w.s < 0) return;
+  // accumulating calls add nothing to keys past every row
+  if (MODE == 1 && a.accumulate && w.k0 > max_seed(a, w.unit)) return;
   stage_rows<T, D>(a, w, mode, qf, lim_s);
   for (int r = threadIdx.x; r < a.Rpad; r += THREADS) {
     float2 st = rowstat[(int64_t)w.unit * a.Rpad + r];
@@ -477,8 +497,8 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
       }
     } else if (lane < 32 && kvalid) {
       int64_t tix = ubase + key;
-      out0[tix] = colsum;                           // delta_t
-      rel_out[tix] = rel_in[tix] + colsum;          // running relevance
+      out0[tix] = a.accumulate ? out0[tix] + colsum : colsum;  // delta_t
+      rel_out[tix] = rel_in[tix] + colsum;                      // running relevance
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
@@ -687,6 +707,21 @@ int dispatch(int dtype, int d, const AttnArgs& a, int mode, int64_t nsplit, Args
   return run_passes<float, 64>(a, mode, nsplit, rest...);
 }
 
+// Dense rollout: row block b of every unit lists positions b*M .. b*M+M-1
+// (-1 past the sequence) as its "seeds".
+__global__ void dense_seeds_kernel(AttnArgs a, int64_t block, int32_t* seeds) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_units = (int64_t)a.S * a.Ly * a.H;
+  if (i >= n_units * a.M) return;
+  const int s = (int)(i / ((int64_t)a.Ly * a.H * a.M));
+  const int64_t pos = block * a.M + i % a.M;
+  seeds[i] = pos < a.cu[s + 1] - a.cu[s] ? (int32_t)pos : -1;
+}
+__global__ void zero_f32_kernel(float* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
 }  // namespace
 
 namespace kvc {
@@ -802,6 +837,68 @@ extern "C" int kvc_propagate(const kvc_shape* sh, const kvc_params* p, const voi
     r = dispatch(sh->dtype, sh->head_dim, a, 1, ns, part, rowstat, (float*)nullptr, (float*)nullptr, cur,
                  (float*)nullptr, (float*)nullptr, (const float*)rel, rel, st);
     if (r) return r;
+    prev = cur;
+  }
+  return KVC_OK;
+}
+
+namespace {
+int dense_rows(const kvc_shape* sh) { return (256 / sh->group) < 64 ? 256 / sh->group : 64; }
+}  // namespace
+
+extern "C" size_t kvc_propagate_dense_workspace(const kvc_shape* sh, const kvc_params* p) {
+  if (kvc::validate_shape(sh) || !p) return 0;
+  kvc_params q = *p;
+  q.n_seeds = dense_rows(sh);
+  return kvc::ws_propagate(sh, &q);
+}
+
+extern "C" int kvc_propagate_dense(const kvc_shape* sh, const kvc_params* p, const void* K, const void* Qctx,
+                                   const float* rel0, float* rel, void* ws, size_t ws_bytes, hipStream_t st) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  KVC_REQUIRE(p, KVC_E_INVAL, "params is NULL");
+  KVC_REQUIRE(p->n_hops >= 0 && p->n_hops <= 8, KVC_E_INVAL, "n_hops must be in [0, 8]");
+  KVC_REQUIRE(K && Qctx && rel0 && rel, KVC_E_INVAL, "kvc_propagate_dense: NULL input or output");
+  KVC_REQUIRE(ws && ws_bytes >= kvc_propagate_dense_workspace(sh, p), KVC_E_WORKSPACE,
+              "kvc_propagate_dense: workspace too small");
+  kvc_params q = *p;
+  q.n_seeds = dense_rows(sh);
+  const int kw = pick_kw(sh);
+  const int64_t ns = n_splits(sh, kw);
+  const int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
+  const int64_t units = (int64_t)sh->n_seq * sh->n_layers * sh->n_kv_heads;
+  if (E == 0) return KVC_OK;
+  AttnArgs a = base_args(sh, &q, kw);
+  a.K = K;
+  a.Q = Qctx;
+  a.R = sh->group * q.n_seeds;
+  a.Rpad = (a.R + 31) / 32 * 32;
+  a.hop_w = p->hop_weight / (float)sh->group;
+  a.accumulate = 1;
+  kvc::Carver c(ws, ws_bytes);
+  float* part = c.take<float>((size_t)ns * a.Rpad * 3);
+  float2* rowstat = c.take<float2>((size_t)units * a.Rpad);
+  float* dbuf = c.take<float>((size_t)E * 2);
+  int32_t* seeds = c.take<int32_t>((size_t)units * q.n_seeds);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, st, rel0, rel, E);
+  KVC_LAUNCH_CHECK("copy");
+  const int64_t nblk = (kvc::max_len(sh) + q.n_seeds - 1) / q.n_seeds;
+  const float* prev = rel0;
+  for (int hop = 0; hop < p->n_hops; ++hop) {
+    float* cur = dbuf + (int64_t)(hop & 1) * E;
+    hipLaunchKernelGGL(zero_f32_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, st, cur, E);
+    KVC_LAUNCH_CHECK("zero");
+    a.prev = prev;
+    a.seeds = seeds;
+    for (int64_t b = 0; b < nblk; ++b) {
+      hipLaunchKernelGGL(dense_seeds_kernel, dim3(kvc_blocks(units * q.n_seeds, 256)), dim3(256), 0, st, a, b,
+                         seeds);
+      KVC_LAUNCH_CHECK("dense_seeds");
+      r = dispatch(sh->dtype, sh->head_dim, a, 1, ns, part, rowstat, (float*)nullptr, (float*)nullptr, cur,
+                   (float*)nullptr, (float*)nullptr, (const float*)rel, rel, st);
+      if (r) return r;
+    }
     prev = cur;
   }
   return KVC_OK;

@@ -33,7 +33,8 @@ EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets"
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
            "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
            "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
-           "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune"]
+           "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune",
+           "kvc_propagate_dense_workspace", "kvc_propagate_dense"]
 
 
 class Shape(C.Structure):
@@ -98,6 +99,8 @@ _sig = {
     "kvc_pack": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Trees), _P, _P, _P,
                            _P, _P, C.POINTER(Ragged), _P, C.c_size_t, _P]),
     "kvc_hybrid_units": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P]),
+    "kvc_propagate_dense_workspace": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params)]),
+    "kvc_propagate_dense": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "kvc_full_view": (C.c_int, [C.POINTER(Shape), _P, _P, _P]),
     "kvc_decode_workspace": (C.c_size_t, [C.POINTER(Ragged), C.c_int32, C.c_int32]),
     "kvc_decode_attn": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
@@ -316,6 +319,17 @@ def auction(pb: Problem, trees=None, rel=None, head_sens=None, slot_start=None, 
                           _ptr(spent_floor), _ptr(ws), ws.numel(), _stream())
     _check("kvc_auction", st)
     return {"taken": taken, "spent": spent, "spent_floor": spent_floor}
+
+
+def propagate_dense(pb: Problem, K, Qctx, rel0):
+    """Dense rollout: every token a seed in every hop. Returns rel [Ly][H][T]."""
+    rel = torch.empty_like(rel0)
+    n = int(_lib.kvc_propagate_dense_workspace(C.byref(pb.shape), C.byref(pb.params)))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=pb.device)
+    st = _lib.kvc_propagate_dense(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(Qctx), _ptr(rel0),
+                                  _ptr(rel), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_propagate_dense", st)
+    return {"rel": rel}
 
 
 def hybrid_units(pb: Problem, head_sens):

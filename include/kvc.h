@@ -173,6 +173,18 @@ int kvc_propagate(const kvc_shape* shape, const kvc_params* prm, const void* K, 
                   const float* rel0, float* rel, int32_t* seeds, void* ws, size_t ws_bytes,
                   hipStream_t stream);
 
+/* Dense rollout: the same hops with every token a seed (the full L x L
+ * causal prefill attention graph, GQA-averaged), so relevance reaches every
+ * token any earlier-relevant token attends, with no seed cut-off:
+ *   delta_t = w * A_hat^T delta_{t-1},  rel = rel0 + delta_1 + ...
+ * (GraceKV page, '03 Bottom-up value flow'; the hop count and weight of
+ * prm). The rows run in blocks of min(64, 256/G) positions per (s, l, h),
+ * each block one pass over the keys up to its last position; the cost is
+ * that of a causal prefill attention per hop. n_seeds is ignored. */
+size_t kvc_propagate_dense_workspace(const kvc_shape* shape, const kvc_params* prm);
+int kvc_propagate_dense(const kvc_shape* shape, const kvc_params* prm, const void* K, const void* Qctx,
+                        const float* rel0, float* rel, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ A0
  * kvc_partition: slots of each sequence's compressible region.
  * GraceKV page, '01 Curvature-guided partition' (cut where the normalized

@@ -84,3 +84,17 @@ def test_score_repeatable():
     b = kvc.score(pb, dinp["K"], dinp["V"], dinp["Qp"])
     for k in ("r0", "feats", "lse", "ent", "head_sens"):
         assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", {"n_hops": 1}), ("tiny", {}), ("stress", {}), ("ragged", {}),
+                                     ("mistral1", {"n_hops": 1})])
+def test_dense_rollout_matches_oracle(name, kw):
+    """Every token a seed in every hop (the oracle with n_seeds >= L), over
+    several row blocks per sequence and ragged lengths."""
+    kvc, cfg, inp, dinp, pb = _setup(name, **kw)
+    cu = inp["cu_seqlens"].numpy()
+    print(f"[dense rollout] {name} {kw} lens={cfg.lens}", flush=True)
+    o_sc = oracle.probe_scores(inp["K"], inp["V"], inp["Qp"], cu, cfg)
+    g = kvc.propagate_dense(pb, dinp["K"], dinp["Qctx"], to_dev(o_sc["r0"]))
+    o = oracle.propagate(inp["K"], inp["Qctx"], o_sc["r0"], cu, cfg.replace(n_seeds=max(cfg.lens)))
+    close(g["rel"], o["rel"], 1e-3, "rel")
