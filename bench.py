@@ -119,7 +119,8 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     cache and the per-step KL against the full cache (x_full of the timed
     steps). Head-level hybrid: 20% of the (layer, KV head) units kept whole
     (DistillCache paper, Appendix E.3). Step-wise eviction: the scoring-MLP
-    loop of DistillCache's Algorithm 1 at the same budget ratio."""
+    loop of DistillCache's Algorithm 1 at the same budget ratio. Dense
+    rollout: both propagation hops with every token a seed."""
     import numpy as np
     import torch
     from eviction_probe_softmax_amd import kvc
@@ -164,6 +165,21 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     init_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "init"]
     dec_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "step"]
     prune_ms = [r[2].elapsed_time(r[3]) for r in rec if r[0] == "step"]
+    # Dense rollout: every token a seed in both hops (a causal L x L pass per
+    # hop); flops count each causal logit once per pass (rowstats, colsum)
+    comp = Compressor(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    sc = kvc.score(comp.pb, inp["K"], inp["V"], inp["Qp"])
+    kvc.propagate_dense(comp.pb, inp["K"], inp["Qctx"], sc["r0"])  # warm-up
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    kvc.propagate_dense(comp.pb, inp["K"], inp["Qctx"], sc["r0"])
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    dms = e[0].elapsed_time(e[1])
+    causal = sum(L * (L + 1) // 2 for L in cfg.lens)
+    flops = cfg.n_hops * 2 * cfg.Ly * cfg.H * cfg.G * causal * 2 * cfg.d
+    out["dense_rollout"] = {"ms": round(dms, 3), "tflops": round(flops / (dms * 1e-3) / 1e12, 1),
+                            "mfma_bf16_frac": round(flops / (dms * 1e-3) / 2.5e15, 4)}
     klv = res["kl"].float().cpu().numpy()
     out["stepwise_r%g" % cfg.budget_ratio] = {
         "init_prune_ms": round(float(np.mean(init_ms)), 3),

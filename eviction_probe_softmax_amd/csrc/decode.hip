@@ -267,7 +267,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
   // afterwards, so no load sits behind a branch.
   const float* lmp = lm ? lm : (const float*)Kb;
 #pragma unroll 1
-  for (int rb = wbase; rb < wbase + WE; rb += 32) {
+  for (int rb = wbase; rb < wbase + WE && rb < n; rb += 32) {  // a wave past the entries only joins the combine
     const int ek = rb + col, ekc = min(ek, (int)n - 1);
     const float bv = lmp[ekc];  // unconditional, selected away without ln mu
     uint4 kr[KS], vr[VIT];
