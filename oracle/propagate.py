@@ -77,3 +77,43 @@ def propagate(K, Qctx, r0, cu, cfg):
                 for t, sv in enumerate(sd):
                     seeds[t, s, l, h, : len(sv)] = sv
     return {"rel": rel.astype(np.float32), "seeds": seeds}
+
+
+def propagate_ar(K, Qctx, r0, cu, cfg):
+    """The "A r" direction (parity pinned by the matrix form w * A_hat r).
+
+    Reading: the same causal prefill attention graph, with relevance flowing
+    from an attended token to every token attending it: token i receives the
+    GQA-mean causal softmax average of the previous increment over its prefix,
+        delta_t(i) = w * (1/G) sum_g sum_{j<=i} b_ig(j) delta_{t-1}(j),
+    r = r0 + delta_1 + ... . Every token is a receiver (no seed cut-off).
+    Returns rel float32 [Ly][H][T].
+    """
+    Ly, H, T, d = K.shape
+    S = len(cu) - 1
+    G, hops = cfg.G, cfg.n_hops
+    w = float(np.float32(cfg.hop_weight))
+    c = 1.0 / np.sqrt(d)
+    rel = np.zeros((Ly, H, T))
+    for s in range(S):
+        a, b = int(cu[s]), int(cu[s + 1])
+        L = b - a
+        if L == 0:
+            continue
+        mask = np.tril(np.ones((L, L), dtype=bool))
+        for l in range(Ly):
+            for h in range(H):
+                Ku = to64(K[l, h, a:b])
+                Qc = to64(Qctx[l, h * G:(h + 1) * G, a:b])
+                Ahat = np.zeros((L, L))
+                for g in range(G):
+                    z = np.where(mask, c * (Qc[g] @ Ku.T), -np.inf)
+                    Ahat += np.exp(z - logsumexp(z, axis=1)[:, None])
+                Ahat /= G
+                prev = np.asarray(r0[l, h, a:b], dtype=np.float64)
+                tot = prev.copy()
+                for _ in range(hops):
+                    prev = w * (Ahat @ prev)
+                    tot += prev
+                rel[l, h, a:b] = tot
+    return {"rel": rel.astype(np.float32)}

@@ -812,3 +812,32 @@ def test_hybrid_floor_skips_whole_heads_and_caps_on_the_rest():
     # shares token 7's last split)
     assert [t[0] for t in tr[:2]] == [1 * L + 7, 2 * L + 20] and fspent[0] == 10
     assert all(c == 0 for _, c in tr[2:]) and (1 * L + 6, 0) in tr[2:]
+
+
+# ---------------------------------------------------------------- "A r" propagation (NEXT 3)
+def test_ar_propagation_matrix_form_and_constant():
+    from oracle.propagate import propagate_ar
+    rng = np.random.default_rng(31)
+    L, d, G = 30, 8, 2
+    K = rng.standard_normal((L, d))
+    Qc = rng.standard_normal((G, L, d))
+    r0 = rng.random(L).astype(np.float32)
+    w = 0.3
+    cfg = _cfg(G=G, d=d, lens=[L], n_hops=2, hop_weight=w)
+    out = propagate_ar(torch.tensor(K.reshape(1, 1, L, d)), torch.tensor(Qc.reshape(1, G, L, d)),
+                       r0.reshape(1, 1, L), np.array([0, L]), cfg)
+    # library softmax per query head, causal; rows are the attending tokens
+    logits = np.einsum("gjd,id->gji", Qc, K) / math.sqrt(d)
+    logits = np.where(np.tril(np.ones((L, L)))[None] > 0, logits, -np.inf)
+    Ahat = scipy.special.softmax(logits, axis=2).mean(0)          # [i attending, j attended]
+    wf = float(np.float32(w))
+    r = r0.astype(np.float64)
+    d1 = wf * Ahat @ r
+    d2 = wf * Ahat @ d1
+    assert np.allclose(out["rel"][0, 0], r + d1 + d2, rtol=1e-6)
+    # every row is a convex average: a constant increment passes on as w * c,
+    # and the first token can only take its own value
+    outc = propagate_ar(torch.tensor(K.reshape(1, 1, L, d)), torch.tensor(Qc.reshape(1, G, L, d)),
+                        np.full((1, 1, L), 2.0, np.float32), np.array([0, L]), cfg.replace(n_hops=1))
+    assert np.allclose(outc["rel"][0, 0], 2.0 + wf * 2.0, rtol=1e-6)
+    assert abs(d1[0] - wf * r[0]) < 1e-12
