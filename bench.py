@@ -120,7 +120,8 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     steps). Head-level hybrid: 20% of the (layer, KV head) units kept whole
     (DistillCache paper, Appendix E.3). Step-wise eviction: the scoring-MLP
     loop of DistillCache's Algorithm 1 at the same budget ratio. Dense
-    rollout: both propagation hops with every token a seed."""
+    rollout: both propagation hops with every token a seed; the "A r"
+    direction: both hops with every token a receiver."""
     import numpy as np
     import torch
     from eviction_probe_softmax_amd import kvc
@@ -180,6 +181,15 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     flops = cfg.n_hops * 2 * cfg.Ly * cfg.H * cfg.G * causal * 2 * cfg.d
     out["dense_rollout"] = {"ms": round(dms, 3), "tflops": round(flops / (dms * 1e-3) / 1e12, 1),
                             "mfma_bf16_frac": round(flops / (dms * 1e-3) / 2.5e15, 4)}
+    # the "A r" direction: one causal row pass per hop
+    kvc.propagate_ar(comp.pb, inp["K"], inp["Qctx"], sc["r0"])  # warm-up
+    e[0].record(stream)
+    kvc.propagate_ar(comp.pb, inp["K"], inp["Qctx"], sc["r0"])
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    ams = e[0].elapsed_time(e[1])
+    out["ar_direction"] = {"ms": round(ams, 3), "tflops": round(flops / 2 / (ams * 1e-3) / 1e12, 1),
+                           "mfma_bf16_frac": round(flops / 2 / (ams * 1e-3) / 2.5e15, 4)}
     klv = res["kl"].float().cpu().numpy()
     out["stepwise_r%g" % cfg.budget_ratio] = {
         "init_prune_ms": round(float(np.mean(init_ms)), 3),

@@ -86,6 +86,8 @@ struct AttnArgs {
   float scale2;           // log2(e) / sqrt(d)
   float hop_w;            // prop: w / G
   int accumulate;         // prop: add this call's increments to delta (row blocks of the dense rollout)
+  const float* kval;      // "A r" pass: a scalar value per key (delta_{t-1}) averaged by each row's softmax
+  float* part_v;          // "A r" pass: per split and row, the value sum at the split's max
 };
 
 // Largest seed position of a unit (-1 if none): keys past it see no row.
@@ -169,7 +171,7 @@ __device__ void stage_rows(const AttnArgs& a, const Work& w, int mode, Frag<T>* 
 }
 
 // ------------------------------------------------------------------ pass 1
-template <class T, int D>
+template <class T, int D, bool VAL = false>
 __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode, float* part) {
   constexpr int KS = D / 16;
   extern __shared__ __align__(16) char smem[];
@@ -185,6 +187,7 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
       o[0] = -INFINITY;
       o[1] = 0.f;
       o[2] = 0.f;
+      if constexpr (VAL) a.part_v[(size_t)blockIdx.x * a.Rpad + r] = 0.f;
     }
     return;
   }
@@ -192,13 +195,14 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nrb = a.Rpad >> 5;
-  float m[8], sm[8], tt[8];
+  float m[8], sm[8], tt[8], vv[8];
   int lim[8];
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
     m[rb] = -INFINITY;
     sm[rb] = 0.f;
     tt[rb] = 0.f;
+    vv[rb] = 0.f;
     lim[rb] = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1;
   }
   int maxlim = -1;
@@ -211,6 +215,14 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       kf[ks] = key < w.k1 ? load_frag<T>(K + key * D + ks * 16 + 8 * (lane >> 5)) : zero_frag<T>();
+    // "A r" pass: the values of the 16 keys a lane's registers hold (clamped
+    // into the sequence; masked keys get zero weight)
+    float dv[VAL ? 16 : 1];
+    if constexpr (VAL) {
+      const float* kv = a.kval + ((int64_t)w.l * a.H + w.h) * a.T + w.tok0;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dv[v] = kv[min(kb + acc_row(v, lane), w.k1 - 1)];
+    }
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
       if (rb >= nrb) break;
@@ -230,15 +242,17 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
       if (mx == -INFINITY) continue;
       float mn = fmaxf(m[rb], mx);
       float f = fast_exp2(m[rb] - mn);
-      float s2 = 0.f, t2 = 0.f;
+      float s2 = 0.f, t2 = 0.f, v2 = 0.f;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float e = fast_exp2(x[v] - mn);
         s2 += e;
         t2 += x[v] == -INFINITY ? 0.f : e * x[v];
+        if constexpr (VAL) v2 += e * dv[v];
       }
       sm[rb] = sm[rb] * f + s2;
       tt[rb] = tt[rb] * f + t2;
+      if constexpr (VAL) vv[rb] = vv[rb] * f + v2;
       m[rb] = mn;
     }
   }
@@ -247,11 +261,13 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
   for (int rb = 0; rb < 8; ++rb) {
     if (rb >= nrb) break;
     float m2 = __shfl_xor(m[rb], 32, 64), s2 = __shfl_xor(sm[rb], 32, 64), t2 = __shfl_xor(tt[rb], 32, 64);
+    float v2 = VAL ? __shfl_xor(vv[rb], 32, 64) : 0.f;
     float mn = fmaxf(m[rb], m2);
     if (mn != -INFINITY) {
       float f1 = exp2f(m[rb] - mn), f2 = exp2f(m2 - mn);
       sm[rb] = sm[rb] * f1 + s2 * f2;
       tt[rb] = tt[rb] * f1 + t2 * f2;
+      if constexpr (VAL) vv[rb] = vv[rb] * f1 + v2 * f2;
     }
     m[rb] = mn;
     if (lane < 32) {
@@ -259,11 +275,12 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
       r[0] = m[rb];
       r[1] = sm[rb];
       r[2] = tt[rb];
+      if constexpr (VAL) red[(size_t)WAVES * a.Rpad * 3 + (size_t)wave * a.Rpad + rb * 32 + lane] = vv[rb];
     }
   }
   __syncthreads();
   for (int r = threadIdx.x; r < a.Rpad; r += THREADS) {
-    float mm = -INFINITY, ss = 0.f, ts = 0.f;
+    float mm = -INFINITY, ss = 0.f, ts = 0.f, vs = 0.f;
     for (int wv = 0; wv < WAVES; ++wv) {
       const float* q = red + ((size_t)wv * a.Rpad + r) * 3;
       float mn = fmaxf(mm, q[0]);
@@ -271,13 +288,57 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
       float f1 = exp2f(mm - mn), f2 = exp2f(q[0] - mn);
       ss = ss * f1 + q[1] * f2;
       ts = ts * f1 + q[2] * f2;
+      if constexpr (VAL) vs = vs * f1 + red[(size_t)WAVES * a.Rpad * 3 + (size_t)wv * a.Rpad + r] * f2;
       mm = mn;
     }
     float* o = part + ((size_t)blockIdx.x * a.Rpad + r) * 3;
     o[0] = mm;
     o[1] = ss;
     o[2] = ts;
+    if constexpr (VAL) a.part_v[(size_t)blockIdx.x * a.Rpad + r] = vs;
   }
+}
+
+// "A r" pass: merge the split partials of every (unit, row) into the row's
+// softmax average of the key values, then hand w/G of the G rows of each
+// position to that position (every position lies in exactly one row block).
+__global__ void rowval_kernel(AttnArgs a, const float* part, int64_t block, float* cur, float* rel) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n_units = (int64_t)a.S * a.Ly * a.H;
+  if (i >= n_units * a.M) return;
+  const int64_t unit = i / a.M;
+  const int k = (int)(i % a.M);
+  const int s = (int)(unit / ((int64_t)a.Ly * a.H));
+  const int lh = (int)(unit % ((int64_t)a.Ly * a.H));
+  const int64_t L = a.cu[s + 1] - a.cu[s];
+  const int64_t pos = block * a.M + k;
+  if (pos >= L) return;
+  int64_t base = 0, ns = 0;
+  for (int q = 0; q <= s; ++q) {
+    const int64_t Lq = a.cu[q + 1] - a.cu[q];
+    ns = (Lq + a.KW - 1) / a.KW;
+    if (q < s) base += ns * a.Ly * a.H;
+  }
+  base += (int64_t)lh * ns;
+  float tot = 0.f;
+  for (int g = 0; g < a.G; ++g) {
+    const int r = k * a.G + g;
+    float mm = -INFINITY, ss = 0.f, vs = 0.f;
+    for (int64_t sp = 0; sp < ns; ++sp) {
+      const float* q = part + ((base + sp) * a.Rpad + r) * 3;
+      const float mn = fmaxf(mm, q[0]);
+      if (mn == -INFINITY) continue;
+      const float f1 = exp2f(mm - mn), f2 = exp2f(q[0] - mn);
+      ss = ss * f1 + q[1] * f2;
+      vs = vs * f1 + a.part_v[(base + sp) * a.Rpad + r] * f2;
+      mm = mn;
+    }
+    tot += ss > 0.f ? vs / ss : 0.f;
+  }
+  const int64_t tix = (int64_t)lh * a.T + a.cu[s] + pos;
+  const float d = a.hop_w * tot;
+  cur[tix] = d;
+  rel[tix] += d;
 }
 
 // Merge the split partials of each (unit, row): lse2 (base 2) and H.
@@ -843,6 +904,20 @@ extern "C" int kvc_propagate(const kvc_shape* sh, const kvc_params* p, const voi
 }
 
 namespace {
+template <class T, int D>
+int launch_rowval(const AttnArgs& a, int64_t nsplit, float* part, hipStream_t st) {
+  const size_t sm = smem_rows(a, D, sizeof(T)) + a.Rpad * sizeof(int) + (size_t)WAVES * a.Rpad * 4 * sizeof(float);
+  (void)hipFuncSetAttribute((const void*)rowstats_kernel<T, D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)sm);
+  hipLaunchKernelGGL((rowstats_kernel<T, D, true>), dim3((unsigned)nsplit), dim3(THREADS), sm, st, a, 1, part);
+  KVC_LAUNCH_CHECK("rowstats_val");
+  return KVC_OK;
+}
+int dispatch_rowval(int dtype, int d, const AttnArgs& a, int64_t nsplit, float* part, hipStream_t st) {
+  if (dtype == KVC_BF16) return d == 128 ? launch_rowval<uint16_t, 128>(a, nsplit, part, st)
+                                         : launch_rowval<uint16_t, 64>(a, nsplit, part, st);
+  return d == 128 ? launch_rowval<float, 128>(a, nsplit, part, st) : launch_rowval<float, 64>(a, nsplit, part, st);
+}
 int dense_rows(const kvc_shape* sh) { return (256 / sh->group) < 64 ? 256 / sh->group : 64; }
 }  // namespace
 
@@ -898,6 +973,65 @@ extern "C" int kvc_propagate_dense(const kvc_shape* sh, const kvc_params* p, con
       r = dispatch(sh->dtype, sh->head_dim, a, 1, ns, part, rowstat, (float*)nullptr, (float*)nullptr, cur,
                    (float*)nullptr, (float*)nullptr, (const float*)rel, rel, st);
       if (r) return r;
+    }
+    prev = cur;
+  }
+  return KVC_OK;
+}
+
+extern "C" size_t kvc_propagate_ar_workspace(const kvc_shape* sh, const kvc_params* p) {
+  if (kvc::validate_shape(sh) || !p) return 0;
+  kvc_params q = *p;
+  q.n_seeds = dense_rows(sh);
+  const int64_t ns = n_splits(sh, pick_kw(sh));
+  const int rpad = (sh->group * q.n_seeds + 31) / 32 * 32;
+  return kvc::ws_propagate(sh, &q) + (size_t)ns * rpad * sizeof(float) + 256;
+}
+
+extern "C" int kvc_propagate_ar(const kvc_shape* sh, const kvc_params* p, const void* K, const void* Qctx,
+                                const float* rel0, float* rel, void* ws, size_t ws_bytes, hipStream_t st) {
+  int r = kvc::validate_shape(sh);
+  if (r) return r;
+  KVC_REQUIRE(p, KVC_E_INVAL, "params is NULL");
+  KVC_REQUIRE(p->n_hops >= 0 && p->n_hops <= 8, KVC_E_INVAL, "n_hops must be in [0, 8]");
+  KVC_REQUIRE(K && Qctx && rel0 && rel, KVC_E_INVAL, "kvc_propagate_ar: NULL input or output");
+  KVC_REQUIRE(ws && ws_bytes >= kvc_propagate_ar_workspace(sh, p), KVC_E_WORKSPACE,
+              "kvc_propagate_ar: workspace too small");
+  kvc_params q = *p;
+  q.n_seeds = dense_rows(sh);
+  const int kw = pick_kw(sh);
+  const int64_t ns = n_splits(sh, kw);
+  const int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
+  const int64_t units = (int64_t)sh->n_seq * sh->n_layers * sh->n_kv_heads;
+  if (E == 0) return KVC_OK;
+  AttnArgs a = base_args(sh, &q, kw);
+  a.K = K;
+  a.Q = Qctx;
+  a.R = sh->group * q.n_seeds;
+  a.Rpad = (a.R + 31) / 32 * 32;
+  a.hop_w = p->hop_weight / (float)sh->group;
+  kvc::Carver c(ws, ws_bytes);
+  float* part = c.take<float>((size_t)ns * a.Rpad * 3);
+  c.take<float2>((size_t)units * a.Rpad);  // same carving as the propagation workspace
+  float* dbuf = c.take<float>((size_t)E * 2);
+  int32_t* seeds = c.take<int32_t>((size_t)units * q.n_seeds);
+  a.part_v = c.take<float>((size_t)ns * a.Rpad);
+  hipLaunchKernelGGL(copy_f32_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, st, rel0, rel, E);
+  KVC_LAUNCH_CHECK("copy");
+  const int64_t nblk = (kvc::max_len(sh) + q.n_seeds - 1) / q.n_seeds;
+  const float* prev = rel0;
+  a.seeds = seeds;
+  for (int hop = 0; hop < p->n_hops; ++hop) {
+    float* cur = dbuf + (int64_t)(hop & 1) * E;
+    a.kval = prev;
+    for (int64_t b = 0; b < nblk; ++b) {
+      hipLaunchKernelGGL(dense_seeds_kernel, dim3(kvc_blocks(units * q.n_seeds, 256)), dim3(256), 0, st, a, b,
+                         seeds);
+      KVC_LAUNCH_CHECK("dense_seeds");
+      if ((r = dispatch_rowval(sh->dtype, sh->head_dim, a, ns, part, st))) return r;
+      hipLaunchKernelGGL(rowval_kernel, dim3(kvc_blocks(units * q.n_seeds, 256)), dim3(256), 0, st, a, part, b, cur,
+                         rel);
+      KVC_LAUNCH_CHECK("rowval");
     }
     prev = cur;
   }

@@ -34,7 +34,8 @@ EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets"
            "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
            "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
            "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune",
-           "kvc_propagate_dense_workspace", "kvc_propagate_dense"]
+           "kvc_propagate_dense_workspace", "kvc_propagate_dense", "kvc_propagate_ar_workspace",
+           "kvc_propagate_ar"]
 
 
 class Shape(C.Structure):
@@ -101,6 +102,8 @@ _sig = {
     "kvc_hybrid_units": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P]),
     "kvc_propagate_dense_workspace": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params)]),
     "kvc_propagate_dense": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, C.c_size_t, _P]),
+    "kvc_propagate_ar_workspace": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params)]),
+    "kvc_propagate_ar": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "kvc_full_view": (C.c_int, [C.POINTER(Shape), _P, _P, _P]),
     "kvc_decode_workspace": (C.c_size_t, [C.POINTER(Ragged), C.c_int32, C.c_int32]),
     "kvc_decode_attn": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
@@ -329,6 +332,17 @@ def propagate_dense(pb: Problem, K, Qctx, rel0):
     st = _lib.kvc_propagate_dense(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(Qctx), _ptr(rel0),
                                   _ptr(rel), _ptr(ws), ws.numel(), _stream())
     _check("kvc_propagate_dense", st)
+    return {"rel": rel}
+
+
+def propagate_ar(pb: Problem, K, Qctx, rel0):
+    """The "A r" direction over every token. Returns rel [Ly][H][T]."""
+    rel = torch.empty_like(rel0)
+    n = int(_lib.kvc_propagate_ar_workspace(C.byref(pb.shape), C.byref(pb.params)))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=pb.device)
+    st = _lib.kvc_propagate_ar(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(Qctx), _ptr(rel0), _ptr(rel),
+                               _ptr(ws), ws.numel(), _stream())
+    _check("kvc_propagate_ar", st)
     return {"rel": rel}
 
 

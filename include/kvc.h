@@ -185,6 +185,18 @@ size_t kvc_propagate_dense_workspace(const kvc_shape* shape, const kvc_params* p
 int kvc_propagate_dense(const kvc_shape* shape, const kvc_params* prm, const void* K, const void* Qctx,
                         const float* rel0, float* rel, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The "A r" direction: relevance flows from attended tokens to the tokens
+ * attending them. Every token i takes the GQA-mean causal softmax average of
+ * the previous increment over its prefix,
+ *   delta_t(i) = w * mean_g sum_{j<=i} softmax_j(<q_ig,k_j>/sqrt d) delta_{t-1}(j),
+ * rel = rel0 + delta_1 + ... (GraceKV page, '03 Bottom-up value flow', read
+ * in the other direction of the attention graph). One causal row pass per
+ * hop and row block (the row softmax and the value average in the same
+ * pass); n_seeds is ignored. */
+size_t kvc_propagate_ar_workspace(const kvc_shape* shape, const kvc_params* prm);
+int kvc_propagate_ar(const kvc_shape* shape, const kvc_params* prm, const void* K, const void* Qctx,
+                     const float* rel0, float* rel, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------ A0
  * kvc_partition: slots of each sequence's compressible region.
  * GraceKV page, '01 Curvature-guided partition' (cut where the normalized

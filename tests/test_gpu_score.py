@@ -98,3 +98,18 @@ def test_dense_rollout_matches_oracle(name, kw):
     g = kvc.propagate_dense(pb, dinp["K"], dinp["Qctx"], to_dev(o_sc["r0"]))
     o = oracle.propagate(inp["K"], inp["Qctx"], o_sc["r0"], cu, cfg.replace(n_seeds=max(cfg.lens)))
     close(g["rel"], o["rel"], 1e-3, "rel")
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", {"n_hops": 1}), ("tiny", {}), ("stress", {}), ("ragged", {}),
+                                     ("mistral1", {"n_hops": 1})])
+def test_ar_direction_matches_oracle(name, kw):
+    """Every token takes the causal softmax average of the previous
+    increment, over several row blocks and ragged lengths."""
+    from oracle.propagate import propagate_ar
+    kvc, cfg, inp, dinp, pb = _setup(name, **kw)
+    cu = inp["cu_seqlens"].numpy()
+    print(f"[A r] {name} {kw} lens={cfg.lens}", flush=True)
+    o_sc = oracle.probe_scores(inp["K"], inp["V"], inp["Qp"], cu, cfg)
+    g = kvc.propagate_ar(pb, dinp["K"], dinp["Qctx"], to_dev(o_sc["r0"]))
+    o = propagate_ar(inp["K"], inp["Qctx"], o_sc["r0"], cu, cfg)
+    close(g["rel"], o["rel"], 1e-3, "rel")
