@@ -18,6 +18,13 @@ Readings (the pages give no constants):
   lambda_curv * kappa_c. Both are quantized to integers as
   round-half-away(x * 2^20) before the DP, which then runs in exact integer
   arithmetic; ties go to the earlier previous cut. Surprisal is not used.
+* Several sampled depths (hidden [D][T][dim], 'Technical details': turns
+  stabilized across sampled depths and windows): the turning score is the
+  mean over every valid (depth, window) pair and the dispersion term the mean
+  over depths of each depth's dispersion.
+* Surprisal (a smaller auxiliary boundary signal): a cut before token b also
+  earns lambda_surp * s_b / max s over the sequence (0 when that maximum is
+  not positive), added to lambda_curv * kappa_b before quantization.
 * Regions shorter than slot_min form a single slot.
 * Fixed-length mode: slots of slot_len tokens, the last one shorter.
 """
@@ -42,6 +49,22 @@ def _q(x: float) -> int:
 def normalize(h: np.ndarray) -> np.ndarray:
     n = np.sqrt((h * h).sum(axis=1, keepdims=True))
     return np.where(n > 0, h / np.where(n > 0, n, 1.0), 0.0)
+
+
+def turning_values(hn: np.ndarray, b: int) -> list:
+    """The valid window turning values at position b of one trajectory."""
+    L = hn.shape[0]
+    vals = []
+    for w in WINDOWS:
+        if b - w < 0 or b + w > L - 1:
+            continue
+        u = hn[b] - hn[b - w]
+        v = hn[b + w] - hn[b]
+        nu, nv = np.linalg.norm(u), np.linalg.norm(v)
+        if nu == 0 or nv == 0:
+            continue
+        vals.append((1.0 - float(u @ v) / (nu * nv)) / 2.0)
+    return vals
 
 
 def turning_scores(hn: np.ndarray) -> np.ndarray:
@@ -71,35 +94,52 @@ def slot_cost(hn: np.ndarray, a: int, n: int, cfg) -> float:
     return disp + float(np.float32(cfg.lambda_len)) * ((n - t) / t) ** 2
 
 
-def slot_costs(hidden, cu, cfg):
+def slot_costs(hidden, cu, cfg, surprisal=None):
     """Quantized DP inputs in the boundary layout.
 
+    hidden: [T][dim] or [D][T][dim] (D sampled depths); surprisal: [T] or None.
     cost_q int64 [T][slot_max - slot_min + 1]: row = index of a slot's LAST
     token (global token index), column = n - slot_min; cut_q int64 [T]: cut
     before that token. Rows outside a sequence's compressible region, and
     slots that would start before it, are left at 0 (never read).
     """
-    T = hidden.shape[0]
+    H = to64(hidden)
+    if H.ndim == 2:
+        H = H[None]
+    D, T = H.shape[0], H.shape[1]
     nmin, nmax = cfg.slot_min, cfg.slot_max
     cost_q = np.zeros((T, nmax - nmin + 1), dtype=np.int64)
     cut_q = np.zeros((T,), dtype=np.int64)
     lam_c = float(np.float32(cfg.lambda_curv))
+    lam_s = float(np.float32(getattr(cfg, "lambda_surp", 0.0)))
+    sur = None if surprisal is None else to64(surprisal)
+    t_len = float(cfg.slot_target)
+    lam_len = float(np.float32(cfg.lambda_len))
     for s in range(len(cu) - 1):
         a0, b0 = int(cu[s]), int(cu[s + 1])
         L = b0 - a0
         if L == 0:
             continue
-        hn = normalize(to64(hidden[a0:b0]))
+        hns = [normalize(H[dd, a0:b0]) for dd in range(D)]
         pe, c0, c1, ss = regions(L, cfg)
-        kap = turning_scores(hn)
+        smax = float(sur[a0:b0].max()) if sur is not None else 0.0
         for c in range(c0, c1):
-            cut_q[a0 + c] = _q(lam_c * kap[c])
+            vals = [v for hn in hns for v in turning_values(hn, c)]
+            bonus = lam_c * (float(np.mean(vals)) if vals else 0.0)
+            if sur is not None and smax > 0:
+                bonus += lam_s * float(sur[a0 + c]) / smax
+            cut_q[a0 + c] = _q(bonus)
         for e in range(c0 + 1, c1 + 1):                # exclusive slot end
             for n in range(nmin, nmax + 1):
                 st = e - n
                 if st < c0:
                     break
-                cost_q[a0 + e - 1, n - nmin] = _q(slot_cost(hn, st, n, cfg))
+                disp = 0.0
+                for hn in hns:
+                    x = hn[st:st + n]
+                    disp += float(((x - x.mean(axis=0)) ** 2).sum())
+                cost = disp / D + lam_len * ((n - t_len) / t_len) ** 2
+                cost_q[a0 + e - 1, n - nmin] = _q(cost)
     return cost_q, cut_q
 
 

@@ -37,7 +37,7 @@ def run_pipeline(inp, cfg, stages=("compress", "decode", "kl")):
     else:
         cost_q = cut_q = None
         if cfg.slot_len == 0:
-            cost_q, cut_q = slot_costs(inp["hidden"], cu, cfg)
+            cost_q, cut_q = slot_costs(inp["hidden"], cu, cfg, inp.get("surprisal"))
             out["dp_cost_q"], out["dp_cut_q"] = cost_q, cut_q
         slots = slots_for(cu, cfg, cost_q, cut_q)
         trees = build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"],

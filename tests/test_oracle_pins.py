@@ -841,3 +841,34 @@ def test_ar_propagation_matrix_form_and_constant():
                         np.full((1, 1, L), 2.0, np.float32), np.array([0, L]), cfg.replace(n_hops=1))
     assert np.allclose(outc["rel"][0, 0], 2.0 + wf * 2.0, rtol=1e-6)
     assert abs(d1[0] - wf * r[0]) < 1e-12
+
+
+# ---------------------------------------------------------------- multi-depth turns and surprisal (NEXT 1)
+def test_partition_depths_and_surprisal_compose():
+    rng = np.random.default_rng(41)
+    L, Dh = 96, 16
+    cfg = _cfg(lens=[L], slot_len=0, slot_min=4, slot_max=12, slot_target=8, lambda_surp=1.0)
+    cu = np.array([0, L])
+    h1 = rng.standard_normal((L, Dh))
+    h2 = rng.standard_normal((L, Dh))
+    c1, k1 = opart.slot_costs(h1, cu, cfg)
+    c2, k2 = opart.slot_costs(h2, cu, cfg)
+    # identical depths reproduce the single trajectory (up to one quantum)
+    cs, ks = opart.slot_costs(np.stack([h1, h1, h1]), cu, cfg)
+    assert np.abs(cs - c1).max() <= 1 and np.abs(ks - k1).max() <= 1
+    # two depths: the mean of the two dispersions (the length term once), and
+    # where both windows are valid at both depths the mean of the two turns
+    cm, km = opart.slot_costs(np.stack([h1, h2]), cu, cfg)
+    valid = c1 != 0
+    assert np.abs(cm[valid] - (c1[valid] + c2[valid]) / 2).max() <= 1
+    inner = slice(8, L - 8)
+    assert np.abs(km[inner] - (k1[inner] + k2[inner]) / 2).max() <= 1
+    # surprisal: lambda_surp * s / max s on top of the turning bonus
+    sur = rng.random(L) * 3.0
+    cs2, ks2 = opart.slot_costs(h1, cu, cfg, surprisal=sur)
+    assert np.array_equal(cs2, c1)
+    want = np.array([opart._q(float(np.float32(cfg.lambda_surp)) * sur[b] / sur.max()) for b in range(L)])
+    assert np.abs(ks2 - k1 - want).max() <= 1
+    # a non-positive surprisal maximum adds nothing
+    _, ks3 = opart.slot_costs(h1, cu, cfg, surprisal=np.zeros(L))
+    assert np.array_equal(ks3, k1)

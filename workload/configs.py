@@ -56,6 +56,9 @@ class Config:
     w_dtype: str = "bf16"
     logit_tau: float = 4.0
     hidden_dim: int = 0          # >0: hidden-state trajectories are drawn
+    n_depth: int = 1             # sampled depths of the hidden-state trajectories (shared turns)
+    surprisal: bool = False      # draw a per-token surprisal (higher at trajectory turns)
+    lambda_surp: float = 1.0     # DP weight of the normalized surprisal at a cut
     plant: str = "spans"         # "evidence" | "spans" | "chains"
     n_plant: int = 64            # evidence tokens / spans / chains per sequence
     span_len: tuple = (4, 16)

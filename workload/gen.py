@@ -10,7 +10,9 @@ Layouts (T = sum of sequence lengths, tokens of all sequences concatenated):
   K, V       [Ly][H][T][d]              cached keys / values
   Qp         [S][Ly][H*G][P][d]         probe queries (question / tail probes)
   Qctx       [Ly][H*G][T][d]            prefill queries of every cached token
-  hidden     [T][hidden_dim]            sampled hidden states (DP slots only)
+  hidden     [T][hidden_dim]            sampled hidden states (DP slots only);
+             [n_depth][T][hidden_dim]   with several sampled depths
+  surprisal  [T] fp32                   per-token surprisal (optional)
   Qd         [T_dec][S][Ly][H*G][d]     decode queries
   Kd, Vd     [Ly][H][S][T_dec][d]       decode-time appended keys / values
   W          [vocab][H*G*d]             seeded vocab projection
@@ -154,6 +156,7 @@ def make_inputs(cfg: Config, device: str = "cpu", seed: int | None = None,
         V = V * sc
 
     hidden = None
+    turns = []          # (global start, length) of every trajectory segment
     if cfg.hidden_dim > 0:
         Dh = cfg.hidden_dim
         hidden = torch.empty((T, Dh), dtype=torch.float32, device=dev)
@@ -163,6 +166,7 @@ def make_inputs(cfg: Config, device: str = "cpu", seed: int | None = None,
             while i < L:
                 n = int(torch.randint(16, 113, (1,), generator=hgen))
                 n = min(n, L - i)
+                turns.append((cu[s] + i, n))
                 c = _unit(torch.randn((Dh,), generator=gen, device=dev))
                 u = _unit(torch.randn((Dh,), generator=gen, device=dev))
                 t = torch.arange(n, device=dev, dtype=torch.float32).view(n, 1) / max(n, 1)
@@ -202,6 +206,33 @@ def make_inputs(cfg: Config, device: str = "cpu", seed: int | None = None,
     W = torch.randn((cfg.vocab, Dm), generator=gen, device=dev, dtype=torch.float32)
     W = (W * (cfg.logit_tau / math.sqrt(Dm))).to(_DT[cfg.w_dtype])
 
+    # Extra sampled depths and the surprisal come from generators of their
+    # own, after every other draw, so the single-depth inputs do not change.
+    # Every depth turns at the same positions with its own directions.
+    if hidden is not None and cfg.n_depth > 1:
+        g2 = torch.Generator(device=dev)
+        g2.manual_seed(seed + 7919)
+        Dh = cfg.hidden_dim
+        layers = [hidden]
+        for _ in range(cfg.n_depth - 1):
+            hd = torch.empty((T, Dh), dtype=torch.float32, device=dev)
+            for (a0, n) in turns:
+                c = _unit(torch.randn((Dh,), generator=g2, device=dev))
+                u = _unit(torch.randn((Dh,), generator=g2, device=dev))
+                t = torch.arange(n, device=dev, dtype=torch.float32).view(n, 1) / max(n, 1)
+                noise = torch.randn((n, Dh), generator=g2, device=dev) * (0.002 / math.sqrt(Dh))
+                hd[a0:a0 + n] = c.view(1, Dh) + 0.5 * t * u.view(1, Dh) + noise
+            layers.append(hd.to(dt))
+        hidden = torch.stack(layers, 0)
+    surprisal = None
+    if cfg.surprisal:
+        g3 = torch.Generator()
+        g3.manual_seed(seed + 104729)
+        sur = -torch.log(torch.rand((T,), generator=g3, dtype=torch.float64).clamp_min(1e-12))
+        for (a0, n) in turns:
+            sur[a0] += 2.0
+        surprisal = sur.float().to(dev)
+
     out = {
         "cu_seqlens": cu_t,
         "K": K.to(dt).contiguous(),
@@ -209,6 +240,7 @@ def make_inputs(cfg: Config, device: str = "cpu", seed: int | None = None,
         "Qp": Qp.to(dt).contiguous(),
         "Qctx": None if Qctx is None else Qctx.to(dt).contiguous(),
         "hidden": hidden,
+        "surprisal": surprisal,
         "Qd": Qd.to(dt).contiguous(),
         "Kd": Kd.to(dt).contiguous(),
         "Vd": Vd.to(dt).contiguous(),
