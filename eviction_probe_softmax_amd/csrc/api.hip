@@ -113,6 +113,8 @@ extern "C" void kvc_params_default(kvc_params* p) {
   p->lambda_curv = 4.0f;
   p->rope_base = 1e6f;
   p->window = 64;
+  p->n_depth = 1;
+  p->lambda_surp = 1.0f;
 }
 
 extern "C" int kvc_budgets(const kvc_shape* shape, const kvc_params* prm, int64_t* B,

@@ -29,9 +29,16 @@ namespace {
 constexpr double QSCALE = 1048576.0;  // 2^20
 constexpr int64_t INF_Q = (int64_t)1 << 52;
 
+constexpr int MAXD = 4;  // sampled depths of the trajectory
+
 struct PartArgs {
-  const void* hidden;
+  const void* hidden;       // [nd][T][Dh]
   int Dh;
+  int nd;                   // sampled depths
+  int64_t dstride;          // elements between depths (T * Dh)
+  const float* surp;        // [T] surprisal, or NULL
+  float lam_surp;
+  float* smax;              // [S] largest surprisal of each sequence
   const int64_t* cu;
   int S;
   int64_t T;
@@ -40,16 +47,16 @@ struct PartArgs {
   int64_t c0[64], c1[64];   // compressible region per sequence (sequence positions)
   int64_t* cost_q;          // [T][nmax - nmin + 1]
   int64_t* cut_q;           // [T]
-  float* inv;               // [T] 1/||h_t||
-  float* nrm2;              // [T] ||h^_t||^2
+  float* inv;               // [nd][T] 1/||h_t||
+  float* nrm2;              // [nd][T] ||h^_t||^2
   int32_t* slot_start;      // [S][stride + 1]
   int32_t* n_slots;         // [S]
 };
 
 template <class T>
 __global__ __launch_bounds__(256) void norm_kernel(PartArgs a) {
-  int64_t t = blockIdx.x;
-  const T* h = (const T*)a.hidden + t * a.Dh;
+  const int64_t t = blockIdx.x, dep = blockIdx.y;
+  const T* h = (const T*)a.hidden + dep * a.dstride + t * a.Dh;
   float ss = 0.f;
   for (int i = threadIdx.x; i < a.Dh; i += 256) {
     float x = ElemIO<T>::ld(h, i);
@@ -62,14 +69,28 @@ __global__ __launch_bounds__(256) void norm_kernel(PartArgs a) {
   if (threadIdx.x == 0) {
     float tot = red[0] + red[1] + red[2] + red[3];
     float iv = tot > 0.f ? 1.f / sqrtf(tot) : 0.f;
-    a.inv[t] = iv;
-    a.nrm2[t] = tot * iv * iv;
+    a.inv[dep * a.T + t] = iv;
+    a.nrm2[dep * a.T + t] = tot * iv * iv;
   }
 }
 
 __device__ __forceinline__ int64_t qround(double x) { return (int64_t)floor(x * QSCALE + 0.5); }
 
-// kappa_b = mean over valid windows of (1 - cos(h^_b - h^_{b-w}, h^_{b+w} - h^_b)) / 2
+// Largest surprisal of each sequence (one block per sequence).
+__global__ __launch_bounds__(256) void surp_max_kernel(PartArgs a) {
+  const int s = blockIdx.x;
+  float m = -INFINITY;
+  for (int64_t t = a.cu[s] + threadIdx.x; t < a.cu[s + 1]; t += 256) m = fmaxf(m, a.surp[t]);
+  __shared__ float red[4];
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) a.smax[s] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// kappa_b = mean over valid (depth, window) pairs of
+// (1 - cos(h^_b - h^_{b-w}, h^_{b+w} - h^_b)) / 2; the cut bonus adds the
+// surprisal over its sequence maximum
 template <class T>
 __global__ __launch_bounds__(256) void turning_kernel(PartArgs a) {
   int64_t t = blockIdx.x;
@@ -80,11 +101,13 @@ __global__ __launch_bounds__(256) void turning_kernel(PartArgs a) {
   const int ws[2] = {2, 8};
   float acc = 0.f;
   int nval = 0;
-  const T* H = (const T*)a.hidden;
+  for (int dep = 0; dep < a.nd; ++dep)
   for (int wi = 0; wi < 2; ++wi) {
+    const T* H = (const T*)a.hidden + dep * a.dstride;
+    const float* inv = a.inv + dep * a.T;
     int w = ws[wi];
     if (b - w < 0 || b + w > L - 1) continue;
-    float ib = a.inv[t], ip = a.inv[t - w], iq = a.inv[t + w];
+    float ib = inv[t], ip = inv[t - w], iq = inv[t + w];
     float uv = 0.f, uu = 0.f, vv = 0.f;
     for (int i = threadIdx.x; i < a.Dh; i += 256) {
       float xb = ElemIO<T>::ld(H, t * a.Dh + i) * ib;
@@ -114,7 +137,9 @@ __global__ __launch_bounds__(256) void turning_kernel(PartArgs a) {
   }
   if (threadIdx.x == 0) {
     float kap = nval ? acc / (float)nval : 0.f;
-    a.cut_q[t] = qround((double)a.lam_curv * (double)kap);
+    double bonus = (double)a.lam_curv * (double)kap;
+    if (a.surp && a.smax[s] > 0.f) bonus += (double)a.lam_surp * (double)a.surp[t] / (double)a.smax[s];
+    a.cut_q[t] = qround(bonus);
   }
 }
 
@@ -128,10 +153,12 @@ __global__ __launch_bounds__(256) void gram_kernel(PartArgs a, float* G) {
   using namespace kvcmf;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // block = 32-row i-block; its 4 waves take j-blocks ib + wave .. (5 tiles cover the band)
-  const int64_t ib = blockIdx.x;
+  const int64_t ib = blockIdx.x, dep = blockIdx.y;
   const int64_t i0 = ib * 32;
   if (i0 >= a.T) return;
-  const T* H = (const T*)a.hidden;
+  const T* H = (const T*)a.hidden + dep * a.dstride;
+  const float* inv = a.inv + dep * a.T;
+  G += dep * a.T * BW;
   for (int jt = wave; jt < 5; jt += 4) {
     const int64_t j0 = i0 + (int64_t)jt * 32;
     if (j0 >= a.T) break;
@@ -149,15 +176,15 @@ __global__ __launch_bounds__(256) void gram_kernel(PartArgs a, float* G) {
     for (int v = 0; v < 16; ++v) {
       int64_t i = i0 + acc_row(v, lane), j = rj;
       int64_t kk = j - i;
-      if (i < a.T && j < a.T && kk >= 0 && kk < BW) G[i * BW + kk] = acc[v] * a.inv[i] * a.inv[j];
+      if (i < a.T && j < a.T && kk >= 0 && kk < BW) G[i * BW + kk] = acc[v] * inv[i] * inv[j];
     }
   }
 }
 
 // Inclusive prefix sums along every band row, in place.
 __global__ void band_prefix_kernel(PartArgs a, float* G) {
-  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= a.T) return;
+  int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // row of every depth
+  if (g >= a.T * a.nd) return;
   float* r = G + g * BW;
   float run = 0.f;
   for (int k = 0; k < BW; ++k) {
@@ -177,19 +204,26 @@ __global__ __launch_bounds__(256) void window_cost_kernel(PartArgs a, const floa
   if (p < a.c0[s] || p >= a.c1[s]) return;
   const int ncol = a.nmax - a.nmin + 1;
   int64_t* row = a.cost_q + t * ncol;
-  float W = 0.f, sq = 0.f;
+  float W[MAXD], sq[MAXD];
+#pragma unroll
+  for (int dd = 0; dd < MAXD; ++dd) W[dd] = sq[dd] = 0.f;
   for (int n = 1; n <= a.nmax; ++n) {
     int64_t i = p - n + 1;                    // token joining the window
     if (i < a.c0[s]) break;
     int64_t g = a.cu[s] + i;
-    const float* gr = G + g * BW;
-    float g0 = gr[0];
-    W += 2.f * (gr[n - 1] - g0) + g0;
-    sq += a.nrm2[g];
+    double disp = 0.0;
+#pragma unroll
+    for (int dd = 0; dd < MAXD; ++dd) {
+      if (dd >= a.nd) break;
+      const float* gr = G + (dd * a.T + g) * BW;
+      float g0 = gr[0];
+      W[dd] += 2.f * (gr[n - 1] - g0) + g0;
+      sq[dd] += a.nrm2[dd * a.T + g];
+      disp += (double)sq[dd] - (double)W[dd] / (double)n;
+    }
     if (n >= a.nmin) {
-      double disp = (double)sq - (double)W / (double)n;
       double x = ((double)n - a.target) / (double)a.target;
-      row[n - a.nmin] = qround(disp + (double)a.lam_len * x * x);
+      row[n - a.nmin] = qround(disp / (double)a.nd + (double)a.lam_len * x * x);
     }
   }
 }
@@ -304,11 +338,14 @@ __global__ void fixed_slots_kernel(PartArgs a, int slot_len) {
 namespace kvc {
 size_t ws_partition(const kvc_shape* s, const kvc_params* p) {
   int ncol = p->slot_max - p->slot_min + 1;
+  const int nd = p->n_depth > 1 ? p->n_depth : 1;
   Carver c(nullptr, 0);
-  c.take<float>((size_t)s->total_tokens * 2);
+  c.take<float>((size_t)s->total_tokens * nd);
+  c.take<float>((size_t)s->total_tokens * nd);
   c.take<int64_t>((size_t)s->total_tokens * (ncol > 0 ? ncol : 1));
   c.take<int64_t>((size_t)s->total_tokens);
-  c.take<float>((size_t)s->total_tokens * BW);
+  c.take<float>((size_t)s->total_tokens * BW * nd);
+  c.take<float>(64);
   return c.off + 256;
 }
 }  // namespace kvc
@@ -316,6 +353,13 @@ size_t ws_partition(const kvc_shape* s, const kvc_params* p) {
 extern "C" int kvc_partition(const kvc_shape* sh, const kvc_params* p, const void* hidden, int32_t hidden_dim,
                              int32_t mode, int64_t* dp_cost_q, int64_t* dp_cut_q, int32_t* slot_start,
                              int32_t* n_slots, void* ws, size_t ws_bytes, hipStream_t st) {
+  return kvc_partition_ex(sh, p, hidden, hidden_dim, nullptr, mode, dp_cost_q, dp_cut_q, slot_start, n_slots, ws,
+                          ws_bytes, st);
+}
+
+extern "C" int kvc_partition_ex(const kvc_shape* sh, const kvc_params* p, const void* hidden, int32_t hidden_dim,
+                                const float* surprisal, int32_t mode, int64_t* dp_cost_q, int64_t* dp_cut_q,
+                                int32_t* slot_start, int32_t* n_slots, void* ws, size_t ws_bytes, hipStream_t st) {
   int r = kvc::validate_shape(sh);
   if (r) return r;
   if ((r = kvc::validate_params(sh, p))) return r;
@@ -348,12 +392,18 @@ extern "C" int kvc_partition(const kvc_shape* sh, const kvc_params* p, const voi
   KVC_REQUIRE(kvc::max_len(sh) <= 32768, KVC_E_SHAPE, "kvc_partition: DP slots need sequences <= 32768 tokens");
   KVC_REQUIRE(ws && ws_bytes >= kvc::ws_partition(sh, p), KVC_E_WORKSPACE, "kvc_partition: workspace too small");
   int ncol = p->slot_max - p->slot_min + 1;
+  KVC_REQUIRE(p->n_depth >= 0 && p->n_depth <= MAXD, KVC_E_INVAL, "kvc_partition: n_depth must be in [1, 4]");
+  a.nd = p->n_depth > 1 ? p->n_depth : 1;
+  a.dstride = sh->total_tokens * (int64_t)hidden_dim;
+  a.surp = surprisal;
+  a.lam_surp = p->lambda_surp;
   kvc::Carver c(ws, ws_bytes);
-  a.inv = c.take<float>((size_t)sh->total_tokens);
-  a.nrm2 = c.take<float>((size_t)sh->total_tokens);
+  a.inv = c.take<float>((size_t)sh->total_tokens * a.nd);
+  a.nrm2 = c.take<float>((size_t)sh->total_tokens * a.nd);
   int64_t* cq = c.take<int64_t>((size_t)sh->total_tokens * ncol);
   int64_t* kq = c.take<int64_t>((size_t)sh->total_tokens);
-  float* gband = c.take<float>((size_t)sh->total_tokens * BW);
+  float* gband = c.take<float>((size_t)sh->total_tokens * BW * a.nd);
+  a.smax = c.take<float>(64);
   if (mode == 1) {
     KVC_REQUIRE(dp_cost_q && dp_cut_q, KVC_E_INVAL, "kvc_partition: mode 1 needs dp_cost_q and dp_cut_q");
     a.cost_q = dp_cost_q;
@@ -367,18 +417,24 @@ extern "C" int kvc_partition(const kvc_shape* sh, const kvc_params* p, const voi
     a.cut_q = dp_cut_q ? dp_cut_q : kq;
     KVC_REQUIRE(p->slot_max <= BW, KVC_E_UNSUPPORTED, "kvc_partition: slot_max above 128");
     KVC_REQUIRE(hidden_dim % 16 == 0, KVC_E_SHAPE, "kvc_partition: hidden_dim must be a multiple of 16");
-    dim3 gt((unsigned)sh->total_tokens), gg(kvc_blocks(sh->total_tokens, 32)), gw(kvc_blocks(sh->total_tokens, 256));
+    dim3 gt((unsigned)sh->total_tokens), gn((unsigned)sh->total_tokens, (unsigned)a.nd);
+    dim3 gg(kvc_blocks(sh->total_tokens, 32), (unsigned)a.nd), gw(kvc_blocks(sh->total_tokens, 256));
     if (sh->total_tokens > 0) {
+      if (surprisal) {
+        hipLaunchKernelGGL(surp_max_kernel, dim3(sh->n_seq), dim3(256), 0, st, a);
+        KVC_LAUNCH_CHECK("surp_max");
+      }
       if (sh->dtype == KVC_BF16) {
-        hipLaunchKernelGGL(norm_kernel<uint16_t>, gt, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(norm_kernel<uint16_t>, gn, dim3(256), 0, st, a);
         hipLaunchKernelGGL(turning_kernel<uint16_t>, gt, dim3(256), 0, st, a);
         hipLaunchKernelGGL(gram_kernel<uint16_t>, gg, dim3(256), 0, st, a, gband);
       } else {
-        hipLaunchKernelGGL(norm_kernel<float>, gt, dim3(256), 0, st, a);
+        hipLaunchKernelGGL(norm_kernel<float>, gn, dim3(256), 0, st, a);
         hipLaunchKernelGGL(turning_kernel<float>, gt, dim3(256), 0, st, a);
         hipLaunchKernelGGL(gram_kernel<float>, gg, dim3(256), 0, st, a, gband);
       }
-      hipLaunchKernelGGL(band_prefix_kernel, gw, dim3(256), 0, st, a, gband);
+      hipLaunchKernelGGL(band_prefix_kernel, dim3(kvc_blocks(sh->total_tokens * a.nd, 256)), dim3(256), 0, st, a,
+                         gband);
       hipLaunchKernelGGL(window_cost_kernel, gw, dim3(256), 0, st, a, (const float*)gband);
       KVC_LAUNCH_CHECK("partition_costs");
     }

@@ -31,7 +31,7 @@ STAGE_SCORE, STAGE_PROPAGATE, STAGE_PARTITION, STAGE_TREES, STAGE_AUCTION, STAGE
 
 EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets", "kvc_pack_capacity",
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
-           "kvc_partition", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
+           "kvc_partition", "kvc_partition_ex", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
            "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
            "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune",
            "kvc_propagate_dense_workspace", "kvc_propagate_dense", "kvc_propagate_ar_workspace",
@@ -53,7 +53,8 @@ class Params(C.Structure):
                 ("value_base", C.c_float), ("floor_frac", C.c_float), ("token_mode", C.c_int32),
                 ("slot_len", C.c_int32), ("slot_min", C.c_int32), ("slot_max", C.c_int32),
                 ("slot_target", C.c_int32), ("lambda_len", C.c_float), ("lambda_curv", C.c_float),
-                ("rope_base", C.c_float), ("hybrid_frac", C.c_float), ("window", C.c_int32)]
+                ("rope_base", C.c_float), ("hybrid_frac", C.c_float), ("window", C.c_int32),
+                ("n_depth", C.c_int32), ("lambda_surp", C.c_float)]
 
 
 class Trees(C.Structure):
@@ -93,6 +94,8 @@ _sig = {
     "kvc_propagate": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, C.c_size_t, _P]),
     "kvc_partition": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, C.c_int32, C.c_int32, _P, _P, _P,
                                 _P, _P, C.c_size_t, _P]),
+    "kvc_partition_ex": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, C.c_int32, _P, C.c_int32, _P, _P, _P,
+                                   _P, _P, C.c_size_t, _P]),
     "kvc_build_trees": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, C.POINTER(Trees), _P, C.c_size_t, _P]),
     "kvc_auction": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.POINTER(Trees), _P, _P, _P, _P, _P,
@@ -220,6 +223,8 @@ def make_problem(cfg, cu_seqlens: torch.Tensor, dtype: torch.dtype, device="cuda
     p.rope_base = cfg.rope_base
     p.hybrid_frac = getattr(cfg, "hybrid_frac", 0.0)
     p.window = getattr(cfg, "window", 64)
+    p.n_depth = getattr(cfg, "n_depth", 1)
+    p.lambda_surp = getattr(cfg, "lambda_surp", 1.0)
     return Problem(sh, p, cu_host, cu_dev, dev)
 
 
@@ -262,7 +267,8 @@ def propagate(pb: Problem, K, Qctx, rel0, want_seeds=True):
     return {"rel": rel, "seeds": seeds}
 
 
-def partition(pb: Problem, hidden=None, hidden_dim=0, cost_q=None, cut_q=None, inject=False, export=False):
+def partition(pb: Problem, hidden=None, hidden_dim=0, cost_q=None, cut_q=None, inject=False, export=False,
+              surprisal=None):
     dev = pb.device
     stride = pb.slot_stride()
     slot_start = torch.empty((pb.S, stride + 1), dtype=torch.int32, device=dev)
@@ -272,9 +278,9 @@ def partition(pb: Problem, hidden=None, hidden_dim=0, cost_q=None, cut_q=None, i
         cost_q = torch.zeros((pb.T, nmax - nmin + 1), dtype=torch.int64, device=dev)
         cut_q = torch.zeros((pb.T,), dtype=torch.int64, device=dev)
     ws = pb.ws(STAGE_PARTITION)
-    st = _lib.kvc_partition(C.byref(pb.shape), C.byref(pb.params), _ptr(hidden), hidden_dim, 1 if inject else 0,
-                            _ptr(cost_q), _ptr(cut_q), _ptr(slot_start), _ptr(n_slots), _ptr(ws), ws.numel(),
-                            _stream())
+    st = _lib.kvc_partition_ex(C.byref(pb.shape), C.byref(pb.params), _ptr(hidden), hidden_dim, _ptr(surprisal),
+                               1 if inject else 0, _ptr(cost_q), _ptr(cut_q), _ptr(slot_start), _ptr(n_slots),
+                               _ptr(ws), ws.numel(), _stream())
     _check("kvc_partition", st)
     return {"slot_start": slot_start, "n_slots": n_slots, "dp_cost_q": cost_q, "dp_cut_q": cut_q}
 

@@ -47,7 +47,7 @@ class Compressor:
         if cfg.slot_len > 0:
             part = kvc.partition(pb)
         else:
-            part = kvc.partition(pb, inp["hidden"], cfg.hidden_dim)
+            part = kvc.partition(pb, inp["hidden"], cfg.hidden_dim, surprisal=inp.get("surprisal"))
         out.update(part)
         tr = kvc.build_trees(pb, inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"], self.rope_cos,
                              self.rope_sin, part["slot_start"], part["n_slots"])

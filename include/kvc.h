@@ -89,6 +89,8 @@ typedef struct kvc_params {
   float rope_base;         /* RoPE theta base */
   float hybrid_frac;       /* head-level hybrid: share of (l, h) units kept whole (0 = off) */
   int32_t window;          /* step-wise eviction: recent queries behind the features (w = 64) */
+  int32_t n_depth;         /* sampled depths of the hidden-state trajectory (1..4) */
+  float lambda_surp;       /* DP weight of surprisal / its sequence maximum at a cut */
 } kvc_params;
 
 typedef struct kvc_trees {
@@ -217,6 +219,18 @@ int kvc_partition(const kvc_shape* shape, const kvc_params* prm, const void* hid
                   int32_t hidden_dim, int32_t mode, int64_t* dp_cost_q, int64_t* dp_cut_q,
                   int32_t* slot_start, int32_t* n_slots, void* ws, size_t ws_bytes,
                   hipStream_t stream);
+/* Slots from several sampled depths and surprisal (GraceKV page, 'Technical
+ * details and default settings': turns stabilized across sampled depths and
+ * windows, surprisal a smaller auxiliary boundary signal). hidden is
+ * [n_depth][T][hidden_dim] (prm->n_depth); the turning score is the mean over
+ * every valid (depth, window) pair, the dispersion the mean over depths, and
+ * a cut before token b also earns lambda_surp * surprisal[b] / (largest
+ * surprisal of its sequence) when that maximum is positive; surprisal [T]
+ * fp32 device, nullable. kvc_partition is this call with surprisal NULL. */
+int kvc_partition_ex(const kvc_shape* shape, const kvc_params* prm, const void* hidden,
+                     int32_t hidden_dim, const float* surprisal, int32_t mode, int64_t* dp_cost_q,
+                     int64_t* dp_cut_q, int32_t* slot_start, int32_t* n_slots, void* ws,
+                     size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------ A4
  * kvc_build_trees: prototype trees per (s, l, h, slot).

@@ -29,7 +29,8 @@ def _run_gpu(cfg, inp):
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("mistral1", {}), ("stress", {}), ("ragged", {}),
                                      ("fulldepth", {}), ("ragged", {"hybrid_frac": 0.5}),
                                      ("fulldepth", {"hybrid_frac": 0.25, "budget_ratio": 0.4}),
-                                     ("mistral1", {"hybrid_frac": 0.5, "budget_ratio": 0.6})])
+                                     ("mistral1", {"hybrid_frac": 0.5, "budget_ratio": 0.6}),
+                                     ("fulldepth", {"n_depth": 3, "surprisal": True})])
 def test_end_to_end_matches_oracle(name, kw):
     cfg = small_config(name, **kw)
     inp = make_inputs(cfg)

@@ -167,7 +167,10 @@ def test_pack_tree_mode(name, kw):
 
 
 @pytest.mark.parametrize("name,kw", [("fulldepth", {}), ("fulldepth", {"lens": [300, 21, 517], "S": 3}),
-                                     ("fulldepth", {"slot_min": 4, "slot_max": 12, "slot_target": 8})])
+                                     ("fulldepth", {"slot_min": 4, "slot_max": 12, "slot_target": 8}),
+                                     ("fulldepth", {"n_depth": 3, "surprisal": True}),
+                                     ("fulldepth", {"n_depth": 2, "surprisal": True, "lens": [300, 21, 517],
+                                                    "S": 3, "lambda_surp": 0.5})])
 def test_partition_dp(name, kw):
     kvc = _kvc()
     cfg = small_config(name, **kw)
@@ -175,14 +178,14 @@ def test_partition_dp(name, kw):
     dinp = inputs_to(inp)
     print(f"[partition] {name} {kw}", flush=True)
     cu = inp["cu_seqlens"].numpy()
-    cq, kq = opart.slot_costs(inp["hidden"], cu, cfg)
+    cq, kq = opart.slot_costs(inp["hidden"], cu, cfg, inp.get("surprisal"))
     slots = oracle.slots_for(cu, cfg, cq, kq)
     pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
     # DP fed the oracle's quantized costs: identical cuts
     g = kvc.partition(pb, cost_q=to_dev(cq), cut_q=to_dev(kq), inject=True)
     assert slots_from_dev(g["slot_start"], g["n_slots"]) == slots
     # the GPU's own costs
-    g2 = kvc.partition(pb, dinp["hidden"], cfg.hidden_dim, export=True)
+    g2 = kvc.partition(pb, dinp["hidden"], cfg.hidden_dim, export=True, surprisal=dinp.get("surprisal"))
     torch.cuda.synchronize()
     gq = as_np(g2["dp_cost_q"]).astype(np.float64)
     valid = cq != 0
