@@ -121,7 +121,8 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     (DistillCache paper, Appendix E.3). Step-wise eviction: the scoring-MLP
     loop of DistillCache's Algorithm 1 at the same budget ratio. Dense
     rollout: both propagation hops with every token a seed; the "A r"
-    direction: both hops with every token a receiver."""
+    direction: both hops with every token a receiver. Slots cut from three
+    sampled depths with the surprisal bonus."""
     import numpy as np
     import torch
     from eviction_probe_softmax_amd import kvc
@@ -153,6 +154,20 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
                      "packed_entries": int(res["cache"]["seg_len"].to(torch.int64).sum()),
                      "units_kept_whole": int(full_units.sum()),
                      "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
+    # Slots cut from three sampled depths with the surprisal bonus
+    from workload import make_inputs
+    vcfg = cfg.replace(n_depth=3, surprisal=True)
+    vin = make_inputs(vcfg, device="cuda")
+    comp = Compressor(vcfg, vin["cu_seqlens"], vin["K"].dtype)
+    comp.compress(vin)  # warm-up
+    e3 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e3[0].record(stream)
+    res3 = comp.compress(vin)
+    e3[1].record(stream)
+    torch.cuda.synchronize()
+    out["dp_3depths_surprisal"] = {"compress_ms": round(e3[0].elapsed_time(e3[1]), 3),
+                                   "slots": int(res3["n_slots"].sum())}
+    del vin, comp, res3
     # Step-wise eviction (DistillCache Algorithm 1) with a seeded scoring MLP:
     # one prefill prune, then per decode step append + decode + score + prune
     from workload import make_policy
