@@ -197,9 +197,56 @@ def _capped_priorities(util, cost, slots, T, cu0=0):
     return cap
 
 
+def _check_capped_top(g, rest, util, slots, T, k_rest):
+    """g: taken flags (flat); rest: capped priorities of the competing ops
+    (-inf elsewhere). Above the threshold priority every op is taken, below
+    none; the ops tied with it are completed best-first from the exposed ones
+    of their slot (the greedy pops the highest utility among exposed ops),
+    which a plain (priority, id) order does not state."""
+    ids = np.nonzero(np.isfinite(rest))[0]
+    order = np.lexsort((ids, -rest[ids]))
+    thr = rest[ids[order[k_rest - 1]]] if k_rest > 0 else np.inf
+    above = np.isfinite(rest) & (rest > thr)
+    tied = np.nonzero(rest == thr)[0]
+    k_tied = k_rest - int(above.sum())
+    assert g[above].all()
+    assert not g[np.isfinite(rest) & (rest < thr)].any()
+    slot_of = {}
+    for (st, n) in slots:
+        for q in range(2 * n):
+            slot_of[2 * st + q] = (st, n)
+    groups = {(int(t) // (2 * T), slot_of[int(t) % (2 * T)]) for t in tied}
+    if len(groups) == 1:
+        (u, (st, n)), = groups
+        nodes = otrees.tree_nodes(0, n)
+        base = u * 2 * T + 2 * st
+        kids, creator = {0: [1] if nodes[0][2] >= 0 else []}, {}
+        for j, (_, _, lc, rc) in enumerate(nodes):
+            if lc >= 0:
+                kids[1 + j] = [1 + c for c in (lc, rc) if nodes[c][2] >= 0]
+                for c in kids[1 + j]:
+                    creator[c] = 1 + j
+        if 1 in kids[0]:
+            creator[1] = 0
+        uflat = util.reshape(-1)
+        tied_set = set(int(t) for t in tied)
+        exposed = [q for q in range(2 * n) if base + q in tied_set and (q == 0 or above[base + creator[q]])]
+        taken_tied = set()
+        for _ in range(k_tied):
+            q = max(exposed, key=lambda q: (float(uflat[base + q]), -(base + q)))
+            exposed.remove(q)
+            taken_tied.add(base + q)
+            exposed += [c for c in kids.get(q, []) if base + c in tied_set]
+        assert set(np.nonzero(g & (rest == thr))[0].tolist()) == taken_tied
+    else:
+        assert int((g & (rest == thr)).sum()) == k_tied
+    return len(tied)
+
+
 def test_fullsize_auction_is_the_capped_priority_top(run):
-    """Without the floor, the greedy auction with unit costs takes exactly the
-    allocatable budget's top ops by (capped priority desc, op index asc)."""
+    """Without the floor, the greedy auction with unit costs takes every op
+    above the allocatable budget's threshold capped priority, none below, and
+    completes the ops tied with it best-first."""
     kvc = _kvc()
     cfg0, inp, out = run["cfg"], run["inp"], run["out"]
     cfg = cfg0.replace(floor_frac=0.0)
@@ -214,14 +261,11 @@ def test_fullsize_auction_is_the_capped_priority_top(run):
     cap = _capped_priorities(util, cost, slots, T).reshape(-1)
     valid = np.isfinite(cap)
     B_alloc = budgets(cfg.lens, cfg)[0]["alloc"]
-    ids = np.nonzero(valid)[0]
-    order = np.lexsort((ids, -cap[ids]))
-    want = np.zeros(cap.shape, dtype=bool)
-    want[ids[order[:B_alloc]]] = True
     got = as_np(au["taken"]).reshape(-1).astype(bool)
-    assert int(as_np(au["spent"])[0]) == min(B_alloc, int(valid.sum()))
-    assert np.array_equal(got, want), int((got != want).sum())
-    print(f"  {int(got.sum())} ops taken of {int(valid.sum())}", flush=True)
+    k = min(B_alloc, int(valid.sum()))
+    assert int(as_np(au["spent"])[0]) == k and int(got.sum()) == k
+    ntied = _check_capped_top(got, cap, util, slots, T, k)
+    print(f"  {int(got.sum())} ops taken of {int(valid.sum())}, {ntied} tied at the threshold", flush=True)
 
 
 def test_fullsize_taken_set_and_pack_structure(run):
@@ -308,3 +352,87 @@ def test_fullsize_decode_sampled(run):
             close(go[0, l, h * G:(h + 1) * G], want, 2e-2, "decode o", floor=1e-2)
         # x is the layer sum of o, in layer order
         close(as_np(x)[0], go[0].sum(axis=0).reshape(-1), 1e-5, "x = sum over layers", floor=1e-5)
+
+
+def test_fullsize_hybrid_auction(run):
+    """Head-level hybrid at full size, floor off: the K units with the largest
+    head sensitivity keep every real op; the rest of the allocatable budget
+    buys exactly the top of the capped-priority order over the other units."""
+    kvc = _kvc()
+    cfg0, inp, out = run["cfg"], run["inp"], run["out"]
+    cfg = cfg0.replace(floor_frac=0.0, hybrid_frac=0.2)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    tr = out["trees"]
+    au = kvc.auction(pb, tr, out["rel"], out["head_sens"], out["slot_start"], out["n_slots"])
+    full_g = as_np(kvc.hybrid_units(pb, out["head_sens"])).reshape(-1).astype(bool)
+    torch.cuda.synchronize()
+    Ly, H, T = cfg.Ly, cfg.H, cfg.T
+    b = budgets(cfg.lens, cfg)[0]
+    K, C = b["full_units"], b["comp_len"]
+    sens = as_np(out["head_sens"]).reshape(-1)
+    order_u = np.lexsort((np.arange(Ly * H), -sens))
+    full = np.zeros(Ly * H, dtype=bool)
+    full[order_u[:K]] = True
+    assert np.array_equal(full_g, full) and K == int(0.2 * Ly * H)
+    util = as_np(tr["op_util"]).reshape(Ly * H, 2 * T)
+    cost = as_np(tr["op_cost"]).reshape(Ly * H, 2 * T)
+    slots = slots_from_dev(out["slot_start"], out["n_slots"])[0]
+    cap = _capped_priorities(util, cost, slots, T)
+    want = np.zeros(cap.shape, dtype=bool)
+    want[full] = cost[full] > 0
+    rest = cap.copy()
+    rest[full] = -np.inf
+    rest = rest.reshape(-1)
+    k_rest = min(b["rest"], int(np.isfinite(rest).sum()))
+    got = as_np(au["taken"]).reshape(Ly * H, 2 * T).astype(bool)
+    assert int(as_np(au["spent"])[0]) == K * C + k_rest
+    assert np.array_equal(got[full], want[full])
+    ntied = _check_capped_top(got.reshape(-1), rest, util, slots, T, k_rest)
+    print(f"  {K} units whole, {int(got.sum())} ops taken, {ntied} tied at the threshold", flush=True)
+
+
+def test_fullsize_stepwise_prunes(run):
+    """Step-wise eviction at full size: feature invariants, the MLP against
+    the oracle on the kernel's own features (sampled tokens), the kept set
+    exactly the top-B of the scores, kept rows bit copies, lengths on the
+    budget schedule over a few steps."""
+    from oracle import stepwise as osw
+    from workload import make_policy
+    kvc = _kvc()
+    cfg, inp = run["cfg"], run["inp"]
+    L = cfg.lens[0]
+    pol_h = make_policy(seed=11)
+    pol = {k: v.cuda() for k, v in pol_h.items()}
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    sw = kvc.Stepwise(pb, pol, 4, inp["K"].dtype, cfg.G)
+    feats = torch.zeros((5, L), dtype=torch.float32, device="cuda")
+    scores = torch.zeros((L,), dtype=torch.float32, device="cuda")
+    sw.init(inp["K"], inp["V"], inp["Qctx"], feats, scores)
+    torch.cuda.synchronize()
+    f, sc = as_np(feats), as_np(scores)
+    assert abs(f[0].sum() - 1.0) < 1e-3 and f[2].min() >= 0.0
+    assert f[3].min() >= 0.0 and f[3].max() <= math.log(L) + 1e-3
+    assert np.allclose(f[4], np.arange(L) / (L - 1), atol=1e-6)
+    pick = np.random.default_rng(0).choice(L, 2000, replace=False)
+    close(sc[pick], osw.policy_scores(f[:, pick].T.astype(np.float64), pol_h), 1e-4, "policy", floor=1e-4)
+    B = osw.step_budget(L, cfg)
+    kept = np.sort(osw.keep_top(sc, np.arange(L), B))
+    pos = as_np(sw.pos[:B]).astype(np.int64)
+    assert sw.lengths[0] == B and np.array_equal(pos, kept)
+    for (l, h) in UNITS:
+        assert torch.equal(sw.K[l, h, :B].cpu(), inp["K"][l, h, kept].cpu())
+        assert torch.equal(sw.V[l, h, :B].cpu(), inp["V"][l, h, kept].cpu())
+    cap = sw.cap_total
+    feats2 = torch.zeros((5, cap), dtype=torch.float32, device="cuda")
+    scores2 = torch.zeros((cap,), dtype=torch.float32, device="cuda")
+    for t in range(4):
+        sw.append(inp["Kd"], inp["Vd"], inp["Qd"][t], t)
+        n = sw.lengths[0]
+        before = as_np(sw.pos[:n]).astype(np.int64)
+        sw.prune(t, feats2, scores2)
+        torch.cuda.synchronize()
+        B = osw.step_budget(L + t + 1, cfg)
+        assert sw.lengths[0] == min(B, n)
+        keep = osw.keep_top(as_np(scores2[:n]), before, B)
+        assert np.array_equal(np.sort(before[keep]), np.sort(as_np(sw.pos[:sw.lengths[0]]).astype(np.int64)))
+    print(f"  first prune kept {len(kept)}, final length {sw.lengths[0]}", flush=True)
