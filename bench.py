@@ -354,7 +354,7 @@ def main():
         "kl_ms": round(float(np.mean(kl_ms)), 3),
         "mean_kl": round(float(klh.mean()), 5),
         "max_kl": round(float(klh.max()), 5),
-        "roofline": {"bound": "hbm", "kernel": "decode call (decode_partial + decode_merge + decode_layersum)",
+        "roofline": {"bound": "hbm", "kernel": "decode call (decode_mfma pieces + decode_merge)",
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_call_comp": int(bytes_comp), "bytes_per_call_full": int(bytes_full)},

@@ -6,13 +6,19 @@
 // DistillCache paper, Sec. 3.1.3: the full and the pruned cache both append
 // each new (k, v).
 //
-// Split-K: each workgroup takes up to CHUNK entries of one (s, l, h) segment
-// (or of its appended tail), computes the G query heads' logits, a local
-// softmax and the weighted value sum, and writes (max, sum, o[d]) per head.
-// The combine kernel merges the chunks of every (s, l, h, g), normalizes and
-// sums the layers in order into x. The step is HBM-bound: every packed K and
-// V byte is read once, 16 bytes per lane, rows of one entry across
-// D/8 consecutive lanes.
+// Split-K over pieces. A plan, made once per cache by a one-workgroup kernel,
+// cuts every (s, l, h) segment into near-equal pieces of at most `chunk`
+// entries and writes one 32-byte record per piece, so a decode step launches
+// the pieces there are and no more (a 25% cache launches a quarter of the
+// full cache's workgroups, each with a full share of work) and a workgroup
+// needs one load before its first K load. The appended tail tokens of every
+// unit form pieces of their own after the segment pieces, computed from the
+// step's tail length. Each piece computes its G query heads' logits, a local
+// softmax and the weighted value sum, and writes (o[G][D], (max, sum)[G]).
+// The merge kernel combines the pieces of every unit into o, and the last
+// unit of an (s, h) to finish sums o over the layers, in layer order, into
+// x. The step is HBM-bound: every packed K and V byte is read once, 16 bytes
+// per lane.
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -20,10 +26,23 @@
 
 namespace {
 
-constexpr int CHUNK = 256;   // entries per workgroup, fp32 caches (VALU kernel)
-constexpr int MCHUNK = 512;  // entries per workgroup, bf16 caches (MFMA kernel)
+constexpr int CHUNK = 256;   // entries per piece, at most: fp32 caches (VALU kernel)
+constexpr int MCHUNK = 768;  // entries per piece, at most: bf16 caches (MFMA kernel)
 constexpr int THREADS = 256;
+constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_PER = 8;  // units per plan thread per round, at most
+// waves of a merge workgroup (LDS holds one G*D row per wave)
+template <int G> constexpr int mrg_waves() { return G <= 4 ? 16 : 8; }
+constexpr int MRG_NPW = 4;    // pieces per wave per merge batch of loads
 constexpr float LOG2E = 1.4426950408889634f;
+
+// What a segment piece's workgroup needs, in one 32-byte load.
+struct __align__(16) PieceRec {
+  int64_t off;  // first row of the piece in the packed cache
+  int32_t u;    // unit (s*Ly + l)*H + h
+  int32_t n;    // entries in the piece (>= 1)
+  int32_t pad0, pad1, pad2, pad3;
+};
 
 struct DecArgs {
   const void* K;
@@ -34,10 +53,147 @@ struct DecArgs {
   const void* Kt;
   const void* Vt;
   const void* Q;
-  int S, Ly, H, G, t_valid, t_cap, nchunk;
-  int chunk;     // entries per partial (CHUNK or MCHUNK)
+  int S, Ly, H, G, D, t_valid, t_cap;
+  int chunk;     // entries per piece, at most (CHUNK or MCHUNK)
+  int maxs;      // segment pieces the plan can hold; tail pieces start here
+  int ntp;       // tail pieces per unit in this step
   float scale2;  // log2(e)/sqrt(d)
+  // the plan
+  int32_t* n_pieces;  // [1] segment pieces in use (<= maxs)
+  PieceRec* piece;    // [maxs]
+  int2* upieces;      // [units] (first segment piece, segment pieces) of each unit
+  int32_t* cnt;       // [S*H] units of the (s, h) merged in this step (back to 0 after it)
+  // results
+  float* part_o;      // [maxs + units*ntp][G][D] value sums of each piece, scaled by 2^-max
+  float2* part_ml;    // [maxs + units*ntp][G] (max of the base-2 logits, sum of 2^(z - max))
+  float* o;           // [units][G][D]
+  float* x;
+  int64_t x_stride;
 };
+
+// Device-scope atomic stores and loads: performed at the device's coherence
+// point rather than in one XCD's L2, so a value stored by one workgroup is
+// seen by another of the same launch without an L2 writeback or invalidate.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every memory operation of this wave has completed (and the compiler keeps
+// memory operations on their side of this point)
+__device__ __forceinline__ void drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The plan: pieces per unit (ceil(len / chunk), the length split evenly, the
+// first len % np pieces one entry longer), an exclusive scan over the units
+// (rounds of PLAN_THREADS * per units), one record per piece, each unit's
+// piece range, the number of pieces, and the merge counters at zero.
+__global__ __launch_bounds__(PLAN_THREADS) void decode_plan_kernel(DecArgs a) {
+  __shared__ int wsum[PLAN_THREADS / 64];
+  const int units = a.S * a.Ly * a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < a.S * a.H; i += PLAN_THREADS) a.cnt[i] = 0;
+  const int per = min(PLAN_PER, (units + PLAN_THREADS - 1) / PLAN_THREADS);
+  int carry = 0;
+  for (int base = 0; base < units; base += PLAN_THREADS * per) {
+    const int u0 = base + tid * per;
+    int sl[PLAN_PER], np[PLAN_PER];
+    int64_t off[PLAN_PER];
+    int local = 0;
+#pragma unroll
+    for (int k = 0; k < PLAN_PER; ++k) {
+      const int u = u0 + k;
+      const bool ok = k < per && u < units;
+      sl[k] = ok ? a.seg_len[u] : 0;
+      off[k] = ok ? a.seg_off[u] : 0;
+      np[k] = (sl[k] + a.chunk - 1) / a.chunk;
+      local += np[k];
+    }
+    int inc = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int run = carry + inc - local, total = 0;
+#pragma unroll
+    for (int w = 0; w < PLAN_THREADS / 64; ++w) {
+      if (w < wave) run += wsum[w];
+      total += wsum[w];
+    }
+#pragma unroll
+    for (int k = 0; k < PLAN_PER; ++k) {
+      const int u = u0 + k;
+      if (k < per && u < units) {
+        a.upieces[u] = make_int2(run, np[k]);
+        if (np[k] > 0) {
+          const int q = sl[k] / np[k], r = sl[k] % np[k];
+          int64_t e = off[k];
+          for (int j = 0; j < np[k] && run + j < a.maxs; ++j) {
+            PieceRec rec;
+            rec.off = e;
+            rec.u = u;
+            rec.n = q + (j < r);
+            rec.pad0 = rec.pad1 = rec.pad2 = rec.pad3 = 0;
+            a.piece[run + j] = rec;
+            e += rec.n;
+          }
+        }
+        run += np[k];
+      }
+    }
+    carry += total;
+    __syncthreads();  // wsum is rewritten by the next round
+  }
+  if (tid == 0) *a.n_pieces = carry < a.maxs ? carry : a.maxs;
+}
+
+// A piece: its rows and ln mu (nullptr for the tail) and its unit.
+template <class T>
+struct Piece {
+  const T* Kb;
+  const T* Vb;
+  const float* lm;
+  int n;  // entries (>= 1)
+  int u;
+};
+
+// Workgroups [0, maxs) take the plan's segment pieces (those past the plan's
+// count return); workgroups from maxs on take tail piece (b - maxs) % ntp of
+// unit (b - maxs) / ntp, the step's t_valid tail tokens split evenly.
+template <class T, int D>
+__device__ __forceinline__ bool load_piece(const DecArgs& a, Piece<T>& pc) {
+  const int b = blockIdx.x;
+  if (b < a.maxs) {
+    const int np = *a.n_pieces;
+    const PieceRec r = a.piece[b];
+    if (b >= np) return false;
+    pc.Kb = (const T*)a.K + r.off * D;
+    pc.Vb = (const T*)a.V + r.off * D;
+    pc.lm = a.lnmu ? a.lnmu + r.off : nullptr;
+    pc.n = r.n;
+    pc.u = r.u;
+    return true;
+  }
+  const int qa = b - a.maxs;
+  const int u = qa / a.ntp, j = qa % a.ntp;
+  const int s = u / (a.Ly * a.H), lh = u % (a.Ly * a.H);
+  const int l = lh / a.H, h = lh % a.H;
+  const int q = a.t_valid / a.ntp, r = a.t_valid % a.ntp;
+  const int64_t e = (((int64_t)l * a.H + h) * a.S + s) * a.t_cap + (int64_t)j * q + min(j, r);
+  pc.Kb = (const T*)a.Kt + e * D;
+  pc.Vb = (const T*)a.Vt + e * D;
+  pc.lm = nullptr;
+  pc.n = q + (j < r);
+  pc.u = u;
+  return true;
+}
 
 template <class T> struct Vec8;
 template <> struct Vec8<uint16_t> {
@@ -63,9 +219,10 @@ template <> struct Vec8<float> {
   static __device__ __forceinline__ void load(const float* p, float* f) { cvt(raw(p), f); }
 };
 
-// partial layout: [unit][chunk][G][D + 2] = o[D], max2, sum
+// fp32 caches: a piece of up to CHUNK entries on the VALU (logits by lane
+// groups of D/8 lanes, one pass of max and exponentials per head in LDS).
 template <class T, int D, int G>
-__global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, float* part) {
+__global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a) {
   constexpr int LPE = D / 8;       // lanes per entry
   constexpr int EPI = 64 / LPE;    // entries per wave iteration
   constexpr int STEP = 4 * EPI;    // entries per workgroup iteration
@@ -73,33 +230,14 @@ __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, floa
   __shared__ float z_s[G][CHUNK];
   __shared__ float m_s[G], l_s[G];
   __shared__ float o_s[4][G][D];
-  const int unit = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
-  const int s = unit / (a.Ly * a.H), lh = unit % (a.Ly * a.H);
+  Piece<T> pc;
+  if (!load_piece<T, D>(a, pc)) return;
+  const T* Kb = pc.Kb;
+  const T* Vb = pc.Vb;
+  const float* lm = pc.lm;
+  const int n = pc.n;
+  const int s = pc.u / (a.Ly * a.H), lh = pc.u % (a.Ly * a.H);
   const int l = lh / a.H, h = lh % a.H;
-  const int seg_idx = (s * a.Ly + l) * a.H + h;
-  const int64_t slen = a.seg_len[seg_idx];
-  // the grid covers max_seg entries per segment; never index past it
-  const int nseg = min((int)((slen + CHUNK - 1) / CHUNK), a.nchunk - (a.t_cap + CHUNK - 1) / CHUNK);
-  const T* Kb;
-  const T* Vb;
-  const float* lm = nullptr;
-  int64_t e0, n;
-  if (chunk < nseg) {
-    int64_t off = a.seg_off[seg_idx];
-    e0 = (int64_t)chunk * CHUNK;
-    n = slen - e0 < CHUNK ? slen - e0 : CHUNK;
-    Kb = (const T*)a.K + (off + e0) * D;
-    Vb = (const T*)a.V + (off + e0) * D;
-    if (a.lnmu) lm = a.lnmu + off + e0;
-  } else {
-    int tc = chunk - nseg;
-    e0 = (int64_t)tc * CHUNK;
-    if (e0 >= a.t_valid) return;
-    n = a.t_valid - e0 < CHUNK ? a.t_valid - e0 : CHUNK;
-    int64_t tb = (((int64_t)l * a.H + h) * a.S + s) * a.t_cap + e0;
-    Kb = (const T*)a.Kt + tb * D;
-    Vb = (const T*)a.Vt + tb * D;
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPE, slot = lane / LPE;
   // query slice of every head of the group for this lane's 8 dims
@@ -189,60 +327,40 @@ __global__ __launch_bounds__(THREADS) void decode_partial_kernel(DecArgs a, floa
     }
   }
   __syncthreads();
-  float* pb = part + ((int64_t)unit * a.nchunk + chunk) * G * (D + 2);
+  const int64_t p = blockIdx.x;
+  float* po = a.part_o + p * G * D;
   for (int i = threadIdx.x; i < G * D; i += THREADS) {
-    int g = i / D, dd = i % D;
-    pb[g * (D + 2) + dd] = o_s[0][g][dd] + o_s[1][g][dd] + o_s[2][g][dd] + o_s[3][g][dd];
+    const int g = i / D, dd = i % D;
+    po[i] = o_s[0][g][dd] + o_s[1][g][dd] + o_s[2][g][dd] + o_s[3][g][dd];
   }
-  if (threadIdx.x < G) {
-    pb[threadIdx.x * (D + 2) + D] = m_s[threadIdx.x];
-    pb[threadIdx.x * (D + 2) + D + 1] = l_s[threadIdx.x];
-  }
+  if (threadIdx.x < G) a.part_ml[p * G + threadIdx.x] = make_float2(m_s[threadIdx.x], l_s[threadIdx.x]);
 }
 
 // bf16 caches: the logits of a 32-entry group come from one MFMA chain
 // (A = the G query heads padded to 32 rows, B = the entries' keys), each wave
 // runs an online softmax over rounds of 64 entries, and the values are
 // accumulated on the VALU with the probabilities broadcast through LDS.
-// Partial layout as the VALU kernel: [unit][chunk][G][D + 2].
 template <int D, int G>
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 ? 2 : 3))) void decode_mfma_kernel(DecArgs a, float* part) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 ? 2 : 3))) void decode_mfma_kernel(DecArgs a) {
   using namespace kvcmf;
   constexpr int KS = D / 16;          // MFMA steps per group (16 dims each)
   constexpr int LPE = D / 8;          // lanes per entry in the value pass
   constexpr int EPI = 64 / LPE;       // entries per value iteration
   constexpr int VIT = 32 / EPI;       // value iterations per 32-entry round
-  constexpr int WE = MCHUNK / 4;      // entries per wave
   constexpr int GP = G < 4 ? G : 4;   // heads held per logit lane
   constexpr int PS = G <= 4 ? 4 : 8;  // row stride of the probability table
   __shared__ __align__(16) uint16_t qs[G][D];
   __shared__ __align__(16) float pw[4][32][PS];
   __shared__ float mw[4][G], lw[4][G];
   __shared__ __align__(16) float ow[4][G][D];
-  const int unit = blockIdx.x / a.nchunk, chunk = blockIdx.x % a.nchunk;
-  const int s = unit / (a.Ly * a.H), lh = unit % (a.Ly * a.H);
+  Piece<uint16_t> pc;
+  if (!load_piece<uint16_t, D>(a, pc)) return;
+  const uint16_t* Kb = pc.Kb;
+  const uint16_t* Vb = pc.Vb;
+  const float* lm = pc.lm;
+  const int n = pc.n;
+  const int s = pc.u / (a.Ly * a.H), lh = pc.u % (a.Ly * a.H);
   const int l = lh / a.H, h = lh % a.H;
-  const int seg_idx = (s * a.Ly + l) * a.H + h;
-  const int64_t slen = a.seg_len[seg_idx];
-  const int nseg = min((int)((slen + MCHUNK - 1) / MCHUNK), a.nchunk - (a.t_cap + MCHUNK - 1) / MCHUNK);
-  const uint16_t* Kb;
-  const uint16_t* Vb;
-  const float* lm = nullptr;
-  int64_t n;
-  if (chunk < nseg) {
-    const int64_t off = a.seg_off[seg_idx], e0 = (int64_t)chunk * MCHUNK;
-    n = slen - e0 < MCHUNK ? slen - e0 : MCHUNK;
-    Kb = (const uint16_t*)a.K + (off + e0) * D;
-    Vb = (const uint16_t*)a.V + (off + e0) * D;
-    if (a.lnmu) lm = a.lnmu + off + e0;
-  } else {
-    const int64_t e0 = (int64_t)(chunk - nseg) * MCHUNK;
-    if (e0 >= a.t_valid) return;
-    n = a.t_valid - e0 < MCHUNK ? a.t_valid - e0 : MCHUNK;
-    const int64_t tb = (((int64_t)l * a.H + h) * a.S + s) * a.t_cap + e0;
-    Kb = (const uint16_t*)a.Kt + tb * D;
-    Vb = (const uint16_t*)a.Vt + tb * D;
-  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int es = lane / LPE, sub = lane % LPE;
@@ -261,6 +379,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[g][j] = 0.f;
   __syncthreads();
+  // each wave takes a run of whole 32-entry rounds
+  const int WE = (((n + 3) >> 2) + 31) & ~31;
   const int wbase = wave * WE;
   // Rounds of 32 entries; many waves per SIMD hide the load latency. Loads
   // past the chunk read its last entry (always valid) and are masked
@@ -374,7 +494,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
       if (es == 0) ow[wave][g][sub * 8 + j] = x;
     }
   __syncthreads();
-  float* pb = part + ((int64_t)unit * a.nchunk + chunk) * G * (D + 2);
+  const int64_t p = blockIdx.x;
+  float* po = a.part_o + p * G * D;
   for (int i = threadIdx.x; i < G * D; i += THREADS) {
     const int g = i / D, dd = i % D;
     float mx = mw[0][g];
@@ -384,7 +505,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       if (mw[w][g] != -INFINITY) o += ow[w][g][dd] * exp2f(mw[w][g] - mx);
-    pb[g * (D + 2) + dd] = o;
+    po[i] = o;
   }
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
@@ -395,134 +516,245 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       if (mw[w][g] != -INFINITY) t += lw[w][g] * exp2f(mw[w][g] - mx);
-    pb[g * (D + 2) + D] = mx;
-    pb[g * (D + 2) + D + 1] = t;
+    a.part_ml[p * G + g] = make_float2(mx, t);
   }
 }
 
-// Merge the chunks of every (s, l, h, g): one workgroup of D threads per
-// (unit, head). The chunk statistics go to LDS first, the chunk weights
-// exp2(m_c - max) and 1 / sum follow from two block reductions, then every
-// thread sums its dimension over the chunks with all loads independent.
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecArgs a, const float* part, float* o) {
-  extern __shared__ float ms[];            // [2][nchunk]: chunk max, then weight; chunk sum
-  __shared__ float red[D / 64];
-  const int G = a.G;
-  const int unit = blockIdx.x / G, g = blockIdx.x % G;  // unit = (s*Ly + l)*H + h
-  const int tid = threadIdx.x;
-  float* mc = ms;
-  float* lc = ms + a.nchunk;
-  const int64_t slen = a.seg_len[unit];
-  const int ck = a.chunk;
-  const int nseg = min((int)((slen + ck - 1) / ck), a.nchunk - (a.t_cap + ck - 1) / ck);
-  const int nc = nseg + (a.t_valid + ck - 1) / ck;
-  const int64_t cs = (int64_t)G * (D + 2);  // chunk stride
-  const float* pb = part + ((int64_t)unit * a.nchunk * G + g) * (D + 2);
-  float mx = -INFINITY;
-  for (int c = tid; c < nc; c += D) {
-    const float m = pb[c * cs + D];
-    mc[c] = m;
-    lc[c] = pb[c * cs + D + 1];
-    mx = fmaxf(mx, m);
-  }
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = red[0];
+// One workgroup of mrg_waves<G>() waves per unit: the unit's pieces (its segment
+// pieces, then its tail pieces) are dealt to the waves, each wave loads its
+// MRG_NPW pieces of a batch together and merges them online (lane = OPL
+// consecutive outputs of one head), the waves are combined through LDS and o
+// is normalized. The unit then counts itself in for its (s, h); the last unit
+// of the (s, h) writes x as the layer sum, in layer order, and sets the
+// counter back to zero. The merged o crosses workgroups through device-scope
+// atomic stores and loads, and a workgroup waits until its stores have
+// completed before it counts itself in.
+template <int D, int G>
+__global__ __launch_bounds__(mrg_waves<G>() * 64) void decode_merge_kernel(DecArgs a) {
+  constexpr int GD = G * D;
+  constexpr int OPL = GD / 64;  // merged outputs per lane, all of one head
+  constexpr int MRG_WAVES = mrg_waves<G>();
+  constexpr int NT = MRG_WAVES * 64;
+  __shared__ float accs[MRG_WAVES][GD];
+  __shared__ float msw[MRG_WAVES][G], lsw[MRG_WAVES][G];
+  __shared__ int last;
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int2 up = a.upieces[u];
+  const int p0 = up.x, nps = max(0, min(up.y, a.maxs - up.x));
+  const int npt = nps + a.ntp;
+  const int64_t t0 = (int64_t)a.maxs + (int64_t)u * a.ntp - nps;  // piece id of list index j >= nps
+  const int g = lane * OPL / D;
+  float M = -INFINITY, L = 0.f, acc[OPL];
 #pragma unroll
-  for (int w = 1; w < D / 64; ++w) mx = fmaxf(mx, red[w]);
-  __syncthreads();
-  float sm = 0.f;
-  for (int c = tid; c < nc; c += D) {
-    const float w = mc[c] == -INFINITY ? 0.f : exp2f(mc[c] - mx);
-    mc[c] = w;
-    sm += lc[c] * w;
-  }
-  sm = wave_sum(sm);
-  if ((tid & 63) == 0) red[tid >> 6] = sm;
-  __syncthreads();
-  float tot = 0.f;
+  for (int q = 0; q < OPL; ++q) acc[q] = 0.f;
+  for (int j0 = 0; j0 < npt; j0 += MRG_WAVES * MRG_NPW) {
+    float2 ml[MRG_NPW];
+    float v[MRG_NPW][OPL];
 #pragma unroll
-  for (int w = 0; w < D / 64; ++w) tot += red[w];
-  float acc = 0.f;
-#pragma unroll 8
-  for (int c = 0; c < nc; ++c) acc += pb[c * cs + tid] * mc[c];
-  o[((int64_t)unit * G + g) * D + tid] = tot > 0.f ? acc / tot : 0.f;
+    for (int k = 0; k < MRG_NPW; ++k) {
+      const int j = min(j0 + wave + MRG_WAVES * k, npt - 1);
+      const int64_t p = j < nps ? (int64_t)p0 + j : t0 + j;
+      ml[k] = a.part_ml[p * G + g];
+      const float* po = a.part_o + p * GD + lane * OPL;
+      if constexpr (OPL >= 4) {
+#pragma unroll
+        for (int q = 0; q < OPL; q += 4) {
+          const float4 t = *(const float4*)(po + q);
+          v[k][q] = t.x; v[k][q + 1] = t.y; v[k][q + 2] = t.z; v[k][q + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < OPL; ++q) v[k][q] = po[q];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MRG_NPW; ++k) {
+      if (j0 + wave + MRG_WAVES * k >= npt || ml[k].x == -INFINITY) continue;
+      const float nm = fmaxf(M, ml[k].x);
+      const float f0 = M == -INFINITY ? 0.f : exp2f(M - nm), f1 = exp2f(ml[k].x - nm);
+      L = L * f0 + ml[k].y * f1;
+#pragma unroll
+      for (int q = 0; q < OPL; ++q) acc[q] = acc[q] * f0 + v[k][q] * f1;
+      M = nm;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < OPL; ++q) accs[wave][lane * OPL + q] = acc[q];
+  if ((lane * OPL) % D == 0) {
+    msw[wave][g] = M;
+    lsw[wave][g] = L;
+  }
+  __syncthreads();
+  for (int i = tid; i < GD; i += NT) {
+    const int gg = i / D;
+    float mx = msw[0][gg];
+#pragma unroll
+    for (int w = 1; w < MRG_WAVES; ++w) mx = fmaxf(mx, msw[w][gg]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < MRG_WAVES; ++w)
+      if (msw[w][gg] != -INFINITY) {
+        const float f = exp2f(msw[w][gg] - mx);
+        num += accs[w][i] * f;
+        den += lsw[w][gg] * f;
+      }
+    st_dev(a.o + (int64_t)u * GD + i, den > 0.f ? num / den : 0.f);
+  }
+  drain();
+  __syncthreads();
+  const int s = u / (a.Ly * a.H), h = u % a.H;
+  if (tid == 0) last = atomicAdd(&a.cnt[s * a.H + h], 1) == a.Ly - 1;
+  __syncthreads();
+  if (!last) return;
+  if (tid == 0) __hip_atomic_store(&a.cnt[s * a.H + h], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t lstride = (int64_t)a.H * GD;
+  for (int i = tid; i < GD; i += NT) {
+    const float* os = a.o + ((int64_t)s * a.Ly * a.H + h) * GD + i;
+    float xs = 0.f;
+#pragma unroll 32
+    for (int l = 0; l < a.Ly; ++l) xs += ld_dev(os + l * lstride);
+    a.x[(int64_t)s * a.x_stride + (int64_t)h * GD + i] = xs;
+  }
 }
 
-// x[s][j] = sum over layers (in order) of o[s][l][j], j < H*G*D
-__global__ void decode_layersum_kernel(DecArgs a, int D, const float* o, float* x_out, int64_t x_stride) {
-  const int64_t HGD = (int64_t)a.H * a.G * D;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.S * HGD) return;
-  int s = (int)(i / HGD);
-  int64_t j = i % HGD;
-  const float* os = o + (int64_t)s * a.Ly * HGD + j;
-  float x = 0.f;
-#pragma unroll 8
-  for (int l = 0; l < a.Ly; ++l) x += os[(int64_t)l * HGD];
-  x_out[(int64_t)s * x_stride + j] = x;
+int64_t units_of(const kvc_ragged* c) { return (int64_t)c->n_seq * c->n_layers * c->n_kv_heads; }
+int chunk_of(const kvc_ragged* c) { return c->dtype == KVC_BF16 ? MCHUNK : CHUNK; }
+// Segment pieces, at most: ceil(len / chunk) < len / chunk + 1 per unit, and
+// the segments hold at most `capacity` entries.
+int64_t max_seg_pieces(const kvc_ragged* c) { return c->capacity / chunk_of(c) + units_of(c); }
+int tail_pieces(const kvc_ragged* c, int32_t t) { return (t + chunk_of(c) - 1) / chunk_of(c); }
+
+struct DecWs {
+  int32_t* n_pieces;
+  PieceRec* piece;
+  int2* upieces;
+  int32_t* cnt;
+  float* part_o;
+  float2* part_ml;
+  float* obuf;
+};
+
+// The plan comes first, so that a workspace sized for a larger t_cap keeps
+// the plan where a smaller one puts it.
+DecWs carve_dec(kvc::Carver& cv, const kvc_ragged* c, int32_t group, int32_t t_cap) {
+  const int64_t units = units_of(c), maxs = max_seg_pieces(c);
+  const int64_t np = maxs + units * tail_pieces(c, t_cap);
+  const int64_t gd = (int64_t)group * c->head_dim;
+  DecWs w;
+  w.n_pieces = cv.take<int32_t>(1);
+  w.piece = cv.take<PieceRec>((size_t)(maxs > 0 ? maxs : 1));
+  w.upieces = cv.take<int2>((size_t)units);
+  w.cnt = cv.take<int32_t>((size_t)c->n_seq * c->n_kv_heads);
+  w.part_o = cv.take<float>((size_t)(np * gd));
+  w.part_ml = cv.take<float2>((size_t)(np * group));
+  w.obuf = cv.take<float>((size_t)(units * gd));
+  return w;
 }
 
-int nchunk_of(const kvc_ragged* c, int t_cap, int chunk) {
-  return (c->max_seg + chunk - 1) / chunk + (t_cap + chunk - 1) / chunk;
-}
-
-}  // namespace
-
-extern "C" size_t kvc_decode_workspace(const kvc_ragged* c, int32_t group, int32_t t_cap) {
-  if (!c || group < 1 || t_cap < 0 || c->max_seg < 0) return 0;
-  int64_t units = (int64_t)c->n_seq * c->n_layers * c->n_kv_heads;
-  kvc::Carver cv(nullptr, 0);
-  cv.take<float>((size_t)units * nchunk_of(c, t_cap, CHUNK) * group * (c->head_dim + 2));  // bound for both kernels
-  cv.take<float>((size_t)units * group * c->head_dim);
-  return cv.off + 256;
-}
-
-extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const void* V_tail, int32_t t_valid,
-                               int32_t t_cap, const void* Q, int32_t group, float* x_out, int64_t x_stride,
-                               float* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
+int check_cache(const kvc_ragged* c, int32_t group, int32_t t_cap, void* ws, size_t ws_bytes) {
   KVC_REQUIRE(c != nullptr, KVC_E_INVAL, "cache is NULL");
-  KVC_REQUIRE(c->seg_off && c->seg_len && Q && x_out, KVC_E_INVAL, "kvc_decode_attn: NULL pointer");
+  KVC_REQUIRE(c->seg_off && c->seg_len, KVC_E_INVAL, "kvc_decode: NULL segment arrays");
   KVC_REQUIRE(c->capacity >= 0 && (c->capacity == 0 || (c->K && c->V)), KVC_E_INVAL,
-              "kvc_decode_attn: NULL cache K/V with a nonzero capacity");
+              "kvc_decode: NULL cache K/V with a nonzero capacity");
   KVC_REQUIRE(c->head_dim == 64 || c->head_dim == 128, KVC_E_SHAPE, "head_dim must be 64 or 128");
   KVC_REQUIRE(c->dtype == KVC_BF16 || c->dtype == KVC_F32, KVC_E_DTYPE, "cache dtype must be bf16 or f32");
   KVC_REQUIRE(group >= 1 && group <= 8, KVC_E_SHAPE, "group must be in [1, 8]");
+  KVC_REQUIRE(group == 1 || group == 2 || group == 4 || group == 8, KVC_E_UNSUPPORTED,
+              "kvc_decode: group must be 1, 2, 4 or 8");
   KVC_REQUIRE(c->n_seq >= 1 && c->n_layers >= 1 && c->n_kv_heads >= 1, KVC_E_SHAPE, "empty cache shape");
-  KVC_REQUIRE(t_valid >= 0 && t_valid <= t_cap, KVC_E_INVAL, "need 0 <= t_valid <= t_cap");
-  KVC_REQUIRE(t_valid == 0 || (K_tail && V_tail), KVC_E_INVAL, "tail pointers are NULL");
-  KVC_REQUIRE(x_stride >= (int64_t)c->n_kv_heads * group * c->head_dim, KVC_E_INVAL, "x_stride too small");
   KVC_REQUIRE(c->max_seg >= 0, KVC_E_INVAL, "max_seg must be >= 0");
+  KVC_REQUIRE(t_cap >= 0, KVC_E_INVAL, "t_cap must be >= 0");
+  KVC_REQUIRE(units_of(c) <= INT32_MAX / 2 && max_seg_pieces(c) + units_of(c) * tail_pieces(c, t_cap) <= INT32_MAX,
+              KVC_E_SHAPE, "kvc_decode: cache too large");
   KVC_REQUIRE(ws && ws_bytes >= kvc_decode_workspace(c, group, t_cap), KVC_E_WORKSPACE,
-              "kvc_decode_attn: workspace too small");
+              "kvc_decode: workspace too small");
+  return KVC_OK;
+}
+
+DecArgs make_args(const kvc_ragged* c, int32_t group, int32_t t_valid, int32_t t_cap, const DecWs& w) {
   DecArgs a{};
   a.K = c->K;
   a.V = c->V;
   a.lnmu = c->lnmu;
   a.seg_off = c->seg_off;
   a.seg_len = c->seg_len;
-  a.Kt = K_tail;
-  a.Vt = V_tail;
-  a.Q = Q;
   a.S = c->n_seq;
   a.Ly = c->n_layers;
   a.H = c->n_kv_heads;
   a.G = group;
+  a.D = c->head_dim;
   a.t_valid = t_valid;
   a.t_cap = t_cap;
-  a.chunk = c->dtype == KVC_BF16 ? MCHUNK : CHUNK;
-  a.nchunk = nchunk_of(c, t_cap, a.chunk);
+  a.chunk = chunk_of(c);
+  a.maxs = (int)max_seg_pieces(c);
+  a.ntp = tail_pieces(c, t_valid);
   a.scale2 = 1.4426950408889634f / sqrtf((float)c->head_dim);
-  int64_t units = (int64_t)a.S * a.Ly * a.H;
+  a.n_pieces = w.n_pieces;
+  a.piece = w.piece;
+  a.upieces = w.upieces;
+  a.cnt = w.cnt;
+  a.part_o = w.part_o;
+  a.part_ml = w.part_ml;
+  return a;
+}
+
+}  // namespace
+
+extern "C" size_t kvc_decode_workspace(const kvc_ragged* c, int32_t group, int32_t t_cap) {
+  if (!c || group < 1 || t_cap < 0 || c->capacity < 0 || c->head_dim < 1 || c->n_seq < 1 || c->n_layers < 1 ||
+      c->n_kv_heads < 1)
+    return 0;
+  kvc::Carver cv(nullptr, 0);
+  carve_dec(cv, c, group, t_cap);
+  return cv.off + 256;
+}
+
+extern "C" int kvc_decode_plan(const kvc_ragged* c, int32_t group, int32_t t_cap, void* ws, size_t ws_bytes,
+                               hipStream_t st) {
+  const int rc = check_cache(c, group, t_cap, ws, ws_bytes);
+  if (rc != KVC_OK) return rc;
   kvc::Carver cv(ws, ws_bytes);
-  float* part = cv.take<float>((size_t)units * a.nchunk * group * (c->head_dim + 2));
-  float* obuf = o_out ? o_out : cv.take<float>((size_t)units * group * c->head_dim);
-  dim3 grid((unsigned)(units * a.nchunk));
-  int d = c->head_dim;
-#define KVC_DEC(TT, DD, GG) hipLaunchKernelGGL((decode_partial_kernel<TT, DD, GG>), grid, dim3(THREADS), 0, st, a, part)
-#define KVC_DECM(DD, GG) hipLaunchKernelGGL((decode_mfma_kernel<DD, GG>), grid, dim3(THREADS), 0, st, a, part)
+  const DecWs w = carve_dec(cv, c, group, t_cap);
+  const DecArgs a = make_args(c, group, 0, t_cap, w);
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, st, a);
+  KVC_LAUNCH_CHECK("decode_plan");
+  return KVC_OK;
+}
+
+namespace {
+int check_step(const kvc_ragged* c, const void* K_tail, const void* V_tail, int32_t t_valid, int32_t t_cap,
+               const void* Q, int32_t group, float* x_out, int64_t x_stride, void* ws, size_t ws_bytes) {
+  const int rc = check_cache(c, group, t_cap, ws, ws_bytes);
+  if (rc != KVC_OK) return rc;
+  KVC_REQUIRE(Q && x_out, KVC_E_INVAL, "kvc_decode_attn: NULL pointer");
+  KVC_REQUIRE(t_valid >= 0 && t_valid <= t_cap, KVC_E_INVAL, "need 0 <= t_valid <= t_cap");
+  KVC_REQUIRE(t_valid == 0 || (K_tail && V_tail), KVC_E_INVAL, "tail pointers are NULL");
+  KVC_REQUIRE(x_stride >= (int64_t)c->n_kv_heads * group * c->head_dim, KVC_E_INVAL, "x_stride too small");
+  return KVC_OK;
+}
+}  // namespace
+
+extern "C" int kvc_decode_attn_planned(const kvc_ragged* c, const void* K_tail, const void* V_tail,
+                                       int32_t t_valid, int32_t t_cap, const void* Q, int32_t group, float* x_out,
+                                       int64_t x_stride, float* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  const int rc = check_step(c, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, ws, ws_bytes);
+  if (rc != KVC_OK) return rc;
+  kvc::Carver cv(ws, ws_bytes);
+  const DecWs w = carve_dec(cv, c, group, t_cap);
+  DecArgs a = make_args(c, group, t_valid, t_cap, w);
+  a.Kt = K_tail;
+  a.Vt = V_tail;
+  a.Q = Q;
+  a.o = o_out ? o_out : w.obuf;
+  a.x = x_out;
+  a.x_stride = x_stride;
+  const dim3 grid((unsigned)(a.maxs + units_of(c) * a.ntp));  // maxs >= units >= 1
+  const int d = c->head_dim;
+#define KVC_DEC(TT, DD, GG) hipLaunchKernelGGL((decode_partial_kernel<TT, DD, GG>), grid, dim3(THREADS), 0, st, a)
+#define KVC_DECM(DD, GG) hipLaunchKernelGGL((decode_mfma_kernel<DD, GG>), grid, dim3(THREADS), 0, st, a)
+#define KVC_MRG(DD, GG) \
+  hipLaunchKernelGGL((decode_merge_kernel<DD, GG>), mgrid, dim3(mrg_waves<GG>() * 64), 0, st, a)
 #define KVC_DEC_G(MAC, ...)                    \
   switch (group) {                             \
     case 1: MAC(__VA_ARGS__, 1); break;        \
@@ -530,25 +762,30 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
     case 4: MAC(__VA_ARGS__, 4); break;        \
     default: MAC(__VA_ARGS__, 8); break;       \
   }
-  KVC_REQUIRE(group == 1 || group == 2 || group == 4 || group == 8, KVC_E_UNSUPPORTED,
-              "kvc_decode_attn: group must be 1, 2, 4 or 8");
   if (c->dtype == KVC_BF16) {
     if (d == 128) { KVC_DEC_G(KVC_DECM, 128); } else { KVC_DEC_G(KVC_DECM, 64); }
   } else {
     if (d == 128) { KVC_DEC_G(KVC_DEC, float, 128); } else { KVC_DEC_G(KVC_DEC, float, 64); }
   }
+  KVC_LAUNCH_CHECK("decode_pieces");
+  const dim3 mgrid((unsigned)units_of(c));
+  if (d == 128) { KVC_DEC_G(KVC_MRG, 128); } else { KVC_DEC_G(KVC_MRG, 64); }
+  KVC_LAUNCH_CHECK("decode_merge");
 #undef KVC_DEC_G
+#undef KVC_MRG
 #undef KVC_DECM
 #undef KVC_DEC
-  KVC_LAUNCH_CHECK("decode_partial");
-  const size_t msm = (size_t)2 * a.nchunk * sizeof(float);
-  if (d == 128)
-    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3((unsigned)(units * group)), dim3(128), msm, st, a, part, obuf);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3((unsigned)(units * group)), dim3(64), msm, st, a, part, obuf);
-  KVC_LAUNCH_CHECK("decode_merge");
-  int64_t nx = (int64_t)a.S * a.H * group * d;
-  hipLaunchKernelGGL(decode_layersum_kernel, dim3(kvc_blocks(nx, 256)), dim3(256), 0, st, a, d, obuf, x_out, x_stride);
-  KVC_LAUNCH_CHECK("decode_layersum");
   return KVC_OK;
+}
+
+extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const void* V_tail, int32_t t_valid,
+                               int32_t t_cap, const void* Q, int32_t group, float* x_out, int64_t x_stride,
+                               float* o_out, void* ws, size_t ws_bytes, hipStream_t st) {
+  // every argument is checked before the first launch
+  int rc = check_step(c, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, ws, ws_bytes);
+  if (rc != KVC_OK) return rc;
+  rc = kvc_decode_plan(c, group, t_cap, ws, ws_bytes, st);
+  if (rc != KVC_OK) return rc;
+  return kvc_decode_attn_planned(c, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, o_out, ws, ws_bytes,
+                                 st);
 }

@@ -32,7 +32,8 @@ STAGE_SCORE, STAGE_PROPAGATE, STAGE_PARTITION, STAGE_TREES, STAGE_AUCTION, STAGE
 EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets", "kvc_pack_capacity",
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
            "kvc_partition", "kvc_partition_ex", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
-           "kvc_decode_workspace", "kvc_decode_attn", "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
+           "kvc_decode_workspace", "kvc_decode_plan", "kvc_decode_attn", "kvc_decode_attn_planned",
+           "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
            "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune",
            "kvc_propagate_dense_workspace", "kvc_propagate_dense", "kvc_propagate_ar_workspace",
            "kvc_propagate_ar"]
@@ -111,6 +112,9 @@ _sig = {
     "kvc_decode_workspace": (C.c_size_t, [C.POINTER(Ragged), C.c_int32, C.c_int32]),
     "kvc_decode_attn": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
                                   C.c_int64, _P, _P, C.c_size_t, _P]),
+    "kvc_decode_attn_planned": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
+                                  C.c_int64, _P, _P, C.c_size_t, _P]),
+    "kvc_decode_plan": (C.c_int, [C.POINTER(Ragged), C.c_int32, C.c_int32, _P, C.c_size_t, _P]),
     "kvc_step_capacity": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.c_int32, _P]),
     "kvc_step_workspace": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params), C.c_int64]),
     "kvc_step_init": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Policy),
@@ -403,8 +407,10 @@ def full_view(pb: Problem, K, V):
 
 
 class Decoder:
-    """Holds the marshalled cache description and a reusable workspace for
-    repeated decode steps over one cache."""
+    """Holds the marshalled cache description, a reusable workspace and the
+    cache's decode plan (kvc_decode_plan, made here on the current stream)
+    for repeated decode steps over one cache. Call plan() again after the
+    cache's segments change."""
 
     def __init__(self, cache, group: int, t_cap: int):
         self.cache = cache
@@ -413,16 +419,28 @@ class Decoder:
         self.t_cap = t_cap
         n = int(_lib.kvc_decode_workspace(C.byref(self.rs), group, t_cap))
         self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=cache["K"].device)
+        self.plan()
+
+    def plan(self):
+        st = _lib.kvc_decode_plan(C.byref(self.rs), self.group, self.t_cap, _ptr(self.ws), self.ws.numel(),
+                                  _stream())
+        _check("kvc_decode_plan", st)
 
     def step(self, K_tail, V_tail, t_valid, Q, x_out, x_stride, o_out=None):
-        st = _lib.kvc_decode_attn(C.byref(self.rs), _ptr(K_tail), _ptr(V_tail), t_valid, self.t_cap, _ptr(Q),
-                                  self.group, _ptr(x_out), x_stride, _ptr(o_out), _ptr(self.ws), self.ws.numel(),
-                                  _stream())
-        _check("kvc_decode_attn", st)
+        st = _lib.kvc_decode_attn_planned(C.byref(self.rs), _ptr(K_tail), _ptr(V_tail), t_valid, self.t_cap, _ptr(Q),
+                                          self.group, _ptr(x_out), x_stride, _ptr(o_out), _ptr(self.ws),
+                                          self.ws.numel(), _stream())
+        _check("kvc_decode_attn_planned", st)
 
 
 def decode_attn(cache, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, o_out=None):
-    Decoder(cache, group, t_cap).step(K_tail, V_tail, t_valid, Q, x_out, x_stride, o_out)
+    """One step through the single-call entry point (plan and step together)."""
+    rs = _ragged_struct(cache)
+    n = int(_lib.kvc_decode_workspace(C.byref(rs), group, t_cap))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=cache["K"].device)
+    st = _lib.kvc_decode_attn(C.byref(rs), _ptr(K_tail), _ptr(V_tail), t_valid, t_cap, _ptr(Q), group, _ptr(x_out),
+                              x_stride, _ptr(o_out), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_decode_attn", st)
 
 
 class KL:
@@ -513,4 +531,6 @@ class Stepwise:
         """Attention of Q_t over the occupied slots (the appended token included)."""
         if self.decoder is None:
             self.decoder = Decoder(self.view(), self.group, self.t_steps)
+        else:
+            self.decoder.plan()  # the student's segments change every step
         self.decoder.step(K_tail, V_tail, 0, Q_t, x_out, x_stride)

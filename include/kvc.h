@@ -109,7 +109,7 @@ typedef struct kvc_ragged {
   int64_t* seg_off;        /* [S][Ly][H] first entry of each (s, l, h) segment */
   int32_t* seg_len;        /* [S][Ly][H] entries in each segment */
   int32_t n_seq, n_layers, n_kv_heads, head_dim, dtype;
-  int32_t max_seg;         /* host upper bound on any seg_len (sizes the decode grid) */
+  int32_t max_seg;         /* host upper bound on any seg_len (>= 0; informational) */
   int64_t capacity;        /* entries the K/V/lnmu/pos buffers hold */
 } kvc_ragged;
 
@@ -316,13 +316,31 @@ int kvc_full_view(const kvc_shape* shape, int64_t* seg_off, int32_t* seg_len, hi
  * entries and the tail tokens 0..t_valid-1 (K_tail/V_tail [Ly][H][S][t_cap][d],
  * ln mu 0); o = softmax(z) V. Q is [S][Ly][H*G][d].
  * x_out[s*x_stride + (h*G+g)*d + j] = sum over l (in order) of o.
- * o_out (nullable) [S][Ly][H*G][d]. Split-K over the segment; the workspace
- * holds the partials (query kvc_decode_workspace). */
+ * o_out (nullable) [S][Ly][H*G][d]. Split-K: every segment is cut into
+ * near-equal pieces of at most 768 (bf16) or 256 (fp32) entries and the tail
+ * tokens into pieces of their own; the workspace (device memory, owned by the
+ * caller, size from kvc_decode_workspace for the largest t_cap to be used)
+ * holds the plan of the pieces, their partials and the merge counters.
+ * Requires sum of seg_len <= capacity and seg_off + seg_len <= capacity.
+ * All calls are asynchronous on `stream`; errors are argument checks only
+ * (KVC_E_INVAL, KVC_E_SHAPE, KVC_E_DTYPE, KVC_E_UNSUPPORTED, KVC_E_WORKSPACE).
+ * kvc_decode_attn plans and runs one step. kvc_decode_plan writes the plan
+ * of the cache's segments into ws (it depends on seg_len, seg_off and
+ * capacity only); kvc_decode_attn_planned runs a step from the plan in ws,
+ * which must have been made for the same segments with the same group and
+ * t_cap (steps over one cache then skip the plan's launch). Two calls that
+ * share a workspace must not overlap. */
 size_t kvc_decode_workspace(const kvc_ragged* cache, int32_t group, int32_t t_cap);
 int kvc_decode_attn(const kvc_ragged* cache, const void* K_tail, const void* V_tail,
                     int32_t t_valid, int32_t t_cap, const void* Q, int32_t group, float* x_out,
                     int64_t x_stride, float* o_out, void* ws, size_t ws_bytes,
                     hipStream_t stream);
+int kvc_decode_plan(const kvc_ragged* cache, int32_t group, int32_t t_cap, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+int kvc_decode_attn_planned(const kvc_ragged* cache, const void* K_tail, const void* V_tail,
+                            int32_t t_valid, int32_t t_cap, const void* Q, int32_t group,
+                            float* x_out, int64_t x_stride, float* o_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------ A9
  * kvc_kl: per-row KL(full || compressed) through a vocab projection.

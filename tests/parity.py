@@ -73,3 +73,24 @@ def jaccard(a, b):
     b = np.asarray(b).astype(bool)
     u = np.logical_or(a, b).sum()
     return 1.0 if u == 0 else np.logical_and(a, b).sum() / u
+
+
+def check_kl(klv, xf, xc, W, kl_oracle, name="", e2e_atol=2e-2):
+    """Per-step KL: the GPU's KL against the oracle's KL of the GPU's own
+    decode outputs within 1e-3 absolute (the KL stage on the same inputs), and
+    against the oracle's end-to-end KL within e2e_atol. The end-to-end gap is
+    wider than the stage's because x-hat is rounded to W's dtype: a relative
+    change of 1e-5 in x (fp32 decode against fp64) flips a few bf16 roundings,
+    and each flip moves a KL near 15 by about 2e-3."""
+    from oracle import kl as okl
+    n = int(np.prod(as_np(klv).shape))
+    wd = "bf16" if W.dtype == torch.bfloat16 else "f32"
+    Wc = W.detach().cpu()
+    got = as_np(klv).reshape(n)
+    stage = okl.kl_rows(as_np(xf).reshape(n, -1).astype(np.float32), as_np(xc).reshape(n, -1).astype(np.float32),
+                        Wc, wd)
+    e_stage = np.abs(got - stage).max()
+    e_e2e = np.abs(got - np.asarray(kl_oracle).reshape(n)).max()
+    print(f"  {name} max|dKL| stage={e_stage:.2e} end-to-end={e_e2e:.2e}", flush=True)
+    assert e_stage <= 1e-3, (name, e_stage)
+    assert e_e2e <= e2e_atol, (name, e_e2e)

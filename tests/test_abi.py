@@ -102,6 +102,17 @@ def test_invalid_arguments_are_rejected_on_the_host(kvc):
                     head_dim=128, dtype=1, max_seg=10, capacity=10)
     st = lib.kvc_decode_attn(C.byref(rg), dummy, dummy, 5, 4, dummy, 4, dummy, 512, None, dummy, 1 << 30, None)
     assert st == -1
+    st = lib.kvc_decode_attn_planned(C.byref(rg), dummy, dummy, 5, 4, dummy, 4, dummy, 512, None, dummy, 1 << 30,
+                                     None)
+    assert st == -1
+    # plan: workspace smaller than kvc_decode_workspace asks for
+    need = lib.kvc_decode_workspace(C.byref(rg), 4, 4)
+    assert need > 0
+    st = lib.kvc_decode_plan(C.byref(rg), 4, 4, dummy, need - 1, None)
+    assert st == -4
+    # plan: group 3 is not supported
+    st = lib.kvc_decode_plan(C.byref(rg), 3, 4, dummy, 1 << 30, None)
+    assert st == -7
     # kl: d_model not a multiple of 128
     st = lib.kvc_kl(2, 100, 50, dummy, dummy, dummy, 1, dummy, dummy, 1 << 30, None)
     assert st == -2

@@ -93,6 +93,40 @@ def test_decode_ragged_cache_with_multiplicity(name):
     close(o, oo, DEC_RTOL, "o_layers", floor=DEC_FLOOR)
 
 
+@pytest.mark.parametrize("name", ["ragged", "mistral1"])
+def test_decode_planned_steps_match_single_call_and_repeat(name):
+    """The planned path (one plan, many steps) gives the single-call path's
+    bits; 16 repeats of one step give identical bits (the pieces, the merge
+    and the last-arriver layer sum are deterministic); o_out holds the layers
+    whose sum, in layer order, is x."""
+    kvc = _kvc()
+    cfg = small_config(name)
+    inp = make_inputs(cfg)
+    dinp = inputs_to(inp)
+    pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
+    cache = kvc.full_view(pb, dinp["K"], dinp["V"])
+    S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
+    dec = kvc.Decoder(cache, cfg.G, Td)
+    for t in (0, Td // 2, Td - 1):
+        print(f"[decode-planned] {name} t={t}", flush=True)
+        q = dinp["Qd"][t].contiguous()
+        a = torch.zeros((S, Dm), dtype=torch.float32, device="cuda")
+        b = torch.zeros((S, Dm), dtype=torch.float32, device="cuda")
+        o = torch.zeros((S, cfg.Ly, cfg.H * cfg.G, cfg.d), dtype=torch.float32, device="cuda")
+        dec.step(dinp["Kd"], dinp["Vd"], t + 1, q, a, Dm)
+        kvc.decode_attn(cache, dinp["Kd"], dinp["Vd"], t + 1, Td, q, cfg.G, b, Dm, o)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+        xs = torch.zeros_like(a)
+        for l in range(cfg.Ly):
+            xs += o[:, l].reshape(S, -1)
+        assert torch.equal(xs, a)
+        for _ in range(16):
+            dec.step(dinp["Kd"], dinp["Vd"], t + 1, q, b, Dm)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("w_dtype,dm,vocab,n", [("f32", 256, 2048, 37), ("bf16", 1024, 1000, 37),
                                                  ("bf16", 4096, 32768, 37), ("bf16", 512, 1000, 100),
                                                  ("f32", 384, 300, 70), ("bf16", 128, 64, 1)])

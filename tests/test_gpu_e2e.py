@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from workload import small_config, make_inputs
-from parity import as_np, inputs_to, jaccard, close
+from parity import as_np, inputs_to, jaccard, close, check_kl
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +41,12 @@ def test_end_to_end_matches_oracle(name, kw):
     assert j >= 0.99, j
     assert np.array_equal(as_np(out["spent"]), o["spent"])
     close(xf, o["x_full"], 2e-2, "x_full", floor=1e-3)
-    err = np.abs(as_np(klv) - o["kl"])
-    print(f"  jaccard={j:.4f} kl_oracle_mean={o['kl'].mean():.4f} max|dKL|={err.max():.2e}", flush=True)
-    assert err.max() <= 1e-3 or j < 1.0, err.max()
+    print(f"  jaccard={j:.4f} kl_oracle_mean={o['kl'].mean():.4f}", flush=True)
     if j == 1.0:
-        assert err.max() <= 1e-3
+        # the packed prototypes are bf16 on the GPU and fp64 in the oracle, so
+        # x_comp carries their rounding, scaled by the summands (not by x)
+        close(xc, o["x_comp"], 2e-2, "x_comp", floor=1e-2)
+        check_kl(klv, xf, xc, inp["W"], o["kl"], name)
 
 
 @pytest.mark.parametrize("name", ["tiny", "stress", "ragged", "mistral1"])

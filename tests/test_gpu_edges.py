@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from workload import small_config, make_inputs
-from parity import close, as_np, inputs_to, jaccard, to_dev, slots_to_dev
+from parity import close, as_np, inputs_to, jaccard, to_dev, slots_to_dev, check_kl
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ def test_degenerate_lengths_end_to_end(base, lens):
     assert j >= 0.99, j
     close(xf, o["x_full"], 2e-2, "x_full", floor=1e-3)
     close(xc, o["x_comp"], 2e-2, "x_comp", floor=1e-3)
-    assert np.abs(as_np(klv) - o["kl"]).max() <= 1e-3
+    check_kl(klv, xf, xc, inp["W"], o["kl"], base)
 
 
 def test_empty_budget_keeps_nothing():
@@ -62,7 +62,7 @@ def test_empty_budget_keeps_nothing():
     assert not as_np(out["taken"]).any()
     o = oracle.run_pipeline(inp, cfg)
     close(xc, o["x_comp"], 2e-2, "x_comp (appended tokens only)", floor=1e-3)
-    assert np.abs(as_np(klv) - o["kl"]).max() <= 1e-3
+    check_kl(klv, xf, xc, inp["W"], o["kl"], "empty budget")
 
 
 @pytest.mark.parametrize("n_dprobe", [48, 20, 1])
