@@ -177,6 +177,21 @@ __global__ void write_tokens_kernel(PackArgs a, const int64_t* off) {
   copy_row<T, D>(a, i, dst, (int32_t)p, lane, 16);
 }
 
+// 8 consecutive elements from fp32 values in one 16-byte store (bf16: RNE)
+// or two (fp32).
+template <class T>
+__device__ __forceinline__ void store8(T* p, const float* x) {
+  if constexpr (sizeof(T) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f32_to_bf16_bits(x[2 * q]) | ((uint32_t)f32_to_bf16_bits(x[2 * q + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+    *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+}
+
 // One workgroup per (unit, slot). Every node decides in parallel whether it
 // is on the frontier (its creator op taken, its own Split not taken; the
 // root's creator is the Add); a block scan gives the frontier in pre-order,
@@ -295,12 +310,15 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
       const float4 sa = *(const float4*)(a.rs + prep * HD + p0), sb = *(const float4*)(a.rs + prep * HD + p0 + 4);
       const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
       const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+      float k0[8], k1[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float m0 = s0[e] / (float)nz, m1 = s1[e] / (float)nz;
-        ElemIO<T>::st(oK, p0 + e, m0 * cs[e] - m1 * sn[e]);
-        ElemIO<T>::st(oK, p0 + HD + e, m1 * cs[e] + m0 * sn[e]);
+        k0[e] = m0 * cs[e] - m1 * sn[e];
+        k1[e] = m1 * cs[e] + m0 * sn[e];
       }
+      store8<T>(oK + p0, k0);
+      store8<T>(oK + HD + p0, k1);
     } else {
       // prototype value: (1 - beta) r_i / rel + beta / n weights (uniform if rel = 0)
       const int d0 = (c - KP) * 8;
@@ -315,8 +333,7 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ElemIO<T>::st(oV, d0 + e, acc[e]);
+      store8<T>(oV + d0, acc);
     }
   }
   for (int f = tid; f < nfr; f += WS_THREADS) {

@@ -412,10 +412,12 @@ __global__ void floor_accept_kernel(FloorArgs f, int S, const SelState* st) {
   for (int q = 0; q < nops; ++q) f.taken[ops[q]] = 1;
 }
 // Candidates after the first one that did not fit, in order; one block per
-// sequence. Each round accepts the earliest remaining candidate whose current
+// sequence (FT_THREADS threads: every round scans all candidates). Each round
+// accepts the earliest remaining candidate whose current
 // path cost is between 1 and the remaining floor budget (candidates before it
 // cost more than what is left, or nothing); at most `remaining` rounds.
-__global__ __launch_bounds__(256) void floor_tail_kernel(FloorArgs f, const SelState* st, Ranges fb,
+constexpr int FT_THREADS = 1024;
+__global__ __launch_bounds__(FT_THREADS) void floor_tail_kernel(FloorArgs f, const SelState* st, Ranges fb,
                                                          int64_t* spent_floor) {
   __shared__ unsigned long long best;
   __shared__ unsigned long long pre;
@@ -427,7 +429,7 @@ __global__ __launch_bounds__(256) void floor_tail_kernel(FloorArgs f, const SelS
   if (threadIdx.x == 0) pre = 0;
   __syncthreads();
   unsigned long long loc = 0;
-  for (int64_t k = threadIdx.x; k < cnt; k += 256) {
+  for (int64_t k = threadIdx.x; k < cnt; k += FT_THREADS) {
     int64_t i = (int64_t)s * f.Fmax + k;
     if (S_.all || f.ckey[i] > S_.prefix) loc += (unsigned long long)f.ccost[i];
   }
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256) void floor_tail_kernel(FloorArgs f, const SelS
     if (rem <= 0) break;
     if (threadIdx.x == 0) best = 0;
     __syncthreads();
-    for (int64_t k = threadIdx.x; k < cnt; k += 256) {
+    for (int64_t k = threadIdx.x; k < cnt; k += FT_THREADS) {
       int64_t i = (int64_t)s * f.Fmax + k;
       uint64_t key = f.ckey[i];
       if (key >= pos) continue;
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(256) void floor_tail_kernel(FloorArgs f, const SelS
     uint64_t win = best;
     __syncthreads();
     if (win == 0) break;
-    for (int64_t k = threadIdx.x; k < cnt; k += 256) {
+    for (int64_t k = threadIdx.x; k < cnt; k += FT_THREADS) {
       int64_t i = (int64_t)s * f.Fmax + k;
       if (f.ckey[i] != win) continue;
       int64_t ops[9];
@@ -848,7 +850,7 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   if ((r = run_select(cr, csrc, st, hist, stream))) return r;
   hipLaunchKernelGGL(floor_accept_kernel, dim3(kvc_blocks(ncand, 256)), dim3(256), 0, stream, fa, sh->n_seq, st);
   KVC_LAUNCH_CHECK("floor_accept");
-  hipLaunchKernelGGL(floor_tail_kernel, dim3(sh->n_seq), dim3(256), 0, stream, fa, st, budget_r, sfloor);
+  hipLaunchKernelGGL(floor_tail_kernel, dim3(sh->n_seq), dim3(FT_THREADS), 0, stream, fa, st, budget_r, sfloor);
   KVC_LAUNCH_CHECK("floor_tail");
 
   // ---- auction over every untaken op
