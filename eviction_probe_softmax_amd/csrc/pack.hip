@@ -197,8 +197,10 @@ __device__ __forceinline__ void store8(T* p, const float* x) {
 // root's creator is the Add); a block scan gives the frontier in pre-order,
 // which is position order. Then 16-byte pieces of the output rows are spread
 // over the threads: leaves are copied, prototype keys (8 rotate-half pairs a
-// piece) and values (8 dims a piece) are averaged over the node's tokens.
+// piece) and values (8 dims a piece) are averaged over the node's tokens by
+// SPL threads a piece.
 constexpr int WS_THREADS = 256;  // >= 2 * 128 - 1 nodes of the largest slot
+constexpr int SPL = 4;           // threads per piece of a prototype
 
 template <class T, int D>
 __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, const int64_t* off) {
@@ -207,6 +209,7 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
   constexpr int VP = D / 8;        // value pieces (8 dims each)
   constexpr int CPN = KP + VP;
   __shared__ int16_t fnode[WS_THREADS], fst[WS_THREADS], fsz[WS_THREADS];
+  __shared__ int ioff[WS_THREADS + 1];
   __shared__ int wcnt[WS_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // block -> (unit lh, sequence s, slot k): grid is (Ly*H*S*stride)
@@ -260,17 +263,51 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
     fsz[q] = (int16_t)sz;
   }
   __syncthreads();
+  // item ranges: a leaf takes CPN items (one per piece), a prototype SPL * CPN
+  // (SPL consecutive threads per piece, each summing every SPL-th token); all
+  // ranges are multiples of SPL, so the SPL threads of a piece are
+  // neighbouring lanes of one wave
+  {
+    const int f = tid;
+    const int ic = f < nfr ? (fsz[f] == 1 ? CPN : SPL * CPN) : 0;
+    int inc = ic;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wcnt[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < WS_THREADS / 64; ++w) {
+      base += w < wave ? wcnt[w] : 0;
+      tot += wcnt[w];
+    }
+    if (f < nfr) ioff[f] = base + inc - ic;
+    if (tid == 0) ioff[nfr] = tot;
+    __syncthreads();
+  }
+  const int nitems = ioff[nfr];
   const T* Ku = (const T*)a.K + (lh * a.T + a.cu[s]) * D;
   const T* Vu = (const T*)a.V + (lh * a.T + a.cu[s]) * D;
   const float* ru = a.rel + lh * a.T + a.cu[s];
-  for (int it = tid; it < nfr * CPN; it += WS_THREADS) {
-    const int f = it / CPN, c = it % CPN;
+  for (int it = tid; it < nitems; it += WS_THREADS) {
+    // entry of this item: the last f with ioff[f] <= it
+    int lo = 0, hi = nfr - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ioff[mid] <= it) lo = mid;
+      else hi = mid - 1;
+    }
+    const int f = lo, local = it - ioff[f];
     const int64_t dst = dst0 + f;
-    if (dst >= a.capacity) continue;
+    if (dst >= a.capacity) continue;  // every item of the entry skips together
     const int j = fnode[f], a0 = t0 + fst[f], nz = fsz[f];   // sequence positions [a0, a0 + nz)
     T* oK = (T*)a.oK + dst * D;
     T* oV = (T*)a.oV + dst * D;
     if (nz == 1) {  // leaf: bit copy of the token's 16-byte pieces
+      const int c = local;
       if (c < KP) {
         *(uint4*)(oK + c * 8) = *(const uint4*)(Ku + (int64_t)a0 * D + c * 8);
         *(uint4*)(oK + HD + c * 8) = *(const uint4*)(Ku + (int64_t)a0 * D + HD + c * 8);
@@ -285,13 +322,14 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
       }
       continue;
     }
+    const int c = local / SPL, sub = local % SPL;
     if (c < KP) {
       // prototype key: mean of the inverse-rotated keys, re-rotated at the representative position
       const int p0 = c * 8;
       float s0[8], s1[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) s0[e] = s1[e] = 0.f;
-      for (int i = a0; i < a0 + nz; ++i) {
+      for (int i = a0 + sub; i < a0 + nz; i += SPL) {
         float x0[8], x1[8];
         kvcmf::Load8<T>::f(Ku + (int64_t)i * D + p0, x0);
         kvcmf::Load8<T>::f(Ku + (int64_t)i * D + HD + p0, x1);
@@ -305,6 +343,15 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
           s1[e] += x1[e] * cs[e] - x0[e] * sn[e];
         }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {  // the SPL partial sums, combined in a fixed order
+#pragma unroll
+        for (int o = 1; o < SPL; o <<= 1) {
+          s0[e] += __shfl_xor(s0[e], o, 64);
+          s1[e] += __shfl_xor(s1[e], o, 64);
+        }
+      }
+      if (sub != 0) continue;
       const int64_t prep = a0 + (nz - 1) / 2;
       const float4 ca = *(const float4*)(a.rc + prep * HD + p0), cb = *(const float4*)(a.rc + prep * HD + p0 + 4);
       const float4 sa = *(const float4*)(a.rs + prep * HD + p0), sb = *(const float4*)(a.rs + prep * HD + p0 + 4);
@@ -326,14 +373,18 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      for (int i = a0; i < a0 + nz; ++i) {
+      for (int i = a0 + sub; i < a0 + nz; i += SPL) {
         const float w = rel_n > 0.f ? (1.f - a.beta) * ru[i] / rel_n + a.beta / (float)nz : 1.f / (float)nz;
         float x[8];
         kvcmf::Load8<T>::f(Vu + (int64_t)i * D + d0, x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
       }
-      store8<T>(oV + d0, acc);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int o = 1; o < SPL; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+      if (sub == 0) store8<T>(oV + d0, acc);
     }
   }
   for (int f = tid; f < nfr; f += WS_THREADS) {
