@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the variant measurements beside the headline line (head-level hybrid, "
                          "step-wise eviction)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring this GPU's own HBM read and bf16 MFMA ceilings (kvc_peak_read, "
+                         "kvc_peak_mfma) before the timed steps")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_fulldepth_traffic.json"))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run five plain device-to-device copies of MIB MiB (to scale HBM byte "
@@ -232,6 +235,14 @@ def main():
 
     cfg = get_config(args.config)
     dev = "cuda"
+    peaks = None
+    if not args.no_peaks:
+        # the machine's own ceilings, measured before anything else is resident
+        peaks = {"hbm_read_gbs": round(kvc.peak_read_gbs(), 1), "mfma_bf16_tflops": round(kvc.peak_mfma_tflops(), 1),
+                 "how": "kvc_peak_read: 2 GiB of nontemporal 16-byte loads; kvc_peak_mfma: register-only "
+                        "32x32x16 bf16 MFMA chains on every SIMD"}
+        print(f"[bench] measured peaks {peaks['hbm_read_gbs']} GB/s, {peaks['mfma_bf16_tflops']} TFLOP/s",
+              file=sys.stderr, flush=True)
     t_gen = time.perf_counter()
     inp = make_inputs(cfg, device=dev, seed=args.seed)
     torch.cuda.synchronize()
@@ -358,7 +369,11 @@ def main():
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_call_comp": int(bytes_comp), "bytes_per_call_full": int(bytes_full)},
+        "measured_peaks": peaks,
     }
+    if peaks:
+        res["roofline"]["peak_measured"] = peaks["hbm_read_gbs"]
+        res["roofline"]["frac_measured"] = round(ach / peaks["hbm_read_gbs"], 4)
     if not args.no_variants:
         res["variants"] = measure_variants(cfg, inp, full, x_full, kl_op, stream)
     if not args.no_cpu_baseline:

@@ -1,0 +1,84 @@
+// Measurement helpers: the HBM read ceiling (nontemporal 16-byte loads) and
+// the bf16 MFMA ceiling (register-only MFMA chains) of the device, timed by
+// the caller.
+#include "kvc_internal.h"
+#include "kvc_peaks.h"
+
+namespace {
+
+typedef unsigned int pk_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int READ_THREADS = 256;
+constexpr int READ_UNROLL = 8;
+
+__global__ __launch_bounds__(READ_THREADS) void peak_read_kernel(const pk_u32x4* __restrict__ p, size_t n16,
+                                                                 uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * READ_THREADS;
+  size_t i = (size_t)blockIdx.x * READ_THREADS + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (READ_UNROLL - 1) * stride < n16; i += READ_UNROLL * stride) {
+    pk_u32x4 v[READ_UNROLL];
+#pragma unroll
+    for (int k = 0; k < READ_UNROLL; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < READ_UNROLL; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < n16; i += stride) {
+    const pk_u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;
+}
+
+__global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* sink) {
+  const int lane = threadIdx.x & 63;
+  // operands: small distinct values per lane, kept in registers
+  kvc_bf16x8 a, b;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(0.001f * (float)((lane + j) & 7));
+    b[j] = (__bf16)(0.001f * (float)((lane * 3 + j) & 7));
+  }
+  kvc_f32x16 c0, c1, c2, c3;  // distinct starting values keep the four chains apart
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    c0[v] = 0.f;
+    c1[v] = 1.f;
+    c2[v] = 2.f;
+    c3[v] = 3.f;
+  }
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) s += c0[v] + c1[v] + c2[v] + c3[v];
+  s = wave_sum(s);
+  __shared__ float ws[4];
+  if (lane == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
+}  // namespace
+
+extern "C" int kvc_peak_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, hipStream_t st) {
+  KVC_REQUIRE(buf && sink, KVC_E_INVAL, "kvc_peak_read: NULL pointer");
+  KVC_REQUIRE(bytes > 0 && bytes % 16 == 0 && ((uintptr_t)buf & 15) == 0, KVC_E_INVAL,
+              "kvc_peak_read: bytes and buf must be nonzero multiples of 16");
+  KVC_REQUIRE(grid >= 1, KVC_E_INVAL, "kvc_peak_read: grid must be >= 1");
+  hipLaunchKernelGGL(peak_read_kernel, dim3((unsigned)grid), dim3(READ_THREADS), 0, st, (const pk_u32x4*)buf,
+                     bytes / 16, sink);
+  KVC_LAUNCH_CHECK("peak_read");
+  return KVC_OK;
+}
+
+extern "C" int kvc_peak_mfma(int32_t grid, int32_t iters, float* sink, hipStream_t st) {
+  KVC_REQUIRE(sink, KVC_E_INVAL, "kvc_peak_mfma: NULL sink");
+  KVC_REQUIRE(grid >= 1 && iters >= 1, KVC_E_INVAL, "kvc_peak_mfma: grid and iters must be >= 1");
+  hipLaunchKernelGGL(peak_mfma_kernel, dim3((unsigned)grid), dim3(256), 0, st, iters, sink);
+  KVC_LAUNCH_CHECK("peak_mfma");
+  return KVC_OK;
+}

@@ -126,6 +126,10 @@ _sig = {
     "kvc_kl_workspace": (C.c_size_t, [C.c_int64, C.c_int32, C.c_int32, C.c_int32]),
     "kvc_kl": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]),
 }
+# measurement helpers (include/kvc_peaks.h)
+PEAK_EXPORTS = ["kvc_peak_read", "kvc_peak_mfma"]
+_sig["kvc_peak_read"] = (C.c_int, [_P, C.c_size_t, C.c_int32, _P, _P])
+_sig["kvc_peak_mfma"] = (C.c_int, [C.c_int32, C.c_int32, _P, _P])
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
     _f.restype = _res
@@ -534,3 +538,37 @@ class Stepwise:
         else:
             self.decoder.plan()  # the student's segments change every step
         self.decoder.step(K_tail, V_tail, 0, Q_t, x_out, x_stride)
+
+
+def _time_ms(launch, reps):
+    launch()
+    launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def peak_read_gbs(nbytes=2 << 30, grid=8192, reps=10):
+    """Measured HBM read ceiling (kvc_peak_read over nbytes of device memory), GB/s."""
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def launch():
+        _check("kvc_peak_read", _lib.kvc_peak_read(_ptr(buf), nbytes, grid, _ptr(sink), _stream()))
+    ms = _time_ms(launch, reps)
+    del buf
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def peak_mfma_tflops(grid=2048, iters=4096, reps=5):
+    """Measured dense bf16 MFMA ceiling (kvc_peak_mfma), TFLOP/s."""
+    sink = torch.zeros(grid, dtype=torch.float32, device="cuda")
+
+    def launch():
+        _check("kvc_peak_mfma", _lib.kvc_peak_mfma(grid, iters, _ptr(sink), _stream()))
+    ms = _time_ms(launch, reps)
+    return grid * 4 * iters * 131072 / (ms * 1e-3) / 1e12

@@ -11,10 +11,11 @@ import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HDR = os.path.join(ROOT, "include", "kvc.h")
+PEAKS_HDR = os.path.join(ROOT, "include", "kvc_peaks.h")
 
 
-def _declared():
-    txt = open(HDR).read()
+def _declared(hdr=HDR):
+    txt = open(hdr).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", txt)))
 
@@ -32,6 +33,23 @@ def test_every_declared_symbol_is_exported(kvc):
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kvc.h but not exported"
     assert set(kvc.EXPORTS) == set(names)
+    # every header under include/ is one of these two
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["kvc.h", "kvc_peaks.h"]
+    peaks = _declared(PEAKS_HDR)
+    for n in peaks:
+        assert hasattr(lib, n), f"{n} declared in kvc_peaks.h but not exported"
+    assert set(kvc.PEAK_EXPORTS) == set(peaks)
+
+
+def test_peak_helpers_reject_bad_arguments(kvc):
+    lib = kvc._lib
+    dummy = C.c_void_p(16)
+    assert lib.kvc_peak_read(None, 1024, 64, dummy, None) == -1
+    assert lib.kvc_peak_read(dummy, 1000, 64, dummy, None) == -1   # not a multiple of 16
+    assert lib.kvc_peak_read(dummy, 1024, 0, dummy, None) == -1
+    assert lib.kvc_peak_mfma(0, 10, dummy, None) == -1
+    assert lib.kvc_peak_mfma(8, 0, dummy, None) == -1
+    assert lib.kvc_peak_mfma(8, 10, None, None) == -1
 
 
 def _problem(kvc, lens, **kw):

@@ -1,0 +1,15 @@
+"""The measurement helpers run on the GPU and give plausible ceilings (they
+are checked only for sanity: the vendor's HBM peak is 8 TB/s and the dense
+bf16 MFMA peak 2.5 PFLOP/s)."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def test_peak_read_and_mfma():
+    from eviction_probe_softmax_amd import kvc
+    gbs = kvc.peak_read_gbs(nbytes=256 << 20, reps=5)
+    tf = kvc.peak_mfma_tflops(grid=1024, iters=512, reps=3)
+    print(f"[peaks] read {gbs:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s", flush=True)
+    assert 1000 < gbs < 8500
+    assert 200 < tf < 2600
