@@ -229,6 +229,7 @@ __global__ __launch_bounds__(256) void window_cost_kernel(PartArgs a, const floa
 }
 
 // exact integer DP; one 1024-thread block per sequence
+constexpr int DP_PF = 4;  // DP steps whose cost loads are in flight
 __global__ __launch_bounds__(1024) void dp_kernel(PartArgs a) {
   constexpr int RING = 512;
   __shared__ int64_t fr[RING];
@@ -258,54 +259,72 @@ __global__ __launch_bounds__(1024) void dp_kernel(PartArgs a) {
   if (threadIdx.x == 0) fr[0] = 0;
   __syncthreads();
   const int step = a.nmin < 16 ? a.nmin : 16;  // ends that depend only on earlier ends
-  for (int64_t e0 = 1; e0 <= Lc; e0 += step) {
-    int64_t e = e0 + wave;               // region-relative end (exclusive)
-    int64_t best = INT64_MAX;
-    const bool mine = wave < step && e <= Lc;
-    if (mine) {
-      // two candidates per lane (slot_max - slot_min < 128); the global loads
-      // go out before the LDS reads of earlier ends
-      int64_t cq[2], kq[2], fv[2];
+  // The cost and cut terms do not depend on the recurrence, so their loads run
+  // DP_PF steps ahead in a ring of register sets: every load is unconditional
+  // (indices clamped into the arrays) and selected away where it does not
+  // apply, so the waits before each step stay partial.
+  int64_t cqb[DP_PF][2], kqb[DP_PF][2];
+  auto issue = [&](int j, int64_t e0s) {
+    const int64_t e = min(e0s + wave, Lc);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int c = lane + 64 * q;
-        int64_t pv = e - (a.nmin + c);
-        cq[q] = (c < ncol && pv >= 0) ? a.cost_q[(gbase + e - 1) * ncol + c] : 0;
-        kq[q] = (c < ncol && pv > 0) ? a.cut_q[gbase + pv] : 0;
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int c = lane + 64 * q;
-        int64_t pv = e - (a.nmin + c);
-        fv[q] = (c < ncol && pv >= 0) ? fr[pv % RING] : INF_Q;
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        int c = lane + 64 * q;
-        if (fv[q] >= INF_Q) continue;
-        int64_t v = fv[q] + cq[q] - kq[q];
-        int64_t key = v * 256 + (255 - c);
-        best = key < best ? key : best;
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        int64_t other = __shfl_xor(best, o, 64);
-        best = other < best ? other : best;
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int c = min(lane + 64 * q, ncol - 1);
+      const int64_t pv = max(e - (a.nmin + c), (int64_t)0);
+      cqb[j][q] = a.cost_q[(gbase + e - 1) * ncol + c];
+      kqb[j][q] = a.cut_q[gbase + pv];
     }
-    __syncthreads();                    // every read of fr for this block is done
-    if (mine && lane == 0) {
-      if (best == INT64_MAX) {
-        fr[e % RING] = INF_Q;
-        arg[e] = 255;
-      } else {
-        int64_t v = best >= 0 ? best / 256 : -((-best + 255) / 256);
-        int c = 255 - (int)(best - v * 256);
-        fr[e % RING] = v;
-        arg[e] = (uint8_t)c;
+  };
+#pragma unroll
+  for (int j = 0; j < DP_PF; ++j) issue(j, 1 + (int64_t)j * step);
+  for (int64_t eb = 1; eb <= Lc; eb += (int64_t)DP_PF * step) {
+#pragma unroll
+    for (int j = 0; j < DP_PF; ++j) {
+      const int64_t e0 = eb + (int64_t)j * step;
+      if (e0 > Lc) break;
+      int64_t e = e0 + wave;               // region-relative end (exclusive)
+      int64_t best = INT64_MAX;
+      const bool mine = wave < step && e <= Lc;
+      if (mine) {
+        int64_t fv[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int c = lane + 64 * q;
+          const int64_t pv = e - (a.nmin + c);
+          fv[q] = (c < ncol && pv >= 0) ? fr[pv % RING] : INF_Q;
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int c = lane + 64 * q;
+          if (fv[q] >= INF_Q) continue;
+          const int64_t pv = e - (a.nmin + c);
+          const int64_t kq = pv > 0 ? kqb[j][q] : 0;
+          const int64_t v = fv[q] + cqb[j][q] - kq;
+          const int64_t key = v * 256 + (255 - c);
+          best = key < best ? key : best;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          const int64_t other = __shfl_xor(best, o, 64);
+          best = other < best ? other : best;
+        }
       }
+      issue(j, e0 + (int64_t)DP_PF * step);  // this register set now serves a later step
+      // no barrier before the writes: this step reads ends e0 - nmax .. e0 - 1
+      // and writes e0 .. e0 + step - 1 (step <= nmin, and the ring holds more
+      // than nmax + step ends), so no write meets a read of the same step
+      if (mine && lane == 0) {
+        if (best == INT64_MAX) {
+          fr[e % RING] = INF_Q;
+          arg[e] = 255;
+        } else {
+          const int64_t v = best >= 0 ? best / 256 : -((-best + 255) / 256);
+          const int c = 255 - (int)(best - v * 256);
+          fr[e % RING] = v;
+          arg[e] = (uint8_t)c;
+        }
+      }
+      __syncthreads();  // the next step reads these ends
     }
-    __syncthreads();
   }
   if (threadIdx.x == 0) {
     // backtrack twice: count, then write the starts in position order
