@@ -93,6 +93,63 @@ def test_decode_ragged_cache_with_multiplicity(name):
     close(o, oo, DEC_RTOL, "o_layers", floor=DEC_FLOOR)
 
 
+@pytest.mark.parametrize("dtype,t_valid", [(torch.bfloat16, 1000), (torch.bfloat16, 769), (torch.float32, 600),
+                                            (torch.float32, 0)])
+def test_decode_long_tails_and_empty_segments(dtype, t_valid):
+    """Tails longer than one piece (768 entries bf16, 256 fp32) split into
+    several tail pieces; units whose segment is empty attend over the tail
+    alone, or (no tail) give zeros; segments of 1, 767, 769 and 2000 entries
+    cover one, two and three segment pieces."""
+    kvc = _kvc()
+    g = torch.Generator().manual_seed(17)
+    S, Ly, H, G, d = 2, 2, 2, 4, 128
+    lens = np.array([[[0, 1], [767, 769]], [[2000, 0], [5, 1536]]], dtype=np.int64)  # [S][Ly][H]
+    N = int(lens.sum())
+    Kc = torch.randn((N, d), generator=g).to(dtype)
+    Vc = torch.randn((N, d), generator=g).to(dtype)
+    lnmu = torch.log(1 + 3 * torch.rand((N,), generator=g)).float()
+    seg_off = np.zeros((S, Ly, H), np.int64)
+    off = 0
+    for s in range(S):
+        for l in range(Ly):
+            for h in range(H):
+                seg_off[s, l, h] = off
+                off += lens[s, l, h]
+    t_cap = max(t_valid, 1)
+    Kd = torch.randn((Ly, H, S, t_cap, d), generator=g).to(dtype)
+    Vd = torch.randn((Ly, H, S, t_cap, d), generator=g).to(dtype)
+    Q = torch.randn((S, Ly, H * G, d), generator=g).to(dtype)
+    print(f"[decode-tails] {dtype} t_valid={t_valid}", flush=True)
+    gcache = {"K": Kc.cuda(), "V": Vc.cuda(), "lnmu": lnmu.cuda(), "pos": None,
+              "seg_off": torch.from_numpy(seg_off).cuda(), "seg_len": torch.from_numpy(lens.astype(np.int32)).cuda(),
+              "n_seq": S, "n_layers": Ly, "n_kv_heads": H, "head_dim": d, "max_seg": int(lens.max())}
+    x = torch.full((S, H * G * d), float("nan"), dtype=torch.float32, device="cuda")
+    o = torch.full((S, Ly, H * G, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.decode_attn(gcache, Kd.cuda(), Vd.cuda(), t_valid, t_cap, Q.cuda(), G, x, H * G * d, o)
+    torch.cuda.synchronize()
+    ocache = {"K": oracle.to64(Kc), "V": oracle.to64(Vc), "lnmu": lnmu.numpy(), "seg_off": seg_off,
+              "seg_len": lens.astype(np.int32)}
+    # the oracle's step t attends over tail tokens 0..t
+    if t_valid > 0:
+        want_x, want_o = oracle.decode_step(ocache, Kd, Vd, Q, t_valid - 1, G)
+    else:
+        want_o = np.zeros((S, Ly, H * G, d))
+        for s in range(S):
+            for l in range(Ly):
+                for h in range(H):
+                    a0, n = int(seg_off[s, l, h]), int(lens[s, l, h])
+                    if n == 0:
+                        continue
+                    Ke, Ve = ocache["K"][a0:a0 + n], ocache["V"][a0:a0 + n]
+                    z = (oracle.to64(Q)[s, l, h * G:(h + 1) * G] @ Ke.T) / math.sqrt(d) + ocache["lnmu"][a0:a0 + n]
+                    p = np.exp(z - z.max(axis=1, keepdims=True))
+                    want_o[s, l, h * G:(h + 1) * G] = (p / p.sum(axis=1, keepdims=True)) @ Ve
+        want_x = want_o.sum(axis=1).reshape(S, -1)
+    rt = DEC_RTOL if dtype == torch.bfloat16 else 1e-4
+    close(o, want_o, rt, "o", floor=DEC_FLOOR)
+    close(x, want_x, rt, "x", floor=DEC_FLOOR)
+
+
 @pytest.mark.parametrize("name", ["ragged", "mistral1"])
 def test_decode_planned_steps_match_single_call_and_repeat(name):
     """The planned path (one plan, many steps) gives the single-call path's
