@@ -150,6 +150,45 @@ def test_decode_long_tails_and_empty_segments(dtype, t_valid):
     close(x, want_x, rt, "x", floor=DEC_FLOOR)
 
 
+def test_decode_plan_over_many_units():
+    """16,384 units (more than one round of the plan's scan), segments of 0..5
+    entries, head dim 64, group 1: every unit's output against the definition."""
+    kvc = _kvc()
+    g = torch.Generator().manual_seed(23)
+    S, Ly, H, G, d, t_cap, t_valid = 64, 16, 16, 1, 64, 3, 2
+    lens = torch.randint(0, 6, (S, Ly, H), generator=g).numpy().astype(np.int64)
+    N = int(lens.sum())
+    Kc = torch.randn((N, d), generator=g).to(torch.bfloat16)
+    Vc = torch.randn((N, d), generator=g).to(torch.bfloat16)
+    seg_off = np.concatenate([[0], np.cumsum(lens.reshape(-1))[:-1]]).reshape(S, Ly, H).astype(np.int64)
+    Kd = torch.randn((Ly, H, S, t_cap, d), generator=g).to(torch.bfloat16)
+    Vd = torch.randn((Ly, H, S, t_cap, d), generator=g).to(torch.bfloat16)
+    Q = torch.randn((S, Ly, H * G, d), generator=g).to(torch.bfloat16)
+    print(f"[decode-units] {S * Ly * H} units, {N} entries", flush=True)
+    gcache = {"K": Kc.cuda(), "V": Vc.cuda(), "lnmu": None, "pos": None,
+              "seg_off": torch.from_numpy(seg_off).cuda(), "seg_len": torch.from_numpy(lens.astype(np.int32)).cuda(),
+              "n_seq": S, "n_layers": Ly, "n_kv_heads": H, "head_dim": d, "max_seg": int(lens.max())}
+    x = torch.full((S, H * G * d), float("nan"), dtype=torch.float32, device="cuda")
+    o = torch.full((S, Ly, H * G, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvc.decode_attn(gcache, Kd.cuda(), Vd.cuda(), t_valid, t_cap, Q.cuda(), G, x, H * G * d, o)
+    torch.cuda.synchronize()
+    # the definition, vectorised over units: softmax over the segment and the tail
+    K64, V64 = oracle.to64(Kc), oracle.to64(Vc)
+    Kd64, Vd64, Q64 = oracle.to64(Kd), oracle.to64(Vd), oracle.to64(Q)
+    want = np.zeros((S, Ly, H * G, d))
+    for s in range(S):
+        for l in range(Ly):
+            for h in range(H):
+                a0, n = int(seg_off[s, l, h]), int(lens[s, l, h])
+                Ke = np.concatenate([K64[a0:a0 + n], Kd64[l, h, s, :t_valid]])
+                Ve = np.concatenate([V64[a0:a0 + n], Vd64[l, h, s, :t_valid]])
+                z = Ke @ Q64[s, l, h] / math.sqrt(d)
+                p = np.exp(z - z.max())
+                want[s, l, h] = (p / p.sum()) @ Ve
+    close(o, want, DEC_RTOL, "o", floor=DEC_FLOOR)
+    close(x, want.sum(axis=1).reshape(S, -1), DEC_RTOL, "x", floor=DEC_FLOOR)
+
+
 @pytest.mark.parametrize("name", ["ragged", "mistral1"])
 def test_decode_planned_steps_match_single_call_and_repeat(name):
     """The planned path (one plan, many steps) gives the single-call path's
