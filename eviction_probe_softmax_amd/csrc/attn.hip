@@ -686,9 +686,13 @@ __global__ void copy_f32_kernel(const float* src, float* dst, int64_t n) {
 }
 
 // ------------------------------------------------------------------ host
+// Key split of the probe and seed passes: the widest of 1024 / 512 / 256 keys
+// that still gives 2048 workgroups (each stages its query rows once, so wider
+// splits stage less; 1024 against 512 saves 0.33 ms of the 3.3 ms of probe and
+// seed passes on the full-depth workload).
 int pick_kw(const kvc_shape* sh) {
   int64_t units = (int64_t)sh->n_layers * sh->n_kv_heads;
-  for (int kw : {512, 256}) {
+  for (int kw : {1024, 512, 256}) {
     int64_t n = 0;
     for (int s = 0; s < sh->n_seq; ++s) n += units * ((sh->cu_seqlens[s + 1] - sh->cu_seqlens[s] + kw - 1) / kw);
     if (n >= 2048) return kw;
@@ -919,14 +923,14 @@ int dispatch_rowval(int dtype, int d, const AttnArgs& a, int64_t nsplit, float* 
   return d == 128 ? launch_rowval<float, 128>(a, nsplit, part, st) : launch_rowval<float, 64>(a, nsplit, part, st);
 }
 int dense_rows(const kvc_shape* sh) { return (256 / sh->group) < 64 ? 256 / sh->group : 64; }
-// Key split of the dense passes, a multiple of the seed passes': every row
+// Key split of the dense passes, a multiple of 512 keys: every row
 // block stages its 256 query rows once per split, and a block's rows see a
 // whole causal prefix, so wide splits stage far less (fewer splits than the
 // workspace, sized with pick_kw, holds). Measured on the full-depth workload
 // (16,384 tokens): the dense rollout 769 ms at 1x, 425 ms at 16x (523 ms at
 // 32x, where one split a unit leaves its column-sum pass too few workgroups);
 // the "A r" direction, a row pass only, 739 ms at 1x, 221 ms at 32x.
-int dense_kw(const kvc_shape* sh, int mult) { return pick_kw(sh) * mult; }
+int dense_kw(int mult) { return 512 * mult; }  // >= pick_kw for mult >= 2
 }  // namespace
 
 extern "C" size_t kvc_propagate_dense_workspace(const kvc_shape* sh, const kvc_params* p) {
@@ -947,7 +951,7 @@ extern "C" int kvc_propagate_dense(const kvc_shape* sh, const kvc_params* p, con
               "kvc_propagate_dense: workspace too small");
   kvc_params q = *p;
   q.n_seeds = dense_rows(sh);
-  const int kw = dense_kw(sh, 16);
+  const int kw = dense_kw(16);
   const int64_t ns = n_splits(sh, kw);
   const int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
   const int64_t units = (int64_t)sh->n_seq * sh->n_layers * sh->n_kv_heads;
@@ -1007,7 +1011,7 @@ extern "C" int kvc_propagate_ar(const kvc_shape* sh, const kvc_params* p, const 
               "kvc_propagate_ar: workspace too small");
   kvc_params q = *p;
   q.n_seeds = dense_rows(sh);
-  const int kw = dense_kw(sh, 32);
+  const int kw = dense_kw(32);
   const int64_t ns = n_splits(sh, kw);
   const int64_t E = (int64_t)sh->n_layers * sh->n_kv_heads * sh->total_tokens;
   const int64_t units = (int64_t)sh->n_seq * sh->n_layers * sh->n_kv_heads;
