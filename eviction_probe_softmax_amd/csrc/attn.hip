@@ -609,75 +609,116 @@ __global__ void headsens_kernel(AttnArgs a, const float* head_part, float* head_
 // Top-M tokens of delta per unit by (value desc, index asc), written in
 // ascending position order, -1 padded. One workgroup per unit: an 8-pass MSB
 // radix select on the 64-bit keys, then an ordered compaction.
-__global__ __launch_bounds__(256) void seeds_kernel(AttnArgs a, const float* delta, int32_t* seeds) {
+// Top-M seeds of one unit: an 8-pass MSB radix select over 64-bit keys
+// (score, then the lower index first) held in registers, each pass a shared
+// histogram and a parallel suffix scan of its 256 bins, then an ordered
+// compaction (per-thread contiguous index ranges, a block scan of the counts).
+constexpr int SEED_THREADS = 1024;
+constexpr int SEED_PER = 16;  // keys a thread keeps in registers; longer sequences loop over global memory
+__device__ __forceinline__ int block_excl_scan_seed(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < SEED_THREADS / 64; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  __syncthreads();  // wsum is reused by the next scan
+  *total = tot;
+  return base + inc - v;
+}
+
+__global__ __launch_bounds__(SEED_THREADS) void seeds_kernel(AttnArgs a, const float* delta, int32_t* seeds) {
   __shared__ uint32_t hist[256];
+  __shared__ int wsum[SEED_THREADS / 64];
   __shared__ uint64_t s_prefix;
   __shared__ int64_t s_need;
-  __shared__ int32_t s_cnt[256];
-  int unit = blockIdx.x;
-  int s = unit / (a.Ly * a.H);
-  int lh = unit % (a.Ly * a.H);
-  int64_t tok0 = a.cu[s];
-  int64_t L = a.cu[s + 1] - tok0;
+  const int unit = blockIdx.x;
+  const int s = unit / (a.Ly * a.H);
+  const int lh = unit % (a.Ly * a.H);
+  const int64_t tok0 = a.cu[s];
+  const int64_t L = a.cu[s + 1] - tok0;
   const float* dl = delta + (int64_t)lh * a.T + tok0;
   int32_t* out = seeds + (int64_t)unit * a.M;
+  const int tid = threadIdx.x;
+  // thread t owns the contiguous index range [t*per, t*per + per)
+  const int64_t per = (L + SEED_THREADS - 1) / SEED_THREADS;
+  const int64_t b0 = min((int64_t)tid * per, L), b1 = min(b0 + per, L);
+  const bool inreg = per <= SEED_PER;
+  uint64_t kr[SEED_PER];
+#pragma unroll
+  for (int q = 0; q < SEED_PER; ++q) {
+    const int64_t i = b0 + q;
+    kr[q] = (inreg && i < b1) ? make_key(dl[i], (uint32_t)i) : 0ull;
+  }
   uint64_t thr = 0;  // select keys >= thr
   if (L > a.M) {
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       s_prefix = 0;
       s_need = a.M;
     }
-    __syncthreads();
     for (int pass = 0; pass < 8; ++pass) {
-      int shift = 56 - 8 * pass;
-      hist[threadIdx.x] = 0;
+      const int shift = 56 - 8 * pass;
+      if (tid < 256) hist[tid] = 0;
       __syncthreads();
-      uint64_t prefix = s_prefix;
-      uint64_t hmask = pass == 0 ? 0ull : (~0ull << (64 - 8 * pass));
-      for (int64_t i = threadIdx.x; i < L; i += blockDim.x) {
-        uint64_t k = make_key(dl[i], (uint32_t)i);
-        if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1u);
+      const uint64_t prefix = s_prefix;
+      const uint64_t hmask = pass == 0 ? 0ull : (~0ull << (64 - 8 * pass));
+      if (inreg) {
+#pragma unroll
+        for (int q = 0; q < SEED_PER; ++q)
+          if (b0 + q < b1 && (kr[q] & hmask) == prefix) atomicAdd(&hist[(kr[q] >> shift) & 255], 1u);
+      } else {
+        for (int64_t i = b0; i < b1; ++i) {
+          const uint64_t k = make_key(dl[i], (uint32_t)i);
+          if ((k & hmask) == prefix) atomicAdd(&hist[(k >> shift) & 255], 1u);
+        }
       }
       __syncthreads();
-      if (threadIdx.x == 0) {
-        int64_t need = s_need, acc = 0;
-        int dsel = 0;
-        for (int dg = 255; dg >= 0; --dg) {
-          if (acc + hist[dg] >= need) {
-            dsel = dg;
-            break;
-          }
-          acc += hist[dg];
-        }
-        s_need = need - acc;
-        s_prefix = prefix | ((uint64_t)dsel << shift);
+      // bins in descending digit order: thread t < 256 holds bin 255 - t; the
+      // selected bin is the one where the running count first reaches `need`
+      const int hv = tid < 256 ? (int)hist[255 - tid] : 0;
+      int tot;
+      const int above = block_excl_scan_seed(hv, wsum, &tot);
+      const int64_t need = s_need;
+      __syncthreads();  // every thread has read s_need and s_prefix
+      if (tid < 256 && above < need && above + hv >= need) {
+        s_need = need - above;
+        s_prefix = prefix | ((uint64_t)(255 - tid) << shift);
       }
       __syncthreads();
     }
     thr = s_prefix;  // the M-th largest key
   }
-  // ordered compaction: contiguous index ranges per thread
-  int64_t per = (L + blockDim.x - 1) / blockDim.x;
-  int64_t b0 = threadIdx.x * per, b1 = b0 + per < L ? b0 + per : L;
+  // ordered compaction
   int c = 0;
-  for (int64_t i = b0; i < b1; ++i)
-    if (L <= a.M || make_key(dl[i], (uint32_t)i) >= thr) ++c;
-  s_cnt[threadIdx.x] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      int v = s_cnt[t];
-      s_cnt[t] = run;
-      run += v;
-    }
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < SEED_PER; ++q)
+      if (b0 + q < b1 && (L <= a.M || kr[q] >= thr)) ++c;
+  } else {
+    for (int64_t i = b0; i < b1; ++i)
+      if (L <= a.M || make_key(dl[i], (uint32_t)i) >= thr) ++c;
   }
-  __syncthreads();
-  int o = s_cnt[threadIdx.x];
-  for (int64_t i = b0; i < b1; ++i)
-    if (L <= a.M || make_key(dl[i], (uint32_t)i) >= thr) out[o++] = (int32_t)i;
-  int total = L < a.M ? (int)L : a.M;
-  for (int k = total + threadIdx.x; k < a.M; k += blockDim.x) out[k] = -1;
+  int tot;
+  int o = block_excl_scan_seed(c, wsum, &tot);
+  if (inreg) {
+#pragma unroll
+    for (int q = 0; q < SEED_PER; ++q)
+      if (b0 + q < b1 && (L <= a.M || kr[q] >= thr)) out[o++] = (int32_t)(b0 + q);
+  } else {
+    for (int64_t i = b0; i < b1; ++i)
+      if (L <= a.M || make_key(dl[i], (uint32_t)i) >= thr) out[o++] = (int32_t)i;
+  }
+  const int total = L < a.M ? (int)L : a.M;
+  for (int k = total + tid; k < a.M; k += SEED_THREADS) out[k] = -1;
 }
 
 __global__ void copy_f32_kernel(const float* src, float* dst, int64_t n) {
@@ -892,7 +933,7 @@ extern "C" int kvc_propagate(const kvc_shape* sh, const kvc_params* p, const voi
   const float* prev = rel0;
   for (int hop = 0; hop < p->n_hops; ++hop) {
     int32_t* sd = seeds ? seeds + (int64_t)hop * units * p->n_seeds : seed_tmp;
-    hipLaunchKernelGGL(seeds_kernel, dim3((unsigned)units), dim3(256), 0, st, a, prev, sd);
+    hipLaunchKernelGGL(seeds_kernel, dim3((unsigned)units), dim3(SEED_THREADS), 0, st, a, prev, sd);
     KVC_LAUNCH_CHECK("seeds");
     float* cur = dbuf + (int64_t)(hop & 1) * E;
     a.seeds = sd;
