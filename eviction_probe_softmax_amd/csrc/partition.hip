@@ -148,36 +148,46 @@ __global__ __launch_bounds__(256) void turning_kernel(PartArgs a) {
 // Tiles of 32 x 32 token pairs; the bf16 hidden states enter the MFMA as they
 // are (products exact, fp32 sums) and the two inverse norms scale the result.
 constexpr int BW = 128;   // band width = longest slot
+constexpr int GRAM_WAVES = 5;  // one 32x32 tile of the band each (5 tiles cover 128 diagonals + the block)
+constexpr int GRAM_UNROLL = 8; // 16-wide k steps whose loads are in flight together
 template <class T>
-__global__ __launch_bounds__(256) void gram_kernel(PartArgs a, float* G) {
+__global__ __launch_bounds__(GRAM_WAVES * 64) void gram_kernel(PartArgs a, float* G) {
   using namespace kvcmf;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // block = 32-row i-block; its 4 waves take j-blocks ib + wave .. (5 tiles cover the band)
+  // block = 32-row i-block; wave w takes the j-block ib + w
   const int64_t ib = blockIdx.x, dep = blockIdx.y;
   const int64_t i0 = ib * 32;
   if (i0 >= a.T) return;
   const T* H = (const T*)a.hidden + dep * a.dstride;
   const float* inv = a.inv + dep * a.T;
   G += dep * a.T * BW;
-  for (int jt = wave; jt < 5; jt += 4) {
-    const int64_t j0 = i0 + (int64_t)jt * 32;
-    if (j0 >= a.T) break;
-    kvc_f32x16 acc = {};
-    const int64_t ri = i0 + (lane & 31), rj = j0 + (lane & 31);
-    const bool vi = ri < a.T, vj = rj < a.T;
-    for (int c = 0; c < a.Dh; c += 16) {
-      int cc = c + 8 * (lane >> 5);
-      Frag<T> fa = vi ? load_frag<T>(H + ri * a.Dh + cc) : zero_frag<T>();
-      Frag<T> fb = vj ? load_frag<T>(H + rj * a.Dh + cc) : zero_frag<T>();
-      mma(acc, fa, fb);
-    }
-    // register v: row i = i0 + acc_row(v), column j = j0 + lane % 32
+  const int jt = wave;
+  const int64_t j0 = i0 + (int64_t)jt * 32;
+  if (j0 >= a.T) return;
+  kvc_f32x16 acc = {};
+  // rows past the end re-read the last row (in bounds); their products are never stored
+  const int64_t ri = min(i0 + (lane & 31), a.T - 1), rj = min(j0 + (lane & 31), a.T - 1);
+  const T* Hi = H + ri * a.Dh + 8 * (lane >> 5);
+  const T* Hj = H + rj * a.Dh + 8 * (lane >> 5);
+  int c = 0;
+  for (; c + 16 * GRAM_UNROLL <= a.Dh; c += 16 * GRAM_UNROLL) {
+    Frag<T> fa[GRAM_UNROLL], fb[GRAM_UNROLL];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      int64_t i = i0 + acc_row(v, lane), j = rj;
-      int64_t kk = j - i;
-      if (i < a.T && j < a.T && kk >= 0 && kk < BW) G[i * BW + kk] = acc[v] * inv[i] * inv[j];
+    for (int u = 0; u < GRAM_UNROLL; ++u) {
+      fa[u] = load_frag<T>(Hi + c + 16 * u);
+      fb[u] = load_frag<T>(Hj + c + 16 * u);
     }
+#pragma unroll
+    for (int u = 0; u < GRAM_UNROLL; ++u) mma(acc, fa[u], fb[u]);
+  }
+  for (; c < a.Dh; c += 16) mma(acc, load_frag<T>(Hi + c), load_frag<T>(Hj + c));
+  // register v: row i = i0 + acc_row(v), column j = j0 + lane % 32
+  const int64_t jj = j0 + (lane & 31);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t i = i0 + acc_row(v, lane);
+    const int64_t kk = jj - i;
+    if (i < a.T && jj < a.T && kk >= 0 && kk < BW) G[i * BW + kk] = acc[v] * inv[i] * inv[jj];
   }
 }
 
@@ -446,11 +456,11 @@ extern "C" int kvc_partition_ex(const kvc_shape* sh, const kvc_params* p, const 
       if (sh->dtype == KVC_BF16) {
         hipLaunchKernelGGL(norm_kernel<uint16_t>, gn, dim3(256), 0, st, a);
         hipLaunchKernelGGL(turning_kernel<uint16_t>, gt, dim3(256), 0, st, a);
-        hipLaunchKernelGGL(gram_kernel<uint16_t>, gg, dim3(256), 0, st, a, gband);
+        hipLaunchKernelGGL(gram_kernel<uint16_t>, gg, dim3(GRAM_WAVES * 64), 0, st, a, gband);
       } else {
         hipLaunchKernelGGL(norm_kernel<float>, gn, dim3(256), 0, st, a);
         hipLaunchKernelGGL(turning_kernel<float>, gt, dim3(256), 0, st, a);
-        hipLaunchKernelGGL(gram_kernel<float>, gg, dim3(256), 0, st, a, gband);
+        hipLaunchKernelGGL(gram_kernel<float>, gg, dim3(GRAM_WAVES * 64), 0, st, a, gband);
       }
       hipLaunchKernelGGL(band_prefix_kernel, dim3(kvc_blocks(sh->total_tokens * a.nd, 256)), dim3(256), 0, st, a,
                          gband);
