@@ -564,6 +564,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         const int st = nst[j], sz = nsz[j];
         float z = 0.f, zh = 0.f;
         if (lane < pd) {
+          #pragma unroll 8
           for (int i = st; i < st + sz; ++i) z += At[i * PA + lane];
           zh = nmu[j] * fast_exp2((LG[qq * LGS + lane] * a.c - lse_s[lane]) * 1.4426950408889634f);
         }
@@ -705,6 +706,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         const int j = coop_j(wave);
         const int st = nst[j], sz = nsz[j];
         float z = 0.f, as = 0.f;
+        #pragma unroll 8
         for (int i = st; i < st + sz; ++i) {
           float av = At[i * PA + lane];
           z += av;
@@ -754,6 +756,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         } else {
           Z = 0.f;
           as = 0.f;
+          #pragma unroll 8
           for (int i = st; i < st + sz; ++i) {
             float av = At[i * PA + lane];
             Z += av;
