@@ -578,17 +578,20 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     if (nint > 0) {
       const int nt = n32 / 32;
       if constexpr (STAGED) {
-        // centred values (zero rows past the slot) from the value chunks this
-        // thread has held since the value statistics: as two bf16 pieces for
-        // bf16 inputs (|v' - hi - lo| <= 2^-18 |v'|), in fp32 otherwise
-        static_assert(Lo::N32 == VR * VG, "staging reuses the value-statistics chunks");
+        // centred values (zero rows past the slot), re-read in the value-statistics
+        // chunk order (an L2 hit; holding them in registers across the error pass
+        // costs spills): as two bf16 pieces for bf16 inputs
+        // (|v' - hi - lo| <= 2^-18 |v'|), in fp32 otherwise
+        static_assert(Lo::N32 == VR * VG, "staging covers the value-statistics chunks");
         uint16_t* Vh = (uint16_t*)Vc;
         uint16_t* Vl = Vh + (size_t)Lo::N32 * Lo::VS;
 #pragma unroll
         for (int r = 0; r < VR; ++r) {
           const int i = vg + r * VG;
           float x[8];
-          vr[r].get(x);
+          Raw8<T> rl;
+          rl.load(Vg + (int64_t)min(i, n - 1) * D + vc);
+          rl.get(x);
 #pragma unroll
           for (int q = 0; q < 8; ++q) x[q] = i < n ? x[q] - vm[vc + q] : 0.f;
           if constexpr (sizeof(T) == 2) {
