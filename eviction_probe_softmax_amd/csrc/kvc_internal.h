@@ -126,6 +126,34 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// Lane exchanges on the VALU's data-parallel primitives (DPP) rather than LDS
+// permutes: quad_perm [1,0,3,2] and [2,3,0,1] (neighbours at distance 1 and 2),
+// row_half_mirror (lane i of each 8-lane group reads lane 7 - i), row_mirror
+// (lane i of each 16-lane row reads lane 15 - i). Each step adds a value that
+// is uniform over one half of a group to the other half's, so every lane of a
+// group ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// sum over aligned groups of W lanes (W = 2, 4, 8, 16 or 64), in every lane of the group
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 64, "group width");
+  if constexpr (W >= 2) v += dpp_f32<0xB1>(v);
+  if constexpr (W >= 4) v += dpp_f32<0x4E>(v);
+  if constexpr (W >= 8) v += dpp_f32<0x141>(v);
+  if constexpr (W >= 16) v += dpp_f32<0x140>(v);
+  if constexpr (W == 64) {
+    // the four row sums, read as wave-uniform scalars
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    v = (r0 + r1) + (r2 + r3);
+  }
+  return v;
+}
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

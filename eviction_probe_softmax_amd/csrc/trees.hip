@@ -362,8 +362,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         y0[e] = x0[e] * cs[e] + x1[e] * sn[e];   // rotation by -theta
         y1[e] = x1[e] * cs[e] - x0[e] * sn[e];
       }
-#pragma unroll
-      for (int o = 1; o < CH; o <<= 1) q += __shfl_xor(q, o, 64);
+      q = group_sum<CH>(q);
       if (ok) {
         float* d0 = Kt + (size_t)i * D + c;
         *(float4*)d0 = make_float4(y0[0], y0[1], y0[2], y0[3]);
@@ -414,14 +413,13 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         vr[r].get(x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) q = fmaf(x[e] - vmc[e], vmc[e], q);
-#pragma unroll
-        for (int o = 1; o < VC; o <<= 1) q += __shfl_xor(q, o, 64);
+        q = group_sum<VC>(q);
         if (i < n && (tid % VC) == 0) sdot[i] = q;
       }
       if (wave == 0) {
         float q = 0.f;
         for (int dd = lane; dd < D; dd += 64) q += vm[dd] * vm[dd];
-        q = wave_sum(q);
+        q = group_sum<64>(q);
         if (lane == 0) misc[0] = q;
       }
     }
@@ -504,8 +502,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
             kn += knorm[i];
           }
         }
-        float nrm2 = wave_sum(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
-        kn = __shfl(kn, 0, 64);
+        float nrm2 = group_sum<64>(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
+        kn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kn), 0));
         float coh = kn > 0.f ? sqrtf(nrm2) / kn : 1.f;
         float mu = fmaxf(1.f, (float)sz * coh);
         if (lane == 0) nmu[j] = mu;
@@ -568,7 +566,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           for (int i = st; i < st + sz; ++i) z += At[i * PA + lane];
           zh = nmu[j] * fast_exp2((LG[qq * LGS + lane] * a.c - lse_s[lane]) * 1.4426950408889634f);
         }
-        float eAn = wave_sum(fabsf(zh - z)), eAd = wave_sum(z);
+        float eAn = group_sum<64>(fabsf(zh - z)), eAd = group_sum<64>(z);
         if (lane == 0) nD[j] = eAd > 0.f ? eAn / eAd : 0.f;
       }
       __syncthreads();  // the next batch's keys overwrite these logits
@@ -772,8 +770,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
             qform_block(Gm, NG, At, rtok, lane, b * 8, st, sz, Z, al, ga, num, den);
         }
         den = den + 2.f * Z * as + Z * Z * mm;
-        float eVn = wave_sum(lane < pd ? sqrtf(fmaxf(num, 0.f)) : 0.f);
-        float eVd = wave_sum(lane < pd ? sqrtf(fmaxf(den, 0.f)) : 0.f);
+        float eVn = group_sum<64>(lane < pd ? sqrtf(fmaxf(num, 0.f)) : 0.f);
+        float eVd = group_sum<64>(lane < pd ? sqrtf(fmaxf(den, 0.f)) : 0.f);
         if (lane == 0) {
           float eA = nD[j];
           float eV = eVd > 0.f ? eVn / eVd : 0.f;
