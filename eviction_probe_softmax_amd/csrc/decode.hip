@@ -428,9 +428,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
     for (int j = 0; j < GP; ++j) {
       const bool ok = ek < n && 4 * half + j < G;
       const float z = ok ? sacc[j] * a.scale2 + bias : -INFINITY;
-      float mx = z;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      const float mx = group_max<32>(z);
       const float mn = fmaxf(m[j], mx);
       const float ea = fast_exp2(m[j] - mn), ep = fast_exp2(z - mn);
       const float alpha = mn == -INFINITY ? 1.f : ea;
@@ -442,7 +440,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 #pragma unroll
       for (int hh = 0; hh < (G + 3) / 4; ++hh) {
         if (4 * hh + j >= G) continue;
-        const float f = __shfl(alpha, hh * 32, 64);
+        const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), hh * 32));
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[4 * hh + j][q] *= f;
       }
@@ -484,10 +482,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
   // the lanes that share `sub`
 #pragma unroll
   for (int j = 0; j < GP; ++j) {
-    float t = lsum[j];
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) t += __shfl_xor(t, o, 64);
-    lsum[j] = t;
+    lsum[j] = group_sum<32>(lsum[j]);
   }
   if (col == 0) {
 #pragma unroll
@@ -502,8 +497,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       float x = acc[g][j];
+      if constexpr (LPE == 16) {
+        x = cross_row_sum(x);
+      } else {
 #pragma unroll
-      for (int o = LPE; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+        for (int o = LPE; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+      }
       if (es == 0) ow[wave][g][sub * 8 + j] = x;
     }
   __syncthreads();

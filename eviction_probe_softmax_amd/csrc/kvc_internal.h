@@ -126,31 +126,80 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
-// Lane exchanges on the VALU's data-parallel primitives (DPP) rather than LDS
-// permutes: quad_perm [1,0,3,2] and [2,3,0,1] (neighbours at distance 1 and 2),
-// row_half_mirror (lane i of each 8-lane group reads lane 7 - i), row_mirror
-// (lane i of each 16-lane row reads lane 15 - i). Each step adds a value that
-// is uniform over one half of a group to the other half's, so every lane of a
-// group ends with the same bits.
+// Lane exchanges on the VALU rather than LDS permutes. DPP: quad_perm [1,0,3,2]
+// and [2,3,0,1] (neighbours at distance 1 and 2), row_half_mirror (lane i of
+// each 8-lane group reads lane 7 - i), row_mirror (lane i of each 16-lane row
+// reads lane 15 - i). v_permlane16_swap / v_permlane32_swap with one register
+// as both operands leave, per lane, the values of rows {2k, 2k+1} (resp. the
+// two 32-lane halves) in the two results. Each step combines a value that is
+// uniform over one half of a group with the other half's, and the operations
+// used are commutative, so every lane of a group ends with the same bits.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-// sum over aligned groups of W lanes (W = 2, 4, 8, 16 or 64), in every lane of the group
+struct OpAdd {
+  static __device__ __forceinline__ float f(float x, float y) { return x + y; }
+};
+struct OpMax {
+  static __device__ __forceinline__ float f(float x, float y) { return fmaxf(x, y); }
+};
+// reduction over aligned groups of W lanes (W = 2, 4, ..., 64), in every lane
+// of the group; every lane of a group must be active (for W >= 32, the wave)
+template <int W, class Op>
+__device__ __forceinline__ float group_reduce(float v) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  if constexpr (W >= 2) v = Op::f(v, dpp_f32<0xB1>(v));
+  if constexpr (W >= 4) v = Op::f(v, dpp_f32<0x4E>(v));
+  if constexpr (W >= 8) v = Op::f(v, dpp_f32<0x141>(v));
+  if constexpr (W >= 16) v = Op::f(v, dpp_f32<0x140>(v));
+  if constexpr (W >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if constexpr (W >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = Op::f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
 template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-  static_assert(W == 2 || W == 4 || W == 8 || W == 16 || W == 64, "group width");
-  if constexpr (W >= 2) v += dpp_f32<0xB1>(v);
-  if constexpr (W >= 4) v += dpp_f32<0x4E>(v);
-  if constexpr (W >= 8) v += dpp_f32<0x141>(v);
-  if constexpr (W >= 16) v += dpp_f32<0x140>(v);
-  if constexpr (W == 64) {
-    // the four row sums, read as wave-uniform scalars
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    v = (r0 + r1) + (r2 + r3);
+__device__ __forceinline__ float group_sum(float v) { return group_reduce<W, OpAdd>(v); }
+template <int W>
+__device__ __forceinline__ float group_max(float v) { return group_reduce<W, OpMax>(v); }
+// sum over the lanes i, i ^ 16, i ^ 32, i ^ 48 (the four rows), in each of them
+__device__ __forceinline__ float cross_row_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
+}
+// minimum of a signed 64-bit value over the wave, in every lane (the same
+// exchanges on both 32-bit halves); the whole wave must be active
+template <int CTRL>
+__device__ __forceinline__ int64_t dpp_i64(int64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), CTRL, 0xF, 0xF, false);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ int64_t wave_min_i64(int64_t v) {
+  v = min(v, dpp_i64<0xB1>(v));
+  v = min(v, dpp_i64<0x4E>(v));
+  v = min(v, dpp_i64<0x141>(v));
+  v = min(v, dpp_i64<0x140>(v));
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
+    const auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const int64_t a = (int64_t)(((uint64_t)rh[0] << 32) | rl[0]), b = (int64_t)(((uint64_t)rh[1] << 32) | rl[1]);
+    v = min(a, b);
+  }
+  {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
+    const auto rl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto rh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const int64_t a = (int64_t)(((uint64_t)rh[0] << 32) | rl[0]), b = (int64_t)(((uint64_t)rh[1] << 32) | rl[1]);
+    v = min(a, b);
   }
   return v;
 }

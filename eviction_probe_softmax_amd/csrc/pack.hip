@@ -345,11 +345,8 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {  // the SPL partial sums, combined in a fixed order
-#pragma unroll
-        for (int o = 1; o < SPL; o <<= 1) {
-          s0[e] += __shfl_xor(s0[e], o, 64);
-          s1[e] += __shfl_xor(s1[e], o, 64);
-        }
+        s0[e] = group_sum<SPL>(s0[e]);
+        s1[e] = group_sum<SPL>(s1[e]);
       }
       if (sub != 0) continue;
       const int64_t prep = a0 + (nz - 1) / 2;
@@ -381,9 +378,7 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
         for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int o = 1; o < SPL; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+      for (int e = 0; e < 8; ++e) acc[e] = group_sum<SPL>(acc[e]);
       if (sub == 0) store8<T>(oV + d0, acc);
     }
   }

@@ -312,11 +312,7 @@ __global__ __launch_bounds__(1024) void dp_kernel(PartArgs a) {
           const int64_t key = v * 256 + (255 - c);
           best = key < best ? key : best;
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const int64_t other = __shfl_xor(best, o, 64);
-          best = other < best ? other : best;
-        }
+        best = wave_min_i64(best);
       }
       issue(j, e0 + (int64_t)DP_PF * step);  // this register set now serves a later step
       // no barrier before the writes: this step reads ends e0 - nmax .. e0 - 1
