@@ -239,8 +239,8 @@ def main():
     if not args.no_peaks:
         # the machine's own ceilings, measured before anything else is resident
         peaks = {"hbm_read_gbs": round(kvc.peak_read_gbs(), 1), "mfma_bf16_tflops": round(kvc.peak_mfma_tflops(), 1),
-                 "how": "kvc_peak_read: 2 GiB of nontemporal 16-byte loads; kvc_peak_mfma: register-only "
-                        "32x32x16 bf16 MFMA chains on every SIMD"}
+                 "how": "kvc_peak_read: 2 GiB of nontemporal 16-byte loads, each workgroup streaming one "
+                        "contiguous span; kvc_peak_mfma: register-only 32x32x16 bf16 MFMA chains on every SIMD"}
         print(f"[bench] measured peaks {peaks['hbm_read_gbs']} GB/s, {peaks['mfma_bf16_tflops']} TFLOP/s",
               file=sys.stderr, flush=True)
     t_gen = time.perf_counter()

@@ -1,6 +1,6 @@
-// Measurement helpers: the HBM read ceiling (nontemporal 16-byte loads) and
-// the bf16 MFMA ceiling (register-only MFMA chains) of the device, timed by
-// the caller.
+// Measurement helpers: the HBM read ceiling (nontemporal 16-byte loads, one
+// contiguous span a workgroup) and the bf16 MFMA ceiling (register-only MFMA
+// chains) of the device, timed by the caller.
 #include "kvc_internal.h"
 #include "kvc_peaks.h"
 
@@ -10,19 +10,22 @@ typedef unsigned int pk_u32x4 __attribute__((ext_vector_type(4)));
 constexpr int READ_THREADS = 256;
 constexpr int READ_UNROLL = 8;
 
+// each workgroup streams one contiguous span of the buffer (whole 128-byte
+// lines per load instruction, nontemporal)
 __global__ __launch_bounds__(READ_THREADS) void peak_read_kernel(const pk_u32x4* __restrict__ p, size_t n16,
-                                                                 uint32_t* sink) {
-  const size_t stride = (size_t)gridDim.x * READ_THREADS;
-  size_t i = (size_t)blockIdx.x * READ_THREADS + threadIdx.x;
+                                                                 size_t span, uint32_t* sink) {
+  const size_t b0 = (size_t)blockIdx.x * span;
+  const size_t b1 = b0 + span < n16 ? b0 + span : n16;
+  size_t i = b0 + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (READ_UNROLL - 1) * stride < n16; i += READ_UNROLL * stride) {
+  for (; i + (READ_UNROLL - 1) * READ_THREADS < b1; i += READ_UNROLL * READ_THREADS) {
     pk_u32x4 v[READ_UNROLL];
 #pragma unroll
-    for (int k = 0; k < READ_UNROLL; ++k) v[k] = __builtin_nontemporal_load(p + i + k * stride);
+    for (int k = 0; k < READ_UNROLL; ++k) v[k] = __builtin_nontemporal_load(p + i + k * READ_THREADS);
 #pragma unroll
     for (int k = 0; k < READ_UNROLL; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < b1; i += READ_THREADS) {
     const pk_u32x4 v = __builtin_nontemporal_load(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
@@ -69,8 +72,9 @@ extern "C" int kvc_peak_read(const void* buf, size_t bytes, int32_t grid, uint32
   KVC_REQUIRE(bytes > 0 && bytes % 16 == 0 && ((uintptr_t)buf & 15) == 0, KVC_E_INVAL,
               "kvc_peak_read: bytes and buf must be nonzero multiples of 16");
   KVC_REQUIRE(grid >= 1, KVC_E_INVAL, "kvc_peak_read: grid must be >= 1");
-  hipLaunchKernelGGL(peak_read_kernel, dim3((unsigned)grid), dim3(READ_THREADS), 0, st, (const pk_u32x4*)buf,
-                     bytes / 16, sink);
+  const size_t n16 = bytes / 16;
+  hipLaunchKernelGGL(peak_read_kernel, dim3((unsigned)grid), dim3(READ_THREADS), 0, st, (const pk_u32x4*)buf, n16,
+                     (n16 + (size_t)grid - 1) / (size_t)grid, sink);
   KVC_LAUNCH_CHECK("peak_read");
   return KVC_OK;
 }

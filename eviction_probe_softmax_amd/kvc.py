@@ -552,7 +552,7 @@ def _time_ms(launch, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def peak_read_gbs(nbytes=2 << 30, grid=8192, reps=10):
+def peak_read_gbs(nbytes=2 << 30, grid=16384, reps=10):
     """Measured HBM read ceiling (kvc_peak_read over nbytes of device memory), GB/s."""
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")

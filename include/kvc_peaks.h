@@ -18,8 +18,9 @@ extern "C" {
 #endif
 
 /* HBM read ceiling: one pass of 16-byte nontemporal loads over `bytes` of
- * device memory at `buf` (both multiples of 16), grid-strided over `grid`
- * workgroups of 256 threads, eight loads in flight per thread. The XOR of
+ * device memory at `buf` (both multiples of 16), cut into `grid` contiguous
+ * spans, one per workgroup of 256 threads (each load instruction covers
+ * whole 128-byte lines), eight loads in flight per thread. The XOR of
  * all words read is stored to *sink (device) only if it equals a fixed
  * constant, so no load can be dropped; the caller times the launch.
  * KVC_E_INVAL on NULL pointers, zero or misaligned sizes, grid < 1. */

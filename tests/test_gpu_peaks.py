@@ -8,7 +8,7 @@ pytestmark = pytest.mark.gpu
 
 def test_peak_read_and_mfma():
     from eviction_probe_softmax_amd import kvc
-    gbs = kvc.peak_read_gbs(nbytes=256 << 20, reps=5)
+    gbs = kvc.peak_read_gbs(nbytes=1 << 30, reps=5)
     tf = kvc.peak_mfma_tflops(grid=1024, iters=512, reps=3)
     print(f"[peaks] read {gbs:.0f} GB/s, bf16 MFMA {tf:.0f} TFLOP/s", flush=True)
     assert 1000 < gbs < 8500
