@@ -49,6 +49,24 @@ def test_end_to_end_matches_oracle(name, kw):
         check_kl(klv, xf, xc, inp["W"], o["kl"], name)
 
 
+@pytest.mark.parametrize("name,seed", [("stress", 2), ("stress", 5), ("ragged", 3), ("ragged", 6),
+                                       ("fulldepth", 4), ("mistral1", 7)])
+def test_end_to_end_other_seeds(name, seed):
+    """The same end-to-end bar on inputs drawn from other seeds."""
+    cfg = small_config(name)
+    inp = make_inputs(cfg, seed=seed)
+    print(f"[e2e-seed] {name} seed={seed}", flush=True)
+    out, xf, xc, klv = _run_gpu(cfg, inp)
+    o = oracle.run_pipeline(inp, cfg)
+    j = jaccard(as_np(out["taken"]), o["taken"])
+    assert j >= 0.99, j
+    assert np.array_equal(as_np(out["spent"]), o["spent"])
+    close(xf, o["x_full"], 2e-2, "x_full", floor=1e-3)
+    if j == 1.0:
+        close(xc, o["x_comp"], 2e-2, "x_comp", floor=1e-2)
+        check_kl(klv, xf, xc, inp["W"], o["kl"], name)
+
+
 @pytest.mark.parametrize("name", ["tiny", "stress", "ragged", "mistral1"])
 def test_full_budget_is_the_identity_on_gpu(name):
     cfg = small_config(name).replace(budget_ratio=1.0)
