@@ -84,36 +84,38 @@ def describe(cfg):
 
 
 def cpu_baseline(cfg):
-    """The oracle as it stands, on a bounded sample of the same workload: the
-    first 2048 tokens of one sequence, one layer, two KV heads, two decode
-    steps. Reported as tokens/s of the full job if its cost scaled with
-    (tokens x layers x KV heads)."""
-    import numpy as np
+    """The oracle as it stands, on bounded samples of the same workload: the
+    first 2048 tokens (384 when slots come from the DP) of one sequence, one
+    layer, one and then eight KV heads, two decode steps. The difference of the
+    two times is the per-(token, layer, KV head) cost; the rest is the
+    per-token cost of the parts that do not repeat per head (slot DP, vocab
+    projection). The full job is priced as per-unit cost x tokens x layers x
+    KV heads + per-token cost x tokens and reported as tokens/s."""
     import torch
     import oracle
     from workload import make_inputs
     # the oracle's DP evaluates every (end, length) cost in numpy: keep its
     # sample short when the workload cuts slots by DP
     n_tok = 384 if cfg.slot_len == 0 and not cfg.token_mode else 2048
-    sample = cfg.replace(S=1, Ly=1, H=2, lens=[min(n_tok, cfg.lens[0])], T_dec=2,
-                         n_plant=max(1, cfg.n_plant // 8))
-    inp = make_inputs(sample, device="cpu")
-    t0 = time.perf_counter()
-    oracle.run_pipeline(inp, sample)
-    dt = time.perf_counter() - t0
-    token_units = sample.lens[0] * sample.Ly * sample.H
-    per_token_unit = dt / token_units
-    full_units = cfg.Ly * cfg.H
-    value = 1.0 / (per_token_unit * full_units)
+    times = {}
+    for H in (1, 8):
+        sample = cfg.replace(S=1, Ly=1, H=H, lens=[min(n_tok, cfg.lens[0])], T_dec=2,
+                             n_plant=max(1, cfg.n_plant // 8))
+        inp = make_inputs(sample, device="cpu")
+        t0 = time.perf_counter()
+        oracle.run_pipeline(inp, sample)
+        times[H] = time.perf_counter() - t0
+    L = sample.lens[0]
+    per_unit = max(times[8] - times[1], 0.0) / (7 * L)           # s per (token, layer, KV head)
+    per_token = max(times[1] - L * per_unit, 0.0) / L              # s per token, once per sequence
+    t_full = per_unit * cfg.T * cfg.Ly * cfg.H + per_token * cfg.T
+    value = cfg.T / t_full
     cores = torch.get_num_threads()
-    try:
-        import numpy.__config__  # noqa: F401
-    except Exception:
-        pass
     return {"value": round(value, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"oracle pipeline (compress + 2 decode steps x 2 caches + KL) on {sample.lens[0]} tokens x "
-                       f"1 layer x 2 KV heads of the {cfg.name} workload in {dt:.1f} s; scaled by "
-                       f"token-units to {cfg.Ly} layers x {cfg.H} KV heads")}
+            "sample": (f"oracle pipeline (compress + 2 decode steps x 2 caches + KL) on {L} tokens x 1 layer x "
+                       f"1 and 8 KV heads of the {cfg.name} workload in {times[1]:.1f} s and {times[8]:.1f} s; "
+                       f"priced for {cfg.T} tokens x {cfg.Ly} layers x {cfg.H} KV heads as per-head-unit "
+                       f"cost x units + per-token cost x tokens")}
 
 
 def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
