@@ -1,15 +1,19 @@
 """Benchmark: one step = the whole hot path on one batch of synthetic input.
 
-Step = compress (probe scores, propagation, DP slots, prototype trees,
-floor + auction, pack) + T_dec decode steps over the full cache and over the
+Step = compress (probe scores, propagation, slots, prototype trees, floor +
+auction, pack) + T_dec decode steps over the full cache and over the
 compressed cache + per-step KL through the vocab projection. Inputs are
-generated on the GPU and resident in HBM before timing starts.
+generated on the GPU and resident in HBM before timing starts. The default
+workload is the ragged batch: 16 sequences of 2K-32K tokens, 32 layers x 8 KV
+heads, 25% budget, 256 decode steps.
 
-Prints ONE JSON line. `value` is whole-step throughput: cached tokens
-compressed (and decoded over) per second, T / step time. Phase times come from
-HIP events on the stream the library runs on; the decode figure is algorithmic
-bytes (every packed K/V byte, ln mu, appended tokens) per decode call divided by
-the call's event time.
+Prints ONE JSON line. `value` is KV tokens compressed per second, T / t_compress
+(t_compress: HIP events on the library's stream around the compression calls,
+median over the timed steps); whole-step throughput (T / step time) is
+reported beside it. The decode figures are algorithmic bytes (every packed K/V
+byte and ln mu, the appended tokens, the queries, each once) per decode call
+divided by the median event time of the calls over each cache; `roofline`
+is the call over the 25% cache.
 """
 from __future__ import annotations
 
@@ -30,18 +34,22 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="fulldepth")
+    ap.add_argument("--config", default="ragged")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-variants", action="store_true",
                     help="measure only the variants (one JSON object with a 'variants' key); for profiling")
-    ap.add_argument("--no-variants", action="store_true",
-                    help="skip the variant measurements beside the headline line (head-level hybrid, "
-                         "step-wise eviction)")
+    ap.add_argument("--variants", action="store_true",
+                    help="also measure the selection variants beside the headline line (head-level hybrid, "
+                         "slots from three depths, step-wise eviction, dense and A r propagation)")
+    ap.add_argument("--trace-summary", default=None, metavar="CSV",
+                    help="only summarize a rocprofv3 kernel_trace.csv of a bench run (per kernel, the decode "
+                         "kernels split by cache: the compressed cache's calls launch fewer workgroups), then exit")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring this GPU's own HBM read and bf16 MFMA ceilings (kvc_peak_read, "
                          "kvc_peak_mfma) before the timed steps")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_fulldepth_traffic.json"))
+    ap.add_argument("--traffic-json", default=None,
+                    help="HBM counter record of the decode call (default profiles/decode_<config>_traffic.json)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run five plain device-to-device copies of MIB MiB (to scale HBM byte "
                          "counters against a kernel of known traffic), then exit")
@@ -220,12 +228,59 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     return out
 
 
+def trace_summary(path):
+    """Per-kernel summary of a rocprofv3 kernel_trace.csv (one row a
+    dispatch): calls, total and mean microseconds, mean grid. The decode
+    kernels are split by cache: within one run the calls over the compressed
+    cache launch fewer workgroups than those over the full cache, so the
+    dispatches of each decode kernel fall into two grid sizes (per step; the
+    tail pieces grow with the step), and the smaller half is the compressed
+    cache's. Prints a markdown table."""
+    import csv
+    from collections import defaultdict
+    rows = list(csv.DictReader(open(path)))
+    key_start = "Start_Timestamp" if "Start_Timestamp" in rows[0] else "Start_Time"
+    key_end = "End_Timestamp" if "End_Timestamp" in rows[0] else "End_Time"
+    by = defaultdict(list)
+    for r in rows:
+        name = r["Kernel_Name"]
+        dur = (int(r[key_end]) - int(r[key_start])) / 1e3
+        grid = int(r.get("Grid_Size_X", r.get("Grid_Size", 0)) or 0)
+        by[name].append((int(r[key_start]), dur, grid))
+    out = defaultdict(list)
+    for name, lst in by.items():
+        short = name.replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0].strip()
+        if short.split("<")[0] in ("decode_mfma_kernel", "decode_partial_kernel", "decode_merge_kernel",
+                                   "decode_layersum_kernel"):
+            lst.sort()
+            # calls come in (full, compressed) pairs in every decode step
+            full, comp = lst[0::2], lst[1::2]
+            if comp and sum(g for _, _, g in comp) > sum(g for _, _, g in full):
+                full, comp = comp, full
+            out[short + " [full cache]"] += full
+            out[short + " [25% cache]"] += comp
+        else:
+            out[short or name] += lst
+    tot = sum(d for lst in by.values() for _, d, _ in lst)
+    print("| kernel | calls | total ms | mean us | median us | mean grid | % of kernel time |")
+    print("|---|---|---|---|---|---|---|")
+    for name, lst in sorted(out.items(), key=lambda kv: -sum(d for _, d, _ in kv[1])):
+        ds = sorted(d for _, d, _ in lst)
+        t = sum(ds)
+        med = ds[len(ds) // 2]
+        print(f"| {name} | {len(ds)} | {t / 1e3:.3f} | {t / len(ds):.2f} | {med:.2f} | "
+              f"{sum(g for _, _, g in lst) / len(lst):.0f} | {100 * t / tot:.1f} |")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -329,18 +384,18 @@ def main():
     q_bytes = units * cfg.G * d * elt
     bytes_comp = n_comp * (2 * d * elt + 4) + units * tail_mean * 2 * d * elt + q_bytes
     bytes_full = n_full * 2 * d * elt + units * tail_mean * 2 * d * elt + q_bytes
-    mean_comp_ms = float(np.mean(dcomp_ms))
-    mean_full_ms = float(np.mean(dfull_ms))
-    gbs_comp = bytes_comp / (mean_comp_ms * 1e-3) / 1e9
-    gbs_full = bytes_full / (mean_full_ms * 1e-3) / 1e9
-    # dominant kernel: decode over both caches (average bytes / average call)
-    ach = (bytes_comp + bytes_full) / ((mean_comp_ms + mean_full_ms) * 1e-3) / 1e9
-    traffic = measured_traffic(args.traffic_json, cfg.name)
+    med_comp_ms = float(np.median(dcomp_ms))
+    med_full_ms = float(np.median(dfull_ms))
+    gbs_comp = bytes_comp / (med_comp_ms * 1e-3) / 1e9
+    gbs_full = bytes_full / (med_full_ms * 1e-3) / 1e9
+    t_compress = float(np.median(comp_ms))
+    tpath = args.traffic_json or os.path.join(ROOT, "profiles", f"decode_{cfg.name}_traffic.json")
+    traffic = measured_traffic(tpath, cfg.name)
     klh = klv.detach().float().cpu().numpy()
     B, A, F = comp.pb.budgets()
     res = {
         "metric": "KV tokens compressed/sec + decode-attn HBM GB/s at 25% budget; mean KL",
-        "value": round(cfg.T / (ms_per_step / 1e3), 3),
+        "value": round(cfg.T / (t_compress / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -351,32 +406,35 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": describe(cfg), "seq_lens": cfg.lens if len(cfg.lens) <= 4 else None,
+        "config": {"workload": describe(cfg), "seq_lens": cfg.lens,
                    "budget_ratio": cfg.budget_ratio, "entries_budget": B, "decode_steps": Td,
                    "vocab": cfg.vocab},
-        "compress_ms": round(float(np.mean(comp_ms)), 3),
-        "compress_tokens_per_s": round(cfg.T / (float(np.mean(comp_ms)) / 1e3), 1),
-        "compress_entries_per_s": round(n_full / (float(np.mean(comp_ms)) / 1e3), 1),
-        "decode_ms_total": round(float(np.mean(dec_ms)), 3),
-        "decode_comp_ms_per_call": round(mean_comp_ms, 4),
-        "decode_full_ms_per_call": round(mean_full_ms, 4),
+        "compress_ms": round(t_compress, 3),
+        "compress_entries_per_s": round(n_full / (t_compress / 1e3), 1),
+        "step_tokens_per_s": round(cfg.T / (ms_per_step / 1e3), 1),
+        "decode_ms_per_step": round(float(np.median(dec_ms)), 3),
+        "decode_comp_ms_per_call": round(med_comp_ms, 4),
+        "decode_full_ms_per_call": round(med_full_ms, 4),
         "decode_hbm_gbps_25pct": round(gbs_comp, 1),
         "decode_hbm_gbps_full": round(gbs_full, 1),
         "packed_entries": n_comp,
         "full_entries": n_full,
-        "kl_ms": round(float(np.mean(kl_ms)), 3),
+        "kl_ms": round(float(np.median(kl_ms)), 3),
         "mean_kl": round(float(klh.mean()), 5),
         "max_kl": round(float(klh.max()), 5),
-        "roofline": {"bound": "hbm", "kernel": "decode call (decode_mfma pieces + decode_merge)",
-                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_call_comp": int(bytes_comp), "bytes_per_call_full": int(bytes_full)},
+        "roofline": {"bound": "hbm", "kernel": "decode call over the 25% cache (decode_mfma pieces + "
+                                               "decode_merge + decode_layersum)",
+                     "achieved": round(gbs_comp, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs_comp / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_call": int(bytes_comp), "ms_per_call": round(med_comp_ms, 4),
+                     "full_cache": {"achieved": round(gbs_full, 1), "frac": round(gbs_full / HBM_PEAK_GBS, 4),
+                                    "bytes_per_call": int(bytes_full), "ms_per_call": round(med_full_ms, 4)}},
         "measured_peaks": peaks,
     }
     if peaks:
         res["roofline"]["peak_measured"] = peaks["hbm_read_gbs"]
-        res["roofline"]["frac_measured"] = round(ach / peaks["hbm_read_gbs"], 4)
-    if not args.no_variants:
+        res["roofline"]["frac_measured"] = round(gbs_comp / peaks["hbm_read_gbs"], 4)
+    if args.variants:
         res["variants"] = measure_variants(cfg, inp, full, x_full, kl_op, stream)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on a CPU sample", file=sys.stderr, flush=True)

@@ -15,10 +15,10 @@
 // unit form pieces of their own after the segment pieces, computed from the
 // step's tail length. Each piece computes its G query heads' logits, a local
 // softmax and the weighted value sum, and writes (o[G][D], (max, sum)[G]).
-// The merge kernel combines the pieces of every unit into o, and the last
-// unit of an (s, h) to finish sums o over the layers, in layer order, into
-// x. The step is HBM-bound: every packed K and V byte is read once, 16 bytes
-// per lane.
+// The merge kernel combines the pieces of every unit into o; a third launch
+// sums o over the layers, in layer order, into x (the launch boundary is
+// what makes every unit's o visible to it). The step is HBM-bound: every
+// packed K and V byte is read once, 16 bytes per lane.
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -62,7 +62,6 @@ struct DecArgs {
   int32_t* n_pieces;  // [1] segment pieces in use (<= maxs)
   PieceRec* piece;    // [maxs]
   int2* upieces;      // [units] (first segment piece, segment pieces) of each unit
-  int32_t* cnt;       // [S*H] units of the (s, h) merged in this step (back to 0 after it)
   // results
   float* part_o;      // [maxs + units*ntp][G][D] value sums of each piece, scaled by 2^-max
   float2* part_ml;    // [maxs + units*ntp][G] (max of the base-2 logits, sum of 2^(z - max))
@@ -71,32 +70,14 @@ struct DecArgs {
   int64_t x_stride;
 };
 
-// Device-scope atomic stores and loads: performed at the device's coherence
-// point rather than in one XCD's L2, so a value stored by one workgroup is
-// seen by another of the same launch without an L2 writeback or invalidate.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// every memory operation of this wave has completed (and the compiler keeps
-// memory operations on their side of this point)
-__device__ __forceinline__ void drain() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // The plan: pieces per unit (ceil(len / chunk), the length split evenly, the
 // first len % np pieces one entry longer), an exclusive scan over the units
 // (rounds of PLAN_THREADS * per units), one record per piece, each unit's
-// piece range, the number of pieces, and the merge counters at zero.
+// piece range and the number of pieces.
 __global__ __launch_bounds__(PLAN_THREADS) void decode_plan_kernel(DecArgs a) {
   __shared__ int wsum[PLAN_THREADS / 64];
   const int units = a.S * a.Ly * a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < a.S * a.H; i += PLAN_THREADS) a.cnt[i] = 0;
   const int per = min(PLAN_PER, (units + PLAN_THREADS - 1) / PLAN_THREADS);
   int carry = 0;
   for (int base = 0; base < units; base += PLAN_THREADS * per) {
@@ -536,11 +517,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 // pieces, then its tail pieces) are dealt to the waves, each wave loads its
 // MRG_NPW pieces of a batch together and merges them online (lane = OPL
 // consecutive outputs of one head), the waves are combined through LDS and o
-// is normalized. The unit then counts itself in for its (s, h); the last unit
-// of the (s, h) writes x as the layer sum, in layer order, and sets the
-// counter back to zero. The merged o crosses workgroups through device-scope
-// atomic stores and loads, and a workgroup waits until its stores have
-// completed before it counts itself in.
+// is normalized and stored. The layer sum reads it in the next launch.
 template <int D, int G>
 __global__ __launch_bounds__(mrg_waves<G>() * 64) void decode_merge_kernel(DecArgs a) {
   constexpr int GD = G * D;
@@ -549,7 +526,6 @@ __global__ __launch_bounds__(mrg_waves<G>() * 64) void decode_merge_kernel(DecAr
   constexpr int NT = MRG_WAVES * 64;
   __shared__ float accs[MRG_WAVES][GD];
   __shared__ float msw[MRG_WAVES][G], lsw[MRG_WAVES][G];
-  __shared__ int last;
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int2 up = a.upieces[u];
@@ -611,23 +587,25 @@ __global__ __launch_bounds__(mrg_waves<G>() * 64) void decode_merge_kernel(DecAr
         num += accs[w][i] * f;
         den += lsw[w][gg] * f;
       }
-    st_dev(a.o + (int64_t)u * GD + i, den > 0.f ? num / den : 0.f);
+    a.o[(int64_t)u * GD + i] = den > 0.f ? num / den : 0.f;
   }
-  drain();
-  __syncthreads();
-  const int s = u / (a.Ly * a.H), h = u % a.H;
-  if (tid == 0) last = atomicAdd(&a.cnt[s * a.H + h], 1) == a.Ly - 1;
-  __syncthreads();
-  if (!last) return;
-  if (tid == 0) __hip_atomic_store(&a.cnt[s * a.H + h], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const int64_t lstride = (int64_t)a.H * GD;
-  for (int i = tid; i < GD; i += NT) {
-    const float* os = a.o + ((int64_t)s * a.Ly * a.H + h) * GD + i;
-    float xs = 0.f;
+}
+
+// x[s][h*G*D + i] = sum over l, in layer order, of o[s][l][h][i]: one thread
+// an output, LS_THREADS outputs a workgroup, the layers' loads unrolled so
+// they are all in flight together.
+constexpr int LS_THREADS = 128;
+__global__ __launch_bounds__(LS_THREADS) void decode_layersum_kernel(DecArgs a, int gd) {
+  const int64_t i = (int64_t)blockIdx.x * LS_THREADS + threadIdx.x;
+  const int64_t per_s = (int64_t)a.H * gd;
+  if (i >= (int64_t)a.S * per_s) return;
+  const int s = (int)(i / per_s);
+  const int64_t r = i % per_s;
+  const float* os = a.o + (int64_t)s * a.Ly * per_s + r;
+  float xs = 0.f;
 #pragma unroll 32
-    for (int l = 0; l < a.Ly; ++l) xs += ld_dev(os + l * lstride);
-    a.x[(int64_t)s * a.x_stride + (int64_t)h * GD + i] = xs;
-  }
+  for (int l = 0; l < a.Ly; ++l) xs += os[l * per_s];
+  a.x[(int64_t)s * a.x_stride + r] = xs;
 }
 
 int64_t units_of(const kvc_ragged* c) { return (int64_t)c->n_seq * c->n_layers * c->n_kv_heads; }
@@ -641,7 +619,6 @@ struct DecWs {
   int32_t* n_pieces;
   PieceRec* piece;
   int2* upieces;
-  int32_t* cnt;
   float* part_o;
   float2* part_ml;
   float* obuf;
@@ -657,7 +634,6 @@ DecWs carve_dec(kvc::Carver& cv, const kvc_ragged* c, int32_t group, int32_t t_c
   w.n_pieces = cv.take<int32_t>(1);
   w.piece = cv.take<PieceRec>((size_t)(maxs > 0 ? maxs : 1));
   w.upieces = cv.take<int2>((size_t)units);
-  w.cnt = cv.take<int32_t>((size_t)c->n_seq * c->n_kv_heads);
   w.part_o = cv.take<float>((size_t)(np * gd));
   w.part_ml = cv.take<float2>((size_t)(np * group));
   w.obuf = cv.take<float>((size_t)(units * gd));
@@ -705,7 +681,6 @@ DecArgs make_args(const kvc_ragged* c, int32_t group, int32_t t_valid, int32_t t
   a.n_pieces = w.n_pieces;
   a.piece = w.piece;
   a.upieces = w.upieces;
-  a.cnt = w.cnt;
   a.part_o = w.part_o;
   a.part_ml = w.part_ml;
   return a;
@@ -783,6 +758,10 @@ extern "C" int kvc_decode_attn_planned(const kvc_ragged* c, const void* K_tail, 
   const dim3 mgrid((unsigned)units_of(c));
   if (d == 128) { KVC_DEC_G(KVC_MRG, 128); } else { KVC_DEC_G(KVC_MRG, 64); }
   KVC_LAUNCH_CHECK("decode_merge");
+  const int gd = group * d;
+  const int64_t nx = (int64_t)c->n_seq * c->n_kv_heads * gd;
+  hipLaunchKernelGGL(decode_layersum_kernel, dim3(kvc_blocks(nx, LS_THREADS)), dim3(LS_THREADS), 0, st, a, gd);
+  KVC_LAUNCH_CHECK("decode_layersum");
 #undef KVC_DEC_G
 #undef KVC_MRG
 #undef KVC_DECM
@@ -801,3 +780,4 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
   return kvc_decode_attn_planned(c, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, o_out, ws, ws_bytes,
                                  st);
 }
+

@@ -105,6 +105,10 @@ CONFIGS = {
     "stress": Config(name="stress", S=4, Ly=32, H=8, G=4, d=128, lens=[32768] * 4,
                      budget_ratio=1.0 / 128, slot_len=64, T_dec=128, vocab=32768,
                      plant="chains", n_plant=8, span_len=(4, 8), seed=1003),
+    # The same stress inputs at a budget of 12.5%.
+    "stress8": Config(name="stress8", S=4, Ly=32, H=8, G=4, d=128, lens=[32768] * 4,
+                      budget_ratio=1.0 / 8, slot_len=64, T_dec=128, vocab=32768,
+                      plant="chains", n_plant=8, span_len=(4, 8), seed=1003),
     # Ragged batch of 16 sequences, exact prompt/recent/suffix regions.
     "ragged": Config(name="ragged", S=16, Ly=32, H=8, G=4, d=128,
                      lens=_ragged_lens(16, 2048, 32768, 1004),
@@ -133,6 +137,8 @@ def small_config(name: str, **kw) -> Config:
     elif name == "stress":
         c = base.replace(S=2, Ly=2, H=2, lens=[600, 433], T_dec=2, vocab=1024,
                          n_plant=3, budget_ratio=1.0 / 8)
+    elif name == "stress8":
+        c = base.replace(S=2, Ly=2, H=2, lens=[600, 433], T_dec=2, vocab=1024, n_plant=3)
     elif name == "ragged":
         c = base.replace(S=3, Ly=2, H=2, lens=[1100, 777, 900], T_dec=2, vocab=1024,
                          n_plant=6, prompt_exact=64, recent_exact=32, suffix_exact=48)
