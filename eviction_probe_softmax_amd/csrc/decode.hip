@@ -20,6 +20,8 @@
 // what makes every unit's o visible to it). The step is HBM-bound: every
 // packed K and V byte is read once, 16 bytes per lane.
 #include <cmath>
+#include <mutex>
+#include <string>
 
 #include "kvc_internal.h"
 #include "mfma_frag.h"
@@ -781,3 +783,53 @@ extern "C" int kvc_decode_attn(const kvc_ragged* c, const void* K_tail, const vo
                                  st);
 }
 
+// ------------------------------------------------------------------ no-allocation entry point
+// For callers that cannot allocate device memory: the workspace of one decode
+// step lives in a file-scope device array, one copy per GPU in the library's
+// code object, held until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// the device address comes from hipGetSymbolAddress, taken once per device on
+// the first call with that device current, and is used for every launch.
+namespace {
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr int MAX_DEVICES = 64;
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  KVC_REQUIRE(e == hipSuccess, KVC_E_HIP, std::string("kvc_decode_attn_static: hipGetDevice: ") + hipGetErrorString(e));
+  KVC_REQUIRE(dev >= 0 && dev < MAX_DEVICES, KVC_E_UNSUPPORTED, "kvc_decode_attn_static: device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    KVC_REQUIRE(e == hipSuccess && p != nullptr, KVC_E_HIP,
+                std::string("kvc_decode_attn_static: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+}  // namespace
+
+extern "C" size_t kvc_decode_static_limit(void) { return STATIC_SCRATCH_BYTES; }
+
+extern "C" int kvc_decode_attn_static(const kvc_ragged* c, const void* K_tail, const void* V_tail, int32_t t_valid,
+                                      int32_t t_cap, const void* Q, int32_t group, float* x_out, int64_t x_stride,
+                                      float* o_out, hipStream_t st) {
+  KVC_REQUIRE(c != nullptr, KVC_E_INVAL, "cache is NULL");
+  const size_t need = kvc_decode_workspace(c, group, t_cap);
+  KVC_REQUIRE(need > 0, KVC_E_INVAL, "kvc_decode_attn_static: bad cache description, group or t_cap");
+  if (need > STATIC_SCRATCH_BYTES)
+    return kvc::set_error(KVC_E_WORKSPACE, "kvc_decode_attn_static: this cache and t_cap need " + std::to_string(need) +
+                                          " bytes of scratch, above the " + std::to_string(STATIC_SCRATCH_BYTES) +
+                                          " the library holds per GPU; call kvc_decode_attn with a workspace");
+  void* ws = nullptr;
+  const int rc = scratch_of_current_device(&ws);
+  if (rc != KVC_OK) return rc;
+  return kvc_decode_attn(c, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, o_out, ws,
+                         STATIC_SCRATCH_BYTES, st);
+}

@@ -33,6 +33,7 @@ EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets"
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
            "kvc_partition", "kvc_partition_ex", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
            "kvc_decode_workspace", "kvc_decode_plan", "kvc_decode_attn", "kvc_decode_attn_planned",
+           "kvc_decode_static_limit", "kvc_decode_attn_static",
            "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
            "kvc_step_workspace", "kvc_step_init", "kvc_step_append", "kvc_step_prune",
            "kvc_propagate_dense_workspace", "kvc_propagate_dense", "kvc_propagate_ar_workspace",
@@ -115,6 +116,9 @@ _sig = {
     "kvc_decode_attn_planned": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
                                   C.c_int64, _P, _P, C.c_size_t, _P]),
     "kvc_decode_plan": (C.c_int, [C.POINTER(Ragged), C.c_int32, C.c_int32, _P, C.c_size_t, _P]),
+    "kvc_decode_static_limit": (C.c_size_t, []),
+    "kvc_decode_attn_static": (C.c_int, [C.POINTER(Ragged), _P, _P, C.c_int32, C.c_int32, _P, C.c_int32, _P,
+                                         C.c_int64, _P, _P]),
     "kvc_step_capacity": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.c_int32, _P]),
     "kvc_step_workspace": (C.c_size_t, [C.POINTER(Shape), C.POINTER(Params), C.c_int64]),
     "kvc_step_init": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Policy),
@@ -445,6 +449,20 @@ def decode_attn(cache, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride
     st = _lib.kvc_decode_attn(C.byref(rs), _ptr(K_tail), _ptr(V_tail), t_valid, t_cap, _ptr(Q), group, _ptr(x_out),
                               x_stride, _ptr(o_out), _ptr(ws), ws.numel(), _stream())
     _check("kvc_decode_attn", st)
+
+
+def decode_static_limit() -> int:
+    """Bytes of the per-GPU scratch array behind decode_attn_static."""
+    return int(_lib.kvc_decode_static_limit())
+
+
+def decode_attn_static(cache, K_tail, V_tail, t_valid, t_cap, Q, group, x_out, x_stride, o_out=None):
+    """One step through the entry point that allocates nothing (its workspace
+    is the library's per-GPU scratch array; calls on one GPU must not overlap)."""
+    rs = _ragged_struct(cache)
+    st = _lib.kvc_decode_attn_static(C.byref(rs), _ptr(K_tail), _ptr(V_tail), t_valid, t_cap, _ptr(Q), group,
+                                     _ptr(x_out), x_stride, _ptr(o_out), _stream())
+    _check("kvc_decode_attn_static", st)
 
 
 class KL:

@@ -4,7 +4,8 @@
  * C ABI. Every entry point takes plain host/device pointers and sizes and is
  * asynchronous on the caller's HIP stream: arguments are validated on the host
  * before anything is launched, the library never synchronizes the device, and
- * it keeps no device memory or state between calls. The caller owns every
+ * it keeps no device memory or state between calls (one exception:
+ * kvc_decode_attn_static's per-GPU scratch array). The caller owns every
  * buffer, including a scratch workspace whose size the matching
  * kvc_*_workspace query returns. On an error return nothing was launched,
  * except KVC_E_HIP (a launch failed: outputs are undefined). kvc_last_error()
@@ -341,6 +342,21 @@ int kvc_decode_attn_planned(const kvc_ragged* cache, const void* K_tail, const v
                             int32_t t_valid, int32_t t_cap, const void* Q, int32_t group,
                             float* x_out, int64_t x_stride, float* o_out, void* ws,
                             size_t ws_bytes, hipStream_t stream);
+
+/* kvc_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as kvc_decode_attn (plan and step in one call)
+ * without a workspace: the step's workspace is a 64 MiB array in the
+ * library's device code, one copy per GPU, held from the first call on that
+ * GPU until the process ends. Returns KVC_E_WORKSPACE (nothing launched) when
+ * kvc_decode_workspace(cache, group, t_cap) exceeds kvc_decode_static_limit().
+ * Calls on one GPU share that array: calls that overlap on one GPU (two
+ * streams, two host threads) race and give undefined results. The stream
+ * must belong to the current device. Allocates nothing. */
+size_t kvc_decode_static_limit(void);
+int kvc_decode_attn_static(const kvc_ragged* cache, const void* K_tail, const void* V_tail,
+                           int32_t t_valid, int32_t t_cap, const void* Q, int32_t group,
+                           float* x_out, int64_t x_stride, float* o_out, hipStream_t stream);
 
 /* ------------------------------------------------------------------ A9
  * kvc_kl: per-row KL(full || compressed) through a vocab projection.
