@@ -19,14 +19,15 @@ Conventions
   (documented in include/kvc.h) and loop over (sequence, layer, KV head) units.
 
 Parity status of each function is stated in its docstring; every function
-is pinned by a CPU test in tests/test_oracle_pins.py unless it says
-"parity unpinned".
+is pinned by a CPU test in tests/test_oracle_pins.py or
+tests/test_oracle_pins_slips.py (the latter also plants plausible slips in the
+oracle and checks that the pin fails) unless it says "parity unpinned".
 """
 from .common import (regions, budgets, rope, rope_inv, to64, bf16_round,  # noqa: F401
                      round_to)
 from .score import probe_scores  # noqa: F401
 from .propagate import propagate  # noqa: F401
-from .partition import (turning_scores, slot_costs, dp_slots, fixed_slots,  # noqa: F401
+from .partition import (turning_score, slot_costs, dp_slots, fixed_slots,  # noqa: F401
                         slots_for)
 from .trees import build_trees, tree_nodes  # noqa: F401
 from .select import floor_select, auction, token_topk  # noqa: F401

@@ -40,6 +40,26 @@ def _frontier(nodes, taken, base):
     return out
 
 
+def prototype_entry(Ku, Vu, r, a, m, rel, mu, cfg):
+    """The packed entry of an internal frontier node covering positions
+    [a, a + m) of one (sequence, layer, KV head) ('Inside one cache entry'):
+    keys inverse-rotated, averaged and re-rotated at p_rep = a + (m-1)//2;
+    value weights (1 - beta) r_i / rel + beta / m (uniform when rel = 0);
+    key and value rounded to the cache dtype; ln(mu) as fp32.
+    Returns (k, v, lnmu, p_rep)."""
+    beta = float(np.float32(cfg.value_base))
+    pos = np.arange(a, a + m, dtype=np.float64)
+    kt = rope_inv(Ku[a:a + m], pos, cfg.rope_base).mean(axis=0)
+    prep = a + (m - 1) // 2
+    kh = rope(kt, prep, cfg.rope_base)
+    if rel > 0:
+        w = (1.0 - beta) * r[a:a + m] / rel + beta / m
+    else:
+        w = np.full(m, 1.0 / m)
+    vh = w @ Vu[a:a + m]
+    return round_to(kh, cfg.dtype), round_to(vh, cfg.dtype), float(np.float32(np.log(mu))), prep
+
+
 def pack(K, V, rel_tok, trees, taken, cu, slots, cfg):
     """K, V: [Ly][H][T][d]; rel_tok float32 [Ly][H][T]; trees: dict with
     float32 node_rel/node_mu [Ly][H][2T]; taken: uint8 op_taken [Ly][H][2T]
@@ -50,7 +70,6 @@ def pack(K, V, rel_tok, trees, taken, cu, slots, cfg):
     """
     Ly, H, T, d = K.shape
     S = len(cu) - 1
-    beta = float(np.float32(cfg.value_base))
     Ks, Vs, lm, ps = [], [], [], []
     seg_off = np.zeros((S, Ly, H), dtype=np.int64)
     seg_len = np.zeros((S, Ly, H), dtype=np.int32)
@@ -88,17 +107,7 @@ def pack(K, V, rel_tok, trees, taken, cu, slots, cfg):
                                 continue
                             rel = float(trees["node_rel"][l, h, nb[1] + j])
                             mu = float(trees["node_mu"][l, h, nb[1] + j])
-                            pos = np.arange(a, a + m, dtype=np.float64)
-                            kt = rope_inv(Ku[a:a + m], pos, cfg.rope_base).mean(axis=0)
-                            prep = a + (m - 1) // 2
-                            kh = rope(kt, prep, cfg.rope_base)
-                            if rel > 0:
-                                w = (1.0 - beta) * r[a:a + m] / rel + beta / m
-                            else:
-                                w = np.full(m, 1.0 / m)
-                            vh = w @ Vu[a:a + m]
-                            ents.append((round_to(kh, cfg.dtype), round_to(vh, cfg.dtype),
-                                         float(np.float32(np.log(mu))), prep))
+                            ents.append(prototype_entry(Ku, Vu, r, a, m, rel, mu, cfg))
                 for i in range(c1, L):
                     tok(i)
                 seg_off[s, l, h] = n_tot

@@ -67,23 +67,11 @@ def turning_values(hn: np.ndarray, b: int) -> list:
     return vals
 
 
-def turning_scores(hn: np.ndarray) -> np.ndarray:
-    """kappa_b for every position b of one sequence (float64)."""
-    L = hn.shape[0]
-    kap = np.zeros(L)
-    for b in range(L):
-        vals = []
-        for w in WINDOWS:
-            if b - w < 0 or b + w > L - 1:
-                continue
-            u = hn[b] - hn[b - w]
-            v = hn[b + w] - hn[b]
-            nu, nv = np.linalg.norm(u), np.linalg.norm(v)
-            if nu == 0 or nv == 0:
-                continue
-            vals.append((1.0 - float(u @ v) / (nu * nv)) / 2.0)
-        kap[b] = float(np.mean(vals)) if vals else 0.0
-    return kap
+def turning_score(hn: np.ndarray, b: int) -> float:
+    """kappa_b of one trajectory: the mean of its valid window values, 0 if
+    there are none."""
+    vals = turning_values(hn, b)
+    return float(np.mean(vals)) if vals else 0.0
 
 
 def slot_cost(hn: np.ndarray, a: int, n: int, cfg) -> float:

@@ -114,10 +114,36 @@ def _slot(ktil, knorm, V, r, Ad, Qd, lse_d, a, n, pos0, cfg, rope_base):
 
 
 def dprobe_rows(cfg):
+    """Probe rows of the distortion: P_d = min(n_dprobe, G*P) rows, every
+    (G*P // P_d)-th row index rho = g*P + p starting at 0."""
     R = cfg.G * cfg.P
     Pd = min(cfg.n_dprobe, R)
     stride = R // Pd
     return np.arange(0, R, stride)[:Pd]
+
+
+def op_utilities(nodes, rel, D, sens):
+    """Operations of one slot and their utilities ('04 Top-down budget flow':
+    relevance x fidelity gain x head sensitivity per new physical entry).
+
+    Returns (util, cost) over the slot's 2n op indices: op 0 = Add(slot),
+    op 1 + j = Split(node j) for internal j (cost 0 marks "no such op": the
+    leaves). Gains: Add covers the absent slot with its root, so it gains
+    rel_root (1 - D_root) (an absent slot counts as D = 1); Split(j) replaces
+    node j by its children and gains rel_j D_j - sum_c rel_c D_c; every op
+    adds (children - 1) = 1 entry. util = fp32(sens * gain / cost)."""
+    m = len(nodes)
+    util = np.zeros(m + 1, dtype=np.float32)
+    cost = np.zeros(m + 1, dtype=np.uint8)
+    util[0] = np.float32(sens * (rel[0] * (1.0 - D[0])))
+    cost[0] = 1
+    for j, (_, _, lc, rc) in enumerate(nodes):
+        if lc < 0:
+            continue
+        gain = rel[j] * D[j] - (rel[lc] * D[lc] + rel[rc] * D[rc])
+        util[1 + j] = np.float32(sens * gain / 1.0)
+        cost[1 + j] = 1
+    return util, cost
 
 
 def build_trees(K, V, Qp, lse, rel_tok, head_sens, cu, slots, cfg, keep_protos=False):
@@ -164,15 +190,9 @@ def build_trees(K, V, Qp, lse, rel_tok, head_sens, cu, slots, cfg, keep_protos=F
                     node_rel[l, h, base:base + m] = rel
                     node_D[l, h, base:base + m] = D
                     node_mu[l, h, base:base + m] = mu
-                    # Add(slot): covers an absent slot with its root
-                    op_util[l, h, base] = np.float32(sens * (rel[0] * (1.0 - D[0])))
-                    op_cost[l, h, base] = 1
-                    for j, (_, _, lc, rc) in enumerate(nodes):
-                        if lc < 0:
-                            continue
-                        gain = rel[j] * D[j] - (rel[lc] * D[lc] + rel[rc] * D[rc])
-                        op_util[l, h, base + 1 + j] = np.float32(sens * gain / 1.0)
-                        op_cost[l, h, base + 1 + j] = 1
+                    u, cst = op_utilities(nodes, rel, D, sens)
+                    op_util[l, h, base:base + m + 1] = u
+                    op_cost[l, h, base:base + m + 1] = cst
                     if keep_protos:
                         protos[(s, l, h, st)] = {"nodes": nodes, "khat": kh, "vhat": vh,
                                                  "mu": mu, "rel": rel, "D": D}

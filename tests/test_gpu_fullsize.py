@@ -98,10 +98,9 @@ def test_fullsize_dp_costs_sampled(run):
         got = int(gq[e - 1, n - cfg.slot_min])
         worst = max(worst, abs(got - want) / max(abs(want), 1))
         assert abs(got - want) <= 1e-4 * abs(want) + 64, (e, n, got, want)
-    kap = opart.turning_scores(hn)
     lam = float(np.float32(cfg.lambda_curv))
     for c in rng.integers(c0, c1, size=300):
-        want = opart._q(lam * kap[int(c)])
+        want = opart._q(lam * opart.turning_score(hn, int(c)))
         assert abs(int(gk[int(c)]) - want) <= 1e-4 * (1 << 22) + 64, (int(c), int(gk[int(c)]), want)
     slots = slots_from_dev(out["slot_start"], out["n_slots"])[0]
     assert slots[0][0] == c0 and slots[-1][0] + slots[-1][1] == c1
