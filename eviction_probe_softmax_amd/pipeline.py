@@ -93,12 +93,14 @@ def _row_view(x, t):
     return _RowView(x, t)
 
 
-def run_stepwise(cfg, inp, policy, record=None):
+def run_stepwise(cfg, inp, policy, record=None, kept_trace=None):
     """Step-wise eviction over the decode steps (DistillCache paper,
     Algorithm 1): prune the prefill cache once, then per step append the new
     pair, decode over the student, prune; the full cache is decoded beside it
     and the per-step KL compares the two. ``record`` (a list) receives HIP
-    event pairs (init, per-step prune) on the library's stream."""
+    event pairs (init, per-step prune) on the library's stream;
+    ``kept_trace`` (a list) receives (step, kept positions per sequence)
+    after every prune (step -1: the prefill prune; this synchronizes)."""
     pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
     sw = kvc.Stepwise(pb, policy, cfg.T_dec, inp["K"].dtype, cfg.G)
     stream = torch.cuda.current_stream()
@@ -112,6 +114,17 @@ def run_stepwise(cfg, inp, policy, record=None):
     sw.init(inp["K"], inp["V"], inp["Qctx"])
     if record is not None:
         record.append(("init", e0, ev()))
+
+    def trace_kept(step):
+        pos = sw.pos.cpu()
+        kept, off = [], 0
+        for s in range(cfg.S):
+            kept.append(pos[off:off + sw.lengths[s]].numpy().copy())
+            off += sw.caps[s]
+        kept_trace.append((step, kept))
+
+    if kept_trace is not None:
+        trace_kept(-1)
     full = kvc.full_view(pb, inp["K"], inp["V"])
     dfull = kvc.Decoder(full, cfg.G, cfg.T_dec)
     S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
@@ -127,6 +140,8 @@ def run_stepwise(cfg, inp, policy, record=None):
         sw.prune(t)
         if record is not None:
             record.append(("step", e0, e1, ev()))
+        if kept_trace is not None:
+            trace_kept(t)
     klv = kvc.kl(x_full.reshape(S * Td, Dm), x_comp.reshape(S * Td, Dm), inp["W"]).reshape(S, Td)
     pos = sw.pos.cpu()
     kept, off = [], 0

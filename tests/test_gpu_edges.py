@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from workload import small_config, make_inputs
-from parity import close, as_np, inputs_to, jaccard, to_dev, slots_to_dev, check_kl
+from parity import close, as_np, inputs_to, jaccard, to_dev, slots_to_dev, check_kl, oracle_on_taken
 
 pytestmark = pytest.mark.gpu
 
@@ -49,8 +49,10 @@ def test_degenerate_lengths_end_to_end(base, lens):
     j = jaccard(as_np(out["taken"]), o["taken"])
     assert j >= 0.99, j
     close(xf, o["x_full"], 2e-2, "x_full", floor=1e-3)
-    close(xc, o["x_comp"], 2e-2, "x_comp", floor=1e-3)
-    check_kl(klv, xf, xc, inp["W"], o["kl"], base)
+    # against the oracle's decode and KL of the GPU's own taken set
+    xc_o, kl_o = oracle_on_taken(inp, cfg, o, out["taken"])
+    close(xc, xc_o, 2e-2, "x_comp", floor=1e-3)
+    check_kl(klv, xf, xc, inp["W"], kl_o, base, o["x_full"], xc_o)
 
 
 def test_empty_budget_keeps_nothing():
@@ -62,7 +64,7 @@ def test_empty_budget_keeps_nothing():
     assert not as_np(out["taken"]).any()
     o = oracle.run_pipeline(inp, cfg)
     close(xc, o["x_comp"], 2e-2, "x_comp (appended tokens only)", floor=1e-3)
-    check_kl(klv, xf, xc, inp["W"], o["kl"], "empty budget")
+    check_kl(klv, xf, xc, inp["W"], o["kl"], "empty budget", o["x_full"], o["x_comp"])
 
 
 @pytest.mark.parametrize("n_dprobe", [48, 20, 1])
