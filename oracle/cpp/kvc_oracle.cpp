@@ -124,15 +124,36 @@ void budgets_of(const ko_shape* sh, const ko_params* p, int s, int64_t* B, int64
 }
 
 // ------------------------------------------------------------------ RoPE (rotate-half pairs)
-void rope_apply(const double* x, double pos, int d, double base, double sign, double* out) {
-  const int h = d / 2;
-  for (int j = 0; j < h; ++j) {
-    const double th = pos * std::pow(base, -2.0 * (double)j / (double)d);
-    const double c = std::cos(th), s = sign * std::sin(th);
-    out[j] = x[j] * c - x[j + h] * s;
-    out[j + h] = x[j + h] * c + x[j] * s;
+// theta_j(pos) = pos * base^(-2j/d); pair (j, j + d/2) rotated by +-theta.
+// The table holds cos and sin of theta_j(pos) for pos < n_pos.
+struct Rope {
+  int d = 0;
+  vector<double> cs, sn;  // [n_pos][d/2]
+  void make(int64_t n_pos, int dd, double base) {
+    d = dd;
+    const int h = d / 2;
+    vector<double> inv(h);
+    for (int j = 0; j < h; ++j) inv[j] = std::pow(base, -2.0 * (double)j / (double)d);
+    cs.resize((size_t)(n_pos * h));
+    sn.resize((size_t)(n_pos * h));
+    for (int64_t p = 0; p < n_pos; ++p)
+      for (int j = 0; j < h; ++j) {
+        const double th = (double)p * inv[j];
+        cs[(size_t)(p * h + j)] = std::cos(th);
+        sn[(size_t)(p * h + j)] = std::sin(th);
+      }
   }
-}
+  // sign +1 rotates, -1 rotates back
+  void apply(const double* x, int64_t pos, double sign, double* out) const {
+    const int h = d / 2;
+    const double* c = &cs[(size_t)(pos * h)];
+    const double* s = &sn[(size_t)(pos * h)];
+    for (int j = 0; j < h; ++j) {
+      out[j] = x[j] * c[j] - x[j + h] * (sign * s[j]);
+      out[j + h] = x[j + h] * c[j] + x[j] * (sign * s[j]);
+    }
+  }
+};
 
 // ------------------------------------------------------------------ trees
 struct Node {
@@ -224,8 +245,10 @@ extern "C" void ko_probe_scores(const ko_shape* sh, const void* K, const void* V
       rows(V, dt, ubase + a, L, d, Vu);
       rows(Qp, dt, (((int64_t)s * Ly + l) * H * G + (int64_t)h * G) * P, R, d, Q);
       Sm.resize((size_t)(R * L));
-      for (int64_t i = 0; i < L; ++i)
-        for (int rr = 0; rr < R; ++rr) Sm[(size_t)(rr * L + i)] = c * dot(&Q[(size_t)rr * d], &Ku[(size_t)i * d], d);
+      for (int64_t i0 = 0; i0 < L; i0 += 64)  // 64 keys at a time stay in cache for every row
+        for (int rr = 0; rr < R; ++rr)
+          for (int64_t i = i0; i < std::min<int64_t>(L, i0 + 64); ++i)
+            Sm[(size_t)(rr * L + i)] = c * dot(&Q[(size_t)rr * d], &Ku[(size_t)i * d], d);
       vector<double> lse(R), ent(R), r0(L, 0.0), wsum(L, 0.0), mg((size_t)(G * L), 0.0);
       for (int rr = 0; rr < R; ++rr) {
         double* srow = &Sm[(size_t)(rr * L)];
@@ -534,6 +557,10 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
   const vector<int> drows = dprobe_rows(G, P, p->n_dprobe);
   const int Pd = (int)drows.size();
   const int64_t units = (int64_t)S * Ly * H;
+  int64_t max_len = 0;
+  for (int s = 0; s < S; ++s) max_len = std::max<int64_t>(max_len, sh->cu[s + 1] - sh->cu[s]);
+  Rope rope;
+  rope.make(max_len, d, base);
   Progress prog("trees", units);
 #pragma omp parallel
   {
@@ -555,7 +582,7 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
       ktil.resize((size_t)(L * d));
       knorm.resize((size_t)L);
       for (int64_t i = 0; i < L; ++i) {
-        rope_apply(&Ku[(size_t)i * d], (double)i, d, base, -1.0, &ktil[(size_t)i * d]);
+        rope.apply(&Ku[(size_t)i * d], i, -1.0, &ktil[(size_t)i * d]);
         knorm[i] = std::sqrt(dot(&ktil[(size_t)i * d], &ktil[(size_t)i * d], d));
       }
       const int64_t qb = (((int64_t)s * Ly + l) * H * G + (int64_t)h * G) * P;
@@ -589,7 +616,7 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
           const double rho = sn > 0 ? std::sqrt(dot(skt.data(), skt.data(), d)) / sn : 1.0;
           mu[j] = std::max(1.0, (double)n * rho);
           for (int x = 0; x < d; ++x) kbar[x] = skt[x] / (double)n;
-          rope_apply(kbar.data(), (double)(st + (n - 1) / 2), d, base, 1.0, khat.data());
+          rope.apply(kbar.data(), st + (n - 1) / 2, 1.0, khat.data());
           std::fill(vhat.begin(), vhat.end(), 0.0);
           for (int64_t i = st; i < st + n; ++i) {
             const double wi = rel[j] > 0 ? (1.0 - beta) * r[i] / rel[j] + beta / (double)n : 1.0 / (double)n;
@@ -905,6 +932,10 @@ extern "C" void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, c
   const int64_t T = sh->T;
   const double base = p->rope_base, beta = (double)p->value_base;
   const int64_t nseg = (int64_t)Ly * H * S;
+  int64_t max_len = 0;
+  for (int s = 0; s < S; ++s) max_len = std::max<int64_t>(max_len, sh->cu[s + 1] - sh->cu[s]);
+  Rope rope;
+  rope.make(max_len, d, base);
   vector<int64_t> cnt((size_t)nseg);
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t x = 0; x < nseg; ++x) {
@@ -953,7 +984,7 @@ extern "C" void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, c
           std::fill(vh.begin(), vh.end(), 0.0);
           for (int64_t i = en.a; i < en.a + en.m; ++i) {
             for (int k = 0; k < d; ++k) tmp[k] = elem(K, dt, (ub + i) * d + k);
-            rope_apply(tmp.data(), (double)i, d, base, -1.0, kt.data());
+            rope.apply(tmp.data(), i, -1.0, kt.data());
             for (int k = 0; k < d; ++k) kbar[k] += kt[k];
             const double wi = rl > 0 ? (1.0 - beta) * (double)rel[ub + i] / rl + beta / (double)en.m
                                      : 1.0 / (double)en.m;
@@ -961,7 +992,7 @@ extern "C" void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, c
           }
           for (int k = 0; k < d; ++k) kbar[k] /= (double)en.m;
           const int64_t prep = en.a + (en.m - 1) / 2;
-          rope_apply(kbar.data(), (double)prep, d, base, 1.0, kh.data());
+          rope.apply(kbar.data(), prep, 1.0, kh.data());
           for (int k = 0; k < d; ++k) {
             store(Kp, dt, e * d + k, kh[k]);
             store(Vp, dt, e * d + k, vh[k]);
