@@ -33,8 +33,12 @@ constexpr int MCHUNK = 768;  // entries per piece, at most: bf16 caches (MFMA ke
 constexpr int THREADS = 256;
 constexpr int PLAN_THREADS = 1024;
 constexpr int PLAN_PER = 8;  // units per plan thread per round, at most
-// waves of a merge workgroup (LDS holds one G*D row per wave)
+// waves of a merge workgroup (LDS holds one G*D row per wave): wide
+// workgroups when there are few units (one wave-batch of pieces each), narrow
+// ones when there are many, so that more of them are resident at once
 template <int G> constexpr int mrg_waves() { return G <= 4 ? 16 : 8; }
+constexpr int MRG_NARROW = 4;
+constexpr int64_t MRG_NARROW_UNITS = 1024;  // units from which the narrow merge is used
 constexpr int MRG_NPW = 4;    // pieces per wave per merge batch of loads
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -520,11 +524,10 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(G == 8 
 // MRG_NPW pieces of a batch together and merges them online (lane = OPL
 // consecutive outputs of one head), the waves are combined through LDS and o
 // is normalized and stored. The layer sum reads it in the next launch.
-template <int D, int G>
-__global__ __launch_bounds__(mrg_waves<G>() * 64) void decode_merge_kernel(DecArgs a) {
+template <int D, int G, int MRG_WAVES>
+__global__ __launch_bounds__(MRG_WAVES * 64) void decode_merge_kernel(DecArgs a) {
   constexpr int GD = G * D;
   constexpr int OPL = GD / 64;  // merged outputs per lane, all of one head
-  constexpr int MRG_WAVES = mrg_waves<G>();
   constexpr int NT = MRG_WAVES * 64;
   __shared__ float accs[MRG_WAVES][GD];
   __shared__ float msw[MRG_WAVES][G], lsw[MRG_WAVES][G];
@@ -742,8 +745,11 @@ extern "C" int kvc_decode_attn_planned(const kvc_ragged* c, const void* K_tail, 
   const int d = c->head_dim;
 #define KVC_DEC(TT, DD, GG) hipLaunchKernelGGL((decode_partial_kernel<TT, DD, GG>), grid, dim3(THREADS), 0, st, a)
 #define KVC_DECM(DD, GG) hipLaunchKernelGGL((decode_mfma_kernel<DD, GG>), grid, dim3(THREADS), 0, st, a)
-#define KVC_MRG(DD, GG) \
-  hipLaunchKernelGGL((decode_merge_kernel<DD, GG>), mgrid, dim3(mrg_waves<GG>() * 64), 0, st, a)
+#define KVC_MRG(DD, GG)                                                                                       \
+  if (units_of(c) >= MRG_NARROW_UNITS)                                                                       \
+    hipLaunchKernelGGL((decode_merge_kernel<DD, GG, MRG_NARROW>), mgrid, dim3(MRG_NARROW * 64), 0, st, a);   \
+  else                                                                                                        \
+    hipLaunchKernelGGL((decode_merge_kernel<DD, GG, mrg_waves<GG>()>), mgrid, dim3(mrg_waves<GG>() * 64), 0, st, a)
 #define KVC_DEC_G(MAC, ...)                    \
   switch (group) {                             \
     case 1: MAC(__VA_ARGS__, 1); break;        \

@@ -17,6 +17,7 @@
 // offset. Writers: exact/kept tokens copy their bits; one wave per slot walks
 // the frontier in pre-order (= position order) and writes leaves and
 // prototypes.
+#include <algorithm>
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -41,6 +42,7 @@ struct PackArgs {
   int S, Ly, H, stride, token_mode;
   int64_t T;
   int64_t pe[64], c1[64];   // per sequence: prompt end (= compressible start), compressible end
+  int64_t xoff[65];         // prefix over sequences of the exact tokens (prompt + recent + suffix)
   float beta;               // uniform share of prototype values
   void* oK;
   void* oV;
@@ -142,39 +144,59 @@ __global__ void seg_kernel(PackArgs a, const int64_t* off, const int64_t* total,
   seg_len[i] = (int32_t)(oe - ob);
 }
 
+// Exact tokens (prompt, recent window, suffix) of every (unit, sequence): one
+// thread per 16-byte piece of a K or V row, over those tokens only.
 template <class T, int D>
-__device__ __forceinline__ void copy_row(const PackArgs& a, int64_t src_row, int64_t dst, int32_t pos, int lane,
-                                         int nlanes) {
-  const T* K = (const T*)a.K + src_row * D;
-  const T* V = (const T*)a.V + src_row * D;
-  T* oK = (T*)a.oK + dst * D;
-  T* oV = (T*)a.oV + dst * D;
-  for (int j = lane; j < D; j += nlanes) {
-    oK[j] = K[j];
-    oV[j] = V[j];
-  }
-  if (lane == 0) {
+__global__ __launch_bounds__(256) void write_exact_kernel(PackArgs a, const int64_t* off) {
+  constexpr int PPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t X = a.xoff[a.S];
+  const int64_t per_lh = X * 2 * PPR;
+  if (g >= (int64_t)a.Ly * a.H * per_lh) return;
+  const int64_t lh = g / per_lh, r = g % per_lh;
+  const int64_t x = r / (2 * PPR);
+  const int pc = (int)(r % (2 * PPR));
+  int s = 0;
+  while (s + 1 < a.S && a.xoff[s + 1] <= x) ++s;
+  const int64_t k = x - a.xoff[s];
+  const int64_t p = k < a.pe[s] ? k : a.c1[s] + (k - a.pe[s]);
+  const int64_t i = lh * a.T + a.cu[s] + p;
+  const int64_t dst = off[i];
+  if (dst >= a.capacity) return;
+  const bool isv = pc >= PPR;
+  const int q = isv ? pc - PPR : pc;
+  const uint4* src = (const uint4*)((const T*)(isv ? a.V : a.K) + i * D) + q;
+  uint4* o = (uint4*)((T*)(isv ? a.oV : a.oK) + dst * D) + q;
+  *o = *src;
+  if (pc == 0) {
     a.olnmu[dst] = 0.f;
-    a.opos[dst] = pos;
+    a.opos[dst] = (int32_t)p;
   }
 }
 
-// exact tokens and (token mode) kept tokens: one thread group of 16 per token
+// Token mode: the kept tokens of the compressible regions, one thread per
+// 16-byte piece of a K or V row.
 template <class T, int D>
-__global__ void write_tokens_kernel(PackArgs a, const int64_t* off) {
-  int64_t E = (int64_t)a.Ly * a.H * a.T;
-  int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 16;
-  int lane = threadIdx.x % 16;
-  if (i >= E) return;
-  int64_t t = i % a.T;
-  int s = seq_of_tok(a, t);
-  int64_t p = t - a.cu[s];
-  bool exact = p < a.pe[s] || p >= a.c1[s];
-  bool kept = exact || (a.token_mode && a.taken[i]);
-  if (!kept) return;
-  int64_t dst = off[i];
+__global__ __launch_bounds__(256) void write_kept_kernel(PackArgs a, const int64_t* off) {
+  constexpr int PPR = D * (int)sizeof(T) / 16;
+  const int64_t E = (int64_t)a.Ly * a.H * a.T;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = g / (2 * PPR);
+  const int pc = (int)(g % (2 * PPR));
+  if (i >= E || !a.taken[i]) return;
+  const int64_t t = i % a.T;
+  const int s = seq_of_tok(a, t);
+  const int64_t p = t - a.cu[s];
+  if (p < a.pe[s] || p >= a.c1[s]) return;
+  const int64_t dst = off[i];
   if (dst >= a.capacity) return;
-  copy_row<T, D>(a, i, dst, (int32_t)p, lane, 16);
+  const bool isv = pc >= PPR;
+  const int q = isv ? pc - PPR : pc;
+  *((uint4*)((T*)(isv ? a.oV : a.oK) + dst * D) + q) = *((const uint4*)((const T*)(isv ? a.V : a.K) + i * D) + q);
+  if (pc == 0) {
+    a.olnmu[dst] = 0.f;
+    a.opos[dst] = (int32_t)p;
+  }
 }
 
 // 8 consecutive elements from fp32 values in one 16-byte store (bf16: RNE)
@@ -212,7 +234,8 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
   __shared__ int ioff[WS_THREADS + 1];
   __shared__ int wcnt[WS_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // block -> (unit lh, sequence s, slot k): grid is (Ly*H*S*stride)
+  // block -> (unit lh, sequence s, slot k): grid is (Ly*H*S*stride); blocks
+  // past a sequence's slots return at once
   int64_t b = blockIdx.x;
   int k = (int)(b % a.stride);
   int64_t rest = b / a.stride;
@@ -449,10 +472,13 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
   a.stride = p->token_mode ? 1 : kvc_slot_stride(sh, p);
   a.token_mode = p->token_mode;
   a.T = sh->total_tokens;
+  a.xoff[0] = 0;
   for (int s = 0; s < sh->n_seq; ++s) {
-    kvc::Regions g = kvc::regions_of(sh->cu_seqlens[s + 1] - sh->cu_seqlens[s], *p);
+    const int64_t L = sh->cu_seqlens[s + 1] - sh->cu_seqlens[s];
+    kvc::Regions g = kvc::regions_of(L, *p);
     a.pe[s] = g.pe;
     a.c1[s] = g.c1;
+    a.xoff[s + 1] = a.xoff[s] + g.pe + (L - g.c1);
   }
   a.beta = p->value_base;
   a.oK = out->K;
@@ -474,17 +500,25 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
                      out->seg_len);
   KVC_LAUNCH_CHECK("pack_seg");
   int d = sh->head_dim;
-  dim3 tg(kvc_blocks(E * 16, 256));
-  if (sh->dtype == KVC_BF16) {
-    if (d == 128) hipLaunchKernelGGL((write_tokens_kernel<uint16_t, 128>), tg, dim3(256), 0, st, a, off);
-    else hipLaunchKernelGGL((write_tokens_kernel<uint16_t, 64>), tg, dim3(256), 0, st, a, off);
-  } else {
-    if (d == 128) hipLaunchKernelGGL((write_tokens_kernel<float, 128>), tg, dim3(256), 0, st, a, off);
-    else hipLaunchKernelGGL((write_tokens_kernel<float, 64>), tg, dim3(256), 0, st, a, off);
+  const int ppr2 = 2 * d * (sh->dtype == KVC_BF16 ? 2 : 4) / 16;  // 16-byte pieces of a K and a V row
+  const int64_t nex = (int64_t)sh->n_layers * sh->n_kv_heads * a.xoff[sh->n_seq] * ppr2;
+#define KVC_PACK_T(KERN, GRID)                                                                             \
+  if (sh->dtype == KVC_BF16) {                                                                             \
+    if (d == 128) hipLaunchKernelGGL((KERN<uint16_t, 128>), GRID, dim3(256), 0, st, a, off);               \
+    else hipLaunchKernelGGL((KERN<uint16_t, 64>), GRID, dim3(256), 0, st, a, off);                         \
+  } else {                                                                                                 \
+    if (d == 128) hipLaunchKernelGGL((KERN<float, 128>), GRID, dim3(256), 0, st, a, off);                  \
+    else hipLaunchKernelGGL((KERN<float, 64>), GRID, dim3(256), 0, st, a, off);                            \
   }
-  KVC_LAUNCH_CHECK("pack_tokens");
-  if (!p->token_mode) {
-    dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride));
+  if (nex > 0) {
+    KVC_PACK_T(write_exact_kernel, dim3(kvc_blocks(nex, 256)));
+    KVC_LAUNCH_CHECK("pack_exact");
+  }
+  if (p->token_mode) {
+    KVC_PACK_T(write_kept_kernel, dim3(kvc_blocks(E * ppr2, 256)));
+    KVC_LAUNCH_CHECK("pack_kept");
+  } else {
+    const dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride));
     if (sh->dtype == KVC_BF16) {
       if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(WS_THREADS), 0, st, a, off);
       else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(WS_THREADS), 0, st, a, off);
@@ -494,5 +528,6 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
     }
     KVC_LAUNCH_CHECK("pack_slots");
   }
+#undef KVC_PACK_T
   return KVC_OK;
 }
