@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarize a rocprofv3 kernel_trace.csv of a bench run (per kernel, the decode "
                          "kernels split by cache: the compressed cache's calls launch fewer workgroups), then exit")
+    ap.add_argument("--counter-summary", default=None, metavar="CSV",
+                    help="only summarize a rocprofv3 --pmc counter_collection.csv of a bench run (mean counter "
+                         "value per dispatch of each kernel, the decode kernels split by cache), then exit")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring this GPU's own HBM read and bf16 MFMA ceilings (kvc_peak_read, "
                          "kvc_peak_mfma) before the timed steps")
@@ -280,6 +283,43 @@ def trace_summary(path):
               f"{sum(g for _, _, g in lst) / len(lst):.0f} | {100 * t / tot:.1f} |")
 
 
+def counter_summary(path):
+    """Mean counter value per dispatch of each kernel in a rocprofv3 --pmc
+    counter_collection.csv, the decode kernels split by cache as in
+    trace_summary (dispatch order alternates full, compressed). Prints a
+    markdown table."""
+    import csv
+    from collections import defaultdict
+    rows = list(csv.DictReader(open(path)))
+    disp = {}
+    for r in rows:
+        key = int(r.get("Dispatch_Id", r.get("Correlation_Id", 0)))
+        d = disp.setdefault(key, {"name": r["Kernel_Name"], "grid": int(r.get("Grid_Size", 0) or 0), "c": {}})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    by = defaultdict(list)
+    for key in sorted(disp):
+        d = disp[key]
+        short = d["name"].replace("void ", "").replace("(anonymous namespace)::", "").split("(")[0].strip()
+        by[short].append(d)
+    out = defaultdict(list)
+    for short, lst in by.items():
+        if short.split("<")[0] in ("decode_mfma_kernel", "decode_partial_kernel", "decode_merge_kernel",
+                                   "decode_layersum_kernel"):
+            full, comp = lst[0::2], lst[1::2]
+            if comp and sum(x["grid"] for x in comp) > sum(x["grid"] for x in full):
+                full, comp = comp, full
+            out[short + " [full cache]"] += full
+            out[short + " [25% cache]"] += comp
+        else:
+            out[short] += lst
+    names = sorted({c for lst in out.values() for d in lst for c in d["c"]})
+    print("| kernel | dispatches | " + " | ".join(f"{c} (mean)" for c in names) + " |")
+    print("|---|---|" + "---|" * len(names))
+    for short, lst in sorted(out.items()):
+        means = [sum(d["c"].get(c, 0.0) for d in lst) / len(lst) for c in names]
+        print(f"| {short} | {len(lst)} | " + " | ".join(f"{m:.1f}" for m in means) + " |")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -288,6 +328,9 @@ def main():
         sys.exit(2)
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -304,8 +347,11 @@ def main():
     if not args.no_peaks:
         # the machine's own ceilings, measured before anything else is resident
         peaks = {"hbm_read_gbs": round(kvc.peak_read_gbs(), 1), "mfma_bf16_tflops": round(kvc.peak_mfma_tflops(), 1),
+                 "exp_mix_gelems": round(kvc.peak_exp_gelems(), 1),
                  "how": "kvc_peak_read: 2 GiB of nontemporal 16-byte loads, each workgroup streaming one "
-                        "contiguous span; kvc_peak_mfma: register-only 32x32x16 bf16 MFMA chains on every SIMD"}
+                        "contiguous span; kvc_peak_mfma: register-only 32x32x16 bf16 MFMA chains on every SIMD; "
+                        "kvc_peak_exp: register-only chains of one v_exp_f32 and three VALU operations (the "
+                        "probe passes' per-logit mix), elements per second"}
         print(f"[bench] measured peaks {peaks['hbm_read_gbs']} GB/s, {peaks['mfma_bf16_tflops']} TFLOP/s",
               file=sys.stderr, flush=True)
     t_gen = time.perf_counter()

@@ -1,6 +1,8 @@
 // Measurement helpers: the HBM read ceiling (nontemporal 16-byte loads, one
-// contiguous span a workgroup) and the bf16 MFMA ceiling (register-only MFMA
-// chains) of the device, timed by the caller.
+// contiguous span a workgroup), the bf16 MFMA ceiling (register-only MFMA
+// chains) and the exponential-mix ceiling (register-only chains of one
+// hardware exponential and three VALU operations) of the device, timed by the
+// caller.
 #include "kvc_internal.h"
 #include "kvc_peaks.h"
 
@@ -65,7 +67,48 @@ __global__ __launch_bounds__(256) void peak_mfma_kernel(int iters, float* sink) 
   if (threadIdx.x == 0) sink[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
 }
 
+// Exponential-mix ceiling: every thread runs 8 independent chains, each round
+// one base-2 exponential (the hardware v_exp_f32) and three VALU operations,
+// x <- fma(e, 0.5, -0.25); e <- exp2(x); s <- s + e; t <- fma(e, h, t), the
+// per-logit mix of the probe passes (a shifted exponential, a running sum and
+// a weighted sum). Values stay in [2^-0.25, 2^0.25]: no denormals, no overflow.
+__global__ __launch_bounds__(256) void peak_exp_kernel(int iters, float* sink) {
+  float x[8], s[8], t[8];
+  const float h = 0.37f + 1e-3f * (float)(threadIdx.x & 7);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    x[k] = 0.01f * (float)k;
+    s[k] = 0.f;
+    t[k] = 0.f;
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float e = __builtin_amdgcn_exp2f(x[k]);
+      s[k] += e;
+      t[k] = fmaf(e, h, t[k]);
+      x[k] = fmaf(e, 0.5f, -0.25f);
+    }
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r += s[k] + t[k];
+  r = wave_sum(r);
+  __shared__ float ws[4];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = r;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = ws[0] + ws[1] + ws[2] + ws[3];
+}
+
 }  // namespace
+
+extern "C" int kvc_peak_exp(int32_t grid, int32_t iters, float* sink, hipStream_t st) {
+  KVC_REQUIRE(sink, KVC_E_INVAL, "kvc_peak_exp: NULL sink");
+  KVC_REQUIRE(grid >= 1 && iters >= 1, KVC_E_INVAL, "kvc_peak_exp: grid and iters must be >= 1");
+  hipLaunchKernelGGL(peak_exp_kernel, dim3((unsigned)grid), dim3(256), 0, st, iters, sink);
+  KVC_LAUNCH_CHECK("peak_exp");
+  return KVC_OK;
+}
 
 extern "C" int kvc_peak_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, hipStream_t st) {
   KVC_REQUIRE(buf && sink, KVC_E_INVAL, "kvc_peak_read: NULL pointer");

@@ -131,9 +131,10 @@ _sig = {
     "kvc_kl": (C.c_int, [C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]),
 }
 # measurement helpers (include/kvc_peaks.h)
-PEAK_EXPORTS = ["kvc_peak_read", "kvc_peak_mfma"]
+PEAK_EXPORTS = ["kvc_peak_read", "kvc_peak_mfma", "kvc_peak_exp"]
 _sig["kvc_peak_read"] = (C.c_int, [_P, C.c_size_t, C.c_int32, _P, _P])
 _sig["kvc_peak_mfma"] = (C.c_int, [C.c_int32, C.c_int32, _P, _P])
+_sig["kvc_peak_exp"] = (C.c_int, [C.c_int32, C.c_int32, _P, _P])
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
     _f.restype = _res
@@ -580,6 +581,17 @@ def peak_read_gbs(nbytes=2 << 30, grid=16384, reps=10):
     ms = _time_ms(launch, reps)
     del buf
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def peak_exp_gelems(grid=2048, iters=2048, reps=5):
+    """Measured exponential-mix ceiling (kvc_peak_exp): elements (one exp2 and
+    three VALU operations each) per second, in G/s."""
+    sink = torch.zeros(grid, dtype=torch.float32, device="cuda")
+
+    def launch():
+        _check("kvc_peak_exp", _lib.kvc_peak_exp(grid, iters, _ptr(sink), _stream()))
+    ms = _time_ms(launch, reps)
+    return grid * 256 * iters * 8 / (ms * 1e-3) / 1e9
 
 
 def peak_mfma_tflops(grid=2048, iters=4096, reps=5):

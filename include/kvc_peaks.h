@@ -34,6 +34,14 @@ int kvc_peak_read(const void* buf, size_t bytes, int32_t grid, uint32_t* sink, h
  * KVC_E_INVAL on a NULL sink, grid < 1 or iters < 1. */
 int kvc_peak_mfma(int32_t grid, int32_t iters, float* sink, hipStream_t stream);
 
+/* Exponential-mix ceiling (the per-logit VALU work of the probe passes):
+ * `grid` workgroups of 256 threads; every thread runs `iters` rounds of 8
+ * independent chains, each round one v_exp_f32 and three VALU operations
+ * (two fused multiply-adds and an add) on registers. Each workgroup stores
+ * one sum to sink[blockIdx] (device, `grid` floats). Elements of a launch =
+ * grid * 256 * iters * 8. KVC_E_INVAL on a NULL sink, grid < 1 or iters < 1. */
+int kvc_peak_exp(int32_t grid, int32_t iters, float* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,9 @@ def test_peak_helpers_reject_bad_arguments(kvc):
     assert lib.kvc_peak_mfma(0, 10, dummy, None) == -1
     assert lib.kvc_peak_mfma(8, 0, dummy, None) == -1
     assert lib.kvc_peak_mfma(8, 10, None, None) == -1
+    assert lib.kvc_peak_exp(0, 10, dummy, None) == -1
+    assert lib.kvc_peak_exp(8, 0, dummy, None) == -1
+    assert lib.kvc_peak_exp(8, 10, None, None) == -1
 
 
 def _problem(kvc, lens, **kw):
