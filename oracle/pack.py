@@ -20,7 +20,7 @@ from __future__ import annotations
 import numpy as np
 
 from .common import to64, rope, rope_inv, regions, round_to
-from .trees import tree_nodes
+from .trees import slot_nodes
 
 
 def _frontier(nodes, taken, base):
@@ -31,10 +31,9 @@ def _frontier(nodes, taken, base):
     stack = [0]
     while stack:
         j = stack.pop()
-        lc, rc = nodes[j][2], nodes[j][3]
-        if lc >= 0 and taken[base + 1 + j]:
-            stack.append(rc)
-            stack.append(lc)
+        ch = nodes[j][2]
+        if ch and taken[base + 1 + j]:
+            stack.extend(reversed(ch))
         else:
             out.append(j)
     return out
@@ -62,7 +61,8 @@ def prototype_entry(Ku, Vu, r, a, m, rel, mu, cfg):
 
 def pack(K, V, rel_tok, trees, taken, cu, slots, cfg):
     """K, V: [Ly][H][T][d]; rel_tok float32 [Ly][H][T]; trees: dict with
-    float32 node_rel/node_mu [Ly][H][2T]; taken: uint8 op_taken [Ly][H][2T]
+    float32 node_rel/node_mu [Ly][H][2T] and the uint32 node_topo records
+    (absent or None: midpoint trees); taken: uint8 op_taken [Ly][H][2T]
     (tree mode) or [Ly][H][T] (token mode); slots: per sequence.
 
     Returns dict: K, V float64 [N][d] (values of the cache dtype), lnmu
@@ -97,7 +97,7 @@ def pack(K, V, rel_tok, trees, taken, cu, slots, cfg):
                 else:
                     r = np.asarray(rel_tok[l, h, a0:b0], dtype=np.float64)
                     for (st, n) in slots[s]:
-                        nodes = tree_nodes(st, n)
+                        nodes = slot_nodes(trees.get("node_topo"), l, h, a0, st, n)
                         base = (l * H + h) * 2 * T + 2 * (a0 + st)
                         nb = (l * H + h, 2 * (a0 + st))
                         for j in _frontier(nodes, tk, base):

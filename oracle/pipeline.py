@@ -41,11 +41,13 @@ def run_pipeline(inp, cfg, stages=("compress", "decode", "kl")):
             out["dp_cost_q"], out["dp_cut_q"] = cost_q, cut_q
         slots = slots_for(cu, cfg, cost_q, cut_q)
         trees = build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"],
-                            cu, slots, cfg)
+                            cu, slots, cfg, cut_q=cut_q)
         out["trees"] = trees
-        ftaken, fspent = floor_select(rel, sc["head_sens"], trees["op_cost"], cu, slots, cfg, full=full)
+        topo = trees["node_topo"]
+        ftaken, fspent = floor_select(rel, sc["head_sens"], trees["op_cost"], cu, slots, cfg, full=full, topo=topo)
         out["floor_taken"], out["floor_spent"] = ftaken, fspent
-        taken, spent = auction(trees["op_util"], trees["op_cost"], ftaken, fspent, cu, slots, cfg, full=full)
+        taken, spent = auction(trees["op_util"], trees["op_cost"], ftaken, fspent, cu, slots, cfg, full=full,
+                               topo=topo)
     out["slots"] = slots
     out["taken"], out["spent"] = taken, spent
     cache = pack(inp["K"], inp["V"], rel, trees, taken, cu, slots, cfg)

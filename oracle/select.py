@@ -42,7 +42,7 @@ import heapq
 import numpy as np
 
 from .common import regions, budgets
-from .trees import tree_nodes
+from .trees import slot_nodes
 
 
 def _f32key(x) -> float:
@@ -55,12 +55,12 @@ def _slot_ops(T, H, l, h, t0):
 
 
 def _leaf_path(nodes, i):
-    """Internal node indices on the path from the root to the leaf of token i."""
+    """Internal node indices on the path from the root to the leaf of token i
+    (nodes as [start, length, children, parent])."""
     path, j = [], 0
-    while nodes[j][2] >= 0:
+    while nodes[j][2]:
         path.append(j)
-        st, m, lc, rc = nodes[j]
-        j = lc if i < st + (m + 1) // 2 else rc
+        j = next(c for c in nodes[j][2] if nodes[c][0] <= i < nodes[c][0] + nodes[c][1])
     return path
 
 
@@ -78,11 +78,12 @@ def hybrid_units(head_sens, cu, cfg):
     return full
 
 
-def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None, full=None):
+def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None, full=None, topo=None):
     """Returns op_taken uint8 [Ly][H][2T] (floor ops only) and spent [S].
     If ``trace`` is a list, accepted candidates are appended as
     (leaf flat id, path cost paid). ``full`` [S][Ly][H] excludes the units
-    kept whole by the head-level hybrid."""
+    kept whole by the head-level hybrid. ``topo``: the trees' node_topo
+    (None: midpoint trees)."""
     Ly, H, T2 = op_cost.shape
     T = T2 // 2
     taken = np.zeros((Ly, H, 2 * T), dtype=np.uint8)
@@ -102,7 +103,7 @@ def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None, full=N
                     continue
                 sens = np.float64(head_sens[s, l, h])
                 for (st, n) in slots[s]:
-                    nodes = tree_nodes(st, n)
+                    nodes = slot_nodes(topo, l, h, a0, st, n)
                     base = _slot_ops(T, H, l, h, a0 + st)
                     for i in range(st, st + n):
                         v = np.float32(sens * np.float64(rel_tok[l, h, a0 + i]))
@@ -121,13 +122,16 @@ def floor_select(rel_tok, head_sens, op_cost, cu, slots, cfg, trace=None, full=N
     return taken, spent
 
 
-def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=None, full=None):
+def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=None, full=None, topo=None):
     """Best-first greedy over every exposed op of each sequence.
 
     Returns op_taken uint8 [Ly][H][2T] (floor ops included) and spent [S]
     (floor + auction entries, and the units kept whole). If ``trace`` is a
     list, the taken ops are appended to it in the order the queue pops them.
-    ``full`` [S][Ly][H]: units kept whole (every real op taken up front)."""
+    ``full`` [S][Ly][H]: units kept whole (every real op taken up front).
+    ``topo``: the trees' node_topo (None: midpoint trees). An op that costs
+    more than what is left is dropped (its subtree never becomes exposed) and
+    the queue goes on."""
     Ly, H, T2 = op_util.shape
     T = T2 // 2
     taken = floor_taken.copy().reshape(-1)
@@ -160,13 +164,13 @@ def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, trace=No
         for l in range(Ly):
             for h in range(H):
                 for (st, n) in slots[s]:
-                    nodes = tree_nodes(st, n)
+                    nodes = slot_nodes(topo, l, h, a0, st, n)
                     base = _slot_ops(T, H, l, h, a0 + st)
                     split = lambda j: base + 1 + j  # noqa: E731
-                    children[base] = [split(0)] if nodes[0][2] >= 0 else []
-                    for j, (_, _, lc, rc) in enumerate(nodes):
-                        if lc >= 0:
-                            children[split(j)] = [split(c) for c in (lc, rc) if nodes[c][2] >= 0]
+                    children[base] = [split(0)] if nodes[0][2] else []
+                    for j, (_, _, ch, _) in enumerate(nodes):
+                        if ch:
+                            children[split(j)] = [split(c) for c in ch if nodes[c][2]]
                     # exposed ops given the floor's choices
                     stack = [base]
                     while stack:

@@ -308,7 +308,7 @@ def test_fullsize_taken_set_and_pack_structure(run):
         l, h = divmod(u, H)
         fr = []
         for (st, n) in slots:
-            nodes = [(a + st, m, lc, rc) for (a, m, lc, rc) in shapes[n]]
+            nodes = otrees.slot_tree(st, n)
             for j in _frontier(nodes, taken[u], 2 * st):
                 a, m = nodes[j][0], nodes[j][1]
                 fr.append((a + (m - 1) // 2, m, a))

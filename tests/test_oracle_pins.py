@@ -285,7 +285,7 @@ def test_frontier_sizes_golden():
                 ok &= bool(taken[creator])
         if not ok:
             continue
-        fr = _frontier(nodes, taken, 0)
+        fr = _frontier(otrees.slot_tree(0, n), taken, 0)
         assert len(fr) == int(taken.sum())
         starts = sorted((nodes[j][0], nodes[j][1]) for j in fr)
         assert [nodes[j][0] for j in fr] == [s for s, _ in starts]   # position order
@@ -407,7 +407,7 @@ def test_auction_matches_brute_force_greedy(ties):
         if trial % 3 == 0:
             base, nodes = slots_ops[0]
             i = int(rng.integers(nodes[0][0], nodes[0][0] + nodes[0][1]))
-            for o in [base] + [base + 1 + j for j in osel._leaf_path(nodes, i)]:
+            for o in [base] + [base + 1 + j for j in osel._leaf_path(otrees.slot_tree(nodes[0][0], nodes[0][1]), i)]:
                 taken0[o] = 1
         pre = int(taken0.sum())
         for B in sorted({1, 2, 3, total_ops // 2, total_ops - 1, total_ops, total_ops + 3}):
@@ -460,7 +460,7 @@ def test_gracekv_toy_auction_golden():
     assert spent[0] == g["total"]
     # P13: a leaf at depth D costs D + 1 (Add plus D Splits)
     for depth_n, want in ((1, 1), (2, 2), (4, 3), (8, 4), (64, 7), (128, 8)):
-        nd = otrees.tree_nodes(0, depth_n)
+        nd = otrees.slot_tree(0, depth_n)
         assert len(osel._leaf_path(nd, 0)) + 1 == want
 
 

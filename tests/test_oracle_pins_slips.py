@@ -153,9 +153,10 @@ def _slipped_utilities(kind):
         add = rel[0] * D[0] if kind == "add_uses_D" else rel[0] * (1.0 - D[0])
         util[0] = np.float32((1.0 if kind == "no_sens" else sens) * add)
         cost[0] = 1
-        for j, (_, _, lc, rc) in enumerate(nodes):
-            if lc < 0:
+        for j, (_, _, ch, _) in enumerate(nodes):
+            if not ch:
                 continue
+            lc, rc = ch
             if kind == "split_sign":
                 g = (rel[lc] * D[lc] + rel[rc] * D[rc]) - rel[j] * D[j]
             elif kind == "split_child_swap":
@@ -269,7 +270,7 @@ def _internal_entries(slots, taken, tr, pk):
     out = []
     e = 0
     for (st, n) in slots[0]:
-        nodes = otrees.tree_nodes(st, n)
+        nodes = otrees.slot_tree(st, n)
         for j in _frontier(nodes, taken.reshape(-1), 2 * st):
             if nodes[j][1] > 1:
                 out.append((e, j, st))

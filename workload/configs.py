@@ -47,6 +47,7 @@ class Config:
     n_hops: int = 2
     n_seeds: int = 32
     hop_weight: float = 0.3
+    split_mode: int = 0          # 0: midpoint binary trees; 1: curvature-candidate cuts + salient three-way splits
     n_dprobe: int = 64
     w_attn: float = 0.25
     w_value: float = 0.75
