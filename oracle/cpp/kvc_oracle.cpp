@@ -5,7 +5,8 @@
 // the pages, with the readings the Python oracle states where the pages are
 // silent (probe rows see every cached key; relevance is the probe mass summed
 // over probes and query heads; propagation follows the seeds' causal prefill
-// attention rows; binary midpoint trees; mu = max(1, n rho); distortion over
+// attention rows; binary midpoint trees, or with split_mode 1 curvature-
+// candidate cuts and salient three-way splits; mu = max(1, n rho); distortion over
 // strided probe rows at 0.25 : 0.75; gains as the decrease of the frontier
 // loss; capped best-first auction; ln mu as a decode logit bias). Sums use
 // `omp simd` reductions, so only their rounding order differs from a
@@ -158,26 +159,119 @@ struct Rope {
 // ------------------------------------------------------------------ trees
 struct Node {
   int64_t st, n;
-  int lc, rc;  // -1: leaf
+  int ch[3], nch;  // children in position order (nch 0: leaf)
+  int parent;      // -1: root
 };
-// binary midpoint tree in pre-order, left child ceil(n/2) tokens
-void tree_nodes(int64_t a, int64_t n, vector<Node>& out) {
+constexpr uint32_t TOPO_NONE = 0xFFFFFFFFu;
+
+// left-to-right float64 sum of fp32 values
+double seq_sum(const float* x, int64_t n) {
+  double s = 0.0;
+  for (int64_t i = 0; i < n; ++i) s += (double)x[i];
+  return s;
+}
+
+// Child intervals of the node [st, st+n), n >= 2 (r and cut indexed by
+// sequence position; cut nullable). split_mode 0: midpoint, left ceil(n/2).
+// split_mode 1 (GraceKV page, 'Technical details and default settings':
+// high-curvature candidates beside the midpoint, a salient token isolated in
+// a three-way child set): the first position i of the node's largest fp32
+// relevance splits the node three ways when n >= 3, the node's relevance S (a
+// left-to-right float64 sum) is positive, 2 r_i > S and i is at least
+// max(floor(n/4), 1) tokens from either end; otherwise one cut among those
+// that leave both children at least ceil(n/4) tokens, the largest cut score
+// winning (ties: the midpoint, then the nearest cut, then the lower one), or
+// the midpoint without cut scores.
+int split_children(int64_t st, int64_t n, const float* r, const int64_t* cut, int mode, int64_t* ca, int64_t* cn) {
+  int64_t b = (n + 1) / 2;
+  if (mode == 1) {
+    if (n >= 3) {
+      int64_t i = 0;
+      for (int64_t k = 1; k < n; ++k)
+        if (r[st + k] > r[st + i]) i = k;
+      const double S = seq_sum(r + st, n);
+      const int64_t q = std::max<int64_t>(n / 4, 1);
+      if (S > 0 && 2.0 * (double)r[st + i] > S && i >= q && i <= n - 1 - q) {
+        ca[0] = st, cn[0] = i;
+        ca[1] = st + i, cn[1] = 1;
+        ca[2] = st + i + 1, cn[2] = n - i - 1;
+        return 3;
+      }
+    }
+    if (cut) {
+      const int64_t m4 = (n + 3) / 4;
+      const int64_t lo = std::max<int64_t>(1, m4), hi = std::min<int64_t>(n - 1, n - m4);
+      int64_t best = b, bv = cut[st + b];
+      for (int64_t c = lo; c <= hi; ++c) {
+        const int64_t v = cut[st + c];
+        const int64_t dc = c > b ? c - b : b - c, db = best > b ? best - b : b - best;
+        if (v > bv || (v == bv && (dc < db || (dc == db && c < best)))) {
+          best = c;
+          bv = v;
+        }
+      }
+      b = best;
+    }
+  }
+  ca[0] = st, cn[0] = b;
+  ca[1] = st + b, cn[1] = n - b;
+  return 2;
+}
+
+// pre-order nodes of the slot [a, a+n)
+void build_tree(int64_t a, int64_t n, const float* r, const int64_t* cut, int mode, vector<Node>& out) {
   out.clear();
   struct Rec {
-    static int go(int64_t st, int64_t m, vector<Node>& o) {
+    static int go(int64_t st, int64_t m, int parent, const float* r, const int64_t* cut, int mode, vector<Node>& o) {
       const int j = (int)o.size();
-      o.push_back(Node{st, m, -1, -1});
+      o.push_back(Node{st, m, {-1, -1, -1}, 0, parent});
       if (m > 1) {
-        const int64_t nl = (m + 1) / 2;
-        const int l = go(st, nl, o);
-        const int r = go(st + nl, m - nl, o);
-        o[j].lc = l;
-        o[j].rc = r;
+        int64_t ca[3], cn[3];
+        const int k = split_children(st, m, r, cut, mode, ca, cn);
+        for (int x = 0; x < k; ++x) {
+          const int c = go(ca[x], cn[x], j, r, cut, mode, o);
+          o[j].ch[x] = c;
+        }
+        o[j].nch = k;
       }
       return j;
     }
   };
-  Rec::go(a, n, out);
+  Rec::go(a, n, -1, r, cut, mode, out);
+}
+
+// the midpoint tree
+void tree_nodes(int64_t a, int64_t n, vector<Node>& out) { build_tree(a, n, nullptr, nullptr, 0, out); }
+
+// node records: bits 0-7 first token - slot start, 8-15 length - 1, 16-23
+// parent + 1, 24-31 next sibling (0: none); TOPO_NONE past the last node
+void encode_topo(const vector<Node>& nodes, int64_t a, int64_t n, uint32_t* rec) {
+  for (int64_t j = 0; j < 2 * n; ++j) rec[j] = TOPO_NONE;
+  vector<int> nxt(nodes.size(), 0);
+  for (const Node& nd : nodes)
+    for (int x = 0; x + 1 < nd.nch; ++x) nxt[nd.ch[x]] = nd.ch[x + 1];
+  for (size_t j = 0; j < nodes.size(); ++j)
+    rec[j] = (uint32_t)(nodes[j].st - a) | ((uint32_t)(nodes[j].n - 1) << 8) | ((uint32_t)(nodes[j].parent + 1) << 16) |
+             ((uint32_t)nxt[j] << 24);
+}
+void decode_topo(const uint32_t* rec, int64_t a, int64_t n, vector<Node>& out) {
+  out.clear();
+  for (int64_t j = 0; j < 2 * n && rec[j] != TOPO_NONE; ++j)
+    out.push_back(Node{a + (rec[j] & 255), (int64_t)((rec[j] >> 8) & 255) + 1, {-1, -1, -1}, 0,
+                       (int)((rec[j] >> 16) & 255) - 1});
+  for (size_t j = 0; j < out.size(); ++j)
+    if (out[j].parent >= 0) {
+      Node& p = out[out[j].parent];
+      p.ch[p.nch++] = (int)j;
+    }
+}
+// the nodes of a slot: from the records when given, else the midpoint tree
+void slot_nodes(const uint32_t* topo, int64_t unit, int64_t T, int64_t a0, int64_t st, int64_t n, vector<Node>& out) {
+  if (!topo) {
+    tree_nodes(st, n, out);
+    return;
+  }
+  decode_topo(topo + unit * 2 * T + 2 * (a0 + st), st, n, out);
 }
 
 vector<int> dprobe_rows(int G, int P, int n_dprobe) {
@@ -544,12 +638,14 @@ extern "C" void ko_slots(const ko_shape* sh, const ko_params* p, const int64_t* 
 // rho: Z = sum a, Z^ = mu exp(c <q, k^> - lse), u = sum a v;
 // e_A = sum |Z^ - Z| / sum Z, e_V = sum ||u - Z v^|| / sum ||u||,
 // D = min(1, w_A e_A + w_V e_V), leaves D = 0. Ops: Add gains
-// rel_root (1 - D_root), Split(j) gains rel_j D_j - sum_c rel_c D_c, cost 1,
-// utility fp32(sens * gain).
+// rel_root (1 - D_root), Split(j) gains rel_j D_j - sum_c rel_c D_c and costs
+// (children - 1), utility fp32(sens * gain / cost). The tree of a slot comes
+// from split_children (the partition's cut scores cut_q, nullable).
 extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const void* K, const void* V,
                                const void* Qp, const float* lse_in, const float* rel_in, const float* sens_in,
-                               const int32_t* slot_start, const int32_t* n_slots, int32_t stride, float* node_rel,
-                               float* node_D, float* node_mu, float* op_util, uint8_t* op_cost) {
+                               const int32_t* slot_start, const int32_t* n_slots, int32_t stride,
+                               const int64_t* cut_q, float* node_rel, float* node_D, float* node_mu, float* op_util,
+                               uint8_t* op_cost, uint32_t* node_topo) {
   const int S = sh->S, Ly = sh->Ly, H = sh->H, G = sh->G, d = sh->d, P = sh->P, dt = sh->dtype;
   const int64_t T = sh->T;
   const double c = 1.0 / std::sqrt((double)d), base = p->rope_base;
@@ -597,14 +693,23 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
       r.resize((size_t)L);
       for (int64_t i = 0; i < L; ++i) r[i] = (double)rel_in[ubase + a0 + i];
       const double sens = (double)sens_in[uu];
+      const float* r32 = rel_in + ubase + a0;
+      const int64_t* cq = cut_q ? cut_q + a0 : nullptr;
       for (const auto& slot : sl.v) {
-        tree_nodes(slot.first, slot.second, nodes);
+        build_tree(slot.first, slot.second, r32, cq, p->split_mode, nodes);
         const int m = (int)nodes.size();
         rel.assign(m, 0.0);
         D.assign(m, 0.0);
         mu.assign(m, 1.0);
-        for (int j = m - 1; j >= 0; --j)
-          rel[j] = nodes[j].lc < 0 ? r[nodes[j].st] : rel[nodes[j].lc] + rel[nodes[j].rc];
+        for (int j = m - 1; j >= 0; --j) {
+          if (nodes[j].nch == 0) {
+            rel[j] = r[nodes[j].st];
+            continue;
+          }
+          double sum = 0.0;
+          for (int x = 0; x < nodes[j].nch; ++x) sum += rel[nodes[j].ch[x]];
+          rel[j] = sum;
+        }
         for (int j = 0; j < m; ++j) {
           const int64_t st = nodes[j].st, n = nodes[j].n;
           std::fill(skt.begin(), skt.end(), 0.0);
@@ -622,7 +727,7 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
             const double wi = rel[j] > 0 ? (1.0 - beta) * r[i] / rel[j] + beta / (double)n : 1.0 / (double)n;
             for (int x = 0; x < d; ++x) vhat[x] += wi * Vu[(size_t)i * d + x];
           }
-          if (nodes[j].lc < 0) continue;
+          if (nodes[j].nch == 0) continue;
           double numA = 0.0, denA = 0.0, numV = 0.0, denV = 0.0;
           for (int k = 0; k < Pd; ++k) {
             const double* arow = &Ad[(size_t)(k * L)];
@@ -656,11 +761,14 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
         op_util[ob] = (float)(sens * (rel[0] * (1.0 - D[0])));
         op_cost[ob] = 1;
         for (int j = 0; j < m; ++j) {
-          if (nodes[j].lc < 0) continue;
-          const double gain = rel[j] * D[j] - (rel[nodes[j].lc] * D[nodes[j].lc] + rel[nodes[j].rc] * D[nodes[j].rc]);
-          op_util[ob + 1 + j] = (float)(sens * gain / 1.0);
-          op_cost[ob + 1 + j] = 1;
+          if (nodes[j].nch == 0) continue;
+          double sub = 0.0;
+          for (int x = 0; x < nodes[j].nch; ++x) sub += rel[nodes[j].ch[x]] * D[nodes[j].ch[x]];
+          const double gain = rel[j] * D[j] - sub;
+          op_util[ob + 1 + j] = (float)(sens * gain / (double)(nodes[j].nch - 1));
+          op_cost[ob + 1 + j] = (uint8_t)(nodes[j].nch - 1);
         }
+        if (node_topo) encode_topo(nodes, slot.first, slot.second, node_topo + ob);
       }
       prog.tick();
     }
@@ -673,9 +781,14 @@ namespace {
 void leaf_path(const vector<Node>& nodes, int64_t i, vector<int>& path) {
   path.clear();
   int j = 0;
-  while (nodes[j].lc >= 0) {
+  while (nodes[j].nch > 0) {
     path.push_back(j);
-    j = i < nodes[j].st + (nodes[j].n + 1) / 2 ? nodes[j].lc : nodes[j].rc;
+    int next = nodes[j].ch[0];
+    for (int x = 0; x < nodes[j].nch; ++x) {
+      const Node& c = nodes[nodes[j].ch[x]];
+      if (i >= c.st && i < c.st + c.n) next = nodes[j].ch[x];
+    }
+    j = next;
   }
 }
 }  // namespace
@@ -685,8 +798,8 @@ void leaf_path(const vector<Node>& nodes, int64_t i, vector<int>& path) {
 // F scanned in order, each paying the not-yet-taken ops of its root-to-leaf
 // path and accepted while the floor spend stays <= F.
 extern "C" void ko_floor(const ko_shape* sh, const ko_params* p, const float* rel, const float* sens,
-                         const uint8_t* op_cost, const int32_t* slot_start, const int32_t* n_slots, int32_t stride,
-                         uint8_t* taken, int64_t* spent) {
+                         const uint8_t* op_cost, const uint32_t* node_topo, const int32_t* slot_start,
+                         const int32_t* n_slots, int32_t stride, uint8_t* taken, int64_t* spent) {
   const int Ly = sh->Ly, H = sh->H;
   const int64_t T = sh->T;
   std::memset(taken, 0, (size_t)((int64_t)Ly * H * 2 * T));
@@ -725,7 +838,7 @@ extern "C" void ko_floor(const ko_shape* sh, const ko_params* p, const float* re
       const auto it = std::upper_bound(sl.v.begin(), sl.v.end(), i,
                                        [](int64_t x, const std::pair<int64_t, int64_t>& y) { return x < y.first; });
       const auto& slot = *(it - 1);
-      tree_nodes(slot.first, slot.second, nodes);
+      slot_nodes(node_topo, unit, T, a0, slot.first, slot.second, nodes);
       leaf_path(nodes, i, path);
       const int64_t base = unit * 2 * T + 2 * (a0 + slot.first);
       ops.assign(1, base);
@@ -747,8 +860,8 @@ extern "C" void ko_floor(const ko_shape* sh, const ko_params* p, const float* re
 // ops of the nodes it creates; until the budget is spent or the queue is
 // empty. NaN utilities rank below everything.
 extern "C" void ko_auction(const ko_shape* sh, const ko_params* p, const float* op_util, const uint8_t* op_cost,
-                           const int32_t* slot_start, const int32_t* n_slots, int32_t stride, uint8_t* taken,
-                           int64_t* spent) {
+                           const uint32_t* node_topo, const int32_t* slot_start, const int32_t* n_slots,
+                           int32_t stride, uint8_t* taken, int64_t* spent) {
   const int Ly = sh->Ly, H = sh->H;
   const int64_t T = sh->T;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -768,8 +881,14 @@ extern "C" void ko_auction(const ko_shape* sh, const ko_params* p, const float* 
     };
     auto worse = [](const Item& x, const Item& y) { return x.key != y.key ? x.key < y.key : x.op > y.op; };
     std::priority_queue<Item, vector<Item>, decltype(worse)> heap(worse);
-    vector<vector<Node>> trees(sl.v.size());
-    for (size_t k = 0; k < sl.v.size(); ++k) tree_nodes(sl.v[k].first, sl.v[k].second, trees[k]);
+    // per (l, h, slot) node lists: the trees differ between units
+    const int64_t nsl = (int64_t)sl.v.size();
+    vector<vector<Node>> trees((size_t)(Ly * H * nsl));
+    for (int l = 0; l < Ly; ++l)
+      for (int h = 0; h < H; ++h)
+        for (int64_t k = 0; k < nsl; ++k)
+          slot_nodes(node_topo, (int64_t)l * H + h, T, a0, sl.v[k].first, sl.v[k].second,
+                     trees[(size_t)(((int64_t)l * H + h) * nsl + k)]);
     auto push = [&](int64_t base, int slot, int node) {
       const int64_t o = node < 0 ? base : base + 1 + node;
       heap.push(Item{rank_key(op_util[o]), o, base, slot, node});
@@ -780,17 +899,18 @@ extern "C" void ko_auction(const ko_shape* sh, const ko_params* p, const float* 
       const vector<Node>& nd = trees[slot];
       out.clear();
       if (node < 0) {
-        if (nd[0].lc >= 0) out.push_back(0);
+        if (nd[0].nch > 0) out.push_back(0);
       } else {
-        for (int ch : {nd[node].lc, nd[node].rc})
-          if (nd[ch].lc >= 0) out.push_back(ch);
+        for (int x = 0; x < nd[node].nch; ++x)
+          if (nd[nd[node].ch[x]].nch > 0) out.push_back(nd[node].ch[x]);
       }
     };
     vector<int> stack, ch;
     for (int l = 0; l < Ly; ++l)
       for (int h = 0; h < H; ++h)
-        for (size_t k = 0; k < sl.v.size(); ++k) {
+        for (int64_t k = 0; k < nsl; ++k) {
           const int64_t base = ((int64_t)l * H + h) * 2 * T + 2 * (a0 + sl.v[k].first);
+          const int tid = (int)(((int64_t)l * H + h) * nsl + k);
           // exposed ops given the floor's choices
           stack.assign(1, -1);
           while (!stack.empty()) {
@@ -798,10 +918,10 @@ extern "C" void ko_auction(const ko_shape* sh, const ko_params* p, const float* 
             stack.pop_back();
             const int64_t o = node < 0 ? base : base + 1 + node;
             if (taken[o]) {
-              children((int)k, node, ch);
+              children(tid, node, ch);
               stack.insert(stack.end(), ch.begin(), ch.end());
             } else {
-              push(base, (int)k, node);
+              push(base, tid, node);
             }
           }
         }
@@ -861,9 +981,8 @@ void frontier(const vector<Node>& nodes, const uint8_t* taken, int64_t base, vec
   while (!stack.empty()) {
     const int j = stack.back();
     stack.pop_back();
-    if (nodes[j].lc >= 0 && taken[base + 1 + j]) {
-      stack.push_back(nodes[j].rc);
-      stack.push_back(nodes[j].lc);
+    if (nodes[j].nch > 0 && taken[base + 1 + j]) {
+      for (int x = nodes[j].nch - 1; x >= 0; --x) stack.push_back(nodes[j].ch[x]);
     } else {
       out.push_back(j);
     }
@@ -878,8 +997,8 @@ struct Ent {
   int node;
   int64_t slot_first;
 };
-void segment_entries(const ko_shape* sh, const ko_params* p, const uint8_t* taken, const SlotList& sl, int s, int l,
-                     int h, vector<Ent>& out) {
+void segment_entries(const ko_shape* sh, const ko_params* p, const uint8_t* taken, const uint32_t* node_topo,
+                     const SlotList& sl, int s, int l, int h, vector<Ent>& out) {
   const int H = sh->H;
   const int64_t T = sh->T, a0 = sh->cu[s], L = sh->cu[s + 1] - a0;
   const Reg rg = regions_of(L, p);
@@ -892,7 +1011,7 @@ void segment_entries(const ko_shape* sh, const ko_params* p, const uint8_t* take
     vector<Node> nodes;
     vector<int> fr;
     for (const auto& slot : sl.v) {
-      tree_nodes(slot.first, slot.second, nodes);
+      slot_nodes(node_topo, (int64_t)l * H + h, T, a0, slot.first, slot.second, nodes);
       const int64_t base = ((int64_t)l * H + h) * 2 * T + 2 * (a0 + slot.first);
       frontier(nodes, taken, base, fr);
       for (int j : fr) {
@@ -908,13 +1027,14 @@ void segment_entries(const ko_shape* sh, const ko_params* p, const uint8_t* take
 }  // namespace
 
 extern "C" int64_t ko_pack_count(const ko_shape* sh, const ko_params* p, const uint8_t* taken,
-                                 const int32_t* slot_start, const int32_t* n_slots, int32_t stride) {
+                                 const uint32_t* node_topo, const int32_t* slot_start, const int32_t* n_slots,
+                                 int32_t stride) {
   int64_t tot = 0;
 #pragma omp parallel for reduction(+ : tot) schedule(dynamic, 1)
   for (int64_t x = 0; x < (int64_t)sh->Ly * sh->H * sh->S; ++x) {
     const int l = (int)(x / (sh->H * sh->S)), h = (int)(x / sh->S % sh->H), s = (int)(x % sh->S);
     vector<Ent> ents;
-    segment_entries(sh, p, taken, slots_of(slot_start, n_slots, stride, s), s, l, h, ents);
+    segment_entries(sh, p, taken, node_topo, slots_of(slot_start, n_slots, stride, s), s, l, h, ents);
     tot += (int64_t)ents.size();
   }
   return tot;
@@ -925,7 +1045,7 @@ extern "C" int64_t ko_pack_count(const ko_shape* sh, const ko_params* p, const u
 // original bits with ln mu 0 and its position; an internal node's prototype
 // rounded to the cache dtype, ln mu and p_rep), recent window, suffix.
 extern "C" void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, const void* V, const float* rel,
-                        const float* node_rel, const float* node_mu, const uint8_t* taken,
+                        const float* node_rel, const float* node_mu, const uint32_t* node_topo, const uint8_t* taken,
                         const int32_t* slot_start, const int32_t* n_slots, int32_t stride, void* Kp, void* Vp,
                         float* lnmu, int32_t* pos, int64_t* seg_off, int32_t* seg_len) {
   const int Ly = sh->Ly, H = sh->H, S = sh->S, d = sh->d, dt = sh->dtype;
@@ -941,7 +1061,7 @@ extern "C" void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, c
   for (int64_t x = 0; x < nseg; ++x) {
     const int l = (int)(x / (H * S)), h = (int)(x / S % H), s = (int)(x % S);
     vector<Ent> ents;
-    segment_entries(sh, p, taken, slots_of(slot_start, n_slots, stride, s), s, l, h, ents);
+    segment_entries(sh, p, taken, node_topo, slots_of(slot_start, n_slots, stride, s), s, l, h, ents);
     cnt[x] = (int64_t)ents.size();
   }
   vector<int64_t> off((size_t)nseg);
@@ -962,7 +1082,7 @@ extern "C" void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, c
       const int l = (int)(x / (H * S)), h = (int)(x / S % H), s = (int)(x % S);
       const int64_t a0 = sh->cu[s];
       const int64_t ub = ((int64_t)l * H + h) * T + a0;
-      segment_entries(sh, p, taken, slots_of(slot_start, n_slots, stride, s), s, l, h, ents);
+      segment_entries(sh, p, taken, node_topo, slots_of(slot_start, n_slots, stride, s), s, l, h, ents);
       int64_t e = off[x];
       for (const Ent& en : ents) {
         if (en.kind == 0) {

@@ -16,7 +16,9 @@
  *   K, V    [Ly][H][T][d]        Qp [S][Ly][H*G][P][d]    Qctx [Ly][H*G][T][d]
  *   per-token [Ly][H][T]          tree arrays [Ly][H][2T]  (slot at global
  *   token t0 of unit (l,h): node j at (l*H+h)*2T + 2*t0 + j, op 0 = Add,
- *   op 1+j = Split(node j))
+ *   op 1+j = Split(node j); node_topo records: bits 0-7 first token - t0,
+ *   8-15 length - 1, 16-23 parent + 1, 24-31 next sibling, 0xFFFFFFFF past
+ *   the slot's last node; a NULL node_topo means midpoint trees)
  * dtype 1 = bf16 bits (uint16), 0 = fp32. Outputs that feed a decision
  * downstream (relevance, sensitivity, utilities) are rounded to fp32, as the
  * stages hand them over.
@@ -47,6 +49,7 @@ typedef struct ko_params {
   int32_t token_mode, slot_len, slot_min, slot_max, slot_target;
   float lambda_len, lambda_curv, lambda_surp;
   double rope_base;
+  int32_t split_mode;     /* 0 midpoint trees; 1 curvature-candidate cuts + salient three-way splits */
 } ko_params;
 
 /* threads the OpenMP loops use */
@@ -73,27 +76,31 @@ void ko_slot_costs(const ko_shape* sh, const ko_params* p, const void* hidden, i
  * slot_len == 0 (cost_q/cut_q from ko_slot_costs), fixed lengths otherwise */
 void ko_slots(const ko_shape* sh, const ko_params* p, const int64_t* cost_q, const int64_t* cut_q, int32_t stride,
               int32_t* slot_start, int32_t* n_slots);
-/* prototype trees: node_rel/node_D/node_mu/op_util f32, op_cost u8, all [Ly][H][2T] */
+/* prototype trees: node_rel/node_D/node_mu/op_util f32, op_cost u8, node_topo
+ * u32 (nullable), all [Ly][H][2T]; cut_q [T] (nullable) the partition's cut
+ * scores for split_mode 1 */
 void ko_build_trees(const ko_shape* sh, const ko_params* p, const void* K, const void* V, const void* Qp,
                     const float* lse, const float* rel, const float* sens, const int32_t* slot_start,
-                    const int32_t* n_slots, int32_t stride, float* node_rel, float* node_D, float* node_mu,
-                    float* op_util, uint8_t* op_cost);
+                    const int32_t* n_slots, int32_t stride, const int64_t* cut_q, float* node_rel, float* node_D,
+                    float* node_mu, float* op_util, uint8_t* op_cost, uint32_t* node_topo);
 /* singleton floor: taken [Ly][H][2T] u8 (floor ops), spent [S] */
 void ko_floor(const ko_shape* sh, const ko_params* p, const float* rel, const float* sens, const uint8_t* op_cost,
-              const int32_t* slot_start, const int32_t* n_slots, int32_t stride, uint8_t* taken, int64_t* spent);
+              const uint32_t* node_topo, const int32_t* slot_start, const int32_t* n_slots, int32_t stride,
+              uint8_t* taken, int64_t* spent);
 /* best-first auction after the floor: taken and spent are updated in place */
 void ko_auction(const ko_shape* sh, const ko_params* p, const float* op_util, const uint8_t* op_cost,
-                const int32_t* slot_start, const int32_t* n_slots, int32_t stride, uint8_t* taken,
-                int64_t* spent);
+                const uint32_t* node_topo, const int32_t* slot_start, const int32_t* n_slots, int32_t stride,
+                uint8_t* taken, int64_t* spent);
 /* token mode: taken [Ly][H][T], spent [S] */
 void ko_token_topk(const ko_shape* sh, const ko_params* p, const float* rel, uint8_t* taken, int64_t* spent);
 /* entries pack writes (to size its outputs) */
-int64_t ko_pack_count(const ko_shape* sh, const ko_params* p, const uint8_t* taken, const int32_t* slot_start,
-                      const int32_t* n_slots, int32_t stride);
+int64_t ko_pack_count(const ko_shape* sh, const ko_params* p, const uint8_t* taken, const uint32_t* node_topo,
+                      const int32_t* slot_start, const int32_t* n_slots, int32_t stride);
 /* the packed cache: Kp, Vp [N][d] in the cache dtype, lnmu [N] f32, pos [N]
  * i32, seg_off/seg_len [S][Ly][H] */
 void ko_pack(const ko_shape* sh, const ko_params* p, const void* K, const void* V, const float* rel,
-             const float* node_rel, const float* node_mu, const uint8_t* taken, const int32_t* slot_start,
+             const float* node_rel, const float* node_mu, const uint32_t* node_topo, const uint8_t* taken,
+             const int32_t* slot_start,
              const int32_t* n_slots, int32_t stride, void* Kp, void* Vp, float* lnmu, int32_t* pos,
              int64_t* seg_off, int32_t* seg_len);
 /* one decode step t over a ragged cache (K/V rows in `dtype`, lnmu nullable)

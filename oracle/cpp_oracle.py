@@ -46,7 +46,7 @@ class Params(C.Structure):
                 ("floor_frac", C.c_float), ("token_mode", C.c_int32), ("slot_len", C.c_int32),
                 ("slot_min", C.c_int32), ("slot_max", C.c_int32), ("slot_target", C.c_int32),
                 ("lambda_len", C.c_float), ("lambda_curv", C.c_float), ("lambda_surp", C.c_float),
-                ("rope_base", C.c_double)]
+                ("rope_base", C.c_double), ("split_mode", C.c_int32)]
 
 
 _lib = None
@@ -111,7 +111,7 @@ def _params(cfg):
                   token_mode=int(bool(cfg.token_mode)), slot_len=cfg.slot_len, slot_min=cfg.slot_min,
                   slot_max=cfg.slot_max, slot_target=cfg.slot_target, lambda_len=cfg.lambda_len,
                   lambda_curv=cfg.lambda_curv, lambda_surp=getattr(cfg, "lambda_surp", 0.0),
-                  rope_base=float(cfg.rope_base))
+                  rope_base=float(cfg.rope_base), split_mode=int(getattr(cfg, "split_mode", 0)))
 
 
 def _dtype_of(t):
@@ -212,7 +212,9 @@ def slots_for(cu, cfg, cost_q=None, cut_q=None):
     return slots_from_arrays(*slot_arrays(cu, cfg, cost_q, cut_q))
 
 
-def build_trees(K, V, Qp, lse, rel, head_sens, cu, slots, cfg):
+def build_trees(K, V, Qp, lse, rel, head_sens, cu, slots, cfg, cut_q=None):
+    """Tree arrays as the Python oracle's build_trees (node_topo included);
+    cut_q: the partition's int64 [T] cut scores (split_mode 1) or None."""
     kp = _Keep()
     sh = _shape(cu, cfg, _DT[K.dtype])
     stride = slot_stride(cu, cfg)
@@ -220,15 +222,21 @@ def build_trees(K, V, Qp, lse, rel, head_sens, cu, slots, cfg):
     shp = (cfg.Ly, cfg.H, 2 * sh.T)
     out = {k: np.zeros(shp, dtype=np.float32) for k in ("node_rel", "node_D", "node_mu", "op_util")}
     out["op_cost"] = np.zeros(shp, dtype=np.uint8)
+    out["node_topo"] = np.full(shp, 0xFFFFFFFF, dtype=np.uint32)
+    cq = None if cut_q is None else np.asarray(cut_q, dtype=np.int64)
     lib().ko_build_trees(C.byref(sh), C.byref(_params(cfg)), kp.ptr(K), kp.ptr(V), kp.ptr(Qp),
                          kp.ptr(np.asarray(lse, dtype=np.float32)), kp.ptr(np.asarray(rel, dtype=np.float32)),
                          kp.ptr(np.asarray(head_sens, dtype=np.float32)), kp.ptr(ss), kp.ptr(ns), C.c_int32(stride),
-                         kp.ptr(out["node_rel"]), kp.ptr(out["node_D"]), kp.ptr(out["node_mu"]),
-                         kp.ptr(out["op_util"]), kp.ptr(out["op_cost"]))
+                         kp.ptr(cq), kp.ptr(out["node_rel"]), kp.ptr(out["node_D"]), kp.ptr(out["node_mu"]),
+                         kp.ptr(out["op_util"]), kp.ptr(out["op_cost"]), kp.ptr(out["node_topo"]))
     return out
 
 
-def floor_select(rel, head_sens, op_cost, cu, slots, cfg):
+def _topo(topo):
+    return None if topo is None else np.asarray(topo, dtype=np.uint32)
+
+
+def floor_select(rel, head_sens, op_cost, cu, slots, cfg, topo=None):
     kp = _Keep()
     sh = _shape(cu, cfg, 1)
     stride = slot_stride(cu, cfg)
@@ -237,11 +245,11 @@ def floor_select(rel, head_sens, op_cost, cu, slots, cfg):
     spent = np.zeros((sh.S,), dtype=np.int64)
     lib().ko_floor(C.byref(sh), C.byref(_params(cfg)), kp.ptr(np.asarray(rel, dtype=np.float32)),
                    kp.ptr(np.asarray(head_sens, dtype=np.float32)), kp.ptr(np.asarray(op_cost, dtype=np.uint8)),
-                   kp.ptr(ss), kp.ptr(ns), C.c_int32(stride), kp.ptr(taken), kp.ptr(spent))
+                   kp.ptr(_topo(topo)), kp.ptr(ss), kp.ptr(ns), C.c_int32(stride), kp.ptr(taken), kp.ptr(spent))
     return taken, spent
 
 
-def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg):
+def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg, topo=None):
     kp = _Keep()
     sh = _shape(cu, cfg, 1)
     stride = slot_stride(cu, cfg)
@@ -249,8 +257,8 @@ def auction(op_util, op_cost, floor_taken, spent_floor, cu, slots, cfg):
     taken = np.array(floor_taken, dtype=np.uint8, copy=True)
     spent = np.array(spent_floor, dtype=np.int64, copy=True)
     lib().ko_auction(C.byref(sh), C.byref(_params(cfg)), kp.ptr(np.asarray(op_util, dtype=np.float32)),
-                     kp.ptr(np.asarray(op_cost, dtype=np.uint8)), kp.ptr(ss), kp.ptr(ns), C.c_int32(stride),
-                     kp.ptr(taken), kp.ptr(spent))
+                     kp.ptr(np.asarray(op_cost, dtype=np.uint8)), kp.ptr(_topo(topo)), kp.ptr(ss), kp.ptr(ns),
+                     C.c_int32(stride), kp.ptr(taken), kp.ptr(spent))
     return taken, spent
 
 
@@ -273,8 +281,9 @@ def pack(K, V, rel, trees, taken, cu, slots, cfg):
     stride = slot_stride(cu, cfg)
     ss, ns = slots_to_arrays(slots, stride)
     tk = np.asarray(taken, dtype=np.uint8)
-    N = int(lib().ko_pack_count(C.byref(sh), C.byref(_params(cfg)), kp.ptr(tk), kp.ptr(ss), kp.ptr(ns),
-                                C.c_int32(stride)))
+    topo = _topo(trees.get("node_topo")) if trees is not None else None
+    N = int(lib().ko_pack_count(C.byref(sh), C.byref(_params(cfg)), kp.ptr(tk), kp.ptr(topo), kp.ptr(ss),
+                                kp.ptr(ns), C.c_int32(stride)))
     rdt = np.uint16 if dt == 1 else np.float32
     out = {"K": np.zeros((N, cfg.d), dtype=rdt), "V": np.zeros((N, cfg.d), dtype=rdt),
            "lnmu": np.zeros(N, dtype=np.float32), "pos": np.zeros(N, dtype=np.int32),
@@ -283,7 +292,8 @@ def pack(K, V, rel, trees, taken, cu, slots, cfg):
     nr = trees["node_rel"] if trees is not None else np.zeros(1, dtype=np.float32)
     nm = trees["node_mu"] if trees is not None else np.zeros(1, dtype=np.float32)
     lib().ko_pack(C.byref(sh), C.byref(_params(cfg)), kp.ptr(K), kp.ptr(V), kp.ptr(np.asarray(rel, dtype=np.float32)),
-                  kp.ptr(np.asarray(nr, dtype=np.float32)), kp.ptr(np.asarray(nm, dtype=np.float32)), kp.ptr(tk),
+                  kp.ptr(np.asarray(nr, dtype=np.float32)), kp.ptr(np.asarray(nm, dtype=np.float32)), kp.ptr(topo),
+                  kp.ptr(tk),
                   kp.ptr(ss), kp.ptr(ns), C.c_int32(stride), kp.ptr(out["K"]), kp.ptr(out["V"]),
                   kp.ptr(out["lnmu"]), kp.ptr(out["pos"]), kp.ptr(out["seg_off"]), kp.ptr(out["seg_len"]))
     return out
@@ -377,12 +387,14 @@ def compress(inp, cfg, timings=None):
             out["dp_cost_q"], out["dp_cut_q"] = cost_q, cut_q
         slots = slots_for(cu, cfg, cost_q, cut_q)
         t = tick("partition", t)
-        trees = build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"], cu, slots, cfg)
+        trees = build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"], cu, slots, cfg,
+                            cut_q=cut_q)
         out["trees"] = trees
         t = tick("trees", t)
-        ftaken, fspent = floor_select(rel, sc["head_sens"], trees["op_cost"], cu, slots, cfg)
+        topo = trees["node_topo"]
+        ftaken, fspent = floor_select(rel, sc["head_sens"], trees["op_cost"], cu, slots, cfg, topo=topo)
         out["floor_taken"], out["floor_spent"] = ftaken, fspent
-        taken, spent = auction(trees["op_util"], trees["op_cost"], ftaken, fspent, cu, slots, cfg)
+        taken, spent = auction(trees["op_util"], trees["op_cost"], ftaken, fspent, cu, slots, cfg, topo=topo)
         t = tick("auction", t)
     out["slots"], out["taken"], out["spent"] = slots, taken, spent
     out["cache"] = pack(inp["K"], inp["V"], rel, trees, taken, cu, slots, cfg)

@@ -17,7 +17,9 @@ from oracle import cpp_oracle as co
 from workload import small_config, make_inputs
 
 CASES = [("tiny", {}), ("mistral1", {}), ("fulldepth", {}), ("stress", {}), ("stress8", {}), ("ragged", {}),
-         ("fulldepth", {"n_depth": 3, "surprisal": True}), ("ragged", {"budget_ratio": 0.6, "floor_frac": 0.3})]
+         ("fulldepth", {"n_depth": 3, "surprisal": True}), ("ragged", {"budget_ratio": 0.6, "floor_frac": 0.3}),
+         ("tiny", {"split_mode": 1}), ("fulldepth", {"split_mode": 1}),
+         ("ragged", {"split_mode": 1, "floor_frac": 0.3})]
 
 
 def _close(a, b, name, rtol=2.0 ** -22):
@@ -57,11 +59,17 @@ def test_slots_trees_and_selection(both):
         for k in ("node_rel", "node_D", "node_mu", "op_util"):
             _close(b["trees"][k], a["trees"][k], k)
         assert np.array_equal(a["trees"]["op_cost"], b["trees"]["op_cost"])
+        assert np.array_equal(a["trees"]["node_topo"], b["trees"]["node_topo"])
+        # the tree shapes on the Python oracle's fp32 relevance: bit-exact
+        tr = co.build_trees(inp["K"], inp["V"], inp["Qp"], a["lse"], a["rel"], a["head_sens"], cu, a["slots"], cfg,
+                            cut_q=a.get("dp_cut_q"))
+        assert np.array_equal(tr["node_topo"], a["trees"]["node_topo"])
         # floor and auction on the Python oracle's fp32 inputs: bit-exact
-        ft, fs = co.floor_select(a["rel"], a["head_sens"], a["trees"]["op_cost"], cu, a["slots"], cfg)
+        topo = a["trees"]["node_topo"]
+        ft, fs = co.floor_select(a["rel"], a["head_sens"], a["trees"]["op_cost"], cu, a["slots"], cfg, topo=topo)
         assert np.array_equal(ft, a["floor_taken"]) and np.array_equal(fs, a["floor_spent"])
         tk, sp = co.auction(a["trees"]["op_util"], a["trees"]["op_cost"], a["floor_taken"], a["floor_spent"], cu,
-                            a["slots"], cfg)
+                            a["slots"], cfg, topo=topo)
         assert np.array_equal(tk, a["taken"]) and np.array_equal(sp, a["spent"])
     else:
         tk, sp = co.token_topk(a["rel"], cu, cfg)
@@ -89,9 +97,10 @@ def test_pack_decode_kl(both):
     assert np.abs(b["kl"] - a["kl"]).max() <= 1e-5
 
 
-@pytest.mark.parametrize("name", ["tiny", "stress", "ragged", "mistral1"])
-def test_cpp_full_budget_is_the_identity(name):
-    cfg = small_config(name).replace(budget_ratio=1.0)
+@pytest.mark.parametrize("name,mode", [("tiny", 0), ("stress", 0), ("ragged", 0), ("mistral1", 0), ("tiny", 1),
+                                       ("fulldepth", 1)])
+def test_cpp_full_budget_is_the_identity(name, mode):
+    cfg = small_config(name).replace(budget_ratio=1.0, split_mode=mode)
     inp = make_inputs(cfg)
     cu = inp["cu_seqlens"].numpy()
     o = co.run_pipeline(inp, cfg)
