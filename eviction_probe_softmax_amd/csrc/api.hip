@@ -58,6 +58,7 @@ int validate_params(const kvc_shape* s, const kvc_params* p) {
                 "slot_max must be >= 2*slot_min-1 so every long region can be cut");
     KVC_REQUIRE(p->slot_target >= 1, KVC_E_INVAL, "slot_target must be >= 1");
   }
+  KVC_REQUIRE(p->split_mode == 0 || p->split_mode == 1, KVC_E_INVAL, "split_mode must be 0 or 1");
   return KVC_OK;
 }
 
@@ -115,6 +116,7 @@ extern "C" void kvc_params_default(kvc_params* p) {
   p->window = 64;
   p->n_depth = 1;
   p->lambda_surp = 1.0f;
+  p->split_mode = 0;
 }
 
 extern "C" int kvc_budgets(const kvc_shape* shape, const kvc_params* prm, int64_t* B,

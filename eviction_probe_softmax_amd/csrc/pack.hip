@@ -7,11 +7,12 @@
 // inverse-rotated keys re-rotated at a representative position, the value is
 // relevance weighted with a uniform base.
 //
-// Every taken op adds exactly one stored entry (Add creates the root, a
-// binary Split replaces one node by two), so the entries of a slot are the
-// taken ops of its 2n op range. Per token t the count c[t] is: 1 for exact
-// tokens, taken[t] in token mode, taken[2t] + taken[2t+1] inside slots (the
-// slot starting at t0 owns ops [2 t0, 2 t0 + 2n)). One exclusive scan over the
+// Every taken op adds op_cost stored entries (Add creates the root; a Split
+// replaces one node by its children: 1 for a binary split, 2 for a three-way
+// one), so the entries of a slot are the costs of the taken ops of its 2n op
+// range. Per token t the count c[t] is: 1 for exact tokens, taken[t] in token
+// mode, the taken costs of ops 2t and 2t+1 inside slots (the slot starting at
+// t0 owns ops [2 t0, 2 t0 + 2n)). One exclusive scan over the
 // whole [Ly][H][T] count array - whose order is exactly the (l, h, s, t) order
 // of the segments - gives every token's (and every slot's first) output
 // offset. Writers: exact/kept tokens copy their bits; one wave per slot walks
@@ -34,6 +35,8 @@ struct PackArgs {
   const float* node_rel;
   const float* node_mu;
   const uint8_t* taken;
+  const uint8_t* op_cost;   // explicit trees: entries each op adds (NULL: 1 each)
+  const uint32_t* topo;     // explicit trees' node records (NULL: midpoint trees)
   const int32_t* slot_start;
   const int32_t* n_slots;
   const float* rc;  // rope cos [pos][d/2]
@@ -65,7 +68,8 @@ __global__ void count_kernel(PackArgs a, int32_t* cnt) {
   else if (a.token_mode) c = a.taken[i];
   else {
     int64_t o = lh * 2 * a.T + 2 * t;
-    c = a.taken[o] + a.taken[o + 1];
+    c = a.op_cost ? (a.taken[o] ? a.op_cost[o] : 0) + (a.taken[o + 1] ? a.op_cost[o + 1] : 0)
+                  : a.taken[o] + a.taken[o + 1];
   }
   cnt[i] = c;
 }
@@ -249,11 +253,19 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
   const uint8_t* tk = a.taken + obase;
   if (!tk[0]) return;                                 // Add not taken: no entry
   const int64_t dst0 = off[lh * a.T + tok0];
-  // frontier flags: one node per thread (pre-order walk from the root)
-  const int m = 2 * n - 1;
+  // frontier flags: one node per thread (its record, or a pre-order walk of
+  // the midpoint tree from the root)
   bool fl = false;
   int st = 0, sz = n;
-  if (tid < m) {
+  if (a.topo) {
+    const uint32_t x = tid < 2 * n ? a.topo[obase + tid] : 0xFFFFFFFFu;
+    if (x != 0xFFFFFFFFu) {
+      st = (int)(x & 255);
+      sz = (int)((x >> 8) & 255) + 1;
+      const int par = (int)((x >> 16) & 255) - 1;
+      fl = tk[par < 0 ? 0 : 1 + par] && !(sz > 1 && tk[1 + tid]);
+    }
+  } else if (tid < 2 * n - 1) {
     int cur = 0, par = -1;
     while (cur != tid) {
       const int nl = (sz + 1) >> 1;
@@ -461,6 +473,11 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
   a.node_rel = trees ? trees->node_rel : nullptr;
   a.node_mu = trees ? trees->node_mu : nullptr;
   a.taken = op_taken;
+  if (!p->token_mode && p->split_mode == 1) {
+    KVC_REQUIRE(trees->node_topo && trees->op_cost, KVC_E_INVAL, "kvc_pack: split_mode 1 needs node_topo and op_cost");
+    a.topo = trees->node_topo;
+    a.op_cost = trees->op_cost;
+  }
   a.slot_start = slot_start;
   a.n_slots = n_slots;
   a.rc = rope_cos;

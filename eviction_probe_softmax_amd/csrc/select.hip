@@ -110,14 +110,14 @@ struct CandSrc {      // floor candidates with their marginal path costs
     return true;
   }
 };
-struct OpSrc {        // auction: untaken real ops keyed by beta
+struct OpSrc {        // auction: untaken real ops keyed by beta, weighted by the entries they add
   const uint64_t* beta;
   const uint8_t* cost;
   const uint8_t* taken;
   __device__ bool get(int64_t i, int s, uint64_t& k, int64_t& w) const {
     if (cost[i] == 0 || taken[i]) return false;
     k = beta[i];
-    w = 1;
+    w = cost[i];
     return true;
   }
 };
@@ -286,10 +286,16 @@ struct TreeArgs {
   const int64_t* cu;
   const int32_t* slot_start;  // [S][stride+1]
   const int32_t* n_slots;
+  const uint32_t* topo;       // node records [Ly][H][2T] (split_mode 1), or NULL: midpoint trees
   int stride;
   int S, Ly, H;
   int64_t T;
 };
+constexpr uint32_t TOPO_NONE = 0xFFFFFFFFu;
+constexpr int MAX_PATH = 16;  // internal nodes on a root-to-leaf path: 7 for midpoint trees of 128
+                              // tokens, 14 for the explicit trees (children <= n - ceil(n/4) tokens)
+__device__ __forceinline__ int topo_len(uint32_t x) { return (int)((x >> 8) & 255) + 1; }
+__device__ __forceinline__ int topo_parent(uint32_t x) { return (int)((x >> 16) & 255) - 1; }
 
 // slot of sequence position t (binary search over the slot starts)
 __device__ __forceinline__ int slot_of(const TreeArgs& a, int s, int t, int& t0, int& n) {
@@ -306,9 +312,28 @@ __device__ __forceinline__ int slot_of(const TreeArgs& a, int s, int t, int& t0,
 }
 
 // Root-to-leaf path of token t in a slot [t0, t0+n): writes internal node
-// pre-order indices, returns their count.
-__device__ __forceinline__ int leaf_path(int t0, int n, int t, int* nodes) {
-  int j = 0, st = t0, sz = n, c = 0;
+// pre-order indices, returns their count. rec: the slot's node records, or
+// NULL for the midpoint tree.
+__device__ __forceinline__ int leaf_path(const uint32_t* rec, int t0, int n, int t, int* nodes) {
+  int c = 0;
+  if (rec) {
+    const int tr = t - t0;
+    int j = 0;
+    uint32_t x = rec[0];
+    while (topo_len(x) > 1 && c < MAX_PATH) {
+      nodes[c++] = j;
+      int ch = j + 1;
+      uint32_t y = rec[ch];
+      while ((int)(y & 255) + topo_len(y) <= tr && (y >> 24) != 0) {   // the child holding t
+        ch = (int)(y >> 24);
+        y = rec[ch];
+      }
+      j = ch;
+      x = y;
+    }
+    return c;
+  }
+  int j = 0, st = t0, sz = n;
   while (sz > 1) {
     nodes[c++] = j;
     int nl = (sz + 1) >> 1;
@@ -364,9 +389,9 @@ __device__ __forceinline__ void cand_path(const FloorArgs& f, int s, int64_t lea
   int t = (int)(leaf % a.T - a.cu[s]);
   int t0, n;
   slot_of(a, s, t, t0, n);
-  int nodes[8];
-  int c = leaf_path(t0, n, t, nodes);
+  int nodes[MAX_PATH];
   int64_t base = lh * 2 * a.T + 2 * (a.cu[s] + t0);
+  int c = leaf_path(a.topo ? a.topo + base : nullptr, t0, n, t, nodes);
   ops[0] = base;
   for (int q = 0; q < c; ++q) ops[1 + q] = base + 1 + nodes[q];
   nops = 1 + c;
@@ -378,7 +403,7 @@ __global__ void floor_cover_kernel(FloorArgs f, int S) {
   int s = (int)(i / f.Fmax);
   int64_t k = i % f.Fmax;
   if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
-  int64_t ops[9];
+  int64_t ops[MAX_PATH + 1];
   int nops;
   cand_path(f, s, f.cid[i], ops, nops);
   uint64_t key = f.ckey[i];
@@ -389,7 +414,7 @@ __global__ void floor_cost_kernel(FloorArgs f, int S) {
   int s = (int)(i / f.Fmax);
   int64_t k = i % f.Fmax;
   if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
-  int64_t ops[9];
+  int64_t ops[MAX_PATH + 1];
   int nops;
   cand_path(f, s, f.cid[i], ops, nops);
   uint64_t key = f.ckey[i];
@@ -406,7 +431,7 @@ __global__ void floor_accept_kernel(FloorArgs f, int S, const SelState* st) {
   if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
   SelState S_ = st[s];
   if (!(S_.all || f.ckey[i] > S_.prefix)) return;
-  int64_t ops[9];
+  int64_t ops[MAX_PATH + 1];
   int nops;
   cand_path(f, s, f.cid[i], ops, nops);
   for (int q = 0; q < nops; ++q) f.taken[ops[q]] = 1;
@@ -447,7 +472,7 @@ __global__ __launch_bounds__(FT_THREADS) void floor_tail_kernel(FloorArgs f, con
       int64_t i = (int64_t)s * f.Fmax + k;
       uint64_t key = f.ckey[i];
       if (key >= pos) continue;
-      int64_t ops[9];
+      int64_t ops[MAX_PATH + 1];
       int nops;
       cand_path(f, s, f.cid[i], ops, nops);
       int c = 0;
@@ -462,7 +487,7 @@ __global__ __launch_bounds__(FT_THREADS) void floor_tail_kernel(FloorArgs f, con
     for (int64_t k = threadIdx.x; k < cnt; k += FT_THREADS) {
       int64_t i = (int64_t)s * f.Fmax + k;
       if (f.ckey[i] != win) continue;
-      int64_t ops[9];
+      int64_t ops[MAX_PATH + 1];
       int nops;
       cand_path(f, s, f.cid[i], ops, nops);
       int c = 0;
@@ -513,7 +538,16 @@ __global__ void beta_kernel(AucArgs a, Ranges r) {
       b = ~0ull;
       // Add
       if (!a.taken[sbase]) b = op_key(a, sbase);
-      if (jop > 0) {
+      if (jop > 0 && ta.topo) {     // explicit trees: up the parent chain
+        const uint32_t* rec = ta.topo + sbase;
+        for (int j = jop - 1; j >= 0; j = topo_parent(rec[j])) {
+          const int64_t o = sbase + 1 + j;
+          if (!a.taken[o]) {
+            uint64_t k = op_key(a, o);
+            if (k < b) b = k;
+          }
+        }
+      } else if (jop > 0) {
         int target = jop - 1;
         int j = 0, sz = nn;
         while (true) {
@@ -551,13 +585,17 @@ __global__ void auction_mark_kernel(AucArgs a, Ranges r, const SelState* st) {
 }
 
 // Finish the tied group below b* with a best-first walk; one block per
-// sequence (thread 0 works: the slot holds at most 2*128 ops).
+// sequence (thread 0 works: the slot holds at most 2*128 ops). An op that
+// costs more than what is left is discarded with its subtree (only a
+// three-way split, cost 2, can meet 1 entry left). kleft[s] receives what is
+// left after the walk (0 or 1).
 __global__ __launch_bounds__(64) void auction_fixup_kernel(AucArgs a, const SelState* st, const int64_t* spent_floor,
-                                                           int64_t* spent) {
-  __shared__ int sz_[256], lc_[256], rc_[256];
+                                                           int64_t* spent, int64_t* kleft) {
+  __shared__ int sz_[256], ns_[256];
   __shared__ uint8_t exposed[257];
   int s = blockIdx.x;
   if (threadIdx.x != 0) return;
+  kleft[s] = 0;
   SelState S_ = st[s];
   if (S_.all) {
     spent[s] = spent_floor[s] + S_.above;
@@ -575,25 +613,31 @@ __global__ __launch_bounds__(64) void auction_fixup_kernel(AucArgs a, const SelS
   int t0, nn;
   slot_of(ta, s, t, t0, nn);
   const int64_t sbase = lh * 2 * ta.T + 2 * (ta.cu[s] + t0);
-  // pre-order node table of the slot: pop a frame, number it, push right then left
-  struct Fr { int sz, parent, side; };
-  Fr fr[20];
-  int ftop = 0, m = 0;
-  fr[ftop++] = {nn, -1, 0};
-  while (ftop > 0) {
-    Fr q = fr[--ftop];
-    int j = m++;
-    sz_[j] = q.sz;
-    lc_[j] = -1;
-    rc_[j] = -1;
-    if (q.parent >= 0) {
-      if (q.side == 0) lc_[q.parent] = j;
-      else rc_[q.parent] = j;
+  // node table of the slot: sizes and next siblings (children of j: j + 1,
+  // then the sibling chain)
+  int m = 0;
+  if (ta.topo) {
+    const uint32_t* rec = ta.topo + sbase;
+    for (; m < 2 * nn && rec[m] != TOPO_NONE; ++m) {
+      sz_[m] = topo_len(rec[m]);
+      ns_[m] = (int)(rec[m] >> 24);
     }
-    if (q.sz > 1) {
-      int nl = (q.sz + 1) >> 1;
-      fr[ftop++] = {q.sz - nl, j, 1};
-      fr[ftop++] = {nl, j, 0};
+  } else {   // midpoint tree: pop a frame, number it, push right then left
+    struct Fr { int sz, sib_of; };
+    Fr fr[20];
+    int ftop = 0;
+    fr[ftop++] = {nn, -1};
+    while (ftop > 0) {
+      Fr q = fr[--ftop];
+      int j = m++;
+      sz_[j] = q.sz;
+      ns_[j] = 0;
+      if (q.sib_of >= 0) ns_[q.sib_of] = j;   // a right child is its left sibling's next
+      if (q.sz > 1) {
+        int nl = (q.sz + 1) >> 1;
+        fr[ftop++] = {q.sz - nl, j + 1};
+        fr[ftop++] = {nl, -1};
+      }
     }
   }
   // exposed[0] = Add, exposed[1+j] = Split(node j)
@@ -612,21 +656,69 @@ __global__ __launch_bounds__(64) void auction_fixup_kernel(AucArgs a, const SelS
     }
     if (best < 0) break;
     exposed[best] = 0;
+    const int c = a.cost[sbase + best];
+    if (c > k) continue;
     a.taken[sbase + best] = 2;
-    --k;
-    int kids[2], nk = 0;
-    if (best == 0) {
-      if (sz_[0] > 1) kids[nk++] = 1;
-    } else {
-      int j = best - 1;
-      if (lc_[j] >= 0 && sz_[lc_[j]] > 1) kids[nk++] = 1 + lc_[j];
-      if (rc_[j] >= 0 && sz_[rc_[j]] > 1) kids[nk++] = 1 + rc_[j];
-    }
-    for (int q = 0; q < nk; ++q) {
-      int64_t o = sbase + kids[q];
-      if (a.cost[o] != 0 && a.taken[o] == 0 && a.beta[o] == T) exposed[kids[q]] = 1;
+    k -= c;
+    // the ops of the nodes it creates: the root's split for Add, the
+    // children's splits for a split
+    int first = best == 0 ? 0 : best;                 // node index of the first created node
+    for (int ch = first; ; ) {
+      if (sz_[ch] > 1) {
+        int64_t o = sbase + 1 + ch;
+        if (a.cost[o] != 0 && a.taken[o] == 0 && a.beta[o] == T) exposed[1 + ch] = 1;
+      }
+      if (best == 0) break;
+      ch = ns_[ch];
+      if (ch == 0) break;
     }
   }
+  spent[s] = spent_floor[s] + S_.budget - k;
+  kleft[s] = k;
+}
+
+// After the walk, budget may be left that the tied group could not use (a
+// three-way split met 1 entry left): the greedy goes on with the best-keyed
+// op that is exposed (its creator taken) and fits. One pass finds it per
+// sequence (keys are unique), a second takes it; with at most 1 entry left
+// and costs of 1 or 2, one such op ends the auction.
+__global__ void auction_extend_kernel(AucArgs a, Ranges r, const int64_t* kleft, unsigned long long* best) {
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  const int64_t k = kleft[s];
+  if (k <= 0) return;
+  const TreeArgs& ta = a.ta;
+  unsigned long long loc = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t op = base + i;
+    const int c = a.cost[op];
+    if (c == 0 || c > k || a.taken[op]) continue;
+    const int64_t lh = op / (2 * ta.T);
+    const int tt = (int)(op % (2 * ta.T) / 2 - ta.cu[s]);
+    int t0, nn;
+    slot_of(ta, s, tt, t0, nn);
+    const int64_t sbase = lh * 2 * ta.T + 2 * (ta.cu[s] + t0);
+    const int jop = (int)(op - sbase);
+    int64_t creator = -1;                 // Add has none
+    if (jop == 1) creator = sbase;
+    else if (jop > 1) creator = sbase + 1 + topo_parent(ta.topo[sbase + jop - 1]);
+    if (creator >= 0 && !a.taken[creator]) continue;
+    const unsigned long long kk = op_key(a, op);
+    if (kk > loc) loc = kk;
+  }
+  if (loc) atomicMax(&best[s], loc);
+}
+
+__global__ void auction_extend_take_kernel(AucArgs a, int S, const unsigned long long* best, int64_t* kleft,
+                                           int64_t* spent) {
+  const int s = threadIdx.x;
+  if (s >= S || kleft[s] <= 0 || best[s] == 0) return;
+  const int64_t op = (int64_t)key_id(best[s]);
+  const int c = a.cost[op];
+  a.taken[op] = 2;
+  kleft[s] -= c;
+  spent[s] += c;
 }
 
 // ------------------------------------------------------------------ per-segment top-B
@@ -693,6 +785,8 @@ size_t ws_auction(const kvc_shape* s, const kvc_params* p) {
     c.take<int32_t>((size_t)s->n_seq * Fmax);
     c.take<int32_t>((size_t)s->n_seq * Fmax);
     c.take<int32_t>(MAXS);
+    c.take<int64_t>(MAXS);               // budget left after the tied group's walk
+    c.take<unsigned long long>(MAXS);    // best op that still fits
   }
   return c.off + 256;
 }
@@ -779,10 +873,12 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(MAXS), 0, stream, (unsigned long long*)ccount, (int64_t)MAXS / 2);
   KVC_LAUNCH_CHECK("zero_count");
 
+  KVC_REQUIRE(p->split_mode == 0 || trees->node_topo, KVC_E_INVAL, "kvc_auction: split_mode 1 needs node_topo");
   TreeArgs ta{};
   ta.cu = sh->cu_seqlens_d;
   ta.slot_start = slot_start;
   ta.n_slots = n_slots;
+  ta.topo = p->split_mode == 1 ? trees->node_topo : nullptr;
   ta.stride = kvc_slot_stride(sh, p);
   ta.S = sh->n_seq;
   ta.Ly = sh->n_layers;
@@ -874,9 +970,21 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
     hipLaunchKernelGGL(auction_mark_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops, st);
     KVC_LAUNCH_CHECK("auction_mark");
   }
+  int64_t* kleft = c.take<int64_t>(MAXS);
+  unsigned long long* xbest = c.take<unsigned long long>(MAXS);
   hipLaunchKernelGGL(auction_fixup_kernel, dim3(sh->n_seq), dim3(64), 0, stream, aa, st, (const int64_t*)sfloor,
-                     spent);
+                     spent, kleft);
   KVC_LAUNCH_CHECK("auction_fixup");
+  if (ta.topo && nbo > 0) {   // only three-way splits (cost 2) can leave budget after the walk
+    hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(MAXS), 0, stream, xbest, (int64_t)MAXS);
+    KVC_LAUNCH_CHECK("zero_extend");
+    hipLaunchKernelGGL(auction_extend_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops,
+                       (const int64_t*)kleft, xbest);
+    KVC_LAUNCH_CHECK("auction_extend");
+    hipLaunchKernelGGL(auction_extend_take_kernel, dim3(1), dim3(MAXS), 0, stream, aa, sh->n_seq,
+                       (const unsigned long long*)xbest, kleft, spent);
+    KVC_LAUNCH_CHECK("auction_extend_take");
+  }
   if (hybrid) {
     hipLaunchKernelGGL(add_whole_kernel, dim3(1), dim3(MAXS), 0, stream, sh->n_seq, whole, spent);
     KVC_LAUNCH_CHECK("add_whole");

@@ -62,6 +62,7 @@ struct TreeKArgs {
   float* node_mu;
   float* op_util;
   uint8_t* op_cost;
+  const uint32_t* topo;    // explicit node records (split_mode 1), else NULL: midpoint trees
 };
 
 // LDS layout (byte offsets, 16-byte aligned) for slots of at most NMAX tokens.
@@ -101,8 +102,10 @@ struct TreeLayout {
   static constexpr size_t nsz = al(nst + (size_t)2 * NMAX * 2);
   static constexpr size_t ndep = al(nsz + (size_t)2 * NMAX * 2);
   static constexpr size_t ilist = al(ndep + (size_t)2 * NMAX * 2);
-  static constexpr size_t misc = al(ilist + (size_t)NMAX * 2);
-  static constexpr size_t total = al(misc + 16);
+  static constexpr size_t npar = al(ilist + (size_t)NMAX * 2);
+  static constexpr size_t nsib = al(npar + (size_t)2 * NMAX * 2);
+  static constexpr size_t misc = al(nsib + (size_t)2 * NMAX * 2);
+  static constexpr size_t total = al(misc + 32);
   // phase-A scratch for the per-group value column sums lives in the weight array
   static_assert((size_t)(WAVES * 64 / (D / 8)) * D * 4 <= (size_t)NMAX * PA * 4, "value-sum scratch");
 };
@@ -268,7 +271,10 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
   int16_t* nsz = (int16_t*)(smem + Lo::nsz);
   int16_t* ndep = (int16_t*)(smem + Lo::ndep);
   int16_t* ilist = (int16_t*)(smem + Lo::ilist);
+  int16_t* npar = (int16_t*)(smem + Lo::npar);   // explicit trees: parent index (-1 root)
+  int16_t* nsib = (int16_t*)(smem + Lo::nsib);   // explicit trees: next sibling (0 none)
   float* misc = (float*)(smem + Lo::misc);
+  int* imisc = (int*)(misc + 4);           // explicit trees: node count, deepest level, root's last child
 
   __shared__ int pre[MAX_SEQ + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -293,7 +299,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     const int64_t lh = cur.lh;
     const int s = cur.s, t0 = cur.t0, n = cur.n;
     const int l = (int)(lh / a.H), h = (int)(lh % a.H);
-    const int m = 2 * n - 1, nint = n - 1;
+    int m = 2 * n - 1, nint = n - 1;       // midpoint trees; explicit trees set these below
     const int n32 = (n + 31) & ~31;
     const int64_t tok0 = a.cu[s] + t0;
     const int64_t obase = lh * 2 * a.T + 2 * tok0;
@@ -304,27 +310,60 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     const float* lse_g = a.lse + (int64_t)unit * a.G * a.P;
 
     // ---- A: node table, token data, value statistics, softmax weights
-    for (int j = tid; j < m; j += THREADS) {
-      int cu = 0, st = 0, sz = n, dep = 0;
-      while (cu != j) {
-        int nl = (sz + 1) >> 1;
-        if (j < cu + 2 * nl) {
-          cu += 1;
-          sz = nl;
-        } else {
-          cu += 2 * nl;
-          st += nl;
-          sz -= nl;
+    // (in any pre-order tree whose leaves are the tokens in order, the nodes
+    // before j are its ancestors and the subtrees left of it, whose leaves are
+    // the tokens left of st: so j - st internal nodes precede j)
+    if (a.topo) {
+      const uint32_t* rec = a.topo + obase;
+      for (int j = tid; j < 2 * n; j += THREADS) {
+        const uint32_t x = rec[j];
+        if (x == 0xFFFFFFFFu) continue;
+        const int st = (int)(x & 255), sz = (int)((x >> 8) & 255) + 1, par = (int)((x >> 16) & 255) - 1;
+        nst[j] = (int16_t)st;
+        nsz[j] = (int16_t)sz;
+        npar[j] = (int16_t)par;
+        nsib[j] = (int16_t)(x >> 24);
+        if (j + 1 == 2 * n || rec[j + 1] == 0xFFFFFFFFu) imisc[0] = j + 1;
+        if (par == 0 && (x >> 24) == 0) imisc[2] = j;
+        if (sz > 1) ilist[j - st] = (int16_t)j;
+        else {
+          nD[j] = 0.f;
+          nmu[j] = 1.f;
         }
-        ++dep;
       }
-      nst[j] = (int16_t)st;
-      nsz[j] = (int16_t)sz;
-      ndep[j] = (int16_t)dep;
-      if (sz > 1) ilist[j - st] = (int16_t)j;  // internal nodes before j = j - (leaves left of st)
-      else {
-        nD[j] = 0.f;
-        nmu[j] = 1.f;
+      if (tid == 0) imisc[1] = 0;
+      __syncthreads();
+      m = imisc[0];
+      nint = m - n;
+      for (int j = tid; j < m; j += THREADS) {
+        int dep = 0;
+        for (int p = npar[j]; p >= 0; p = npar[p]) ++dep;
+        ndep[j] = (int16_t)dep;
+        if (nsz[j] > 1) atomicMax(&imisc[1], dep);
+      }
+    } else {
+      for (int j = tid; j < m; j += THREADS) {
+        int cu = 0, st = 0, sz = n, dep = 0;
+        while (cu != j) {
+          int nl = (sz + 1) >> 1;
+          if (j < cu + 2 * nl) {
+            cu += 1;
+            sz = nl;
+          } else {
+            cu += 2 * nl;
+            st += nl;
+            sz -= nl;
+          }
+          ++dep;
+        }
+        nst[j] = (int16_t)st;
+        nsz[j] = (int16_t)sz;
+        ndep[j] = (int16_t)dep;
+        if (sz > 1) ilist[j - st] = (int16_t)j;
+        else {
+          nD[j] = 0.f;
+          nmu[j] = 1.f;
+        }
       }
     }
     for (int rho = tid; rho < PDMAX; rho += THREADS) lse_s[rho] = rho < pd ? lse_g[(int64_t)rho * a.pstride] : 0.f;
@@ -453,16 +492,28 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       if (pd < PDMAX)
         for (int it = tid; it < n * (PDMAX - pd); it += THREADS) At[(it / (PDMAX - pd)) * PA + pd + it % (PDMAX - pd)] = 0.f;
     }
-    // bottom-up value flow by height (children of pre-order node j: j+1 and j + 2 ceil(sz/2))
+    // bottom-up value flow: a parent is the fp32 sum of its children, left to right
     for (int j = tid; j < m; j += THREADS)
       if (nsz[j] == 1) nrel[j] = rtok[nst[j]];
     __syncthreads();
-    for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
-      for (int j = tid; j < m; j += THREADS) {
-        int sz = nsz[j];
-        if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
+    if (a.topo) {  // by depth, deepest internal level first (first child j+1, then the sibling chain)
+      for (int dd = imisc[1]; dd >= 0; --dd) {
+        for (int j = tid; j < m; j += THREADS)
+          if (nsz[j] > 1 && ndep[j] == dd) {
+            float sum = nrel[j + 1];
+            for (int c = nsib[j + 1]; c != 0; c = nsib[c]) sum += nrel[c];
+            nrel[j] = sum;
+          }
+        __syncthreads();
       }
-      __syncthreads();
+    } else {  // by height (children of pre-order node j: j+1 and j + 2 ceil(sz/2))
+      for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
+        for (int j = tid; j < m; j += THREADS) {
+          int sz = nsz[j];
+          if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
+        }
+        __syncthreads();
+      }
     }
 
     // ---- B: prototype keys, multiplicity, attention-partition error
@@ -699,10 +750,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           if (ti != tj) Gm[cc * NG + r] = acc[v];
         }
       }
-      // the root (c = 0) and its children (c = 1, 2) are shared by every wave
-      const int nl0 = (n + 1) >> 1;
-      auto coop_j = [&](int c) { return c == 0 ? 0 : (c == 1 ? 1 : 2 * nl0); };
-      auto coop_ok = [&](int c) { return c == 0 ? n >= 2 : (c == 1 ? nl0 >= 2 : n - nl0 >= 2); };
+      // the root (c = 0) and its first and last children (c = 1, 2) are shared by
+      // every wave; a three-way root's middle child is a single token
+      const int rlast = a.topo ? imisc[2] : 2 * ((n + 1) >> 1);
+      auto coop_j = [&](int c) { return c == 0 ? 0 : (c == 1 ? 1 : rlast); };
+      auto coop_ok = [&](int c) { return nsz[coop_j(c)] >= 2; };
       if (wave < 3 && coop_ok(wave)) {
         const int j = coop_j(wave);
         const int st = nst[j], sz = nsz[j];
@@ -794,10 +846,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         u = sens * (nrel[0] * (1.f - nD[0]));
         cst = 1;
       } else if (q - 1 < m && nsz[q - 1] > 1) {
-        int j = q - 1, lc = j + 1, rc = j + 2 * ((nsz[j] + 1) >> 1);
-        float gain = nrel[j] * nD[j] - (nrel[lc] * nD[lc] + nrel[rc] * nD[rc]);
-        u = sens * gain;
-        cst = 1;
+        const int j = q - 1;
+        if (a.topo) {  // children: j+1, then the sibling chain; cost = children - 1
+          int c = j + 1, k = 1;
+          float sub = nrel[c] * nD[c];
+          for (c = nsib[c]; c != 0; c = nsib[c], ++k) sub += nrel[c] * nD[c];
+          u = sens * (nrel[j] * nD[j] - sub) / (float)(k - 1);
+          cst = (uint8_t)(k - 1);
+        } else {
+          const int lc = j + 1, rc = j + 2 * ((nsz[j] + 1) >> 1);
+          u = sens * (nrel[j] * nD[j] - (nrel[lc] * nD[lc] + nrel[rc] * nD[rc]));
+          cst = 1;
+        }
       }
       a.op_util[obase + q] = u;
       a.op_cost[obase + q] = cst;
@@ -846,6 +906,122 @@ __global__ __launch_bounds__(1024) void tree_bucket_kernel(const int32_t* slot_s
     __syncthreads();
   }
   if (tid < 2) counts[tid * S + s] = base[tid];
+}
+
+// ------------------------------------------------------------------ explicit tree shapes
+// GraceKV page, 'Technical details and default settings': high-curvature
+// split candidates beside the midpoint, a salient token isolated in a
+// three-way child set. One thread builds one slot's tree depth-first (node j
+// numbered when popped, so in pre-order) with its stack in LDS, and writes
+// the node records; a record's next-sibling field is known once that sibling
+// is numbered, so a node with a later sibling hands its record to the
+// sibling's stack entry, which writes it. Children are at most n - ceil(n/4)
+// tokens (or n - 1 - max(floor(n/4), 1) for a three-way split's sides), so a
+// 128-token slot is at most 14 internal levels deep and at most 2 later
+// siblings wait per level: 32 stack entries suffice.
+constexpr int TOPO_THREADS = 64;
+constexpr int TOPO_STACK = 32;
+
+struct TopoArgs {
+  const float* rel;        // [Ly][H][T]
+  const int64_t* cut;      // [T] partition cut scores or NULL
+  const int32_t* slot_start;
+  const int32_t* n_slots;
+  const int64_t* cu;
+  uint32_t* topo;          // [Ly][H][2T]
+  int S, stride, mode;
+  int64_t T, items;        // items = Ly*H*S*stride
+};
+
+// children of the node [st, st+n) (sequence positions; n >= 2): returns 2 or 3
+__device__ int topo_children(const float* r, const int64_t* cut, int mode, int st, int n, int* ca, int* cn) {
+  int b = (n + 1) >> 1;
+  if (mode == 1) {
+    if (n >= 3) {
+      int i = 0;
+      float rmax = r[st];
+      double S = 0.0;
+      for (int k = 0; k < n; ++k) {   // left to right: the order the decision is defined in
+        const float v = r[st + k];
+        S += (double)v;
+        if (v > rmax) {
+          rmax = v;
+          i = k;
+        }
+      }
+      const int q = max(n >> 2, 1);
+      if (S > 0.0 && 2.0 * (double)rmax > S && i >= q && i <= n - 1 - q) {
+        ca[0] = st, cn[0] = i;
+        ca[1] = st + i, cn[1] = 1;
+        ca[2] = st + i + 1, cn[2] = n - i - 1;
+        return 3;
+      }
+    }
+    if (cut) {
+      const int m4 = (n + 3) >> 2;
+      const int lo = max(1, m4), hi = min(n - 1, n - m4);
+      int best = b;
+      int64_t bv = cut[st + b];
+      for (int c = lo; c <= hi; ++c) {
+        const int64_t v = cut[st + c];
+        const int dc = abs(c - b), db = abs(best - b);
+        if (v > bv || (v == bv && (dc < db || (dc == db && c < best)))) {
+          best = c;
+          bv = v;
+        }
+      }
+      b = best;
+    }
+  }
+  ca[0] = st, cn[0] = b;
+  ca[1] = st + b, cn[1] = n - b;
+  return 2;
+}
+
+__global__ __launch_bounds__(TOPO_THREADS) void tree_topo_kernel(TopoArgs a) {
+  __shared__ uint2 stk[TOPO_STACK][TOPO_THREADS];   // x: entry, y: the previous sibling's record + index
+  const int tid = threadIdx.x;
+  const int64_t i = (int64_t)blockIdx.x * TOPO_THREADS + tid;
+  if (i >= a.items) return;
+  const int k = (int)(i % a.stride);
+  const int64_t rest = i / a.stride;
+  const int s = (int)(rest % a.S);
+  const int64_t lh = rest / a.S;
+  if (k >= a.n_slots[s]) return;
+  const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
+  const int t0 = ss[k], n = ss[k + 1] - ss[k];
+  if (n <= 0) return;
+  const float* r = a.rel + lh * a.T + a.cu[s];               // sequence positions
+  const int64_t* cut = a.cut ? a.cut + a.cu[s] : nullptr;
+  uint32_t* rec = a.topo + lh * 2 * a.T + 2 * (a.cu[s] + t0);
+  // entry x: bits 0-7 start - t0, 8-15 length - 1, 16-23 parent + 1, 24 has a
+  // later sibling, 25 y holds the previous sibling's record
+  int top = 0, m = 0;
+  stk[top++][tid] = make_uint2((uint32_t)(n - 1) << 8, 0u);
+  while (top > 0) {
+    const uint2 e = stk[--top][tid];
+    const int j = m++;
+    if (e.x & (1u << 25)) rec[e.y >> 24] = (e.y & 0xFFFFFFu) | ((uint32_t)j << 24);
+    const uint32_t low = e.x & 0xFFFFFFu;
+    if (e.x & (1u << 24)) {
+      uint2 nx = stk[top - 1][tid];
+      nx.x |= 1u << 25;
+      nx.y = low | ((uint32_t)j << 24);
+      stk[top - 1][tid] = nx;
+    } else {
+      rec[j] = low;
+    }
+    const int st = (int)(e.x & 255), len = (int)((e.x >> 8) & 255) + 1;
+    if (len > 1) {
+      int ca[3], cn[3];
+      const int nc = topo_children(r, cut, a.mode, t0 + st, len, ca, cn);
+      for (int c = nc - 1; c >= 0 && top < TOPO_STACK; --c)
+        stk[top++][tid] = make_uint2((uint32_t)(ca[c] - t0) | ((uint32_t)(cn[c] - 1) << 8) |
+                                         ((uint32_t)(j + 1) << 16) | (c < nc - 1 ? 1u << 24 : 0u),
+                                     0u);
+    }
+  }
+  for (int j = m; j < 2 * n; ++j) rec[j] = 0xFFFFFFFFu;
 }
 
 int slot_nmax(const kvc_params* p) { return p->slot_len > 0 ? p->slot_len : p->slot_max; }
@@ -898,6 +1074,15 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
                                const float* rope_cos, const float* rope_sin, const int32_t* slot_start,
                                const int32_t* n_slots, kvc_trees* out, void* ws, size_t ws_bytes,
                                hipStream_t st) {
+  return kvc_build_trees_ex(sh, p, K, V, Qprobe, probe_lse, rel, head_sens, rope_cos, rope_sin, slot_start, n_slots,
+                            nullptr, out, ws, ws_bytes, st);
+}
+
+extern "C" int kvc_build_trees_ex(const kvc_shape* sh, const kvc_params* p, const void* K, const void* V,
+                                  const void* Qprobe, const float* probe_lse, const float* rel,
+                                  const float* head_sens, const float* rope_cos, const float* rope_sin,
+                                  const int32_t* slot_start, const int32_t* n_slots, const int64_t* dp_cut_q,
+                                  kvc_trees* out, void* ws, size_t ws_bytes, hipStream_t st) {
   int r = kvc::validate_shape(sh);
   if (r) return r;
   if ((r = kvc::validate_params(sh, p))) return r;
@@ -905,6 +1090,8 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   KVC_REQUIRE(K && V && Qprobe && probe_lse && rel && head_sens && rope_cos && rope_sin && slot_start && n_slots &&
                   out && out->node_rel && out->node_D && out->node_mu && out->op_util && out->op_cost,
               KVC_E_INVAL, "kvc_build_trees: NULL pointer");
+  KVC_REQUIRE(p->split_mode == 0 || out->node_topo, KVC_E_INVAL,
+              "kvc_build_trees: split_mode 1 needs out->node_topo");
   const int d = sh->head_dim;
   KVC_REQUIRE(d == 64 || d == 128, KVC_E_UNSUPPORTED, "kvc_build_trees: head_dim must be 64 or 128");
   const size_t need = kvc::ws_trees(sh, p);
@@ -940,8 +1127,26 @@ extern "C" int kvc_build_trees(const kvc_shape* sh, const kvc_params* p, const v
   a.node_mu = out->node_mu;
   a.op_util = out->op_util;
   a.op_cost = out->op_cost;
+  a.topo = p->split_mode == 1 ? out->node_topo : nullptr;
   const int64_t bound = (int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride;  // slot count bound
   if (bound == 0) return KVC_OK;
+  if (out->node_topo) {
+    TopoArgs ta{};
+    ta.rel = rel;
+    ta.cut = p->split_mode == 1 ? dp_cut_q : nullptr;
+    ta.slot_start = slot_start;
+    ta.n_slots = n_slots;
+    ta.cu = sh->cu_seqlens_d;
+    ta.topo = out->node_topo;
+    ta.S = sh->n_seq;
+    ta.stride = a.stride;
+    ta.mode = p->split_mode;
+    ta.T = sh->total_tokens;
+    ta.items = bound;
+    hipLaunchKernelGGL(tree_topo_kernel, dim3((unsigned)((bound + TOPO_THREADS - 1) / TOPO_THREADS)),
+                       dim3(TOPO_THREADS), 0, st, ta);
+    KVC_LAUNCH_CHECK("tree_topo");
+  }
   kvc::Carver cv(ws, ws_bytes);
   int2* lists = cv.take<int2>((size_t)2 * a.S * a.stride);
   int32_t* counts = cv.take<int32_t>((size_t)2 * a.S);

@@ -31,7 +31,7 @@ STAGE_SCORE, STAGE_PROPAGATE, STAGE_PARTITION, STAGE_TREES, STAGE_AUCTION, STAGE
 
 EXPORTS = ["kvc_strerror", "kvc_last_error", "kvc_params_default", "kvc_budgets", "kvc_pack_capacity",
            "kvc_slot_stride", "kvc_workspace_size", "kvc_rope_table", "kvc_score", "kvc_propagate",
-           "kvc_partition", "kvc_partition_ex", "kvc_build_trees", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
+           "kvc_partition", "kvc_partition_ex", "kvc_build_trees", "kvc_build_trees_ex", "kvc_auction", "kvc_hybrid_units", "kvc_pack", "kvc_full_view",
            "kvc_decode_workspace", "kvc_decode_plan", "kvc_decode_attn", "kvc_decode_attn_planned",
            "kvc_decode_static_limit", "kvc_decode_attn_static",
            "kvc_kl_workspace", "kvc_kl", "kvc_step_capacity",
@@ -56,12 +56,12 @@ class Params(C.Structure):
                 ("slot_len", C.c_int32), ("slot_min", C.c_int32), ("slot_max", C.c_int32),
                 ("slot_target", C.c_int32), ("lambda_len", C.c_float), ("lambda_curv", C.c_float),
                 ("rope_base", C.c_float), ("hybrid_frac", C.c_float), ("window", C.c_int32),
-                ("n_depth", C.c_int32), ("lambda_surp", C.c_float)]
+                ("n_depth", C.c_int32), ("lambda_surp", C.c_float), ("split_mode", C.c_int32)]
 
 
 class Trees(C.Structure):
     _fields_ = [("node_rel", C.c_void_p), ("node_D", C.c_void_p), ("node_mu", C.c_void_p),
-                ("op_util", C.c_void_p), ("op_cost", C.c_void_p)]
+                ("op_util", C.c_void_p), ("op_cost", C.c_void_p), ("node_topo", C.c_void_p)]
 
 
 class Policy(C.Structure):
@@ -100,6 +100,8 @@ _sig = {
                                    _P, _P, C.c_size_t, _P]),
     "kvc_build_trees": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, C.POINTER(Trees), _P, C.c_size_t, _P]),
+    "kvc_build_trees_ex": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, C.POINTER(Trees), _P, C.c_size_t, _P]),
     "kvc_auction": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), C.POINTER(Trees), _P, _P, _P, _P, _P,
                               _P, _P, _P, C.c_size_t, _P]),
     "kvc_pack": (C.c_int, [C.POINTER(Shape), C.POINTER(Params), _P, _P, _P, C.POINTER(Trees), _P, _P, _P,
@@ -238,6 +240,7 @@ def make_problem(cfg, cu_seqlens: torch.Tensor, dtype: torch.dtype, device="cuda
     p.window = getattr(cfg, "window", 64)
     p.n_depth = getattr(cfg, "n_depth", 1)
     p.lambda_surp = getattr(cfg, "lambda_surp", 1.0)
+    p.split_mode = getattr(cfg, "split_mode", 0)
     return Problem(sh, p, cu_host, cu_dev, dev)
 
 
@@ -305,24 +308,29 @@ def empty_trees(pb: Problem):
             "node_D": torch.zeros(n, dtype=torch.float32, device=dev),
             "node_mu": torch.zeros(n, dtype=torch.float32, device=dev),
             "op_util": torch.zeros(n, dtype=torch.float32, device=dev),
-            "op_cost": torch.zeros(n, dtype=torch.uint8, device=dev)}
+            "op_cost": torch.zeros(n, dtype=torch.uint8, device=dev),
+            "node_topo": (torch.full(n, -1, dtype=torch.int32, device=dev) if pb.params.split_mode else None)}
 
 
 def _trees_struct(tr):
     if tr is None:
         return None
     return Trees(node_rel=_ptr(tr["node_rel"]), node_D=_ptr(tr["node_D"]), node_mu=_ptr(tr["node_mu"]),
-                 op_util=_ptr(tr["op_util"]), op_cost=_ptr(tr["op_cost"]))
+                 op_util=_ptr(tr["op_util"]), op_cost=_ptr(tr["op_cost"]), node_topo=_ptr(tr.get("node_topo")))
 
 
-def build_trees(pb: Problem, K, V, Qp, lse, rel, head_sens, rope_cos, rope_sin, slot_start, n_slots, out=None):
+def build_trees(pb: Problem, K, V, Qp, lse, rel, head_sens, rope_cos, rope_sin, slot_start, n_slots, out=None,
+                cut_q=None):
+    """kvc_build_trees_ex. cut_q: the partition's int64 [T] cut scores (DP
+    slots) or None; node_topo (int32 view of the uint32 records) is allocated
+    when split_mode is 1."""
     tr = out if out is not None else empty_trees(pb)
     ts = _trees_struct(tr)
     ws = pb.ws(STAGE_TREES)
-    st = _lib.kvc_build_trees(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(V), _ptr(Qp), _ptr(lse),
-                              _ptr(rel), _ptr(head_sens), _ptr(rope_cos), _ptr(rope_sin), _ptr(slot_start),
-                              _ptr(n_slots), C.byref(ts), _ptr(ws), ws.numel(), _stream())
-    _check("kvc_build_trees", st)
+    st = _lib.kvc_build_trees_ex(C.byref(pb.shape), C.byref(pb.params), _ptr(K), _ptr(V), _ptr(Qp), _ptr(lse),
+                                 _ptr(rel), _ptr(head_sens), _ptr(rope_cos), _ptr(rope_sin), _ptr(slot_start),
+                                 _ptr(n_slots), _ptr(cut_q), C.byref(ts), _ptr(ws), ws.numel(), _stream())
+    _check("kvc_build_trees_ex", st)
     return tr
 
 

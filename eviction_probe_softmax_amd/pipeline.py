@@ -44,13 +44,15 @@ class Compressor:
             out.update(au)
             out["cache"] = kvc.pack(pb, inp["K"], inp["V"], rel, None, au["taken"], None, None, None, None)
             return out
+        split = getattr(cfg, "split_mode", 0) == 1
         if cfg.slot_len > 0:
             part = kvc.partition(pb)
-        else:
-            part = kvc.partition(pb, inp["hidden"], cfg.hidden_dim, surprisal=inp.get("surprisal"))
+        else:   # curvature-candidate splits read the partition's cut scores
+            part = kvc.partition(pb, inp["hidden"], cfg.hidden_dim, surprisal=inp.get("surprisal"), export=split)
         out.update(part)
         tr = kvc.build_trees(pb, inp["K"], inp["V"], inp["Qp"], sc["lse"], rel, sc["head_sens"], self.rope_cos,
-                             self.rope_sin, part["slot_start"], part["n_slots"])
+                             self.rope_sin, part["slot_start"], part["n_slots"],
+                             cut_q=part["dp_cut_q"] if split else None)
         out["trees"] = tr
         au = kvc.auction(pb, tr, rel, sc["head_sens"], part["slot_start"], part["n_slots"])
         out.update(au)

@@ -92,6 +92,8 @@ typedef struct kvc_params {
   int32_t window;          /* step-wise eviction: recent queries behind the features (w = 64) */
   int32_t n_depth;         /* sampled depths of the hidden-state trajectory (1..4) */
   float lambda_surp;       /* DP weight of surprisal / its sequence maximum at a cut */
+  int32_t split_mode;      /* trees: 0 midpoint binary splits; 1 curvature-candidate cuts and
+                              salient three-way splits (see kvc_build_trees_ex) */
 } kvc_params;
 
 typedef struct kvc_trees {
@@ -100,6 +102,13 @@ typedef struct kvc_trees {
   float* node_mu;          /* [Ly][H][2T] node multiplicity >= 1 */
   float* op_util;          /* [Ly][H][2T] utility per new entry of each op */
   uint8_t* op_cost;        /* [Ly][H][2T] entries an op adds (0 = no such op) */
+  uint32_t* node_topo;     /* [Ly][H][2T] node records (nullable when split_mode = 0, where the
+                              trees are the implicit midpoint trees; required when split_mode = 1):
+                              node j of the slot at global token t0 of unit (l,h) at
+                              (l*H+h)*2T + 2*t0 + j holds bits 0-7 its first token - t0, 8-15 its
+                              length - 1, 16-23 its parent's index + 1 (0: the root), 24-31 its
+                              next sibling's index (0: none); 0xFFFFFFFF past the slot's last node.
+                              Nodes are in pre-order, children in position order. */
 } kvc_trees;
 
 typedef struct kvc_ragged {
@@ -251,6 +260,29 @@ int kvc_build_trees(const kvc_shape* shape, const kvc_params* prm, const void* K
                     const float* head_sens, const float* rope_cos, const float* rope_sin,
                     const int32_t* slot_start, const int32_t* n_slots, kvc_trees* out,
                     void* ws, size_t ws_bytes, hipStream_t stream);
+/* kvc_build_trees_ex: the same with the tree shapes of prm->split_mode.
+ * GraceKV page, 'Technical details and default settings' (tree construction
+ * weighs high-curvature split candidates beside the midpoint and may isolate
+ * a salient token in a three-way child set). split_mode 1 decides each node
+ * [a, a+n), n >= 2, top-down, before any distortion: with i the first
+ * position of the node's largest relevance (fp32), the node splits three ways
+ * [a, i), {i}, [i+1, a+n) when n >= 3, its relevance S (a left-to-right
+ * float64 sum of the fp32 values) is positive, 2 r_i > S and i lies at least
+ * max(floor(n/4), 1) tokens from either end; otherwise at one cut among those
+ * leaving both children at least ceil(n/4) tokens: the largest dp_cut_q score
+ * (ties: the midpoint, then the nearest cut, then the lower one), or the
+ * midpoint when dp_cut_q is NULL. A three-way split costs 2 entries and its
+ * utility is s_lh * gain / 2. dp_cut_q: [T] int64 device, the partition's
+ * quantized cut scores (cut before that token; kvc_partition exports them),
+ * nullable; ignored when split_mode = 0. out->node_topo receives the node
+ * records (required when split_mode = 1; when non-NULL with split_mode 0 the
+ * midpoint trees' records are written). kvc_build_trees is this call with
+ * dp_cut_q NULL. */
+int kvc_build_trees_ex(const kvc_shape* shape, const kvc_params* prm, const void* K, const void* V,
+                       const void* Qprobe, const float* probe_lse, const float* rel,
+                       const float* head_sens, const float* rope_cos, const float* rope_sin,
+                       const int32_t* slot_start, const int32_t* n_slots, const int64_t* dp_cut_q,
+                       kvc_trees* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------ A5/A6
  * kvc_auction: spend each sequence's budget.
@@ -258,7 +290,9 @@ int kvc_build_trees(const kvc_shape* shape, const kvc_params* prm, const void* K
  * the top leaves by s_lh*r_i, scanned in order, each paying its untaken path,
  * while the floor spend stays <= floor_frac * allocatable budget) and '04
  * Top-down budget flow' (best-first greedy: the exposed op with the highest
- * utility, lower op id on ties, is taken next until the budget is spent).
+ * utility, lower op id on ties, is taken next until the budget is spent; an op
+ * that costs more than what is left is discarded with its subtree). With
+ * prm->split_mode 1 the trees' node_topo records give the tree shapes.
  * Writes op_taken [Ly][H][2T] uint8 (1 = taken; every other byte of the
  * layout is cleared) and spent [S] int64 (entries bought, floor included);
  * spent_floor [S] (nullable) = floor part.
@@ -297,7 +331,9 @@ int kvc_hybrid_units(const kvc_shape* shape, const kvc_params* prm, const float*
  * leaf the original K/V bits (ln mu 0, its position). Segments are stored in
  * (l, h, s) order; entries in position order: prompt, slot frontiers (kept
  * tokens in token mode), recent window, suffix. out->capacity must be at
- * least kvc_pack_capacity(); seg_off/seg_len/K/V/lnmu/pos are written. */
+ * least kvc_pack_capacity(); seg_off/seg_len/K/V/lnmu/pos are written. With
+ * prm->split_mode 1 the trees' node_topo records give the tree shapes and a
+ * taken op adds op_cost entries. */
 int kvc_pack(const kvc_shape* shape, const kvc_params* prm, const void* K, const void* V,
              const float* rel, const kvc_trees* trees, const uint8_t* op_taken,
              const int32_t* slot_start, const int32_t* n_slots, const float* rope_cos,

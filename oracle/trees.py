@@ -266,11 +266,12 @@ def op_utilities(nodes, rel, D, sens):
     return util, cost
 
 
-def build_trees(K, V, Qp, lse, rel_tok, head_sens, cu, slots, cfg, keep_protos=False, cut_q=None):
+def build_trees(K, V, Qp, lse, rel_tok, head_sens, cu, slots, cfg, keep_protos=False, cut_q=None, topo=None):
     """Build every tree. K, V: [Ly][H][T][d]; Qp: [S][Ly][H*G][P][d];
     lse: float32 [S][Ly][H*G][P]; rel_tok, head_sens: float32; slots: per
     sequence [(start, n)]; cut_q: the partition's int64 [T] cut scores (DP
-    slots, split_mode 1) or None.
+    slots, split_mode 1) or None; topo: node_topo records [Ly][H][2T] whose
+    shapes are used instead of deciding them (None: decide them).
 
     Returns float32 node_rel/node_D/node_mu and op_util [Ly][H][2T], uint8
     op_cost [Ly][H][2T], uint32 node_topo [Ly][H][2T]; with keep_protos, also
@@ -308,7 +309,8 @@ def build_trees(K, V, Qp, lse, rel_tok, head_sens, cu, slots, cfg, keep_protos=F
                 cq = None if cut_q is None else np.asarray(cut_q[a0:b0])
                 sens = float(head_sens[s, l, h])
                 for (st, n) in slots[s]:
-                    nodes = slot_tree(st, n, r32, cq, mode)
+                    nodes = (slot_tree(st, n, r32, cq, mode) if topo is None
+                             else decode_topo(topo[l, h, 2 * (a0 + st):2 * (a0 + st) + 2 * n], st))
                     rel, D, mu, kh, vh = _slot_nodes(nodes, ktil, knorm, Vu, r, Ad, Q, ls, 0, cfg, cfg.rope_base)
                     base = 2 * (a0 + st)
                     m = len(nodes)

@@ -64,8 +64,16 @@ def slots_from_dev(slot_start, n_slots):
 
 
 def trees_to_dev(tr, dev="cuda"):
-    return {k: torch.from_numpy(np.ascontiguousarray(tr[k])).to(dev)
-            for k in ("node_rel", "node_D", "node_mu", "op_util", "op_cost")}
+    out = {k: torch.from_numpy(np.ascontiguousarray(tr[k])).to(dev)
+           for k in ("node_rel", "node_D", "node_mu", "op_util", "op_cost")}
+    if tr.get("node_topo") is not None:   # uint32 records as int32 bits
+        out["node_topo"] = torch.from_numpy(np.ascontiguousarray(tr["node_topo"]).view(np.int32)).to(dev)
+    return out
+
+
+def topo_np(t):
+    """A device node_topo (int32 bits) as uint32 numpy."""
+    return as_np(t).view(np.uint32)
 
 
 def jaccard(a, b):
@@ -146,13 +154,19 @@ def check_kl(klv, xf, xc, W, kl_oracle, name="", xf_oracle=None, xc_oracle=None,
     assert not bad.any(), (name, int(np.argmax(err - lim)), float(err.max()), float(lim[np.argmax(err - lim)]))
 
 
-def oracle_on_taken(inp, cfg, o, taken):
+def oracle_on_taken(inp, cfg, o, taken, topo=None):
     """The oracle's pack, decode and KL of a given taken set (the GPU's), with
     the oracle's own relevance, trees and slots: x_comp [S][T_dec][d_model]
-    and kl [S][T_dec]."""
+    and kl [S][T_dec]. topo (uint32 node records, the GPU's): tree shapes the
+    taken set refers to; where they differ from the oracle's, the oracle's
+    trees are rebuilt on them."""
     import oracle
     cu = inp["cu_seqlens"].numpy()
-    cache = oracle.pack(inp["K"], inp["V"], o["rel"], o.get("trees"), as_np(taken), cu, o["slots"], cfg)
+    trees = o.get("trees")
+    if topo is not None and trees is not None and not np.array_equal(topo, trees["node_topo"]):
+        trees = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], o["lse"], o["rel"], o["head_sens"], cu,
+                                   o["slots"], cfg, topo=topo)
+    cache = oracle.pack(inp["K"], inp["V"], o["rel"], trees, as_np(taken), cu, o["slots"], cfg)
     xc = oracle.decode_all(cache, inp["Kd"], inp["Vd"], inp["Qd"], cfg.G)
     n = xc.shape[0] * xc.shape[1]
     kl = oracle.kl_rows(o["x_full"].reshape(n, -1), xc.reshape(n, -1), inp["W"], cfg.w_dtype)

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 from workload import small_config, make_inputs
-from parity import as_np, inputs_to, jaccard, close, check_kl, oracle_on_taken, slots_from_dev
+from parity import as_np, inputs_to, jaccard, close, check_kl, oracle_on_taken, slots_from_dev, topo_np
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,10 @@ def _run_gpu(cfg, inp):
                                      ("fulldepth", {}), ("ragged", {"hybrid_frac": 0.5}),
                                      ("fulldepth", {"hybrid_frac": 0.25, "budget_ratio": 0.4}),
                                      ("mistral1", {"hybrid_frac": 0.5, "budget_ratio": 0.6}),
-                                     ("fulldepth", {"n_depth": 3, "surprisal": True})])
+                                     ("fulldepth", {"n_depth": 3, "surprisal": True}),
+                                     ("tiny", {"split_mode": 1}), ("fulldepth", {"split_mode": 1}),
+                                     ("ragged", {"split_mode": 1}),
+                                     ("fulldepth", {"split_mode": 1, "n_depth": 3, "surprisal": True})])
 def test_end_to_end_matches_oracle(name, kw):
     cfg = small_config(name, **kw)
     inp = make_inputs(cfg)
@@ -51,7 +54,14 @@ def _compare(cfg, inp, out, xf, xc, klv, o, name):
         assert slots_from_dev(out["slot_start"], out["n_slots"]) == o["slots"]
     close(xf, o["x_full"], 2e-2, "x_full", floor=1e-3)
     print(f"  jaccard={j:.4f} kl_oracle_mean={o['kl'].mean():.4f}", flush=True)
-    xc_o, kl_o = oracle_on_taken(inp, cfg, o, out["taken"])
+    topo = None
+    if getattr(cfg, "split_mode", 0):
+        topo = topo_np(out["trees"]["node_topo"])
+        same = float((topo == o["trees"]["node_topo"]).mean())
+        print(f"  tree shapes equal to the oracle's at {same:.5f} of the records; three-way splits taken "
+              f"{int(((o['trees']['op_cost'] == 2) & (o['taken'] > 0)).sum())}", flush=True)
+        assert same >= 0.99, same
+    xc_o, kl_o = oracle_on_taken(inp, cfg, o, out["taken"], topo)
     if j == 1.0:
         assert np.array_equal(xc_o, o["x_comp"]) and np.array_equal(kl_o, o["kl"])
     # the packed prototypes are bf16 on the GPU and fp64 in the oracle, so
@@ -72,9 +82,10 @@ def test_end_to_end_other_seeds(name, seed):
     _compare(cfg, inp, out, xf, xc, klv, o, name)
 
 
-@pytest.mark.parametrize("name", ["tiny", "stress", "ragged", "mistral1"])
-def test_full_budget_is_the_identity_on_gpu(name):
-    cfg = small_config(name).replace(budget_ratio=1.0)
+@pytest.mark.parametrize("name,mode", [("tiny", 0), ("stress", 0), ("ragged", 0), ("mistral1", 0), ("tiny", 1),
+                                       ("fulldepth", 1)])
+def test_full_budget_is_the_identity_on_gpu(name, mode):
+    cfg = small_config(name).replace(budget_ratio=1.0, split_mode=mode)
     inp = make_inputs(cfg)
     print(f"[identity] {name}", flush=True)
     out, xf, xc, klv = _run_gpu(cfg, inp)

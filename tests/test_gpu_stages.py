@@ -9,7 +9,7 @@ import torch
 import oracle
 from oracle import partition as opart
 from workload import small_config, make_inputs
-from parity import (close, as_np, to_dev, inputs_to, slots_to_dev, slots_from_dev, trees_to_dev)
+from parity import (close, as_np, to_dev, inputs_to, slots_to_dev, slots_from_dev, trees_to_dev, topo_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,12 @@ def _compare_cache(c, oc, exact):
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("fulldepth", {}),
                                      ("stress", {"slot_len": 128}),
                                      ("fulldepth", {"slot_min": 64, "slot_max": 128, "slot_target": 120}),
-                                     ("tiny", {"slot_len": 128})])
+                                     ("tiny", {"slot_len": 128}),
+                                     ("tiny", {"split_mode": 1}), ("fulldepth", {"split_mode": 1}),
+                                     ("ragged", {"split_mode": 1}),
+                                     ("fulldepth", {"split_mode": 1, "slot_min": 64, "slot_max": 128,
+                                                    "slot_target": 120}),
+                                     ("tiny", {"split_mode": 1, "slot_len": 128})])
 def test_trees_match_oracle(name, kw):
     kvc = _kvc()
     cfg = small_config(name, **kw)
@@ -93,23 +98,33 @@ def test_trees_match_oracle(name, kw):
     ss, ns = slots_to_dev(slots, pb.slot_stride())
     rc, rs = kvc.rope_table(cfg.rope_base, cfg.d, max(cfg.lens))
     g = kvc.build_trees(pb, dinp["K"], dinp["V"], dinp["Qp"], to_dev(sc["lse"]), to_dev(pr["rel"]),
-                        to_dev(sc["head_sens"]), rc, rs, ss, ns)
+                        to_dev(sc["head_sens"]), rc, rs, ss, ns, cut_q=to_dev(kq) if cfg.split_mode else None)
     torch.cuda.synchronize()
-    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
+    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg,
+                           cut_q=kq)
+    if cfg.split_mode:   # the shapes: integer and fixed-order decisions on the same inputs, bit-exact
+        gt = topo_np(g["node_topo"])
+        print(f"  three-way splits {int((o['op_cost'] == 2).sum())}, nodes {int((o['node_topo'] != 0xFFFFFFFF).sum())}",
+              flush=True)
+        assert np.array_equal(gt, o["node_topo"])
     assert np.array_equal(as_np(g["op_cost"]), o["op_cost"])
     close(g["node_rel"], o["node_rel"], 1e-5, "node_rel")
     close(g["node_mu"], o["node_mu"], 1e-4, "node_mu")
     close(g["node_D"], o["node_D"], 1e-3, "node_D", floor=1e-3)
     close(g["op_util"], o["op_util"], 1e-3, "op_util", floor=1e-3)
-    # P4 on the GPU output: parents are the exact fp32 sums of their children
+    # P4 on the GPU output: parents are the exact fp32 sums of their children (left to right)
     nr = as_np(g["node_rel"])
     for s, lst in enumerate(slots):
         for (a, n) in lst[:3]:
-            nodes = oracle.tree_nodes(0, n)
             base = 2 * (int(cu[s]) + a)
-            for j, (_, _, lc, rc_) in enumerate(nodes):
-                if lc >= 0:
-                    assert nr[0, 0, base + j] == np.float32(nr[0, 0, base + lc] + nr[0, 0, base + rc_])
+            nodes = (oracle.trees.decode_topo(o["node_topo"][0, 0, base:base + 2 * n], a) if cfg.split_mode
+                     else oracle.trees.slot_tree(a, n))
+            for j, (_, _, ch, _) in enumerate(nodes):
+                if ch:
+                    acc = np.float32(nr[0, 0, base + ch[0]])
+                    for c in ch[1:]:
+                        acc = np.float32(acc + nr[0, 0, base + c])
+                    assert nr[0, 0, base + j] == acc
 
 
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("fulldepth", {}),
@@ -118,7 +133,10 @@ def test_trees_match_oracle(name, kw):
                                      ("fulldepth", {"hybrid_frac": 0.25, "budget_ratio": 0.4}),
                                      ("ragged", {"hybrid_frac": 0.5, "floor_frac": 0.3}),
                                      ("stress", {"hybrid_frac": 0.5}),
-                                     ("tiny", {"hybrid_frac": 1.0, "budget_ratio": 1.0})])
+                                     ("tiny", {"hybrid_frac": 1.0, "budget_ratio": 1.0}),
+                                     ("tiny", {"split_mode": 1}), ("tiny", {"split_mode": 1, "floor_frac": 0.3}),
+                                     ("fulldepth", {"split_mode": 1}), ("ragged", {"split_mode": 1}),
+                                     ("fulldepth", {"split_mode": 1, "hybrid_frac": 0.25, "budget_ratio": 0.4})])
 def test_floor_and_auction_bit_exact(name, kw):
     kvc = _kvc()
     cfg = small_config(name, **kw)
@@ -129,10 +147,16 @@ def test_floor_and_auction_bit_exact(name, kw):
     if cfg.slot_len == 0:
         cq, kq = opart.slot_costs(inp["hidden"], cu, cfg)
     slots = oracle.slots_for(cu, cfg, cq, kq)
-    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
+    o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg,
+                           cut_q=kq)
     full = _full(cfg, cu, sc)
-    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg, full=full)
-    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg, full=full)
+    topo = o["node_topo"] if cfg.split_mode else None
+    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg, full=full,
+                                        topo=topo)
+    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg, full=full, topo=topo)
+    if cfg.split_mode:
+        print(f"  three-way splits {int((o['op_cost'] == 2).sum())}, taken {int(((o['op_cost'] == 2) & (taken > 0)).sum())}",
+              flush=True)
     pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
     ss, ns = slots_to_dev(slots, pb.slot_stride())
     g = kvc.auction(pb, trees_to_dev(o), to_dev(pr["rel"]), to_dev(sc["head_sens"]), ss, ns)
@@ -145,7 +169,9 @@ def test_floor_and_auction_bit_exact(name, kw):
     assert np.array_equal(gt, taken), f"{int((gt != taken).sum())} ops differ"
 
 
-@pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("stress", {"slot_len": 128})])
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("stress", {"slot_len": 128}),
+                                     ("tiny", {"split_mode": 1}), ("tiny", {"split_mode": 1, "budget_ratio": 0.6}),
+                                     ("ragged", {"split_mode": 1})])
 def test_pack_tree_mode(name, kw):
     kvc = _kvc()
     cfg = small_config(name, **kw)
@@ -155,8 +181,9 @@ def test_pack_tree_mode(name, kw):
     cu, sc, pr = _oracle_front(cfg, inp)
     slots = oracle.slots_for(cu, cfg)
     o = oracle.build_trees(inp["K"], inp["V"], inp["Qp"], sc["lse"], pr["rel"], sc["head_sens"], cu, slots, cfg)
-    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg)
-    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg)
+    topo = o["node_topo"] if cfg.split_mode else None
+    ft, fs = oracle.select.floor_select(pr["rel"], sc["head_sens"], o["op_cost"], cu, slots, cfg, topo=topo)
+    taken, spent = oracle.select.auction(o["op_util"], o["op_cost"], ft, fs, cu, slots, cfg, topo=topo)
     pb = kvc.make_problem(cfg, inp["cu_seqlens"], inp["K"].dtype)
     ss, ns = slots_to_dev(slots, pb.slot_stride())
     rc, rs = kvc.rope_table(cfg.rope_base, cfg.d, max(cfg.lens))
@@ -201,3 +228,45 @@ def test_partition_dp(name, kw):
             assert lst[0][0] == c0 and lst[-1][0] + lst[-1][1] == c1
             if c1 - c0 >= cfg.slot_min:
                 assert all(cfg.slot_min <= n <= cfg.slot_max for _, n in lst)
+
+
+def test_auction_with_three_way_splits_on_random_forests():
+    """Cost-2 operations where the budget runs out on them: random tree
+    shapes (binary and three-way splits) and utilities, every budget from a
+    single entry to past the total, with and without a floor path taken up
+    front; the GPU's threshold form, tie walk and extension against the
+    oracle's best-first queue, bit-exact."""
+    import test_oracle_pins_splits as sp
+    from oracle import trees as otrees
+    kvc = _kvc()
+    rng = np.random.default_rng(31)
+    n_short = 0
+    for trial in range(24):
+        lens, starts, T, util, cost, topo, slots_ops = sp._forest(rng, int(rng.integers(2, 6)), trial % 2 == 1)
+        total = int(cost.sum())
+        slots = [[(st, n) for st, n in zip(starts, lens)]]
+        trees = {"node_rel": np.zeros((1, 1, 2 * T), np.float32), "node_D": np.zeros((1, 1, 2 * T), np.float32),
+                 "node_mu": np.ones((1, 1, 2 * T), np.float32), "op_util": util.reshape(1, 1, -1),
+                 "op_cost": cost.reshape(1, 1, -1), "node_topo": topo}
+        rel = rng.random((1, 1, T)).astype(np.float32)
+        sens = np.ones((1, 1, 1), np.float32)
+        for B in sorted({1, 2, 3, total // 2, total - 1, total, total + 2}):
+            if B < 1:
+                continue
+            for ff in (0.0, 0.5):
+                cfg = sp._cfg(lens=[T], slot_len=0, slot_min=1, slot_max=128, budget_ratio=0.0, budget_min=B,
+                              floor_frac=ff, G=4, P=16, d=64)
+                cu = np.array([0, T])
+                ft, fs = oracle.select.floor_select(rel, sens, trees["op_cost"], cu, slots, cfg, topo=topo)
+                want, spent = oracle.select.auction(trees["op_util"], trees["op_cost"], ft, fs, cu, slots, cfg,
+                                                    topo=topo)
+                pb = kvc.make_problem(cfg, torch.tensor([0, T]), torch.float32)
+                ss, ns = slots_to_dev(slots, pb.slot_stride())
+                g = kvc.auction(pb, trees_to_dev(trees), to_dev(rel), to_dev(sens), ss, ns)
+                torch.cuda.synchronize()
+                assert np.array_equal(as_np(g["spent_floor"]), fs), (trial, B, ff)
+                assert np.array_equal(as_np(g["spent"]), spent), (trial, B, ff, as_np(g["spent"]), spent)
+                assert np.array_equal(as_np(g["taken"]), want), (trial, B, ff)
+                n_short += int(spent[0]) < min(B, total)
+    print(f"  budgets left partly unspent by a three-way split: {n_short}", flush=True)
+    assert n_short > 0
