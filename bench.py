@@ -41,7 +41,10 @@ def parse():
                     help="measure only the variants (one JSON object with a 'variants' key); for profiling")
     ap.add_argument("--variants", action="store_true",
                     help="also measure the selection variants beside the headline line (head-level hybrid, "
-                         "slots from three depths, step-wise eviction, dense and A r propagation)")
+                         "tree splits, slots from three depths, step-wise eviction, dense and A r propagation)")
+    ap.add_argument("--variant", action="append", default=None, metavar="NAME",
+                    help="with --variants/--only-variants: measure only these (head_hybrid_0.2, tree_splits, "
+                         "dp_3depths_surprisal, stepwise, dense_rollout, ar_direction); repeatable")
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarize a rocprofv3 kernel_trace.csv of a bench run (per kernel, the decode "
                          "kernels split by cache: the compressed cache's calls launch fewer workgroups), then exit")
@@ -137,12 +140,14 @@ def cpu_baseline(cfg, inp):
             "decode_gbps_25pct": round(dec_bytes / t_dec / 1e9, 2)}
 
 
-def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
+def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2, names=None):
     """Selection variants on the same inputs, outside the headline value:
     compression time, packed entries, decode time per call over the packed
     cache and the per-step KL against the full cache (x_full of the timed
     steps). Head-level hybrid: 20% of the (layer, KV head) units kept whole
-    (DistillCache paper, Appendix E.3). Step-wise eviction: the scoring-MLP
+    (DistillCache paper, Appendix E.3). Tree splits: curvature-candidate cuts
+    (DP slots only) and salient three-way splits (GraceKV page, technical
+    details). Step-wise eviction: the scoring-MLP
     loop of DistillCache's Algorithm 1 at the same budget ratio. Dense
     rollout: both propagation hops with every token a seed; the "A r"
     direction: both hops with every token a receiver. Slots cut from three
@@ -153,7 +158,10 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
     from eviction_probe_softmax_amd.pipeline import Compressor, _row_view
     out = {}
     S, Td, Dm = cfg.S, cfg.T_dec, cfg.d_model
-    for name, kw in (("head_hybrid_0.2", {"hybrid_frac": 0.2}),):
+    want = (lambda n: True) if not names else (lambda n: n in names)  # noqa: E731
+    for name, kw in (("head_hybrid_0.2", {"hybrid_frac": 0.2}), ("tree_splits", {"split_mode": 1})):
+        if not want(name):
+            continue
         vcfg = cfg.replace(**kw)
         comp = Compressor(vcfg, inp["cu_seqlens"], inp["K"].dtype)
         x_comp = torch.empty((S, Td, Dm), dtype=torch.float32, device="cuda")
@@ -172,70 +180,84 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2):
             cms.append(e[0].elapsed_time(e[1]))
             dms.append(e[1].elapsed_time(e[2]) / Td)
         klv = kl_op(x_full.reshape(S * Td, Dm), x_comp.reshape(S * Td, Dm), inp["W"]).float().cpu().numpy()
-        full_units = kvc.hybrid_units(comp.pb, res["head_sens"])
         out[name] = {"compress_ms": round(float(np.mean(cms)), 3),
                      "decode_ms_per_call": round(float(np.mean(dms)), 4),
                      "packed_entries": int(res["cache"]["seg_len"].to(torch.int64).sum()),
-                     "units_kept_whole": int(full_units.sum()),
                      "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
-    # Slots cut from three sampled depths with the surprisal bonus
-    from workload import make_inputs
-    vcfg = cfg.replace(n_depth=3, surprisal=True)
-    vin = make_inputs(vcfg, device="cuda")
-    comp = Compressor(vcfg, vin["cu_seqlens"], vin["K"].dtype)
-    comp.compress(vin)  # warm-up
-    e3 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    e3[0].record(stream)
-    res3 = comp.compress(vin)
-    e3[1].record(stream)
-    torch.cuda.synchronize()
-    out["dp_3depths_surprisal"] = {"compress_ms": round(e3[0].elapsed_time(e3[1]), 3),
-                                   "slots": int(res3["n_slots"].sum())}
-    del vin, comp, res3
+        if vcfg.hybrid_frac > 0:
+            out[name]["units_kept_whole"] = int(kvc.hybrid_units(comp.pb, res["head_sens"]).sum())
+        if vcfg.split_mode:
+            cost = res["trees"]["op_cost"]
+            three = cost == 2
+            out[name]["three_way_splits"] = int(three.sum())
+            out[name]["three_way_taken"] = int((three & (res["taken"] > 0)).sum())
+            out[name]["curvature_cuts"] = vcfg.slot_len == 0
+    # Slots cut from three sampled depths with the surprisal bonus (DP slots)
+    if want("dp_3depths_surprisal") and cfg.slot_len == 0:
+        from workload import make_inputs
+        vcfg = cfg.replace(n_depth=3, surprisal=True)
+        vin = make_inputs(vcfg, device="cuda")
+        comp = Compressor(vcfg, vin["cu_seqlens"], vin["K"].dtype)
+        comp.compress(vin)  # warm-up
+        e3 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e3[0].record(stream)
+        res3 = comp.compress(vin)
+        e3[1].record(stream)
+        torch.cuda.synchronize()
+        out["dp_3depths_surprisal"] = {"compress_ms": round(e3[0].elapsed_time(e3[1]), 3),
+                                       "slots": int(res3["n_slots"].sum())}
+        del vin, comp, res3
+    if not (want("stepwise") or want("dense_rollout") or want("ar_direction")):
+        return out
     # Step-wise eviction (DistillCache Algorithm 1) with a seeded scoring MLP:
     # one prefill prune, then per decode step append + decode + score + prune
-    from workload import make_policy
-    from eviction_probe_softmax_amd.pipeline import run_stepwise
-    pol = make_policy(device="cuda")
-    run_stepwise(cfg, inp, pol)  # warm-up
-    rec = []
-    torch.cuda.synchronize()
-    res = run_stepwise(cfg, inp, pol, record=rec)
-    torch.cuda.synchronize()
-    init_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "init"]
-    dec_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "step"]
-    prune_ms = [r[2].elapsed_time(r[3]) for r in rec if r[0] == "step"]
+    if want("stepwise"):
+        from workload import make_policy
+        from eviction_probe_softmax_amd.pipeline import run_stepwise
+        pol = make_policy(device="cuda")
+        run_stepwise(cfg, inp, pol)  # warm-up
+        rec = []
+        torch.cuda.synchronize()
+        res = run_stepwise(cfg, inp, pol, record=rec)
+        torch.cuda.synchronize()
+        init_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "init"]
+        dec_ms = [r[1].elapsed_time(r[2]) for r in rec if r[0] == "step"]
+        prune_ms = [r[2].elapsed_time(r[3]) for r in rec if r[0] == "step"]
+        klv = res["kl"].float().cpu().numpy()
+        out["stepwise_r%g" % cfg.budget_ratio] = {
+            "init_prune_ms": round(float(np.mean(init_ms)), 3),
+            "append_decode_ms_per_step": round(float(np.mean(dec_ms)), 4),
+            "score_prune_ms_per_step": round(float(np.mean(prune_ms)), 4),
+            "cached_entries_last_step": int(sum(res["stepwise"].lengths)) * cfg.Ly * cfg.H,
+            "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
+    if not (want("dense_rollout") or want("ar_direction")):
+        return out
     # Dense rollout: every token a seed in both hops (a causal L x L pass per
     # hop); flops count each causal logit once per pass (rowstats, colsum)
     comp = Compressor(cfg, inp["cu_seqlens"], inp["K"].dtype)
     sc = kvc.score(comp.pb, inp["K"], inp["V"], inp["Qp"])
-    kvc.propagate_dense(comp.pb, inp["K"], inp["Qctx"], sc["r0"])  # warm-up
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    e[0].record(stream)
-    kvc.propagate_dense(comp.pb, inp["K"], inp["Qctx"], sc["r0"])
-    e[1].record(stream)
-    torch.cuda.synchronize()
-    dms = e[0].elapsed_time(e[1])
     causal = sum(L * (L + 1) // 2 for L in cfg.lens)
     flops = cfg.n_hops * 2 * cfg.Ly * cfg.H * cfg.G * causal * 2 * cfg.d
-    out["dense_rollout"] = {"ms": round(dms, 3), "tflops": round(flops / (dms * 1e-3) / 1e12, 1),
-                            "mfma_bf16_frac": round(flops / (dms * 1e-3) / 2.5e15, 4)}
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    if want("dense_rollout"):
+        kvc.propagate_dense(comp.pb, inp["K"], inp["Qctx"], sc["r0"])  # warm-up
+        e[0].record(stream)
+        kvc.propagate_dense(comp.pb, inp["K"], inp["Qctx"], sc["r0"])
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        dms = e[0].elapsed_time(e[1])
+        out["dense_rollout"] = {"ms": round(dms, 3), "tflops": round(flops / (dms * 1e-3) / 1e12, 1),
+                                "mfma_bf16_frac": round(flops / (dms * 1e-3) / 2.5e15, 4)}
     # the "A r" direction: one causal row pass per hop
-    kvc.propagate_ar(comp.pb, inp["K"], inp["Qctx"], sc["r0"])  # warm-up
-    e[0].record(stream)
-    kvc.propagate_ar(comp.pb, inp["K"], inp["Qctx"], sc["r0"])
-    e[1].record(stream)
-    torch.cuda.synchronize()
-    ams = e[0].elapsed_time(e[1])
-    out["ar_direction"] = {"ms": round(ams, 3), "tflops": round(flops / 2 / (ams * 1e-3) / 1e12, 1),
-                           "mfma_bf16_frac": round(flops / 2 / (ams * 1e-3) / 2.5e15, 4)}
-    klv = res["kl"].float().cpu().numpy()
-    out["stepwise_r%g" % cfg.budget_ratio] = {
-        "init_prune_ms": round(float(np.mean(init_ms)), 3),
-        "append_decode_ms_per_step": round(float(np.mean(dec_ms)), 4),
-        "score_prune_ms_per_step": round(float(np.mean(prune_ms)), 4),
-        "cached_entries_last_step": int(sum(res["stepwise"].lengths)) * cfg.Ly * cfg.H,
-        "mean_kl": round(float(klv.mean()), 5), "max_kl": round(float(klv.max()), 5)}
+    if want("ar_direction"):
+        kvc.propagate_ar(comp.pb, inp["K"], inp["Qctx"], sc["r0"])  # warm-up
+        e[0].record(stream)
+        kvc.propagate_ar(comp.pb, inp["K"], inp["Qctx"], sc["r0"])
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ams = e[0].elapsed_time(e[1])
+        out["ar_direction"] = {"ms": round(ams, 3), "tflops": round(flops / 2 / (ams * 1e-3) / 1e12, 1),
+                               "mfma_bf16_frac": round(flops / 2 / (ams * 1e-3) / 2.5e15, 4)}
     return out
 
 
@@ -368,7 +390,7 @@ def main():
         dfull = kvc.Decoder(full, cfg.G, Td)
         for t in range(Td):
             dfull.step(inp["Kd"], inp["Vd"], t + 1, inp["Qd"][t], _row_view(x_full, t), Td * Dm)
-        v = measure_variants(cfg, inp, full, x_full, kl_op, torch.cuda.current_stream())
+        v = measure_variants(cfg, inp, full, x_full, kl_op, torch.cuda.current_stream(), names=args.variant)
         print(json.dumps({"config": {"workload": describe(cfg)}, "variants": v}), flush=True)
         return
     elt = inp["K"].element_size()
@@ -489,7 +511,7 @@ def main():
         res["roofline"]["peak_measured"] = peaks["hbm_read_gbs"]
         res["roofline"]["frac_measured"] = round(gbs_comp / peaks["hbm_read_gbs"], 4)
     if args.variants:
-        res["variants"] = measure_variants(cfg, inp, full, x_full, kl_op, stream)
+        res["variants"] = measure_variants(cfg, inp, full, x_full, kl_op, stream, names=args.variant)
     if not args.no_cpu_baseline:
         print("[bench] timing the C++ oracle on the host cores", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(cfg, inp)

@@ -640,12 +640,13 @@ extern "C" void ko_slots(const ko_shape* sh, const ko_params* p, const int64_t* 
 // D = min(1, w_A e_A + w_V e_V), leaves D = 0. Ops: Add gains
 // rel_root (1 - D_root), Split(j) gains rel_j D_j - sum_c rel_c D_c and costs
 // (children - 1), utility fp32(sens * gain / cost). The tree of a slot comes
-// from split_children (the partition's cut scores cut_q, nullable).
+// from split_children (the partition's cut scores cut_q, nullable), or from
+// given node records topo_in (nullable).
 extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const void* K, const void* V,
                                const void* Qp, const float* lse_in, const float* rel_in, const float* sens_in,
                                const int32_t* slot_start, const int32_t* n_slots, int32_t stride,
-                               const int64_t* cut_q, float* node_rel, float* node_D, float* node_mu, float* op_util,
-                               uint8_t* op_cost, uint32_t* node_topo) {
+                               const int64_t* cut_q, const uint32_t* topo_in, float* node_rel, float* node_D,
+                               float* node_mu, float* op_util, uint8_t* op_cost, uint32_t* node_topo) {
   const int S = sh->S, Ly = sh->Ly, H = sh->H, G = sh->G, d = sh->d, P = sh->P, dt = sh->dtype;
   const int64_t T = sh->T;
   const double c = 1.0 / std::sqrt((double)d), base = p->rope_base;
@@ -696,7 +697,10 @@ extern "C" void ko_build_trees(const ko_shape* sh, const ko_params* p, const voi
       const float* r32 = rel_in + ubase + a0;
       const int64_t* cq = cut_q ? cut_q + a0 : nullptr;
       for (const auto& slot : sl.v) {
-        build_tree(slot.first, slot.second, r32, cq, p->split_mode, nodes);
+        if (topo_in)
+          slot_nodes(topo_in, (int64_t)l * H + h, T, a0, slot.first, slot.second, nodes);
+        else
+          build_tree(slot.first, slot.second, r32, cq, p->split_mode, nodes);
         const int m = (int)nodes.size();
         rel.assign(m, 0.0);
         D.assign(m, 0.0);

@@ -78,11 +78,13 @@ void ko_slots(const ko_shape* sh, const ko_params* p, const int64_t* cost_q, con
               int32_t* slot_start, int32_t* n_slots);
 /* prototype trees: node_rel/node_D/node_mu/op_util f32, op_cost u8, node_topo
  * u32 (nullable), all [Ly][H][2T]; cut_q [T] (nullable) the partition's cut
- * scores for split_mode 1 */
+ * scores for split_mode 1; topo_in (nullable) node records whose tree shapes
+ * are used instead of deciding them */
 void ko_build_trees(const ko_shape* sh, const ko_params* p, const void* K, const void* V, const void* Qp,
                     const float* lse, const float* rel, const float* sens, const int32_t* slot_start,
-                    const int32_t* n_slots, int32_t stride, const int64_t* cut_q, float* node_rel, float* node_D,
-                    float* node_mu, float* op_util, uint8_t* op_cost, uint32_t* node_topo);
+                    const int32_t* n_slots, int32_t stride, const int64_t* cut_q, const uint32_t* topo_in,
+                    float* node_rel, float* node_D, float* node_mu, float* op_util, uint8_t* op_cost,
+                    uint32_t* node_topo);
 /* singleton floor: taken [Ly][H][2T] u8 (floor ops), spent [S] */
 void ko_floor(const ko_shape* sh, const ko_params* p, const float* rel, const float* sens, const uint8_t* op_cost,
               const uint32_t* node_topo, const int32_t* slot_start, const int32_t* n_slots, int32_t stride,

@@ -212,9 +212,14 @@ def slots_for(cu, cfg, cost_q=None, cut_q=None):
     return slots_from_arrays(*slot_arrays(cu, cfg, cost_q, cut_q))
 
 
-def build_trees(K, V, Qp, lse, rel, head_sens, cu, slots, cfg, cut_q=None):
+def _topo(topo):
+    return None if topo is None else np.asarray(topo, dtype=np.uint32)
+
+
+def build_trees(K, V, Qp, lse, rel, head_sens, cu, slots, cfg, cut_q=None, topo=None):
     """Tree arrays as the Python oracle's build_trees (node_topo included);
-    cut_q: the partition's int64 [T] cut scores (split_mode 1) or None."""
+    cut_q: the partition's int64 [T] cut scores (split_mode 1) or None; topo:
+    node records whose shapes are used instead of deciding them, or None."""
     kp = _Keep()
     sh = _shape(cu, cfg, _DT[K.dtype])
     stride = slot_stride(cu, cfg)
@@ -227,13 +232,9 @@ def build_trees(K, V, Qp, lse, rel, head_sens, cu, slots, cfg, cut_q=None):
     lib().ko_build_trees(C.byref(sh), C.byref(_params(cfg)), kp.ptr(K), kp.ptr(V), kp.ptr(Qp),
                          kp.ptr(np.asarray(lse, dtype=np.float32)), kp.ptr(np.asarray(rel, dtype=np.float32)),
                          kp.ptr(np.asarray(head_sens, dtype=np.float32)), kp.ptr(ss), kp.ptr(ns), C.c_int32(stride),
-                         kp.ptr(cq), kp.ptr(out["node_rel"]), kp.ptr(out["node_D"]), kp.ptr(out["node_mu"]),
+                         kp.ptr(cq), kp.ptr(_topo(topo)), kp.ptr(out["node_rel"]), kp.ptr(out["node_D"]), kp.ptr(out["node_mu"]),
                          kp.ptr(out["op_util"]), kp.ptr(out["op_cost"]), kp.ptr(out["node_topo"]))
     return out
-
-
-def _topo(topo):
-    return None if topo is None else np.asarray(topo, dtype=np.uint32)
 
 
 def floor_select(rel, head_sens, op_cost, cu, slots, cfg, topo=None):

@@ -27,7 +27,7 @@ import torch
 
 from oracle import cpp_oracle as co
 from workload import get_config, make_inputs
-from parity import as_np, close, jaccard, check_kl, slots_from_dev
+from parity import as_np, close, jaccard, check_kl, slots_from_dev, topo_np
 
 pytestmark = pytest.mark.gpu
 
@@ -81,8 +81,11 @@ def _oracle_select(sub, cfg_s, pre):
     if cfg_s.token_mode:
         taken, spent = co.token_topk(pre["rel"], cu, cfg_s)
     else:
-        ft, fs = co.floor_select(pre["rel"], pre["head_sens"], pre["trees"]["op_cost"], cu, pre["slots"], cfg_s)
-        taken, spent = co.auction(pre["trees"]["op_util"], pre["trees"]["op_cost"], ft, fs, cu, pre["slots"], cfg_s)
+        topo = pre["trees"]["node_topo"] if cfg_s.split_mode else None
+        ft, fs = co.floor_select(pre["rel"], pre["head_sens"], pre["trees"]["op_cost"], cu, pre["slots"], cfg_s,
+                                 topo=topo)
+        taken, spent = co.auction(pre["trees"]["op_util"], pre["trees"]["op_cost"], ft, fs, cu, pre["slots"], cfg_s,
+                                  topo=topo)
     cache = co.pack(sub["K"], sub["V"], pre["rel"], pre.get("trees"), taken, cu, pre["slots"], cfg_s)
     return taken, spent, cache
 
@@ -100,8 +103,9 @@ def _oracle_pre(sub, cfg_s):
             cq, kq = co.slot_costs(sub["hidden"], cu, cfg_s, sub.get("surprisal"))
         pre["slots"] = co.slots_for(cu, cfg_s, cq, kq)
         t2 = time.perf_counter()
+        pre["cut_q"] = kq
         pre["trees"] = co.build_trees(sub["K"], sub["V"], sub["Qp"], pre["lse"], pre["rel"], pre["head_sens"], cu,
-                                      pre["slots"], cfg_s)
+                                      pre["slots"], cfg_s, cut_q=kq)
         _log(f"  oracle: scores+propagation {t1 - t0:.1f}s, slots {t2 - t1:.1f}s, trees "
              f"{time.perf_counter() - t2:.1f}s ({co.threads()} threads)")
     return pre
@@ -151,12 +155,23 @@ def _check_sequence(cfg, inp, out, xf, xc, klv, steps, s, pre=None, tag=""):
          f"({rows} rows compared), max |d ln mu| {worst:.2e}")
     assert j >= 0.99, j
     assert matched >= 0.9 * units, matched
-    # the oracle's pack of the GPU's taken set, and decode + KL at the steps
-    if np.array_equal(taken_g, taken_o):
+    # the oracle's pack of the GPU's taken set (on the GPU's tree shapes), and
+    # decode + KL at the steps
+    trees_g = pre.get("trees")
+    if cfg.split_mode:
+        topo_g = topo_np(out["trees"]["node_topo"])[:, :, 2 * a:2 * b]
+        same = float((topo_g == trees_g["node_topo"]).mean())
+        _log(f"  tree shapes equal to the oracle's at {same:.6f} of the records; three-way splits "
+             f"{int((trees_g['op_cost'] == 2).sum())}, taken {int(((trees_g['op_cost'] == 2) & (taken_o > 0)).sum())}")
+        assert same >= 0.99, same
+        if same < 1.0:
+            trees_g = co.build_trees(sub["K"], sub["V"], sub["Qp"], pre["lse"], pre["rel"], pre["head_sens"],
+                                     np.array([0, L]), pre["slots"], cfg_s, topo=topo_g)
+    if np.array_equal(taken_g, taken_o) and trees_g is pre.get("trees"):
         cache_g = cache_o
     else:
         cu = np.array([0, L])
-        cache_g = co.pack(sub["K"], sub["V"], pre["rel"], pre.get("trees"), taken_g, cu, pre["slots"], cfg_s)
+        cache_g = co.pack(sub["K"], sub["V"], pre["rel"], trees_g, taken_g, cu, pre["slots"], cfg_s)
     fv = co.full_view(sub["K"], sub["V"], np.array([0, L]))
     xf_o = np.stack([co.decode_step(fv, sub["Kd"], sub["Vd"], sub["Qd"][t], t, cfg.G)[0] for t in steps])
     xc_o = np.stack([co.decode_step(cache_g, sub["Kd"], sub["Vd"], sub["Qd"][t], t, cfg.G)[0] for t in steps])
@@ -167,8 +182,8 @@ def _check_sequence(cfg, inp, out, xf, xc, klv, steps, s, pre=None, tag=""):
     return pre
 
 
-def _run(name, seqs, steps, extra=None):
-    cfg = get_config(name)
+def _run(name, seqs, steps, extra=None, cfg_kw=None):
+    cfg = get_config(name).replace(**(cfg_kw or {}))
     t0 = time.perf_counter()
     inp = make_inputs(cfg, device="cuda")
     torch.cuda.synchronize()
@@ -192,6 +207,12 @@ def test_fullsize_e2e_mistral1():
 @pytest.mark.timeout(900)
 def test_fullsize_e2e_fulldepth():
     _run("fulldepth", [0], [0, 31, 63])
+
+
+@pytest.mark.timeout(900)
+def test_fullsize_e2e_fulldepth_tree_splits():
+    # curvature-candidate cuts and salient three-way splits (split_mode 1)
+    _run("fulldepth", [0], [0, 63], cfg_kw={"split_mode": 1})
 
 
 @pytest.mark.timeout(900)

@@ -64,6 +64,11 @@ def test_slots_trees_and_selection(both):
         tr = co.build_trees(inp["K"], inp["V"], inp["Qp"], a["lse"], a["rel"], a["head_sens"], cu, a["slots"], cfg,
                             cut_q=a.get("dp_cut_q"))
         assert np.array_equal(tr["node_topo"], a["trees"]["node_topo"])
+        # given shapes: the same trees from the records alone
+        tg = co.build_trees(inp["K"], inp["V"], inp["Qp"], a["lse"], a["rel"], a["head_sens"], cu, a["slots"], cfg,
+                            topo=a["trees"]["node_topo"])
+        for k in ("node_topo", "op_cost", "node_rel", "node_D", "node_mu", "op_util"):
+            assert np.array_equal(tg[k], tr[k]), k
         # floor and auction on the Python oracle's fp32 inputs: bit-exact
         topo = a["trees"]["node_topo"]
         ft, fs = co.floor_select(a["rel"], a["head_sens"], a["trees"]["op_cost"], cu, a["slots"], cfg, topo=topo)
