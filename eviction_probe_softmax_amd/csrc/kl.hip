@@ -273,6 +273,162 @@ __global__ __launch_bounds__(THREADS) void gemm_kl_kernel(const T* xh, const T* 
   }
 }
 
+// ------------------------------------------------------------------ many rows
+// From a thousand rows on the projection is MFMA work (2 * rows * vocab *
+// d_model flops against one read of W), and the small kernel above is bound
+// by LDS traffic: every 32x32x16 product needs 1.25 KB of fragment reads.
+// Here a workgroup of 8 waves (two per SIMD) owns a 256 x 256 output tile and
+// each wave a 64 x 128 block (8 accumulators of 32 x 32): a 16-k step reads 6
+// fragments for 8 products. Operand tiles go global -> LDS with the direct
+// 16-byte LDS loads (no register staging), four 32-k stages deep: the loads
+// of stage s + 3 are in flight while stage s is multiplied. One such load
+// writes the 64 lanes' 16-byte pieces to 1 KB of LDS in lane order; lane L
+// of a load covering tile rows 16 b .. 16 b + 15 brings row 16 b + L / 4,
+// piece (L % 4) ^ f(row) of that row's 64-byte chunk, so LDS holds every row
+// with its four pieces permuted by f(row) = ((row >> 1) ^ (row >> 3)) & 3,
+// and a fragment read of 8 or 16 consecutive rows at one k touches distinct
+// banks. Consecutive workgroups take consecutive row tiles of one column
+// tile, so the W chunks in flight are shared by the workgroups running
+// together (an order blocked per XCD measured no better).
+constexpr int BT = 256;            // rows and vocab columns of a workgroup tile
+constexpr int BK = 32;             // k of one LDS stage (two 16-k MFMA steps): 64 bytes a row
+constexpr int NSTG = 4;            // LDS stages
+constexpr int BIG_MIN_ROWS = 1024; // the tiled kernel from this many (padded) rows on
+
+__device__ __forceinline__ int kl_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+constexpr int BIG_THREADS = 512;   // 8 waves: 2 per SIMD, each 64 rows x 128 columns
+
+__global__ __launch_bounds__(BIG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kl_big_kernel(const uint16_t* xh, const uint16_t* W, int64_t n_pairs, int dm, int vocab, int ntr, int ntc,
+                        float* part) {
+  __shared__ __align__(16) uint16_t lds[NSTG][2][BT * BK];   // [stage][x^, W][row][k], pieces permuted
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int tr = blockIdx.x % ntr, tc = blockIdx.x / ntr;   // row tiles fastest
+  const int64_t r0 = (int64_t)tr * BT, c0 = (int64_t)tc * BT;
+  // this lane's source in each of the wave's 2 loads per operand and stage:
+  // load j covers tile rows 16 (2 wave + j) .. + 15
+  const int lrow = lane >> 2;
+  const uint16_t* xsrc[2];
+  const uint16_t* wsrc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 16 + lrow;
+    const int pg = (lane & 3) ^ kl_swz(row);
+    xsrc[j] = xh + (r0 + row) * dm + pg * 8;
+    wsrc[j] = W + (c0 + row) * dm + pg * 8;
+  }
+  const int nch = dm / BK;
+  kvc_f32x16 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = kvc_f32x16{};
+  auto issue = [&](int ch) {   // loads of chunk ch into its stage
+    const int st = ch % NSTG;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint16_t* dx = lds[st][0] + (2 * wave + j) * 16 * BK;
+      uint16_t* dw = lds[st][1] + (2 * wave + j) * 16 * BK;
+      __builtin_amdgcn_global_load_lds((const void*)(xsrc[j] + ch * BK),
+                                       (__attribute__((address_space(3))) void*)dx, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(wsrc[j] + ch * BK),
+                                       (__attribute__((address_space(3))) void*)dw, 16, 0, 0);
+    }
+  };
+  // fragment rows: x^ rows wr*64 + 32 u + (lane & 31), W rows wc*128 + 32 u + (lane & 31)
+  const int ra = wr * 64 + (lane & 31), rb = wc * 128 + (lane & 31);
+  auto compute = [&](int st) {
+    const uint16_t* sx = lds[st][0];
+    const uint16_t* sw = lds[st][1];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int q = 2 * ks + (lane >> 5);
+      kvc_bf16x8 fa[2], fb[4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int xr = ra + 32 * u;
+        fa[u] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sx + xr * BK + ((q ^ kl_swz(xr)) * 8)));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int wr2 = rb + 32 * u;
+        fb[u] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sw + wr2 * BK + ((q ^ kl_swz(wr2)) * 8)));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  // Stage it: wait until this wave's loads of chunk it have landed (4 loads a
+  // chunk per wave; chunks it + 1, it + 2 may still fly), then a barrier makes
+  // every wave's loads of it visible and guarantees that every wave is done
+  // reading stage it - 1, whose buffer chunk it + 3 then refills. The wait
+  // counts are immediates. (A plain s_barrier: __syncthreads would also wait
+  // for every load in flight.)
+#pragma unroll
+  for (int c = 0; c < 3; ++c)
+    if (c < nch) issue(c);
+  for (int it = 0; it < nch; ++it) {
+    if (it + 2 < nch)   // uniform branches
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else if (it + 1 < nch)
+      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    if (it + 3 < nch) issue(it + 3);
+    compute(it % NSTG);
+  }
+  // epilogue: lane owns columns c0 + wc*128 + 32 u + (lane & 31); registers
+  // v, v+1 (v % 4 in {0, 2}) of row block q hold rows 2p and 2p+1 of a pair.
+  // Each pair's statistics over the wave's 128 columns.
+  const int nsub = vocab / 128;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+#pragma clang fp contract(off)
+      const int row = wr * 64 + q * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      const int64_t pair = (r0 + row) >> 1;
+      float y[4], yh[4];
+      float mf = -INFINITY, mc = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        y[u] = acc[q][u][v] * LOG2E;
+        yh[u] = acc[q][u][v + 1] * LOG2E;
+        mf = fmaxf(mf, y[u]);
+        mc = fmaxf(mc, yh[u]);
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        mf = fmaxf(mf, __shfl_xor(mf, o, 64));
+        mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+      }
+      float sf = 0.f, sc = 0.f, t = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float ef = fast_exp2(y[u] - mf), ec = fast_exp2(yh[u] - mc);
+        sf += ef;
+        sc += ec;
+        t += ef * (acc[q][u][v] - acc[q][u][v + 1]);
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        sf += __shfl_xor(sf, o, 64);
+        sc += __shfl_xor(sc, o, 64);
+        t += __shfl_xor(t, o, 64);
+      }
+      if ((lane & 31) == 0 && pair < n_pairs) {
+        float* pp = part + (pair * nsub + (int64_t)tc * 2 + wc) * 5;
+        pp[0] = mf; pp[1] = sf; pp[2] = mc; pp[3] = sc; pp[4] = t;
+      }
+    }
+  }
+}
+
 // One workgroup per pair: threads merge strided subsets of the column-tile
 // partials, then the wave and the workgroup merge theirs.
 __global__ __launch_bounds__(256) void kl_combine_kernel(const float* part, int64_t n_pairs, int nsub, float* kl) {
@@ -305,11 +461,20 @@ __global__ __launch_bounds__(256) void kl_combine_kernel(const float* part, int6
   kl[p] = st.t / st.sf - lse_f + lse_c;
 }
 
+// rows padded for the kernel that will run: 256 for the tiled one, else 32
+bool kl_big(int64_t n_pairs, int32_t d_model, int32_t vocab, int32_t w_dtype) {
+  return w_dtype == KVC_BF16 && 2 * n_pairs >= BIG_MIN_ROWS && vocab % BT == 0 && d_model % 64 == 0;
+}
+int64_t kl_rows_padded(int64_t n_pairs, int32_t d_model, int32_t vocab, int32_t w_dtype) {
+  const int64_t q = kl_big(n_pairs, d_model, vocab, w_dtype) ? BT : 32;
+  return (2 * n_pairs + q - 1) / q * q;
+}
+
 }  // namespace
 
 extern "C" size_t kvc_kl_workspace(int64_t n_pairs, int32_t d_model, int32_t vocab, int32_t w_dtype) {
   if (n_pairs <= 0 || d_model <= 0 || vocab <= 0) return 0;
-  int64_t m_pad = (2 * n_pairs + 31) / 32 * 32;
+  int64_t m_pad = kl_rows_padded(n_pairs, d_model, vocab, w_dtype);
   size_t elt = w_dtype == KVC_BF16 ? 2 : 4;
   int64_t ntile = (vocab + NT - 1) / NT;
   kvc::Carver c(nullptr, 0);
@@ -327,7 +492,8 @@ extern "C" int kvc_kl(int64_t n_pairs, int32_t d_model, int32_t vocab, const flo
   KVC_REQUIRE(x_full && x_comp && W && kl_out, KVC_E_INVAL, "kvc_kl: NULL pointer");
   KVC_REQUIRE(ws && ws_bytes >= kvc_kl_workspace(n_pairs, d_model, vocab, w_dtype), KVC_E_WORKSPACE,
               "kvc_kl: workspace too small");
-  int64_t m_pad = (2 * n_pairs + 31) / 32 * 32;
+  const bool big = kl_big(n_pairs, d_model, vocab, w_dtype);
+  int64_t m_pad = kl_rows_padded(n_pairs, d_model, vocab, w_dtype);
   int64_t ntile = (vocab + NT - 1) / NT;
   kvc::Carver c(ws, ws_bytes);
   size_t elt = w_dtype == KVC_BF16 ? 2 : 4;
@@ -338,6 +504,16 @@ extern "C" int kvc_kl(int64_t n_pairs, int32_t d_model, int32_t vocab, const flo
     hipLaunchKernelGGL(rmsnorm_cast_kernel<uint16_t>, dim3((unsigned)m_pad), dim3(256), 0, st, x_full, x_comp,
                        n_pairs, d_model, m_pad, (uint16_t*)xh);
     KVC_LAUNCH_CHECK("rmsnorm_cast");
+    if (big) {
+      const int ntr = (int)(m_pad / BT), ntc = vocab / BT;
+      hipLaunchKernelGGL(gemm_kl_big_kernel, dim3((unsigned)(ntr * ntc)), dim3(BIG_THREADS), 0, st,
+                         (const uint16_t*)xh, (const uint16_t*)W, n_pairs, d_model, vocab, ntr, ntc, part);
+      KVC_LAUNCH_CHECK("gemm_kl_big");
+      hipLaunchKernelGGL(kl_combine_kernel, dim3((unsigned)n_pairs), dim3(256), 0, st, part, n_pairs, vocab / 128,
+                         kl_out);
+      KVC_LAUNCH_CHECK("kl_combine");
+      return KVC_OK;
+    }
     const int sm = 2 * (KlTile<uint16_t>::XS + KlTile<uint16_t>::WS) * 16;
     (void)hipFuncSetAttribute((const void*)gemm_kl_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize, sm);
     hipLaunchKernelGGL(gemm_kl_kernel<uint16_t>, g2, dim3(THREADS), sm, st, (const uint16_t*)xh,

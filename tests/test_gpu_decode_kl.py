@@ -225,10 +225,15 @@ def test_decode_planned_steps_match_single_call_and_repeat(name):
 
 @pytest.mark.parametrize("w_dtype,dm,vocab,n", [("f32", 256, 2048, 37), ("bf16", 1024, 1000, 37),
                                                  ("bf16", 4096, 32768, 37), ("bf16", 512, 1000, 100),
-                                                 ("f32", 384, 300, 70), ("bf16", 128, 64, 1)])
+                                                 ("f32", 384, 300, 70), ("bf16", 128, 64, 1),
+                                                 ("bf16", 256, 8192, 1024), ("bf16", 1024, 4096, 600),
+                                                 ("bf16", 256, 1024, 1100)])
 def test_kl_matches_oracle(w_dtype, dm, vocab, n):
     """n pairs give 2n rows: 37 leaves a partial last row block, 100 and 70
-    span two 128-row tiles, vocab 1000 / 300 / 64 leave partial column tiles."""
+    span two 128-row tiles, vocab 1000 / 300 / 64 leave partial column tiles;
+    from 1,024 rows on (bf16, vocab a multiple of 256) the 256 x 256-tiled
+    kernel runs: 2,048 rows x 8,192 columns, and 1,200 and 2,200 rows with a
+    padded last row tile."""
     kvc = _kvc()
     g = torch.Generator().manual_seed(3)
     xf = torch.randn((n, dm), generator=g)
@@ -243,3 +248,23 @@ def test_kl_matches_oracle(w_dtype, dm, vocab, n):
     assert err.max() <= 1e-3, (err.max(), want[:4], as_np(got)[:4])
     same = kvc.kl(xf.cuda(), xf.cuda(), W.cuda())
     assert torch.all(same == 0), same
+
+
+def test_kl_at_the_ragged_batch_shape_on_sampled_pairs():
+    """The bench's KL call: 4,096 pairs (8,192 rows) x d_model 4,096 x vocab
+    32,768 in bf16; sampled pairs against the oracle, identical rows give 0."""
+    kvc = _kvc()
+    g = torch.Generator().manual_seed(5)
+    n, dm, vocab = 4096, 4096, 32768
+    xf = torch.randn((n, dm), generator=g)
+    xc = xf + 0.3 * torch.randn((n, dm), generator=g)
+    xc[7] = xf[7]
+    W = (torch.randn((vocab, dm), generator=g) * (4.0 / math.sqrt(dm))).to(torch.bfloat16)
+    got = as_np(kvc.kl(xf.cuda(), xc.cuda(), W.cuda()))
+    torch.cuda.synchronize()
+    idx = [0, 1, 7, 255, 256, 1023, 2048, 3333, 4095]
+    want = oracle.kl_rows(xf[idx].numpy(), xc[idx].numpy(), W, "bf16")
+    err = np.abs(got[idx] - want)
+    print(f"[kl] ragged shape: max |dKL| {err.max():.2e} over {len(idx)} sampled pairs", flush=True)
+    assert err.max() <= 1e-3, (err.max(), got[idx], want)
+    assert got[7] == 0.0
