@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--trace-summary", default=None, metavar="CSV",
                     help="only summarize a rocprofv3 kernel_trace.csv of a bench run (per kernel, the decode "
                          "kernels split by cache: the compressed cache's calls launch fewer workgroups), then exit")
+    ap.add_argument("--trace-steps", type=int, default=0, metavar="N",
+                    help="with --trace-summary: the bench steps the trace covers (warm-up included), to split "
+                         "kernels launched a few times a step by launch position")
     ap.add_argument("--counter-summary", default=None, metavar="CSV",
                     help="only summarize a rocprofv3 --pmc counter_collection.csv of a bench run (mean counter "
                          "value per dispatch of each kernel, the decode kernels split by cache), then exit")
@@ -261,14 +264,17 @@ def measure_variants(cfg, inp, full, x_full, kl_op, stream, steps=2, names=None)
     return out
 
 
-def trace_summary(path):
+def trace_summary(path, nsteps=0):
     """Per-kernel summary of a rocprofv3 kernel_trace.csv (one row a
     dispatch): calls, total and mean microseconds, mean grid. The decode
     kernels are split by cache: within one run the calls over the compressed
     cache launch fewer workgroups than those over the full cache, so the
     dispatches of each decode kernel fall into two grid sizes (per step; the
     tail pieces grow with the step), and the smaller half is the compressed
-    cache's. Prints a markdown table."""
+    cache's. With nsteps (the bench steps the trace covers, warm-up
+    included), a kernel launched 2-4 times a step is split by its launch
+    position within the step (#1, #2, ...: the probe pass, then the
+    propagation hops). Prints a markdown table."""
     import csv
     from collections import defaultdict
     rows = list(csv.DictReader(open(path)))
@@ -292,6 +298,11 @@ def trace_summary(path):
                 full, comp = comp, full
             out[short + " [full cache]"] += full
             out[short + " [25% cache]"] += comp
+        elif nsteps and len(lst) % nsteps == 0 and 2 <= len(lst) // nsteps <= 4:
+            per = len(lst) // nsteps
+            lst.sort()
+            for k in range(per):
+                out[f"{short} #{k + 1}"] += lst[k::per]
         else:
             out[short or name] += lst
     tot = sum(d for lst in by.values() for _, d, _ in lst)
@@ -349,7 +360,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(args.trace_summary, args.trace_steps)
         return
     if args.counter_summary:
         counter_summary(args.counter_summary)
