@@ -106,9 +106,26 @@ struct TreeLayout {
   static constexpr size_t nsib = al(npar + (size_t)2 * NMAX * 2);
   static constexpr size_t misc = al(nsib + (size_t)2 * NMAX * 2);
   static constexpr size_t total = al(misc + 32);
+  // value-error scratch of midpoint trees (small slots), over the staged values
+  // once the Gram matrix is formed: cross-block partials, the (a^T G a, Z, a.s)
+  // of the children and grandchildren of the root, the big nodes' G w vectors
+  // and w^T G w, and the root's a^T G w partials
+  static constexpr int MP_ITEMS = 20;
+  static constexpr size_t mp_part = 0;
+  static constexpr size_t mp_q = al(mp_part + (size_t)MP_ITEMS * PDMAX * 4);
+  static constexpr size_t mp_gv = al(mp_q + (size_t)3 * 6 * PDMAX * 4);
+  static constexpr size_t mp_w = al(mp_gv + (size_t)3 * NMAX * 4);
+  static constexpr size_t mp_rq = al(mp_w + 16);
+  static constexpr size_t mp_end = al(mp_rq + (size_t)4 * PDMAX * 4);
+  static_assert(!STAGED || mp_end <= R1B, "midpoint value-error scratch fits over the staged values");
   // phase-A scratch for the per-group value column sums lives in the weight array
   static_assert((size_t)(WAVES * 64 / (D / 8)) * D * 4 <= (size_t)NMAX * PA * 4, "value-sum scratch");
 };
+
+// the hardware square root and reciprocal (about 1 ulp each) instead of the
+// correctly rounded library sequences, which cost a dozen instructions apiece
+__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
+__device__ __forceinline__ float hw_div(float x, float y) { return x * __builtin_amdgcn_rcpf(y); }
 
 // x = hi + lo in bf16 pieces, each the round-to-nearest-even of the
 // remainder so far: |x - hi - lo| <= 2^-18 |x|
@@ -207,6 +224,80 @@ __device__ __forceinline__ void qform_block(const float* Gm, int NG, const float
   }
   num = fmaf(2.f, sn, num);
   den = fmaf(2.f, sd, den);
+}
+
+// Value-aggregate forms of one node of at most S tokens, lane = distortion row:
+// Z = sum a_i, as = sum a_i s_i and, with c_i = a_i - Z w_i (w_i = al r_i + ga),
+// num = c^T G c and qa = a^T G a over the node's block of the centred value
+// Gram, each pair of tokens once by symmetry. sz is uniform over the wave.
+template <int S>
+__device__ __forceinline__ void small_forms(const float* Gm, int NG, const float* At, const float* rtok,
+                                            const float* sdot, int lane, int st, int sz, int nrows, float al,
+                                            float ga, float& Z, float& as, float& num, float& qa) {
+  // a window of S tokens [ws, ws + S) inside the first nrows rows (where the
+  // Gram matrix is written) holds the node; tokens of the window outside the
+  // node are masked to zero, and every load is an immediate offset from one
+  // base, so the whole block of loads can be in flight at once
+  const int ws = min(st, nrows - S);
+  const float* Ab = At + ws * PA + lane;
+  const float* Gb = Gm + ws * NG + ws;
+  float av[S], cv[S];
+  bool in[S];
+  Z = 0.f;
+  as = 0.f;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    in[k] = ws + k >= st && ws + k < st + sz;
+    const float x = Ab[k * PA], sd = sdot[ws + k];
+    av[k] = in[k] ? x : 0.f;
+    Z += av[k];
+    as = fmaf(av[k], in[k] ? sd : 0.f, as);
+  }
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const float c = av[k] - Z * fmaf(al, rtok[ws + k], ga);
+    cv[k] = in[k] ? c : 0.f;
+  }
+  num = 0.f;
+  qa = 0.f;
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const float gd = 0.5f * Gb[k * NG + k];
+    float tc = gd * cv[k], ta = gd * av[k];
+#pragma unroll
+    for (int l = k + 1; l < S; ++l) {
+      const float g = Gb[k * NG + l];
+      tc = fmaf(g, cv[l], tc);
+      ta = fmaf(g, av[l], ta);
+    }
+    num = fmaf(cv[k], tc, num);
+    qa = fmaf(av[k], ta, qa);
+  }
+  num *= 2.f;
+  qa *= 2.f;
+}
+
+// Pairs of one cross block: rows [r_lo, r_hi) inside the aligned 4-row group
+// g, columns [c_lo, c_hi): sum_r a_r sum_j G_rj a_j for lane = distortion row
+// (G is symmetric, so the group's four entries of row j are one 16-byte read).
+__device__ __forceinline__ float cross_block(const float* Gm, int NG, const float* At, int lane, int g, int r_lo,
+                                             int r_hi, int c_lo, int c_hi) {
+  float ar[4], t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * g + e;
+    ar[e] = (r >= r_lo && r < r_hi) ? At[r * PA + lane] : 0.f;
+  }
+#pragma unroll 4
+  for (int j = c_lo; j < c_hi; ++j) {
+    const float aj = At[j * PA + lane];
+    const float4 g4 = *(const float4*)(Gm + j * NG + 4 * g);
+    t[0] = fmaf(g4.x, aj, t[0]);
+    t[1] = fmaf(g4.y, aj, t[1]);
+    t[2] = fmaf(g4.z, aj, t[2]);
+    t[3] = fmaf(g4.w, aj, t[3]);
+  }
+  return fmaf(ar[0], t[0], fmaf(ar[1], t[1], fmaf(ar[2], t[2], ar[3] * t[3])));
 }
 
 struct ItemDesc {
@@ -408,7 +499,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         *(float4*)(d0 + 4) = make_float4(y0[4], y0[5], y0[6], y0[7]);
         *(float4*)(d0 + HD) = make_float4(y1[0], y1[1], y1[2], y1[3]);
         *(float4*)(d0 + HD + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
-        if (c == 0) knorm[i] = sqrtf(q);
+        if (c == 0) knorm[i] = hw_sqrt(q);
       }
     }
     // value statistics: thread (group g, chunk vc) keeps tokens g, g+VG, ... in registers
@@ -438,7 +529,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       float acc = 0.f;
 #pragma unroll
       for (int g = 0; g < VG; ++g) acc += vsum[g * D + dd];
-      vm[dd] = acc / (float)n;
+      vm[dd] = hw_div(acc, (float)n);
     }
     __syncthreads();
     {
@@ -518,6 +609,115 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 
     // ---- B: prototype keys, multiplicity, attention-partition error
     const int nrb = (pd + 31) / 32;
+    if constexpr (STAGED) {
+      // Every internal node at once (at most 63): each wave forms the summed
+      // keys, multiplicities and prototype keys of its nodes in registers; once
+      // every sum has read the inverse-rotated keys, the prototype keys replace
+      // them (bf16 hi/lo pieces, or fp32) and each of up to four waves runs one
+      // 32x32 tile of the prototype logits on MFMA.
+      constexpr int NPW2 = (NMAX + WAVES - 1) / WAVES;
+      const int nbk = (nint + 31) / 32;
+      const int ntile = nrb * nbk;
+      const int trb = wave % max(nrb, 1), tnb = wave / max(nrb, 1);
+      const int rho_t = trb * 32 + (lane & 31);
+      float pc[NPW2], ps[NPW2];
+#pragma unroll
+      for (int u = 0; u < NPW2; ++u) {
+        const int qq = wave + u * WAVES;
+        pc[u] = ps[u] = 0.f;
+        if (qq < nint && lane < HD) {
+          const int j = ilist[qq];
+          const int64_t prep = t0 + nst[j] + (nsz[j] - 1) / 2;
+          pc[u] = a.rc[prep * HD + lane];
+          ps[u] = a.rs[prep * HD + lane];
+        }
+      }
+      float kp0[NPW2], kp1[NPW2];
+#pragma unroll
+      for (int u = 0; u < NPW2; ++u) {
+        const int qq = wave + u * WAVES;
+        kp0[u] = kp1[u] = 0.f;
+        if (qq >= nint) continue;
+        const int j = ilist[qq];
+        const int st = nst[j], sz = nsz[j];
+        float s0 = 0.f, s1 = 0.f, kn = 0.f;
+        if (lane < HD) {
+#pragma unroll 4
+          for (int i = st; i < st + sz; ++i) {
+            s0 += Kt[(size_t)i * D + lane];
+            s1 += Kt[(size_t)i * D + lane + HD];
+            kn += knorm[i];
+          }
+        }
+        const float nrm2 = group_sum<64>(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
+        kn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kn), 0));
+        const float coh = kn > 0.f ? hw_div(hw_sqrt(nrm2), kn) : 1.f;
+        const float mu = fmaxf(1.f, (float)sz * coh);
+        if (lane == 0) nmu[j] = mu;
+        const float rsz = __builtin_amdgcn_rcpf((float)sz);
+        const float m0 = s0 * rsz, m1 = s1 * rsz;
+        kp0[u] = m0 * pc[u] - m1 * ps[u];
+        kp1[u] = m1 * pc[u] + m0 * ps[u];
+      }
+      __syncthreads();  // every sum has read the inverse-rotated keys
+      uint16_t* PKh = (uint16_t*)(smem + Lo::r1);  // [64][KHS] hi pieces (bf16 inputs)
+      uint16_t* PKl = PKh + (size_t)64 * KHS;       // [64][KHS] lo pieces
+      float* PK = (float*)(smem + Lo::r1);         // [64][KHS] fp32 keys (fp32 inputs)
+      static_assert((size_t)64 * KHS * 4 <= Lo::R1B, "prototype keys of every node fit over the keys");
+#pragma unroll
+      for (int u = 0; u < NPW2; ++u) {
+        const int qq = wave + u * WAVES;
+        if (qq >= nint || lane >= HD) continue;
+        if constexpr (sizeof(T) == 2) {
+          // k^ = hi + lo with |k^ - hi - lo| <= 2^-18 |k^|; the queries are exact in bf16
+          const uint16_t h0 = f32_to_bf16_bits(kp0[u]), h1 = f32_to_bf16_bits(kp1[u]);
+          PKh[qq * KHS + lane] = h0;
+          PKh[qq * KHS + lane + HD] = h1;
+          PKl[qq * KHS + lane] = f32_to_bf16_bits(kp0[u] - bf16_bits_to_f32(h0));
+          PKl[qq * KHS + lane + HD] = f32_to_bf16_bits(kp1[u] - bf16_bits_to_f32(h1));
+        } else {
+          PK[qq * KHS + lane] = kp0[u];
+          PK[qq * KHS + lane + HD] = kp1[u];
+        }
+      }
+      __syncthreads();
+      float* LGa = (float*)(smem + Lo::kh);  // [64][LGS] prototype logits of every node
+      static_assert((size_t)64 * LGS * 4 <= Lo::KHR, "logits of every node fit");
+      if (wave < ntile) {
+        kvc_f32x16 acc = {};
+        const int row = tnb * 32 + (lane & 31);
+#pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          const int c = u * 16 + 8 * (lane >> 5);
+          const Frag<T> qf = rho_t < pd ? load_frag<T>(Qu + (int64_t)rho_t * a.pstride * D + c) : zero_frag<T>();
+          if constexpr (sizeof(T) == 2) {
+            mma(acc, load_frag<uint16_t>(PKh + row * KHS + c), qf);
+            mma(acc, load_frag<uint16_t>(PKl + row * KHS + c), qf);
+          } else {
+            mma(acc, load_frag<T>(PK + row * KHS + c), qf);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) LGa[(tnb * 32 + acc_row(v, lane)) * LGS + rho_t] = acc[v];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NPW2; ++u) {
+        const int qq = wave + u * WAVES;
+        if (qq >= nint) continue;
+        const int j = ilist[qq];
+        const int st = nst[j], sz = nsz[j];
+        float z = 0.f, zh = 0.f;
+        if (lane < pd) {
+#pragma unroll 8
+          for (int i = st; i < st + sz; ++i) z += At[i * PA + lane];
+          zh = nmu[j] * fast_exp2((LGa[qq * LGS + lane] * a.c - lse_s[lane]) * 1.4426950408889634f);
+        }
+        const float eAn = group_sum<64>(fabsf(zh - z)), eAd = group_sum<64>(z);
+        if (lane == 0) nD[j] = eAd > 0.f ? hw_div(eAn, eAd) : 0.f;
+      }
+      // the value staging of C overwrites the keys only after its own barrier
+    } else
     for (int q0 = 0; q0 < nint; q0 += NB) {
       const int nb = min(NB, nint - q0);
       float pc[NPW], ps[NPW];
@@ -555,11 +755,12 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         }
         float nrm2 = group_sum<64>(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
         kn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kn), 0));
-        float coh = kn > 0.f ? sqrtf(nrm2) / kn : 1.f;
+        float coh = kn > 0.f ? hw_div(hw_sqrt(nrm2), kn) : 1.f;
         float mu = fmaxf(1.f, (float)sz * coh);
         if (lane == 0) nmu[j] = mu;
         if (lane < HD) {
-          float m0 = s0 / (float)sz, m1 = s1 / (float)sz;
+          const float rsz = __builtin_amdgcn_rcpf((float)sz);
+          float m0 = s0 * rsz, m1 = s1 * rsz;
           const float k0 = m0 * pc[u] - m1 * ps[u], k1 = m1 * pc[u] + m0 * ps[u];
           if constexpr (sizeof(T) == 2) {
             // k^ = hi + lo with |k^ - hi - lo| <= 2^-18 |k^|; the queries are exact in bf16
@@ -618,7 +819,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           zh = nmu[j] * fast_exp2((LG[qq * LGS + lane] * a.c - lse_s[lane]) * 1.4426950408889634f);
         }
         float eAn = group_sum<64>(fabsf(zh - z)), eAd = group_sum<64>(z);
-        if (lane == 0) nD[j] = eAd > 0.f ? eAn / eAd : 0.f;
+        if (lane == 0) nD[j] = eAd > 0.f ? hw_div(eAn, eAd) : 0.f;
       }
       __syncthreads();  // the next batch's keys overwrite these logits
     }
@@ -750,6 +951,156 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           if (ti != tj) Gm[cc * NG + r] = acc[v];
         }
       }
+      if (STAGED && !a.topo) {
+        // Midpoint trees of at most 64 tokens. Nodes of at most 16 tokens take
+        // one wave each and evaluate c^T G c and a^T G a directly. The larger
+        // ones (the root and its children) are assembled from their children:
+        // a^T G a = sum over children + 2 x (pairs across children), the cross
+        // pairs spread over every wave in aligned 4-row groups; with w the
+        // node's value weights, c^T G c = a^T G a - 2 Z a^T G w + Z^2 w^T G w.
+        __syncthreads();  // the Gram matrix is complete; the staged values are free
+        constexpr int SMALLN = 16;
+        float* mpart = (float*)(smem + Lo::r1 + Lo::mp_part);  // [MP_ITEMS][PDMAX]
+        float* mq = (float*)(smem + Lo::r1 + Lo::mp_q);         // [3: a^T G a, Z, a.s][6 slots][PDMAX]
+        float* mgv = (float*)(smem + Lo::r1 + Lo::mp_gv);       // [3: root, L, R][NMAX]
+        float* mww = (float*)(smem + Lo::r1 + Lo::mp_w);        // [3] w^T G w
+        float* mrq = (float*)(smem + Lo::r1 + Lo::mp_rq);       // [4][PDMAX]
+        const float mm = misc[0];
+        const int nl = (n + 1) >> 1, nr = n - nl;
+        const int nll = (nl + 1) >> 1, nrl = (nr + 1) >> 1;
+        const int jR = 2 * nl;
+        const bool bigT = n > SMALLN, bigL = nl > SMALLN, bigR = nr > SMALLN;
+        // cross items: root (rows [0, nl) x columns [nl, n)), L (rows [0, nll) x
+        // [nll, nl)), R (rows [nl, nl + nrl) x [nl + nrl, n)), in 4-row groups
+        const int K0 = bigT ? (nl + 3) >> 2 : 0;
+        const int K1 = bigL ? (nll + 3) >> 2 : 0;
+        const int g2 = nl >> 2;
+        const int K2 = bigR ? ((nl + nrl + 3) >> 2) - g2 : 0;
+        // slot of a node whose (a^T G a, Z, a.s) a big parent reads
+        auto slot_of = [&](int j) {
+          if (bigT && j == 1) return 0;
+          if (bigT && j == jR) return 1;
+          if (bigL && j == 2) return 2;
+          if (bigL && j == 1 + 2 * nll) return 3;
+          if (bigR && j == jR + 1) return 4;
+          if (bigR && j == jR + 2 * nrl) return 5;
+          return -1;
+        };
+        auto weights = [&](int j, int sz, float& al, float& ga) {
+          const float rl = nrel[j];
+          al = rl > 0.f ? hw_div(1.f - a.beta, rl) : 0.f;
+          ga = hw_div(rl > 0.f ? a.beta : 1.f, (float)sz);
+        };
+        auto finish = [&](int j, float num, float den) {
+          const float eVn = group_sum<64>(lane < pd ? hw_sqrt(fmaxf(num, 0.f)) : 0.f);
+          const float eVd = group_sum<64>(lane < pd ? hw_sqrt(fmaxf(den, 0.f)) : 0.f);
+          if (lane == 0) {
+            const float eV = eVd > 0.f ? hw_div(eVn, eVd) : 0.f;
+            nD[j] = fminf(1.f, a.wA * nD[j] + a.wV * eV);
+          }
+        };
+        // cross items, dealt to the waves in order
+        for (int k = wave; k < K0 + K1 + K2; k += WAVES) {
+          float x;
+          if (k < K0) x = cross_block(Gm, NG, At, lane, k, 0, nl, nl, n);
+          else if (k < K0 + K1) x = cross_block(Gm, NG, At, lane, k - K0, 0, nll, nll, nl);
+          else x = cross_block(Gm, NG, At, lane, g2 + (k - K0 - K1), nl, nl + nrl, nl + nrl, n);
+          mpart[k * PDMAX + lane] = x;
+        }
+        // G w of the big nodes (lane = token), and w^T G w
+        if (wave == WAVES - 2 && bigT) {
+          float al, ga;
+          weights(0, n, al, ga);
+          float gv = 0.f;
+          if (lane < n) {
+#pragma unroll 4
+            for (int j = 0; j < n; ++j) gv = fmaf(Gm[j * NG + lane], fmaf(al, rtok[j], ga), gv);
+            mgv[lane] = gv;
+          }
+          const float ww = group_sum<64>(lane < n ? fmaf(al, rtok[lane], ga) * gv : 0.f);
+          if (lane == 0) mww[0] = ww;
+        }
+        if (wave == WAVES - 1 && (bigL || bigR)) {
+          const bool inL = lane < nl;
+          float alL, gaL, alR, gaR;
+          weights(1, nl, alL, gaL);
+          weights(jR, nr, alR, gaR);
+          const float al = inL ? alL : alR, ga = inL ? gaL : gaR;
+          const int vst = inL ? 0 : nl, vn = inL ? nl : nr;
+          float gv = 0.f;
+          if (lane < n) {
+            for (int j = 0; j < vn; ++j) gv = fmaf(Gm[(vst + j) * NG + lane], fmaf(al, rtok[vst + j], ga), gv);
+            mgv[(inL ? 1 : 2) * NMAX + lane] = gv;
+          }
+          const float wg = lane < n ? fmaf(al, rtok[lane], ga) * gv : 0.f;
+          const float wwL = group_sum<64>(inL ? wg : 0.f), wwR = group_sum<64>(inL ? 0.f : wg);
+          if (lane == 0) {
+            mww[1] = wwL;
+            mww[2] = wwR;
+          }
+        }
+        // nodes of at most 16 tokens, one wave each
+        for (int q = wave; q < nint; q += WAVES) {
+          const int j = ilist[q];
+          const int st = nst[j], sz = nsz[j];
+          if (sz > SMALLN) continue;
+          float al, ga;
+          weights(j, sz, al, ga);
+          float Z, as, num, qa;
+          if (sz <= 2) small_forms<2>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          else if (sz <= 4) small_forms<4>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          else if (sz <= 8) small_forms<8>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          else small_forms<16>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          const int sl = slot_of(j);
+          if (sl >= 0) {
+            mq[(0 * 6 + sl) * PDMAX + lane] = qa;
+            mq[(1 * 6 + sl) * PDMAX + lane] = Z;
+            mq[(2 * 6 + sl) * PDMAX + lane] = as;
+          }
+          finish(j, num, fmaf(2.f * Z, as, fmaf(Z * Z, mm, qa)));
+        }
+        __syncthreads();
+        // big children of the root, from their children; the root's a^T G w in quarters
+        auto big_node = [&](int j, int vst, int sz, int k0, int k1, int c0, int gvs, float qaw) {
+          float x = 0.f;
+          for (int k = k0; k < k1; ++k) x += mpart[k * PDMAX + lane];
+          const float qa = mq[(0 * 6 + c0) * PDMAX + lane] + mq[(0 * 6 + c0 + 1) * PDMAX + lane] + 2.f * x;
+          const float Z = mq[(1 * 6 + c0) * PDMAX + lane] + mq[(1 * 6 + c0 + 1) * PDMAX + lane];
+          const float as = mq[(2 * 6 + c0) * PDMAX + lane] + mq[(2 * 6 + c0 + 1) * PDMAX + lane];
+          if (gvs > 0) {  // a^T G w over the node's tokens (gvs 1, 2: L, R)
+            qaw = 0.f;
+#pragma unroll 4
+            for (int i = vst; i < vst + sz; ++i) qaw = fmaf(At[i * PA + lane], mgv[gvs * NMAX + i], qaw);
+          }
+          const float num = fmaf(Z * Z, mww[gvs], fmaf(-2.f * Z, qaw, qa));
+          finish(j, num, fmaf(2.f * Z, as, fmaf(Z * Z, mm, qa)));
+          return make_float3(qa, Z, as);
+        };
+        if (wave == 0 && bigL) {
+          const float3 r = big_node(1, 0, nl, K0, K0 + K1, 2, 1, 0.f);
+          mq[(0 * 6 + 0) * PDMAX + lane] = r.x;
+          mq[(1 * 6 + 0) * PDMAX + lane] = r.y;
+          mq[(2 * 6 + 0) * PDMAX + lane] = r.z;
+        }
+        if (wave == 1 && bigR) {
+          const float3 r = big_node(jR, nl, nr, K0 + K1, K0 + K1 + K2, 4, 2, 0.f);
+          mq[(0 * 6 + 1) * PDMAX + lane] = r.x;
+          mq[(1 * 6 + 1) * PDMAX + lane] = r.y;
+          mq[(2 * 6 + 1) * PDMAX + lane] = r.z;
+        }
+        if (wave >= 2 && wave < 6 && bigT) {
+          const int i0 = (wave - 2) * 16, i1 = min(i0 + 16, n);
+          float p = 0.f;
+          for (int i = i0; i < i1; ++i) p = fmaf(At[i * PA + lane], mgv[i], p);
+          mrq[(wave - 2) * PDMAX + lane] = p;
+        }
+        __syncthreads();
+        if (wave == 0 && bigT) {
+          const float qaw = mrq[lane] + mrq[PDMAX + lane] + mrq[2 * PDMAX + lane] + mrq[3 * PDMAX + lane];
+          big_node(0, 0, n, 0, K0, 0, 0, qaw);  // the root's a^T G w is summed from the quarters
+        }
+        __syncthreads();
+      } else {
       // the root (c = 0) and its first and last children (c = 1, 2) are shared by
       // every wave; a three-way root's middle child is a single token
       const int rlast = a.topo ? imisc[2] : 2 * ((n + 1) >> 1);
@@ -779,8 +1130,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           const int st = nst[j], sz = nsz[j];
           const float Z = zc[(c * 2) * PDMAX + lane];
           const float rl = nrel[j];
-          const float al = rl > 0.f ? (1.f - a.beta) / rl : 0.f;
-          const float ga = rl > 0.f ? a.beta / (float)sz : 1.f / (float)sz;
+          const float al = rl > 0.f ? hw_div(1.f - a.beta, rl) : 0.f;
+          const float ga = hw_div(rl > 0.f ? a.beta : 1.f, (float)sz);
           const int b0 = st >> 3, b1 = (st + sz + 7) >> 3;
           for (int b = b0; b < b1; ++b, ++item)
             if (item % WAVES == wave) qform_block(Gm, NG, At, rtok, lane, b * 8, st, sz, Z, al, ga, pn[c], pq[c]);
@@ -816,21 +1167,22 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
             as = fmaf(av, sdot[i], as);
           }
           const float rl = nrel[j];
-          const float al = rl > 0.f ? (1.f - a.beta) / rl : 0.f;
-          const float ga = rl > 0.f ? a.beta / (float)sz : 1.f / (float)sz;
+          const float al = rl > 0.f ? hw_div(1.f - a.beta, rl) : 0.f;
+          const float ga = hw_div(rl > 0.f ? a.beta : 1.f, (float)sz);
           for (int b = st >> 3; b < (st + sz + 7) >> 3; ++b)
             qform_block(Gm, NG, At, rtok, lane, b * 8, st, sz, Z, al, ga, num, den);
         }
         den = den + 2.f * Z * as + Z * Z * mm;
-        float eVn = group_sum<64>(lane < pd ? sqrtf(fmaxf(num, 0.f)) : 0.f);
-        float eVd = group_sum<64>(lane < pd ? sqrtf(fmaxf(den, 0.f)) : 0.f);
+        float eVn = group_sum<64>(lane < pd ? hw_sqrt(fmaxf(num, 0.f)) : 0.f);
+        float eVd = group_sum<64>(lane < pd ? hw_sqrt(fmaxf(den, 0.f)) : 0.f);
         if (lane == 0) {
           float eA = nD[j];
-          float eV = eVd > 0.f ? eVn / eVd : 0.f;
+          float eV = eVd > 0.f ? hw_div(eVn, eVd) : 0.f;
           nD[j] = fminf(1.f, a.wA * eA + a.wV * eV);
         }
       }
       __syncthreads();
+      }
     }
     // ---- outputs: node arrays and op utilities
     const float sens = a.sens[unit];
