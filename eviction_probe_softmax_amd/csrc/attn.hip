@@ -16,16 +16,18 @@
 // registers. In rowstats the MFMA computes K Q^T so a lane owns one query row
 // (its statistics never leave the lane); in colsum it computes Q K^T so a
 // lane owns one key (its column sums never leave the lane pair).
+#include <algorithm>
 #include <cmath>
 
 #include "kvc_internal.h"
 
 namespace {
 
-constexpr int WAVES = 4;
+constexpr int WAVES = 8;
 constexpr int THREADS = WAVES * 64;
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <class T> struct Frag;
 template <> struct Frag<uint16_t> { kvc_bf16x8 v; };
@@ -172,12 +174,13 @@ __device__ void stage_rows(const AttnArgs& a, const Work& w, int mode, Frag<T>* 
 
 // ------------------------------------------------------------------ pass 1
 template <class T, int D, bool VAL = false>
-__global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode, float* part) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 4 : 2))) void rowstats_kernel(
+    AttnArgs a, int mode, float* part) {
   constexpr int KS = D / 16;
   extern __shared__ __align__(16) char smem[];
   Frag<T>* qf = (Frag<T>*)smem;
   int* lim_s = (int*)(smem + (size_t)a.Rpad * D * sizeof(T));
-  float* red = (float*)(lim_s + a.Rpad);  // [WAVES][Rpad][3]
+  float* red = (float*)smem;  // [WAVES][Rpad][3] (+ [WAVES][Rpad]), over the staged rows once the keys are done
   Work w = decode_work(a, blockIdx.x);
   if (w.s < 0) return;
   if (mode == 1 && w.k0 > max_seed(a, w.unit)) {
@@ -196,14 +199,17 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nrb = a.Rpad >> 5;
   float m[8], sm[8], tt[8], vv[8];
-  int lim[8];
+  int minlim[8];  // the smallest last key over each row block
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
     m[rb] = -INFINITY;
     sm[rb] = 0.f;
     tt[rb] = 0.f;
     vv[rb] = 0.f;
-    lim[rb] = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1;
+    int mnl = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) mnl = min(mnl, __shfl_xor(mnl, o, 64));
+    minlim[rb] = __builtin_amdgcn_readfirstlane(mnl);
   }
   int maxlim = -1;
   for (int r = 0; r < a.Rpad; ++r) maxlim = max(maxlim, lim_s[r]);
@@ -230,12 +236,34 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[(rb * KS + ks) * 64 + lane]);
       // lane owns query row rb*32 + lane%32; register v holds key kb + acc_row(v)
+      if (!VAL && kb + 31 < w.k1 && kb + 31 <= minlim[rb]) {
+        // every key of the block is visible to every row of the block: no
+        // masks; the maximum of the raw products scales to the logits' (the
+        // scale is positive), and 2^x x is summed as 2^x times the raw product
+        float mx = acc[0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+        const float mn = fmaxf(m[rb], mx * a.scale2);
+        const float f = fast_exp2(m[rb] - mn);
+        float s2 = 0.f, t2 = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float e = fast_exp2(fmaf(acc[v], a.scale2, -mn));
+          s2 += e;
+          t2 = fmaf(e, acc[v], t2);
+        }
+        sm[rb] = fmaf(sm[rb], f, s2);
+        tt[rb] = fmaf(tt[rb], f, t2 * a.scale2);
+        m[rb] = mn;
+        continue;
+      }
       float x[16];
       float mx = -INFINITY;
+      const int lim = lim_s[rb * 32 + (lane & 31)];  // this lane's row's last key
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         int64_t kk = kb + acc_row(v, lane);
-        bool ok = kk < w.k1 && kk <= lim[rb];
+        bool ok = kk < w.k1 && kk <= lim;
         x[v] = ok ? acc[v] * a.scale2 : -INFINITY;
         mx = fmaxf(mx, x[v]);
       }
@@ -256,6 +284,7 @@ __global__ __launch_bounds__(THREADS) void rowstats_kernel(AttnArgs a, int mode,
       m[rb] = mn;
     }
   }
+  __syncthreads();  // every wave is done with the staged rows: the merge area overwrites them
   // merge the lane pair (l, l+32) that shares a row, then the waves
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
@@ -420,35 +449,52 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
   const int64_t ubase = ((int64_t)w.l * a.H + w.h) * a.T + w.tok0;
   const T* K = (const T*)a.K + ubase * D;
   float hs_num = 0.f, hs_den = 0.f;
-  // key blocks are double-buffered: the next block's keys (and, for the
-  // features, this block's values) load while this block is computed; past
-  // the end a lane reads the last key (masked by kvalid)
-  Frag<T> kf[KS];
-  {
-    const int64_t key = min(w.k0 + wave * 32 + (lane & 31), w.k1 - 1);
+  int minlim[8];  // the smallest last key over each row block (every row of a probe pass sees every key)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(K + key * D + ks * 16 + 8 * (lane >> 5));
+  for (int rb = 0; rb < 8; ++rb) {
+    int mnl = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) mnl = min(mnl, __shfl_xor(mnl, o, 64));
+    minlim[rb] = __builtin_amdgcn_readfirstlane(mnl);
   }
+  // a lane owns one key; past the end it reads the last key (masked by kvalid)
   for (int64_t kb = w.k0 + wave * 32; kb < w.k1; kb += WAVES * 32) {
     int64_t key = kb + (lane & 31);
     bool kvalid = key < w.k1;
     const int64_t keyc = kvalid ? key : w.k1 - 1;
-    Frag<T> kn[KS];
-    {
-      const int64_t kk = min(kb + WAVES * 32 + (lane & 31), w.k1 - 1);
+    Frag<T> kf[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kn[ks] = load_frag<T>(K + kk * D + ks * 16 + 8 * (lane >> 5));
-    }
-    Frag<T> vrow[MODE == 0 ? D / 16 : 1];
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = load_frag<T>(K + keyc * D + ks * 16 + 8 * (lane >> 5));
+    float vn = 0.f;
     if constexpr (MODE == 0) {
+      // value norm: lanes l and l+32 each sum half of the row
       const T* Vr = (const T*)a.V + (ubase + keyc) * D + (lane >> 5) * (D / 2);
+      float vs = 0.f;
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) vrow[j] = load_frag<T>(Vr + j * 8);
+      for (int j = 0; j < D / 16; ++j) {
+        const Frag<T> vrow = load_frag<T>(Vr + j * 8);
+        if constexpr (sizeof(T) == 2) {
+          // squares of bf16 pairs summed in fp32 (v_dot2c_f32_bf16)
+          const uint4 u = __builtin_bit_cast(uint4, vrow.v);
+          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w4[e]);
+            vs = __builtin_amdgcn_fdot2_f32_bf16(x, x, vs, false);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) vs += vrow.v[e] * vrow.v[e];
+        }
+      }
+      if (!kvalid) vs = 0.f;
+      vs += __shfl_xor(vs, 32, 64);
+      vn = sqrtf(vs);
     }
     float colsum = 0.f, hsum = 0.f;
-    float mg[8];
+    float mg[8], csr[8];  // per query head; per row block (fast path, assigned to heads below)
 #pragma unroll
-    for (int g = 0; g < 8; ++g) mg[g] = 0.f;
+    for (int g = 0; g < 8; ++g) mg[g] = csr[g] = 0.f;
     if (kb <= maxlim) {
 #pragma unroll
       for (int rb = 0; rb < 8; ++rb) {
@@ -458,6 +504,34 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
         for (int ks = 0; ks < KS; ++ks) mma(acc, qf[(rb * KS + ks) * 64 + lane], kf[ks]);
         // lane owns key `key`; register v holds query row rb*32 + acc_row(v),
         // and registers 4q..4q+3 hold four consecutive rows
+        if (kb + 31 < w.k1 && (MODE == 0 || kb + 31 <= minlim[rb]) && (MODE == 1 || a.P % 32 == 0)) {
+          // every key of the block is in range for every row of the block: no
+          // masks (a probe block lies inside one query head)
+          float cs = 0.f, hs = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row0 = rb * 32 + acc_row(q * 4, lane);
+            const float4 ls4 = *(const float4*)(lse_s + row0);
+            const float4 o4 = *(const float4*)((MODE == 0 ? ent_s : w_s) + row0);
+            const float lsv[4] = {ls4.x, ls4.y, ls4.z, ls4.w}, ov[4] = {o4.x, o4.y, o4.z, o4.w};
+#pragma unroll
+            for (int vv = 0; vv < 4; ++vv) {
+              const float p = fast_exp2(fmaf(acc[q * 4 + vv], a.scale2, -lsv[vv]));
+              if constexpr (MODE == 0) {
+                cs += p;
+                hs = fmaf(p, ov[vv], hs);
+              } else {
+                cs = fmaf(ov[vv], p, cs);
+              }
+            }
+          }
+          colsum += cs;
+          if constexpr (MODE == 0) {
+            hsum += hs;
+            csr[rb] += cs;
+          }
+          continue;
+        }
         float rbs = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -492,8 +566,8 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
           }
           if (mode == 0) {
             // an 8-row group lies inside one query head (P is a multiple of 8);
-            // with P >= 32 the whole 32-row block does
-            if (a.P >= 32) {
+            // with P a multiple of 32 the whole 32-row block does
+            if (a.P % 32 == 0) {
               rbs += part_g;
             } else {
               int g = (rb * 32 + q * 8) / a.P;
@@ -503,7 +577,7 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
             }
           }
         }
-        if (mode == 0 && a.P >= 32) {
+        if (mode == 0 && a.P % 32 == 0) {
           const int g = rb * 32 / a.P;
 #pragma unroll
           for (int gg = 0; gg < 8; ++gg)
@@ -511,31 +585,27 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
         }
       }
     }
+    if (mode == 0 && a.P % 32 == 0) {
+      // row block rb belongs to query head rb * 32 / P
+      const int bph = a.P >> 5;
+      if (bph == 1) {
+#pragma unroll
+        for (int g = 0; g < 8; ++g) mg[g] += csr[g];
+      } else if (bph == 2) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) mg[g] += csr[2 * g] + csr[2 * g + 1];
+      } else if (bph == 4) {
+        mg[0] += (csr[0] + csr[1]) + (csr[2] + csr[3]);
+        mg[1] += (csr[4] + csr[5]) + (csr[6] + csr[7]);
+      } else {
+        mg[0] += ((csr[0] + csr[1]) + (csr[2] + csr[3])) + ((csr[4] + csr[5]) + (csr[6] + csr[7]));
+      }
+    }
     colsum += __shfl_xor(colsum, 32, 64);
     if (mode == 0) {
       hsum += __shfl_xor(hsum, 32, 64);
 #pragma unroll
       for (int g = 0; g < 8; ++g) mg[g] += __shfl_xor(mg[g], 32, 64);
-      // value norm: lanes l and l+32 each sum half of the row
-      float vs = 0.f;
-#pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
-        if constexpr (sizeof(T) == 2) {
-          const uint4 u = __builtin_bit_cast(uint4, vrow[j].v);
-          const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x0 = __uint_as_float(w4[e] << 16), x1 = __uint_as_float(w4[e] & 0xffff0000u);
-            vs += x0 * x0 + x1 * x1;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vs += vrow[j].v[e] * vrow[j].v[e];
-        }
-      }
-      if (!kvalid) vs = 0.f;
-      vs += __shfl_xor(vs, 32, 64);
-      float vn = sqrtf(vs);
       if (lane < 32 && kvalid) {
         float mean = colsum / (float)a.G;
         float var = 0.f;
@@ -561,8 +631,6 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
       out0[tix] = a.accumulate ? out0[tix] + colsum : colsum;  // delta_t
       rel_out[tix] = rel_in[tix] + colsum;                      // running relevance
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = kn[ks];
   }
   if (mode == 0) {
     hs_num = wave_sum(hs_num);
@@ -733,7 +801,7 @@ __global__ void copy_f32_kernel(const float* src, float* dst, int64_t n) {
 // seed passes on the full-depth workload).
 int pick_kw(const kvc_shape* sh) {
   int64_t units = (int64_t)sh->n_layers * sh->n_kv_heads;
-  for (int kw : {1024, 512, 256}) {
+  for (int kw : {4096, 2048, 1024, 512, 256}) {
     int64_t n = 0;
     for (int s = 0; s < sh->n_seq; ++s) n += units * ((sh->cu_seqlens[s + 1] - sh->cu_seqlens[s] + kw - 1) / kw);
     if (n >= 2048) return kw;
@@ -766,7 +834,8 @@ size_t smem_rows(const AttnArgs& a, int d, int elt) { return (size_t)a.Rpad * d 
 
 template <class T, int D>
 int launch_pass1(const AttnArgs& a, int mode, int64_t nsplit, float* part, hipStream_t st) {
-  size_t sm = smem_rows(a, D, sizeof(T)) + a.Rpad * sizeof(int) + (size_t)WAVES * a.Rpad * 3 * sizeof(float);
+  // the staged rows and their limits, then (over them) the per-wave merge area
+  size_t sm = std::max(smem_rows(a, D, sizeof(T)) + a.Rpad * sizeof(int), (size_t)WAVES * a.Rpad * 3 * sizeof(float));
   (void)hipFuncSetAttribute((const void*)rowstats_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   hipLaunchKernelGGL((rowstats_kernel<T, D>), dim3((unsigned)nsplit), dim3(THREADS), sm, st, a, mode, part);
   KVC_LAUNCH_CHECK("rowstats");
@@ -951,7 +1020,7 @@ extern "C" int kvc_propagate(const kvc_shape* sh, const kvc_params* p, const voi
 namespace {
 template <class T, int D>
 int launch_rowval(const AttnArgs& a, int64_t nsplit, float* part, hipStream_t st) {
-  const size_t sm = smem_rows(a, D, sizeof(T)) + a.Rpad * sizeof(int) + (size_t)WAVES * a.Rpad * 4 * sizeof(float);
+  const size_t sm = std::max(smem_rows(a, D, sizeof(T)) + a.Rpad * sizeof(int), (size_t)WAVES * a.Rpad * 4 * sizeof(float));
   (void)hipFuncSetAttribute((const void*)rowstats_kernel<T, D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)sm);
   hipLaunchKernelGGL((rowstats_kernel<T, D, true>), dim3((unsigned)nsplit), dim3(THREADS), sm, st, a, 1, part);

@@ -46,6 +46,22 @@ def test_score_matches_oracle(name):
         assert np.allclose(tot, cfg.G * cfg.P, rtol=1e-4)
 
 
+@pytest.mark.parametrize("name,P", [("stress", 40), ("ragged", 48), ("mistral1", 32), ("stress", 24)])
+def test_score_head_masses_with_other_probe_counts(name, P):
+    """Probe counts that are not multiples of 32 put rows of two query heads in
+    one 32-row block: the per-head masses behind the variance feature must
+    still follow the heads (DistillCache paper, Sec. 3.1.1)."""
+    kvc, cfg, inp, dinp, pb = _setup(name, P=P)
+    print(f"[score] {name} P={P} G={cfg.G}", flush=True)
+    g = kvc.score(pb, dinp["K"], dinp["V"], dinp["Qp"])
+    torch.cuda.synchronize()
+    o = oracle.probe_scores(inp["K"], inp["V"], inp["Qp"], inp["cu_seqlens"].numpy(), cfg)
+    close(g["r0"], o["r0"], 1e-3, "r0")
+    close(g["lse"], o["lse"], 1e-3, "lse")
+    close(g["feats"][2], o["feats"][2], 1e-2, "sigma", floor=1e-4)
+    close(g["feats"][3], o["feats"][3], 1e-3, "entropy")
+
+
 @pytest.mark.parametrize("name", CASES)
 def test_propagate_matches_oracle(name):
     kvc, cfg, inp, dinp, pb = _setup(name)
