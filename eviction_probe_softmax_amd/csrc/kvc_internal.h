@@ -167,6 +167,26 @@ template <int W>
 __device__ __forceinline__ float group_sum(float v) { return group_reduce<W, OpAdd>(v); }
 template <int W>
 __device__ __forceinline__ float group_max(float v) { return group_reduce<W, OpMax>(v); }
+// Four sums over the wave at once (the whole wave active). v_permlane32_swap
+// on (a, b) leaves the pair sums of a in lanes 0-31 and of b in lanes 32-63,
+// likewise for (c, d); v_permlane16_swap on the two results leaves, per
+// 16-lane row, a (row 0), c (row 1), b (row 2), d (row 3); DPP finishes each
+// row. Returns (sum a, sum b, sum c, sum d), uniform over the wave.
+__device__ __forceinline__ float4 wave_sum4(float a, float b, float c, float d) {
+  const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(d), false, false);
+  const float x = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
+  const float y = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
+  const auto xy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  float v = __uint_as_float(xy[0]) + __uint_as_float(xy[1]);
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const int iv = __float_as_int(v);
+  return make_float4(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(iv, 16)), __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
+}
 // sum over the lanes i, i ^ 16, i ^ 32, i ^ 48 (the four rows), in each of them
 __device__ __forceinline__ float cross_row_sum(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

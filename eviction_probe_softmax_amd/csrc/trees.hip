@@ -111,7 +111,12 @@ struct TreeLayout {
   // of the children and grandchildren of the root, the big nodes' G w vectors
   // and w^T G w, and the root's a^T G w partials
   static constexpr int MP_ITEMS = 20;
-  static constexpr size_t mp_part = 0;
+  // with room in r1 the Gram matrix of midpoint trees goes there too, so the
+  // prototype logits (over kh) survive until the value error is formed and
+  // both errors of a node are finished together
+  static constexpr size_t MP_BYTES = 3 * 6 * PDMAX * 4 + 3 * NMAX * 4 + 16 + 4 * PDMAX * 4 + MP_ITEMS * PDMAX * 4 + 5 * 16;
+  static constexpr bool LGKEEP = STAGED && al(GM) + MP_BYTES <= R1B;
+  static constexpr size_t mp_part = LGKEEP ? al(GM) : 0;
   static constexpr size_t mp_q = al(mp_part + (size_t)MP_ITEMS * PDMAX * 4);
   static constexpr size_t mp_gv = al(mp_q + (size_t)3 * 6 * PDMAX * 4);
   static constexpr size_t mp_w = al(mp_gv + (size_t)3 * NMAX * 4);
@@ -701,8 +706,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         for (int v = 0; v < 16; ++v) LGa[(tnb * 32 + acc_row(v, lane)) * LGS + rho_t] = acc[v];
       }
       __syncthreads();
+      // the attention-partition error: here for explicit trees (and when the
+      // logits cannot be kept), else with the value error in C
 #pragma unroll
       for (int u = 0; u < NPW2; ++u) {
+        if (Lo::LGKEEP && !a.topo) break;
         const int qq = wave + u * WAVES;
         if (qq >= nint) continue;
         const int j = ilist[qq];
@@ -862,16 +870,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           }
         }
         __syncthreads();
-        for (int tile = wave; tile < nt * (nt + 1) / 2; tile += WAVES) {
-          int ti = 0, rem = tile;
-          while (rem >= nt - ti) {
-            rem -= nt - ti;
-            ++ti;
-          }
-          const int tj = ti + rem;
+        // at most three tiles (slots of at most 64 tokens): one per wave, written
+        // once every wave has read the staged values (midpoint trees keep the
+        // Gram matrix over them)
+        static_assert(Lo::N32 <= 64 && WAVES >= 3, "one Gram tile per wave");
+        const int ti = wave >= nt ? 1 : 0, tj = wave >= nt ? 1 : wave;
+        kvc_f32x16 acc = {};
+        if (wave < nt * (nt + 1) / 2) {
           const int oa = (ti * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
           const int ob = (tj * 32 + (lane & 31)) * Lo::VS + 8 * (lane >> 5);
-          kvc_f32x16 acc = {};
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -886,11 +893,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) mma(acc, load_frag<float>(Vc + oa + ks * 16), load_frag<float>(Vc + ob + ks * 16));
           }
+        }
+        if (Lo::LGKEEP && !a.topo) __syncthreads();
+        if (wave < nt * (nt + 1) / 2) {
+          float* Gd = (Lo::LGKEEP && !a.topo) ? (float*)(smem + Lo::r1) : Gm;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int r = ti * 32 + acc_row(v, lane), cc = tj * 32 + (lane & 31);
-            Gm[r * NG + cc] = acc[v];
-            if (ti != tj) Gm[cc * NG + r] = acc[v];
+            Gd[r * NG + cc] = acc[v];
+            if (ti != tj) Gd[cc * NG + r] = acc[v];
           }
         }
       } else
@@ -959,6 +970,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         // pairs spread over every wave in aligned 4-row groups; with w the
         // node's value weights, c^T G c = a^T G a - 2 Z a^T G w + Z^2 w^T G w.
         __syncthreads();  // the Gram matrix is complete; the staged values are free
+        const float* G2 = Lo::LGKEEP ? (const float*)(smem + Lo::r1) : Gm;
+        const float* LGa = (const float*)(smem + Lo::kh);  // [64][LGS] prototype logits (when kept)
         constexpr int SMALLN = 16;
         float* mpart = (float*)(smem + Lo::r1 + Lo::mp_part);  // [MP_ITEMS][PDMAX]
         float* mq = (float*)(smem + Lo::r1 + Lo::mp_q);         // [3: a^T G a, Z, a.s][6 slots][PDMAX]
@@ -991,20 +1004,36 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           al = rl > 0.f ? hw_div(1.f - a.beta, rl) : 0.f;
           ga = hw_div(rl > 0.f ? a.beta : 1.f, (float)sz);
         };
-        auto finish = [&](int j, float num, float den) {
-          const float eVn = group_sum<64>(lane < pd ? hw_sqrt(fmaxf(num, 0.f)) : 0.f);
-          const float eVd = group_sum<64>(lane < pd ? hw_sqrt(fmaxf(den, 0.f)) : 0.f);
+        // D = min(1, wA eA + wV eV); with the logits kept, eA is formed here from
+        // the node's Z (the four sums over the distortion rows in one reduction)
+        auto finish = [&](int j, float Z, float num, float den) {
+          const float sn = lane < pd ? hw_sqrt(fmaxf(num, 0.f)) : 0.f, sd = lane < pd ? hw_sqrt(fmaxf(den, 0.f)) : 0.f;
+          float eA;
+          float4 r;
+          if constexpr (Lo::LGKEEP) {
+            float an = 0.f, ad = 0.f;
+            if (lane < pd) {
+              const float zh = nmu[j] * fast_exp2((LGa[(j - nst[j]) * LGS + lane] * a.c - lse_s[lane]) * 1.4426950408889634f);
+              an = fabsf(zh - Z);
+              ad = Z;
+            }
+            r = wave_sum4(sn, sd, an, ad);
+            eA = r.w > 0.f ? hw_div(r.z, r.w) : 0.f;
+          } else {
+            r = wave_sum4(sn, sd, 0.f, 0.f);
+            eA = nD[j];
+          }
           if (lane == 0) {
-            const float eV = eVd > 0.f ? hw_div(eVn, eVd) : 0.f;
-            nD[j] = fminf(1.f, a.wA * nD[j] + a.wV * eV);
+            const float eV = r.y > 0.f ? hw_div(r.x, r.y) : 0.f;
+            nD[j] = fminf(1.f, a.wA * eA + a.wV * eV);
           }
         };
         // cross items, dealt to the waves in order
         for (int k = wave; k < K0 + K1 + K2; k += WAVES) {
           float x;
-          if (k < K0) x = cross_block(Gm, NG, At, lane, k, 0, nl, nl, n);
-          else if (k < K0 + K1) x = cross_block(Gm, NG, At, lane, k - K0, 0, nll, nll, nl);
-          else x = cross_block(Gm, NG, At, lane, g2 + (k - K0 - K1), nl, nl + nrl, nl + nrl, n);
+          if (k < K0) x = cross_block(G2, NG, At, lane, k, 0, nl, nl, n);
+          else if (k < K0 + K1) x = cross_block(G2, NG, At, lane, k - K0, 0, nll, nll, nl);
+          else x = cross_block(G2, NG, At, lane, g2 + (k - K0 - K1), nl, nl + nrl, nl + nrl, n);
           mpart[k * PDMAX + lane] = x;
         }
         // G w of the big nodes (lane = token), and w^T G w
@@ -1014,7 +1043,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           float gv = 0.f;
           if (lane < n) {
 #pragma unroll 4
-            for (int j = 0; j < n; ++j) gv = fmaf(Gm[j * NG + lane], fmaf(al, rtok[j], ga), gv);
+            for (int j = 0; j < n; ++j) gv = fmaf(G2[j * NG + lane], fmaf(al, rtok[j], ga), gv);
             mgv[lane] = gv;
           }
           const float ww = group_sum<64>(lane < n ? fmaf(al, rtok[lane], ga) * gv : 0.f);
@@ -1029,7 +1058,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           const int vst = inL ? 0 : nl, vn = inL ? nl : nr;
           float gv = 0.f;
           if (lane < n) {
-            for (int j = 0; j < vn; ++j) gv = fmaf(Gm[(vst + j) * NG + lane], fmaf(al, rtok[vst + j], ga), gv);
+            for (int j = 0; j < vn; ++j) gv = fmaf(G2[(vst + j) * NG + lane], fmaf(al, rtok[vst + j], ga), gv);
             mgv[(inL ? 1 : 2) * NMAX + lane] = gv;
           }
           const float wg = lane < n ? fmaf(al, rtok[lane], ga) * gv : 0.f;
@@ -1047,17 +1076,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           float al, ga;
           weights(j, sz, al, ga);
           float Z, as, num, qa;
-          if (sz <= 2) small_forms<2>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
-          else if (sz <= 4) small_forms<4>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
-          else if (sz <= 8) small_forms<8>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
-          else small_forms<16>(Gm, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          if (sz <= 2) small_forms<2>(G2, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          else if (sz <= 4) small_forms<4>(G2, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          else if (sz <= 8) small_forms<8>(G2, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
+          else small_forms<16>(G2, NG, At, rtok, sdot, lane, st, sz, n32, al, ga, Z, as, num, qa);
           const int sl = slot_of(j);
           if (sl >= 0) {
             mq[(0 * 6 + sl) * PDMAX + lane] = qa;
             mq[(1 * 6 + sl) * PDMAX + lane] = Z;
             mq[(2 * 6 + sl) * PDMAX + lane] = as;
           }
-          finish(j, num, fmaf(2.f * Z, as, fmaf(Z * Z, mm, qa)));
+          finish(j, Z, num, fmaf(2.f * Z, as, fmaf(Z * Z, mm, qa)));
         }
         __syncthreads();
         // big children of the root, from their children; the root's a^T G w in quarters
@@ -1073,7 +1102,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
             for (int i = vst; i < vst + sz; ++i) qaw = fmaf(At[i * PA + lane], mgv[gvs * NMAX + i], qaw);
           }
           const float num = fmaf(Z * Z, mww[gvs], fmaf(-2.f * Z, qaw, qa));
-          finish(j, num, fmaf(2.f * Z, as, fmaf(Z * Z, mm, qa)));
+          finish(j, Z, num, fmaf(2.f * Z, as, fmaf(Z * Z, mm, qa)));
           return make_float3(qa, Z, as);
         };
         if (wave == 0 && bigL) {
