@@ -105,6 +105,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+// The same rounding by gfx950's v_cvt_pk_bf16_f32 (identical bits for every
+// fp32 input). Only for values computed in fp32: the compiler may merge a
+// preceding double -> float conversion into one double -> bf16 rounding.
+__device__ __forceinline__ uint16_t f32_to_bf16_hw(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <class T> struct ElemIO;
 template <> struct ElemIO<float> {

@@ -210,7 +210,7 @@ __device__ __forceinline__ void store8(T* p, const float* x) {
   if constexpr (sizeof(T) == 2) {
     uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f32_to_bf16_bits(x[2 * q]) | ((uint32_t)f32_to_bf16_bits(x[2 * q + 1]) << 16);
+    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f32_to_bf16_hw(x[2 * q]) | ((uint32_t)f32_to_bf16_hw(x[2 * q + 1]) << 16);
     *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);

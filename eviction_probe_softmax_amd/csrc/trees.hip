@@ -137,10 +137,10 @@ __device__ __forceinline__ float hw_div(float x, float y) { return x * __builtin
 __device__ __forceinline__ void split8(float* x, kvc_bf16x8& hi, kvc_bf16x8& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint16_t b = f32_to_bf16_bits(x[j]);
+    uint16_t b = f32_to_bf16_hw(x[j]);
     x[j] -= bf16_bits_to_f32(b);
     hi[j] = __builtin_bit_cast(__bf16, b);
-    uint16_t c = f32_to_bf16_bits(x[j]);
+    uint16_t c = f32_to_bf16_hw(x[j]);
     x[j] -= bf16_bits_to_f32(c);
     lo[j] = __builtin_bit_cast(__bf16, c);
   }
@@ -675,11 +675,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         if (qq >= nint || lane >= HD) continue;
         if constexpr (sizeof(T) == 2) {
           // k^ = hi + lo with |k^ - hi - lo| <= 2^-18 |k^|; the queries are exact in bf16
-          const uint16_t h0 = f32_to_bf16_bits(kp0[u]), h1 = f32_to_bf16_bits(kp1[u]);
+          const uint16_t h0 = f32_to_bf16_hw(kp0[u]), h1 = f32_to_bf16_hw(kp1[u]);
           PKh[qq * KHS + lane] = h0;
           PKh[qq * KHS + lane + HD] = h1;
-          PKl[qq * KHS + lane] = f32_to_bf16_bits(kp0[u] - bf16_bits_to_f32(h0));
-          PKl[qq * KHS + lane + HD] = f32_to_bf16_bits(kp1[u] - bf16_bits_to_f32(h1));
+          PKl[qq * KHS + lane] = f32_to_bf16_hw(kp0[u] - bf16_bits_to_f32(h0));
+          PKl[qq * KHS + lane + HD] = f32_to_bf16_hw(kp1[u] - bf16_bits_to_f32(h1));
         } else {
           PK[qq * KHS + lane] = kp0[u];
           PK[qq * KHS + lane + HD] = kp1[u];
@@ -772,11 +772,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
           const float k0 = m0 * pc[u] - m1 * ps[u], k1 = m1 * pc[u] + m0 * ps[u];
           if constexpr (sizeof(T) == 2) {
             // k^ = hi + lo with |k^ - hi - lo| <= 2^-18 |k^|; the queries are exact in bf16
-            const uint16_t h0 = f32_to_bf16_bits(k0), h1 = f32_to_bf16_bits(k1);
+            const uint16_t h0 = f32_to_bf16_hw(k0), h1 = f32_to_bf16_hw(k1);
             KHh[qq * KHS + lane] = h0;
             KHh[qq * KHS + lane + HD] = h1;
-            KHl[qq * KHS + lane] = f32_to_bf16_bits(k0 - bf16_bits_to_f32(h0));
-            KHl[qq * KHS + lane + HD] = f32_to_bf16_bits(k1 - bf16_bits_to_f32(h1));
+            KHl[qq * KHS + lane] = f32_to_bf16_hw(k0 - bf16_bits_to_f32(h0));
+            KHl[qq * KHS + lane + HD] = f32_to_bf16_hw(k1 - bf16_bits_to_f32(h1));
           } else {
             KH[qq * KHS + lane] = k0;
             KH[qq * KHS + lane + HD] = k1;
@@ -856,8 +856,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
             uint16_t hb[8], lb[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              hb[q] = f32_to_bf16_bits(x[q]);
-              lb[q] = f32_to_bf16_bits(x[q] - bf16_bits_to_f32(hb[q]));
+              hb[q] = f32_to_bf16_hw(x[q]);
+              lb[q] = f32_to_bf16_hw(x[q] - bf16_bits_to_f32(hb[q]));
             }
             *(uint4*)(Vh + i * Lo::VS + vc) = make_uint4(hb[0] | (uint32_t)hb[1] << 16, hb[2] | (uint32_t)hb[3] << 16,
                                                           hb[4] | (uint32_t)hb[5] << 16, hb[6] | (uint32_t)hb[7] << 16);
