@@ -191,6 +191,11 @@ __device__ __forceinline__ float4 wave_sum4(float a, float b, float c, float d) 
   return make_float4(__int_as_float(__builtin_amdgcn_readlane(iv, 0)), __int_as_float(__builtin_amdgcn_readlane(iv, 32)),
                      __int_as_float(__builtin_amdgcn_readlane(iv, 16)), __int_as_float(__builtin_amdgcn_readlane(iv, 48)));
 }
+// sum over the lanes i and i ^ 32, in both
+__device__ __forceinline__ float group_sum_x32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // sum over the lanes i, i ^ 16, i ^ 32, i ^ 48 (the four rows), in each of them
 __device__ __forceinline__ float cross_row_sum(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -499,11 +499,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       }
       q = group_sum<CH>(q);
       if (ok) {
-        float* d0 = Kt + (size_t)i * D + c;
-        *(float4*)d0 = make_float4(y0[0], y0[1], y0[2], y0[3]);
-        *(float4*)(d0 + 4) = make_float4(y0[4], y0[5], y0[6], y0[7]);
-        *(float4*)(d0 + HD) = make_float4(y1[0], y1[1], y1[2], y1[3]);
-        *(float4*)(d0 + HD + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
+        if constexpr (STAGED) {
+          // the two halves of each rotation pair side by side: (d, d + HD) at 2d, 2d + 1
+          float* d0 = Kt + (size_t)i * D + 2 * c;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) *(float4*)(d0 + 2 * e) = make_float4(y0[e], y1[e], y0[e + 1], y1[e + 1]);
+        } else {
+          float* d0 = Kt + (size_t)i * D + c;
+          *(float4*)d0 = make_float4(y0[0], y0[1], y0[2], y0[3]);
+          *(float4*)(d0 + 4) = make_float4(y0[4], y0[5], y0[6], y0[7]);
+          *(float4*)(d0 + HD) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+          *(float4*)(d0 + HD + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
+        }
         if (c == 0) knorm[i] = hw_sqrt(q);
       }
     }
@@ -625,16 +632,26 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       const int ntile = nrb * nbk;
       const int trb = wave % max(nrb, 1), tnb = wave / max(nrb, 1);
       const int rho_t = trb * 32 + (lane & 31);
+      // Summed keys: a wave instruction reads NR rows of the interleaved keys,
+      // 16 bytes a lane (lane = (row of the instruction, 4-float column)); the
+      // rows of the other lane groups are added by lane swaps, after which a
+      // lane of the first two groups keeps one rotation pair (d, d + HD)
+      constexpr int R4 = D / 4, NR = 64 / R4;
+      static_assert(NR == 2 || NR == 4, "rows per instruction");
+      const int rsub = lane / R4, kq = lane % R4;
+      const int dsel = 2 * kq + (rsub & 1);
+      const bool own = rsub < 2;
+      const float4* Kt4 = (const float4*)Kt;
       float pc[NPW2], ps[NPW2];
 #pragma unroll
       for (int u = 0; u < NPW2; ++u) {
         const int qq = wave + u * WAVES;
         pc[u] = ps[u] = 0.f;
-        if (qq < nint && lane < HD) {
+        if (qq < nint && own) {
           const int j = ilist[qq];
           const int64_t prep = t0 + nst[j] + (nsz[j] - 1) / 2;
-          pc[u] = a.rc[prep * HD + lane];
-          ps[u] = a.rs[prep * HD + lane];
+          pc[u] = a.rc[prep * HD + dsel];
+          ps[u] = a.rs[prep * HD + dsel];
         }
       }
       float kp0[NPW2], kp1[NPW2];
@@ -645,22 +662,36 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         if (qq >= nint) continue;
         const int j = ilist[qq];
         const int st = nst[j], sz = nsz[j];
-        float s0 = 0.f, s1 = 0.f, kn = 0.f;
-        if (lane < HD) {
+        float4 ac = make_float4(0.f, 0.f, 0.f, 0.f);
+        float kn = 0.f;
 #pragma unroll 4
-          for (int i = st; i < st + sz; ++i) {
-            s0 += Kt[(size_t)i * D + lane];
-            s1 += Kt[(size_t)i * D + lane + HD];
-            kn += knorm[i];
-          }
+        for (int i = st + rsub; i < st + sz; i += NR) {
+          const float4 x = Kt4[(size_t)i * R4 + kq];
+          ac.x += x.x;
+          ac.y += x.y;
+          ac.z += x.z;
+          ac.w += x.w;
+          kn += knorm[i];
         }
-        const float nrm2 = group_sum<64>(lane < HD ? s0 * s0 + s1 * s1 : 0.f);
-        kn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(kn), 0));
+        if constexpr (NR == 2) {
+          ac.x = group_sum_x32(ac.x);
+          ac.y = group_sum_x32(ac.y);
+          ac.z = group_sum_x32(ac.z);
+          ac.w = group_sum_x32(ac.w);
+          kn = group_sum_x32(kn);
+        } else {
+          ac.x = cross_row_sum(ac.x);
+          ac.y = cross_row_sum(ac.y);
+          ac.z = cross_row_sum(ac.z);
+          ac.w = cross_row_sum(ac.w);
+          kn = cross_row_sum(kn);
+        }
+        const float nrm2 = group_sum<R4>(ac.x * ac.x + ac.y * ac.y + ac.z * ac.z + ac.w * ac.w);
         const float coh = kn > 0.f ? hw_div(hw_sqrt(nrm2), kn) : 1.f;
         const float mu = fmaxf(1.f, (float)sz * coh);
         if (lane == 0) nmu[j] = mu;
         const float rsz = __builtin_amdgcn_rcpf((float)sz);
-        const float m0 = s0 * rsz, m1 = s1 * rsz;
+        const float m0 = ((rsub & 1) ? ac.z : ac.x) * rsz, m1 = ((rsub & 1) ? ac.w : ac.y) * rsz;
         kp0[u] = m0 * pc[u] - m1 * ps[u];
         kp1[u] = m1 * pc[u] + m0 * ps[u];
       }
@@ -672,17 +703,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
 #pragma unroll
       for (int u = 0; u < NPW2; ++u) {
         const int qq = wave + u * WAVES;
-        if (qq >= nint || lane >= HD) continue;
+        if (qq >= nint || !own) continue;
         if constexpr (sizeof(T) == 2) {
           // k^ = hi + lo with |k^ - hi - lo| <= 2^-18 |k^|; the queries are exact in bf16
           const uint16_t h0 = f32_to_bf16_hw(kp0[u]), h1 = f32_to_bf16_hw(kp1[u]);
-          PKh[qq * KHS + lane] = h0;
-          PKh[qq * KHS + lane + HD] = h1;
-          PKl[qq * KHS + lane] = f32_to_bf16_hw(kp0[u] - bf16_bits_to_f32(h0));
-          PKl[qq * KHS + lane + HD] = f32_to_bf16_hw(kp1[u] - bf16_bits_to_f32(h1));
+          PKh[qq * KHS + dsel] = h0;
+          PKh[qq * KHS + dsel + HD] = h1;
+          PKl[qq * KHS + dsel] = f32_to_bf16_hw(kp0[u] - bf16_bits_to_f32(h0));
+          PKl[qq * KHS + dsel + HD] = f32_to_bf16_hw(kp1[u] - bf16_bits_to_f32(h1));
         } else {
-          PK[qq * KHS + lane] = kp0[u];
-          PK[qq * KHS + lane + HD] = kp1[u];
+          PK[qq * KHS + dsel] = kp0[u];
+          PK[qq * KHS + dsel + HD] = kp1[u];
         }
       }
       __syncthreads();
