@@ -464,6 +464,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
     }
     for (int rho = tid; rho < PDMAX; rho += THREADS) lse_s[rho] = rho < pd ? lse_g[(int64_t)rho * a.pstride] : 0.f;
     for (int i = tid; i < n; i += THREADS) rtok[i] = a.rel[lh * a.T + tok0 + i];
+    // the value rows for the statistics below, loaded first so that they arrive
+    // while the keys are rotated: thread (group g, chunk vc) keeps tokens g, g+VG, ...
+    const int vc = (tid % VC) * 8, vg = tid / VC;
+    Raw8<T> vr[VR];
+#pragma unroll
+    for (int r = 0; r < VR; ++r) {
+      const int i = vg + r * VG;
+      if (i < n) vr[r].load(Vg + (int64_t)i * D + vc);
+      else vr[r].zero();
+    }
     // inverse-rotated keys and key norms: one 8-pair chunk per item, all loads issued together
 #pragma unroll
     for (int r = 0; r < (NMAX * CH + THREADS - 1) / THREADS; ++r) {
@@ -514,15 +524,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
         if (c == 0) knorm[i] = hw_sqrt(q);
       }
     }
-    // value statistics: thread (group g, chunk vc) keeps tokens g, g+VG, ... in registers
-    const int vc = (tid % VC) * 8, vg = tid / VC;
-    Raw8<T> vr[VR];
-#pragma unroll
-    for (int r = 0; r < VR; ++r) {
-      const int i = vg + r * VG;
-      if (i < n) vr[r].load(Vg + (int64_t)i * D + vc);
-      else vr[r].zero();
-    }
+    // value statistics (the value rows were loaded before the keys)
     {
       float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
