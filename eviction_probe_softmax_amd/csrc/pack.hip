@@ -46,6 +46,7 @@ struct PackArgs {
   int64_t T;
   int64_t pe[64], c1[64];   // per sequence: prompt end (= compressible start), compressible end
   int64_t xoff[65];         // prefix over sequences of the exact tokens (prompt + recent + suffix)
+  int32_t sbound[65];       // prefix over sequences of a bound on their slot counts (the slot writer's grid)
   float beta;               // uniform share of prototype values
   void* oK;
   void* oV;
@@ -238,13 +239,15 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
   __shared__ int ioff[WS_THREADS + 1];
   __shared__ int wcnt[WS_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // block -> (unit lh, sequence s, slot k): grid is (Ly*H*S*stride); blocks
-  // past a sequence's slots return at once
-  int64_t b = blockIdx.x;
-  int k = (int)(b % a.stride);
-  int64_t rest = b / a.stride;
-  int s = (int)(rest % a.S);
-  int64_t lh = rest / a.S;
+  // block -> (unit lh, sequence s, slot k): the grid holds, per unit, a bound
+  // on each sequence's slot count (its length over the shortest slot, plus
+  // one); blocks past a sequence's slots return at once
+  const int64_t b = blockIdx.x, nb = a.sbound[a.S];
+  const int64_t lh = b / nb;
+  const int r = (int)(b - lh * nb);
+  int s = 0;
+  while (r >= a.sbound[s + 1]) ++s;
+  const int k = r - a.sbound[s];
   if (k >= a.n_slots[s]) return;
   const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
   const int t0 = ss[k], n = ss[k + 1] - ss[k];
@@ -497,6 +500,14 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
     a.c1[s] = g.c1;
     a.xoff[s + 1] = a.xoff[s] + g.pe + (L - g.c1);
   }
+  {
+    const int64_t smin = std::max<int64_t>(1, p->slot_len > 0 ? p->slot_len : p->slot_min);
+    a.sbound[0] = 0;
+    for (int s = 0; s < sh->n_seq; ++s) {
+      const int64_t L = sh->cu_seqlens[s + 1] - sh->cu_seqlens[s];
+      a.sbound[s + 1] = a.sbound[s] + (int32_t)std::min<int64_t>(a.stride, (L + smin - 1) / smin + 1);
+    }
+  }
   a.beta = p->value_base;
   a.oK = out->K;
   a.oV = out->V;
@@ -535,7 +546,7 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
     KVC_PACK_T(write_kept_kernel, dim3(kvc_blocks(E * ppr2, 256)));
     KVC_LAUNCH_CHECK("pack_kept");
   } else {
-    const dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * sh->n_seq * a.stride));
+    const dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * a.sbound[sh->n_seq]));
     if (sh->dtype == KVC_BF16) {
       if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(WS_THREADS), 0, st, a, off);
       else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(WS_THREADS), 0, st, a, off);
