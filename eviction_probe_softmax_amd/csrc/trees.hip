@@ -597,27 +597,31 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC)
       if (pd < PDMAX)
         for (int it = tid; it < n * (PDMAX - pd); it += THREADS) At[(it / (PDMAX - pd)) * PA + pd + it % (PDMAX - pd)] = 0.f;
     }
-    // bottom-up value flow: a parent is the fp32 sum of its children, left to right
-    for (int j = tid; j < m; j += THREADS)
-      if (nsz[j] == 1) nrel[j] = rtok[nst[j]];
-    __syncthreads();
-    if (a.topo) {  // by depth, deepest internal level first (first child j+1, then the sibling chain)
-      for (int dd = imisc[1]; dd >= 0; --dd) {
-        for (int j = tid; j < m; j += THREADS)
-          if (nsz[j] > 1 && ndep[j] == dd) {
-            float sum = nrel[j + 1];
-            for (int c = nsib[j + 1]; c != 0; c = nsib[c]) sum += nrel[c];
-            nrel[j] = sum;
-          }
-        __syncthreads();
-      }
-    } else {  // by height (children of pre-order node j: j+1 and j + 2 ceil(sz/2))
-      for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
-        for (int j = tid; j < m; j += THREADS) {
-          int sz = nsz[j];
-          if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
+    // bottom-up value flow: a parent is the fp32 sum of its children, left to
+    // right. One wave (idle in the weights' MFMA for slots of up to 64 tokens)
+    // runs every level; its LDS accesses stay in order, so the levels need no
+    // workgroup barrier; the barriers of phase B publish nrel before C reads it.
+    if (wave == WAVES - 1) {
+      for (int j = lane; j < m; j += 64)
+        if (nsz[j] == 1) nrel[j] = rtok[nst[j]];
+      if (a.topo) {  // by depth, deepest internal level first (first child j+1, then the sibling chain)
+        for (int dd = imisc[1]; dd >= 0; --dd) {
+          __builtin_amdgcn_wave_barrier();
+          for (int j = lane; j < m; j += 64)
+            if (nsz[j] > 1 && ndep[j] == dd) {
+              float sum = nrel[j + 1];
+              for (int c = nsib[j + 1]; c != 0; c = nsib[c]) sum += nrel[c];
+              nrel[j] = sum;
+            }
         }
-        __syncthreads();
+      } else {  // by height (children of pre-order node j: j+1 and j + 2 ceil(sz/2))
+        for (int ht = 1; (1 << (ht - 1)) < n; ++ht) {
+          __builtin_amdgcn_wave_barrier();
+          for (int j = lane; j < m; j += 64) {
+            int sz = nsz[j];
+            if (sz > 1 && 32 - __clz(sz - 1) == ht) nrel[j] = nrel[j + 1] + nrel[j + 2 * ((sz + 1) >> 1)];
+          }
+        }
       }
     }
 
