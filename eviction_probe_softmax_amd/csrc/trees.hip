@@ -31,8 +31,11 @@
 
 #include "kvc_internal.h"
 #include "mfma_frag.h"
+#include "trees_common.h"
 
 namespace {
+
+using namespace kvc_tree;
 
 constexpr int PDMAX = 64;   // distortion rows (one per lane)
 constexpr int PA = 64;      // token stride of the softmax weights a[i][rho]
@@ -40,30 +43,6 @@ constexpr int NB = 32;      // internal nodes per prototype-logit batch
 constexpr int LGS = PDMAX + 4;
 constexpr int SMALL = 64;   // slots up to this length use the small-slot variant
 
-struct TreeKArgs {
-  const void* K;
-  const void* V;
-  const void* Qp;
-  const float* lse;        // [S][Ly][H*G][P]
-  const float* rel;        // [Ly][H][T]
-  const float* sens;       // [S][Ly][H]
-  const float* rc;
-  const float* rs;
-  const int32_t* slot_start;
-  const int2* list;        // [S][stride] (start, length) of the slots of this size class
-  const int32_t* count;    // [S] their number
-  const int64_t* cu;
-  int S, Ly, H, G, P, stride, pd, pstride;
-  int64_t T;
-  float c;                 // 1/sqrt(d)
-  float beta, wA, wV;
-  float* node_rel;
-  float* node_D;
-  float* node_mu;
-  float* op_util;
-  uint8_t* op_cost;
-  const uint32_t* topo;    // explicit node records (split_mode 1), else NULL: midpoint trees
-};
 
 // LDS layout (byte offsets, 16-byte aligned) for slots of at most NMAX tokens.
 template <int NMAX, int D, int WAVES>
@@ -127,10 +106,6 @@ struct TreeLayout {
   static_assert((size_t)(WAVES * 64 / (D / 8)) * D * 4 <= (size_t)NMAX * PA * 4, "value-sum scratch");
 };
 
-// the hardware square root and reciprocal (about 1 ulp each) instead of the
-// correctly rounded library sequences, which cost a dozen instructions apiece
-__device__ __forceinline__ float hw_sqrt(float x) { return __builtin_amdgcn_sqrtf(x); }
-__device__ __forceinline__ float hw_div(float x, float y) { return x * __builtin_amdgcn_rcpf(y); }
 
 // x = hi + lo in bf16 pieces, each the round-to-nearest-even of the
 // remainder so far: |x - hi - lo| <= 2^-18 |x|
@@ -305,27 +280,6 @@ __device__ __forceinline__ float cross_block(const float* Gm, int NG, const floa
   return fmaf(ar[0], t[0], fmaf(ar[1], t[1], fmaf(ar[2], t[2], ar[3] * t[3])));
 }
 
-struct ItemDesc {
-  int64_t lh;
-  int s, t0, n;
-};
-
-// Work item w (unit-major over this size class) -> unit, sequence, slot.
-// pre[s] = number of this class's slots in sequences before s (pre[S] = total).
-__device__ __forceinline__ ItemDesc item_desc(const TreeKArgs& a, const int* pre, int64_t nsl, int64_t w) {
-  ItemDesc d;
-  d.lh = w / nsl;
-  const int rr = (int)(w - d.lh * nsl);
-  int s = 0;
-  while (rr >= pre[s + 1]) ++s;
-  d.s = s;
-  const int2 e = a.list[(int64_t)s * a.stride + (rr - pre[s])];
-  d.t0 = e.x;
-  d.n = e.y;
-  return d;
-}
-
-constexpr int MAX_SEQ = 256;  // sequences per call (prefix of the class counts lives in LDS)
 
 template <class T, int D, int NMAX, int WAVES, int OCC>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(OCC))) void tree_kernel(TreeKArgs a) {
