@@ -52,6 +52,49 @@ __global__ __launch_bounds__(256) void rmsnorm_cast_kernel(const float* xf, cons
   for (int i = threadIdx.x; i < dm; i += blockDim.x) ElemIO<T>::st(o, i, (float)((double)x[i] * r));
 }
 
+// The same for bf16 output with d_model a multiple of 4 up to 8192: each
+// thread keeps its float4 pieces of the row in registers (one read of x) and
+// stores four bf16 at a time. Same arithmetic: the fp64 sum of squares (in
+// another order: the sum is exact to far below the roundings that follow),
+// then x * r in fp64 rounded to fp32 and to bf16.
+constexpr int RMS_V4 = 8;   // float4 pieces a thread holds: d_model <= 4 * 256 * 8
+__global__ __launch_bounds__(256) void rmsnorm_cast_bf16_kernel(const float* xf, const float* xc, int64_t n_pairs,
+                                                                int dm, uint16_t* out) {
+  const int64_t row = blockIdx.x;
+  const int n4 = dm >> 2, tid = threadIdx.x;
+  uint2* o = (uint2*)(out + row * dm);
+  if (row >= 2 * n_pairs) {  // padding rows
+    for (int i = tid; i < n4; i += 256) o[i] = make_uint2(0u, 0u);
+    return;
+  }
+  const float4* x = (const float4*)(((row & 1) ? xc : xf) + (row >> 1) * dm);
+  __shared__ double red[4];
+  float4 v[RMS_V4];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < RMS_V4; ++k) {
+    const int i = tid + 256 * k;
+    v[k] = i < n4 ? x[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += (double)v[k].x * (double)v[k].x + (double)v[k].y * (double)v[k].y + (double)v[k].z * (double)v[k].z +
+          (double)v[k].w * (double)v[k].w;
+  }
+  ss = wave_sum_d(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const double r = 1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)dm + 1e-6);
+#pragma unroll
+  for (int k = 0; k < RMS_V4; ++k) {
+    const int i = tid + 256 * k;
+    if (i < n4) {
+      const uint32_t b0 = f32_to_bf16_bits((float)((double)v[k].x * r));
+      const uint32_t b1 = f32_to_bf16_bits((float)((double)v[k].y * r));
+      const uint32_t b2 = f32_to_bf16_bits((float)((double)v[k].z * r));
+      const uint32_t b3 = f32_to_bf16_bits((float)((double)v[k].w * r));
+      o[i] = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
+  }
+}
+
 template <class T> struct Frag;
 template <> struct Frag<uint16_t> { kvc_bf16x8 v; };
 template <> struct Frag<float> { float v[8]; };
@@ -277,156 +320,266 @@ __global__ __launch_bounds__(THREADS) void gemm_kl_kernel(const T* xh, const T* 
 // From a thousand rows on the projection is MFMA work (2 * rows * vocab *
 // d_model flops against one read of W), and the small kernel above is bound
 // by LDS traffic: every 32x32x16 product needs 1.25 KB of fragment reads.
-// Here a workgroup of 8 waves (two per SIMD) owns a 256 x 256 output tile and
-// each wave a 64 x 128 block (8 accumulators of 32 x 32): a 16-k step reads 6
-// fragments for 8 products. Operand tiles go global -> LDS with the direct
-// 16-byte LDS loads (no register staging), four 32-k stages deep: the loads
-// of stage s + 3 are in flight while stage s is multiplied. One such load
-// writes the 64 lanes' 16-byte pieces to 1 KB of LDS in lane order; lane L
-// of a load covering tile rows 16 b .. 16 b + 15 brings row 16 b + L / 4,
-// piece (L % 4) ^ f(row) of that row's 64-byte chunk, so LDS holds every row
-// with its four pieces permuted by f(row) = ((row >> 1) ^ (row >> 3)) & 3,
-// and a fragment read of 8 or 16 consecutive rows at one k touches distinct
-// banks. Consecutive workgroups take consecutive row tiles of one column
-// tile, so the W chunks in flight are shared by the workgroups running
-// together (an order blocked per XCD measured no better).
+// Here a workgroup of 4 waves (one per SIMD) owns a 256 x 256 output tile and
+// each wave a 128 x 128 block as 8 x 8 accumulators of 16 x 16 (256
+// registers a lane, held in the accumulation registers). With one wave a
+// SIMD, chains of 16x16x32 products keep the matrix cores busier than
+// 32x32x16 ones (94% against 76% of the bf16 peak in a register-only chain
+// on MI355X). A stage is 64 k: two 16x16x32 steps of 16 fragment reads and
+// 64 products a wave. Operand tiles go global -> LDS with the direct 16-byte
+// LDS loads (no register staging), two stages (128 KB). A load of 64 lanes
+// covers 8 tile rows x 128 bytes: whole cache lines, since the fetch rate of
+// a CU is set by how many line requests it keeps in flight (half-line
+// requests of 32-k stages held it near 12 bytes a clock). Lane L brings row
+// L / 8, piece (L % 8) ^ f(row) of that row's 128-byte chunk, and writes it
+// to the next 16 bytes of LDS, so LDS holds every row with its eight pieces
+// permuted by f(row) = (row ^ (row >> 3)) & 7: a fragment read of 16
+// consecutive rows at one k piece touches distinct banks. Stage it + 2 is
+// fetched as soon as every wave has finished reading stage it (the barrier
+// between its two steps), so the loads have a whole stage of products to
+// land. The loads and the next step's fragment reads are spread over the
+// products, one every four products: issued in a block, they held up the
+// product issue (2.06 -> 1.89 ms a call at 8,192 rows x 4,096 x 32,768).
+// Consecutive workgroups take consecutive row tiles of one column tile, so
+// the W chunks in flight are shared by the workgroups running together.
 constexpr int BT = 256;            // rows and vocab columns of a workgroup tile
-constexpr int BK = 32;             // k of one LDS stage (two 16-k MFMA steps): 64 bytes a row
-constexpr int NSTG = 4;            // LDS stages
+constexpr int BK = 64;             // k of one LDS stage (two 16x16x32 products): 128 bytes a row
 constexpr int BIG_MIN_ROWS = 1024; // the tiled kernel from this many (padded) rows on
 
-__device__ __forceinline__ int kl_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int kl_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-constexpr int BIG_THREADS = 512;   // 8 waves: 2 per SIMD, each 64 rows x 128 columns
+constexpr int BIG_THREADS = 256;   // 4 waves: 1 per SIMD, each 128 rows x 128 columns
+constexpr int BIG_LOADS = BT / 8 / (BIG_THREADS / 64);    // 8-row loads per operand, wave and stage (8)
 
-__global__ __launch_bounds__(BIG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+typedef float kl_f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(BIG_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kl_big_kernel(const uint16_t* xh, const uint16_t* W, int64_t n_pairs, int dm, int vocab, int ntr, int ntc,
                         float* part) {
-  __shared__ __align__(16) uint16_t lds[NSTG][2][BT * BK];   // [stage][x^, W][row][k], pieces permuted
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __align__(16) uint16_t lds[2][2][BT * BK];   // [stage][x^, W][row][k], pieces permuted
+  // every argument in registers before the main loop: a scalar load still in
+  // flight there would make each wait for fragment reads a wait for all of
+  // them (scalar and LDS reads share one counter)
+  asm volatile("" ::"s"(n_pairs), "s"(vocab), "s"(part), "s"(xh), "s"(W));
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
-  const int tr = blockIdx.x % ntr, tc = blockIdx.x / ntr;   // row tiles fastest
-  const int64_t r0 = (int64_t)tr * BT, c0 = (int64_t)tc * BT;
-  // this lane's source in each of the wave's 2 loads per operand and stage:
-  // load j covers tile rows 16 (2 wave + j) .. + 15
-  const int lrow = lane >> 2;
-  const uint16_t* xsrc[2];
-  const uint16_t* wsrc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (2 * wave + j) * 16 + lrow;
-    const int pg = (lane & 3) ^ kl_swz(row);
-    xsrc[j] = xh + (r0 + row) * dm + pg * 8;
-    wsrc[j] = W + (c0 + row) * dm + pg * 8;
-  }
-  const int nch = dm / BK;
-  kvc_f32x16 acc[2][4];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = kvc_f32x16{};
-  auto issue = [&](int ch) {   // loads of chunk ch into its stage
-    const int st = ch % NSTG;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint16_t* dx = lds[st][0] + (2 * wave + j) * 16 * BK;
-      uint16_t* dw = lds[st][1] + (2 * wave + j) * 16 * BK;
-      __builtin_amdgcn_global_load_lds((const void*)(xsrc[j] + ch * BK),
-                                       (__attribute__((address_space(3))) void*)dx, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(wsrc[j] + ch * BK),
-                                       (__attribute__((address_space(3))) void*)dw, 16, 0, 0);
-    }
+  const int ntiles = ntr * ntc;
+  // The workgroup walks tiles blockIdx.x, + gridDim.x, ...: tile t is row
+  // tile t % ntr of column tile t / ntr (row tiles fastest).
+  // This lane's source in each of the wave's loads per operand and stage:
+  // load j covers tile rows 8 (8 wave + j) .. + 7. The loads address each
+  // operand's 256-row tile through a buffer resource (its byte size the
+  // range: a load past it reads zeros), with a byte offset per lane and load
+  // that is the same for both operands, every chunk and every tile, and the
+  // chunk's offset in a scalar.
+  const int lrow = lane >> 3;
+  const int row0 = BIG_LOADS * 8 * wave + lrow;
+  const int tile_bytes = BT * dm * 2;
+  auto xres_of = [&](int t) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(xh + (int64_t)(t % ntr) * BT * dm), 0, tile_bytes, 0x00020000);
   };
-  // fragment rows: x^ rows wr*64 + 32 u + (lane & 31), W rows wc*128 + 32 u + (lane & 31)
-  const int ra = wr * 64 + (lane & 31), rb = wc * 128 + (lane & 31);
-  auto compute = [&](int st) {
+  auto wres_of = [&](int t) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)(t / ntr) * BT * dm), 0, tile_bytes, 0x00020000);
+  };
+  unsigned voff[BIG_LOADS];
+#pragma unroll
+  for (int j = 0; j < BIG_LOADS; ++j)
+    voff[j] = (unsigned)(((row0 + 8 * j) * dm + ((lane & 7) ^ kl_swz(row0 + 8 * j)) * 8) * 2);
+  const int nch = dm / BK;   // even: d_model is a multiple of 128
+  kl_f32x4 acc[8][8];
+  // Wait states between register writes and the written-out products that
+  // read them (and between those products and the reads of the results):
+  // each row of accumulators passes through a no-op that takes it as an
+  // operand, so the writes come before it and the reads after it.
+  auto settle = [&](int a) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc[a][0]), "+a"(acc[a][1]), "+a"(acc[a][2]), "+a"(acc[a][3]), "+a"(acc[a][4]),
+                   "+a"(acc[a][5]), "+a"(acc[a][6]), "+a"(acc[a][7]));
+  };
+  auto clear = [&]() {
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+      for (int b = 0; b < 8; ++b) acc[a][b] = kl_f32x4{};
+#pragma unroll
+    for (int a = 0; a < 8; ++a) settle(a);
+  };
+  // load j of chunk ch (tile rows 8 (8 wave + j) .. + 7) into stage st
+  auto load_x = [&](__amdgpu_buffer_rsrc_t res, int ch, int st, int j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        res, (__attribute__((address_space(3))) void*)(lds[st][0] + (BIG_LOADS * wave + j) * 8 * BK), 16, voff[j],
+        ch * BK * 2, 0, 0);
+  };
+  auto load_w = [&](__amdgpu_buffer_rsrc_t res, int ch, int st, int j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        res, (__attribute__((address_space(3))) void*)(lds[st][1] + (BIG_LOADS * wave + j) * 8 * BK), 16, voff[j],
+        ch * BK * 2, 0, 0);
+  };
+  // fragments of step ks of a stage: lane L holds row 16 u + (L & 15) of the
+  // wave's x^ rows (fa[u]) and of its W rows (fb[u]), k piece 4 ks + L / 16
+  // (8 consecutive k)
+  const int ra = wr * 128 + (lane & 15), rb = wc * 128 + (lane & 15), kp = lane >> 4;
+  auto frags = [&](int st, int ks, kvc_bf16x8* fa, kvc_bf16x8* fb) {
     const uint16_t* sx = lds[st][0];
     const uint16_t* sw = lds[st][1];
+    const int q = 4 * ks + kp;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int q = 2 * ks + (lane >> 5);
-      kvc_bf16x8 fa[2], fb[4];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int xr = ra + 32 * u;
-        fa[u] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sx + xr * BK + ((q ^ kl_swz(xr)) * 8)));
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int wr2 = rb + 32 * u;
-        fb[u] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sw + wr2 * BK + ((q ^ kl_swz(wr2)) * 8)));
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+    for (int u = 0; u < 8; ++u) {
+      const int xr = ra + 16 * u, wr2 = rb + 16 * u;
+      fa[u] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sx + xr * BK + ((q ^ kl_swz(xr)) * 8)));
+      fb[u] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sw + wr2 * BK + ((q ^ kl_swz(wr2)) * 8)));
     }
   };
-  // Stage it: wait until this wave's loads of chunk it have landed (4 loads a
-  // chunk per wave; chunks it + 1, it + 2 may still fly), then a barrier makes
-  // every wave's loads of it visible and guarantees that every wave is done
-  // reading stage it - 1, whose buffer chunk it + 3 then refills. The wait
-  // counts are immediates. (A plain s_barrier: __syncthreads would also wait
-  // for every load in flight.)
+  // Products of one step, column block by column block: fb[v] is dead after
+  // its 8 products, so the next step's fb[v] (and fa'[v]) are read right
+  // after them, one LDS read per four products. The next x^ fragments need a
+  // second register set (fa is live to the last column), the W fragments do
+  // not. The product is written out so that it accumulates in place in its
+  // accumulation registers: with the reads interleaved, the compiler's own
+  // register assignment moved accumulators between register files around
+  // nearly every product. Volatile, so the products and the LDS reads issue
+  // in this order; the inputs' waits for LDS reads are the compiler's, and
+  // no product reads an accumulator written fewer than 64 products before.
+  auto mfma = [](kl_f32x4& c, const kvc_bf16x8& a, const kvc_bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  };
+  // With lx/lw given the step also issues this wave's loads of chunk lch
+  // into stage lst, one operand piece every four products.
+  auto step = [&](const kvc_bf16x8* fa, kvc_bf16x8* fb, int nst, int nks, kvc_bf16x8* na, bool load,
+                  __amdgpu_buffer_rsrc_t lx, __amdgpu_buffer_rsrc_t lw, int lch, int lst) {
+    const uint16_t* sx = lds[nst][0];
+    const uint16_t* sw = lds[nst][1];
+    const int q = 4 * nks + kp;
 #pragma unroll
-  for (int c = 0; c < 3; ++c)
-    if (c < nch) issue(c);
-  for (int it = 0; it < nch; ++it) {
-    if (it + 2 < nch)   // uniform branches
-      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-    else if (it + 1 < nch)
-      asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    if (it + 3 < nch) issue(it + 3);
-    compute(it % NSTG);
-  }
-  // epilogue: lane owns columns c0 + wc*128 + 32 u + (lane & 31); registers
-  // v, v+1 (v % 4 in {0, 2}) of row block q hold rows 2p and 2p+1 of a pair.
-  // Each pair's statistics over the wave's 128 columns.
+    for (int v = 0; v < 8; ++v) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) mfma(acc[a][v], fa[a], fb[v]);
+      const int xr = ra + 16 * v;
+      na[v] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sx + xr * BK + ((q ^ kl_swz(xr)) * 8)));
+      if (load) load_x(lx, lch, lst, v);
+#pragma unroll
+      for (int a = 4; a < 8; ++a) mfma(acc[a][v], fa[a], fb[v]);
+      if (load) load_w(lw, lch, lst, v);
+      const int wr2 = rb + 16 * v;
+      fb[v] = __builtin_bit_cast(kvc_bf16x8, *(const uint4*)(sw + wr2 * BK + ((q ^ kl_swz(wr2)) * 8)));
+    }
+  };
+  // While direct LDS loads are in flight the compiler can only wait for all
+  // LDS reads at once, so each fragment set is consumed (ready()) right after
+  // the products that hide its reads.
+  auto ready = [](const kvc_bf16x8* f) {
+    asm volatile("" ::"v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]), "v"(f[4]), "v"(f[5]), "v"(f[6]), "v"(f[7]));
+  };
+  // epilogue of tile t: lane owns columns c0 + wc*128 + 16 v + (lane & 15),
+  // v = 0..7; element i of accumulator [u][v] is row wr*128 + 16 u +
+  // 4 (lane >> 4) + i, so elements 0, 1 and 2, 3 are rows 2p and 2p+1 of a
+  // pair. Each pair's statistics over the wave's 128 columns: the lane's 8,
+  // then the 16 lanes of its row group.
   const int nsub = vocab / 128;
+  auto epilogue = [&](int t) {
+    const int64_t r0 = (int64_t)(t % ntr) * BT;
+    const int tc = t / ntr;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+    for (int u = 0; u < 8; ++u) {
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) {
+      for (int i = 0; i < 4; i += 2) {
 #pragma clang fp contract(off)
-      const int row = wr * 64 + q * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-      const int64_t pair = (r0 + row) >> 1;
-      float y[4], yh[4];
-      float mf = -INFINITY, mc = -INFINITY;
+        const int row = wr * 128 + 16 * u + 4 * (lane >> 4) + i;
+        const int64_t pair = (r0 + row) >> 1;
+        float y[8], yh[8];
+        float mf = -INFINITY, mc = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        y[u] = acc[q][u][v] * LOG2E;
-        yh[u] = acc[q][u][v + 1] * LOG2E;
-        mf = fmaxf(mf, y[u]);
-        mc = fmaxf(mc, yh[u]);
-      }
+        for (int v = 0; v < 8; ++v) {
+          y[v] = acc[u][v][i] * LOG2E;
+          yh[v] = acc[u][v][i + 1] * LOG2E;
+          mf = fmaxf(mf, y[v]);
+          mc = fmaxf(mc, yh[v]);
+        }
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        mf = fmaxf(mf, __shfl_xor(mf, o, 64));
-        mc = fmaxf(mc, __shfl_xor(mc, o, 64));
-      }
-      float sf = 0.f, sc = 0.f, t = 0.f;
+        for (int o = 1; o < 16; o <<= 1) {
+          mf = fmaxf(mf, __shfl_xor(mf, o, 64));
+          mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+        }
+        float sf = 0.f, sc = 0.f, tt = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float ef = fast_exp2(y[u] - mf), ec = fast_exp2(yh[u] - mc);
-        sf += ef;
-        sc += ec;
-        t += ef * (acc[q][u][v] - acc[q][u][v + 1]);
-      }
+        for (int v = 0; v < 8; ++v) {
+          const float ef = fast_exp2(y[v] - mf), ec = fast_exp2(yh[v] - mc);
+          sf += ef;
+          sc += ec;
+          tt += ef * (acc[u][v][i] - acc[u][v][i + 1]);
+        }
 #pragma unroll
-      for (int o = 1; o < 32; o <<= 1) {
-        sf += __shfl_xor(sf, o, 64);
-        sc += __shfl_xor(sc, o, 64);
-        t += __shfl_xor(t, o, 64);
-      }
-      if ((lane & 31) == 0 && pair < n_pairs) {
-        float* pp = part + (pair * nsub + (int64_t)tc * 2 + wc) * 5;
-        pp[0] = mf; pp[1] = sf; pp[2] = mc; pp[3] = sc; pp[4] = t;
+        for (int o = 1; o < 16; o <<= 1) {
+          sf += __shfl_xor(sf, o, 64);
+          sc += __shfl_xor(sc, o, 64);
+          tt += __shfl_xor(tt, o, 64);
+        }
+        if ((lane & 15) == 0 && pair < n_pairs) {
+          float* pp = part + (pair * nsub + (int64_t)tc * 2 + wc) * 5;
+          pp[0] = mf; pp[1] = sf; pp[2] = mc; pp[3] = sc; pp[4] = tt;
+        }
       }
     }
+  };
+  // Iteration it of a tile multiplies stage it & 1 (chunk it) in two steps.
+  // The first step reads the second step's fragments of the same stage;
+  // then this wave's loads of the next chunk (the only ones in flight) are
+  // waited for, and the barrier makes every wave's loads of it visible and
+  // guarantees that every read of chunk it is complete, so the chunk two
+  // ahead may refill its stage. A plain s_barrier, since __syncthreads would
+  // also wait for the loads just issued. The second step reads the first
+  // step's fragments of the next chunk and loads the chunk two ahead: in the
+  // last two iterations of a tile these are chunks 0 and 1 of the
+  // workgroup's next tile, so its first products wait for no load; after the
+  // last tile the loads repeat the last chunk (no branch around them) and
+  // nothing reads that copy, nor the fragments read past the last chunk.
+  int t = blockIdx.x;
+  __amdgpu_buffer_rsrc_t xres = xres_of(t), wres = wres_of(t);
+#pragma unroll
+  for (int j = 0; j < BIG_LOADS; ++j) {
+    load_x(xres, 0, 0, j);
+    load_w(wres, 0, 0, j);
   }
+#pragma unroll
+  for (int j = 0; j < BIG_LOADS; ++j) {
+    load_x(xres, 1, 1, j);
+    load_w(wres, 1, 1, j);
+  }
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");   // chunk 0 landed
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  clear();
+  kvc_bf16x8 fa0[8], fa1[8], fb[8];
+  frags(0, 0, fa0, fb);
+  ready(fa0);
+  ready(fb);
+  for (; t < ntiles; t += gridDim.x) {
+    const int tn = t + gridDim.x;
+    const bool more = tn < ntiles;
+    const __amdgpu_buffer_rsrc_t nxres = more ? xres_of(tn) : xres, nwres = more ? wres_of(tn) : wres;
+    for (int it = 0; it < nch; ++it) {
+      const int st = it & 1;
+      step(fa0, fb, st, 1, fa1, false, xres, wres, 0, 0);
+      ready(fa1);
+      ready(fb);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next chunk landed
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const bool cross = it + 2 >= nch;
+      const int lch = !cross ? it + 2 : (more ? it + 2 - nch : nch - 1);
+      step(fa1, fb, st ^ 1, 0, fa0, true, cross ? nxres : xres, cross ? nwres : wres, lch, st);
+      ready(fa0);
+      ready(fb);
+    }
+#pragma unroll
+    for (int a = 0; a < 8; ++a) settle(a);
+    epilogue(t);
+    clear();
+    xres = nxres;
+    wres = nwres;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the repeated loads of the last chunk
 }
 
 // One workgroup per pair: threads merge strided subsets of the column-tile
@@ -501,12 +654,22 @@ extern "C" int kvc_kl(int64_t n_pairs, int32_t d_model, int32_t vocab, const flo
   float* part = c.take<float>((size_t)n_pairs * ntile * NCW * 5);
   dim3 g2((unsigned)ntile, (unsigned)((m_pad + MT - 1) / MT));
   if (w_dtype == KVC_BF16) {
-    hipLaunchKernelGGL(rmsnorm_cast_kernel<uint16_t>, dim3((unsigned)m_pad), dim3(256), 0, st, x_full, x_comp,
-                       n_pairs, d_model, m_pad, (uint16_t*)xh);
+    if (d_model <= 4 * 256 * RMS_V4)
+      hipLaunchKernelGGL(rmsnorm_cast_bf16_kernel, dim3((unsigned)m_pad), dim3(256), 0, st, x_full, x_comp, n_pairs,
+                         d_model, (uint16_t*)xh);
+    else
+      hipLaunchKernelGGL(rmsnorm_cast_kernel<uint16_t>, dim3((unsigned)m_pad), dim3(256), 0, st, x_full, x_comp,
+                         n_pairs, d_model, m_pad, (uint16_t*)xh);
     KVC_LAUNCH_CHECK("rmsnorm_cast");
     if (big) {
       const int ntr = (int)(m_pad / BT), ntc = vocab / BT;
-      hipLaunchKernelGGL(gemm_kl_big_kernel, dim3((unsigned)(ntr * ntc)), dim3(BIG_THREADS), 0, st,
+      // one workgroup a CU (128 KB of LDS, one wave a SIMD), each walking
+      // its tiles
+      int dev = 0, ncu = 0;
+      (void)hipGetDevice(&dev);
+      if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+      const int grid = ntr * ntc < ncu ? ntr * ntc : ncu;
+      hipLaunchKernelGGL(gemm_kl_big_kernel, dim3((unsigned)grid), dim3(BIG_THREADS), 0, st,
                          (const uint16_t*)xh, (const uint16_t*)W, n_pairs, d_model, vocab, ntr, ntc, part);
       KVC_LAUNCH_CHECK("gemm_kl_big");
       hipLaunchKernelGGL(kl_combine_kernel, dim3((unsigned)n_pairs), dim3(256), 0, st, part, n_pairs, vocab / 128,
