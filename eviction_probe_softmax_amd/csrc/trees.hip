@@ -1418,8 +1418,14 @@ template <class T, int D>
 int launch_both(TreeKArgs a, int2* lists, int32_t* counts, int64_t bound, int nmax, int ncu, hipStream_t st) {
   a.list = lists;
   a.count = counts;
-  // small slots: two 8-wave workgroups per CU (4 waves per SIMD); large: one
-  int r = launch_trees<T, D, SMALL, 8, 4>(a, bound, ncu, st);
+  // small slots: two 8-wave workgroups per CU (4 waves per SIMD); large: one.
+  // Midpoint trees of bf16 slots with head dimension 128 take the kernel on
+  // the fixed 64-position layout.
+  int r;
+  if constexpr (sizeof(T) == 2 && D == 128)
+    r = a.topo == nullptr ? launch_trees_v(a, bound, ncu, st) : launch_trees<T, D, SMALL, 8, 4>(a, bound, ncu, st);
+  else
+    r = launch_trees<T, D, SMALL, 8, 4>(a, bound, ncu, st);
   if (r || nmax <= SMALL) return r;
   a.list = lists + (int64_t)a.S * a.stride;
   a.count = counts + a.S;

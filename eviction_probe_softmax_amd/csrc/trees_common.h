@@ -58,5 +58,9 @@ __device__ __forceinline__ ItemDesc item_desc(const TreeKArgs& a, const int* pre
 
 constexpr int MAX_SEQ = 256;  // sequences per call (prefix of the class counts lives in LDS)
 
+// Midpoint trees of slots of at most 64 tokens, bf16 keys and values of head
+// dimension 128, on the fixed 64-position layout (trees_v.hip).
+int launch_trees_v(const TreeKArgs& a, int64_t bound, int ncu, hipStream_t st);
+
 
 }  // namespace kvc_tree

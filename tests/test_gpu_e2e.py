@@ -26,15 +26,10 @@ def _run_gpu(cfg, inp):
     return out, xf, xc, klv
 
 
-# The stress case faulted the GPU once while an experimental tree kernel for
-# slots of at most 64 tokens ran in the tree stage (that kernel is no longer in
-# the library). No out-of-range index was found for it on the CPU, so the
-# cause is not shown and the case stays off the GPU until it is.
-FAULTED_TREE_V = "faulted the GPU under a since-removed tree kernel; cause not shown (see the comment above)"
 
 
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("mistral1", {}),
-                                     pytest.param("stress", {}, marks=pytest.mark.skip(reason=FAULTED_TREE_V)),
+                                     ("stress", {}),
                                      ("ragged", {}),
                                      ("fulldepth", {}), ("ragged", {"hybrid_frac": 0.5}),
                                      ("fulldepth", {"hybrid_frac": 0.25, "budget_ratio": 0.4}),

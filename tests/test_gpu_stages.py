@@ -74,18 +74,11 @@ def _compare_cache(c, oc, exact):
     close(lm, oc["lnmu"], 1e-3, "ln mu", floor=1e-3)
 
 
-# This case faulted the GPU once while an experimental tree kernel for slots
-# of at most 64 tokens ran in its place (that kernel is no longer in the
-# library; the general tree kernel handles every slot again). A CPU replay of
-# every global and LDS index that kernel formed on these inputs found none out
-# of range, so the cause is not shown and the case stays off the GPU until it is.
-FAULTED_TREE_V = "faulted the GPU under a since-removed tree kernel; cause not shown (see the comment above)"
 
 
 @pytest.mark.parametrize("name,kw", [("tiny", {}), ("stress", {}), ("ragged", {}), ("fulldepth", {}),
                                      ("stress", {"slot_len": 128}),
-                                     pytest.param("fulldepth", {"slot_min": 64, "slot_max": 128, "slot_target": 120},
-                                                  marks=pytest.mark.skip(reason=FAULTED_TREE_V)),
+                                     ("fulldepth", {"slot_min": 64, "slot_max": 128, "slot_target": 120}),
                                      ("tiny", {"slot_len": 128}),
                                      ("fulldepth", {"slot_min": 8, "slot_max": 64, "slot_target": 40}),
                                      ("tiny", {"split_mode": 1}), ("fulldepth", {"split_mode": 1}),
