@@ -36,8 +36,9 @@
 //     lse_rho) on MFMA, value column sums; waves 4-7 (lane = rotation pair,
 //     16 positions each): inverse-rotated keys, key norms, key sums of the
 //     blocks of up to 16 positions, their multiplicities and prototype keys;
-//  S2 waves 0-2: the centred value Gram matrix on MFMA; waves 4-6: the blocks
-//     of 32 and 64 positions;
+//  S2 waves 0-2: the centred value Gram matrix on MFMA, a 32 x 32 tile each
+//     (partial row sums, a barrier, then each stores its tile); waves 4-6: the
+//     blocks of 32 and 64 positions;
 //  S3 waves 0-3: prototype logits on MFMA; waves 4-7: w and g per depth;
 //  S4 waves 0-5 (probe-row half x two depths): T on MFMA, then per node and
 //     row the two value forms and the attention-partition terms, summed over
@@ -641,84 +642,49 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
     __syncthreads();
 
     // ---- S2
-    if (wave == 0) {
-      // Gram matrix of the slot's values: the bf16 values are exact MFMA
-      // inputs, so G = V V^T is exact up to the fp32 accumulation; centred as
-      // G'_vi = G_vi - r_v - r_i + R with the row means r_v = <v_v, m> and
-      // R = |m|^2 (m the slot's value mean; positions without a token are 0)
-      const int tr0 = tok[l32], tr1 = tok[32 + l32];
-      kvc_f32x16 g00 = {}, g01 = {}, g11 = {};
+    // Waves 0-2: one tile each of the Gram matrix of the slot's values (the
+    // bf16 values are exact MFMA inputs, so G = V V^T is exact up to the fp32
+    // accumulation): tiles (0, 0), (0, 1) and (1, 1) of 32 x 32 positions, and
+    // their partial row sums (tile (0, 1) also gives the row sums of (1, 0) as
+    // its column sums): part0 = wl[0, 64) from the diagonal tiles, part1 =
+    // wl[64, 128) from the off-diagonal one. After the barrier each wave
+    // centres and stores its tile: G'_vi = G_vi - r_v - r_i + R with the row
+    // means r_v = (part0_v + part1_v) / n = <v_v, m> and R = |m|^2 (m the
+    // slot's value mean; positions without a token are 0).
+    kvc_f32x16 gt = {};
+    const int gti = wave == 2 ? 1 : 0, gtj = wave == 0 ? 0 : 1;
+    if (wave < 3) {
+      const int ra = tok[gti * 32 + l32], rb = tok[gtj * 32 + l32];
 #pragma unroll 2
       for (int k = 0; k < 8; ++k) {
         const int c = k * 16 + 8 * hb;
-        const Frag<uint16_t> f0 = tr0 >= 0 ? load_frag<uint16_t>(Vg + (int64_t)tr0 * DH + c) : zero_frag<uint16_t>();
-        const Frag<uint16_t> f1 = tr1 >= 0 ? load_frag<uint16_t>(Vg + (int64_t)tr1 * DH + c) : zero_frag<uint16_t>();
-        mma(g00, f0, f0);
-        mma(g01, f0, f1);
-        mma(g11, f1, f1);
-      }
-      // row sums: rows 0-31 over both column tiles; rows 32-63 from the
-      // column sums of tile (0,1) (symmetry) and the rows of tile (1,1)
-      float* rsum = wl;
-      const float rn = 1.f / (float)n;
-      {
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = g00[r] + g01[r];
-        int base = 0;
-        reduce_scatter<16, 16>(x, lane, base);
-        if ((lane & 1) == 0) rsum[8 * (base >> 2) + 4 * hb + (base & 3)] = x[0] * rn;
-      }
-      float cs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cs += g01[r];
-      cs = group_sum_x32(cs);
-      {
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = g11[r];
-        int base = 0;
-        reduce_scatter<16, 16>(x, lane, base);
-        if ((lane & 1) == 0) rsum[32 + 8 * (base >> 2) + 4 * hb + (base & 3)] = x[0];
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (hb == 0) rsum[32 + l32] = (rsum[32 + l32] + cs) * rn;
-      __builtin_amdgcn_wave_barrier();
-      const float rl = rsum[lane];
-      const float R = group_sum<64>(rl) * rn;
-      sdv[lane] = rl - R;
-      if (lane == 0) misc[0] = R;
-      auto store = [&](const kvc_f32x16& acc, int ti, int tj) {
-        const int col = tj * 32 + l32;
-        const float rc = rsum[col];
-        const bool cok = tok[col] >= 0;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int r0 = ti * 32 + 8 * g + 4 * hb;
-          const float4 rr = *(const float4*)(rsum + r0);
-          const int4 tt = *(const int4*)(tok + r0);
-          const float rrv[4] = {rr.x, rr.y, rr.z, rr.w};
-          const int ttv[4] = {tt.x, tt.y, tt.z, tt.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = r0 + e;
-            const float gv = (cok && ttv[e] >= 0) ? ((acc[4 * g + e] - rrv[e]) - rc) + R : 0.f;
-            const uint16_t hi = f32_to_bf16_hw(gv), lo = f32_to_bf16_hw(gv - bf16_bits_to_f32(hi));
-            Gh[row * GS + col] = hi;
-            Gl[row * GS + col] = lo;
-            if (ti != tj) {
-              Gh[col * GS + row] = hi;
-              Gl[col * GS + row] = lo;
-            }
-          }
+        const Frag<uint16_t> fa = ra >= 0 ? load_frag<uint16_t>(Vg + (int64_t)ra * DH + c) : zero_frag<uint16_t>();
+        if (wave == 1) {
+          const Frag<uint16_t> fb = rb >= 0 ? load_frag<uint16_t>(Vg + (int64_t)rb * DH + c) : zero_frag<uint16_t>();
+          mma(gt, fa, fb);
+        } else {
+          mma(gt, fa, fa);
         }
-      };
-      store(g00, 0, 0);
-      store(g01, 0, 1);
-      store(g11, 1, 1);
+      }
+      float* part = wl + (wave == 1 ? 64 : 0) + 32 * gti;
+      {
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = gt[r];
+        int base = 0;
+        reduce_scatter<16, 16>(x, lane, base);
+        if ((lane & 1) == 0) part[8 * (base >> 2) + 4 * hb + (base & 3)] = x[0];
+      }
+      if (wave == 1) {
+        float cs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cs += gt[r];
+        cs = group_sum_x32(cs);
+        if (hb == 0) wl[64 + 32 + l32] = cs;
+      }
     } else if (wave >= 4 && wave < 7) {
       // blocks 1 (the root, 64 positions), 2 and 3 (32 positions each) from
-      // the 16-position key sums; waves 1-3 have no work in this stage
+      // the 16-position key sums; waves 3 and 7 have no work in this stage
       const int b = wave - 3, p = lane;
       const int g0 = b == 3 ? 2 : 0, g1 = b == 2 ? 2 : 4;
       float k0s = 0.f, k1s = 0.f;
@@ -745,6 +711,39 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4))) vo
         Kh[b * KR + HD + p] = h1;
         Kl[b * KR + p] = f32_to_bf16_hw(k0 - bf16_bits_to_f32(h0));
         Kl[b * KR + HD + p] = f32_to_bf16_hw(k1 - bf16_bits_to_f32(h1));
+      }
+    }
+    __syncthreads();
+    if (wave < 3) {
+      const float rn = 1.f / (float)n;
+      const float rl = (wl[lane] + wl[64 + lane]) * rn;
+      const float R = group_sum<64>(rl) * rn;
+      if (wave == 0) {
+        sdv[lane] = rl - R;
+        if (lane == 0) misc[0] = R;
+      }
+      const int col = gtj * 32 + l32;
+      const float rc = (wl[col] + wl[64 + col]) * rn;
+      const bool cok = tok[col] >= 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = gti * 32 + 8 * g + 4 * hb;
+        const float4 p0 = *(const float4*)(wl + r0), p1 = *(const float4*)(wl + 64 + r0);
+        const int4 tt = *(const int4*)(tok + r0);
+        const float rrv[4] = {(p0.x + p1.x) * rn, (p0.y + p1.y) * rn, (p0.z + p1.z) * rn, (p0.w + p1.w) * rn};
+        const int ttv[4] = {tt.x, tt.y, tt.z, tt.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = r0 + e;
+          const float gv = (cok && ttv[e] >= 0) ? ((gt[4 * g + e] - rrv[e]) - rc) + R : 0.f;
+          const uint16_t hi = f32_to_bf16_hw(gv), lo = f32_to_bf16_hw(gv - bf16_bits_to_f32(hi));
+          Gh[row * GS + col] = hi;
+          Gl[row * GS + col] = lo;
+          if (gti != gtj) {
+            Gh[col * GS + row] = hi;
+            Gl[col * GS + row] = lo;
+          }
+        }
       }
     }
     __syncthreads();
