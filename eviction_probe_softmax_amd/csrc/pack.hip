@@ -204,50 +204,69 @@ __global__ __launch_bounds__(256) void write_kept_kernel(PackArgs a, const int64
   }
 }
 
-// 8 consecutive elements from fp32 values in one 16-byte store (bf16: RNE)
-// or two (fp32).
+// One wave per (unit, slot); the waves of a workgroup take the same slot of
+// consecutive units (units fastest), so the RoPE rows of the slot's
+// positions are shared in L2. Each node decides whether it is on the
+// frontier (its creator op taken, its own Split not taken; the root's creator
+// is the Add), 64 nodes at a time; the frontier nodes in pre-order are the
+// slot's output rows in order and cover its tokens in position order. Their
+// extents and value-weight terms go to the wave's LDS. Then the wave walks
+// the slot's tokens in groups of eight (one round of loads a group), lane p
+// holding rotation pair (p, p + d/2) of the key and dims (2p, 2p + 1) of the
+// value, and accumulates into the current entry: at an entry's last token a
+// leaf writes its token's rows (the loaded values, exact), a prototype the
+// mean of its inverse-rotated keys re-rotated at its representative position
+// and its weighted value.
+constexpr int WS_WAVES = 4;
+constexpr int WS_MAXE = 128;   // frontier entries of a slot of at most 128 tokens
+constexpr int WS_G = 8;        // tokens a group
+
 template <class T>
-__device__ __forceinline__ void store8(T* p, const float* x) {
+__device__ __forceinline__ float ld1(const T* p) {
+  if constexpr (sizeof(T) == 2) return bf16_bits_to_f32(*p);
+  else return *p;
+}
+template <class T>
+__device__ __forceinline__ float2 ld2(const T* p) {   // two consecutive elements
   if constexpr (sizeof(T) == 2) {
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[q] = (uint32_t)f32_to_bf16_hw(x[2 * q]) | ((uint32_t)f32_to_bf16_hw(x[2 * q + 1]) << 16);
-    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+    const uint32_t w = *(const uint32_t*)p;
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u));
   } else {
-    *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
-    *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    return *(const float2*)p;
   }
 }
+template <class T>
+__device__ __forceinline__ void st1(T* p, float x) {
+  if constexpr (sizeof(T) == 2) *p = f32_to_bf16_hw(x);
+  else *p = x;
+}
+template <class T>
+__device__ __forceinline__ void st2(T* p, float x, float y) {
+  if constexpr (sizeof(T) == 2) *(uint32_t*)p = (uint32_t)f32_to_bf16_hw(x) | ((uint32_t)f32_to_bf16_hw(y) << 16);
+  else *(float2*)p = make_float2(x, y);
+}
 
-// One workgroup per (unit, slot). Every node decides in parallel whether it
-// is on the frontier (its creator op taken, its own Split not taken; the
-// root's creator is the Add); a block scan gives the frontier in pre-order,
-// which is position order. Then 16-byte pieces of the output rows are spread
-// over the threads: leaves are copied, prototype keys (8 rotate-half pairs a
-// piece) and values (8 dims a piece) are averaged over the node's tokens by
-// SPL threads a piece.
-constexpr int WS_THREADS = 256;  // >= 2 * 128 - 1 nodes of the largest slot
-constexpr int SPL = 4;           // threads per piece of a prototype
+struct WsEntries {
+  int16_t sz[WS_MAXE];   // tokens of entry e (its first is the end of the previous one)
+  float alpha[WS_MAXE];  // value weight of token i: alpha r_i + gamma
+  float gamma[WS_MAXE];
+  float lnmu[WS_MAXE];   // log multiplicity (0 for a leaf)
+};
 
 template <class T, int D>
-__global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, const int64_t* off) {
+__global__ __launch_bounds__(WS_WAVES * 64) void write_slots_kernel(PackArgs a, const int64_t* off) {
   constexpr int HD = D / 2;
-  constexpr int KP = HD / 8;       // key pieces (8 rotate-half pairs each)
-  constexpr int VP = D / 8;        // value pieces (8 dims each)
-  constexpr int CPN = KP + VP;
-  __shared__ int16_t fnode[WS_THREADS], fst[WS_THREADS], fsz[WS_THREADS];
-  __shared__ int ioff[WS_THREADS + 1];
-  __shared__ int wcnt[WS_THREADS / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // block -> (unit lh, sequence s, slot k): the grid holds, per unit, a bound
-  // on each sequence's slot count (its length over the shortest slot, plus
-  // one); blocks past a sequence's slots return at once
-  const int64_t b = blockIdx.x, nb = a.sbound[a.S];
-  const int64_t lh = b / nb;
-  const int r = (int)(b - lh * nb);
+  __shared__ WsEntries ent_all[WS_WAVES];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  WsEntries& ent = ent_all[wv];
+  const int64_t nunits = (int64_t)a.Ly * a.H;
+  const int64_t w = (int64_t)blockIdx.x * WS_WAVES + wv;
+  const int64_t row = w / nunits;              // slot row over the sequences' slot bounds
+  const int64_t lh = w - row * nunits;
+  if (row >= a.sbound[a.S]) return;
   int s = 0;
-  while (r >= a.sbound[s + 1]) ++s;
-  const int k = r - a.sbound[s];
+  while (row >= a.sbound[s + 1]) ++s;
+  const int k = (int)(row - a.sbound[s]);
   if (k >= a.n_slots[s]) return;
   const int32_t* ss = a.slot_start + (int64_t)s * (a.stride + 1);
   const int t0 = ss[k], n = ss[k + 1] - ss[k];
@@ -256,176 +275,121 @@ __global__ __launch_bounds__(WS_THREADS) void write_slots_kernel(PackArgs a, con
   const uint8_t* tk = a.taken + obase;
   if (!tk[0]) return;                                 // Add not taken: no entry
   const int64_t dst0 = off[lh * a.T + tok0];
-  // frontier flags: one node per thread (its record, or a pre-order walk of
-  // the midpoint tree from the root)
-  bool fl = false;
-  int st = 0, sz = n;
-  if (a.topo) {
-    const uint32_t x = tid < 2 * n ? a.topo[obase + tid] : 0xFFFFFFFFu;
-    if (x != 0xFFFFFFFFu) {
-      st = (int)(x & 255);
-      sz = (int)((x >> 8) & 255) + 1;
-      const int par = (int)((x >> 16) & 255) - 1;
-      fl = tk[par < 0 ? 0 : 1 + par] && !(sz > 1 && tk[1 + tid]);
-    }
-  } else if (tid < 2 * n - 1) {
-    int cur = 0, par = -1;
-    while (cur != tid) {
-      const int nl = (sz + 1) >> 1;
-      par = cur;
-      if (tid < cur + 2 * nl) {
-        cur += 1;
-        sz = nl;
+  // frontier nodes in pre-order -> entries
+  const int nn = a.topo ? 2 * n : 2 * n - 1;         // node records of the slot
+  int ne = 0;
+  for (int base = 0; base < nn; base += 64) {
+    const int j = base + lane;
+    bool fl = false;
+    int sz = n;
+    if (j < nn) {
+      if (a.topo) {
+        const uint32_t x = a.topo[obase + j];
+        if (x != 0xFFFFFFFFu) {
+          sz = (int)((x >> 8) & 255) + 1;
+          const int par = (int)((x >> 16) & 255) - 1;
+          fl = tk[par < 0 ? 0 : 1 + par] && !(sz > 1 && tk[1 + j]);
+        }
       } else {
-        cur += 2 * nl;
-        st += nl;
-        sz -= nl;
+        int cur = 0, par = -1;   // pre-order walk of the midpoint tree from the root
+        while (cur != j) {
+          const int nl = (sz + 1) >> 1;
+          par = cur;
+          if (j < cur + 2 * nl) {
+            cur += 1;
+            sz = nl;
+          } else {
+            cur += 2 * nl;
+            sz -= nl;
+          }
+        }
+        fl = tk[par < 0 ? 0 : 1 + par] && !(sz > 1 && tk[1 + j]);
       }
     }
-    const int creator = par < 0 ? 0 : 1 + par;
-    fl = tk[creator] && !(sz > 1 && tk[1 + tid]);
-  }
-  const uint64_t bm = __ballot(fl);
-  if (lane == 0) wcnt[wave] = __popcll(bm);
-  __syncthreads();
-  int q = 0, nfr = 0;
-#pragma unroll
-  for (int w = 0; w < WS_THREADS / 64; ++w) {
-    q += w < wave ? wcnt[w] : 0;
-    nfr += wcnt[w];
-  }
-  if (fl) {
-    q += __popcll(bm & (lane == 0 ? 0ull : (~0ull >> (64 - lane))));
-    fnode[q] = (int16_t)tid;
-    fst[q] = (int16_t)st;
-    fsz[q] = (int16_t)sz;
-  }
-  __syncthreads();
-  // item ranges: a leaf takes CPN items (one per piece), a prototype SPL * CPN
-  // (SPL consecutive threads per piece, each summing every SPL-th token); all
-  // ranges are multiples of SPL, so the SPL threads of a piece are
-  // neighbouring lanes of one wave
-  {
-    const int f = tid;
-    const int ic = f < nfr ? (fsz[f] == 1 ? CPN : SPL * CPN) : 0;
-    int inc = ic;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
+    const uint64_t m = __ballot(fl);
+    if (fl) {
+      const int e = ne + __popcll(m & ((1ull << lane) - 1ull));
+      float al = 0.f, ga = 1.f, lm = 0.f;
+      if (sz > 1) {
+        const float rel_n = a.node_rel[obase + j];
+        al = rel_n > 0.f ? (1.f - a.beta) / rel_n : 0.f;   // weights (1 - beta) r_i / rel + beta / n, or 1 / n
+        ga = (rel_n > 0.f ? a.beta : 1.f) / (float)sz;
+        lm = logf(a.node_mu[obase + j]);
+      }
+      ent.sz[e] = (int16_t)sz;
+      ent.alpha[e] = al;
+      ent.gamma[e] = ga;
+      ent.lnmu[e] = lm;
     }
-    if (lane == 63) wcnt[wave] = inc;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < WS_THREADS / 64; ++w) {
-      base += w < wave ? wcnt[w] : 0;
-      tot += wcnt[w];
-    }
-    if (f < nfr) ioff[f] = base + inc - ic;
-    if (tid == 0) ioff[nfr] = tot;
-    __syncthreads();
+    ne += __popcll(m);
   }
-  const int nitems = ioff[nfr];
+  __builtin_amdgcn_wave_barrier();   // the entries are written before any lane reads them
   const T* Ku = (const T*)a.K + (lh * a.T + a.cu[s]) * D;
   const T* Vu = (const T*)a.V + (lh * a.T + a.cu[s]) * D;
   const float* ru = a.rel + lh * a.T + a.cu[s];
-  for (int it = tid; it < nitems; it += WS_THREADS) {
-    // entry of this item: the last f with ioff[f] <= it
-    int lo = 0, hi = nfr - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ioff[mid] <= it) lo = mid;
-      else hi = mid - 1;
+  const int p = lane < HD ? lane : HD - 1;   // lanes past the pairs repeat the last one (not stored)
+  int e = 0, ea = t0, esz = ent.sz[0];       // current entry, its first position and size
+  float al = ent.alpha[0], ga = ent.gamma[0];
+  float s0 = 0.f, s1 = 0.f, v0 = 0.f, v1 = 0.f, cp = 0.f, sp = 0.f;
+  for (int g = t0; g < t0 + n; g += WS_G) {
+    float x0[WS_G], x1[WS_G], c[WS_G], sn[WS_G], r[WS_G];
+    float2 y[WS_G];
+#pragma unroll
+    for (int u = 0; u < WS_G; ++u) {   // past the slot: repeats of its last token, unused
+      const int i = min(g + u, t0 + n - 1);
+      const T* kr = Ku + (int64_t)i * D;
+      x0[u] = ld1(kr + p);
+      x1[u] = ld1(kr + HD + p);
+      c[u] = a.rc[(int64_t)i * HD + p];
+      sn[u] = a.rs[(int64_t)i * HD + p];
+      y[u] = ld2(Vu + (int64_t)i * D + 2 * p);
+      r[u] = ru[i];
     }
-    const int f = lo, local = it - ioff[f];
-    const int64_t dst = dst0 + f;
-    if (dst >= a.capacity) continue;  // every item of the entry skips together
-    const int j = fnode[f], a0 = t0 + fst[f], nz = fsz[f];   // sequence positions [a0, a0 + nz)
-    T* oK = (T*)a.oK + dst * D;
-    T* oV = (T*)a.oV + dst * D;
-    if (nz == 1) {  // leaf: bit copy of the token's 16-byte pieces
-      const int c = local;
-      if (c < KP) {
-        *(uint4*)(oK + c * 8) = *(const uint4*)(Ku + (int64_t)a0 * D + c * 8);
-        *(uint4*)(oK + HD + c * 8) = *(const uint4*)(Ku + (int64_t)a0 * D + HD + c * 8);
-        if constexpr (sizeof(T) == 4) {
-          *(uint4*)(oK + c * 8 + 4) = *(const uint4*)(Ku + (int64_t)a0 * D + c * 8 + 4);
-          *(uint4*)(oK + HD + c * 8 + 4) = *(const uint4*)(Ku + (int64_t)a0 * D + HD + c * 8 + 4);
+#pragma unroll
+    for (int u = 0; u < WS_G; ++u) {
+      const int i = g + u;
+      if (i >= t0 + n) break;
+      s0 += x0[u] * c[u] + x1[u] * sn[u];   // rotation by -theta
+      s1 += x1[u] * c[u] - x0[u] * sn[u];
+      const float wt = fmaf(al, r[u], ga);
+      v0 += wt * y[u].x;
+      v1 += wt * y[u].y;
+      if (i == ea + (esz - 1) / 2) {   // representative position
+        cp = c[u];
+        sp = sn[u];
+      }
+      if (i == ea + esz - 1) {   // last token of entry e
+        const int64_t d = dst0 + e;
+        if (d < a.capacity) {
+          T* oK = (T*)a.oK + d * D;
+          T* oV = (T*)a.oV + d * D;
+          if (lane < HD) {
+            if (esz == 1) {   // leaf: the token's rows (values loaded exactly)
+              st1(oK + lane, x0[u]);
+              st1(oK + HD + lane, x1[u]);
+              st2(oV + 2 * lane, y[u].x, y[u].y);
+            } else {
+              const float m0 = s0 / (float)esz, m1 = s1 / (float)esz;
+              st1(oK + lane, m0 * cp - m1 * sp);
+              st1(oK + HD + lane, m1 * cp + m0 * sp);
+              st2(oV + 2 * lane, v0, v1);
+            }
+          }
+          if (lane == 0) {
+            a.olnmu[d] = ent.lnmu[e];
+            a.opos[d] = ea + (esz - 1) / 2;
+          }
         }
-      } else {
-        const int d0 = (c - KP) * 8;
-        *(uint4*)(oV + d0) = *(const uint4*)(Vu + (int64_t)a0 * D + d0);
-        if constexpr (sizeof(T) == 4) *(uint4*)(oV + d0 + 4) = *(const uint4*)(Vu + (int64_t)a0 * D + d0 + 4);
-      }
-      continue;
-    }
-    const int c = local / SPL, sub = local % SPL;
-    if (c < KP) {
-      // prototype key: mean of the inverse-rotated keys, re-rotated at the representative position
-      const int p0 = c * 8;
-      float s0[8], s1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s0[e] = s1[e] = 0.f;
-      for (int i = a0 + sub; i < a0 + nz; i += SPL) {
-        float x0[8], x1[8];
-        kvcmf::Load8<T>::f(Ku + (int64_t)i * D + p0, x0);
-        kvcmf::Load8<T>::f(Ku + (int64_t)i * D + HD + p0, x1);
-        const float4 ca = *(const float4*)(a.rc + (int64_t)i * HD + p0), cb = *(const float4*)(a.rc + (int64_t)i * HD + p0 + 4);
-        const float4 sa = *(const float4*)(a.rs + (int64_t)i * HD + p0), sb = *(const float4*)(a.rs + (int64_t)i * HD + p0 + 4);
-        const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-        const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          s0[e] += x0[e] * cs[e] + x1[e] * sn[e];   // rotation by -theta
-          s1[e] += x1[e] * cs[e] - x0[e] * sn[e];
+        ++e;
+        ea = i + 1;
+        if (e < ne) {
+          esz = ent.sz[e];
+          al = ent.alpha[e];
+          ga = ent.gamma[e];
         }
+        s0 = s1 = v0 = v1 = 0.f;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {  // the SPL partial sums, combined in a fixed order
-        s0[e] = group_sum<SPL>(s0[e]);
-        s1[e] = group_sum<SPL>(s1[e]);
-      }
-      if (sub != 0) continue;
-      const int64_t prep = a0 + (nz - 1) / 2;
-      const float4 ca = *(const float4*)(a.rc + prep * HD + p0), cb = *(const float4*)(a.rc + prep * HD + p0 + 4);
-      const float4 sa = *(const float4*)(a.rs + prep * HD + p0), sb = *(const float4*)(a.rs + prep * HD + p0 + 4);
-      const float cs[8] = {ca.x, ca.y, ca.z, ca.w, cb.x, cb.y, cb.z, cb.w};
-      const float sn[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-      float k0[8], k1[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float m0 = s0[e] / (float)nz, m1 = s1[e] / (float)nz;
-        k0[e] = m0 * cs[e] - m1 * sn[e];
-        k1[e] = m1 * cs[e] + m0 * sn[e];
-      }
-      store8<T>(oK + p0, k0);
-      store8<T>(oK + HD + p0, k1);
-    } else {
-      // prototype value: (1 - beta) r_i / rel + beta / n weights (uniform if rel = 0)
-      const int d0 = (c - KP) * 8;
-      const float rel_n = a.node_rel[obase + j];
-      float acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      for (int i = a0 + sub; i < a0 + nz; i += SPL) {
-        const float w = rel_n > 0.f ? (1.f - a.beta) * ru[i] / rel_n + a.beta / (float)nz : 1.f / (float)nz;
-        float x[8];
-        kvcmf::Load8<T>::f(Vu + (int64_t)i * D + d0, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += w * x[e];
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = group_sum<SPL>(acc[e]);
-      if (sub == 0) store8<T>(oV + d0, acc);
     }
-  }
-  for (int f = tid; f < nfr; f += WS_THREADS) {
-    const int64_t dst = dst0 + f;
-    if (dst >= a.capacity) continue;
-    const int nz = fsz[f];
-    a.olnmu[dst] = nz == 1 ? 0.f : logf(a.node_mu[obase + fnode[f]]);
-    a.opos[dst] = t0 + fst[f] + (nz - 1) / 2;
   }
 }
 
@@ -546,13 +510,14 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
     KVC_PACK_T(write_kept_kernel, dim3(kvc_blocks(E * ppr2, 256)));
     KVC_LAUNCH_CHECK("pack_kept");
   } else {
-    const dim3 sg((unsigned)((int64_t)sh->n_layers * sh->n_kv_heads * a.sbound[sh->n_seq]));
+    const int64_t nwaves = (int64_t)sh->n_layers * sh->n_kv_heads * a.sbound[sh->n_seq];
+    const dim3 sg((unsigned)((nwaves + WS_WAVES - 1) / WS_WAVES));
     if (sh->dtype == KVC_BF16) {
-      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(WS_THREADS), 0, st, a, off);
-      else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(WS_THREADS), 0, st, a, off);
+      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<uint16_t, 128>), sg, dim3(WS_WAVES * 64), 0, st, a, off);
+      else hipLaunchKernelGGL((write_slots_kernel<uint16_t, 64>), sg, dim3(WS_WAVES * 64), 0, st, a, off);
     } else {
-      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<float, 128>), sg, dim3(WS_THREADS), 0, st, a, off);
-      else hipLaunchKernelGGL((write_slots_kernel<float, 64>), sg, dim3(WS_THREADS), 0, st, a, off);
+      if (d == 128) hipLaunchKernelGGL((write_slots_kernel<float, 128>), sg, dim3(WS_WAVES * 64), 0, st, a, off);
+      else hipLaunchKernelGGL((write_slots_kernel<float, 64>), sg, dim3(WS_WAVES * 64), 0, st, a, off);
     }
     KVC_LAUNCH_CHECK("pack_slots");
   }
