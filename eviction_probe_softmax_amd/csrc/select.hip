@@ -25,6 +25,7 @@
 //   not fit; the few candidates after it are resolved by at most
 //   (remaining budget) rounds of "earliest candidate whose current path cost
 //   fits".
+#include <algorithm>
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -572,6 +573,91 @@ __global__ void beta_kernel(AucArgs a, Ranges r) {
   }
 }
 
+// The same for midpoint trees, one wave per (unit, slot): every node's path
+// minimum B(j) = min(B(parent), key of Split j if untaken), B above the root
+// the Add's key if untaken, computed depth by depth in LDS from one load of the
+// slot's taken flags and utilities. The waves of a workgroup take the same
+// slot of consecutive units. beta of an untaken op that adds entries: its
+// node's B (the Add: its own key); of any other op: 0.
+constexpr int BS_WAVES = 4;
+struct SlotRows {
+  int32_t sbound[MAXS + 1];   // prefix over sequences of a bound on their slot counts
+};
+__global__ __launch_bounds__(BS_WAVES * 64) void beta_slot_kernel(AucArgs a, SlotRows sr) {
+  __shared__ uint64_t Bs[BS_WAVES][256];
+  const TreeArgs& ta = a.ta;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nunits = (int64_t)ta.Ly * ta.H;
+  const int64_t w = (int64_t)blockIdx.x * BS_WAVES + wv;
+  const int64_t row = w / nunits;
+  const int64_t lh = w - row * nunits;
+  if (row >= sr.sbound[ta.S]) return;
+  int s = 0;
+  while (row >= sr.sbound[s + 1]) ++s;
+  const int k = (int)(row - sr.sbound[s]);
+  if (k >= ta.n_slots[s]) return;
+  const int32_t* ss = ta.slot_start + (int64_t)s * (ta.stride + 1);
+  const int n = ss[k + 1] - ss[k];
+  const int64_t sbase = lh * 2 * ta.T + 2 * (ta.cu[s] + ss[k]);
+  const bool add_taken = a.taken[sbase] != 0;
+  const uint64_t kadd = add_taken ? ~0ull : op_key(a, sbase);
+  const int nn = 2 * n - 1;   // nodes of the midpoint tree
+  int par[4], dep[4];
+  uint64_t key[4];
+  int maxd = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = lane + 64 * q;
+    par[q] = -1;
+    dep[q] = -1;
+    key[q] = ~0ull;
+    if (j < nn) {
+      int cur = 0, sz = n, d = 0;
+      while (cur != j) {   // pre-order walk from the root
+        const int nl = (sz + 1) >> 1;
+        par[q] = cur;
+        ++d;
+        if (j < cur + 2 * nl) {
+          cur += 1;
+          sz = nl;
+        } else {
+          cur += 2 * nl;
+          sz -= nl;
+        }
+      }
+      dep[q] = d;
+      maxd = d > maxd ? d : maxd;
+      const int64_t o = sbase + 1 + j;
+      if (!a.taken[o]) key[q] = op_key(a, o);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int x = __shfl_xor(maxd, o, 64);
+    maxd = x > maxd ? x : maxd;
+  }
+  uint64_t* B = Bs[wv];
+  for (int d = 0; d <= maxd; ++d) {   // parents before children: a wave's LDS accesses stay in order
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (dep[q] == d) {
+        const uint64_t pb = par[q] < 0 ? kadd : B[par[q]];
+        B[lane + 64 * q] = pb < key[q] ? pb : key[q];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (lane == 0) a.beta[sbase] = (a.cost[sbase] != 0 && !add_taken) ? kadd : 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int j = lane + 64 * q;
+    if (j < nn) {
+      const int64_t o = sbase + 1 + j;
+      a.beta[o] = (a.cost[o] != 0 && !a.taken[o]) ? B[j] : 0;
+    }
+  }
+}
+
 __global__ void auction_mark_kernel(AucArgs a, Ranges r, const SelState* st) {
   int s;
   int64_t base, n;
@@ -956,7 +1042,20 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   aa.cost = trees->op_cost;
   aa.taken = op_taken;
   aa.beta = cover;
-  if (nbo > 0) {
+  if (nbo > 0 && !ta.topo) {   // midpoint trees: one wave a (unit, slot)
+    SlotRows sr{};
+    const int64_t smin = std::max<int64_t>(1, p->slot_len > 0 ? p->slot_len : p->slot_min);
+    for (int s = 0; s < sh->n_seq; ++s) {
+      const int64_t L = sh->cu_seqlens[s + 1] - sh->cu_seqlens[s];
+      sr.sbound[s + 1] = sr.sbound[s] + (int32_t)std::min<int64_t>(ta.stride, (L + smin - 1) / smin + 1);
+    }
+    const int64_t nw = (int64_t)LH * sr.sbound[sh->n_seq];
+    if (nw > 0) {
+      hipLaunchKernelGGL(beta_slot_kernel, dim3((unsigned)((nw + BS_WAVES - 1) / BS_WAVES)), dim3(BS_WAVES * 64), 0,
+                         stream, aa, sr);
+      KVC_LAUNCH_CHECK("beta_slot");
+    }
+  } else if (nbo > 0) {
     hipLaunchKernelGGL(beta_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops);
     KVC_LAUNCH_CHECK("beta");
   }
