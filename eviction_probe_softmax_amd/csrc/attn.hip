@@ -199,17 +199,21 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nrb = a.Rpad >> 5;
   float m[8], sm[8], tt[8], vv[8];
-  int minlim[8];  // the smallest last key over each row block
+  int minlim[8], maxl[8];  // the smallest and the largest last key over each row block
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
     m[rb] = -INFINITY;
     sm[rb] = 0.f;
     tt[rb] = 0.f;
     vv[rb] = 0.f;
-    int mnl = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1;
+    int mnl = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1, mxl = mnl;
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) mnl = min(mnl, __shfl_xor(mnl, o, 64));
+    for (int o = 16; o > 0; o >>= 1) {
+      mnl = min(mnl, __shfl_xor(mnl, o, 64));
+      mxl = max(mxl, __shfl_xor(mxl, o, 64));
+    }
     minlim[rb] = __builtin_amdgcn_readfirstlane(mnl);
+    maxl[rb] = __builtin_amdgcn_readfirstlane(mxl);
   }
   int maxlim = -1;
   for (int r = 0; r < a.Rpad; ++r) maxlim = max(maxlim, lim_s[r]);
@@ -232,6 +236,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(sizeof(
 #pragma unroll
     for (int rb = 0; rb < 8; ++rb) {
       if (rb >= nrb) break;
+      if (kb > maxl[rb]) continue;   // no row of the block sees these keys (seed rows ascend by position)
       kvc_f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) mma(acc, kf[ks], qf[(rb * KS + ks) * 64 + lane]);
@@ -449,13 +454,19 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
   const int64_t ubase = ((int64_t)w.l * a.H + w.h) * a.T + w.tok0;
   const T* K = (const T*)a.K + ubase * D;
   float hs_num = 0.f, hs_den = 0.f;
-  int minlim[8];  // the smallest last key over each row block (every row of a probe pass sees every key)
+  // the smallest and the largest last key over each row block (every row of
+  // a probe pass sees every key)
+  int minlim[8], maxl[8];
 #pragma unroll
   for (int rb = 0; rb < 8; ++rb) {
-    int mnl = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1;
+    int mnl = rb < nrb ? lim_s[rb * 32 + (lane & 31)] : -1, mxl = mnl;
 #pragma unroll
-    for (int o = 16; o > 0; o >>= 1) mnl = min(mnl, __shfl_xor(mnl, o, 64));
+    for (int o = 16; o > 0; o >>= 1) {
+      mnl = min(mnl, __shfl_xor(mnl, o, 64));
+      mxl = max(mxl, __shfl_xor(mxl, o, 64));
+    }
     minlim[rb] = __builtin_amdgcn_readfirstlane(mnl);
+    maxl[rb] = __builtin_amdgcn_readfirstlane(mxl);
   }
   // a lane owns one key; past the end it reads the last key (masked by kvalid)
   for (int64_t kb = w.k0 + wave * 32; kb < w.k1; kb += WAVES * 32) {
@@ -499,6 +510,7 @@ __global__ __launch_bounds__(THREADS) void colsum_kernel(AttnArgs a, const float
 #pragma unroll
       for (int rb = 0; rb < 8; ++rb) {
         if (rb >= nrb) break;
+        if (MODE == 1 && kb > maxl[rb]) continue;   // no row of the block sees these keys: they add 0
         kvc_f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) mma(acc, qf[(rb * KS + ks) * 64 + lane], kf[ks]);
