@@ -201,6 +201,22 @@ __global__ void zero_u8_kernel(uint8_t* p, int64_t n) {
   if (i < n) p[i] = 0;
 }
 
+__global__ void zero16_kernel(uint4* p, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+// nbytes zero bytes at p: 16-byte stores over the aligned part, bytes elsewhere
+void zero_bytes(void* p, int64_t nbytes, hipStream_t stream) {
+  if (nbytes <= 0) return;
+  int64_t head = 0;
+  if ((uintptr_t)p & 15) head = std::min<int64_t>(nbytes, 16 - (int64_t)((uintptr_t)p & 15));
+  if (head) hipLaunchKernelGGL(zero_u8_kernel, dim3(1), dim3(256), 0, stream, (uint8_t*)p, head);
+  const int64_t n16 = (nbytes - head) / 16, tail = nbytes - head - 16 * n16;
+  if (n16) hipLaunchKernelGGL(zero16_kernel, dim3(kvc_blocks(n16, 256)), dim3(256), 0, stream, (uint4*)((uint8_t*)p + head), n16);
+  if (tail)
+    hipLaunchKernelGGL(zero_u8_kernel, dim3(1), dim3(256), 0, stream, (uint8_t*)p + head + 16 * n16, tail);
+}
+
 int64_t ranges_blocks(const Ranges& r) {
   int64_t n = 0;
   for (int s = 0; s < r.S; ++s) n += r.nchunk[s] * r.U;
@@ -922,7 +938,7 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
 
   if (p->token_mode) {
     KVC_REQUIRE(rel, KVC_E_INVAL, "kvc_auction: token mode needs rel");
-    hipLaunchKernelGGL(zero_u8_kernel, dim3(kvc_blocks(E, 256)), dim3(256), 0, stream, op_taken, E);
+    zero_bytes(op_taken, E, stream);
     KVC_LAUNCH_CHECK("zero_taken");
     Ranges rg{};
     fill_ranges(rg, sh, p, 1, false);
@@ -952,9 +968,9 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   int32_t* ccost = c.take<int32_t>((size_t)sh->n_seq * Fmax);
   int32_t* ccount = c.take<int32_t>(MAXS);
   int64_t E2 = 2 * E;
-  hipLaunchKernelGGL(zero_u8_kernel, dim3(kvc_blocks(E2, 256)), dim3(256), 0, stream, op_taken, E2);
+  zero_bytes(op_taken, E2, stream);
   KVC_LAUNCH_CHECK("zero_taken");
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(kvc_blocks(E2, 256)), dim3(256), 0, stream, (unsigned long long*)cover, E2);
+  zero_bytes(cover, E2 * 8, stream);
   KVC_LAUNCH_CHECK("zero_cover");
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(MAXS), 0, stream, (unsigned long long*)ccount, (int64_t)MAXS / 2);
   KVC_LAUNCH_CHECK("zero_count");
