@@ -224,9 +224,10 @@ int64_t ranges_blocks(const Ranges& r) {
 }
 
 template <class Src>
-int run_select(const Ranges& r, const Src& src, SelState* st, unsigned long long* hist, hipStream_t stream) {
+int run_passes(const Ranges& r, const Src& src, SelState* st, unsigned long long* hist, hipStream_t stream, int p0,
+               int p1) {
   int64_t nb = ranges_blocks(r);
-  for (int pass = 0; pass < 8; ++pass) {
+  for (int pass = p0; pass < p1; ++pass) {
     if (nb > 0) {
       hipLaunchKernelGGL(hist_kernel<Src>, dim3((unsigned)nb), dim3(256), 0, stream, r, src, st, pass, hist);
       KVC_LAUNCH_CHECK("select_hist");
@@ -235,6 +236,63 @@ int run_select(const Ranges& r, const Src& src, SelState* st, unsigned long long
     KVC_LAUNCH_CHECK("select_choose");
   }
   return KVC_OK;
+}
+template <class Src>
+int run_select(const Ranges& r, const Src& src, SelState* st, unsigned long long* hist, hipStream_t stream) {
+  return run_passes(r, src, st, hist, stream, 0, 8);
+}
+
+// The elements still in the running after the first two passes (key matching
+// the 16-bit prefix, weight > 0), appended per sequence as (key, weight)
+// pairs: a block stages its chunk's matches in LDS (one LDS atomic a wave),
+// reserves their place with one global atomic, then copies them out. A
+// sequence's count may pass cap (then its list is incomplete and the caller
+// selects over the full source).
+template <class Src>
+__global__ __launch_bounds__(256) void compact_kernel(Ranges r, Src src, const SelState* st, uint64_t* ckey,
+                                                     int32_t* cw, unsigned int* ccnt, int64_t cap) {
+  __shared__ uint64_t sk[CH];
+  __shared__ int32_t sw[CH];
+  __shared__ unsigned int nloc, gbase;
+  int s;
+  int64_t base, n;
+  if (!range_work(r, blockIdx.x, s, base, n)) return;
+  const SelState S_ = st[s];
+  if (S_.all) return;
+  if (threadIdx.x == 0) nloc = 0;
+  __syncthreads();
+  const uint64_t hmask = ~0ull << 48;
+  const int lane = threadIdx.x & 63;
+  for (int64_t i0 = 0; i0 < n; i0 += 256) {   // a uniform trip count: every lane takes part in the ballot
+    const int64_t i = i0 + threadIdx.x;
+    uint64_t k = 0;
+    int64_t w = 0;
+    bool m = false;
+    if (i < n && src.get(base + i, s, k, w)) m = w > 0 && (k & hmask) == S_.prefix;
+    const uint64_t b = __ballot(m);
+    if (!b) continue;
+    const int lead = __builtin_ctzll(b);
+    unsigned int pos = 0;
+    if (lane == lead) pos = atomicAdd(&nloc, (unsigned int)__popcll(b));
+    pos = __shfl(pos, lead, 64);
+    if (m) {
+      const unsigned int q = pos + (unsigned int)__popcll(b & ((1ull << lane) - 1ull));
+      sk[q] = k;
+      sw[q] = (int32_t)w;
+    }
+  }
+  __syncthreads();
+  const unsigned int cnt = nloc;
+  if (cnt == 0) return;
+  if (threadIdx.x == 0) gbase = atomicAdd(&ccnt[s], cnt);
+  __syncthreads();
+  for (unsigned int q = threadIdx.x; q < cnt; q += 256) {
+    const int64_t idx = (int64_t)gbase + q;
+    if (idx < cap) {
+      ckey[(int64_t)s * cap + idx] = sk[q];
+      cw[(int64_t)s * cap + idx] = sw[q];
+    }
+  }
 }
 
 // ------------------------------------------------------------------ token mode
@@ -870,6 +928,15 @@ void fill_ranges(Ranges& r, const kvc_shape* sh, const kvc_params* p, int per_to
 }  // namespace
 
 namespace kvc {
+// capacity of a sequence's candidate list in the auction's select: 2^20, or
+// fewer where no sequence has that many ops
+int64_t auction_cand_cap(const kvc_shape* s, const kvc_params* p) {
+  Ranges ops{};
+  fill_ranges(ops, s, p, 0, true);
+  int64_t mx = 1;
+  for (int q = 0; q < s->n_seq; ++q) mx = std::max<int64_t>(mx, ops.len[q] * ops.U);
+  return std::min<int64_t>(mx, (int64_t)1 << 20);
+}
 size_t ws_auction(const kvc_shape* s, const kvc_params* p) {
   int64_t E = (int64_t)s->n_layers * s->n_kv_heads * s->total_tokens;
   std::vector<int64_t> B(s->n_seq), A(s->n_seq), F(s->n_seq);
@@ -889,6 +956,10 @@ size_t ws_auction(const kvc_shape* s, const kvc_params* p) {
     c.take<int32_t>(MAXS);
     c.take<int64_t>(MAXS);               // budget left after the tied group's walk
     c.take<unsigned long long>(MAXS);    // best op that still fits
+    const int64_t cap = auction_cand_cap(s, p);
+    c.take<uint64_t>((size_t)s->n_seq * cap);  // the auction's candidates after two passes: keys
+    c.take<int32_t>((size_t)s->n_seq * cap);   // and weights
+    c.take<unsigned int>(MAXS);                // their counts
   }
   return c.off + 256;
 }
@@ -1080,13 +1151,50 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
                      budget_r, 0, (const int64_t*)sfloor);
   KVC_LAUNCH_CHECK("init_state");
   OpSrc osrc{cover, trees->op_cost, op_taken};
-  if ((r = run_select(ops, osrc, st, hist, stream))) return r;
+  int64_t* kleft = c.take<int64_t>(MAXS);
+  unsigned long long* xbest = c.take<unsigned long long>(MAXS);
+  {
+    // two passes over every op; then the ops still in the running go to
+    // per-sequence lists and the last six passes read those (all of them
+    // over every op again if a list overflowed)
+    const int64_t cap = kvc::auction_cand_cap(sh, p);
+    uint64_t* lkey = c.take<uint64_t>((size_t)sh->n_seq * cap);
+    int32_t* lw = c.take<int32_t>((size_t)sh->n_seq * cap);
+    unsigned int* lcnt = c.take<unsigned int>(MAXS);
+    if ((r = run_passes(ops, osrc, st, hist, stream, 0, 2))) return r;
+    zero_bytes(lcnt, (int64_t)MAXS * sizeof(unsigned int), stream);
+    if (nbo > 0) {
+      hipLaunchKernelGGL(compact_kernel<OpSrc>, dim3((unsigned)nbo), dim3(256), 0, stream, ops, osrc, st, lkey, lw,
+                         lcnt, cap);
+      KVC_LAUNCH_CHECK("select_compact");
+    }
+    std::vector<unsigned int> hc(sh->n_seq);
+    KVC_REQUIRE(hipMemcpyAsync(hc.data(), lcnt, sizeof(unsigned int) * sh->n_seq, hipMemcpyDeviceToHost, stream) ==
+                        hipSuccess &&
+                    hipStreamSynchronize(stream) == hipSuccess,
+                KVC_E_HIP, "kvc_auction: reading the candidate counts failed");
+    bool over = false;
+    Ranges cr{};
+    cr.S = sh->n_seq;
+    cr.U = 1;
+    cr.unit_stride = 0;
+    for (int s = 0; s < sh->n_seq; ++s) {
+      over |= (int64_t)hc[s] > cap;
+      cr.start[s] = (int64_t)s * cap;
+      cr.len[s] = hc[s];
+      cr.nchunk[s] = (cr.len[s] + CH - 1) / CH;
+    }
+    if (over) {
+      if ((r = run_passes(ops, osrc, st, hist, stream, 2, 8))) return r;
+    } else {
+      CandSrc lsrc{lkey, lw};
+      if ((r = run_passes(cr, lsrc, st, hist, stream, 2, 8))) return r;
+    }
+  }
   if (nbo > 0) {
     hipLaunchKernelGGL(auction_mark_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops, st);
     KVC_LAUNCH_CHECK("auction_mark");
   }
-  int64_t* kleft = c.take<int64_t>(MAXS);
-  unsigned long long* xbest = c.take<unsigned long long>(MAXS);
   hipLaunchKernelGGL(auction_fixup_kernel, dim3(sh->n_seq), dim3(64), 0, stream, aa, st, (const int64_t*)sfloor,
                      spent, kleft);
   KVC_LAUNCH_CHECK("auction_fixup");
