@@ -257,7 +257,9 @@ template <class T, int D>
 __global__ __launch_bounds__(WS_WAVES * 64) void write_slots_kernel(PackArgs a, const int64_t* off) {
   constexpr int HD = D / 2;
   __shared__ WsEntries ent_all[WS_WAVES];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave index and everything derived from it are wave-uniform: scalar
+  // registers and scalar branches
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   WsEntries& ent = ent_all[wv];
   const int64_t nunits = (int64_t)a.Ly * a.H;
   const int64_t w = (int64_t)blockIdx.x * WS_WAVES + wv;
@@ -328,8 +330,11 @@ __global__ __launch_bounds__(WS_WAVES * 64) void write_slots_kernel(PackArgs a, 
   const T* Vu = (const T*)a.V + (lh * a.T + a.cu[s]) * D;
   const float* ru = a.rel + lh * a.T + a.cu[s];
   const int p = lane < HD ? lane : HD - 1;   // lanes past the pairs repeat the last one (not stored)
-  int e = 0, ea = t0, esz = ent.sz[0];       // current entry, its first position and size
-  float al = ent.alpha[0], ga = ent.gamma[0];
+  // the current entry's parameters, read from LDS by every lane, are made
+  // scalar so that the flush tests below are uniform branches
+  auto uni = [](float x) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x))); };
+  int e = 0, ea = t0, esz = __builtin_amdgcn_readfirstlane((int)ent.sz[0]);   // current entry, first position, size
+  float al = uni(ent.alpha[0]), ga = uni(ent.gamma[0]);
   float s0 = 0.f, s1 = 0.f, v0 = 0.f, v1 = 0.f, cp = 0.f, sp = 0.f;
   for (int g = t0; g < t0 + n; g += WS_G) {
     float x0[WS_G], x1[WS_G], c[WS_G], sn[WS_G], r[WS_G];
@@ -376,16 +381,16 @@ __global__ __launch_bounds__(WS_WAVES * 64) void write_slots_kernel(PackArgs a, 
             }
           }
           if (lane == 0) {
-            a.olnmu[d] = ent.lnmu[e];
+            a.olnmu[d] = ent.lnmu[e];   // lane 0 alone: a plain LDS read
             a.opos[d] = ea + (esz - 1) / 2;
           }
         }
         ++e;
         ea = i + 1;
         if (e < ne) {
-          esz = ent.sz[e];
-          al = ent.alpha[e];
-          ga = ent.gamma[e];
+          esz = __builtin_amdgcn_readfirstlane((int)ent.sz[e]);
+          al = uni(ent.alpha[e]);
+          ga = uni(ent.gamma[e]);
         }
         s0 = s1 = v0 = v1 = 0.f;
       }
