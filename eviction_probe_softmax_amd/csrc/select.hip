@@ -660,7 +660,7 @@ struct SlotRows {
 __global__ __launch_bounds__(BS_WAVES * 64) void beta_slot_kernel(AucArgs a, SlotRows sr) {
   __shared__ uint64_t Bs[BS_WAVES][256];
   const TreeArgs& ta = a.ta;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nunits = (int64_t)ta.Ly * ta.H;
   const int64_t w = (int64_t)blockIdx.x * BS_WAVES + wv;
   const int64_t row = w / nunits;
