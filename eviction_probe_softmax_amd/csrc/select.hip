@@ -295,6 +295,41 @@ __global__ __launch_bounds__(256) void compact_kernel(Ranges r, Src src, const S
   }
 }
 
+// A select over every element of r for two passes, then over the elements
+// still in the running, compacted into per-sequence lists (lkey, lw: cap a
+// sequence; lcnt their counts); all eight passes over every element if a
+// list overflows. Reads the counts back: waits on stream once.
+template <class Src>
+int select_compact(const Ranges& r, const Src& src, SelState* st, unsigned long long* hist, hipStream_t stream,
+                   uint64_t* lkey, int32_t* lw, unsigned int* lcnt, int64_t cap) {
+  int rc;
+  if ((rc = run_passes(r, src, st, hist, stream, 0, 2))) return rc;
+  zero_bytes(lcnt, (int64_t)MAXS * sizeof(unsigned int), stream);
+  const int64_t nb = ranges_blocks(r);
+  if (nb > 0) {
+    hipLaunchKernelGGL(compact_kernel<Src>, dim3((unsigned)nb), dim3(256), 0, stream, r, src, st, lkey, lw, lcnt, cap);
+    KVC_LAUNCH_CHECK("select_compact");
+  }
+  std::vector<unsigned int> hc(r.S);
+  KVC_REQUIRE(hipMemcpyAsync(hc.data(), lcnt, sizeof(unsigned int) * r.S, hipMemcpyDeviceToHost, stream) == hipSuccess &&
+                  hipStreamSynchronize(stream) == hipSuccess,
+              KVC_E_HIP, "kvc_auction: reading the candidate counts failed");
+  bool over = false;
+  Ranges cr{};
+  cr.S = r.S;
+  cr.U = 1;
+  cr.unit_stride = 0;
+  for (int s = 0; s < r.S; ++s) {
+    over |= (int64_t)hc[s] > cap;
+    cr.start[s] = (int64_t)s * cap;
+    cr.len[s] = hc[s];
+    cr.nchunk[s] = (cr.len[s] + CH - 1) / CH;
+  }
+  if (over) return run_passes(r, src, st, hist, stream, 2, 8);
+  CandSrc lsrc{lkey, lw};
+  return run_passes(cr, lsrc, st, hist, stream, 2, 8);
+}
+
 // ------------------------------------------------------------------ token mode
 __global__ __launch_bounds__(256) void mark_tokens_kernel(Ranges r, TokSrc src, const SelState* st, uint8_t* taken,
                                                           int64_t* spent) {
@@ -1038,6 +1073,12 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   int32_t* cid = c.take<int32_t>((size_t)sh->n_seq * Fmax);
   int32_t* ccost = c.take<int32_t>((size_t)sh->n_seq * Fmax);
   int32_t* ccount = c.take<int32_t>(MAXS);
+  int64_t* kleft = c.take<int64_t>(MAXS);
+  unsigned long long* xbest = c.take<unsigned long long>(MAXS);
+  const int64_t lcap = kvc::auction_cand_cap(sh, p);   // candidate lists of the leaf and op selects
+  uint64_t* lkey = c.take<uint64_t>((size_t)sh->n_seq * lcap);
+  int32_t* lw = c.take<int32_t>((size_t)sh->n_seq * lcap);
+  unsigned int* lcnt = c.take<unsigned int>(MAXS);
   int64_t E2 = 2 * E;
   zero_bytes(op_taken, E2, stream);
   KVC_LAUNCH_CHECK("zero_taken");
@@ -1074,7 +1115,7 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
                      budget_r, 0, (const int64_t*)nullptr);
   KVC_LAUNCH_CHECK("init_state");
   LeafSrc lsrc{rel, head_sens, full, sh->total_tokens, LH};
-  if ((r = run_select(leaves, lsrc, st, hist, stream))) return r;
+  if ((r = select_compact(leaves, lsrc, st, hist, stream, lkey, lw, lcnt, lcap))) return r;
   FloorArgs fa{};
   fa.ta = ta;
   fa.rel = rel;
@@ -1151,46 +1192,9 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
                      budget_r, 0, (const int64_t*)sfloor);
   KVC_LAUNCH_CHECK("init_state");
   OpSrc osrc{cover, trees->op_cost, op_taken};
-  int64_t* kleft = c.take<int64_t>(MAXS);
-  unsigned long long* xbest = c.take<unsigned long long>(MAXS);
-  {
-    // two passes over every op; then the ops still in the running go to
-    // per-sequence lists and the last six passes read those (all of them
-    // over every op again if a list overflowed)
-    const int64_t cap = kvc::auction_cand_cap(sh, p);
-    uint64_t* lkey = c.take<uint64_t>((size_t)sh->n_seq * cap);
-    int32_t* lw = c.take<int32_t>((size_t)sh->n_seq * cap);
-    unsigned int* lcnt = c.take<unsigned int>(MAXS);
-    if ((r = run_passes(ops, osrc, st, hist, stream, 0, 2))) return r;
-    zero_bytes(lcnt, (int64_t)MAXS * sizeof(unsigned int), stream);
-    if (nbo > 0) {
-      hipLaunchKernelGGL(compact_kernel<OpSrc>, dim3((unsigned)nbo), dim3(256), 0, stream, ops, osrc, st, lkey, lw,
-                         lcnt, cap);
-      KVC_LAUNCH_CHECK("select_compact");
-    }
-    std::vector<unsigned int> hc(sh->n_seq);
-    KVC_REQUIRE(hipMemcpyAsync(hc.data(), lcnt, sizeof(unsigned int) * sh->n_seq, hipMemcpyDeviceToHost, stream) ==
-                        hipSuccess &&
-                    hipStreamSynchronize(stream) == hipSuccess,
-                KVC_E_HIP, "kvc_auction: reading the candidate counts failed");
-    bool over = false;
-    Ranges cr{};
-    cr.S = sh->n_seq;
-    cr.U = 1;
-    cr.unit_stride = 0;
-    for (int s = 0; s < sh->n_seq; ++s) {
-      over |= (int64_t)hc[s] > cap;
-      cr.start[s] = (int64_t)s * cap;
-      cr.len[s] = hc[s];
-      cr.nchunk[s] = (cr.len[s] + CH - 1) / CH;
-    }
-    if (over) {
-      if ((r = run_passes(ops, osrc, st, hist, stream, 2, 8))) return r;
-    } else {
-      CandSrc lsrc{lkey, lw};
-      if ((r = run_passes(cr, lsrc, st, hist, stream, 2, 8))) return r;
-    }
-  }
+  // two passes over every op; then the ops still in the running go to the
+  // candidate lists and the last six passes read those
+  if ((r = select_compact(ops, osrc, st, hist, stream, lkey, lw, lcnt, lcap))) return r;
   if (nbo > 0) {
     hipLaunchKernelGGL(auction_mark_kernel, dim3((unsigned)nbo), dim3(256), 0, stream, aa, ops, st);
     KVC_LAUNCH_CHECK("auction_mark");
