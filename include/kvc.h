@@ -309,9 +309,9 @@ int kvc_build_trees_ex(const kvc_shape* shape, const kvc_params* prm, const void
  * allocatable budget minus K*C (C = compressible tokens per unit). spent
  * includes the K*C entries; spent_floor does not. head_sens is then needed
  * in token mode too.
- * Tree mode waits on stream once, mid-call: after two passes of its radix
- * select it reads back how many ops are still in the running (a few bytes)
- * to size the remaining passes. */
+ * Tree mode waits on stream twice, mid-call: after two passes of each of its
+ * two radix selects (floor leaves, ops) it reads back how many elements are
+ * still in the running (a few bytes) to size the remaining passes. */
 int kvc_auction(const kvc_shape* shape, const kvc_params* prm, const kvc_trees* trees,
                 const float* rel, const float* head_sens, const int32_t* slot_start,
                 const int32_t* n_slots, uint8_t* op_taken, int64_t* spent,
