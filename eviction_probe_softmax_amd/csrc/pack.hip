@@ -150,20 +150,19 @@ __global__ void seg_kernel(PackArgs a, const int64_t* off, const int64_t* total,
 }
 
 // Exact tokens (prompt, recent window, suffix) of every (unit, sequence): one
-// thread per 16-byte piece of a K or V row, over those tokens only.
+// thread per 16-byte piece of a K or V row, over those tokens only. Grid:
+// (pieces of the longest sequence's exact tokens / 256, units, sequences), so
+// the sequence and unit of a block are uniform.
 template <class T, int D>
 __global__ __launch_bounds__(256) void write_exact_kernel(PackArgs a, const int64_t* off) {
   constexpr int PPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+  const int s = blockIdx.z;
+  const int64_t lh = blockIdx.y;
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t X = a.xoff[a.S];
-  const int64_t per_lh = X * 2 * PPR;
-  if (g >= (int64_t)a.Ly * a.H * per_lh) return;
-  const int64_t lh = g / per_lh, r = g % per_lh;
-  const int64_t x = r / (2 * PPR);
-  const int pc = (int)(r % (2 * PPR));
-  int s = 0;
-  while (s + 1 < a.S && a.xoff[s + 1] <= x) ++s;
-  const int64_t k = x - a.xoff[s];
+  const int64_t nx = a.xoff[s + 1] - a.xoff[s];   // exact tokens of sequence s
+  if (g >= nx * 2 * PPR) return;
+  const int64_t k = g / (2 * PPR);
+  const int pc = (int)(g % (2 * PPR));
   const int64_t p = k < a.pe[s] ? k : a.c1[s] + (k - a.pe[s]);
   const int64_t i = lh * a.T + a.cu[s] + p;
   const int64_t dst = off[i];
@@ -498,7 +497,9 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
   KVC_LAUNCH_CHECK("pack_seg");
   int d = sh->head_dim;
   const int ppr2 = 2 * d * (sh->dtype == KVC_BF16 ? 2 : 4) / 16;  // 16-byte pieces of a K and a V row
-  const int64_t nex = (int64_t)sh->n_layers * sh->n_kv_heads * a.xoff[sh->n_seq] * ppr2;
+  int64_t xmax = 0;   // exact tokens of the longest exact region
+  for (int s = 0; s < sh->n_seq; ++s) xmax = std::max<int64_t>(xmax, a.xoff[s + 1] - a.xoff[s]);
+  const int64_t nex = xmax * ppr2;
 #define KVC_PACK_T(KERN, GRID)                                                                             \
   if (sh->dtype == KVC_BF16) {                                                                             \
     if (d == 128) hipLaunchKernelGGL((KERN<uint16_t, 128>), GRID, dim3(256), 0, st, a, off);               \
@@ -508,7 +509,7 @@ extern "C" int kvc_pack(const kvc_shape* sh, const kvc_params* p, const void* K,
     else hipLaunchKernelGGL((KERN<float, 64>), GRID, dim3(256), 0, st, a, off);                            \
   }
   if (nex > 0) {
-    KVC_PACK_T(write_exact_kernel, dim3(kvc_blocks(nex, 256)));
+    KVC_PACK_T(write_exact_kernel, dim3(kvc_blocks(nex, 256), (unsigned)(sh->n_layers * sh->n_kv_heads), (unsigned)sh->n_seq));
     KVC_LAUNCH_CHECK("pack_exact");
   }
   if (p->token_mode) {
