@@ -721,6 +721,7 @@ __global__ __launch_bounds__(SEED_THREADS) void seeds_kernel(AttnArgs a, const f
   __shared__ int wsum[SEED_THREADS / 64];
   __shared__ uint64_t s_prefix;
   __shared__ int64_t s_need;
+  __shared__ int s_done;
   const int unit = blockIdx.x;
   const int s = unit / (a.Ly * a.H);
   const int lh = unit % (a.Ly * a.H);
@@ -744,6 +745,7 @@ __global__ __launch_bounds__(SEED_THREADS) void seeds_kernel(AttnArgs a, const f
     if (tid == 0) {
       s_prefix = 0;
       s_need = a.M;
+      s_done = 0;
     }
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
@@ -772,10 +774,14 @@ __global__ __launch_bounds__(SEED_THREADS) void seeds_kernel(AttnArgs a, const f
       if (tid < 256 && above < need && above + hv >= need) {
         s_need = need - above;
         s_prefix = prefix | ((uint64_t)(255 - tid) << shift);
+        // the whole bin is taken: its prefix (lower bits zero) already
+        // separates the M largest keys from the rest
+        s_done = above + hv == need;
       }
       __syncthreads();
+      if (s_done) break;
     }
-    thr = s_prefix;  // the M-th largest key
+    thr = s_prefix;  // the M-th largest key, or the prefix of the last bin taken whole
   }
   // ordered compaction
   int c = 0;
