@@ -471,6 +471,7 @@ struct FloorArgs {
   int32_t* cid;        // [S][Fmax] leaf flat index
   int32_t* ccost;      // [S][Fmax]
   int32_t* ccount;     // [S]
+  int2* cslot;         // [S][Fmax] the candidate's slot (start, length), set by floor_cover
   int64_t Fmax;
 };
 
@@ -493,18 +494,23 @@ __global__ __launch_bounds__(256) void floor_collect_kernel(Ranges r, LeafSrc sr
   }
 }
 
-__device__ __forceinline__ void cand_path(const FloorArgs& f, int s, int64_t leaf, int64_t* ops, int& nops) {
+// root path of a candidate leaf whose slot [t0, t0 + n) is known
+__device__ __forceinline__ void cand_path_at(const FloorArgs& f, int s, int64_t leaf, int t0, int n, int64_t* ops,
+                                             int& nops) {
   const TreeArgs& a = f.ta;
   int64_t lh = leaf / a.T;
   int t = (int)(leaf % a.T - a.cu[s]);
-  int t0, n;
-  slot_of(a, s, t, t0, n);
   int nodes[MAX_PATH];
   int64_t base = lh * 2 * a.T + 2 * (a.cu[s] + t0);
   int c = leaf_path(a.topo ? a.topo + base : nullptr, t0, n, t, nodes);
   ops[0] = base;
   for (int q = 0; q < c; ++q) ops[1 + q] = base + 1 + nodes[q];
   nops = 1 + c;
+}
+__device__ __forceinline__ void cand_path(const FloorArgs& f, int s, int64_t leaf, int64_t* ops, int& nops) {
+  int t0, n;
+  slot_of(f.ta, s, (int)(leaf % f.ta.T - f.ta.cu[s]), t0, n);
+  cand_path_at(f, s, leaf, t0, n, ops, nops);
 }
 
 // one thread per candidate slot of every sequence
@@ -515,7 +521,11 @@ __global__ void floor_cover_kernel(FloorArgs f, int S) {
   if (s >= S || k >= min((int64_t)f.ccount[s], f.Fmax)) return;
   int64_t ops[MAX_PATH + 1];
   int nops;
-  cand_path(f, s, f.cid[i], ops, nops);
+  const int64_t leaf = f.cid[i];
+  int t0, n;
+  slot_of(f.ta, s, (int)(leaf % f.ta.T - f.ta.cu[s]), t0, n);
+  f.cslot[i] = make_int2(t0, n);   // kept for the tail's rounds
+  cand_path_at(f, s, leaf, t0, n, ops, nops);
   uint64_t key = f.ckey[i];
   for (int q = 0; q < nops; ++q) atomicMax((unsigned long long*)&f.cover[ops[q]], (unsigned long long)key);
 }
@@ -584,7 +594,8 @@ __global__ __launch_bounds__(FT_THREADS) void floor_tail_kernel(FloorArgs f, con
       if (key >= pos) continue;
       int64_t ops[MAX_PATH + 1];
       int nops;
-      cand_path(f, s, f.cid[i], ops, nops);
+      const int2 sl = f.cslot[i];
+      cand_path_at(f, s, f.cid[i], sl.x, sl.y, ops, nops);
       int c = 0;
       for (int q = 0; q < nops; ++q)
         if (!f.taken[ops[q]]) c += f.op_cost[ops[q]];
@@ -599,7 +610,8 @@ __global__ __launch_bounds__(FT_THREADS) void floor_tail_kernel(FloorArgs f, con
       if (f.ckey[i] != win) continue;
       int64_t ops[MAX_PATH + 1];
       int nops;
-      cand_path(f, s, f.cid[i], ops, nops);
+      const int2 sl = f.cslot[i];
+      cand_path_at(f, s, f.cid[i], sl.x, sl.y, ops, nops);
       int c = 0;
       for (int q = 0; q < nops; ++q)
         if (!f.taken[ops[q]]) c += f.op_cost[ops[q]];
@@ -995,6 +1007,7 @@ size_t ws_auction(const kvc_shape* s, const kvc_params* p) {
     c.take<uint64_t>((size_t)s->n_seq * cap);  // the auction's candidates after two passes: keys
     c.take<int32_t>((size_t)s->n_seq * cap);   // and weights
     c.take<unsigned int>(MAXS);                // their counts
+    c.take<int2>((size_t)s->n_seq * Fmax);     // floor candidates' slots
   }
   return c.off + 256;
 }
@@ -1079,6 +1092,7 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   uint64_t* lkey = c.take<uint64_t>((size_t)sh->n_seq * lcap);
   int32_t* lw = c.take<int32_t>((size_t)sh->n_seq * lcap);
   unsigned int* lcnt = c.take<unsigned int>(MAXS);
+  int2* cslot = c.take<int2>((size_t)sh->n_seq * Fmax);
   int64_t E2 = 2 * E;
   zero_bytes(op_taken, E2, stream);
   KVC_LAUNCH_CHECK("zero_taken");
@@ -1127,6 +1141,7 @@ extern "C" int kvc_auction(const kvc_shape* sh, const kvc_params* p, const kvc_t
   fa.cid = cid;
   fa.ccost = ccost;
   fa.ccount = ccount;
+  fa.cslot = cslot;
   fa.Fmax = Fmax;
   int64_t nb = ranges_blocks(leaves);
   bool any_floor = false;
